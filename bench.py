@@ -1,0 +1,317 @@
+#!/usr/bin/env python3
+"""Decode-step throughput of page-scored sparse attention on one MI355X.
+
+One step = one pass of the whole hot path over the batch:
+  page level (default gqa_ragged, also mha_tiny / long_context):
+      page_score -> page_topk -> sparse_paged_decode -> lse_merge
+      (statistics built once beforehand, timed separately)
+  high_batch: pagestats_update (append + refresh) -> the four above
+  h2o_token:  pagestats_update (append + reset) -> h2o_accumulate ->
+      page_topk -> sparse_paged_decode -> lse_merge
+
+Inputs are seeded synthetic tensors already resident in HBM.  To measure
+HBM rather than the 256 MB memory-side cache, the timed steps rotate over R
+replicas of the workload (separate caches, statistics and buffers, like the
+layers of a model), so each step's data was last touched R-1 steps earlier.
+
+Prints ONE JSON line: steps/s (value), effective HBM GB/s of the step and of
+each kernel (algorithmic bytes / time, HIP events on the launch stream), the
+roofline entry of the dominant kernel, and the float64 oracle timed on a
+bounded sample on the host cores (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gqa_ragged",
+                    choices=["mha_tiny", "gqa_ragged", "h2o_token", "long_context",
+                             "high_batch"])
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="rotation depth (0 = enough to exceed 1 GiB per cycle)")
+    ap.add_argument("--splits", type=int, default=0, help="override num_splits")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+# ------------------------------------------------------ algorithmic bytes
+
+def unique_kv_bytes(wl, sel_idx, sel_cnt, seq_lens, H_sel):
+    """K+V bytes of every distinct (request, kv head, page) selected, counted
+    once, over its valid rows."""
+    G_sel = wl.H_q // H_sel if H_sel == wl.H_q else 1
+    total = 0
+    pages_total = 0
+    for b in range(wl.B):
+        S = int(seq_lens[b])
+        for h in range(wl.H_kv):
+            if H_sel == wl.H_q:
+                rows = range(h * wl.G, (h + 1) * wl.G)
+            else:
+                rows = [h]
+            u = set()
+            for r in rows:
+                u.update(sel_idx[b, r, :sel_cnt[b, r]].tolist())
+            pages = np.fromiter(u, dtype=np.int64, count=len(u))
+            n = np.minimum(wl.P, S - pages * wl.P)
+            total += int(n.sum()) * wl.D * 2 * 2
+            pages_total += len(u)
+    del G_sel
+    return total, pages_total
+
+
+def kernel_bytes(wl, sel_idx, sel_cnt, seq_lens, num_splits, token_level):
+    """Algorithmic HBM bytes of each kernel of one step (formulas in DESIGN)."""
+    B, Hq, Hkv, D, P = wl.B, wl.H_q, wl.H_kv, wl.D, wl.P
+    N = (seq_lens.astype(np.int64) + P - 1) // P
+    H_sel = Hkv if token_level else Hq
+    cnt = int(sel_cnt.sum())
+    kv, upages = unique_kv_bytes(wl, sel_idx, sel_cnt, seq_lens, H_sel)
+    out = {}
+    if token_level:
+        S = seq_lens.astype(np.int64)
+        out["pagestats_update"] = B * Hkv * D * 2 * 2 * 2 + B * Hkv * 2 + B * 8
+        out["h2o_accumulate"] = int((S * Hkv * D * 2).sum() + (S * Hkv * 2 * 2).sum()
+                                    + (S * Hkv * 4 * 2).sum() + (S * Hkv * 4).sum()
+                                    + B * Hq * D * 4 + S.sum() * 4 * 2)
+    else:
+        if wl.steps > 1:   # append + tail refresh
+            out["pagestats_update"] = int(B * Hkv * D * 2 * 2 * 2
+                                          + B * Hkv * D * 2 * (P - 1)
+                                          + B * Hkv * D * 8)
+        out["page_score"] = int((N * (Hkv * 8 * D + Hq * 4 + 4)).sum() + B * Hq * D * 4)
+    out["page_topk"] = int((N * H_sel * 4).sum() + cnt * 4)
+    out["sparse_paged_decode"] = int(kv + B * Hq * D * 4 + cnt * 4
+                                     + B * Hq * num_splits * (D + 1) * 4)
+    out["lse_merge"] = int(B * Hq * num_splits * (D + 1) * 4 + B * Hq * (D + 1) * 4)
+    return out, upages
+
+
+# ------------------------------------------------------------ cpu baseline
+
+def cpu_baseline(wl, cache_bits, q, seq_lens, seconds, token_level, hh_bits=None):
+    """The float64 oracle on a bounded sample of requests (whole step for
+    those requests), scaled to steps/s of the full batch."""
+    import oracle
+    oracle.build() if not os.path.exists(os.path.join(
+        os.path.dirname(os.path.abspath(oracle.__file__)), "liboracle.so")) else None
+    qd = q.double().numpy()
+    reps, rows_done, t_used = 0, 0, 0.0
+    b = 0
+    if token_level:
+        while t_used < seconds and reps < 10_000:
+            bb = b % wl.B
+            bt = wl.block_table[bb:bb + 1]
+            sl = seq_lens[bb:bb + 1]
+            hh = hh_bits.copy()
+            t0 = time.perf_counter()
+            sc = oracle.h2o_step(qd[bb:bb + 1], cache_bits, bt, sl, hh, wl.bos,
+                                 wl.eos, wl.softmax_scale, wl.decay)
+            for h in range(wl.H_kv):
+                sel = oracle.select(sc[0, h, :int(sl[0])], wl.topk_pages, 0.0,
+                                    wl.bos, wl.eos)
+                for g in range(wl.G):
+                    oracle.attend(qd[bb, h * wl.G + g], cache_bits, h, bt[0],
+                                  int(sl[0]), sel, wl.softmax_scale)
+            t_used += time.perf_counter() - t0
+            reps += 1
+            rows_done += 1
+            b += 1
+        sample = f"{rows_done} request-steps of the token-level step (1 of {wl.B} requests each)"
+    else:
+        st_cache = {}
+        while t_used < seconds and reps < 10_000:
+            bb = b % wl.B
+            if bb not in st_cache:
+                st_cache[bb] = oracle.page_stats(cache_bits, wl.block_table[bb:bb + 1],
+                                                 seq_lens[bb:bb + 1], wl.P)
+            t0 = time.perf_counter()
+            k_cap = min(max(wl.topk_pages, int(math.floor(wl.topk_frac * wl.bt_ld)),
+                            wl.bos + wl.eos), wl.bt_ld)
+            oracle.decode_step(qd[bb:bb + 1], cache_bits, wl.block_table[bb:bb + 1],
+                               seq_lens[bb:bb + 1], st_cache[bb], wl.w_avg, wl.w_peak,
+                               wl.topk_pages, wl.topk_frac, wl.bos, wl.eos,
+                               wl.softmax_scale, k_cap)
+            t_used += time.perf_counter() - t0
+            reps += 1
+            rows_done += 1
+            b += 1
+        sample = (f"{rows_done} request-steps of score+select+attend "
+                  f"(1 of {wl.B} requests each, statistics prebuilt)")
+    per_request = t_used / rows_done
+    steps_per_s = 1.0 / (per_request * wl.B)
+    return {"value": steps_per_s, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": sample, "seconds": round(t_used, 2)}
+
+
+# -------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by request / kv head with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        return 2
+    import torch
+    import sparse_kv_cache_amd  # noqa: F401  (loads lazily; fails loudly if unbuilt)
+    from sparse_kv_cache_amd import workloads as W
+    from sparse_kv_cache_amd.decode import SparseDecoder
+
+    sparse_kv_cache_amd.load_library()
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    wl = W.WORKLOADS[args.workload]()
+    token_level = wl.name == "h2o_token"
+    if args.splits:
+        wl.num_splits = args.splits
+    t_gen = time.perf_counter()
+    cache0 = W.make_cache(wl, device=dev)
+    q = W.make_queries(wl, 0, device=dev)
+    bt = torch.from_numpy(wl.block_table).to(dev)
+    seq_steps = [torch.from_numpy(wl.seq_lens_at(s)).to(dev) for s in range(wl.steps)]
+    per_step_mb = {"mha_tiny": 0.3, "gqa_ragged": 120, "h2o_token": 46,
+                   "long_context": 190, "high_batch": 4500}[wl.name]
+    R = args.replicas or max(1, min(16, math.ceil(1024 / per_step_mb)))
+    if wl.name == "high_batch":
+        R = 1
+    caches = [cache0] + [cache0.clone() for _ in range(R - 1)]
+    decs = [SparseDecoder.for_workload(wl, device=dev) for _ in range(R)]
+    new_kv = [W.make_new_kv(wl, s, device=dev) for s in range(min(wl.steps, 64))] \
+        if wl.steps > 1 else None
+    if token_level:
+        hh0 = W.make_hh(wl, device=dev)
+        for d in decs:
+            d.hh.copy_(hh0)
+    stats_ms = None
+    if not token_level:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for c, d in zip(caches, decs):
+            d.rebuild_stats(c, bt, seq_steps[0])
+        e1.record()
+        torch.cuda.synchronize()
+        stats_ms = e0.elapsed_time(e1) / R
+    gen_s = time.perf_counter() - t_gen
+
+    names = (["pagestats_update"] if wl.steps > 1 else []) + \
+        (["h2o_accumulate"] if token_level else ["page_score"]) + \
+        ["page_topk", "sparse_paged_decode", "lse_merge"]
+
+    def run_step(i, evs=None):
+        r = i % R
+        d, c = decs[r], caches[r]
+        s = i % wl.steps
+        sl = seq_steps[s]
+        rec = (lambda k: evs[k].record()) if evs is not None else (lambda k: None)
+        k = 0
+        rec(k); k += 1
+        if wl.steps > 1:
+            kn, vn = new_kv[s % len(new_kv)]
+            d.append(c, bt, sl, kn, vn)
+            rec(k); k += 1
+        if token_level:
+            d.accumulate(q, c, bt, sl)
+        else:
+            d.score(q, bt, sl)
+        rec(k); k += 1
+        d.select(sl)
+        rec(k); k += 1
+        d.attend(q, c, bt, sl)
+        rec(k); k += 1
+        d.merge()
+        rec(k); k += 1
+
+    for i in range(args.warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+
+    nev = len(names) + 1
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run_step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_kernel_ms = {n: 0.0 for n in names}
+    step_ms = 0.0
+    for ev in events:
+        for j, n in enumerate(names):
+            per_kernel_ms[n] += ev[j].elapsed_time(ev[j + 1])
+        step_ms += ev[0].elapsed_time(ev[-1])
+    per_kernel_ms = {n: v / args.steps for n, v in per_kernel_ms.items()}
+    gpu_ms = step_ms / args.steps
+    ms_per_step = wall * 1000.0 / args.steps
+
+    # algorithmic bytes from the selections the last step produced
+    last = (args.warmup + args.steps - 1)
+    d = decs[last % R]
+    sl_last = wl.seq_lens_at(last % wl.steps)
+    sel_idx = d.sel_idx.cpu().numpy()
+    sel_cnt = d.sel_cnt.cpu().numpy()
+    kb, upages = kernel_bytes(wl, sel_idx, sel_cnt, sl_last, wl.num_splits, token_level)
+    step_bytes = sum(kb.values())
+    kern = {}
+    for n in names:
+        t = per_kernel_ms[n]
+        kern[n] = {"us": round(t * 1000, 2), "bytes": kb[n],
+                   "GBps": round(kb[n] / (t * 1e-3) / 1e9, 1) if t > 0 else None}
+    dominant = max(names, key=lambda n: per_kernel_ms[n])
+    focus = "sparse_paged_decode"
+    a = kb[focus] / (per_kernel_ms[focus] * 1e-3) / 1e9
+    roofline = {"kernel": focus, "bound": "hbm", "achieved": round(a, 1),
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(a / PEAK_HBM_GBPS, 4),
+                "traffic": None, "bytes_per_launch": kb[focus],
+                "us_per_launch": round(per_kernel_ms[focus] * 1000, 2)}
+
+    result = {
+        "metric": "sparse decode steps/s + effective HBM GB/s (% of peak), GQA 32/8 D=128",
+        "value": round(args.steps / (wall), 3),
+        "unit": "steps/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "gpu_ms_per_step": round(gpu_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "kv_dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H_q": wl.H_q, "H_kv": wl.H_kv,
+                   "D": wl.D, "page_size": wl.P, "topk_pages": wl.topk_pages,
+                   "topk_frac": wl.topk_frac, "num_splits": wl.num_splits,
+                   "mean_seq_len": float(np.mean(sl_last)), "replicas": R,
+                   "parallelism": "single-gpu"},
+        "effective_GBps": round(step_bytes / (gpu_ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(step_bytes / (gpu_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "step_bytes": int(step_bytes), "unique_page_heads": int(upages),
+        "kernels": kern, "dominant_kernel": dominant,
+        "stats_rebuild_ms": None if stats_ms is None else round(stats_ms, 4),
+        "roofline": roofline,
+        "setup_s": round(gen_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        from sparse_kv_cache_amd.workloads import bf16_bits
+        cb = bf16_bits(caches[last % R])
+        hb = bf16_bits(hh0) if token_level else None
+        result["cpu_baseline"] = cpu_baseline(wl, cb, q.cpu(), sl_last,
+                                              args.cpu_seconds, token_level, hb)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,214 @@
+/*
+ * sparsekv.h -- C ABI of libsparsekv.so: decode-time page-scored sparse
+ * attention over a paged bf16 KV cache, hand-written HIP for gfx950 (MI355X).
+ *
+ * Sources (cited by page title and section):
+ *   [VTX] vortex_torch pull request "flow: add H2O sparse attention
+ *         (page-level and token-level, MHA + GQA)": "Page-level variants"
+ *         (page score), "Token-level variants" (accumulator, reset on write,
+ *         decay), the follow-up's oracle harness (reserved bos/eos window).
+ *   [EKV] EntmaxKV README, "How it works" and "Quick start": the cache layout
+ *         [2, num_blocks, page_size, H_kv, D] plus a block table, per-page key
+ *         statistics, top-k pages per query head with the tail page in the
+ *         budget, exact attention over the selection, append of k_new/v_new.
+ *   [MLA] vllm.cpp test_ops_mla_chunked_context.cpp: chunked attention merged
+ *         by log-sum-exp, MergeAttnStates and its -inf / +inf rules.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer is a DEVICE pointer owned by the caller.  The library
+ *     never allocates, frees or synchronises; each call only enqueues work on
+ *     `stream` and returns.  Outputs are caller buffers; the cache, the page
+ *     statistics and hh_score are updated in place.
+ *   - Tensors are dense row-major, except for the explicit leading dimensions
+ *     bt_ld (block table row length) and score_ld (score row length).
+ *   - bf16 values travel as their uint16_t bit patterns.
+ *   - seq_lens[b] is the token count of request b INCLUDING the token appended
+ *     this step.  Request b has N_b = ceil(seq_lens[b] / page_size) logical
+ *     pages; logical page p is physical block block_table[b * bt_ld + p].
+ *     Kernels clamp N_b to bt_ld (and to score_ld where scores are indexed) so
+ *     that a bad length cannot index outside the caller's tables.
+ *   - Query head i reads kv head i / G with G = H_q / H_kv (consecutive
+ *     groups); H_q must be a multiple of H_kv and G <= 16.
+ *   - Supported shapes: D in {64, 128}; page_size in {1, 2, 4, 8, 16};
+ *     h2o_accumulate also needs H_kv <= 16.
+ *   - Device-side contents (block ids, lengths, selections) are trusted: they
+ *     must lie inside the caller's buffers.
+ *
+ * Return value of every int entry point
+ *   SKV_OK (0) on success.  SKV_EINVAL (-22) for a bad scalar argument,
+ *   SKV_EFAULT (-14) for a required NULL pointer: both are detected before
+ *   anything is enqueued.  SKV_EIO (-5) if the launch itself failed
+ *   (hipGetLastError).  sparsekv_last_error() returns a message for the most
+ *   recent failure on the calling thread.
+ */
+#ifndef SPARSEKV_H
+#define SPARSEKV_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SKV_OK 0
+#define SKV_EIO (-5)
+#define SKV_EFAULT (-14)
+#define SKV_EINVAL (-22)
+
+/* Message for the latest non-zero return on this thread ("" if none). */
+const char *sparsekv_last_error(void);
+
+/*
+ * pagestats_update -- per-page key statistics, optionally fused with the KV
+ * append of one decode step.   [VTX "Page-level variants": element-wise
+ * min / max envelope and mean of the keys; EKV "How it works" and
+ * "Quick start": statistics kept per page, k_new / v_new appended by the
+ * decode call; VTX "Token-level variants" point 2: the score slot of a freshly
+ * written token is zeroed.]
+ *
+ *   kv_cache   bf16 [2, num_blocks, page_size, H_kv, D]   in/out
+ *   k_min,
+ *   k_max      bf16 [num_blocks, H_kv, D]                 out (exact)
+ *   k_mean     fp32 [num_blocks, H_kv, D]                 out (fp32 sum / n)
+ *              The three may all be NULL (page_size 1 needs no statistics).
+ *   block_table int32 [B, bt_ld], seq_lens int32 [B]
+ *   k_new, v_new bf16 [B, H_kv, D] or both NULL.
+ *     Both NULL  = rebuild: statistics of every page p < N_b of every request,
+ *                  over its n = min(P, S_b - p*P) valid rows.
+ *     Both given = append: token S_b - 1 is written (block
+ *                  bt[b][(S_b-1)/P], row (S_b-1)%P), then the statistics of
+ *                  that tail page are recomputed over its valid rows.
+ *   hh_score   bf16 [num_blocks * page_size, H_kv] or NULL; in append mode the
+ *              written slot is set to 0 for every kv head.
+ */
+int pagestats_update(uint16_t *kv_cache, int64_t num_blocks, int page_size,
+                     int H_kv, int D, uint16_t *k_min, uint16_t *k_max,
+                     float *k_mean, const int32_t *block_table, int64_t bt_ld,
+                     const int32_t *seq_lens, int B, const uint16_t *k_new,
+                     const uint16_t *v_new, uint16_t *hh_score,
+                     hipStream_t stream);
+
+/*
+ * page_score -- score of every page p < N_b for every query head.
+ * [VTX "Page-level variants": average relevance q . mean(k), peak relevance
+ * sum_d max(q_d * max_d, q_d * min_d) (an upper bound of max_t q . k_t that
+ * needs both envelopes because q is signed), combined as
+ * w_avg * avg + w_peak * peak; EKV "How it works": pages are scored from the
+ * statistics alone, without touching the cached tokens.]
+ *
+ *   q        fp32 [B, H_q, D]
+ *   k_min, k_max bf16 / k_mean fp32 [num_blocks, H_kv, D] (from pagestats_update)
+ *   scores   fp32 [B, H_q, score_ld], logical page order; entries p >= N_b
+ *            are not written.  score_ld >= bt_ld.
+ * The softmax scale is not applied (a positive factor does not change ranks).
+ */
+int page_score(const float *q, int B, int H_q, int H_kv, int D,
+               const uint16_t *k_min, const uint16_t *k_max,
+               const float *k_mean, const int32_t *block_table, int64_t bt_ld,
+               const int32_t *seq_lens, int page_size, float w_avg,
+               float w_peak, float *scores, int64_t score_ld,
+               hipStream_t stream);
+
+/*
+ * page_topk -- top-k selection per row (b, h), h < H_sel.
+ * [EKV "How it works": keep topk_pages per query head, the budget counts
+ * pages and includes the always-attended tail page; VTX follow-up: the
+ * reserved leading bos and trailing eos entries are kept unconditionally and
+ * only the window between them is ranked.]
+ *
+ *   N = min(ceil(seq_lens[b] / page_size), score_ld) candidates per row.
+ *   k = min(N, max(topk_pages, floor(topk_frac * N))), floor taken in double
+ *       of the fp32 topk_frac.
+ *   R = [0, bos) u [N - eos, N) clipped to [0, N) is always selected; the
+ *   other max(0, k - |R|) entries are the highest scores of [bos, N - eos),
+ *   ties going to the lower index (-0.0 equals +0.0; scores must not be NaN).
+ *   sel_idx  int32 [B, H_sel, k_cap]: ascending indices, padded with -1.
+ *   sel_cnt  int32 [B, H_sel]: number selected (= max(|R|, k)).
+ *   Requires k_cap >= max(topk_pages, floor(topk_frac * score_ld), bos + eos)
+ *   and score_ld <= 32768.
+ */
+int page_topk(const float *scores, int64_t score_ld, int B, int H_sel,
+              const int32_t *seq_lens, int page_size, int topk_pages,
+              float topk_frac, int reserved_bos, int reserved_eos,
+              int32_t *sel_idx, int32_t *sel_cnt, int k_cap,
+              hipStream_t stream);
+
+/*
+ * sparse_paged_decode -- split-K exact softmax attention over the tokens of
+ * the selected pages.  [EKV "How it works": only the selected pages are
+ * attended and the attention is exact over that selection; MLA: chunked
+ * partials merged by log-sum-exp equal single-shot attention.]
+ *
+ *   H_sel == H_q : row (b, i) of sel_idx is query head i's own selection.
+ *   H_sel == H_kv: the G query heads of kv head h share row (b, h) (the
+ *                  token-level flow selects per kv head).
+ *   Each selection row (cnt entries, ascending) is cut into num_splits
+ *   contiguous groups of c = ceil(cnt / num_splits) entries; split s holds
+ *   entries [s*c, min((s+1)*c, cnt)).  Tokens are {p*P + t : t < n_p} with
+ *   n_p = min(P, S_b - p*P); l = scale * q . k.  Per (b, i, s):
+ *     o_part   fp32 [B, H_q, num_splits, D]  = sum softmax(l) v over the split
+ *     lse_part fp32 [B, H_q, num_splits]     = ln sum exp(l)  (-inf if empty,
+ *                                               with o_part = 0)
+ *   Pages selected by several heads of one kv head inside the same split are
+ *   read from memory once for all of them.
+ */
+int sparse_paged_decode(const float *q, int B, int H_q, int H_kv, int D,
+                        const uint16_t *kv_cache, int64_t num_blocks,
+                        int page_size, const int32_t *block_table,
+                        int64_t bt_ld, const int32_t *seq_lens,
+                        const int32_t *sel_idx, const int32_t *sel_cnt,
+                        int k_cap, int H_sel, float scale, int num_splits,
+                        float *o_part, float *lse_part, hipStream_t stream);
+
+/*
+ * lse_merge -- N-way log-sum-exp merge of split partials.  [MLA:
+ * MergeAttnStates algebra; a +inf lse is read as -inf; if every partial is
+ * -inf the first partial is emitted with lse -inf.]
+ *
+ *   o_part [rows, num_splits, D], lse_part [rows, num_splits] (fp32)
+ *   out    fp32 [rows, D];  lse_out fp32 [rows] or NULL.
+ *   With M = max lse_s, w_s = exp(lse_s - M):
+ *     out = sum w_s o_s / sum w_s,  lse = M + ln sum w_s.
+ */
+int lse_merge(const float *o_part, const float *lse_part, int rows,
+              int num_splits, int D, float *out, float *lse_out,
+              hipStream_t stream);
+
+/*
+ * h2o_accumulate -- token-level heavy-hitter accumulator step (page_size 1).
+ * [VTX "Token-level variants": the accumulated quantity is the softmax
+ * attention probability over the request's scored tokens, scale defaults to
+ * D^-0.5, the accumulator decays (0.984375 = 1 - 2^-6, exact in bf16) and is
+ * stored in bf16; the follow-up's reference step: softmax over the window
+ * [bos, S - eos) only.]
+ *
+ *   Per (b, kv head h): qbar = mean of the G query rows of the group,
+ *   l_t = scale * qbar . k_t for t in W = [bos, S_b - eos), p = softmax_W(l),
+ *   hh_t <- bf16( bf16(p_t) + bf16(decay) * hh_t ) for t in W (fp32 math,
+ *   round-to-nearest-even stores); entries outside W are not touched.
+ *   hh_score bf16 [num_blocks, H_kv] (token slot = physical block), in place.
+ *   scores   fp32 [B, H_kv, score_ld]: the new hh value of every t < S_b, in
+ *            logical order (input of page_topk with H_sel = H_kv).
+ *   scratch  fp32 device buffer of at least
+ *            h2o_scratch_floats(B, H_kv, bt_ld) floats (its contents on entry
+ *            are ignored).
+ *   decay must lie in (0, 1].
+ */
+int h2o_accumulate(const float *q, int B, int H_q, int H_kv, int D,
+                   const uint16_t *kv_cache, int64_t num_blocks, int page_size,
+                   const int32_t *block_table, int64_t bt_ld,
+                   const int32_t *seq_lens, int reserved_bos, int reserved_eos,
+                   float scale, float decay, uint16_t *hh_score, float *scores,
+                   int64_t score_ld, float *scratch, int64_t scratch_floats,
+                   hipStream_t stream);
+
+/* Scratch size (floats) h2o_accumulate needs for B requests, H_kv heads and
+ * rows of at most max_tokens tokens.  No device work; -1 on bad arguments. */
+int64_t h2o_scratch_floats(int B, int H_kv, int64_t max_tokens);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSEKV_H */

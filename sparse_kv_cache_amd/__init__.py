@@ -1,0 +1,267 @@
+"""sparse_kv_cache_amd -- page-scored sparse decode attention for MI355X.
+
+Thin Python binding of the C ABI in ``include/sparsekv.h`` (libsparsekv.so,
+hand-written HIP for gfx950).  Every function here only checks tensor
+dtypes / shapes / devices, marshals ``data_ptr()`` values and the current HIP
+stream, and calls the entry point of the same name; all arithmetic runs in the
+library's kernels.  PyTorch supplies device memory and streams only.
+
+The library is loaded on first use.  If it has not been built, every call
+raises ``RuntimeError``: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "pagestats_update", "page_score", "page_topk", "sparse_paged_decode",
+    "lse_merge", "h2o_accumulate", "h2o_scratch_floats", "library_path",
+    "load_library", "SparseKVError", "EXPORTED_SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libsparsekv.so")
+_lib = None
+
+EXPORTED_SYMBOLS = (
+    "pagestats_update", "page_score", "page_topk", "sparse_paged_decode",
+    "lse_merge", "h2o_accumulate", "h2o_scratch_floats", "sparsekv_last_error",
+)
+
+
+class SparseKVError(RuntimeError):
+    """A non-zero return code from the library."""
+
+    def __init__(self, fn, code, msg):
+        super().__init__(f"{fn} returned {code}: {msg}")
+        self.code = code
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libsparsekv.so (once).  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; "
+            "g.build()'` (or python sparse_kv_cache_amd/build.py) first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    V, I, L, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    lib.sparsekv_last_error.restype = ctypes.c_char_p
+    lib.sparsekv_last_error.argtypes = []
+    lib.pagestats_update.argtypes = [V, L, I, I, I, V, V, V, V, L, V, I, V, V, V, V]
+    lib.page_score.argtypes = [V, I, I, I, I, V, V, V, V, L, V, I, F, F, V, L, V]
+    lib.page_topk.argtypes = [V, L, I, I, V, I, I, F, I, I, V, V, I, V]
+    lib.sparse_paged_decode.argtypes = [V, I, I, I, I, V, L, I, V, L, V, V, V, I, I,
+                                        F, I, V, V, V]
+    lib.lse_merge.argtypes = [V, V, I, I, I, V, V, V]
+    lib.h2o_accumulate.argtypes = [V, I, I, I, I, V, L, I, V, L, V, I, I, F, F, V, V,
+                                   L, V, L, V]
+    lib.h2o_scratch_floats.argtypes = [I, I, L]
+    lib.h2o_scratch_floats.restype = ctypes.c_int64
+    for name in EXPORTED_SYMBOLS[:6]:
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+# ----------------------------------------------------------------- helpers
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(name, t, dtype, ndim=None, device=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _rc(name, code):
+    if code != 0:
+        msg = load_library().sparsekv_last_error().decode(errors="replace")
+        raise SparseKVError(name, code, msg)
+
+
+def _row_len(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    return t.shape[1]
+
+
+# ------------------------------------------------------------ entry points
+
+def pagestats_update(kv_cache, k_min, k_max, k_mean, block_table, seq_lens,
+                     k_new=None, v_new=None, hh_score=None, stream=None):
+    """Rebuild (k_new is None) or append-and-refresh the page statistics."""
+    lib = load_library()
+    _check("kv_cache", kv_cache, torch.bfloat16, 5)
+    dev = kv_cache.device
+    _, NB, P, H_kv, D = kv_cache.shape
+    for n, t, dt in (("k_min", k_min, torch.bfloat16), ("k_max", k_max, torch.bfloat16),
+                     ("k_mean", k_mean, torch.float32)):
+        _check(n, t, dt, 3, dev)
+        if t is not None and tuple(t.shape) != (NB, H_kv, D):
+            raise ValueError(f"{n} must be [num_blocks, H_kv, D]")
+    _check("block_table", block_table, torch.int32, 2, dev)
+    _check("seq_lens", seq_lens, torch.int32, 1, dev)
+    _check("k_new", k_new, torch.bfloat16, 3, dev)
+    _check("v_new", v_new, torch.bfloat16, 3, dev)
+    _check("hh_score", hh_score, torch.bfloat16, 2, dev)
+    B = seq_lens.shape[0]
+    if block_table.shape[0] != B:
+        raise ValueError("block_table rows must equal len(seq_lens)")
+    for n, t in (("k_new", k_new), ("v_new", v_new)):
+        if t is not None and tuple(t.shape) != (B, H_kv, D):
+            raise ValueError(f"{n} must be [B, H_kv, D]")
+    if hh_score is not None and tuple(hh_score.shape) != (NB * P, H_kv):
+        raise ValueError("hh_score must be [num_blocks * page_size, H_kv]")
+    _rc("pagestats_update", lib.pagestats_update(
+        _ptr(kv_cache), NB, P, H_kv, D, _ptr(k_min), _ptr(k_max), _ptr(k_mean),
+        _ptr(block_table), block_table.shape[1], _ptr(seq_lens), B, _ptr(k_new),
+        _ptr(v_new), _ptr(hh_score), _stream(stream)))
+
+
+def page_score(q, k_min, k_max, k_mean, block_table, seq_lens, page_size,
+               w_avg, w_peak, scores, stream=None):
+    """scores[b, i, p] for p < N_b from the page statistics."""
+    lib = load_library()
+    _check("q", q, torch.float32, 3)
+    dev = q.device
+    B, H_q, D = q.shape
+    _check("k_min", k_min, torch.bfloat16, 3, dev)
+    _check("k_max", k_max, torch.bfloat16, 3, dev)
+    _check("k_mean", k_mean, torch.float32, 3, dev)
+    _check("block_table", block_table, torch.int32, 2, dev)
+    _check("seq_lens", seq_lens, torch.int32, 1, dev)
+    _check("scores", scores, torch.float32, 3, dev)
+    H_kv = k_min.shape[1]
+    if tuple(scores.shape[:2]) != (B, H_q):
+        raise ValueError("scores must be [B, H_q, score_ld]")
+    _rc("page_score", lib.page_score(
+        _ptr(q), B, H_q, H_kv, D, _ptr(k_min), _ptr(k_max), _ptr(k_mean),
+        _ptr(block_table), block_table.shape[1], _ptr(seq_lens), int(page_size),
+        float(w_avg), float(w_peak), _ptr(scores), scores.shape[2], _stream(stream)))
+
+
+def page_topk(scores, seq_lens, page_size, topk_pages, sel_idx, sel_cnt,
+              topk_frac=0.0, reserved_bos=0, reserved_eos=1, stream=None):
+    """Top-k rows of scores [B, H_sel, score_ld] into sel_idx [B, H_sel, k_cap]."""
+    lib = load_library()
+    _check("scores", scores, torch.float32, 3)
+    dev = scores.device
+    B, H_sel, ld = scores.shape
+    _check("seq_lens", seq_lens, torch.int32, 1, dev)
+    _check("sel_idx", sel_idx, torch.int32, 3, dev)
+    _check("sel_cnt", sel_cnt, torch.int32, 2, dev)
+    if tuple(sel_idx.shape[:2]) != (B, H_sel) or tuple(sel_cnt.shape) != (B, H_sel):
+        raise ValueError("sel_idx must be [B, H_sel, k_cap] and sel_cnt [B, H_sel]")
+    _rc("page_topk", lib.page_topk(
+        _ptr(scores), ld, B, H_sel, _ptr(seq_lens), int(page_size), int(topk_pages),
+        float(topk_frac), int(reserved_bos), int(reserved_eos), _ptr(sel_idx),
+        _ptr(sel_cnt), sel_idx.shape[2], _stream(stream)))
+
+
+def sparse_paged_decode(q, kv_cache, block_table, seq_lens, sel_idx, sel_cnt,
+                        scale, o_part, lse_part, stream=None):
+    """Split-K partials over the selected pages.  H_sel = sel_idx.shape[1];
+    num_splits = o_part.shape[2]."""
+    lib = load_library()
+    _check("q", q, torch.float32, 3)
+    dev = q.device
+    B, H_q, D = q.shape
+    _check("kv_cache", kv_cache, torch.bfloat16, 5, dev)
+    _, NB, P, H_kv, D2 = kv_cache.shape
+    if D2 != D:
+        raise ValueError("q and kv_cache head dims differ")
+    _check("block_table", block_table, torch.int32, 2, dev)
+    _check("seq_lens", seq_lens, torch.int32, 1, dev)
+    _check("sel_idx", sel_idx, torch.int32, 3, dev)
+    _check("sel_cnt", sel_cnt, torch.int32, 2, dev)
+    _check("o_part", o_part, torch.float32, 4, dev)
+    _check("lse_part", lse_part, torch.float32, 3, dev)
+    ns = o_part.shape[2]
+    H_sel = sel_idx.shape[1]
+    if tuple(o_part.shape) != (B, H_q, ns, D) or tuple(lse_part.shape) != (B, H_q, ns):
+        raise ValueError("o_part must be [B, H_q, splits, D] and lse_part [B, H_q, splits]")
+    if sel_idx.shape[0] != B or tuple(sel_cnt.shape) != (B, H_sel):
+        raise ValueError("sel_idx must be [B, H_sel, k_cap] and sel_cnt [B, H_sel]")
+    _rc("sparse_paged_decode", lib.sparse_paged_decode(
+        _ptr(q), B, H_q, H_kv, D, _ptr(kv_cache), NB, P, _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), _ptr(sel_idx), _ptr(sel_cnt),
+        sel_idx.shape[2], H_sel, float(scale), ns, _ptr(o_part), _ptr(lse_part),
+        _stream(stream)))
+
+
+def lse_merge(o_part, lse_part, out, lse_out=None, stream=None):
+    """Merge [..., splits, D] partials into out [..., D] (and lse_out [...])."""
+    lib = load_library()
+    _check("o_part", o_part, torch.float32)
+    dev = o_part.device
+    _check("lse_part", lse_part, torch.float32, None, dev)
+    _check("out", out, torch.float32, None, dev)
+    _check("lse_out", lse_out, torch.float32, None, dev)
+    D = o_part.shape[-1]
+    ns = o_part.shape[-2]
+    rows = o_part.numel() // (ns * D) if o_part.numel() else 0
+    if lse_part.numel() != rows * ns or out.numel() != rows * D:
+        raise ValueError("inconsistent partial / output sizes")
+    if lse_out is not None and lse_out.numel() != rows:
+        raise ValueError("lse_out must hold one value per row")
+    _rc("lse_merge", lib.lse_merge(_ptr(o_part), _ptr(lse_part), rows, ns, D,
+                                   _ptr(out), _ptr(lse_out), _stream(stream)))
+
+
+def h2o_scratch_floats(B, H_kv, max_tokens) -> int:
+    return int(load_library().h2o_scratch_floats(int(B), int(H_kv), int(max_tokens)))
+
+
+def h2o_accumulate(q, kv_cache, block_table, seq_lens, hh_score, scores, scratch,
+                   scale, decay=0.984375, reserved_bos=0, reserved_eos=1,
+                   stream=None):
+    """Token-level H2O step (page_size 1): updates hh_score in place and writes
+    the new values as scores [B, H_kv, score_ld]."""
+    lib = load_library()
+    _check("q", q, torch.float32, 3)
+    dev = q.device
+    B, H_q, D = q.shape
+    _check("kv_cache", kv_cache, torch.bfloat16, 5, dev)
+    _, NB, P, H_kv, _ = kv_cache.shape
+    _check("block_table", block_table, torch.int32, 2, dev)
+    _check("seq_lens", seq_lens, torch.int32, 1, dev)
+    _check("hh_score", hh_score, torch.bfloat16, 2, dev)
+    _check("scores", scores, torch.float32, 3, dev)
+    _check("scratch", scratch, torch.float32, 1, dev)
+    if tuple(hh_score.shape) != (NB * P, H_kv):
+        raise ValueError("hh_score must be [num_blocks, H_kv]")
+    if tuple(scores.shape[:2]) != (B, H_kv):
+        raise ValueError("scores must be [B, H_kv, score_ld]")
+    _rc("h2o_accumulate", lib.h2o_accumulate(
+        _ptr(q), B, H_q, H_kv, D, _ptr(kv_cache), NB, P, _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), int(reserved_bos), int(reserved_eos),
+        float(scale), float(decay), _ptr(hh_score), _ptr(scores), scores.shape[2],
+        _ptr(scratch), scratch.numel(), _stream(stream)))

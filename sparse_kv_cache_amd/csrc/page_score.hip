@@ -1,0 +1,176 @@
+// page_score.hip -- score every page of every request for every query head
+// from the per-page statistics alone.
+//
+// Score: vortex_torch pull request "flow: add H2O sparse attention",
+// "Page-level variants": average relevance q . mean(k) plus the peak bound
+// sum_d max(q_d * max_d, q_d * min_d), combined as w_avg * avg + w_peak * peak.
+// EntmaxKV README "How it works": pages are scored from their statistics,
+// without touching the cached tokens.
+//
+// Arithmetic.  With mid = (max + min) / 2 and half = (max - min) / 2 >= 0,
+//   max(q * max, q * min) = q * mid + |q| * half
+// exactly, for either sign of q.  For bf16 envelopes mid and half are exact in
+// fp32, so each dim contributes
+//   q * (w_avg * mean + w_peak * mid) + |q| * (w_peak * half),
+// two FMAs per (dim, query head) after a per-dim setup shared by the whole
+// query group.
+//
+// Mapping.  One block per (tile of pages, kv head, request); a page-head's
+// statistics (256 + 256 + 512 bytes at D = 128) are read by D/8 lanes with
+// 16-byte loads, so a wave covers 64/(D/8) pages per load and every byte of
+// statistics is read once for the whole query group, whose rows sit in
+// registers.  Groups larger than 8 are split over grid.y slices.
+#include "skv_device.h"
+#include "skv_host.h"
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kIter = 4;
+
+template <int D, int GS>
+__global__ __launch_bounds__(256) void page_score_kernel(
+    const float* __restrict__ q, int H_q, int H_kv, int G,
+    const uint16_t* __restrict__ kmin, const uint16_t* __restrict__ kmax,
+    const float* __restrict__ kmean, const int32_t* __restrict__ bt,
+    int64_t bt_ld, const int32_t* __restrict__ seq_lens, int P, float w_avg,
+    float w_peak, float* __restrict__ scores, int64_t score_ld,
+    int64_t max_pages) {
+  constexpr int LPR = D / 8;          // lanes per page-head
+  constexpr int PPW = 64 / LPR;       // page-heads per wave load
+  constexpr int TILE = kIter * kWaves * PPW;
+  const int b = blockIdx.z;
+  const int nslices = (G + GS - 1) / GS;
+  const int h = blockIdx.y / nslices;
+  const int g0 = (blockIdx.y % nslices) * GS;
+  const int S = seq_lens[b];
+  int64_t N = (static_cast<int64_t>(S) + P - 1) / P;
+  if (N > max_pages) N = max_pages;
+  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * TILE;
+  if (p0 >= N) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int sub = lane / LPR;
+  const int c = lane % LPR;
+
+  float qv[GS][8], qa[GS][8];
+#pragma unroll
+  for (int g = 0; g < GS; ++g) {
+    const bool ok = g0 + g < G;
+    const float* qr = q + (static_cast<int64_t>(b) * H_q + h * G + g0 + g) * D + c * 8;
+    float4 a = ok ? *reinterpret_cast<const float4*>(qr) : make_float4(0, 0, 0, 0);
+    float4 bb = ok ? *reinterpret_cast<const float4*>(qr + 4) : make_float4(0, 0, 0, 0);
+    qv[g][0] = a.x; qv[g][1] = a.y; qv[g][2] = a.z; qv[g][3] = a.w;
+    qv[g][4] = bb.x; qv[g][5] = bb.y; qv[g][6] = bb.z; qv[g][7] = bb.w;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qa[g][i] = fabsf(qv[g][i]);
+  }
+
+  const int32_t* btr = bt + static_cast<int64_t>(b) * bt_ld;
+  uint4 mn[kIter], mx[kIter];
+  float4 me0[kIter], me1[kIter];
+  int64_t pg[kIter];
+#pragma unroll
+  for (int it = 0; it < kIter; ++it) {
+    pg[it] = p0 + (it * kWaves + wave) * PPW + sub;
+    if (pg[it] < N) {
+      const int64_t blk = btr[pg[it]];
+      const int64_t off = (blk * H_kv + h) * D + c * 8;
+      mn[it] = *reinterpret_cast<const uint4*>(kmin + off);
+      mx[it] = *reinterpret_cast<const uint4*>(kmax + off);
+      me0[it] = *reinterpret_cast<const float4*>(kmean + off);
+      me1[it] = *reinterpret_cast<const float4*>(kmean + off + 4);
+    } else {
+      mn[it] = mx[it] = make_uint4(0, 0, 0, 0);
+      me0[it] = me1[it] = make_float4(0, 0, 0, 0);
+    }
+  }
+
+#pragma unroll
+  for (int it = 0; it < kIter; ++it) {
+    float lo[8], hi[8];
+    skv::unpack8(mn[it], lo);
+    skv::unpack8(mx[it], hi);
+    const float me[8] = {me0[it].x, me0[it].y, me0[it].z, me0[it].w,
+                         me1[it].x, me1[it].y, me1[it].z, me1[it].w};
+    float mp[8], hp[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float mid = (hi[i] + lo[i]) * 0.5f;
+      const float half = (hi[i] - lo[i]) * 0.5f;
+      mp[i] = fmaf(w_avg, me[i], w_peak * mid);
+      hp[i] = w_peak * half;
+    }
+    float mine = 0.0f;
+#pragma unroll
+    for (int g = 0; g < GS; ++g) {
+      float s = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s = fmaf(qv[g][i], mp[i], fmaf(qa[g][i], hp[i], s));
+      s = skv::group_sum<LPR>(s);
+      if (c == g) mine = s;
+    }
+    if (pg[it] < N && c < GS && g0 + c < G)
+      scores[(static_cast<int64_t>(b) * H_q + h * G + g0 + c) * score_ld + pg[it]] = mine;
+  }
+}
+
+template <int D, int GS>
+void launch_score(dim3 grid, hipStream_t stream, const float* q, int H_q,
+                  int H_kv, int G, const uint16_t* kmin, const uint16_t* kmax,
+                  const float* kmean, const int32_t* bt, int64_t bt_ld,
+                  const int32_t* seq_lens, int P, float w_avg, float w_peak,
+                  float* scores, int64_t score_ld, int64_t max_pages) {
+  hipLaunchKernelGGL((page_score_kernel<D, GS>), grid, dim3(256), 0, stream, q,
+                     H_q, H_kv, G, kmin, kmax, kmean, bt, bt_ld, seq_lens, P,
+                     w_avg, w_peak, scores, score_ld, max_pages);
+}
+
+}  // namespace
+
+extern "C" int page_score(const float* q, int B, int H_q, int H_kv, int D,
+                          const uint16_t* k_min, const uint16_t* k_max,
+                          const float* k_mean, const int32_t* block_table,
+                          int64_t bt_ld, const int32_t* seq_lens, int page_size,
+                          float w_avg, float w_peak, float* scores,
+                          int64_t score_ld, hipStream_t stream) {
+  SKV_REQUIRE(B >= 0 && H_kv > 0 && H_q > 0 && H_q % H_kv == 0,
+              "page_score: need H_q a positive multiple of H_kv (H_q=%d, H_kv=%d)", H_q, H_kv);
+  const int G = H_q / H_kv;
+  SKV_REQUIRE(G <= 16, "page_score: group size %d > 16", G);
+  SKV_REQUIRE(D == 64 || D == 128, "page_score: D must be 64 or 128 (got %d)", D);
+  SKV_REQUIRE(skv_supported_page_size(page_size),
+              "page_score: page_size must be 1, 2, 4, 8 or 16 (got %d)", page_size);
+  SKV_REQUIRE(bt_ld > 0 && score_ld >= bt_ld,
+              "page_score: need bt_ld > 0 and score_ld >= bt_ld");
+  SKV_REQUIRE(B <= 65535 && H_kv * 2 <= 65535, "page_score: grid too large");
+  SKV_REQUIRE_PTR(q);
+  SKV_REQUIRE_PTR(k_min);
+  SKV_REQUIRE_PTR(k_max);
+  SKV_REQUIRE_PTR(k_mean);
+  SKV_REQUIRE_PTR(block_table);
+  SKV_REQUIRE_PTR(seq_lens);
+  SKV_REQUIRE_PTR(scores);
+  if (B == 0) { skv::clear_error(); return SKV_OK; }
+  const int64_t max_pages = bt_ld;
+  const int GS = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
+  const int slices = (G + GS - 1) / GS;
+  const int ppw = 64 / (D / 8);
+  const int tile = kIter * kWaves * ppw;
+  dim3 grid(static_cast<unsigned>((max_pages + tile - 1) / tile),
+            static_cast<unsigned>(H_kv * slices), static_cast<unsigned>(B));
+#define SKV_SCORE(DD, GG)                                                        \
+  launch_score<DD, GG>(grid, stream, q, H_q, H_kv, G, k_min, k_max, k_mean,       \
+                       block_table, bt_ld, seq_lens, page_size, w_avg, w_peak,   \
+                       scores, score_ld, max_pages)
+  if (D == 128) {
+    if (GS == 1) SKV_SCORE(128, 1); else if (GS == 2) SKV_SCORE(128, 2);
+    else if (GS == 4) SKV_SCORE(128, 4); else SKV_SCORE(128, 8);
+  } else {
+    if (GS == 1) SKV_SCORE(64, 1); else if (GS == 2) SKV_SCORE(64, 2);
+    else if (GS == 4) SKV_SCORE(64, 4); else SKV_SCORE(64, 8);
+  }
+#undef SKV_SCORE
+  SKV_CHECK_LAUNCH();
+}

@@ -1,0 +1,214 @@
+// page_topk.hip -- per-row top-k selection with the reserved pages forced in,
+// ties to the lower index, output ascending.
+//
+// Selection: EntmaxKV README "How it works" (keep topk_pages per query head;
+// the budget counts pages and includes the always-attended tail page);
+// vortex_torch pull request "flow: add H2O sparse attention", hardware
+// follow-up (the reserved leading bos and trailing eos entries are kept and
+// only the window between them is ranked).
+//
+// Method.  One block per row.  Scores become order-preserving uint32 keys
+// (-0.0 folded onto +0.0) held in registers, ITEMS contiguous entries per
+// thread.  A most-significant-digit radix select (four 8-bit passes, LDS
+// histogram with shared atomics, digit search by one wave) finds the exact
+// key T of the m-th best candidate and how many entries equal to T are still
+// needed.  Entries above T are taken; among those equal to T the lowest
+// indices are taken, ranked by a block-wide prefix count in index order.  A
+// second prefix count over the final flags writes the indices in ascending
+// order with no sort.
+#include <limits.h>
+
+#include "skv_device.h"
+#include "skv_host.h"
+
+namespace {
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;                        // -0.0 == +0.0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int BLOCK, int ITEMS>
+__global__ __launch_bounds__(BLOCK) void page_topk_kernel(
+    const float* __restrict__ scores, int64_t score_ld, int H_sel,
+    const int32_t* __restrict__ seq_lens, int P, int topk_pages,
+    double topk_frac, int bos, int eos, int32_t* __restrict__ sel_idx,
+    int32_t* __restrict__ sel_cnt, int k_cap) {
+  __shared__ int hist[256];
+  __shared__ int scan_smem[BLOCK / 64 + 1];
+  __shared__ int s_digit, s_remaining;
+
+  const int64_t row = blockIdx.x;
+  const int b = static_cast<int>(row / H_sel);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+
+  int64_t N64 = (static_cast<int64_t>(seq_lens[b]) + P - 1) / P;
+  if (N64 > score_ld) N64 = score_ld;
+  if (N64 < 0) N64 = 0;
+  const int N = static_cast<int>(N64);
+  int k = topk_pages;
+  const double f = floor(topk_frac * static_cast<double>(N));
+  if (f > static_cast<double>(k)) k = static_cast<int>(f);
+  if (k > N) k = N;
+  const int lo = bos < N ? bos : N;
+  int hi = N - eos > 0 ? N - eos : 0;
+  if (hi < lo) hi = lo;
+  const int nres = N - (hi - lo);
+  const int want = k - nres > 0 ? k - nres : 0;
+  const int ncand = hi - lo;
+
+  const float* srow = scores + row * score_ld;
+  const int base = tid * ITEMS;
+  uint32_t key[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int p = base + i;
+    key[i] = (p >= lo && p < hi) ? order_key(srow[p]) : 0u;
+  }
+
+  uint32_t T;
+  int r_eq;
+  if (want == 0) {
+    T = 0xffffffffu; r_eq = 0;             // reserved entries only
+  } else if (want >= ncand) {
+    T = 0u; r_eq = INT_MAX;                // every candidate
+  } else {
+    uint32_t prefix = 0u, pmask = 0u;
+    int remaining = want;
+#pragma unroll 1
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      for (int j = tid; j < 256; j += BLOCK) hist[j] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < ITEMS; ++i) {
+        const int p = base + i;
+        if (p >= lo && p < hi && (key[i] & pmask) == prefix)
+          atomicAdd(&hist[(key[i] >> shift) & 255u], 1);
+      }
+      __syncthreads();
+      if (tid < 64) {
+        int cs[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cs[j] = hist[4 * lane + j];
+        const int sum = cs[0] + cs[1] + cs[2] + cs[3];
+        int suf = sum;                      // sum over lanes >= lane
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_down(suf, o);
+          if (lane + o < 64) suf += y;
+        }
+        int above = suf - sum;              // entries in higher digits
+#pragma unroll
+        for (int j = 3; j >= 0; --j) {
+          if (above < remaining && above + cs[j] >= remaining) {
+            s_digit = 4 * lane + j;
+            s_remaining = remaining - above;
+          }
+          above += cs[j];
+        }
+      }
+      __syncthreads();
+      const uint32_t d = static_cast<uint32_t>(s_digit);
+      remaining = s_remaining;
+      prefix |= d << shift;
+      pmask |= 0xffu << shift;
+    }
+    T = prefix;
+    r_eq = remaining;
+  }
+
+  int eq = 0;
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int p = base + i;
+    eq += (p >= lo && p < hi && key[i] == T) ? 1 : 0;
+  }
+  int total_eq;
+  int er = skv::block_exclusive_scan(eq, &total_eq, scan_smem);
+
+  uint32_t flags = 0u;
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int p = base + i;
+    bool take;
+    if (p >= N) take = false;
+    else if (p < lo || p >= hi) take = true;
+    else if (key[i] > T) take = true;
+    else if (key[i] == T) { take = er < r_eq; ++er; }
+    else take = false;
+    if (take) { flags |= 1u << i; ++cnt; }
+  }
+  int total;
+  int pos = skv::block_exclusive_scan(cnt, &total, scan_smem);
+  int32_t* out = sel_idx + row * k_cap;
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    if (flags & (1u << i)) {
+      if (pos < k_cap) out[pos] = base + i;
+      ++pos;
+    }
+  }
+  for (int j = total + tid; j < k_cap; j += BLOCK) out[j] = -1;
+  if (tid == 0) sel_cnt[row] = total < k_cap ? total : k_cap;
+}
+
+template <int BLOCK, int ITEMS>
+void launch_topk(int64_t rows, hipStream_t stream, const float* scores,
+                 int64_t score_ld, int H_sel, const int32_t* seq_lens, int P,
+                 int topk_pages, double topk_frac, int bos, int eos,
+                 int32_t* sel_idx, int32_t* sel_cnt, int k_cap) {
+  hipLaunchKernelGGL((page_topk_kernel<BLOCK, ITEMS>), dim3(static_cast<unsigned>(rows)),
+                     dim3(BLOCK), 0, stream, scores, score_ld, H_sel, seq_lens, P,
+                     topk_pages, topk_frac, bos, eos, sel_idx, sel_cnt, k_cap);
+}
+
+}  // namespace
+
+extern "C" int page_topk(const float* scores, int64_t score_ld, int B,
+                         int H_sel, const int32_t* seq_lens, int page_size,
+                         int topk_pages, float topk_frac, int reserved_bos,
+                         int reserved_eos, int32_t* sel_idx, int32_t* sel_cnt,
+                         int k_cap, hipStream_t stream) {
+  SKV_REQUIRE(B >= 0 && H_sel > 0, "page_topk: need B >= 0 and H_sel > 0");
+  SKV_REQUIRE(score_ld > 0 && score_ld <= 32768,
+              "page_topk: score_ld must be in [1, 32768] (got %lld)", (long long)score_ld);
+  SKV_REQUIRE(skv_supported_page_size(page_size),
+              "page_topk: page_size must be 1, 2, 4, 8 or 16 (got %d)", page_size);
+  SKV_REQUIRE(topk_pages >= 1, "page_topk: topk_pages must be >= 1 (got %d)", topk_pages);
+  SKV_REQUIRE(topk_frac >= 0.0f && topk_frac <= 1.0f,
+              "page_topk: topk_frac must be in [0, 1]");
+  SKV_REQUIRE(reserved_bos >= 0 && reserved_eos >= 0,
+              "page_topk: reserved_bos / reserved_eos must be >= 0");
+  const double frac = static_cast<double>(topk_frac);
+  int64_t need = topk_pages;
+  const int64_t fk = static_cast<int64_t>(floor(frac * static_cast<double>(score_ld)));
+  if (fk > need) need = fk;
+  if (static_cast<int64_t>(reserved_bos) + reserved_eos > need)
+    need = static_cast<int64_t>(reserved_bos) + reserved_eos;
+  if (need > score_ld) need = score_ld;
+  SKV_REQUIRE(k_cap >= need, "page_topk: k_cap %d < largest possible selection %lld",
+              k_cap, (long long)need);
+  SKV_REQUIRE_PTR(scores);
+  SKV_REQUIRE_PTR(seq_lens);
+  SKV_REQUIRE_PTR(sel_idx);
+  SKV_REQUIRE_PTR(sel_cnt);
+  const int64_t rows = static_cast<int64_t>(B) * H_sel;
+  SKV_REQUIRE(rows <= 0x7fffffff, "page_topk: too many rows");
+  if (rows == 0) { skv::clear_error(); return SKV_OK; }
+#define SKV_TOPK(BL, IT)                                                          \
+  launch_topk<BL, IT>(rows, stream, scores, score_ld, H_sel, seq_lens, page_size, \
+                      topk_pages, frac, reserved_bos, reserved_eos, sel_idx,      \
+                      sel_cnt, k_cap)
+  if (score_ld <= 1024) SKV_TOPK(256, 4);
+  else if (score_ld <= 2048) SKV_TOPK(256, 8);
+  else if (score_ld <= 4096) SKV_TOPK(256, 16);
+  else if (score_ld <= 8192) SKV_TOPK(512, 16);
+  else if (score_ld <= 16384) SKV_TOPK(1024, 16);
+  else SKV_TOPK(1024, 32);
+#undef SKV_TOPK
+  SKV_CHECK_LAUNCH();
+}

@@ -1,0 +1,124 @@
+// skv_device.h -- device helpers shared by the HIP kernels of libsparsekv
+// (gfx950, wave64).  Internal to the library; not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace skv {
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ bf16
+// A bf16 value is the upper half of an IEEE binary32 pattern.
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) {
+  return __uint_as_float(w << 16);
+}
+__device__ __forceinline__ float bf16_hi(uint32_t w) {
+  return __uint_as_float(w & 0xffff0000u);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Unpack 8 bf16 (one 16-byte vector) into floats.
+__device__ __forceinline__ void unpack8(const uint4 v, float (&x)[8]) {
+  x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+  x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+  x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
+  x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+}
+
+// ------------------------------------------------- cross-lane reductions
+// DPP moves inside a row of 16 lanes.  quad_perm [1,0,3,2] (0xB1) and
+// [2,3,0,1] (0x4E) exchange within quads, row_half_mirror (0x141) reverses
+// each 8-lane half, row_mirror (0x140) reverses the 16-lane row.  Each step
+// adds two symmetric operands, so every lane of a group ends with the same
+// bits.
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(
+      0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of LPR lanes (LPR = 8 or 16).
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(LPR == 8 || LPR == 16, "group of 8 or 16 lanes");
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  if constexpr (LPR == 16) x += dpp<0x140>(x);
+  return x;
+}
+
+template <int LPR>
+__device__ __forceinline__ float group_max(float x) {
+  static_assert(LPR == 8 || LPR == 16, "group of 8 or 16 lanes");
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  if constexpr (LPR == 16) x = fmaxf(x, dpp<0x140>(x));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Exclusive prefix sum over the block.  smem needs nwaves + 1 ints.  Every
+// thread of the block must call it.
+__device__ __forceinline__ int block_exclusive_scan(int x, int* total,
+                                                    int* smem) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int nwaves = (blockDim.x + kWave - 1) / kWave;
+  int inc = wave_inclusive_scan(x);
+  if (lane == kWave - 1) smem[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < nwaves ? smem[lane] : 0;
+    int wi = wave_inclusive_scan(w);
+    if (lane < nwaves) smem[lane] = wi - w;
+    if (lane == nwaves - 1) smem[nwaves] = wi;
+  }
+  __syncthreads();
+  int r = inc - x + smem[wave];
+  *total = smem[nwaves];
+  __syncthreads();
+  return r;
+}
+
+// log2(e) and ln(2) for base-2 exponentials.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+}  // namespace skv

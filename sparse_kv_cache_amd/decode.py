@@ -1,0 +1,132 @@
+"""Decode-step composites over the C ABI.
+
+``SparseDecoder`` owns the per-step device buffers (page statistics, scores,
+selections, split partials, outputs) for one cache shape and calls the
+library's entry points in the order of a decode step:
+
+  page level   [pagestats_update (append)] -> page_score -> page_topk
+               -> sparse_paged_decode -> lse_merge
+  token level  pagestats_update (append + hh reset) -> h2o_accumulate
+               -> page_topk (per kv head) -> sparse_paged_decode -> lse_merge
+
+This mirrors the decode call of the EntmaxKV README ("Quick start": score,
+select, attend and append in one call) cut at kernel granularity.  Nothing
+here computes: it allocates once and marshals arguments.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import (h2o_accumulate, h2o_scratch_floats, lse_merge, page_score,
+               page_topk, pagestats_update, sparse_paged_decode)
+
+
+def selection_capacity(score_ld, topk_pages, topk_frac=0.0, bos=0, eos=1):
+    """Largest selection a row of at most score_ld entries can produce."""
+    need = max(int(topk_pages), int(math.floor(float(topk_frac) * score_ld)),
+               int(bos) + int(eos))
+    return min(need, int(score_ld))
+
+
+class SparseDecoder:
+    """Buffers and call order of one decode step.
+
+    kv_cache: bf16 [2, num_blocks, P, H_kv, D]; block_table int32 [B, bt_ld].
+    token_level=True selects the H2O flow (page_size must be 1)."""
+
+    def __init__(self, B, H_q, H_kv, D, num_blocks, page_size, bt_ld, *,
+                 topk_pages, topk_frac=0.0, bos=0, eos=1, w_avg=1.0, w_peak=1.0,
+                 scale=None, num_splits=1, decay=0.984375, token_level=False,
+                 device="cuda"):
+        self.B, self.H_q, self.H_kv, self.D = B, H_q, H_kv, D
+        self.num_blocks, self.P, self.bt_ld = num_blocks, page_size, bt_ld
+        self.topk_pages, self.topk_frac = topk_pages, topk_frac
+        self.bos, self.eos = bos, eos
+        self.w_avg, self.w_peak = w_avg, w_peak
+        self.scale = D ** -0.5 if scale is None else scale
+        self.num_splits, self.decay = num_splits, decay
+        self.token_level = token_level
+        dev = torch.device(device)
+        self.H_sel = H_kv if token_level else H_q
+        self.k_cap = selection_capacity(bt_ld, topk_pages, topk_frac, bos, eos)
+        f32, i32, bf = torch.float32, torch.int32, torch.bfloat16
+        if token_level:
+            if page_size != 1:
+                raise ValueError("the token-level flow needs page_size 1")
+            self.k_min = self.k_max = self.k_mean = None
+            self.hh = torch.zeros((num_blocks, H_kv), dtype=bf, device=dev)
+            n = h2o_scratch_floats(B, H_kv, bt_ld)
+            self.scratch = torch.empty(n, dtype=f32, device=dev)
+        else:
+            self.k_min = torch.empty((num_blocks, H_kv, D), dtype=bf, device=dev)
+            self.k_max = torch.empty((num_blocks, H_kv, D), dtype=bf, device=dev)
+            self.k_mean = torch.empty((num_blocks, H_kv, D), dtype=f32, device=dev)
+            self.hh = None
+            self.scratch = None
+        self.scores = torch.empty((B, self.H_sel, bt_ld), dtype=f32, device=dev)
+        self.sel_idx = torch.empty((B, self.H_sel, self.k_cap), dtype=i32, device=dev)
+        self.sel_cnt = torch.empty((B, self.H_sel), dtype=i32, device=dev)
+        self.o_part = torch.empty((B, H_q, num_splits, D), dtype=f32, device=dev)
+        self.lse_part = torch.empty((B, H_q, num_splits), dtype=f32, device=dev)
+        self.out = torch.empty((B, H_q, D), dtype=f32, device=dev)
+        self.lse = torch.empty((B, H_q), dtype=f32, device=dev)
+
+    @classmethod
+    def for_workload(cls, wl, device="cuda", num_splits=None):
+        return cls(wl.B, wl.H_q, wl.H_kv, wl.D, wl.num_blocks, wl.P, wl.bt_ld,
+                   topk_pages=wl.topk_pages, topk_frac=wl.topk_frac, bos=wl.bos,
+                   eos=wl.eos, w_avg=wl.w_avg, w_peak=wl.w_peak,
+                   scale=wl.softmax_scale,
+                   num_splits=wl.num_splits if num_splits is None else num_splits,
+                   decay=wl.decay, token_level=(wl.name == "h2o_token"),
+                   device=device)
+
+    # ------------------------------------------------------------ stages
+    def rebuild_stats(self, kv_cache, block_table, seq_lens, stream=None):
+        pagestats_update(kv_cache, self.k_min, self.k_max, self.k_mean,
+                         block_table, seq_lens, stream=stream)
+
+    def append(self, kv_cache, block_table, seq_lens, k_new, v_new, stream=None):
+        pagestats_update(kv_cache, self.k_min, self.k_max, self.k_mean,
+                         block_table, seq_lens, k_new, v_new, self.hh,
+                         stream=stream)
+
+    def score(self, q, block_table, seq_lens, stream=None):
+        if self.token_level:
+            raise RuntimeError("token-level scores come from h2o_accumulate")
+        page_score(q, self.k_min, self.k_max, self.k_mean, block_table, seq_lens,
+                   self.P, self.w_avg, self.w_peak, self.scores, stream=stream)
+
+    def accumulate(self, q, kv_cache, block_table, seq_lens, stream=None):
+        h2o_accumulate(q, kv_cache, block_table, seq_lens, self.hh, self.scores,
+                       self.scratch, self.scale, self.decay, self.bos, self.eos,
+                       stream=stream)
+
+    def select(self, seq_lens, stream=None):
+        page_topk(self.scores, seq_lens, self.P, self.topk_pages, self.sel_idx,
+                  self.sel_cnt, self.topk_frac, self.bos, self.eos, stream=stream)
+
+    def attend(self, q, kv_cache, block_table, seq_lens, stream=None):
+        sparse_paged_decode(q, kv_cache, block_table, seq_lens, self.sel_idx,
+                            self.sel_cnt, self.scale, self.o_part, self.lse_part,
+                            stream=stream)
+
+    def merge(self, stream=None):
+        lse_merge(self.o_part, self.lse_part, self.out, self.lse, stream=stream)
+
+    # -------------------------------------------------------------- step
+    def step(self, q, kv_cache, block_table, seq_lens, k_new=None, v_new=None,
+             stream=None):
+        """One decode step; returns (out, lse) views of the decoder's buffers."""
+        if k_new is not None:
+            self.append(kv_cache, block_table, seq_lens, k_new, v_new, stream)
+        if self.token_level:
+            self.accumulate(q, kv_cache, block_table, seq_lens, stream)
+        else:
+            self.score(q, block_table, seq_lens, stream)
+        self.select(seq_lens, stream)
+        self.attend(q, kv_cache, block_table, seq_lens, stream)
+        self.merge(stream)
+        return self.out, self.lse

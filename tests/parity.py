@@ -1,0 +1,241 @@
+"""Helpers of the GPU-vs-oracle parity tests.
+
+Parity rules (stated once here, used by every GPU test):
+  * k_min / k_max: bit-exact.  k_mean: within the recursive-summation bound
+    n * 2^-24 * sum_t |k_t| / n of an fp32 sum of n bf16 values, plus 1e-7.
+  * page scores, kernel in isolation (oracle fed the GPU's own statistics):
+    within 2 * D * 2^-24 * sum_d |term_d| (fp32 dot-product bound).
+  * selection, kernel in isolation (oracle fed the GPU's fp32 scores):
+    identical index lists.  End to end (oracle from the cache in float64):
+    identical, except rows whose k-th and (k+1)-th oracle scores differ by
+    less than 1e-5 relative (page level) or by at most one bf16 ulp of the
+    k-th value (token level); such rows must still hold every candidate
+    ranked clearly above the boundary and none ranked clearly below it.
+  * attention (oracle over the GPU's own selection): out within 2e-3
+    absolute, lse within 1e-4 absolute; split partials likewise.
+  * hh (token level, oracle fed the GPU's pre-step hh): at most one bf16 ulp
+    apart (bit patterns of non-negative values differ by <= 1).
+Outputs are poisoned (NaN / -7) before each GPU call so unwritten elements
+fail.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from sparse_kv_cache_amd import workloads as W
+
+OUT_ATOL = 2e-3
+LSE_ATOL = 1e-4
+PAGE_GAP_REL = 1e-5
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a)) if isinstance(a, np.ndarray) else a
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda().contiguous()
+
+
+def poison(dec):
+    for t in (dec.scores, dec.o_part, dec.lse_part, dec.out, dec.lse):
+        t.fill_(float("nan"))
+    dec.sel_idx.fill_(-7)
+    dec.sel_cnt.fill_(-7)
+
+
+def bits(t):
+    return W.bf16_bits(t)
+
+
+# ------------------------------------------------------------- sub-batch
+
+def sub_batch(wl, cache_gpu, rows, seq_lens=None, extra=()):
+    """Host copy of the blocks used by requests ``rows`` with a remapped
+    block table.  ``extra`` are GPU tensors indexed by block on dim 0 (stats)
+    gathered the same way.  Returns (cache_bits, bt, seq_lens, blocks, extras)."""
+    sl = wl.seq_lens if seq_lens is None else np.asarray(seq_lens)
+    rows = list(rows)
+    N = (sl[rows].astype(np.int64) + wl.P - 1) // wl.P
+    blocks = np.unique(np.concatenate([wl.block_table[b, :n] for b, n in zip(rows, N)]))
+    idx = torch.from_numpy(blocks.astype(np.int64)).cuda()
+    cache = bits(cache_gpu.index_select(1, idx))
+    bt = np.zeros((len(rows), wl.bt_ld), dtype=np.int32)
+    for r, (b, n) in enumerate(zip(rows, N)):
+        bt[r, :n] = np.searchsorted(blocks, wl.block_table[b, :n])
+    ex = [t.index_select(0, idx).cpu() for t in extra]
+    return cache, bt, sl[rows].astype(np.int32), blocks, ex
+
+
+# ----------------------------------------------------------------- checks
+
+def check_stats(gpu_min, gpu_max, gpu_mean, cache_bits, bt, sl, P, blocks_used):
+    """gpu_* indexed like the oracle's output (physical blocks of cache_bits)."""
+    mn, mx, me = oracle.page_stats(cache_bits, bt, sl, P)
+    gmin = oracle.bf16_decode(gpu_min[blocks_used])
+    gmax = oracle.bf16_decode(gpu_max[blocks_used])
+    assert np.array_equal(gmin, mn[blocks_used]), "k_min differs"
+    assert np.array_equal(gmax, mx[blocks_used]), "k_max differs"
+    # bound: n * u * sum|k| / n = u * sum|k|; sum|k| <= n * max(|min|, |max|)
+    n = np.zeros(len(blocks_used))
+    for b in range(bt.shape[0]):
+        Nb = (int(sl[b]) + P - 1) // P
+        for p in range(Nb):
+            j = np.searchsorted(blocks_used, bt[b, p])
+            n[j] = min(P, int(sl[b]) - p * P)
+    amax = np.maximum(np.abs(mn[blocks_used]), np.abs(mx[blocks_used]))
+    tol = (2.0 ** -24) * n[:, None, None] * amax + 1e-7
+    err = np.abs(gpu_mean[blocks_used].astype(np.float64) - me[blocks_used])
+    assert np.all(err <= tol), f"k_mean error {err.max()} over bound"
+    return mn, mx, me
+
+
+def score_abs_terms(q, mn, mx, me, bt, sl, P, w_avg, w_peak):
+    M = np.maximum(np.abs(mn), np.abs(mx))
+    return oracle.page_score(np.abs(q), -M, M, np.abs(me), bt, sl, P,
+                             abs(w_avg), abs(w_peak))
+
+
+def check_scores(gpu_scores, q, stats_d, bt, sl, P, w_avg, w_peak):
+    """gpu_scores [B, H_q, ld] fp32 vs the oracle fed the same statistics."""
+    mn, mx, me = stats_d
+    ref = oracle.page_score(q, mn, mx, me, bt, sl, P, w_avg, w_peak,
+                            ld=gpu_scores.shape[2])
+    terms = score_abs_terms(q, mn, mx, me, bt, sl, P, w_avg, w_peak)
+    D = q.shape[2]
+    valid = ~np.isnan(ref)
+    g = gpu_scores.astype(np.float64)
+    assert not np.any(np.isnan(g[valid])), "unwritten score"
+    err = np.abs(g[valid] - ref[valid])
+    tol = 2 * D * 2.0 ** -24 * terms[valid] + 1e-6
+    assert np.all(err <= tol), f"score error {err.max()} over bound"
+    return ref
+
+
+def selection_rows(sel_idx, sel_cnt):
+    out = []
+    for r in range(sel_cnt.shape[0]):
+        c = int(sel_cnt[r])
+        out.append(sel_idx[r, :c].tolist())
+    return out
+
+
+def check_padding(sel_idx, sel_cnt):
+    for r in range(sel_cnt.shape[0]):
+        c = int(sel_cnt[r])
+        assert c >= 0
+        assert np.all(sel_idx[r, c:] == -1), "padding not -1"
+
+
+def check_selection_exact(gpu_idx, gpu_cnt, scores_rows, N_rows, topk, frac,
+                          bos, eos):
+    """GPU selection equals the oracle's on the same (GPU) scores."""
+    check_padding(gpu_idx, gpu_cnt)
+    for r, (s, n) in enumerate(zip(scores_rows, N_rows)):
+        want = oracle.select(s[:n].astype(np.float64), topk, frac, bos, eos).tolist()
+        got = gpu_idx[r, :int(gpu_cnt[r])].tolist()
+        assert got == want, f"row {r}: selection differs from oracle on GPU scores"
+
+
+def _window(N, bos, eos):
+    lo = min(bos, N)
+    hi = max(N - eos, 0)
+    return lo, max(hi, lo)
+
+
+def check_selection_vs_oracle(gpu_rows, oracle_scores_rows, N_rows, topk, frac,
+                              bos, eos, token_level=False):
+    """End-to-end rule with the near-tie exemption.  Returns #exempt rows."""
+    exempt = 0
+    for r, (got, s, n) in enumerate(zip(gpu_rows, oracle_scores_rows, N_rows)):
+        s = s[:n]
+        want = oracle.select(s, topk, frac, bos, eos).tolist()
+        if got == want:
+            continue
+        lo, hi = _window(n, bos, eos)
+        k = oracle.budget(n, topk, frac)
+        m = k - (n - (hi - lo))
+        cand = sorted(range(lo, hi), key=lambda p: (-s[p], p))
+        assert 0 < m < len(cand), f"row {r}: mismatch with no boundary"
+        a, b = s[cand[m - 1]], s[cand[m]]
+        if token_level:
+            bound_ok = abs(a - b) <= 2.0 ** (np.floor(np.log2(abs(a))) - 7)
+        else:
+            den = max(abs(a), abs(b))
+            bound_ok = den == 0 or abs(a - b) / den < PAGE_GAP_REL
+        assert bound_ok, f"row {r}: selection differs away from a near tie"
+        assert len(got) == len(want), f"row {r}: wrong count"
+        gs = set(got)
+        band = (2.0 ** (np.floor(np.log2(abs(a))) - 7) if token_level
+                else PAGE_GAP_REL * max(abs(a), abs(b)))
+        for p in range(n):
+            if p < lo or p >= hi:
+                assert p in gs, f"row {r}: reserved page {p} missing"
+            elif s[p] > a + band:
+                assert p in gs, f"row {r}: page {p} clearly above the boundary missing"
+            elif s[p] < b - band:
+                assert p not in gs, f"row {r}: page {p} clearly below the boundary taken"
+        exempt += 1
+    return exempt
+
+
+def check_attention(gpu_out, gpu_lse, q, cache_bits, bt, sl, rows_sel, G, scale):
+    """gpu_out [B, H_q, D], gpu_lse [B, H_q]; rows_sel[b][i] = pages."""
+    B, H_q, D = q.shape
+    worst = 0.0
+    for b in range(B):
+        for i in range(H_q):
+            o, lse = oracle.attend(q[b, i], cache_bits, i // G, bt[b], sl[b],
+                                   rows_sel[b][i], scale)
+            go = gpu_out[b, i].astype(np.float64)
+            assert not np.any(np.isnan(go)), f"NaN output at ({b},{i})"
+            e = np.abs(go - o).max()
+            worst = max(worst, e)
+            assert e <= OUT_ATOL, f"out ({b},{i}) err {e}"
+            if np.isinf(lse):
+                assert np.isinf(gpu_lse[b, i]) and gpu_lse[b, i] < 0
+            else:
+                assert abs(float(gpu_lse[b, i]) - lse) <= LSE_ATOL, \
+                    f"lse ({b},{i}) {gpu_lse[b, i]} vs {lse}"
+    return worst
+
+
+def check_partials(o_part, lse_part, q, cache_bits, bt, sl, rows_sel, G, scale):
+    """Split s of a row holds entries [s*c, (s+1)*c), c = ceil(cnt/splits)."""
+    B, H_q, ns, D = o_part.shape
+    for b in range(B):
+        for i in range(H_q):
+            pages = list(rows_sel[b][i])
+            c = -(-len(pages) // ns)
+            for s in range(ns):
+                chunk = pages[s * c:(s + 1) * c] if c else []
+                o, lse = oracle.attend(q[b, i], cache_bits, i // G, bt[b], sl[b],
+                                       chunk, scale)
+                if np.isinf(lse):
+                    assert np.isinf(lse_part[b, i, s]) and lse_part[b, i, s] < 0
+                    assert np.all(o_part[b, i, s] == 0)
+                    continue
+                e = np.abs(o_part[b, i, s].astype(np.float64) - o).max()
+                assert e <= OUT_ATOL, f"partial ({b},{i},{s}) err {e}"
+                assert abs(float(lse_part[b, i, s]) - lse) <= LSE_ATOL
+
+
+def per_head_rows(sel_rows, B, H_q, H_sel):
+    """Expand selection rows to [b][i] (shared rows serve the whole group)."""
+    G = H_q // H_sel
+    out = []
+    for b in range(B):
+        out.append([sel_rows[b * H_sel + i // G] for i in range(H_q)])
+    return out
+
+
+def bf16_bits_apart(a_bits, b_bits):
+    return np.abs(a_bits.astype(np.int64) - b_bits.astype(np.int64))

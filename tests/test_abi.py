@@ -1,0 +1,135 @@
+"""Host-side checks of the C ABI (no GPU work).
+
+* libsparsekv.so loads and exports every function ``include/sparsekv.h``
+  declares;
+* argument validation rejects bad scalars (-EINVAL) and NULL pointers
+  (-EFAULT) before anything is enqueued, with a message;
+* the scratch-size query of the token-level step;
+* the product package has no import path into the oracle.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparsekv.h")
+
+import sparse_kv_cache_amd as skv  # noqa: E402
+
+EINVAL, EFAULT = -22, -14
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z0-9_]+\s*\*?\s*([a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(skv.library_path()):
+        from sparse_kv_cache_amd import build
+        build.build()
+    return skv.load_library()
+
+
+def test_header_declares_the_six_operations():
+    names = _declared()
+    for n in ("pagestats_update", "page_score", "page_topk", "sparse_paged_decode",
+              "lse_merge", "h2o_accumulate", "h2o_scratch_floats",
+              "sparsekv_last_error"):
+        assert n in names
+    assert set(names) == set(skv.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", skv.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for n in _declared():
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def _msg(lib):
+    return lib.sparsekv_last_error().decode()
+
+
+def test_validation_rejects_bad_scalars(lib):
+    p = ctypes.c_void_p(16)          # never dereferenced: rejected first
+    s = ctypes.c_void_p(0)
+    # D must be 64 or 128
+    assert lib.pagestats_update(p, 8, 16, 2, 96, p, p, p, p, 4, p, 1, None, None,
+                                None, s) == EINVAL
+    assert "D must be" in _msg(lib)
+    # page_size 3 unsupported
+    assert lib.page_score(p, 1, 4, 2, 64, p, p, p, p, 4, p, 3, 1.0, 1.0, p, 4,
+                          s) == EINVAL
+    # H_q not a multiple of H_kv
+    assert lib.page_score(p, 1, 5, 2, 64, p, p, p, p, 4, p, 16, 1.0, 1.0, p, 4,
+                          s) == EINVAL
+    # score_ld < bt_ld
+    assert lib.page_score(p, 1, 4, 2, 64, p, p, p, p, 8, p, 16, 1.0, 1.0, p, 4,
+                          s) == EINVAL
+    # topk < 1, k_cap too small, score_ld too long
+    assert lib.page_topk(p, 64, 1, 4, p, 16, 0, 0.0, 0, 1, p, p, 8, s) == EINVAL
+    assert lib.page_topk(p, 64, 1, 4, p, 16, 9, 0.0, 0, 1, p, p, 8, s) == EINVAL
+    assert "k_cap" in _msg(lib)
+    assert lib.page_topk(p, 64, 1, 4, p, 16, 4, 0.5, 0, 1, p, p, 8, s) == EINVAL
+    assert lib.page_topk(p, 40000, 1, 4, p, 16, 4, 0.0, 0, 1, p, p, 8, s) == EINVAL
+    # H_sel neither H_q nor H_kv; splits < 1
+    assert lib.sparse_paged_decode(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p, 4, 3,
+                                   0.1, 2, p, p, s) == EINVAL
+    assert lib.sparse_paged_decode(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p, 4, 8,
+                                   0.1, 0, p, p, s) == EINVAL
+    # h2o: page size must be 1, decay in (0, 1]
+    assert lib.h2o_accumulate(p, 1, 8, 2, 128, p, 8, 16, p, 8, p, 0, 1, 0.1, 0.98,
+                              p, p, 8, p, 10 ** 6, s) == EINVAL
+    assert lib.h2o_accumulate(p, 1, 8, 2, 128, p, 8, 1, p, 8, p, 0, 1, 0.1, 1.5,
+                              p, p, 8, p, 10 ** 6, s) == EINVAL
+    # h2o: scratch too small
+    assert lib.h2o_accumulate(p, 1, 8, 2, 128, p, 8, 1, p, 8, p, 0, 1, 0.1, 0.98,
+                              p, p, 8, p, 3, s) == EINVAL
+    assert "scratch" in _msg(lib)
+    assert lib.lse_merge(p, p, 4, 0, 128, p, None, s) == EINVAL
+
+
+def test_validation_rejects_null_pointers(lib):
+    p = ctypes.c_void_p(16)
+    s = ctypes.c_void_p(0)
+    assert lib.lse_merge(None, p, 4, 2, 128, p, None, s) == EFAULT
+    assert "o_part" in _msg(lib)
+    assert lib.page_topk(p, 64, 1, 4, p, 16, 4, 0.0, 0, 1, None, p, 8, s) == EFAULT
+    assert lib.sparse_paged_decode(p, 1, 8, 2, 128, None, 8, 16, p, 4, p, p, p, 4,
+                                   8, 0.1, 2, p, p, s) == EFAULT
+    assert lib.pagestats_update(None, 8, 16, 2, 64, p, p, p, p, 4, p, 1, None,
+                                None, None, s) == EFAULT
+    # statistics buffers must be all given or all NULL
+    assert lib.pagestats_update(p, 8, 16, 2, 64, p, None, p, p, 4, p, 1, None,
+                                None, None, s) == EINVAL
+    # rebuild mode needs them
+    assert lib.pagestats_update(p, 8, 16, 2, 64, None, None, None, p, 4, p, 1,
+                                None, None, None, s) == EINVAL
+
+
+def test_scratch_size_query(lib):
+    n = lib.h2o_scratch_floats(4, 8, 4352)
+    chunks = -(-4352 // 256)
+    assert n == 4 * 8 * 4352 + 4 * 8 * chunks * 2
+    assert lib.h2o_scratch_floats(1, 0, 10) == -1
+    assert skv.h2o_scratch_floats(4, 8, 4352) == n
+
+
+def test_product_package_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "sparse_kv_cache_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", text, re.M), f
+                assert "sparsekv_oracle" not in text, f
+                assert "liboracle" not in text, f

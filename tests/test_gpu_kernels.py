@@ -1,0 +1,268 @@
+"""GPU parity of each entry point against the float64 oracle, on small seeded
+cases that span several tiles, ragged tails and the degenerate cases (one
+token, budget >= N, budget 1, empty splits, exact ties, -0.0, +/-inf lse).
+All calls go through the C ABI (sparse_kv_cache_amd binding)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_kv_cache_amd as skv
+from sparse_kv_cache_amd import workloads as W
+from sparse_kv_cache_amd.decode import SparseDecoder
+
+from parity import (bits, check_attention, check_partials, check_scores,
+                    check_selection_exact, check_selection_vs_oracle,
+                    check_stats, dev, per_head_rows, poison, say,
+                    selection_rows, bf16_bits_apart)
+
+pytestmark = pytest.mark.gpu
+
+# seed, B, H_q, H_kv, D, P, max_pages, topk, frac, bos, eos, splits, w_avg, w_peak
+PAGE_CASES = [
+    (0, 2, 4, 2, 64, 16, 9, 3, 0.0, 0, 1, 2, 1.0, 1.0),
+    (1, 3, 8, 2, 128, 16, 20, 5, 0.0, 0, 1, 3, 1.0, 0.5),
+    (2, 2, 7, 1, 128, 16, 12, 4, 0.0, 1, 2, 4, 0.5, -1.0),
+    (3, 2, 3, 3, 64, 4, 30, 6, 0.2, 0, 1, 5, 1.0, 1.0),
+    (4, 2, 16, 2, 128, 16, 40, 9, 0.0, 0, 1, 8, 1.0, 1.0),
+    (5, 1, 16, 1, 64, 1, 200, 17, 0.0, 2, 3, 3, 1.0, 1.0),
+    (6, 2, 8, 2, 128, 16, 6, 50, 0.0, 0, 1, 4, 1.0, 1.0),
+    (7, 4, 4, 4, 128, 16, 3, 1, 0.0, 0, 1, 1, 1.0, 1.0),
+    (8, 2, 32, 8, 128, 16, 64, 16, 0.0, 0, 1, 8, 1.0, 0.5),
+    (9, 2, 12, 4, 64, 8, 25, 7, 0.3, 1, 1, 2, 1.0, 2.0),
+    (10, 1, 6, 2, 128, 2, 80, 9, 0.0, 0, 1, 16, 1.0, 1.0),
+]
+
+
+def _decoder(wl):
+    return SparseDecoder(wl.B, wl.H_q, wl.H_kv, wl.D, wl.num_blocks, wl.P,
+                         wl.bt_ld, topk_pages=wl.topk_pages, topk_frac=wl.topk_frac,
+                         bos=wl.bos, eos=wl.eos, w_avg=wl.w_avg, w_peak=wl.w_peak,
+                         scale=wl.softmax_scale, num_splits=wl.num_splits)
+
+
+def run_page_case(wl, cache_cpu, q_cpu, exact_ties=False):
+    cache = dev(cache_cpu)
+    q = dev(q_cpu)
+    bt = dev(wl.block_table)
+    sl = dev(wl.seq_lens)
+    d = _decoder(wl)
+    poison(d)
+    d.k_min.fill_(float("nan")); d.k_max.fill_(float("nan")); d.k_mean.fill_(float("nan"))
+    d.rebuild_stats(cache, bt, sl)
+    d.score(q, bt, sl)
+    d.select(sl)
+    d.attend(q, cache, bt, sl)
+    d.merge()
+    torch.cuda.synchronize()
+
+    cb = bits(cache)
+    qd = q_cpu.double().numpy()
+    used = W.referenced_blocks(wl)
+    gmin, gmax = bits(d.k_min), bits(d.k_max)
+    gmean = d.k_mean.cpu().numpy()
+    st = check_stats(gmin, gmax, gmean, cb, wl.block_table, wl.seq_lens, wl.P, used)
+    # the score kernel in isolation: oracle fed the GPU statistics
+    gst = (oracle.bf16_decode(gmin), oracle.bf16_decode(gmax), gmean.astype(np.float64))
+    gs = d.scores.cpu().numpy()
+    check_scores(gs, qd, gst, wl.block_table, wl.seq_lens, wl.P, wl.w_avg, wl.w_peak)
+    # the top-k kernel in isolation: oracle fed the GPU scores
+    N = wl.pages()
+    sel_idx = d.sel_idx.cpu().numpy().reshape(-1, d.k_cap)
+    sel_cnt = d.sel_cnt.cpu().numpy().reshape(-1)
+    rowsN = np.repeat(N, wl.H_q)
+    check_selection_exact(sel_idx, sel_cnt, gs.reshape(-1, wl.bt_ld), rowsN,
+                          wl.topk_pages, wl.topk_frac, wl.bos, wl.eos)
+    # end to end: oracle statistics and scores in float64
+    ref_scores = oracle.page_score(qd, *st, wl.block_table, wl.seq_lens, wl.P,
+                                   wl.w_avg, wl.w_peak)
+    rows = selection_rows(sel_idx, sel_cnt)
+    ex = check_selection_vs_oracle(rows, ref_scores.reshape(-1, wl.bt_ld), rowsN,
+                                   wl.topk_pages, wl.topk_frac, wl.bos, wl.eos)
+    if exact_ties:
+        assert ex == 0
+    # attention over the GPU's own selection
+    per = per_head_rows(rows, wl.B, wl.H_q, wl.H_q)
+    check_partials(d.o_part.cpu().numpy(), d.lse_part.cpu().numpy(), qd, cb,
+                   wl.block_table, wl.seq_lens, per, wl.G, wl.softmax_scale)
+    worst = check_attention(d.out.cpu().numpy(), d.lse.cpu().numpy(), qd, cb,
+                            wl.block_table, wl.seq_lens, per, wl.G,
+                            wl.softmax_scale)
+    return worst, ex
+
+
+@pytest.mark.parametrize("case", PAGE_CASES, ids=[f"page{c[0]}" for c in PAGE_CASES])
+def test_page_level_step(case):
+    (seed, B, H_q, H_kv, D, P, maxp, topk, frac, bos, eos, ns, wa, wp) = case
+    say(f"[gpu] page-level case {case}")
+    wl = W.small_case(seed=seed, B=B, H_q=H_q, H_kv=H_kv, D=D, P=P, max_pages=maxp,
+                      topk_pages=topk, topk_frac=frac, bos=bos, eos=eos,
+                      w_avg=wa, w_peak=wp, num_splits=ns)
+    worst, ex = run_page_case(wl, W.make_cache(wl), W.make_queries(wl))
+    say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}")
+
+
+def test_all_equal_scores_tie_break_to_lower_index():
+    say("[gpu] zero cache: every score ties")
+    wl = W.small_case(seed=20, B=2, H_q=4, H_kv=2, D=128, P=16, max_pages=30,
+                      topk_pages=5, num_splits=3, min_len=100)
+    cache = torch.zeros((2, wl.num_blocks, 16, 2, 128), dtype=torch.bfloat16)
+    worst, ex = run_page_case(wl, cache, W.make_queries(wl), exact_ties=True)
+
+
+def test_topk_rows_against_oracle_all_sizes():
+    rng = np.random.default_rng(0)
+    for ld in (1, 5, 64, 1000, 1024, 2048, 2049, 4096, 5000, 8192, 12000, 16384,
+               20000, 32768):
+        B, H = 3, 2
+        say(f"[gpu] page_topk score_ld={ld}")
+        sl = rng.integers(1, ld, size=B, endpoint=True).astype(np.int32)
+        sc = rng.integers(-6, 7, size=(B, H, ld)).astype(np.float32)      # ties
+        sc[0] = rng.standard_normal((H, ld)).astype(np.float32)
+        sc[..., ::7] = -0.0
+        sc[..., 3::11] = 0.0
+        for topk, frac, bos, eos in ((1, 0.0, 0, 1), (7, 0.0, 2, 3), (3, 0.1, 0, 1),
+                                     (ld + 5, 0.0, 0, 1), (max(1, ld // 3), 0.0, 0, 0)):
+            k_cap = min(max(topk, int(np.floor(np.float64(np.float32(frac)) * ld)),
+                            bos + eos), ld)
+            k_cap = max(k_cap, 1)
+            scores = dev(sc)
+            idx = torch.full((B, H, k_cap), -7, dtype=torch.int32, device="cuda")
+            cnt = torch.full((B, H), -7, dtype=torch.int32, device="cuda")
+            skv.page_topk(scores, dev(sl), 1, topk, idx, cnt, frac, bos, eos)
+            torch.cuda.synchronize()
+            check_selection_exact(idx.cpu().numpy().reshape(-1, k_cap),
+                                  cnt.cpu().numpy().reshape(-1),
+                                  sc.reshape(-1, ld).astype(np.float64),
+                                  np.repeat(sl, H), topk, frac, bos, eos)
+
+
+def test_lse_merge_edge_cases_and_random():
+    say("[gpu] lse_merge")
+    rng = np.random.default_rng(1)
+    for D in (64, 128):
+        rows, ns = 37, 9
+        o = rng.standard_normal((rows, ns, D)).astype(np.float32)
+        l = (rng.standard_normal((rows, ns)) * 3).astype(np.float32)
+        l[0, :] = -np.inf                     # every split empty
+        l[1, :4] = -np.inf
+        l[2, 2] = np.inf                      # +inf is read as -inf
+        l[3, :] = -np.inf
+        l[3, 5] = np.inf
+        l[4, 0] = 80.0                        # large spread
+        out = torch.full((rows, D), float("nan"), device="cuda")
+        lse = torch.full((rows,), float("nan"), device="cuda")
+        skv.lse_merge(dev(o), dev(l), out, lse)
+        torch.cuda.synchronize()
+        go, gl = out.cpu().numpy(), lse.cpu().numpy()
+        for r in range(rows):
+            want, wl_ = oracle.lse_merge(o[r].astype(np.float64), l[r].astype(np.float64))
+            np.testing.assert_allclose(go[r], want, rtol=1e-5, atol=1e-5)
+            if np.isinf(wl_):
+                assert np.isinf(gl[r]) and gl[r] < 0
+            else:
+                assert abs(gl[r] - wl_) <= 1e-5
+        np.testing.assert_array_equal(go[0], o[0, 0])
+        np.testing.assert_array_equal(go[3], o[3, 0])
+
+
+@pytest.mark.parametrize("P", [16, 4, 1])
+def test_append_refresh_and_reset(P):
+    say(f"[gpu] pagestats append P={P}")
+    wl = W.small_case(seed=30 + P, B=5, H_q=8, H_kv=2, D=128, P=P,
+                      max_pages=max(3, 48 // P), min_len=1)
+    cache_cpu = W.make_cache(wl)
+    cache = dev(cache_cpu)
+    bt, sl = dev(wl.block_table), dev(wl.seq_lens)
+    kn, vn = W.make_new_kv(wl, step=3)
+    hh = torch.full((wl.num_blocks * P, wl.H_kv), 7.5, dtype=torch.bfloat16,
+                    device="cuda")
+    kmin = torch.full((wl.num_blocks, 2, 128), float("nan"), dtype=torch.bfloat16,
+                      device="cuda")
+    kmax = kmin.clone()
+    kmean = torch.full((wl.num_blocks, 2, 128), float("nan"), device="cuda")
+    skv.pagestats_update(cache, kmin, kmax, kmean, bt, sl)          # rebuild
+    skv.pagestats_update(cache, kmin, kmax, kmean, bt, sl, dev(kn), dev(vn), hh)
+    torch.cuda.synchronize()
+    cb = bits(cache_cpu).copy()
+    hh_ref = bits(torch.full((wl.num_blocks * P, wl.H_kv), 7.5,
+                             dtype=torch.bfloat16)).copy()
+    oracle.append(cb, wl.block_table, wl.seq_lens, bits(kn), bits(vn), hh_ref)
+    assert np.array_equal(bits(cache), cb), "cache bytes differ after append"
+    assert np.array_equal(bits(hh), hh_ref), "hh reset differs"
+    used = W.referenced_blocks(wl)
+    check_stats(bits(kmin), bits(kmax), kmean.cpu().numpy(), cb, wl.block_table,
+                wl.seq_lens, P, used)
+
+
+def test_token_level_step_teacher_forced():
+    say("[gpu] h2o small, teacher forced")
+    S0, B, H_q, H_kv, D = 300, 3, 8, 2, 128
+    wl = W.h2o_token(seed=40, steps=6, prompt=S0, B=B)
+    wl.H_q, wl.H_kv, wl.D = H_q, H_kv, D
+    wl.bos, wl.eos, wl.topk_pages, wl.num_splits = 4, 8, 40, 5
+    wl.seq_lens = np.array([S0, S0 - 37, 11], dtype=np.int32)
+    cache = dev(W.make_cache(wl))
+    bt = dev(wl.block_table)
+    d = SparseDecoder(B, H_q, H_kv, D, wl.num_blocks, 1, wl.bt_ld,
+                      topk_pages=wl.topk_pages, bos=wl.bos, eos=wl.eos,
+                      scale=wl.softmax_scale, num_splits=wl.num_splits,
+                      token_level=True)
+    d.hh.copy_(W.make_hh(wl).cuda())
+    for step in range(wl.steps):
+        sl_np = wl.seq_lens_at(step)
+        sl = dev(sl_np)
+        q_cpu = W.make_queries(wl, step)
+        q = dev(q_cpu)
+        kn, vn = W.make_new_kv(wl, step)
+        pre_cache, pre_hh = bits(cache).copy(), bits(d.hh).copy()
+        poison(d)
+        d.append(cache, bt, sl, dev(kn), dev(vn))
+        torch.cuda.synchronize()
+        oracle.append(pre_cache, wl.block_table, sl_np, bits(kn), bits(vn), pre_hh)
+        assert np.array_equal(bits(cache), pre_cache)
+        assert np.array_equal(bits(d.hh), pre_hh)
+        d.accumulate(q, cache, bt, sl)
+        d.select(sl)
+        d.attend(q, cache, bt, sl)
+        d.merge()
+        torch.cuda.synchronize()
+        hh_ref = pre_hh.copy()
+        qd = q_cpu.double().numpy()
+        ref_scores = oracle.h2o_step(qd, pre_cache, wl.block_table, sl_np, hh_ref,
+                                     wl.bos, wl.eos, wl.softmax_scale, wl.decay)
+        gh = bits(d.hh)
+        apart = bf16_bits_apart(gh, hh_ref)
+        assert apart.max() <= 1, f"step {step}: hh more than one ulp off"
+        gs = d.scores.cpu().numpy()
+        for b in range(B):
+            n = int(sl_np[b])
+            slots = wl.block_table[b, :n]
+            np.testing.assert_array_equal(gs[b, :, :n].T, oracle.bf16_decode(gh[slots]))
+        sel_idx = d.sel_idx.cpu().numpy().reshape(-1, d.k_cap)
+        sel_cnt = d.sel_cnt.cpu().numpy().reshape(-1)
+        Nrows = np.repeat(sl_np, H_kv)
+        check_selection_exact(sel_idx, sel_cnt, gs.reshape(-1, wl.bt_ld), Nrows,
+                              wl.topk_pages, 0.0, wl.bos, wl.eos)
+        rows = selection_rows(sel_idx, sel_cnt)
+        check_selection_vs_oracle(rows, ref_scores.reshape(-1, wl.bt_ld), Nrows,
+                                  wl.topk_pages, 0.0, wl.bos, wl.eos, token_level=True)
+        per = per_head_rows(rows, B, H_q, H_kv)
+        check_partials(d.o_part.cpu().numpy(), d.lse_part.cpu().numpy(), qd,
+                       bits(cache), wl.block_table, sl_np, per, H_q // H_kv,
+                       wl.softmax_scale)
+        check_attention(d.out.cpu().numpy(), d.lse.cpu().numpy(), qd, bits(cache),
+                        wl.block_table, sl_np, per, H_q // H_kv, wl.softmax_scale)
+        say(f"  step {step}: hh ulps off max {apart.max()}, "
+            f"{int((apart > 0).sum())} of {apart.size}")
+
+
+def test_invalid_arguments_raise_before_launch():
+    say("[gpu] argument errors")
+    q = torch.zeros((1, 4, 96), device="cuda")
+    with pytest.raises(skv.SparseKVError) as e:
+        skv.lse_merge(torch.zeros((1, 2, 96), device="cuda"),
+                      torch.zeros((1, 2), device="cuda"), torch.zeros((1, 96), device="cuda"))
+    assert e.value.code == -22
+    with pytest.raises(TypeError):
+        skv.page_score(q.double(), None, None, None, None, None, 16, 1, 1, None)

@@ -1,0 +1,164 @@
+"""GPU parity on the five decode workloads at their real sizes, in the launch
+configuration the benchmark times (SparseDecoder, same splits).
+
+mha_tiny, gqa_ragged and long_context are compared in full; high_batch on a
+sample of requests (shortest, longest and three others) after two appended
+steps; h2o_token teacher-forced at its first two steps and its last step, plus
+the probability-mass invariant after all 256 steps."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_kv_cache_amd import workloads as W
+from sparse_kv_cache_amd.decode import SparseDecoder
+
+from parity import (bits, bf16_bits_apart, check_attention, check_partials,
+                    check_scores, check_selection_exact,
+                    check_selection_vs_oracle, check_stats, dev, per_head_rows,
+                    poison, say, selection_rows, sub_batch)
+
+pytestmark = pytest.mark.gpu
+
+
+def page_level_parity(wl, cache, q_cpu, seq_lens_np, rows, d, partial_heads=4):
+    """Compare decoder d's buffers (already computed for the whole batch) with
+    the oracle on requests ``rows``."""
+    cb, bt, sl, blocks, (gmin, gmax, gmean) = sub_batch(
+        wl, cache, rows, seq_lens_np, extra=(d.k_min, d.k_max, d.k_mean))
+    qd = q_cpu.double().numpy()[rows]
+    used = np.arange(len(blocks))
+    st = check_stats(bits(gmin), bits(gmax), gmean.numpy(), cb, bt, sl, wl.P, used)
+    gst = (oracle.bf16_decode(bits(gmin)), oracle.bf16_decode(bits(gmax)),
+           gmean.numpy().astype(np.float64))
+    gs = d.scores.cpu().numpy()[rows]
+    check_scores(gs, qd, gst, bt, sl, wl.P, wl.w_avg, wl.w_peak)
+    N = (sl.astype(np.int64) + wl.P - 1) // wl.P
+    rowsN = np.repeat(N, wl.H_q)
+    sel_idx = d.sel_idx.cpu().numpy()[rows].reshape(-1, d.k_cap)
+    sel_cnt = d.sel_cnt.cpu().numpy()[rows].reshape(-1)
+    check_selection_exact(sel_idx, sel_cnt, gs.reshape(-1, wl.bt_ld), rowsN,
+                          wl.topk_pages, wl.topk_frac, wl.bos, wl.eos)
+    ref_scores = oracle.page_score(qd, *st, bt, sl, wl.P, wl.w_avg, wl.w_peak)
+    sel_rows = selection_rows(sel_idx, sel_cnt)
+    ex = check_selection_vs_oracle(sel_rows, ref_scores.reshape(-1, wl.bt_ld), rowsN,
+                                   wl.topk_pages, wl.topk_frac, wl.bos, wl.eos)
+    per = per_head_rows(sel_rows, len(rows), wl.H_q, wl.H_q)
+    hs = slice(0, partial_heads)
+    check_partials(d.o_part.cpu().numpy()[rows][:, hs], d.lse_part.cpu().numpy()[rows][:, hs],
+                   qd[:, hs], cb, bt, sl, [p[hs] for p in per], wl.G, wl.softmax_scale)
+    worst = check_attention(d.out.cpu().numpy()[rows], d.lse.cpu().numpy()[rows], qd,
+                            cb, bt, sl, per, wl.G, wl.softmax_scale)
+    return worst, ex
+
+
+def _static_workload(name):
+    wl = W.WORKLOADS[name]()
+    say(f"[gpu] workload {name}: generating")
+    cache = W.make_cache(wl, device="cuda")
+    q_cpu = W.make_queries(wl)
+    d = SparseDecoder.for_workload(wl)
+    bt, sl = dev(wl.block_table), dev(wl.seq_lens)
+    poison(d)
+    d.rebuild_stats(cache, bt, sl)
+    d.step(dev(q_cpu), cache, bt, sl)
+    torch.cuda.synchronize()
+    say(f"[gpu] workload {name}: checking")
+    worst, ex = page_level_parity(wl, cache, q_cpu, wl.seq_lens, range(wl.B), d)
+    say(f"  {name}: max |out - oracle| {worst:.2e}, near-tie rows {ex}")
+
+
+def test_mha_tiny():
+    _static_workload("mha_tiny")
+
+
+def test_gqa_ragged():
+    _static_workload("gqa_ragged")
+
+
+def test_long_context():
+    _static_workload("long_context")
+
+
+def test_high_batch_sampled_after_appends():
+    wl = W.high_batch()
+    say("[gpu] workload high_batch: generating 300k-block pool")
+    cache = W.make_cache(wl, device="cuda")
+    d = SparseDecoder.for_workload(wl)
+    bt = dev(wl.block_table)
+    sl0 = dev(wl.seq_lens)
+    d.rebuild_stats(cache, bt, sl0)
+    steps = 2
+    for step in range(steps):
+        sl_np = wl.seq_lens_at(step)
+        kn, vn = W.make_new_kv(wl, step, device="cuda")
+        q_cpu = W.make_queries(wl, step)
+        poison(d)
+        d.step(dev(q_cpu), cache, bt, dev(sl_np), kn, vn)
+    torch.cuda.synchronize()
+    order = np.argsort(wl.seq_lens)
+    rows = sorted({int(order[0]), int(order[-1]), 7, 64, 101})
+    say(f"[gpu] workload high_batch: checking requests {rows}")
+    worst, ex = page_level_parity(wl, cache, q_cpu, sl_np, rows, d, partial_heads=2)
+    say(f"  high_batch: max |out - oracle| {worst:.2e}, near-tie rows {ex}")
+
+
+def test_h2o_token_sequence():
+    wl = W.h2o_token()
+    say("[gpu] workload h2o_token: generating")
+    cache = W.make_cache(wl, device="cuda")
+    d = SparseDecoder.for_workload(wl)
+    d.hh.copy_(W.make_hh(wl, device="cuda"))
+    bt = dev(wl.block_table)
+    checked = {0, 1, wl.steps - 1}
+    G = wl.G
+    for step in range(wl.steps):
+        sl_np = wl.seq_lens_at(step)
+        sl = dev(sl_np)
+        q_cpu = W.make_queries(wl, step)
+        q = dev(q_cpu)
+        kn, vn = W.make_new_kv(wl, step, device="cuda")
+        if step not in checked:
+            d.step(q, cache, bt, sl, kn, vn)
+            continue
+        say(f"[gpu] h2o_token step {step}: teacher-forced check")
+        poison(d)
+        d.append(cache, bt, sl, kn, vn)
+        torch.cuda.synchronize()
+        pre_cache, pre_hh = bits(cache), bits(d.hh).copy()
+        d.accumulate(q, cache, bt, sl)
+        d.select(sl)
+        d.attend(q, cache, bt, sl)
+        d.merge()
+        torch.cuda.synchronize()
+        qd = q_cpu.double().numpy()
+        hh_ref = pre_hh.copy()
+        ref = oracle.h2o_step(qd, pre_cache, wl.block_table, sl_np, hh_ref, wl.bos,
+                              wl.eos, wl.softmax_scale, wl.decay)
+        gh = bits(d.hh)
+        apart = bf16_bits_apart(gh, hh_ref)
+        assert apart.max() <= 1
+        gs = d.scores.cpu().numpy()
+        sel_idx = d.sel_idx.cpu().numpy().reshape(-1, d.k_cap)
+        sel_cnt = d.sel_cnt.cpu().numpy().reshape(-1)
+        Nrows = np.repeat(sl_np, wl.H_kv)
+        check_selection_exact(sel_idx, sel_cnt, gs.reshape(-1, wl.bt_ld), Nrows,
+                              wl.topk_pages, 0.0, wl.bos, wl.eos)
+        rows = selection_rows(sel_idx, sel_cnt)
+        ex = check_selection_vs_oracle(rows, ref.reshape(-1, wl.bt_ld), Nrows,
+                                       wl.topk_pages, 0.0, wl.bos, wl.eos,
+                                       token_level=True)
+        per = per_head_rows(rows, wl.B, wl.H_q, wl.H_kv)
+        worst = check_attention(d.out.cpu().numpy(), d.lse.cpu().numpy(), qd,
+                                pre_cache, wl.block_table, sl_np, per, G,
+                                wl.softmax_scale)
+        say(f"  step {step}: hh off-by-one-ulp {int((apart > 0).sum())}/{apart.size}, "
+            f"near-tie rows {ex}, max |out - oracle| {worst:.2e}")
+    # every step adds one unit of softmax mass per (request, kv head)
+    gh = oracle.bf16_decode(bits(d.hh))
+    exact = (1 - wl.decay ** wl.steps) / (1 - wl.decay)
+    for b in range(wl.B):
+        n = int(wl.seq_lens_at(wl.steps - 1)[b])
+        mass = gh[wl.block_table[b, :n]].sum(0)
+        assert np.all(np.abs(mass / exact - 1) <= 0.10), (mass, exact)
+    say(f"  h2o_token mass after {wl.steps} steps: {mass} (exact {exact:.2f})")
