@@ -76,7 +76,9 @@ def unique_kv_bytes(wl, sel_idx, sel_cnt, seq_lens, H_sel):
 
 
 def kernel_bytes(wl, sel_idx, sel_cnt, seq_lens, num_splits, token_level):
-    """Algorithmic HBM bytes of each kernel of one step (formulas in DESIGN)."""
+    """Algorithmic HBM bytes of each kernel of one step: the bytes the
+    operation must move at least (unique selected K/V once, statistics, scores,
+    indices, partials)."""
     B, Hq, Hkv, D, P = wl.B, wl.H_q, wl.H_kv, wl.D, wl.P
     N = (seq_lens.astype(np.int64) + P - 1) // P
     H_sel = Hkv if token_level else Hq
@@ -165,7 +167,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by request / kv head with no exchange; see DESIGN.md)",
+              "(the path shards by request and kv head with no exchange between GPUs)",
               file=sys.stderr)
         return 2
     import torch
@@ -209,6 +211,25 @@ def main():
         stats_ms = e0.elapsed_time(e1) / R
     gen_s = time.perf_counter() - t_gen
 
+    # A plain device copy of known size: its duration is the achievable HBM
+    # rate on this machine, and under a counter profile its FETCH_SIZE /
+    # WRITE_SIZE readings calibrate the counters (256 MiB read + 256 MiB
+    # written per launch).
+    copy_bytes = 256 << 20
+    csrc = torch.empty(copy_bytes, dtype=torch.uint8, device=dev)
+    cdst = torch.empty(copy_bytes, dtype=torch.uint8, device=dev)
+    csrc.fill_(1)
+    copy_ms = []
+    for _ in range(3):
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        cdst.copy_(csrc)
+        c1.record()
+        torch.cuda.synchronize()
+        copy_ms.append(c0.elapsed_time(c1))
+    copy_gbps = 2 * copy_bytes / (min(copy_ms) * 1e-3) / 1e9
+    del csrc, cdst
+
     names = (["pagestats_update"] if wl.steps > 1 else []) + \
         (["h2o_accumulate"] if token_level else ["page_score"]) + \
         ["page_topk", "sparse_paged_decode", "lse_merge"]
@@ -230,7 +251,7 @@ def main():
         else:
             d.score(q, bt, sl)
         rec(k); k += 1
-        d.select(sl)
+        d.select(sl, bt)
         rec(k); k += 1
         d.attend(q, c, bt, sl)
         rec(k); k += 1
@@ -301,6 +322,7 @@ def main():
         "kernels": kern, "dominant_kernel": dominant,
         "stats_rebuild_ms": None if stats_ms is None else round(stats_ms, 4),
         "roofline": roofline,
+        "copy_GBps": round(copy_gbps, 1),
         "setup_s": round(gen_s, 1),
     }
     if not args.no_cpu_baseline:

@@ -125,6 +125,10 @@ int page_score(const float *q, int B, int H_q, int H_kv, int D,
  *   ties going to the lower index (-0.0 equals +0.0; scores must not be NaN).
  *   sel_idx  int32 [B, H_sel, k_cap]: ascending indices, padded with -1.
  *   sel_cnt  int32 [B, H_sel]: number selected (= max(|R|, k)).
+ *   sel_blk  int32 [B, H_sel, k_cap] or NULL: when given, the physical block
+ *            block_table[b * bt_ld + p] of every selected page p (-1 padded,
+ *            -1 for p >= bt_ld), so the decode needs no block-table lookup.
+ *            block_table / bt_ld are read only when sel_blk is given.
  *   Requires k_cap >= max(topk_pages, floor(topk_frac * score_ld), bos + eos)
  *   and score_ld <= 32768.
  */
@@ -132,6 +136,7 @@ int page_topk(const float *scores, int64_t score_ld, int B, int H_sel,
               const int32_t *seq_lens, int page_size, int topk_pages,
               float topk_frac, int reserved_bos, int reserved_eos,
               int32_t *sel_idx, int32_t *sel_cnt, int k_cap,
+              const int32_t *block_table, int64_t bt_ld, int32_t *sel_blk,
               hipStream_t stream);
 
 /*
@@ -143,23 +148,29 @@ int page_topk(const float *scores, int64_t score_ld, int B, int H_sel,
  *   H_sel == H_q : row (b, i) of sel_idx is query head i's own selection.
  *   H_sel == H_kv: the G query heads of kv head h share row (b, h) (the
  *                  token-level flow selects per kv head).
- *   Each selection row (cnt entries, ascending) is cut into num_splits
- *   contiguous groups of c = ceil(cnt / num_splits) entries; split s holds
- *   entries [s*c, min((s+1)*c, cnt)).  Tokens are {p*P + t : t < n_p} with
- *   n_p = min(P, S_b - p*P); l = scale * q . k.  Per (b, i, s):
+ *   Each selection row (cnt entries, ascending, -1 padded) is cut into
+ *   num_splits contiguous groups of c = ceil(k_cap / num_splits) entries;
+ *   split s holds entries [s*c, min((s+1)*c, cnt)).  Tokens are
+ *   {p*P + t : t < n_p} with n_p = min(P, S_b - p*P); l = scale * q . k.
+ *   Per (b, i, s):
  *     o_part   fp32 [B, H_q, num_splits, D]  = sum softmax(l) v over the split
  *     lse_part fp32 [B, H_q, num_splits]     = ln sum exp(l)  (-inf if empty,
  *                                               with o_part = 0)
- *   Pages selected by several heads of one kv head inside the same split are
- *   read from memory once for all of them.
+ *   sel_blk (nullable) is page_topk's block-id output for the same rows;
+ *   when given, the block table is not read.
+ *   With H_sel == H_kv every row a block loads serves all G query heads of
+ *   the group; with H_sel == H_q each query head's chunk is walked by its own
+ *   wave(s), and pages shared by heads of a group are served by the caches
+ *   after their first read.
  */
 int sparse_paged_decode(const float *q, int B, int H_q, int H_kv, int D,
                         const uint16_t *kv_cache, int64_t num_blocks,
                         int page_size, const int32_t *block_table,
                         int64_t bt_ld, const int32_t *seq_lens,
                         const int32_t *sel_idx, const int32_t *sel_cnt,
-                        int k_cap, int H_sel, float scale, int num_splits,
-                        float *o_part, float *lse_part, hipStream_t stream);
+                        const int32_t *sel_blk, int k_cap, int H_sel,
+                        float scale, int num_splits, float *o_part,
+                        float *lse_part, hipStream_t stream);
 
 /*
  * lse_merge -- N-way log-sum-exp merge of split partials.  [MLA:

@@ -59,9 +59,9 @@ def load_library():
     lib.sparsekv_last_error.argtypes = []
     lib.pagestats_update.argtypes = [V, L, I, I, I, V, V, V, V, L, V, I, V, V, V, V]
     lib.page_score.argtypes = [V, I, I, I, I, V, V, V, V, L, V, I, F, F, V, L, V]
-    lib.page_topk.argtypes = [V, L, I, I, V, I, I, F, I, I, V, V, I, V]
-    lib.sparse_paged_decode.argtypes = [V, I, I, I, I, V, L, I, V, L, V, V, V, I, I,
-                                        F, I, V, V, V]
+    lib.page_topk.argtypes = [V, L, I, I, V, I, I, F, I, I, V, V, I, V, L, V, V]
+    lib.sparse_paged_decode.argtypes = [V, I, I, I, I, V, L, I, V, L, V, V, V, V, I,
+                                        I, F, I, V, V, V]
     lib.lse_merge.argtypes = [V, V, I, I, I, V, V, V]
     lib.h2o_accumulate.argtypes = [V, I, I, I, I, V, L, I, V, L, V, I, I, F, F, V, V,
                                    L, V, L, V]
@@ -169,8 +169,10 @@ def page_score(q, k_min, k_max, k_mean, block_table, seq_lens, page_size,
 
 
 def page_topk(scores, seq_lens, page_size, topk_pages, sel_idx, sel_cnt,
-              topk_frac=0.0, reserved_bos=0, reserved_eos=1, stream=None):
-    """Top-k rows of scores [B, H_sel, score_ld] into sel_idx [B, H_sel, k_cap]."""
+              topk_frac=0.0, reserved_bos=0, reserved_eos=1, block_table=None,
+              sel_blk=None, stream=None):
+    """Top-k rows of scores [B, H_sel, score_ld] into sel_idx [B, H_sel, k_cap];
+    with sel_blk (and block_table) also the selected pages' physical blocks."""
     lib = load_library()
     _check("scores", scores, torch.float32, 3)
     dev = scores.device
@@ -180,16 +182,27 @@ def page_topk(scores, seq_lens, page_size, topk_pages, sel_idx, sel_cnt,
     _check("sel_cnt", sel_cnt, torch.int32, 2, dev)
     if tuple(sel_idx.shape[:2]) != (B, H_sel) or tuple(sel_cnt.shape) != (B, H_sel):
         raise ValueError("sel_idx must be [B, H_sel, k_cap] and sel_cnt [B, H_sel]")
+    _check("sel_blk", sel_blk, torch.int32, 3, dev)
+    bt_ld = 0
+    if sel_blk is not None:
+        if block_table is None:
+            raise ValueError("sel_blk needs block_table")
+        _check("block_table", block_table, torch.int32, 2, dev)
+        if sel_blk.shape != sel_idx.shape:
+            raise ValueError("sel_blk must have sel_idx's shape")
+        bt_ld = block_table.shape[1]
     _rc("page_topk", lib.page_topk(
         _ptr(scores), ld, B, H_sel, _ptr(seq_lens), int(page_size), int(topk_pages),
         float(topk_frac), int(reserved_bos), int(reserved_eos), _ptr(sel_idx),
-        _ptr(sel_cnt), sel_idx.shape[2], _stream(stream)))
+        _ptr(sel_cnt), sel_idx.shape[2],
+        _ptr(block_table) if sel_blk is not None else None, bt_ld, _ptr(sel_blk),
+        _stream(stream)))
 
 
 def sparse_paged_decode(q, kv_cache, block_table, seq_lens, sel_idx, sel_cnt,
-                        scale, o_part, lse_part, stream=None):
+                        scale, o_part, lse_part, sel_blk=None, stream=None):
     """Split-K partials over the selected pages.  H_sel = sel_idx.shape[1];
-    num_splits = o_part.shape[2]."""
+    num_splits = o_part.shape[2]; sel_blk (optional) from page_topk."""
     lib = load_library()
     _check("q", q, torch.float32, 3)
     dev = q.device
@@ -210,11 +223,14 @@ def sparse_paged_decode(q, kv_cache, block_table, seq_lens, sel_idx, sel_cnt,
         raise ValueError("o_part must be [B, H_q, splits, D] and lse_part [B, H_q, splits]")
     if sel_idx.shape[0] != B or tuple(sel_cnt.shape) != (B, H_sel):
         raise ValueError("sel_idx must be [B, H_sel, k_cap] and sel_cnt [B, H_sel]")
+    _check("sel_blk", sel_blk, torch.int32, 3, dev)
+    if sel_blk is not None and sel_blk.shape != sel_idx.shape:
+        raise ValueError("sel_blk must have sel_idx's shape")
     _rc("sparse_paged_decode", lib.sparse_paged_decode(
         _ptr(q), B, H_q, H_kv, D, _ptr(kv_cache), NB, P, _ptr(block_table),
         block_table.shape[1], _ptr(seq_lens), _ptr(sel_idx), _ptr(sel_cnt),
-        sel_idx.shape[2], H_sel, float(scale), ns, _ptr(o_part), _ptr(lse_part),
-        _stream(stream)))
+        _ptr(sel_blk), sel_idx.shape[2], H_sel, float(scale), ns, _ptr(o_part),
+        _ptr(lse_part), _stream(stream)))
 
 
 def lse_merge(o_part, lse_part, out, lse_out=None, stream=None):

@@ -6,53 +6,80 @@
 // read as -inf; when every lse is -inf the first partial is emitted with lse
 // -inf instead of 0/0).
 //
-// Mapping.  One wave per output row; each lane owns D/64 dims, so every split's
-// partial row is one coalesced 256- or 512-byte read.
+// Mapping.  One block per output row (see the kernel).
 #include "skv_device.h"
 #include "skv_host.h"
 
 namespace {
 
+constexpr int kThreads = 256;
+constexpr int kWChunk = 1024;          // split weights staged in LDS per pass
+
+// One block per output row.  The block first reduces max(lse) over the
+// splits, then stages the weights exp(lse_s - M) in LDS; threads are
+// (split group g, dim d) pairs, so each split's partial row is one coalesced
+// read and every thread keeps ns / (256 / D) independent loads in flight.
 template <int D>
-__global__ __launch_bounds__(256) void lse_merge_kernel(
+__global__ __launch_bounds__(kThreads) void lse_merge_kernel(
     const float* __restrict__ o_part, const float* __restrict__ lse_part,
     int rows, int ns, float* __restrict__ out, float* __restrict__ lse_out) {
-  constexpr int VPL = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  constexpr int NGRP = kThreads / D;
+  __shared__ float ws[kWChunk];
+  __shared__ float red[kThreads / 64];
+  __shared__ float accs[NGRP][D];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* L = lse_part + row * ns;
-  const float* O = o_part + row * ns * D;
-  float M = -INFINITY;
-  for (int s = lane; s < ns; s += 64) {
+  const float* O = o_part + row * static_cast<int64_t>(ns) * D;
+
+  float m = -INFINITY;
+  for (int s = tid; s < ns; s += kThreads) {
     float l = L[s];
     if (isinf(l)) l = -INFINITY;
-    M = fmaxf(M, l);
+    m = fmaxf(m, l);
   }
-  M = skv::wave_max(M);
-  float* dst = out + row * D + lane * VPL;
-  if (M == -INFINITY) {
+  m = skv::wave_max(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  float M = red[0];
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) dst[j] = O[lane * VPL + j];
-    if (lse_out != nullptr && lane == 0) lse_out[row] = -INFINITY;
+  for (int w = 1; w < kThreads / 64; ++w) M = fmaxf(M, red[w]);
+  __syncthreads();
+  if (M == -INFINITY) {
+    for (int d = tid; d < D; d += kThreads) out[row * D + d] = O[d];
+    if (lse_out != nullptr && tid == 0) lse_out[row] = -INFINITY;
     return;
   }
-  float acc[VPL];
-#pragma unroll
-  for (int j = 0; j < VPL; ++j) acc[j] = 0.0f;
-  float W = 0.0f;
-  for (int s = 0; s < ns; ++s) {
-    const float l = L[s];
-    if (isinf(l)) continue;
-    const float w = __expf(l - M);
-    W += w;
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) acc[j] = fmaf(w, O[s * D + lane * VPL + j], acc[j]);
+  const int g = tid / D, d = tid % D;
+  float acc = 0.0f, wsum = 0.0f;
+  for (int c0 = 0; c0 < ns; c0 += kWChunk) {
+    const int cend = min(ns, c0 + kWChunk);
+    for (int s = c0 + tid; s < cend; s += kThreads) {
+      const float l = L[s];
+      const float w = isinf(l) ? 0.0f : __expf(l - M);
+      ws[s - c0] = w;
+      wsum += w;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int s = c0 + g; s < cend; s += NGRP)
+      acc = fmaf(ws[s - c0], O[static_cast<int64_t>(s) * D + d], acc);
+    __syncthreads();
   }
-  const float inv = 1.0f / W;
+  wsum = skv::wave_sum(wsum);
+  if (lane == 0) red[wave] = wsum;
+  accs[g][d] = acc;
+  __syncthreads();
+  if (tid < D) {
+    float W = 0.0f;
 #pragma unroll
-  for (int j = 0; j < VPL; ++j) dst[j] = acc[j] * inv;
-  if (lse_out != nullptr && lane == 0) lse_out[row] = M + __logf(W);
+    for (int w = 0; w < kThreads / 64; ++w) W += red[w];
+    float a = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NGRP; ++k) a += accs[k][tid];
+    out[row * D + tid] = a / W;
+    if (lse_out != nullptr && tid == 0) lse_out[row] = M + __logf(W);
+  }
 }
 
 }  // namespace
@@ -67,7 +94,7 @@ extern "C" int lse_merge(const float* o_part, const float* lse_part, int rows,
   SKV_REQUIRE_PTR(lse_part);
   SKV_REQUIRE_PTR(out);
   if (rows == 0) { skv::clear_error(); return SKV_OK; }
-  dim3 grid(static_cast<unsigned>((rows + 3) / 4));
+  dim3 grid(static_cast<unsigned>(rows));
   if (D == 128)
     hipLaunchKernelGGL(lse_merge_kernel<128>, grid, dim3(256), 0, stream, o_part,
                        lse_part, rows, num_splits, out, lse_out);

@@ -18,8 +18,8 @@
 // Mapping.  One block per (tile of pages, kv head, request); a page-head's
 // statistics (256 + 256 + 512 bytes at D = 128) are read by D/8 lanes with
 // 16-byte loads, so a wave covers 64/(D/8) pages per load and every byte of
-// statistics is read once for the whole query group, whose rows sit in
-// registers.  Groups larger than 8 are split over grid.y slices.
+// statistics is read once for the whole query group, whose rows sit in LDS.
+// Groups larger than 8 are split over grid.y slices.
 #include "skv_device.h"
 #include "skv_host.h"
 
@@ -54,19 +54,6 @@ __global__ __launch_bounds__(256) void page_score_kernel(
   const int sub = lane / LPR;
   const int c = lane % LPR;
 
-  float qv[GS][8], qa[GS][8];
-#pragma unroll
-  for (int g = 0; g < GS; ++g) {
-    const bool ok = g0 + g < G;
-    const float* qr = q + (static_cast<int64_t>(b) * H_q + h * G + g0 + g) * D + c * 8;
-    float4 a = ok ? *reinterpret_cast<const float4*>(qr) : make_float4(0, 0, 0, 0);
-    float4 bb = ok ? *reinterpret_cast<const float4*>(qr + 4) : make_float4(0, 0, 0, 0);
-    qv[g][0] = a.x; qv[g][1] = a.y; qv[g][2] = a.z; qv[g][3] = a.w;
-    qv[g][4] = bb.x; qv[g][5] = bb.y; qv[g][6] = bb.z; qv[g][7] = bb.w;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qa[g][i] = fabsf(qv[g][i]);
-  }
-
   const int32_t* btr = bt + static_cast<int64_t>(b) * bt_ld;
   uint4 mn[kIter], mx[kIter];
   float4 me0[kIter], me1[kIter];
@@ -74,18 +61,24 @@ __global__ __launch_bounds__(256) void page_score_kernel(
 #pragma unroll
   for (int it = 0; it < kIter; ++it) {
     pg[it] = p0 + (it * kWaves + wave) * PPW + sub;
-    if (pg[it] < N) {
-      const int64_t blk = btr[pg[it]];
-      const int64_t off = (blk * H_kv + h) * D + c * 8;
-      mn[it] = *reinterpret_cast<const uint4*>(kmin + off);
-      mx[it] = *reinterpret_cast<const uint4*>(kmax + off);
-      me0[it] = *reinterpret_cast<const float4*>(kmean + off);
-      me1[it] = *reinterpret_cast<const float4*>(kmean + off + 4);
-    } else {
-      mn[it] = mx[it] = make_uint4(0, 0, 0, 0);
-      me0[it] = me1[it] = make_float4(0, 0, 0, 0);
-    }
+    // unconditional loads (pages past N read page p0's entry, whose result
+    // is never stored) keep the count of loads in flight static
+    const int64_t blk = btr[pg[it] < N ? pg[it] : p0];
+    const int64_t off = (blk * H_kv + h) * D + c * 8;
+    mn[it] = *reinterpret_cast<const uint4*>(kmin + off);
+    mx[it] = *reinterpret_cast<const uint4*>(kmax + off);
+    me0[it] = *reinterpret_cast<const float4*>(kmean + off);
+    me1[it] = *reinterpret_cast<const float4*>(kmean + off + 4);
   }
+
+  // (statistics loads are in flight) the group's query rows go to LDS (2 x 16-byte reads per head and page
+  // slot) so the registers go to loads in flight
+  __shared__ __align__(16) float qs[GS][D];
+  for (int i = threadIdx.x; i < GS * D; i += blockDim.x) {
+    const int g = i / D, d = i % D;
+    qs[g][d] = g0 + g < G ? q[(static_cast<int64_t>(b) * H_q + h * G + g0 + g) * D + d] : 0.0f;
+  }
+  __syncthreads();
 
 #pragma unroll
   for (int it = 0; it < kIter; ++it) {
@@ -105,9 +98,12 @@ __global__ __launch_bounds__(256) void page_score_kernel(
     float mine = 0.0f;
 #pragma unroll
     for (int g = 0; g < GS; ++g) {
+      const float4 qa = *reinterpret_cast<const float4*>(&qs[g][c * 8]);
+      const float4 qb = *reinterpret_cast<const float4*>(&qs[g][c * 8 + 4]);
+      const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
       float s = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s = fmaf(qv[g][i], mp[i], fmaf(qa[g][i], hp[i], s));
+      for (int i = 0; i < 8; ++i) s = fmaf(qv[i], mp[i], fmaf(fabsf(qv[i]), hp[i], s));
       s = skv::group_sum<LPR>(s);
       if (c == g) mine = s;
     }

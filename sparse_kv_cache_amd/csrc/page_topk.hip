@@ -9,13 +9,14 @@
 //
 // Method.  One block per row.  Scores become order-preserving uint32 keys
 // (-0.0 folded onto +0.0) held in registers, ITEMS contiguous entries per
-// thread.  A most-significant-digit radix select (four 8-bit passes, LDS
-// histogram with shared atomics, digit search by one wave) finds the exact
-// key T of the m-th best candidate and how many entries equal to T are still
-// needed.  Entries above T are taken; among those equal to T the lowest
-// indices are taken, ranked by a block-wide prefix count in index order.  A
-// second prefix count over the final flags writes the indices in ascending
-// order with no sort.
+// thread.  A most-significant-digit radix select finds the key prefix of the
+// m-th best candidate: the bits every candidate shares are skipped (block
+// OR / AND), each pass histograms the next 8 bits of the keys still matching
+// the prefix (LDS atomics; one wave finds the digit), and the select stops
+// early once the chosen bin is taken whole.  Keys above the prefix are taken;
+// among those equal to it the lowest indices are taken, ranked by a
+// block-wide prefix count in index order.  A second prefix count over the
+// final flags writes the indices in ascending order with no sort.
 #include <limits.h>
 
 #include "skv_device.h"
@@ -34,15 +35,18 @@ __global__ __launch_bounds__(BLOCK) void page_topk_kernel(
     const float* __restrict__ scores, int64_t score_ld, int H_sel,
     const int32_t* __restrict__ seq_lens, int P, int topk_pages,
     double topk_frac, int bos, int eos, int32_t* __restrict__ sel_idx,
-    int32_t* __restrict__ sel_cnt, int k_cap) {
+    int32_t* __restrict__ sel_cnt, int k_cap, const int32_t* __restrict__ bt,
+    int64_t bt_ld, int32_t* __restrict__ sel_blk) {
+  constexpr int NW = BLOCK / 64;
   __shared__ int hist[256];
-  __shared__ int scan_smem[BLOCK / 64 + 1];
-  __shared__ int s_digit, s_remaining;
+  __shared__ int scan_smem[NW + 1];
+  __shared__ uint32_t s_or[NW], s_and[NW];
+  __shared__ int s_digit, s_remaining, s_bin;
 
   const int64_t row = blockIdx.x;
   const int b = static_cast<int>(row / H_sel);
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
+  const int lane = tid & 63, wave = tid >> 6;
 
   int64_t N64 = (static_cast<int64_t>(seq_lens[b]) + P - 1) / P;
   if (N64 > score_ld) N64 = score_ld;
@@ -62,31 +66,70 @@ __global__ __launch_bounds__(BLOCK) void page_topk_kernel(
   const float* srow = scores + row * score_ld;
   const int base = tid * ITEMS;
   uint32_t key[ITEMS];
+  const bool vec = ((score_ld & 3) == 0) &&
+                   ((reinterpret_cast<uintptr_t>(scores) & 15) == 0) &&
+                   (base + ITEMS <= hi) && (base >= lo);
+  if (vec) {
 #pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const int p = base + i;
-    key[i] = (p >= lo && p < hi) ? order_key(srow[p]) : 0u;
+    for (int i = 0; i < ITEMS; i += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(srow + base + i);
+      key[i] = order_key(v.x); key[i + 1] = order_key(v.y);
+      key[i + 2] = order_key(v.z); key[i + 3] = order_key(v.w);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      const int p = base + i;
+      key[i] = (p >= lo && p < hi) ? order_key(srow[p]) : 0u;
+    }
   }
 
-  uint32_t T;
+  // Selection state: candidates whose (key & pmask) exceeds prefix are taken;
+  // among those equal to prefix under pmask, the r_eq lowest indices.
+  uint32_t prefix, pmask;
   int r_eq;
   if (want == 0) {
-    T = 0xffffffffu; r_eq = 0;             // reserved entries only
+    prefix = 0xffffffffu; pmask = 0xffffffffu; r_eq = 0;   // reserved only
   } else if (want >= ncand) {
-    T = 0u; r_eq = INT_MAX;                // every candidate
+    prefix = 0u; pmask = 0u; r_eq = INT_MAX;               // every candidate
   } else {
-    uint32_t prefix = 0u, pmask = 0u;
+    // Bits shared by every candidate need no radix pass: start the digits at
+    // the highest bit where two candidates differ.
+    uint32_t o = 0u, a = 0xffffffffu;
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      const int p = base + i;
+      if (p >= lo && p < hi) { o |= key[i]; a &= key[i]; }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      o |= __shfl_xor(o, off);
+      a &= __shfl_xor(a, off);
+    }
+    if (lane == 0) { s_or[wave] = o; s_and[wave] = a; }
+    __syncthreads();
+    o = 0u; a = 0xffffffffu;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) { o |= s_or[w]; a &= s_and[w]; }
+    const uint32_t diff = o ^ a;          // bits that vary among candidates
+    prefix = a & ~diff;                   // (bits outside diff's span agree)
+    int top = diff ? 31 - __clz(diff) : -1;
+    pmask = top >= 0 ? ~((2u << top) - 1u) : 0xffffffffu;
+    if (top == 31) pmask = 0u;
+    prefix &= pmask;
     int remaining = want;
-#pragma unroll 1
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
+    bool done = false;
+    while (!done && top >= 0) {
+      const int shift = top >= 7 ? top - 7 : 0;
+      const int width = top - shift + 1;
+      const uint32_t dmask = (width == 32) ? 0xffffffffu : ((1u << width) - 1u);
       for (int j = tid; j < 256; j += BLOCK) hist[j] = 0;
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i) {
         const int p = base + i;
         if (p >= lo && p < hi && (key[i] & pmask) == prefix)
-          atomicAdd(&hist[(key[i] >> shift) & 255u], 1);
+          atomicAdd(&hist[(key[i] >> shift) & dmask], 1);
       }
       __syncthreads();
       if (tid < 64) {
@@ -94,11 +137,11 @@ __global__ __launch_bounds__(BLOCK) void page_topk_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) cs[j] = hist[4 * lane + j];
         const int sum = cs[0] + cs[1] + cs[2] + cs[3];
-        int suf = sum;                      // sum over lanes >= lane
+        int suf = sum;                      // entries in bins of lanes >= lane
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int y = __shfl_down(suf, o);
-          if (lane + o < 64) suf += y;
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_down(suf, off);
+          if (lane + off < 64) suf += y;
         }
         int above = suf - sum;              // entries in higher digits
 #pragma unroll
@@ -106,17 +149,20 @@ __global__ __launch_bounds__(BLOCK) void page_topk_kernel(
           if (above < remaining && above + cs[j] >= remaining) {
             s_digit = 4 * lane + j;
             s_remaining = remaining - above;
+            s_bin = cs[j];
           }
           above += cs[j];
         }
       }
       __syncthreads();
-      const uint32_t d = static_cast<uint32_t>(s_digit);
+      const uint32_t dg = static_cast<uint32_t>(s_digit);
       remaining = s_remaining;
-      prefix |= d << shift;
-      pmask |= 0xffu << shift;
+      prefix |= dg << shift;
+      pmask |= dmask << shift;
+      done = (remaining == s_bin);          // the whole bin is taken
+      top = shift - 1;
+      __syncthreads();
     }
-    T = prefix;
     r_eq = remaining;
   }
 
@@ -124,7 +170,7 @@ __global__ __launch_bounds__(BLOCK) void page_topk_kernel(
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
     const int p = base + i;
-    eq += (p >= lo && p < hi && key[i] == T) ? 1 : 0;
+    eq += (p >= lo && p < hi && (key[i] & pmask) == prefix) ? 1 : 0;
   }
   int total_eq;
   int er = skv::block_exclusive_scan(eq, &total_eq, scan_smem);
@@ -134,25 +180,34 @@ __global__ __launch_bounds__(BLOCK) void page_topk_kernel(
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
     const int p = base + i;
+    const uint32_t km = key[i] & pmask;
     bool take;
     if (p >= N) take = false;
     else if (p < lo || p >= hi) take = true;
-    else if (key[i] > T) take = true;
-    else if (key[i] == T) { take = er < r_eq; ++er; }
+    else if (km > prefix) take = true;
+    else if (km == prefix) { take = er < r_eq; ++er; }
     else take = false;
     if (take) { flags |= 1u << i; ++cnt; }
   }
   int total;
   int pos = skv::block_exclusive_scan(cnt, &total, scan_smem);
   int32_t* out = sel_idx + row * k_cap;
+  int32_t* bout = sel_blk != nullptr ? sel_blk + row * k_cap : nullptr;
+  const int32_t* btr = bout != nullptr ? bt + static_cast<int64_t>(b) * bt_ld : nullptr;
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
     if (flags & (1u << i)) {
-      if (pos < k_cap) out[pos] = base + i;
+      if (pos < k_cap) {
+        out[pos] = base + i;
+        if (bout != nullptr) bout[pos] = base + i < bt_ld ? btr[base + i] : -1;
+      }
       ++pos;
     }
   }
-  for (int j = total + tid; j < k_cap; j += BLOCK) out[j] = -1;
+  for (int j = total + tid; j < k_cap; j += BLOCK) {
+    out[j] = -1;
+    if (bout != nullptr) bout[j] = -1;
+  }
   if (tid == 0) sel_cnt[row] = total < k_cap ? total : k_cap;
 }
 
@@ -160,10 +215,12 @@ template <int BLOCK, int ITEMS>
 void launch_topk(int64_t rows, hipStream_t stream, const float* scores,
                  int64_t score_ld, int H_sel, const int32_t* seq_lens, int P,
                  int topk_pages, double topk_frac, int bos, int eos,
-                 int32_t* sel_idx, int32_t* sel_cnt, int k_cap) {
+                 int32_t* sel_idx, int32_t* sel_cnt, int k_cap, const int32_t* bt,
+                 int64_t bt_ld, int32_t* sel_blk) {
   hipLaunchKernelGGL((page_topk_kernel<BLOCK, ITEMS>), dim3(static_cast<unsigned>(rows)),
                      dim3(BLOCK), 0, stream, scores, score_ld, H_sel, seq_lens, P,
-                     topk_pages, topk_frac, bos, eos, sel_idx, sel_cnt, k_cap);
+                     topk_pages, topk_frac, bos, eos, sel_idx, sel_cnt, k_cap, bt,
+                     bt_ld, sel_blk);
 }
 
 }  // namespace
@@ -172,7 +229,8 @@ extern "C" int page_topk(const float* scores, int64_t score_ld, int B,
                          int H_sel, const int32_t* seq_lens, int page_size,
                          int topk_pages, float topk_frac, int reserved_bos,
                          int reserved_eos, int32_t* sel_idx, int32_t* sel_cnt,
-                         int k_cap, hipStream_t stream) {
+                         int k_cap, const int32_t* block_table, int64_t bt_ld,
+                         int32_t* sel_blk, hipStream_t stream) {
   SKV_REQUIRE(B >= 0 && H_sel > 0, "page_topk: need B >= 0 and H_sel > 0");
   SKV_REQUIRE(score_ld > 0 && score_ld <= 32768,
               "page_topk: score_ld must be in [1, 32768] (got %lld)", (long long)score_ld);
@@ -196,13 +254,17 @@ extern "C" int page_topk(const float* scores, int64_t score_ld, int B,
   SKV_REQUIRE_PTR(seq_lens);
   SKV_REQUIRE_PTR(sel_idx);
   SKV_REQUIRE_PTR(sel_cnt);
+  if (sel_blk != nullptr) {
+    SKV_REQUIRE_PTR(block_table);
+    SKV_REQUIRE(bt_ld > 0, "page_topk: bt_ld must be > 0 when sel_blk is given");
+  }
   const int64_t rows = static_cast<int64_t>(B) * H_sel;
   SKV_REQUIRE(rows <= 0x7fffffff, "page_topk: too many rows");
   if (rows == 0) { skv::clear_error(); return SKV_OK; }
 #define SKV_TOPK(BL, IT)                                                          \
   launch_topk<BL, IT>(rows, stream, scores, score_ld, H_sel, seq_lens, page_size, \
                       topk_pages, frac, reserved_bos, reserved_eos, sel_idx,      \
-                      sel_cnt, k_cap)
+                      sel_cnt, k_cap, block_table, bt_ld, sel_blk)
   if (score_ld <= 1024) SKV_TOPK(256, 4);
   else if (score_ld <= 2048) SKV_TOPK(256, 8);
   else if (score_ld <= 4096) SKV_TOPK(256, 16);

@@ -6,62 +6,319 @@
 // test_ops_mla_chunked_context.cpp: partial attention outputs with their
 // log-sum-exps merge into the single-shot result (the merge is lse_merge).
 //
-// Mapping.  One block (4 waves) per (split, kv head, request).  A block owns
-// split s of the selection row(s) of its kv head: with one selection per
-// query head, the G rows of the group; with a selection shared by the group
-// (token-level flow), one row.  Per round the block copies up to 256 entries
-// of those rows into LDS and, for per-head rows, merges them: an entry is
-// kept only at its first occurrence and carries a G-bit mask of the heads
-// that selected it (binary search in the other heads' ascending rows).  So a
-// page picked by several heads of the group is read from HBM once for all of
-// them, and its block id is resolved once per round.
+// Common layout.  A token row of one kv head is D bf16 values = D/8 lanes x
+// 16 bytes, so a wave holds 64/(D/8) rows per load and a group of 16 token
+// rows (one page at page_size 16, or 16/P pages) takes NL = 16/(64/(D/8))
+// 16-byte loads per lane for K and as many for V.  Dot products reduce over
+// the D/8 lanes of a row with DPP row moves.  Every lane keeps an online
+// softmax state (max, sum, 8-dim accumulator) for its own rows; states are
+// merged across row slots (lane shuffles) and waves (LDS) once, at the end.
+// Exponentials are base 2 with the scale pre-multiplied by log2(e).  Loads run
+// NPIPE groups ahead of the arithmetic (packed bf16 in registers, unpacked on
+// use), so each wave keeps up to NPIPE x 2 x 4 KB of K/V in flight.
 //
-// Token rows are processed in groups of 16 (one page at page_size 16, or 16
-// pages of fewer rows).  A token row of one kv head is D bf16 values = D/8
-// lanes x 16 bytes, so a wave holds 64/(D/8) rows per load and each group
-// takes 16/(64/(D/8)) 16-byte loads per lane for K and as many for V; the
-// next group's loads are issued before the current one is computed.  The dot
-// products reduce over the D/8 lanes of a row with DPP row moves; every lane
-// keeps an online-softmax state (max, sum, 8-dim accumulator) per head of the
-// group for its own rows, and the states are merged across row slots (lane
-// shuffles) and across waves (LDS) only once, at the end.  Exponentials are
-// base 2 with the scale pre-multiplied by log2(e).
+// Split s of a selection row holds its entries [s*c, min((s+1)*c, cnt)) with
+// c = ceil(k_cap / num_splits), so a block can fetch its chunk without first
+// reading the count.
+//
+// Two mappings:
+//  * wave kernel (one selection per query head): one wave per (request,
+//    query head, split); the per-lane state is one head's, which leaves the
+//    registers to the load pipeline and 4 waves per SIMD.  A page that
+//    several heads of a group selected is fetched by each of their waves at
+//    about the same time on one CU and served by L2 after the first read.
+//  * group kernel (one selection shared by the group, the token-level flow):
+//    one block per (split, kv head, request); each wave walks part of the
+//    shared chunk once and applies every query head of the group to the rows
+//    it loaded.
+#include <stdlib.h>
+#include <string.h>
+
 #include "skv_device.h"
 #include "skv_host.h"
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kMaxEnt = 256;          // entries per round
+constexpr int kMaxEnt = 256;          // LDS entries per round (group kernel)
+constexpr int kXcds = 8;              // accelerator complex dies of an MI355X
+#ifndef SKV_DECODE_PIPE
+#define SKV_DECODE_PIPE 2             // groups of 16 rows in flight per wave
+#endif
+#ifndef SKV_DECODE_WPE
+#define SKV_DECODE_WPE 3              // waves per SIMD the wave kernel is sized for
+#endif
+#ifndef SKV_DECODE_WPE16
+#define SKV_DECODE_WPE16 3            // same, page_size 16 path
+#endif
 
-struct RowLoad {
-  uint4 k, v;
-  uint32_t mask;                      // heads that attend this row
+// One head, one group of 16 token rows: fold the rows' logits and values into
+// the lane's online-softmax state.  Rows with ok == false were loaded from a
+// placeholder address; their values are replaced, never multiplied.
+template <int LPR, int NL>
+__device__ __forceinline__ void attend_rows(const float (&qq)[8],
+                                            const uint4 (&K)[NL],
+                                            const uint4 (&V)[NL],
+                                            const bool (&ok)[NL], float& m,
+                                            float& l, float (&acc)[8]) {
+  float lg[NL];
+  float mx = m;
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    float x[8];
+    skv::unpack8(K[j], x);
+    float d = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) d = fmaf(qq[i], x[i], d);
+    d = skv::group_sum<LPR>(d);
+    lg[j] = ok[j] ? d : -INFINITY;
+    mx = fmaxf(mx, lg[j]);
+  }
+  if (mx == -INFINITY) return;            // none of this lane's rows yet
+  const float alpha = exp2f(m - mx);      // 0 while m == -inf
+  float pj[NL];
+  float ps = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NL; ++j) { pj[j] = exp2f(lg[j] - mx); ps += pj[j]; }
+  l = fmaf(l, alpha, ps);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    // masked rows: zero the packed words (never multiply a placeholder row)
+    const uint4 vw = ok[j] ? V[j] : make_uint4(0, 0, 0, 0);
+    float v[8];
+    skv::unpack8(vw, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = fmaf(pj[j], v[i], acc[i]);
+  }
+  m = mx;
+}
+
+// Merge the online-softmax states of the 64/LPR row slots of a wave (lanes
+// c, c + LPR, ...); afterwards every lane holds the wave's state for its dims.
+template <int LPR>
+__device__ __forceinline__ void merge_slots(float& m, float& l, float (&acc)[8]) {
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1) {
+    const float m2 = __shfl_xor(m, o);
+    const float l2 = __shfl_xor(l, o);
+    const float mx = fmaxf(m, m2);
+    const float a = mx == -INFINITY ? 0.0f : exp2f(m - mx);
+    const float b = mx == -INFINITY ? 0.0f : exp2f(m2 - mx);
+    l = l * a + l2 * b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float a2 = __shfl_xor(acc[i], o);
+      acc[i] = acc[i] * a + a2 * b;
+    }
+    m = mx;
+  }
+}
+
+struct Chunk {
+  int start, len;
 };
 
-template <int D, int GMAX>
-__global__ __launch_bounds__(256) void sparse_decode_kernel(
+__device__ __forceinline__ Chunk split_chunk(int cnt, int k_cap, int num_splits, int s) {
+  cnt = cnt < 0 ? 0 : (cnt > k_cap ? k_cap : cnt);
+  const int c = (k_cap + num_splits - 1) / num_splits;
+  const int start = s * c;
+  int len = cnt - start;
+  len = len < 0 ? 0 : (len > c ? c : len);
+  return {start, len};
+}
+
+// ------------------------------------------------------------- wave kernel
+
+// One wave per (request, query head, split) chunk.  Waves are independent: no
+// LDS and no barriers.  Lane j of a wave holds entry j of the chunk (its block
+// id and valid row count, fetched once); the rows of a 16-row group take
+// their block ids from those lanes with a permute.  Within a (request, kv
+// head) the chunks are numbered s * G + g, so the query heads of one split
+// share a block, and all blocks of the (request, kv head) go to one XCD:
+// pages several heads selected are fetched through one L2 at about the same
+// time.
+template <int D, int WB, int NPIPE, int PFIX>
+__global__ __launch_bounds__(WB * 64)
+__attribute__((amdgpu_waves_per_eu(PFIX == 16 ? SKV_DECODE_WPE16 : SKV_DECODE_WPE)))
+void sparse_decode_wave_kernel(
     const float* __restrict__ q, int H_q, int H_kv, int G,
     const uint16_t* __restrict__ kv, int64_t num_blocks, int P,
     const int32_t* __restrict__ bt, int64_t bt_ld,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_idx,
-    const int32_t* __restrict__ sel_cnt, int k_cap, int shared_sel,
-    float scale_log2, int num_splits, float* __restrict__ o_part,
+    const int32_t* __restrict__ sel_cnt, const int32_t* __restrict__ sel_blk,
+    int k_cap, float scale_log2, int num_splits, float* __restrict__ o_part,
+    float* __restrict__ lse_part, int64_t n_groups, int blocks_per_group) {
+  constexpr int LPR = D / 8;
+  constexpr int RPL = 64 / LPR;
+  constexpr int NL = 16 / RPL;
+  const int lane = threadIdx.x & 63;
+  // Blocks are dealt to the 8 XCDs round-robin by id; block id -> (xcd, k)
+  // -> (request/kv-head group, block within the group) so that every block of
+  // one (request, kv head) runs on the same XCD and shares its L2.
+  const int xcd = blockIdx.x % kXcds;
+  const int64_t k = blockIdx.x / kXcds;
+  const int64_t grp_bh = xcd + kXcds * (k / blocks_per_group);
+  const int local = static_cast<int>(k % blocks_per_group) * WB + (threadIdx.x >> 6);
+  if (grp_bh >= n_groups || local >= num_splits * G) return;
+  const int g = local % G;
+  const int s = local / G;
+  const int h = static_cast<int>(grp_bh % H_kv);
+  const int b = static_cast<int>(grp_bh / H_kv);
+  const int64_t qrow = static_cast<int64_t>(b) * H_q + h * G + g;
+  const int slot = lane / LPR, c = lane % LPR;
+  const int S = seq_lens[b];
+  int64_t Nb = (static_cast<int64_t>(S) + P - 1) / P;
+  if (Nb > bt_ld) Nb = bt_ld;
+  // The chunk's place in the row depends only on k_cap, so its entries (and
+  // block ids, when the selection carries them) are fetched together with the
+  // count instead of after it.
+  const int cap = (k_cap + num_splits - 1) / num_splits;
+  const int start = s * cap;
+  const int32_t* selr = sel_idx + qrow * k_cap + start;
+  const int32_t* sblk = sel_blk != nullptr ? sel_blk + qrow * k_cap + start : nullptr;
+  int cnt = sel_cnt[qrow];
+  cnt = cnt < 0 ? 0 : (cnt > k_cap ? k_cap : cnt);
+  int clen = cnt - start;
+  clen = clen < 0 ? 0 : (clen > cap ? cap : clen);
+
+  float qq[8];
+  {
+    const float4 qa = *reinterpret_cast<const float4*>(q + qrow * D + c * 8);
+    const float4 qb = *reinterpret_cast<const float4*>(q + qrow * D + c * 8 + 4);
+    qq[0] = qa.x * scale_log2; qq[1] = qa.y * scale_log2;
+    qq[2] = qa.z * scale_log2; qq[3] = qa.w * scale_log2;
+    qq[4] = qb.x * scale_log2; qq[5] = qb.y * scale_log2;
+    qq[6] = qb.z * scale_log2; qq[7] = qb.w * scale_log2;
+  }
+  float m = -INFINITY, l = 0.0f, acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+
+  const int32_t* btr = bt + static_cast<int64_t>(b) * bt_ld;
+  const int64_t head_off = static_cast<int64_t>(h) * D + c * 8;
+  const int64_t row_stride = static_cast<int64_t>(H_kv) * D;
+  const int64_t v_off = num_blocks * P * row_stride;
+  const int epg = 16 / P;
+
+  for (int w0 = 0; w0 < cap; w0 += 64) {
+    int p = -1, sb = -1;
+    if (w0 + lane < cap) {
+      p = selr[w0 + lane];
+      if (sblk != nullptr) sb = sblk[w0 + lane];
+    }
+    const int nw = min(64, clen - w0);
+    if (nw <= 0) break;
+    int my_blk = 0, my_nv = 0;
+    if (lane < nw && p >= 0 && p < Nb) {
+      my_blk = sblk != nullptr ? sb : btr[p];
+      const int n = S - p * P;
+      my_nv = n < P ? n : P;
+    }
+    const int ngroups = (nw + epg - 1) / epg;
+    auto load = [&](int grp, uint4 (&K)[NL], uint4 (&V)[NL], bool (&ok)[NL]) {
+      if constexpr (PFIX == 16) {
+        // one page per group: its block id and row count are wave-uniform
+        // (read from lane grp), so the row addresses are a scalar page base
+        // plus a per-lane constant
+        const int gc = grp < nw ? grp : 0;
+        const int blk = __builtin_amdgcn_readlane(my_blk, gc);
+        const int nv = grp < nw ? __builtin_amdgcn_readlane(my_nv, gc) : 0;
+        const uint16_t* kp = kv + static_cast<int64_t>(blk) * 16 * row_stride;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+          const int t = slot + RPL * j;
+          ok[j] = t < nv;
+          const uint32_t off = ok[j] ? static_cast<uint32_t>(t * row_stride + head_off) : 0u;
+          const uint16_t* base = ok[j] ? kp : kv + head_off;
+          K[j] = *reinterpret_cast<const uint4*>(base + off);
+          V[j] = *reinterpret_cast<const uint4*>(base + v_off + off);
+        }
+      } else {
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        const int rr = slot + RPL * j;            // row in group, 0..15
+        const int e = grp * epg + rr / P;
+        const int t = rr % P;
+        const int ec = e < 64 ? e : 63;
+        const int blk = __shfl(my_blk, ec);
+        const int nv = __shfl(my_nv, ec);
+        ok[j] = grp < ngroups && e < nw && t < nv;
+        // masked rows read row 0 of block 0: the loads are unconditional so
+        // the count in flight is static and the waits stay exact
+        const int64_t off = ok[j] ? (static_cast<int64_t>(blk) * P + t) * row_stride + head_off
+                                  : head_off;
+        K[j] = *reinterpret_cast<const uint4*>(kv + off);
+        V[j] = *reinterpret_cast<const uint4*>(kv + v_off + off);
+      }
+      }
+    };
+    uint4 K0[NL], V0[NL], K1[NL], V1[NL], K2[NL], V2[NL];
+    bool o0[NL], o1[NL], o2[NL];
+    int grp = 0;
+    load(0, K0, V0, o0);
+    load(1, K1, V1, o1);
+    if constexpr (NPIPE >= 3) load(2, K2, V2, o2);
+    while (grp < ngroups) {
+      if constexpr (NPIPE >= 3) {
+        attend_rows<LPR, NL>(qq, K0, V0, o0, m, l, acc);
+        if (++grp >= ngroups) break;
+        load(grp + 2, K0, V0, o0);
+        attend_rows<LPR, NL>(qq, K1, V1, o1, m, l, acc);
+        if (++grp >= ngroups) break;
+        load(grp + 2, K1, V1, o1);
+        attend_rows<LPR, NL>(qq, K2, V2, o2, m, l, acc);
+        if (++grp >= ngroups) break;
+        load(grp + 2, K2, V2, o2);
+      } else {
+        attend_rows<LPR, NL>(qq, K0, V0, o0, m, l, acc);
+        if (++grp >= ngroups) break;
+        load(grp + 1, K0, V0, o0);
+        attend_rows<LPR, NL>(qq, K1, V1, o1, m, l, acc);
+        if (++grp >= ngroups) break;
+        load(grp + 1, K1, V1, o1);
+      }
+    }
+  }
+
+  merge_slots<LPR>(m, l, acc);
+  const int64_t prow = qrow * num_splits + s;
+  if (slot == 0) {
+    float4* dst = reinterpret_cast<float4*>(o_part + prow * D + c * 8);
+    if (m == -INFINITY) {
+      dst[0] = make_float4(0, 0, 0, 0);
+      dst[1] = make_float4(0, 0, 0, 0);
+    } else {
+      const float inv = 1.0f / l;
+      dst[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+      dst[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+    }
+  }
+  if (lane == 0) lse_part[prow] = m == -INFINITY ? -INFINITY : (m + log2f(l)) * skv::kLn2;
+}
+
+// ------------------------------------------------------------ group kernel
+
+template <int D, int GMAX>
+__global__ __launch_bounds__(256) void sparse_decode_group_kernel(
+    const float* __restrict__ q, int H_q, int H_kv, int G,
+    const uint16_t* __restrict__ kv, int64_t num_blocks, int P,
+    const int32_t* __restrict__ bt, int64_t bt_ld,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_idx,
+    const int32_t* __restrict__ sel_cnt, const int32_t* __restrict__ sel_blk,
+    int k_cap, float scale_log2, int num_splits, float* __restrict__ o_part,
     float* __restrict__ lse_part) {
-  constexpr int LPR = D / 8;          // lanes per token row
-  constexpr int RPL = 64 / LPR;       // rows per wave load
-  constexpr int NL = 16 / RPL;        // loads per 16-row group
-  constexpr int R = kMaxEnt / GMAX;   // entries per head per round
+  constexpr int LPR = D / 8;
+  constexpr int RPL = 64 / LPR;
+  constexpr int NL = 16 / RPL;
+  constexpr int WAVES = 4;
 
   __shared__ __align__(16) float qs[GMAX][D];
-  __shared__ int32_t raw[GMAX][R];
   __shared__ int32_t e_blk[kMaxEnt];
   __shared__ int32_t e_nv[kMaxEnt];
-  __shared__ uint32_t e_mask[kMaxEnt];
-  __shared__ int scan_smem[kWaves + 1];
-  __shared__ int s_len[GMAX], s_start[GMAX], s_rows[GMAX];
-  __shared__ float red_m[kWaves][GMAX], red_l[kWaves][GMAX];
-  __shared__ float red_acc[kWaves][GMAX][D];
+  __shared__ int s_start, s_len;
+  __shared__ float red_m[WAVES][GMAX], red_l[WAVES][GMAX];
+  __shared__ float red_acc[WAVES][GMAX][D];
 
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
@@ -70,35 +327,21 @@ __global__ __launch_bounds__(256) void sparse_decode_kernel(
   const int S = seq_lens[b];
   int64_t Nb = (static_cast<int64_t>(S) + P - 1) / P;
   if (Nb > bt_ld) Nb = bt_ld;
-  const int nrows = shared_sel ? 1 : G;      // selection rows of this block
-  const uint32_t all_heads = (G >= 32) ? 0xffffffffu : ((1u << G) - 1u);
+  const int row = b * H_kv + h;
 
+  if (tid == 0) {
+    const Chunk ch = split_chunk(sel_cnt[row], k_cap, num_splits, s);
+    s_start = ch.start;
+    s_len = ch.len;
+  }
   for (int i = tid; i < GMAX * D; i += blockDim.x) {
     const int g = i / D, d = i % D;
     qs[g][d] = g < G ? q[(static_cast<int64_t>(b) * H_q + h * G + g) * D + d] * scale_log2
                      : 0.0f;
   }
-  if (tid < GMAX) {
-    int len = 0, start = 0, row = 0;
-    if (tid < nrows) {
-      row = shared_sel ? b * H_kv + h : b * H_q + h * G + tid;
-      int cnt = sel_cnt[row];
-      cnt = cnt < 0 ? 0 : (cnt > k_cap ? k_cap : cnt);
-      const int chunk = (cnt + num_splits - 1) / num_splits;
-      start = s * chunk;
-      len = cnt - start;
-      len = len < 0 ? 0 : (len > chunk ? chunk : len);
-    }
-    s_len[tid] = len;
-    s_start[tid] = start;
-    s_rows[tid] = row;
-  }
   __syncthreads();
-  int max_len = 0;
-  for (int g = 0; g < nrows; ++g) max_len = max(max_len, s_len[g]);
-  const int rounds = (max_len + R - 1) / R;
+  const int rounds = (s_len + kMaxEnt - 1) / kMaxEnt;
 
-  // per-lane online softmax state, one per head of the group
   float m[GMAX], l[GMAX], acc[GMAX][8];
 #pragma unroll
   for (int g = 0; g < GMAX; ++g) {
@@ -106,169 +349,76 @@ __global__ __launch_bounds__(256) void sparse_decode_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[g][i] = 0.0f;
   }
-
   const int64_t head_off = static_cast<int64_t>(h) * D + c * 8;
-  const int64_t row_stride = static_cast<int64_t>(H_kv) * D;       // per token row
-  const int64_t v_off = num_blocks * P * row_stride;               // V half
+  const int64_t row_stride = static_cast<int64_t>(H_kv) * D;
+  const int64_t v_off = num_blocks * P * row_stride;
+  const int32_t* btr = bt + static_cast<int64_t>(b) * bt_ld;
+  const int epg = 16 / P;
 
   for (int rd = 0; rd < rounds; ++rd) {
-    // 1. copy this round's part of each row into LDS
-    {
-      const int g = tid / R, j = tid % R;
-      if (g < GMAX) {
-        int v = -1;
-        if (g < nrows) {
-          const int pos = rd * R + j;
-          if (pos < s_len[g])
-            v = sel_idx[static_cast<int64_t>(s_rows[g]) * k_cap + s_start[g] + pos];
-        }
-        raw[g][j] = v;
-      }
-    }
-    __syncthreads();
-    // 2. merge duplicates across the group, resolve block ids
-    int keep = 0;
-    int32_t my_blk = 0, my_nv = 0;
-    uint32_t my_mask = 0;
-    {
-      const int g = tid / R, j = tid % R;
-      int p = -1;
-      if (g < nrows) p = raw[g][j];
-      if (p >= 0 && p < Nb) {
-        bool first = true;
-        uint32_t mask = 1u << g;
-        if (shared_sel) {
-          mask = all_heads;
-        } else {
-          for (int g2 = 0; g2 < nrows; ++g2) {
-            if (g2 == g) continue;
-            int len2 = s_len[g2] - rd * R;
-            len2 = len2 < 0 ? 0 : (len2 > R ? R : len2);
-            int a = 0, z = len2;            // lower bound of p in raw[g2][0, len2)
-            while (a < z) {
-              const int mid = (a + z) >> 1;
-              if (raw[g2][mid] < p) a = mid + 1; else z = mid;
-            }
-            if (a < len2 && raw[g2][a] == p) {
-              mask |= 1u << g2;
-              if (g2 < g) first = false;
-            }
-          }
-        }
-        if (first) {
-          keep = 1;
-          my_mask = mask;
-          my_blk = bt[static_cast<int64_t>(b) * bt_ld + p];
-          const int nv = S - p * P;
-          my_nv = nv < P ? nv : P;
+    for (int j = tid; j < kMaxEnt; j += blockDim.x) {
+      const int pos = rd * kMaxEnt + j;
+      int blk = -1, nv = 0;
+      if (pos < s_len) {
+        const int64_t at = static_cast<int64_t>(row) * k_cap + s_start + pos;
+        const int p = sel_idx[at];
+        if (p >= 0 && p < Nb) {
+          blk = sel_blk != nullptr ? sel_blk[at] : btr[p];
+          const int n = S - p * P;
+          nv = n < P ? n : P;
         }
       }
-    }
-    int nent;
-    const int pos = skv::block_exclusive_scan(keep, &nent, scan_smem);
-    if (keep) {
-      e_blk[pos] = my_blk;
-      e_nv[pos] = my_nv;
-      e_mask[pos] = my_mask;
+      e_blk[j] = blk;
+      e_nv[j] = nv;
     }
     __syncthreads();
-
-    // 3. attend: groups of 16 token rows
-    const int epg = 16 / P;                       // entries per group
-    const int ngroups = (nent + epg - 1) / epg;
-    auto load = [&](int grp, RowLoad (&x)[NL]) {
+    int n_here = s_len - rd * kMaxEnt;
+    n_here = n_here > kMaxEnt ? kMaxEnt : n_here;
+    const int ngroups = (n_here + epg - 1) / epg;
+    auto load = [&](int grp, uint4 (&K)[NL], uint4 (&V)[NL], bool (&ok)[NL]) {
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
-        const int rr = slot + RPL * j;            // row in group, 0..15
+        const int rr = slot + RPL * j;
         const int e = grp * epg + rr / P;
         const int t = rr % P;
-        x[j].mask = 0u;
-        x[j].k = x[j].v = make_uint4(0, 0, 0, 0);
-        if (grp < ngroups && e < nent && t < e_nv[e]) {
-          const int64_t off = (static_cast<int64_t>(e_blk[e]) * P + t) * row_stride + head_off;
-          x[j].mask = e_mask[e];
-          x[j].k = *reinterpret_cast<const uint4*>(kv + off);
-          x[j].v = *reinterpret_cast<const uint4*>(kv + v_off + off);
-        }
+        const int ec = e < kMaxEnt ? e : kMaxEnt - 1;
+        ok[j] = grp < ngroups && e < n_here && t < e_nv[ec];
+        const int64_t off = ok[j] ? (static_cast<int64_t>(e_blk[ec]) * P + t) * row_stride + head_off
+                                  : head_off;
+        K[j] = *reinterpret_cast<const uint4*>(kv + off);
+        V[j] = *reinterpret_cast<const uint4*>(kv + v_off + off);
       }
     };
-    RowLoad cur[NL], nxt[NL];
-    int grp = wave;
-    load(grp, cur);
-    while (grp < ngroups) {
-      const int ngrp = grp + kWaves;
-      load(ngrp, nxt);
-      float kf[NL][8], vf[NL][8];
-      uint32_t any_mask = 0u;
-#pragma unroll
-      for (int j = 0; j < NL; ++j) {
-        skv::unpack8(cur[j].k, kf[j]);
-        skv::unpack8(cur[j].v, vf[j]);
-        any_mask |= cur[j].mask;
-      }
-      // heads attended by any row of the group, uniform across the wave
-      uint32_t gm = any_mask;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) gm |= __shfl_xor(gm, o);
+    auto apply = [&](const uint4 (&K)[NL], const uint4 (&V)[NL], const bool (&ok)[NL]) {
 #pragma unroll
       for (int g = 0; g < GMAX; ++g) {
-        if (g >= G || !((gm >> g) & 1u)) continue;
+        if (g >= G) continue;
         const float4 qa = *reinterpret_cast<const float4*>(&qs[g][c * 8]);
         const float4 qb = *reinterpret_cast<const float4*>(&qs[g][c * 8 + 4]);
         const float qq[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-        float lg[NL];
-        float mx = m[g];
-#pragma unroll
-        for (int j = 0; j < NL; ++j) {
-          float d = 0.0f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) d = fmaf(qq[i], kf[j][i], d);
-          d = skv::group_sum<LPR>(d);
-          lg[j] = ((cur[j].mask >> g) & 1u) ? d : -INFINITY;
-          mx = fmaxf(mx, lg[j]);
-        }
-        if (mx == -INFINITY) continue;            // none of my rows yet
-        const float alpha = exp2f(m[g] - mx);     // 0 when m[g] == -inf
-        float ps = 0.0f;
-        float pj[NL];
-#pragma unroll
-        for (int j = 0; j < NL; ++j) { pj[j] = exp2f(lg[j] - mx); ps += pj[j]; }
-        l[g] = fmaf(l[g], alpha, ps);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float a = acc[g][i] * alpha;
-#pragma unroll
-          for (int j = 0; j < NL; ++j) a = fmaf(pj[j], vf[j][i], a);
-          acc[g][i] = a;
-        }
-        m[g] = mx;
+        attend_rows<LPR, NL>(qq, K, V, ok, m[g], l[g], acc[g]);
       }
-#pragma unroll
-      for (int j = 0; j < NL; ++j) cur[j] = nxt[j];
-      grp = ngrp;
+    };
+    uint4 K0[NL], V0[NL], K1[NL], V1[NL];
+    bool o0[NL], o1[NL];
+    int grp = wave;
+    load(grp, K0, V0, o0);
+    while (grp < ngroups) {
+      load(grp + WAVES, K1, V1, o1);
+      apply(K0, V0, o0);
+      grp += WAVES;
+      if (grp >= ngroups) break;
+      load(grp + WAVES, K0, V0, o0);
+      apply(K1, V1, o1);
+      grp += WAVES;
     }
-    __syncthreads();                              // LDS lists reused next round
+    __syncthreads();
   }
 
-  // 4. merge the row slots of the wave (lanes c, c+LPR, ...)
 #pragma unroll
   for (int g = 0; g < GMAX; ++g) {
     if (g >= G) continue;
-#pragma unroll
-    for (int o = LPR; o < 64; o <<= 1) {
-      const float m2 = __shfl_xor(m[g], o);
-      const float l2 = __shfl_xor(l[g], o);
-      const float mx = fmaxf(m[g], m2);
-      const float a = mx == -INFINITY ? 0.0f : exp2f(m[g] - mx);
-      const float bb = mx == -INFINITY ? 0.0f : exp2f(m2 - mx);
-      l[g] = l[g] * a + l2 * bb;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float a2 = __shfl_xor(acc[g][i], o);
-        acc[g][i] = acc[g][i] * a + a2 * bb;
-      }
-      m[g] = mx;
-    }
+    merge_slots<LPR>(m[g], l[g], acc[g]);
     if (slot == 0) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) red_acc[wave][g][c * 8 + i] = acc[g][i];
@@ -276,13 +426,11 @@ __global__ __launch_bounds__(256) void sparse_decode_kernel(
     }
   }
   __syncthreads();
-
-  // 5. merge the waves and write the split's partial
   for (int i = tid; i < G * D; i += blockDim.x) {
     const int g = i / D, d = i % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w][g]);
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, red_m[w][g]);
     const int64_t prow = (static_cast<int64_t>(b) * H_q + h * G + g) * num_splits + s;
     if (M == -INFINITY) {
       o_part[prow * D + d] = 0.0f;
@@ -291,7 +439,7 @@ __global__ __launch_bounds__(256) void sparse_decode_kernel(
     }
     float L = 0.0f, A = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < WAVES; ++w) {
       const float e = exp2f(red_m[w][g] - M);
       L = fmaf(red_l[w][g], e, L);
       A = fmaf(red_acc[w][g][d], e, A);
@@ -301,18 +449,32 @@ __global__ __launch_bounds__(256) void sparse_decode_kernel(
   }
 }
 
+struct Args {
+  const float* q; int H_q, H_kv, G; const uint16_t* kv; int64_t num_blocks; int P;
+  const int32_t* bt; int64_t bt_ld; const int32_t* seq_lens; const int32_t* sel_idx;
+  const int32_t* sel_cnt; const int32_t* sel_blk; int k_cap; float scale_log2; int num_splits;
+  float* o_part; float* lse_part;
+};
+
+constexpr int kWaveBlock = 4;          // waves per block of the wave kernel
+
+template <int D, int PFIX>
+void launch_wave(hipStream_t st, const Args& a, int64_t n_groups) {
+  const int per_group = (a.num_splits * a.G + kWaveBlock - 1) / kWaveBlock;
+  const int64_t blocks = kXcds * per_group * ((n_groups + kXcds - 1) / kXcds);
+  hipLaunchKernelGGL((sparse_decode_wave_kernel<D, kWaveBlock, SKV_DECODE_PIPE, PFIX>),
+                     dim3(static_cast<unsigned>(blocks)), dim3(kWaveBlock * 64), 0, st,
+                     a.q, a.H_q, a.H_kv, a.G, a.kv, a.num_blocks, a.P, a.bt, a.bt_ld,
+                     a.seq_lens, a.sel_idx, a.sel_cnt, a.sel_blk, a.k_cap, a.scale_log2,
+                     a.num_splits, a.o_part, a.lse_part, n_groups, per_group);
+}
+
 template <int D, int GMAX>
-void launch_decode(dim3 grid, hipStream_t stream, const float* q, int H_q,
-                   int H_kv, int G, const uint16_t* kv, int64_t num_blocks,
-                   int P, const int32_t* bt, int64_t bt_ld,
-                   const int32_t* seq_lens, const int32_t* sel_idx,
-                   const int32_t* sel_cnt, int k_cap, int shared_sel,
-                   float scale_log2, int num_splits, float* o_part,
-                   float* lse_part) {
-  hipLaunchKernelGGL((sparse_decode_kernel<D, GMAX>), grid, dim3(kWaves * 64), 0,
-                     stream, q, H_q, H_kv, G, kv, num_blocks, P, bt, bt_ld,
-                     seq_lens, sel_idx, sel_cnt, k_cap, shared_sel, scale_log2,
-                     num_splits, o_part, lse_part);
+void launch_group(dim3 grid, hipStream_t st, const Args& a) {
+  hipLaunchKernelGGL((sparse_decode_group_kernel<D, GMAX>), grid, dim3(256), 0, st,
+                     a.q, a.H_q, a.H_kv, a.G, a.kv, a.num_blocks, a.P, a.bt, a.bt_ld,
+                     a.seq_lens, a.sel_idx, a.sel_cnt, a.sel_blk, a.k_cap, a.scale_log2,
+                     a.num_splits, a.o_part, a.lse_part);
 }
 
 }  // namespace
@@ -323,7 +485,8 @@ extern "C" int sparse_paged_decode(const float* q, int B, int H_q, int H_kv,
                                    const int32_t* block_table, int64_t bt_ld,
                                    const int32_t* seq_lens,
                                    const int32_t* sel_idx,
-                                   const int32_t* sel_cnt, int k_cap,
+                                   const int32_t* sel_cnt,
+                                   const int32_t* sel_blk, int k_cap,
                                    int H_sel, float scale, int num_splits,
                                    float* o_part, float* lse_part,
                                    hipStream_t stream) {
@@ -352,25 +515,37 @@ extern "C" int sparse_paged_decode(const float* q, int B, int H_q, int H_kv,
   SKV_REQUIRE_PTR(o_part);
   SKV_REQUIRE_PTR(lse_part);
   if (B == 0) { skv::clear_error(); return SKV_OK; }
-  const int shared_sel = (H_sel == H_kv && G > 1) ? 1 : 0;
-  const int GM = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
+  const bool shared_sel = (H_sel == H_kv && G > 1);
   dim3 grid(static_cast<unsigned>(num_splits), static_cast<unsigned>(H_kv),
             static_cast<unsigned>(B));
-  const float scale_log2 = scale * skv::kLog2e;
-#define SKV_DEC(DD, GG)                                                         \
-  launch_decode<DD, GG>(grid, stream, q, H_q, H_kv, G, kv_cache, num_blocks,     \
-                        page_size, block_table, bt_ld, seq_lens, sel_idx,       \
-                        sel_cnt, k_cap, shared_sel, scale_log2, num_splits,     \
-                        o_part, lse_part)
-  if (D == 128) {
-    if (GM == 1) SKV_DEC(128, 1); else if (GM == 2) SKV_DEC(128, 2);
-    else if (GM == 4) SKV_DEC(128, 4); else if (GM == 8) SKV_DEC(128, 8);
-    else SKV_DEC(128, 16);
+  const Args a{q, H_q, H_kv, G, kv_cache, num_blocks, page_size, block_table, bt_ld,
+               seq_lens, sel_idx, sel_cnt, sel_blk, k_cap, scale * skv::kLog2e, num_splits,
+               o_part, lse_part};
+  if (shared_sel) {
+    const int GM = G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
+    if (D == 128) {
+      if (GM == 2) launch_group<128, 2>(grid, stream, a);
+      else if (GM == 4) launch_group<128, 4>(grid, stream, a);
+      else if (GM == 8) launch_group<128, 8>(grid, stream, a);
+      else launch_group<128, 16>(grid, stream, a);
+    } else {
+      if (GM == 2) launch_group<64, 2>(grid, stream, a);
+      else if (GM == 4) launch_group<64, 4>(grid, stream, a);
+      else if (GM == 8) launch_group<64, 8>(grid, stream, a);
+      else launch_group<64, 16>(grid, stream, a);
+    }
   } else {
-    if (GM == 1) SKV_DEC(64, 1); else if (GM == 2) SKV_DEC(64, 2);
-    else if (GM == 4) SKV_DEC(64, 4); else if (GM == 8) SKV_DEC(64, 8);
-    else SKV_DEC(64, 16);
+    const int64_t n_groups = static_cast<int64_t>(B) * H_kv;
+    const int64_t per_group = (static_cast<int64_t>(num_splits) * G + kWaveBlock - 1) / kWaveBlock;
+    SKV_REQUIRE(per_group * (n_groups + kXcds) < 0x7fffffffLL,
+                "sparse_paged_decode: grid too large");
+    if (page_size == 16) {
+      if (D == 128) launch_wave<128, 16>(stream, a, n_groups);
+      else launch_wave<64, 16>(stream, a, n_groups);
+    } else {
+      if (D == 128) launch_wave<128, 0>(stream, a, n_groups);
+      else launch_wave<64, 0>(stream, a, n_groups);
+    }
   }
-#undef SKV_DEC
   SKV_CHECK_LAUNCH();
 }

@@ -68,6 +68,8 @@ class SparseDecoder:
         self.scores = torch.empty((B, self.H_sel, bt_ld), dtype=f32, device=dev)
         self.sel_idx = torch.empty((B, self.H_sel, self.k_cap), dtype=i32, device=dev)
         self.sel_cnt = torch.empty((B, self.H_sel), dtype=i32, device=dev)
+        self.sel_blk = torch.empty((B, self.H_sel, self.k_cap), dtype=i32, device=dev)
+        self.use_sel_blk = True
         self.o_part = torch.empty((B, H_q, num_splits, D), dtype=f32, device=dev)
         self.lse_part = torch.empty((B, H_q, num_splits), dtype=f32, device=dev)
         self.out = torch.empty((B, H_q, D), dtype=f32, device=dev)
@@ -104,13 +106,16 @@ class SparseDecoder:
                        self.scratch, self.scale, self.decay, self.bos, self.eos,
                        stream=stream)
 
-    def select(self, seq_lens, stream=None):
+    def select(self, seq_lens, block_table=None, stream=None):
+        blk = self.sel_blk if (self.use_sel_blk and block_table is not None) else None
         page_topk(self.scores, seq_lens, self.P, self.topk_pages, self.sel_idx,
-                  self.sel_cnt, self.topk_frac, self.bos, self.eos, stream=stream)
+                  self.sel_cnt, self.topk_frac, self.bos, self.eos,
+                  block_table=block_table, sel_blk=blk, stream=stream)
 
     def attend(self, q, kv_cache, block_table, seq_lens, stream=None):
         sparse_paged_decode(q, kv_cache, block_table, seq_lens, self.sel_idx,
                             self.sel_cnt, self.scale, self.o_part, self.lse_part,
+                            sel_blk=self.sel_blk if self.use_sel_blk else None,
                             stream=stream)
 
     def merge(self, stream=None):
@@ -126,7 +131,7 @@ class SparseDecoder:
             self.accumulate(q, kv_cache, block_table, seq_lens, stream)
         else:
             self.score(q, block_table, seq_lens, stream)
-        self.select(seq_lens, stream)
+        self.select(seq_lens, block_table, stream)
         self.attend(q, kv_cache, block_table, seq_lens, stream)
         self.merge(stream)
         return self.out, self.lse

@@ -50,6 +50,7 @@ def poison(dec):
         t.fill_(float("nan"))
     dec.sel_idx.fill_(-7)
     dec.sel_cnt.fill_(-7)
+    dec.sel_blk.fill_(-7)
 
 
 def bits(t):
@@ -145,6 +146,15 @@ def check_selection_exact(gpu_idx, gpu_cnt, scores_rows, N_rows, topk, frac,
         assert got == want, f"row {r}: selection differs from oracle on GPU scores"
 
 
+def check_sel_blk(sel_blk, sel_idx, block_table):
+    """sel_blk [B, H_sel, k_cap] holds block_table[b, p] of each selected p."""
+    B = sel_idx.shape[0]
+    for b in range(B):
+        idx = sel_idx[b]
+        want = np.where(idx >= 0, block_table[b][np.clip(idx, 0, None)], -1)
+        assert np.array_equal(sel_blk[b], want), f"request {b}: sel_blk differs"
+
+
 def _window(N, bos, eos):
     lo = min(bos, N)
     hi = max(N - eos, 0)
@@ -167,14 +177,14 @@ def check_selection_vs_oracle(gpu_rows, oracle_scores_rows, N_rows, topk, frac,
         assert 0 < m < len(cand), f"row {r}: mismatch with no boundary"
         a, b = s[cand[m - 1]], s[cand[m]]
         if token_level:
-            bound_ok = abs(a - b) <= 2.0 ** (np.floor(np.log2(abs(a))) - 7)
+            bound_ok = abs(a - b) <= 2.0 ** (np.floor(np.log2(max(abs(a), 2.0 ** -133))) - 7)
         else:
             den = max(abs(a), abs(b))
             bound_ok = den == 0 or abs(a - b) / den < PAGE_GAP_REL
         assert bound_ok, f"row {r}: selection differs away from a near tie"
         assert len(got) == len(want), f"row {r}: wrong count"
         gs = set(got)
-        band = (2.0 ** (np.floor(np.log2(abs(a))) - 7) if token_level
+        band = (2.0 ** (np.floor(np.log2(max(abs(a), 2.0 ** -133))) - 7) if token_level
                 else PAGE_GAP_REL * max(abs(a), abs(b)))
         for p in range(n):
             if p < lo or p >= hi:
@@ -208,13 +218,14 @@ def check_attention(gpu_out, gpu_lse, q, cache_bits, bt, sl, rows_sel, G, scale)
     return worst
 
 
-def check_partials(o_part, lse_part, q, cache_bits, bt, sl, rows_sel, G, scale):
-    """Split s of a row holds entries [s*c, (s+1)*c), c = ceil(cnt/splits)."""
+def check_partials(o_part, lse_part, q, cache_bits, bt, sl, rows_sel, G, scale,
+                   k_cap):
+    """Split s of a row holds entries [s*c, (s+1)*c), c = ceil(k_cap/splits)."""
     B, H_q, ns, D = o_part.shape
+    c = -(-k_cap // ns)
     for b in range(B):
         for i in range(H_q):
             pages = list(rows_sel[b][i])
-            c = -(-len(pages) // ns)
             for s in range(ns):
                 chunk = pages[s * c:(s + 1) * c] if c else []
                 o, lse = oracle.attend(q[b, i], cache_bits, i // G, bt[b], sl[b],

@@ -14,7 +14,7 @@ from sparse_kv_cache_amd.decode import SparseDecoder
 from parity import (bits, check_attention, check_partials, check_scores,
                     check_selection_exact, check_selection_vs_oracle,
                     check_stats, dev, per_head_rows, poison, say,
-                    selection_rows, bf16_bits_apart)
+                    selection_rows, bf16_bits_apart, check_sel_blk)
 
 pytestmark = pytest.mark.gpu
 
@@ -51,10 +51,18 @@ def run_page_case(wl, cache_cpu, q_cpu, exact_ties=False):
     d.k_min.fill_(float("nan")); d.k_max.fill_(float("nan")); d.k_mean.fill_(float("nan"))
     d.rebuild_stats(cache, bt, sl)
     d.score(q, bt, sl)
-    d.select(sl)
+    d.select(sl, bt)
     d.attend(q, cache, bt, sl)
     d.merge()
     torch.cuda.synchronize()
+    # the same decode through the block table instead of the selection's ids
+    o_with = d.out.clone()
+    d.use_sel_blk = False
+    d.out.fill_(float("nan"))
+    d.attend(q, cache, bt, sl)
+    d.merge()
+    torch.cuda.synchronize()
+    assert torch.equal(o_with, d.out), "decode differs with / without sel_blk"
 
     cb = bits(cache)
     qd = q_cpu.double().numpy()
@@ -73,6 +81,7 @@ def run_page_case(wl, cache_cpu, q_cpu, exact_ties=False):
     rowsN = np.repeat(N, wl.H_q)
     check_selection_exact(sel_idx, sel_cnt, gs.reshape(-1, wl.bt_ld), rowsN,
                           wl.topk_pages, wl.topk_frac, wl.bos, wl.eos)
+    check_sel_blk(d.sel_blk.cpu().numpy(), d.sel_idx.cpu().numpy(), wl.block_table)
     # end to end: oracle statistics and scores in float64
     ref_scores = oracle.page_score(qd, *st, wl.block_table, wl.seq_lens, wl.P,
                                    wl.w_avg, wl.w_peak)
@@ -84,7 +93,7 @@ def run_page_case(wl, cache_cpu, q_cpu, exact_ties=False):
     # attention over the GPU's own selection
     per = per_head_rows(rows, wl.B, wl.H_q, wl.H_q)
     check_partials(d.o_part.cpu().numpy(), d.lse_part.cpu().numpy(), qd, cb,
-                   wl.block_table, wl.seq_lens, per, wl.G, wl.softmax_scale)
+                   wl.block_table, wl.seq_lens, per, wl.G, wl.softmax_scale, d.k_cap)
     worst = check_attention(d.out.cpu().numpy(), d.lse.cpu().numpy(), qd, cb,
                             wl.block_table, wl.seq_lens, per, wl.G,
                             wl.softmax_scale)
@@ -223,7 +232,7 @@ def test_token_level_step_teacher_forced():
         assert np.array_equal(bits(cache), pre_cache)
         assert np.array_equal(bits(d.hh), pre_hh)
         d.accumulate(q, cache, bt, sl)
-        d.select(sl)
+        d.select(sl, bt)
         d.attend(q, cache, bt, sl)
         d.merge()
         torch.cuda.synchronize()
@@ -250,7 +259,7 @@ def test_token_level_step_teacher_forced():
         per = per_head_rows(rows, B, H_q, H_kv)
         check_partials(d.o_part.cpu().numpy(), d.lse_part.cpu().numpy(), qd,
                        bits(cache), wl.block_table, sl_np, per, H_q // H_kv,
-                       wl.softmax_scale)
+                       wl.softmax_scale, d.k_cap)
         check_attention(d.out.cpu().numpy(), d.lse.cpu().numpy(), qd, bits(cache),
                         wl.block_table, sl_np, per, H_q // H_kv, wl.softmax_scale)
         say(f"  step {step}: hh ulps off max {apart.max()}, "

@@ -16,7 +16,7 @@ from sparse_kv_cache_amd.decode import SparseDecoder
 from parity import (bits, bf16_bits_apart, check_attention, check_partials,
                     check_scores, check_selection_exact,
                     check_selection_vs_oracle, check_stats, dev, per_head_rows,
-                    poison, say, selection_rows, sub_batch)
+                    poison, say, selection_rows, sub_batch, check_sel_blk)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,6 +39,8 @@ def page_level_parity(wl, cache, q_cpu, seq_lens_np, rows, d, partial_heads=4):
     sel_cnt = d.sel_cnt.cpu().numpy()[rows].reshape(-1)
     check_selection_exact(sel_idx, sel_cnt, gs.reshape(-1, wl.bt_ld), rowsN,
                           wl.topk_pages, wl.topk_frac, wl.bos, wl.eos)
+    check_sel_blk(d.sel_blk.cpu().numpy()[rows], d.sel_idx.cpu().numpy()[rows],
+                  wl.block_table[list(rows)])
     ref_scores = oracle.page_score(qd, *st, bt, sl, wl.P, wl.w_avg, wl.w_peak)
     sel_rows = selection_rows(sel_idx, sel_cnt)
     ex = check_selection_vs_oracle(sel_rows, ref_scores.reshape(-1, wl.bt_ld), rowsN,
@@ -46,7 +48,8 @@ def page_level_parity(wl, cache, q_cpu, seq_lens_np, rows, d, partial_heads=4):
     per = per_head_rows(sel_rows, len(rows), wl.H_q, wl.H_q)
     hs = slice(0, partial_heads)
     check_partials(d.o_part.cpu().numpy()[rows][:, hs], d.lse_part.cpu().numpy()[rows][:, hs],
-                   qd[:, hs], cb, bt, sl, [p[hs] for p in per], wl.G, wl.softmax_scale)
+                   qd[:, hs], cb, bt, sl, [p[hs] for p in per], wl.G, wl.softmax_scale,
+                   d.k_cap)
     worst = check_attention(d.out.cpu().numpy()[rows], d.lse.cpu().numpy()[rows], qd,
                             cb, bt, sl, per, wl.G, wl.softmax_scale)
     return worst, ex
@@ -127,7 +130,7 @@ def test_h2o_token_sequence():
         torch.cuda.synchronize()
         pre_cache, pre_hh = bits(cache), bits(d.hh).copy()
         d.accumulate(q, cache, bt, sl)
-        d.select(sl)
+        d.select(sl, bt)
         d.attend(q, cache, bt, sl)
         d.merge()
         torch.cuda.synchronize()
