@@ -13,11 +13,14 @@ Inputs are seeded synthetic tensors already resident in HBM.  To measure
 HBM rather than the 256 MB memory-side cache, the timed steps rotate over R
 replicas of the workload (separate caches, statistics and buffers, like the
 layers of a model), so each step's data was last touched R-1 steps earlier.
+The timed steps are one HIP graph replay (exactly K steps), bracketed by HIP
+events and device synchronisation.
 
 Prints ONE JSON line: steps/s (value), effective HBM GB/s of the step and of
-each kernel (algorithmic bytes / time, HIP events on the launch stream), the
-roofline entry of the dominant kernel, and the float64 oracle timed on a
-bounded sample on the host cores (cpu_baseline).
+each kernel (algorithmic bytes / kernel time; each kernel is timed alone,
+launched back to back over the replicas in a graph, with HIP events on the
+launch stream), the roofline entry of the decode kernel, and the float64
+oracle timed on a bounded sample on the host cores (cpu_baseline).
 """
 from __future__ import annotations
 
@@ -45,6 +48,8 @@ def parse():
                     help="rotation depth (0 = enough to exceed 1 GiB per cycle)")
     ap.add_argument("--splits", type=int, default=0, help="override num_splits")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="enqueue kernel by kernel instead of replaying HIP graphs")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     return ap.parse_args()
 
@@ -234,54 +239,81 @@ def main():
         (["h2o_accumulate"] if token_level else ["page_score"]) + \
         ["page_topk", "sparse_paged_decode", "lse_merge"]
 
-    def run_step(i, evs=None):
+    def enqueue(i, name):
+        """Enqueue kernel `name` of step i (replica i % R, sequence step i % steps)."""
         r = i % R
         d, c = decs[r], caches[r]
         s = i % wl.steps
         sl = seq_steps[s]
-        rec = (lambda k: evs[k].record()) if evs is not None else (lambda k: None)
-        k = 0
-        rec(k); k += 1
-        if wl.steps > 1:
+        if name == "pagestats_update":
             kn, vn = new_kv[s % len(new_kv)]
             d.append(c, bt, sl, kn, vn)
-            rec(k); k += 1
-        if token_level:
+        elif name == "h2o_accumulate":
             d.accumulate(q, c, bt, sl)
-        else:
+        elif name == "page_score":
             d.score(q, bt, sl)
-        rec(k); k += 1
-        d.select(sl, bt)
-        rec(k); k += 1
-        d.attend(q, c, bt, sl)
-        rec(k); k += 1
-        d.merge()
-        rec(k); k += 1
+        elif name == "page_topk":
+            d.select(sl, bt)
+        elif name == "sparse_paged_decode":
+            d.attend(q, c, bt, sl)
+        else:
+            d.merge()
 
-    for i in range(args.warmup):
-        run_step(i)
+    def run_steps(first, count):
+        for i in range(first, first + count):
+            for n in names:
+                enqueue(i, n)
+
+    def captured(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    # The step sequence is captured into HIP graphs (one launch for the whole
+    # warm-up, one for the whole timed region): Python's per-call submission
+    # cost would otherwise leave the GPU idle between the short kernels.
+    if args.no_graph:
+        run_steps(0, args.warmup)
+    else:
+        g_warm = captured(lambda: run_steps(0, args.warmup)) if args.warmup else None
+        g_timed = captured(lambda: run_steps(args.warmup, args.steps))
+        if g_warm is not None:
+            g_warm.replay()
     torch.cuda.synchronize()
 
-    nev = len(names) + 1
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)]
-              for _ in range(args.steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        run_step(args.warmup + i, events[i])
+    e0.record()
+    if args.no_graph:
+        run_steps(args.warmup, args.steps)
+    else:
+        g_timed.replay()
+    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_kernel_ms = {n: 0.0 for n in names}
-    step_ms = 0.0
-    for ev in events:
-        for j, n in enumerate(names):
-            per_kernel_ms[n] += ev[j].elapsed_time(ev[j + 1])
-        step_ms += ev[0].elapsed_time(ev[-1])
-    per_kernel_ms = {n: v / args.steps for n, v in per_kernel_ms.items()}
-    gpu_ms = step_ms / args.steps
+    gpu_ms = e0.elapsed_time(e1) / args.steps
     ms_per_step = wall * 1000.0 / args.steps
 
-    # algorithmic bytes from the selections the last step produced
+    # Per-kernel durations: each kernel alone, launched back to back over the
+    # replicas inside one graph, timed with HIP events around the replay.
+    per_kernel_ms = {}
+    base = args.warmup + args.steps
+    reps = max(2 * R, 16)
+    for n in names:
+        g = captured(lambda: [enqueue(base + j, n) for j in range(reps)])
+        g.replay()
+        k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        k0.record()
+        g.replay()
+        k1.record()
+        torch.cuda.synchronize()
+        per_kernel_ms[n] = k0.elapsed_time(k1) / reps
+        del g
+
+    # algorithmic bytes from the selections of the last timed step's replica
     last = (args.warmup + args.steps - 1)
     d = decs[last % R]
     sl_last = wl.seq_lens_at(last % wl.steps)

@@ -8,9 +8,10 @@
 // window [bos, S - eos); for a query group the group-mean query is used.
 //
 // Two launches over (token chunk, request):
-//   1. logits l_t = scale * log2(e) * qbar . k_t for every kv head, one token
-//      row of H_kv * D bf16 read with 16-byte loads (D/8 lanes per head row);
-//      the chunk's (max, sum 2^(l - max)) per head go to scratch.
+//   1. logits l_t = scale * log2(e) * qbar . k_t for every kv head over
+//      64-token chunks, one token row of H_kv * D bf16 read with 16-byte loads
+//      (D/8 lanes per head row); the chunk's (max, sum 2^(l - max)) per head go
+//      to scratch.
 //   2. merge of the chunk partials into (M, Z) per head, then per token:
 //      p = 2^(l - M) / Z, stored bf16(p), hh <- bf16(bf16(p) + decay * hh)
 //      (one fp32 fma, then round-to-nearest-even), and the new hh value is
@@ -21,7 +22,8 @@
 
 namespace {
 
-constexpr int kChunk = 256;     // tokens per block
+constexpr int kChunk = 64;      // tokens per block of the logits pass
+constexpr int kUpd = 256;       // tokens per block of the update pass
 constexpr int kUnroll = 8;      // row loads in flight per lane
 
 __device__ __forceinline__ void window(int S, int64_t bt_ld, int bos, int eos,
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(256) void h2o_update_kernel(
   const int c = blockIdx.x;
   int ntok, lo, hi;
   window(seq_lens[b], bt_ld, bos, eos, &ntok, &lo, &hi);
-  const int t0 = c * kChunk;
+  const int t0 = c * kUpd;
   if (t0 >= ntok) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -214,6 +216,7 @@ extern "C" int h2o_accumulate(const float* q, int B, int H_q, int H_kv, int D,
               (long long)scratch_floats, (long long)need);
   if (B == 0) { skv::clear_error(); return SKV_OK; }
   const int nch = static_cast<int>(nchunks(bt_ld));
+  const int nupd = static_cast<int>((bt_ld + kUpd - 1) / kUpd);
   float* logits = scratch;
   float* part = scratch + static_cast<int64_t>(B) * H_kv * bt_ld;
   // decay is applied as its bf16 value, which is exact for 0.984375
@@ -230,7 +233,8 @@ extern "C" int h2o_accumulate(const float* q, int B, int H_q, int H_kv, int D,
                        H_kv, H_q / H_kv, kv_cache, block_table, bt_ld, seq_lens,
                        reserved_bos, reserved_eos, scale_log2, logits, part, nch);
   const size_t sm2 = sizeof(float) * 2 * static_cast<size_t>(H_kv);
-  hipLaunchKernelGGL(h2o_update_kernel, grid, dim3(kChunk), sm2, stream, H_kv,
+  hipLaunchKernelGGL(h2o_update_kernel, dim3(static_cast<unsigned>(nupd), static_cast<unsigned>(B)),
+                     dim3(kUpd), sm2, stream, H_kv,
                      block_table, bt_ld, seq_lens, reserved_bos, reserved_eos,
                      decay_b, hh_score, scores, score_ld, logits, part, nch);
   SKV_CHECK_LAUNCH();

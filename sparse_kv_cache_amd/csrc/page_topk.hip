@@ -12,11 +12,12 @@
 // thread.  A most-significant-digit radix select finds the key prefix of the
 // m-th best candidate: the bits every candidate shares are skipped (block
 // OR / AND), each pass histograms the next 8 bits of the keys still matching
-// the prefix (LDS atomics; one wave finds the digit), and the select stops
-// early once the chosen bin is taken whole.  Keys above the prefix are taken;
-// among those equal to it the lowest indices are taken, ranked by a
-// block-wide prefix count in index order.  A second prefix count over the
-// final flags writes the indices in ascending order with no sort.
+// the prefix into its own LDS histogram (atomics; every wave then finds the
+// digit itself, so a pass costs one barrier), and the select stops as soon as
+// the chosen bin is taken whole.  Keys above the prefix are taken; when equal
+// keys must be split, the lowest indices are taken, ranked by a block-wide
+// prefix count in index order.  A prefix count over the final flags writes
+// the indices in ascending order with no sort.
 #include <limits.h>
 
 #include "skv_device.h"
@@ -38,10 +39,13 @@ __global__ __launch_bounds__(BLOCK) void page_topk_kernel(
     int32_t* __restrict__ sel_cnt, int k_cap, const int32_t* __restrict__ bt,
     int64_t bt_ld, int32_t* __restrict__ sel_blk) {
   constexpr int NW = BLOCK / 64;
-  __shared__ int hist[256];
+  constexpr int kBits = 8;                       // digit width
+  constexpr int kBins = 1 << kBits;
+  constexpr int kPasses = 4;                     // 32 / 8
+  constexpr int kPerLane = kBins / 64;           // bins a lane scans
+  __shared__ __align__(16) int hist[kPasses][kBins];   // one histogram per pass
   __shared__ int scan_smem[NW + 1];
   __shared__ uint32_t s_or[NW], s_and[NW];
-  __shared__ int s_digit, s_remaining, s_bin;
 
   const int64_t row = blockIdx.x;
   const int b = static_cast<int>(row / H_sel);
@@ -83,11 +87,32 @@ __global__ __launch_bounds__(BLOCK) void page_topk_kernel(
       key[i] = (p >= lo && p < hi) ? order_key(srow[p]) : 0u;
     }
   }
+  // block ids of this thread's entries, fetched alongside the keys
+  int32_t bid[ITEMS];
+  if (sel_blk != nullptr) {
+    const int32_t* btr = bt + static_cast<int64_t>(b) * bt_ld;
+    if (((bt_ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(bt) & 15) == 0) &&
+        base + ITEMS <= N && base + ITEMS <= bt_ld) {
+#pragma unroll
+      for (int i = 0; i < ITEMS; i += 4) {
+        const int4 v = *reinterpret_cast<const int4*>(btr + base + i);
+        bid[i] = v.x; bid[i + 1] = v.y; bid[i + 2] = v.z; bid[i + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < ITEMS; ++i) {
+        const int p = base + i;
+        bid[i] = (p < N && p < bt_ld) ? btr[p] : -1;
+      }
+    }
+  }
+  for (int j = tid; j < kPasses * kBins; j += BLOCK) (&hist[0][0])[j] = 0;
 
   // Selection state: candidates whose (key & pmask) exceeds prefix are taken;
   // among those equal to prefix under pmask, the r_eq lowest indices.
   uint32_t prefix, pmask;
   int r_eq;
+  bool ties = false;                   // r_eq < number equal to the prefix
   if (want == 0) {
     prefix = 0xffffffffu; pmask = 0xffffffffu; r_eq = 0;   // reserved only
   } else if (want >= ncand) {
@@ -107,73 +132,86 @@ __global__ __launch_bounds__(BLOCK) void page_topk_kernel(
       a &= __shfl_xor(a, off);
     }
     if (lane == 0) { s_or[wave] = o; s_and[wave] = a; }
-    __syncthreads();
+    __syncthreads();                   // also orders the histogram clearing
     o = 0u; a = 0xffffffffu;
 #pragma unroll
     for (int w = 0; w < NW; ++w) { o |= s_or[w]; a &= s_and[w]; }
-    const uint32_t diff = o ^ a;          // bits that vary among candidates
-    prefix = a & ~diff;                   // (bits outside diff's span agree)
+    const uint32_t diff = o ^ a;       // bits that vary among candidates
     int top = diff ? 31 - __clz(diff) : -1;
     pmask = top >= 0 ? ~((2u << top) - 1u) : 0xffffffffu;
     if (top == 31) pmask = 0u;
-    prefix &= pmask;
+    prefix = a & pmask;
     int remaining = want;
-    bool done = false;
-    while (!done && top >= 0) {
-      const int shift = top >= 7 ? top - 7 : 0;
+    int bin = ncand;                   // entries matching the prefix so far
+    int pass = 0;
+    while (remaining < bin && top >= 0) {
+      const int shift = top >= kBits - 1 ? top - (kBits - 1) : 0;
       const int width = top - shift + 1;
-      const uint32_t dmask = (width == 32) ? 0xffffffffu : ((1u << width) - 1u);
-      for (int j = tid; j < 256; j += BLOCK) hist[j] = 0;
-      __syncthreads();
+      const uint32_t dmask = (1u << width) - 1u;
+      int* hp = hist[pass];
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i) {
         const int p = base + i;
         if (p >= lo && p < hi && (key[i] & pmask) == prefix)
-          atomicAdd(&hist[(key[i] >> shift) & dmask], 1);
+          atomicAdd(&hp[(key[i] >> shift) & dmask], 1);
       }
       __syncthreads();
-      if (tid < 64) {
-        int cs[4];
+      // every wave finds the digit itself: no broadcast, no second barrier.
+      // Lane l scans bins [kPerLane * l, kPerLane * (l + 1)).
+      int cs[kPerLane];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) cs[j] = hist[4 * lane + j];
-        const int sum = cs[0] + cs[1] + cs[2] + cs[3];
-        int suf = sum;                      // entries in bins of lanes >= lane
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const int y = __shfl_down(suf, off);
-          if (lane + off < 64) suf += y;
-        }
-        int above = suf - sum;              // entries in higher digits
-#pragma unroll
-        for (int j = 3; j >= 0; --j) {
-          if (above < remaining && above + cs[j] >= remaining) {
-            s_digit = 4 * lane + j;
-            s_remaining = remaining - above;
-            s_bin = cs[j];
-          }
-          above += cs[j];
-        }
+      for (int j = 0; j < kPerLane; j += 4) {
+        const int4 v = *reinterpret_cast<const int4*>(&hp[kPerLane * lane + j]);
+        cs[j] = v.x; cs[j + 1] = v.y; cs[j + 2] = v.z; cs[j + 3] = v.w;
       }
-      __syncthreads();
-      const uint32_t dg = static_cast<uint32_t>(s_digit);
-      remaining = s_remaining;
+      int sum = 0;
+#pragma unroll
+      for (int j = 0; j < kPerLane; ++j) sum += cs[j];
+      int suf = sum;                   // entries in bins of lanes >= lane
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_down(suf, off);
+        if (lane + off < 64) suf += y;
+      }
+      int above = suf - sum;           // entries in higher digits
+      int my_digit = 0, my_rem = 0, my_bin = 0;
+      bool found = false;
+#pragma unroll
+      for (int j = kPerLane - 1; j >= 0; --j) {
+        if (above < remaining && above + cs[j] >= remaining) {
+          my_digit = kPerLane * lane + j;
+          my_rem = remaining - above;
+          my_bin = cs[j];
+          found = true;
+        }
+        above += cs[j];
+      }
+      const unsigned long long ball = __ballot(found);
+      const int src = __ffsll(static_cast<long long>(ball)) - 1;
+      const uint32_t dg = static_cast<uint32_t>(__shfl(my_digit, src));
+      remaining = __shfl(my_rem, src);
+      bin = __shfl(my_bin, src);
       prefix |= dg << shift;
       pmask |= dmask << shift;
-      done = (remaining == s_bin);          // the whole bin is taken
       top = shift - 1;
-      __syncthreads();
+      ++pass;
     }
     r_eq = remaining;
+    ties = remaining < bin;            // fully resolved with equal keys left
   }
 
-  int eq = 0;
+  // ranks among the entries equal to the prefix (only needed for ties)
+  int er = 0;
+  if (ties) {
+    int eq = 0;
 #pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const int p = base + i;
-    eq += (p >= lo && p < hi && (key[i] & pmask) == prefix) ? 1 : 0;
+    for (int i = 0; i < ITEMS; ++i) {
+      const int p = base + i;
+      eq += (p >= lo && p < hi && (key[i] & pmask) == prefix) ? 1 : 0;
+    }
+    int total_eq;
+    er = skv::block_exclusive_scan(eq, &total_eq, scan_smem);
   }
-  int total_eq;
-  int er = skv::block_exclusive_scan(eq, &total_eq, scan_smem);
 
   uint32_t flags = 0u;
   int cnt = 0;
@@ -193,13 +231,12 @@ __global__ __launch_bounds__(BLOCK) void page_topk_kernel(
   int pos = skv::block_exclusive_scan(cnt, &total, scan_smem);
   int32_t* out = sel_idx + row * k_cap;
   int32_t* bout = sel_blk != nullptr ? sel_blk + row * k_cap : nullptr;
-  const int32_t* btr = bout != nullptr ? bt + static_cast<int64_t>(b) * bt_ld : nullptr;
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
     if (flags & (1u << i)) {
       if (pos < k_cap) {
         out[pos] = base + i;
-        if (bout != nullptr) bout[pos] = base + i < bt_ld ? btr[base + i] : -1;
+        if (bout != nullptr) bout[pos] = bid[i];
       }
       ++pos;
     }

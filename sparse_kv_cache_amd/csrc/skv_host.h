@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/sparsekv.h"
@@ -56,6 +57,12 @@ static inline float skv_host_round_bf16(float f) {
   float r;
   memcpy(&r, &u, sizeof r);
   return r;
+}
+
+// A tuning switch read from the environment (set and not "0").
+static inline bool skv_env_flag(const char* name) {
+  const char* v = getenv(name);
+  return v != nullptr && v[0] != '\0' && !(v[0] == '0' && v[1] == '\0');
 }
 
 static inline bool skv_supported_page_size(int p) {

@@ -14,8 +14,8 @@
 // softmax state (max, sum, 8-dim accumulator) for its own rows; states are
 // merged across row slots (lane shuffles) and waves (LDS) once, at the end.
 // Exponentials are base 2 with the scale pre-multiplied by log2(e).  Loads run
-// NPIPE groups ahead of the arithmetic (packed bf16 in registers, unpacked on
-// use), so each wave keeps up to NPIPE x 2 x 4 KB of K/V in flight.
+// one group ahead of the arithmetic (packed bf16 in registers, unpacked on
+// use), so each wave keeps up to 2 x 2 x 4 KB of K/V in flight.
 //
 // Split s of a selection row holds its entries [s*c, min((s+1)*c, cnt)) with
 // c = ceil(k_cap / num_splits), so a block can fetch its chunk without first
@@ -41,9 +41,6 @@ namespace {
 
 constexpr int kMaxEnt = 256;          // LDS entries per round (group kernel)
 constexpr int kXcds = 8;              // accelerator complex dies of an MI355X
-#ifndef SKV_DECODE_PIPE
-#define SKV_DECODE_PIPE 2             // groups of 16 rows in flight per wave
-#endif
 #ifndef SKV_DECODE_WPE
 #define SKV_DECODE_WPE 3              // waves per SIMD the wave kernel is sized for
 #endif
@@ -94,6 +91,81 @@ __device__ __forceinline__ void attend_rows(const float (&qq)[8],
   m = mx;
 }
 
+// The same fold with the query split into bf16 hi + lo halves (q ~= hi + lo
+// to about 16 significant bits): each dot product runs on the packed bf16
+// key words with v_dot2c_f32_bf16 (fp32 accumulation, exact bf16 products),
+// so keys are never unpacked.  `full` (wave-uniform) says every row is valid.
+typedef __bf16 skv_bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(skv_bf16x2, a),
+                                         __builtin_bit_cast(skv_bf16x2, b), c, false);
+}
+
+__device__ __forceinline__ void split_query(const float (&qq)[8], uint32_t (&qh)[4],
+                                            uint32_t (&ql)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint16_t h0 = skv::f32_to_bf16(qq[2 * i]), h1 = skv::f32_to_bf16(qq[2 * i + 1]);
+    const uint16_t l0 = skv::f32_to_bf16(qq[2 * i] - skv::bf16_to_f32(h0));
+    const uint16_t l1 = skv::f32_to_bf16(qq[2 * i + 1] - skv::bf16_to_f32(h1));
+    qh[i] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+    ql[i] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
+  }
+}
+
+template <int LPR, int NL>
+__device__ __forceinline__ void attend_rows_split(const uint32_t (&qh)[4],
+                                                  const uint32_t (&ql)[4],
+                                                  const uint4 (&K)[NL],
+                                                  const uint4 (&V)[NL],
+                                                  const bool (&ok)[NL], bool full,
+                                                  float& m, float& l,
+                                                  float (&acc)[8]) {
+  float lg[NL];
+  float mx = m;
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    float d = 0.0f;
+    d = dot2(K[j].x, qh[0], d); d = dot2(K[j].x, ql[0], d);
+    d = dot2(K[j].y, qh[1], d); d = dot2(K[j].y, ql[1], d);
+    d = dot2(K[j].z, qh[2], d); d = dot2(K[j].z, ql[2], d);
+    d = dot2(K[j].w, qh[3], d); d = dot2(K[j].w, ql[3], d);
+    d = skv::group_sum<LPR>(d);
+    lg[j] = ok[j] ? d : -INFINITY;
+    mx = fmaxf(mx, lg[j]);
+  }
+  if (mx == -INFINITY) return;            // none of this lane's rows yet
+  const float alpha = __builtin_amdgcn_exp2f(m - mx);   // 0 while m == -inf
+  float pj[NL];
+  float ps = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NL; ++j) { pj[j] = __builtin_amdgcn_exp2f(lg[j] - mx); ps += pj[j]; }
+  l = fmaf(l, alpha, ps);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+  if (full) {
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      float v[8];
+      skv::unpack8(V[j], v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(pj[j], v[i], acc[i]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      // masked rows: zero the packed words (never multiply a placeholder row)
+      const uint4 vw = ok[j] ? V[j] : make_uint4(0, 0, 0, 0);
+      float v[8];
+      skv::unpack8(vw, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(pj[j], v[i], acc[i]);
+    }
+  }
+  m = mx;
+}
+
 // Merge the online-softmax states of the 64/LPR row slots of a wave (lanes
 // c, c + LPR, ...); afterwards every lane holds the wave's state for its dims.
 template <int LPR>
@@ -138,7 +210,7 @@ __device__ __forceinline__ Chunk split_chunk(int cnt, int k_cap, int num_splits,
 // share a block, and all blocks of the (request, kv head) go to one XCD:
 // pages several heads selected are fetched through one L2 at about the same
 // time.
-template <int D, int WB, int NPIPE, int PFIX>
+template <int D, int WB, int PFIX>
 __global__ __launch_bounds__(WB * 64)
 __attribute__((amdgpu_waves_per_eu(PFIX == 16 ? SKV_DECODE_WPE16 : SKV_DECODE_WPE)))
 void sparse_decode_wave_kernel(
@@ -191,6 +263,8 @@ void sparse_decode_wave_kernel(
     qq[4] = qb.x * scale_log2; qq[5] = qb.y * scale_log2;
     qq[6] = qb.z * scale_log2; qq[7] = qb.w * scale_log2;
   }
+  uint32_t qh[4], ql[4];
+  split_query(qq, qh, ql);
   float m = -INFINITY, l = 0.0f, acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
@@ -216,7 +290,7 @@ void sparse_decode_wave_kernel(
       my_nv = n < P ? n : P;
     }
     const int ngroups = (nw + epg - 1) / epg;
-    auto load = [&](int grp, uint4 (&K)[NL], uint4 (&V)[NL], bool (&ok)[NL]) {
+    auto load = [&](int grp, uint4 (&K)[NL], uint4 (&V)[NL], bool (&ok)[NL], bool& full) {
       if constexpr (PFIX == 16) {
         // one page per group: its block id and row count are wave-uniform
         // (read from lane grp), so the row addresses are a scalar page base
@@ -224,6 +298,7 @@ void sparse_decode_wave_kernel(
         const int gc = grp < nw ? grp : 0;
         const int blk = __builtin_amdgcn_readlane(my_blk, gc);
         const int nv = grp < nw ? __builtin_amdgcn_readlane(my_nv, gc) : 0;
+        full = nv == 16;
         const uint16_t* kp = kv + static_cast<int64_t>(blk) * 16 * row_stride;
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
@@ -235,6 +310,7 @@ void sparse_decode_wave_kernel(
           V[j] = *reinterpret_cast<const uint4*>(base + v_off + off);
         }
       } else {
+      full = false;
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
         const int rr = slot + RPL * j;            // row in group, 0..15
@@ -253,31 +329,22 @@ void sparse_decode_wave_kernel(
       }
       }
     };
-    uint4 K0[NL], V0[NL], K1[NL], V1[NL], K2[NL], V2[NL];
-    bool o0[NL], o1[NL], o2[NL];
+    // Two groups in flight: while one is folded in, the next one's loads
+    // are outstanding; each refill is unconditional (past the end it reads
+    // placeholders) so the number of loads in flight stays static.
+    uint4 K0[NL], V0[NL], K1[NL], V1[NL];
+    bool o0[NL], o1[NL];
+    bool f0 = false, f1 = false;
     int grp = 0;
-    load(0, K0, V0, o0);
-    load(1, K1, V1, o1);
-    if constexpr (NPIPE >= 3) load(2, K2, V2, o2);
+    load(0, K0, V0, o0, f0);
+    load(1, K1, V1, o1, f1);
     while (grp < ngroups) {
-      if constexpr (NPIPE >= 3) {
-        attend_rows<LPR, NL>(qq, K0, V0, o0, m, l, acc);
-        if (++grp >= ngroups) break;
-        load(grp + 2, K0, V0, o0);
-        attend_rows<LPR, NL>(qq, K1, V1, o1, m, l, acc);
-        if (++grp >= ngroups) break;
-        load(grp + 2, K1, V1, o1);
-        attend_rows<LPR, NL>(qq, K2, V2, o2, m, l, acc);
-        if (++grp >= ngroups) break;
-        load(grp + 2, K2, V2, o2);
-      } else {
-        attend_rows<LPR, NL>(qq, K0, V0, o0, m, l, acc);
-        if (++grp >= ngroups) break;
-        load(grp + 1, K0, V0, o0);
-        attend_rows<LPR, NL>(qq, K1, V1, o1, m, l, acc);
-        if (++grp >= ngroups) break;
-        load(grp + 1, K1, V1, o1);
-      }
+      attend_rows_split<LPR, NL>(qh, ql, K0, V0, o0, f0, m, l, acc);
+      if (++grp >= ngroups) break;
+      load(grp + 1, K0, V0, o0, f0);
+      attend_rows_split<LPR, NL>(qh, ql, K1, V1, o1, f1, m, l, acc);
+      if (++grp >= ngroups) break;
+      load(grp + 1, K1, V1, o1, f1);
     }
   }
 
@@ -462,7 +529,7 @@ template <int D, int PFIX>
 void launch_wave(hipStream_t st, const Args& a, int64_t n_groups) {
   const int per_group = (a.num_splits * a.G + kWaveBlock - 1) / kWaveBlock;
   const int64_t blocks = kXcds * per_group * ((n_groups + kXcds - 1) / kXcds);
-  hipLaunchKernelGGL((sparse_decode_wave_kernel<D, kWaveBlock, SKV_DECODE_PIPE, PFIX>),
+  hipLaunchKernelGGL((sparse_decode_wave_kernel<D, kWaveBlock, PFIX>),
                      dim3(static_cast<unsigned>(blocks)), dim3(kWaveBlock * 64), 0, st,
                      a.q, a.H_q, a.H_kv, a.G, a.kv, a.num_blocks, a.P, a.bt, a.bt_ld,
                      a.seq_lens, a.sel_idx, a.sel_cnt, a.sel_blk, a.k_cap, a.scale_log2,

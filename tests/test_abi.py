@@ -120,7 +120,7 @@ def test_validation_rejects_null_pointers(lib):
 
 def test_scratch_size_query(lib):
     n = lib.h2o_scratch_floats(4, 8, 4352)
-    chunks = -(-4352 // 256)
+    chunks = -(-4352 // 64)
     assert n == 4 * 8 * 4352 + 4 * 8 * chunks * 2
     assert lib.h2o_scratch_floats(1, 0, 10) == -1
     assert skv.h2o_scratch_floats(4, 8, 4352) == n
