@@ -109,6 +109,42 @@ def kernel_bytes(wl, sel_idx, sel_cnt, seq_lens, num_splits, token_level):
     return out, upages
 
 
+# ------------------------------------------------------ measured traffic
+
+DECODE_SOURCES = ("sparse_kv_cache_amd/csrc/sparse_decode.hip",
+                  "sparse_kv_cache_amd/csrc/skv_device.h")
+
+
+def decode_source_hash():
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha1()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(workload):
+    """HBM bytes per decode launch from the committed counter summary of this
+    workload (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy's reading),
+    or None when there is none or the decode kernel's sources have changed
+    since the counters were taken."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    start = text.find("```json")
+    if start < 0:
+        return None
+    body = text[start + 7:text.find("```", start + 7)].strip()
+    rec = json.loads(body)
+    if rec.get("source_sha1") != decode_source_hash():
+        return None
+    return int(rec["traffic"])
+
+
 # ------------------------------------------------------------ cpu baseline
 
 def cpu_baseline(wl, cache_bits, q, seq_lens, seconds, token_level, hh_bits=None):
@@ -331,7 +367,7 @@ def main():
     a = kb[focus] / (per_kernel_ms[focus] * 1e-3) / 1e9
     roofline = {"kernel": focus, "bound": "hbm", "achieved": round(a, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(a / PEAK_HBM_GBPS, 4),
-                "traffic": None, "bytes_per_launch": kb[focus],
+                "traffic": profiled_traffic(wl.name), "bytes_per_launch": kb[focus],
                 "us_per_launch": round(per_kernel_ms[focus] * 1000, 2)}
 
     result = {
