@@ -247,6 +247,11 @@ void sparse_decode_wave_kernel(
   // count instead of after it.
   const int cap = (k_cap + num_splits - 1) / num_splits;
   const int start = s * cap;
+  // entries of this chunk that exist in the row: the last chunks of a row
+  // whose capacity is not a multiple of num_splits (or is below it) are
+  // shorter or empty, and nothing past the row's k_cap entries is read
+  int avail = k_cap - start;
+  avail = avail < 0 ? 0 : (avail > cap ? cap : avail);
   const int32_t* selr = sel_idx + qrow * k_cap + start;
   const int32_t* sblk = sel_blk != nullptr ? sel_blk + qrow * k_cap + start : nullptr;
   int cnt = sel_cnt[qrow];
@@ -275,9 +280,9 @@ void sparse_decode_wave_kernel(
   const int64_t v_off = num_blocks * P * row_stride;
   const int epg = 16 / P;
 
-  for (int w0 = 0; w0 < cap; w0 += 64) {
+  for (int w0 = 0; w0 < avail; w0 += 64) {
     int p = -1, sb = -1;
-    if (w0 + lane < cap) {
+    if (w0 + lane < avail) {
       p = selr[w0 + lane];
       if (sblk != nullptr) sb = sblk[w0 + lane];
     }

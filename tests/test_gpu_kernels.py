@@ -31,6 +31,8 @@ PAGE_CASES = [
     (8, 2, 32, 8, 128, 16, 64, 16, 0.0, 0, 1, 8, 1.0, 0.5),
     (9, 2, 12, 4, 64, 8, 25, 7, 0.3, 1, 1, 2, 1.0, 2.0),
     (10, 1, 6, 2, 128, 2, 80, 9, 0.0, 0, 1, 16, 1.0, 1.0),
+    # more splits than selection capacity: most chunks start past the row
+    (11, 2, 8, 2, 128, 16, 24, 4, 0.0, 0, 1, 32, 1.0, 1.0),
 ]
 
 
