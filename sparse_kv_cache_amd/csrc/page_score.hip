@@ -19,14 +19,14 @@
 // statistics (256 + 256 + 512 bytes at D = 128) are read by D/8 lanes with
 // 16-byte loads, so a wave covers 64/(D/8) pages per load and every byte of
 // statistics is read once for the whole query group, whose rows sit in LDS.
-// Groups larger than 8 are split over grid.y slices.
+// Groups larger than 8 are split into slices of 8 (grid.x = kv head x slice).
 #include "skv_device.h"
 #include "skv_host.h"
 
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kIter = 4;
+constexpr int kIter = 2;
 
 template <int D, int GS>
 __global__ __launch_bounds__(256) void page_score_kernel(
@@ -39,14 +39,16 @@ __global__ __launch_bounds__(256) void page_score_kernel(
   constexpr int LPR = D / 8;          // lanes per page-head
   constexpr int PPW = 64 / LPR;       // page-heads per wave load
   constexpr int TILE = kIter * kWaves * PPW;
+  // kv heads vary fastest in launch order: blocks dispatched together read
+  // neighbouring statistics rows (all heads of a page are contiguous)
   const int b = blockIdx.z;
   const int nslices = (G + GS - 1) / GS;
-  const int h = blockIdx.y / nslices;
-  const int g0 = (blockIdx.y % nslices) * GS;
+  const int h = blockIdx.x / nslices;
+  const int g0 = (blockIdx.x % nslices) * GS;
   const int S = seq_lens[b];
   int64_t N = (static_cast<int64_t>(S) + P - 1) / P;
   if (N > max_pages) N = max_pages;
-  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * TILE;
+  const int64_t p0 = static_cast<int64_t>(blockIdx.y) * TILE;
   if (p0 >= N) return;
 
   const int lane = threadIdx.x & 63;
@@ -71,8 +73,8 @@ __global__ __launch_bounds__(256) void page_score_kernel(
     me1[it] = *reinterpret_cast<const float4*>(kmean + off + 4);
   }
 
-  // (statistics loads are in flight) the group's query rows go to LDS (2 x 16-byte reads per head and page
-  // slot) so the registers go to loads in flight
+  // while the statistics loads are in flight, the group's query rows go to
+  // LDS, leaving the registers to those loads
   __shared__ __align__(16) float qs[GS][D];
   for (int i = threadIdx.x; i < GS * D; i += blockDim.x) {
     const int g = i / D, d = i % D;
@@ -140,7 +142,7 @@ extern "C" int page_score(const float* q, int B, int H_q, int H_kv, int D,
               "page_score: page_size must be 1, 2, 4, 8 or 16 (got %d)", page_size);
   SKV_REQUIRE(bt_ld > 0 && score_ld >= bt_ld,
               "page_score: need bt_ld > 0 and score_ld >= bt_ld");
-  SKV_REQUIRE(B <= 65535 && H_kv * 2 <= 65535, "page_score: grid too large");
+  SKV_REQUIRE(B <= 65535, "page_score: grid too large");
   SKV_REQUIRE_PTR(q);
   SKV_REQUIRE_PTR(k_min);
   SKV_REQUIRE_PTR(k_max);
@@ -154,8 +156,10 @@ extern "C" int page_score(const float* q, int B, int H_q, int H_kv, int D,
   const int slices = (G + GS - 1) / GS;
   const int ppw = 64 / (D / 8);
   const int tile = kIter * kWaves * ppw;
-  dim3 grid(static_cast<unsigned>((max_pages + tile - 1) / tile),
-            static_cast<unsigned>(H_kv * slices), static_cast<unsigned>(B));
+  const int64_t tiles = (max_pages + tile - 1) / tile;
+  SKV_REQUIRE(tiles <= 65535, "page_score: bt_ld %lld too long", (long long)bt_ld);
+  dim3 grid(static_cast<unsigned>(H_kv * slices), static_cast<unsigned>(tiles),
+            static_cast<unsigned>(B));
 #define SKV_SCORE(DD, GG)                                                        \
   launch_score<DD, GG>(grid, stream, q, H_q, H_kv, G, k_min, k_max, k_mean,       \
                        block_table, bt_ld, seq_lens, page_size, w_avg, w_peak,   \

@@ -167,13 +167,8 @@ __global__ __launch_bounds__(BLOCK) void page_topk_kernel(
       int sum = 0;
 #pragma unroll
       for (int j = 0; j < kPerLane; ++j) sum += cs[j];
-      int suf = sum;                   // entries in bins of lanes >= lane
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_down(suf, off);
-        if (lane + off < 64) suf += y;
-      }
-      int above = suf - sum;           // entries in higher digits
+      const int incl = skv::wave_inclusive_scan(sum);
+      int above = __builtin_amdgcn_readlane(incl, 63) - incl;   // in higher digits
       int my_digit = 0, my_rem = 0, my_bin = 0;
       bool found = false;
 #pragma unroll
@@ -187,10 +182,10 @@ __global__ __launch_bounds__(BLOCK) void page_topk_kernel(
         above += cs[j];
       }
       const unsigned long long ball = __ballot(found);
-      const int src = __ffsll(static_cast<long long>(ball)) - 1;
-      const uint32_t dg = static_cast<uint32_t>(__shfl(my_digit, src));
-      remaining = __shfl(my_rem, src);
-      bin = __shfl(my_bin, src);
+      const int src = __ffsll(static_cast<long long>(ball)) - 1;   // wave-uniform
+      const uint32_t dg = static_cast<uint32_t>(__builtin_amdgcn_readlane(my_digit, src));
+      remaining = __builtin_amdgcn_readlane(my_rem, src);
+      bin = __builtin_amdgcn_readlane(my_bin, src);
       prefix |= dg << shift;
       pmask |= dmask << shift;
       top = shift - 1;
@@ -234,7 +229,7 @@ __global__ __launch_bounds__(BLOCK) void page_topk_kernel(
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
     if (flags & (1u << i)) {
-      if (pos < k_cap) {
+      if (pos >= 0 && pos < k_cap) {
         out[pos] = base + i;
         if (bout != nullptr) bout[pos] = bid[i];
       }

@@ -85,12 +85,16 @@ __device__ __forceinline__ float wave_max(float x) {
 }
 
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  // Hillis-Steele inside each 16-lane row with row_shr:1,2,4,8 (lanes with no
+  // source add the 0 passed as `old`), then row_bcast:15 carries each row's
+  // last lane into the next row (rows 1 and 3) and row_bcast:31 carries lane
+  // 31 into rows 2 and 3.
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);
   return x;
 }
 
