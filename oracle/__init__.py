@@ -50,6 +50,8 @@ def _load():
     lib.oracle_page_stats.argtypes = [P, i64, i32, i32, i32, P, i64, P, i32, P, P, P]
     lib.oracle_page_score.argtypes = [P, i32, i32, i32, i32, P, P, P, P, i64, P,
                                       i32, f64, f64, P, i64]
+    lib.oracle_page_score_group.argtypes = [P, i32, i32, i32, i32, P, P, P, P, i64, P,
+                                      i32, f64, f64, P, i64]
     lib.oracle_budget.argtypes = [i32, i32, f64]
     lib.oracle_budget.restype = i32
     lib.oracle_select.argtypes = [P, i32, i32, f64, i32, i32, P]
@@ -136,6 +138,26 @@ def page_score(q, kmin, kmax, kmean, block_table, seq_lens, page_size,
     lib.oracle_page_score(_ptr(qd), B, H_q, H_kv, D, _ptr(mn), _ptr(mx), _ptr(me),
                           _ptr(bt), bt.shape[1], _ptr(sl), page_size,
                           float(w_avg), float(w_peak), _ptr(s), ld)
+    return s
+
+
+def page_score_group(q, kmin, kmax, kmean, block_table, seq_lens, page_size,
+                     w_avg, w_peak, ld=None):
+    """Group-shared page scores [B, H_kv, ld]: the mean over each kv head's
+    query group of the per-head scores (float64, NaN beyond N_b)."""
+    lib = _load()
+    qd = _c(q, np.float64)
+    B, H_q, D = qd.shape
+    mn, mx, me = (_c(a, np.float64) for a in (kmin, kmax, kmean))
+    H_kv = mn.shape[1]
+    bt = _c(block_table, np.int32)
+    sl = _c(seq_lens, np.int32)
+    if ld is None:
+        ld = bt.shape[1]
+    s = np.full((B, H_kv, ld), np.nan)
+    lib.oracle_page_score_group(_ptr(qd), B, H_q, H_kv, D, _ptr(mn), _ptr(mx),
+                                _ptr(me), _ptr(bt), bt.shape[1], _ptr(sl), page_size,
+                                float(w_avg), float(w_peak), _ptr(s), ld)
     return s
 
 

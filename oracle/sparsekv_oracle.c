@@ -173,6 +173,45 @@ void oracle_page_score(const double *q, int B, int H_q, int H_kv, int D,
     }
 }
 
+/* Group-shared page score, for a selection made once per kv head: the mean,
+ * over the G query heads that read kv head h, of the per-head score above.
+ * The vortex_torch pull request names GQA variants of the page-level flow
+ * that reduce over the query-group axis; the reduction is read here as the
+ * plain mean of the group's scores (its ranking equals that of the sum).
+ * Output [B, H_kv, ld]. */
+void oracle_page_score_group(const double *q, int B, int H_q, int H_kv, int D,
+                             const double *kmin, const double *kmax,
+                             const double *kmean, const int32_t *block_table,
+                             int64_t bt_ld, const int32_t *seq_lens, int P,
+                             double w_avg, double w_peak, double *scores,
+                             int64_t ld)
+{
+    int G = H_q / H_kv;
+    for (int b = 0; b < B; ++b) {
+        int N = pages_of(seq_lens[b], P);
+        for (int h = 0; h < H_kv; ++h) {
+            for (int p = 0; p < N; ++p) {
+                int64_t blk = block_table[(int64_t)b * bt_ld + p];
+                const double *mn = kmin + (blk * H_kv + h) * D;
+                const double *mx = kmax + (blk * H_kv + h) * D;
+                const double *me = kmean + (blk * H_kv + h) * D;
+                double total = 0.0;
+                for (int g = 0; g < G; ++g) {
+                    const double *qi = q + ((int64_t)b * H_q + h * G + g) * D;
+                    double avg = 0.0, peak = 0.0;
+                    for (int d = 0; d < D; ++d) {
+                        avg += qi[d] * me[d];
+                        double up = qi[d] * mx[d], lo = qi[d] * mn[d];
+                        peak += up > lo ? up : lo;
+                    }
+                    total += w_avg * avg + w_peak * peak;
+                }
+                scores[((int64_t)b * H_kv + h) * ld + p] = total / G;
+            }
+        }
+    }
+}
+
 /* --------------------------------------------------------- selection (O4) */
 
 struct ranked {

@@ -172,3 +172,68 @@ def test_scores_independent_of_physical_placement():
     m = ~np.isnan(s1)
     assert np.array_equal(s1[m], s2[m])
     assert torch.__version__  # torch present for the generators
+
+
+# ----------------------------------------------------- group-shared scores
+
+def _gscores(wl, cache, q, w_avg, w_peak):
+    st = oracle.page_stats(cache, wl.block_table, wl.seq_lens, wl.P)
+    return oracle.page_score_group(q, *st, wl.block_table, wl.seq_lens, wl.P,
+                                   w_avg, w_peak)
+
+
+def test_group_mean_term_is_page_mean_of_the_group_mean_query():
+    # The mean term is linear in q: the group's mean score equals the page
+    # mean of q_bar . k with q_bar the group's mean query, from raw rows.
+    for seed in range(3):
+        wl, cache, q = _case(40 + seed, H_q=8, H_kv=2, min_len=20)
+        avg = _gscores(wl, cache, q, 1.0, 0.0)
+        G = wl.G
+        for b in range(wl.B):
+            for h in range(wl.H_kv):
+                qbar = q[b, h * G:(h + 1) * G].mean(0)
+                for p in range(int(wl.pages()[b])):
+                    rows = _page_rows(wl, cache, b, p)[:, h, :]
+                    np.testing.assert_allclose(avg[b, h, p], (rows @ qbar).mean(),
+                                               rtol=1e-12, atol=1e-12)
+
+
+def test_group_peak_bounds_every_head_average_logit():
+    # mean over g of max_t q_g.k_t >= max_t of the mean logit: the group peak
+    # term bounds the best mean logit of the page (brute force over rows).
+    for seed in range(3):
+        wl, cache, q = _case(50 + seed, H_q=6, H_kv=2, min_len=20)
+        u = _gscores(wl, cache, q, 0.0, 1.0)
+        G = wl.G
+        for b in range(wl.B):
+            for h in range(wl.H_kv):
+                for p in range(int(wl.pages()[b])):
+                    rows = _page_rows(wl, cache, b, p)[:, h, :]
+                    per_head_max = (rows @ q[b, h * G:(h + 1) * G].T).max(0)
+                    assert u[b, h, p] >= per_head_max.mean() - 1e-12 * max(1.0, abs(u[b, h, p]))
+
+
+def test_group_of_one_is_the_per_head_score():
+    wl, cache, q = _case(60, H_q=3, H_kv=3)
+    a = _gscores(wl, cache, q, 0.8, -0.3)
+    b = _scores(wl, cache, q, 0.8, -0.3)
+    m = ~np.isnan(b)
+    assert np.array_equal(np.isnan(a), np.isnan(b))
+    np.testing.assert_allclose(a[m], b[m], rtol=1e-13, atol=1e-13)
+
+
+def test_group_score_ignores_head_order_within_a_group():
+    wl, cache, q = _case(61, H_q=8, H_kv=2)
+    a = _gscores(wl, cache, q, 1.0, 0.5)
+    q2 = q.copy()
+    rng = np.random.default_rng(1)
+    for h in range(2):
+        q2[:, h * 4:(h + 1) * 4] = q[:, h * 4 + rng.permutation(4)]
+    b = _gscores(wl, cache, q2, 1.0, 0.5)
+    m = ~np.isnan(a)
+    np.testing.assert_allclose(a[m], b[m], rtol=1e-13, atol=1e-13)
+    # and heads of the other group do not leak in
+    q3 = q.copy()
+    q3[:, 4:] = rng.standard_normal(q3[:, 4:].shape)
+    c = _gscores(wl, cache, q3, 1.0, 0.5)
+    np.testing.assert_allclose(a[:, 0][m[:, 0]], c[:, 0][m[:, 0]], rtol=1e-13, atol=1e-13)
