@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--replicas", type=int, default=0,
                     help="rotation depth (0 = enough to exceed 1 GiB per cycle)")
     ap.add_argument("--splits", type=int, default=0, help="override num_splits")
+    ap.add_argument("--select", default="head", choices=["head", "group"],
+                    help="page level: select per query head, or once per kv head "
+                         "from the group's mean score (shared by the group)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="enqueue kernel by kernel instead of replaying HIP graphs")
@@ -80,13 +83,14 @@ def unique_kv_bytes(wl, sel_idx, sel_cnt, seq_lens, H_sel):
     return total, pages_total
 
 
-def kernel_bytes(wl, sel_idx, sel_cnt, seq_lens, num_splits, token_level):
+def kernel_bytes(wl, sel_idx, sel_cnt, seq_lens, num_splits, token_level,
+                 group_select=False):
     """Algorithmic HBM bytes of each kernel of one step: the bytes the
     operation must move at least (unique selected K/V once, statistics, scores,
     indices, partials)."""
     B, Hq, Hkv, D, P = wl.B, wl.H_q, wl.H_kv, wl.D, wl.P
     N = (seq_lens.astype(np.int64) + P - 1) // P
-    H_sel = Hkv if token_level else Hq
+    H_sel = Hkv if (token_level or group_select) else Hq
     cnt = int(sel_cnt.sum())
     kv, upages = unique_kv_bytes(wl, sel_idx, sel_cnt, seq_lens, H_sel)
     out = {}
@@ -101,7 +105,7 @@ def kernel_bytes(wl, sel_idx, sel_cnt, seq_lens, num_splits, token_level):
             out["pagestats_update"] = int(B * Hkv * D * 2 * 2 * 2
                                           + B * Hkv * D * 2 * (P - 1)
                                           + B * Hkv * D * 8)
-        out["page_score"] = int((N * (Hkv * 8 * D + Hq * 4 + 4)).sum() + B * Hq * D * 4)
+        out["page_score"] = int((N * (Hkv * 8 * D + H_sel * 4 + 4)).sum() + B * Hq * D * 4)
     out["page_topk"] = int((N * H_sel * 4).sum() + cnt * 4)
     out["sparse_paged_decode"] = int(kv + B * Hq * D * 4 + cnt * 4
                                      + B * Hq * num_splits * (D + 1) * 4)
@@ -234,7 +238,9 @@ def main():
     if wl.name == "high_batch":
         R = 1
     caches = [cache0] + [cache0.clone() for _ in range(R - 1)]
-    decs = [SparseDecoder.for_workload(wl, device=dev) for _ in range(R)]
+    group = args.select == "group" and not token_level
+    decs = [SparseDecoder.for_workload(wl, device=dev, group_select=group)
+            for _ in range(R)]
     new_kv = [W.make_new_kv(wl, s, device=dev) for s in range(min(wl.steps, 64))] \
         if wl.steps > 1 else None
     if token_level:
@@ -355,7 +361,8 @@ def main():
     sl_last = wl.seq_lens_at(last % wl.steps)
     sel_idx = d.sel_idx.cpu().numpy()
     sel_cnt = d.sel_cnt.cpu().numpy()
-    kb, upages = kernel_bytes(wl, sel_idx, sel_cnt, sl_last, wl.num_splits, token_level)
+    kb, upages = kernel_bytes(wl, sel_idx, sel_cnt, sl_last, wl.num_splits, token_level,
+                              group)
     step_bytes = sum(kb.values())
     kern = {}
     for n in names:
@@ -383,6 +390,7 @@ def main():
                    "D": wl.D, "page_size": wl.P, "topk_pages": wl.topk_pages,
                    "topk_frac": wl.topk_frac, "num_splits": wl.num_splits,
                    "mean_seq_len": float(np.mean(sl_last)), "replicas": R,
+                   "selection": ("kv_head" if (group or token_level) else "query_head"),
                    "parallelism": "single-gpu"},
         "effective_GBps": round(step_bytes / (gpu_ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(step_bytes / (gpu_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),

@@ -111,6 +111,28 @@ int page_score(const float *q, int B, int H_q, int H_kv, int D,
                hipStream_t stream);
 
 /*
+ * page_score_group -- one score per (request, kv head, page): the mean, over
+ * the G = H_q / H_kv query heads that read kv head h, of page_score's value.
+ * [VTX: the GQA variants of the page-level flow reduce over the query-group
+ * axis; the reduction is read as the plain mean of the group's scores, which
+ * ranks pages as their sum does.  Selecting once per kv head (page_topk with
+ * H_sel = H_kv) lets sparse_paged_decode read each selected page once for the
+ * whole group.]
+ *
+ *   Arguments and layouts as page_score, except
+ *   scores   fp32 [B, H_kv, score_ld]; entries p >= N_b are not written.
+ * The mean is formed per dim from the group's mean query and mean |q|
+ * (mean_g max(q_g max, q_g min) summed over d equals the mean of the
+ * per-head peaks exactly), so its cost does not grow with G.
+ */
+int page_score_group(const float *q, int B, int H_q, int H_kv, int D,
+                     const uint16_t *k_min, const uint16_t *k_max,
+                     const float *k_mean, const int32_t *block_table,
+                     int64_t bt_ld, const int32_t *seq_lens, int page_size,
+                     float w_avg, float w_peak, float *scores, int64_t score_ld,
+                     hipStream_t stream);
+
+/*
  * page_topk -- top-k selection per row (b, h), h < H_sel.
  * [EKV "How it works": keep topk_pages per query head, the budget counts
  * pages and includes the always-attended tail page; VTX follow-up: the

@@ -17,8 +17,9 @@ import os
 import torch
 
 __all__ = [
-    "pagestats_update", "page_score", "page_topk", "sparse_paged_decode",
-    "lse_merge", "h2o_accumulate", "h2o_scratch_floats", "library_path",
+    "pagestats_update", "page_score", "page_score_group", "page_topk",
+    "sparse_paged_decode", "lse_merge", "h2o_accumulate", "h2o_scratch_floats",
+    "library_path",
     "load_library", "SparseKVError", "EXPORTED_SYMBOLS",
 ]
 
@@ -27,9 +28,12 @@ _LIB_PATH = os.path.join(_HERE, "libsparsekv.so")
 _lib = None
 
 EXPORTED_SYMBOLS = (
-    "pagestats_update", "page_score", "page_topk", "sparse_paged_decode",
-    "lse_merge", "h2o_accumulate", "h2o_scratch_floats", "sparsekv_last_error",
+    "pagestats_update", "page_score", "page_score_group", "page_topk",
+    "sparse_paged_decode", "lse_merge", "h2o_accumulate", "h2o_scratch_floats",
+    "sparsekv_last_error",
 )
+_INT_RETURNING = ("pagestats_update", "page_score", "page_score_group", "page_topk",
+                  "sparse_paged_decode", "lse_merge", "h2o_accumulate")
 
 
 class SparseKVError(RuntimeError):
@@ -59,6 +63,7 @@ def load_library():
     lib.sparsekv_last_error.argtypes = []
     lib.pagestats_update.argtypes = [V, L, I, I, I, V, V, V, V, L, V, I, V, V, V, V]
     lib.page_score.argtypes = [V, I, I, I, I, V, V, V, V, L, V, I, F, F, V, L, V]
+    lib.page_score_group.argtypes = lib.page_score.argtypes
     lib.page_topk.argtypes = [V, L, I, I, V, I, I, F, I, I, V, V, I, V, L, V, V]
     lib.sparse_paged_decode.argtypes = [V, I, I, I, I, V, L, I, V, L, V, V, V, V, I,
                                         I, F, I, V, V, V]
@@ -67,7 +72,7 @@ def load_library():
                                    L, V, L, V]
     lib.h2o_scratch_floats.argtypes = [I, I, L]
     lib.h2o_scratch_floats.restype = ctypes.c_int64
-    for name in EXPORTED_SYMBOLS[:6]:
+    for name in _INT_RETURNING:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -146,10 +151,7 @@ def pagestats_update(kv_cache, k_min, k_max, k_mean, block_table, seq_lens,
         _ptr(v_new), _ptr(hh_score), _stream(stream)))
 
 
-def page_score(q, k_min, k_max, k_mean, block_table, seq_lens, page_size,
-               w_avg, w_peak, scores, stream=None):
-    """scores[b, i, p] for p < N_b from the page statistics."""
-    lib = load_library()
+def _score_args(q, k_min, k_max, k_mean, block_table, seq_lens, scores, H_out):
     _check("q", q, torch.float32, 3)
     dev = q.device
     B, H_q, D = q.shape
@@ -160,9 +162,31 @@ def page_score(q, k_min, k_max, k_mean, block_table, seq_lens, page_size,
     _check("seq_lens", seq_lens, torch.int32, 1, dev)
     _check("scores", scores, torch.float32, 3, dev)
     H_kv = k_min.shape[1]
-    if tuple(scores.shape[:2]) != (B, H_q):
-        raise ValueError("scores must be [B, H_q, score_ld]")
+    if tuple(scores.shape[:2]) != (B, H_out(H_q, H_kv)):
+        raise ValueError("scores has the wrong leading shape")
+    return B, H_q, H_kv, D
+
+
+def page_score(q, k_min, k_max, k_mean, block_table, seq_lens, page_size,
+               w_avg, w_peak, scores, stream=None):
+    """scores[b, i, p] ([B, H_q, score_ld]) for p < N_b from the page statistics."""
+    lib = load_library()
+    B, H_q, H_kv, D = _score_args(q, k_min, k_max, k_mean, block_table, seq_lens,
+                                  scores, lambda hq, hkv: hq)
     _rc("page_score", lib.page_score(
+        _ptr(q), B, H_q, H_kv, D, _ptr(k_min), _ptr(k_max), _ptr(k_mean),
+        _ptr(block_table), block_table.shape[1], _ptr(seq_lens), int(page_size),
+        float(w_avg), float(w_peak), _ptr(scores), scores.shape[2], _stream(stream)))
+
+
+def page_score_group(q, k_min, k_max, k_mean, block_table, seq_lens, page_size,
+                     w_avg, w_peak, scores, stream=None):
+    """scores[b, h, p] ([B, H_kv, score_ld]): the mean of the kv head's query
+    group's page scores, for one selection per kv head."""
+    lib = load_library()
+    B, H_q, H_kv, D = _score_args(q, k_min, k_max, k_mean, block_table, seq_lens,
+                                  scores, lambda hq, hkv: hkv)
+    _rc("page_score_group", lib.page_score_group(
         _ptr(q), B, H_q, H_kv, D, _ptr(k_min), _ptr(k_max), _ptr(k_mean),
         _ptr(block_table), block_table.shape[1], _ptr(seq_lens), int(page_size),
         float(w_avg), float(w_peak), _ptr(scores), scores.shape[2], _stream(stream)))

@@ -28,7 +28,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kIter = 2;
 
-template <int D, int GS>
+template <int D, int GS, bool AGG>
 __global__ __launch_bounds__(256) void page_score_kernel(
     const float* __restrict__ q, int H_q, int H_kv, int G,
     const uint16_t* __restrict__ kmin, const uint16_t* __restrict__ kmax,
@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void page_score_kernel(
   // kv heads vary fastest in launch order: blocks dispatched together read
   // neighbouring statistics rows (all heads of a page are contiguous)
   const int b = blockIdx.z;
-  const int nslices = (G + GS - 1) / GS;
+  const int nslices = AGG ? 1 : (G + GS - 1) / GS;
   const int h = blockIdx.x / nslices;
   const int g0 = (blockIdx.x % nslices) * GS;
   const int S = seq_lens[b];
@@ -75,10 +75,26 @@ __global__ __launch_bounds__(256) void page_score_kernel(
 
   // while the statistics loads are in flight, the group's query rows go to
   // LDS, leaving the registers to those loads
-  __shared__ __align__(16) float qs[GS][D];
-  for (int i = threadIdx.x; i < GS * D; i += blockDim.x) {
-    const int g = i / D, d = i % D;
-    qs[g][d] = g0 + g < G ? q[(static_cast<int64_t>(b) * H_q + h * G + g0 + g) * D + d] : 0.0f;
+  __shared__ __align__(16) float qs[AGG ? 2 : GS][D];
+  if constexpr (AGG) {
+    // The group's mean score is linear in (q, |q|) per dim:
+    //   mean_g [q_g . mp + |q_g| . hp] = qbar . mp + mean_g|q_g| . hp
+    // so one row of means and one of mean magnitudes replace the G rows.
+    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+      float sq = 0.0f, sa = 0.0f;
+      for (int g = 0; g < G; ++g) {
+        const float v = q[(static_cast<int64_t>(b) * H_q + h * G + g) * D + d];
+        sq += v;
+        sa += fabsf(v);
+      }
+      qs[0][d] = sq / static_cast<float>(G);
+      qs[1][d] = sa / static_cast<float>(G);
+    }
+  } else {
+    for (int i = threadIdx.x; i < GS * D; i += blockDim.x) {
+      const int g = i / D, d = i % D;
+      qs[g][d] = g0 + g < G ? q[(static_cast<int64_t>(b) * H_q + h * G + g0 + g) * D + d] : 0.0f;
+    }
   }
   __syncthreads();
 
@@ -97,32 +113,97 @@ __global__ __launch_bounds__(256) void page_score_kernel(
       mp[i] = fmaf(w_avg, me[i], w_peak * mid);
       hp[i] = w_peak * half;
     }
-    float mine = 0.0f;
-#pragma unroll
-    for (int g = 0; g < GS; ++g) {
-      const float4 qa = *reinterpret_cast<const float4*>(&qs[g][c * 8]);
-      const float4 qb = *reinterpret_cast<const float4*>(&qs[g][c * 8 + 4]);
+    if constexpr (AGG) {
+      const float4 qa = *reinterpret_cast<const float4*>(&qs[0][c * 8]);
+      const float4 qb = *reinterpret_cast<const float4*>(&qs[0][c * 8 + 4]);
+      const float4 aa = *reinterpret_cast<const float4*>(&qs[1][c * 8]);
+      const float4 ab = *reinterpret_cast<const float4*>(&qs[1][c * 8 + 4]);
       const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+      const float av[8] = {aa.x, aa.y, aa.z, aa.w, ab.x, ab.y, ab.z, ab.w};
       float s = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s = fmaf(qv[i], mp[i], fmaf(fabsf(qv[i]), hp[i], s));
+      for (int i = 0; i < 8; ++i) s = fmaf(qv[i], mp[i], fmaf(av[i], hp[i], s));
       s = skv::group_sum<LPR>(s);
-      if (c == g) mine = s;
+      if (pg[it] < N && c == 0)
+        scores[(static_cast<int64_t>(b) * H_kv + h) * score_ld + pg[it]] = s;
+    } else {
+      float mine = 0.0f;
+#pragma unroll
+      for (int g = 0; g < GS; ++g) {
+        const float4 qa = *reinterpret_cast<const float4*>(&qs[g][c * 8]);
+        const float4 qb = *reinterpret_cast<const float4*>(&qs[g][c * 8 + 4]);
+        const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s = fmaf(qv[i], mp[i], fmaf(fabsf(qv[i]), hp[i], s));
+        s = skv::group_sum<LPR>(s);
+        if (c == g) mine = s;
+      }
+      if (pg[it] < N && c < GS && g0 + c < G)
+        scores[(static_cast<int64_t>(b) * H_q + h * G + g0 + c) * score_ld + pg[it]] = mine;
     }
-    if (pg[it] < N && c < GS && g0 + c < G)
-      scores[(static_cast<int64_t>(b) * H_q + h * G + g0 + c) * score_ld + pg[it]] = mine;
   }
 }
 
-template <int D, int GS>
+template <int D, int GS, bool AGG>
 void launch_score(dim3 grid, hipStream_t stream, const float* q, int H_q,
                   int H_kv, int G, const uint16_t* kmin, const uint16_t* kmax,
                   const float* kmean, const int32_t* bt, int64_t bt_ld,
                   const int32_t* seq_lens, int P, float w_avg, float w_peak,
                   float* scores, int64_t score_ld, int64_t max_pages) {
-  hipLaunchKernelGGL((page_score_kernel<D, GS>), grid, dim3(256), 0, stream, q,
+  hipLaunchKernelGGL((page_score_kernel<D, GS, AGG>), grid, dim3(256), 0, stream, q,
                      H_q, H_kv, G, kmin, kmax, kmean, bt, bt_ld, seq_lens, P,
                      w_avg, w_peak, scores, score_ld, max_pages);
+}
+
+// Shared by both entry points: validation, grid, dispatch on (D, group size).
+int score_pages(const char* who, bool group, const float* q, int B, int H_q,
+                int H_kv, int D, const uint16_t* k_min, const uint16_t* k_max,
+                const float* k_mean, const int32_t* block_table, int64_t bt_ld,
+                const int32_t* seq_lens, int page_size, float w_avg, float w_peak,
+                float* scores, int64_t score_ld, hipStream_t stream) {
+  SKV_REQUIRE(B >= 0 && H_kv > 0 && H_q > 0 && H_q % H_kv == 0,
+              "%s: need H_q a positive multiple of H_kv (H_q=%d, H_kv=%d)", who, H_q, H_kv);
+  const int G = H_q / H_kv;
+  SKV_REQUIRE(G <= 16, "%s: group size %d > 16", who, G);
+  SKV_REQUIRE(D == 64 || D == 128, "%s: D must be 64 or 128 (got %d)", who, D);
+  SKV_REQUIRE(skv_supported_page_size(page_size),
+              "%s: page_size must be 1, 2, 4, 8 or 16 (got %d)", who, page_size);
+  SKV_REQUIRE(bt_ld > 0 && score_ld >= bt_ld,
+              "%s: need bt_ld > 0 and score_ld >= bt_ld", who);
+  SKV_REQUIRE(B <= 65535, "%s: grid too large", who);
+  SKV_REQUIRE_PTR_W(who, q);
+  SKV_REQUIRE_PTR_W(who, k_min);
+  SKV_REQUIRE_PTR_W(who, k_max);
+  SKV_REQUIRE_PTR_W(who, k_mean);
+  SKV_REQUIRE_PTR_W(who, block_table);
+  SKV_REQUIRE_PTR_W(who, seq_lens);
+  SKV_REQUIRE_PTR_W(who, scores);
+  const int64_t max_pages = bt_ld;
+  const int GS = group ? 1 : G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
+  const int slices = group ? 1 : (G + GS - 1) / GS;
+  const int ppw = 64 / (D / 8);
+  const int tile = kIter * kWaves * ppw;
+  const int64_t tiles = (max_pages + tile - 1) / tile;
+  SKV_REQUIRE(tiles <= 65535, "%s: bt_ld %lld too long", who, (long long)bt_ld);
+  if (B == 0) { skv::clear_error(); return SKV_OK; }
+  dim3 grid(static_cast<unsigned>(H_kv * slices), static_cast<unsigned>(tiles),
+            static_cast<unsigned>(B));
+#define SKV_SCORE(DD, GG, AA)                                                    \
+  launch_score<DD, GG, AA>(grid, stream, q, H_q, H_kv, G, k_min, k_max, k_mean,   \
+                           block_table, bt_ld, seq_lens, page_size, w_avg,      \
+                           w_peak, scores, score_ld, max_pages)
+  if (group) {
+    if (D == 128) SKV_SCORE(128, 1, true); else SKV_SCORE(64, 1, true);
+  } else if (D == 128) {
+    if (GS == 1) SKV_SCORE(128, 1, false); else if (GS == 2) SKV_SCORE(128, 2, false);
+    else if (GS == 4) SKV_SCORE(128, 4, false); else SKV_SCORE(128, 8, false);
+  } else {
+    if (GS == 1) SKV_SCORE(64, 1, false); else if (GS == 2) SKV_SCORE(64, 2, false);
+    else if (GS == 4) SKV_SCORE(64, 4, false); else SKV_SCORE(64, 8, false);
+  }
+#undef SKV_SCORE
+  SKV_CHECK_LAUNCH();
 }
 
 }  // namespace
@@ -133,44 +214,18 @@ extern "C" int page_score(const float* q, int B, int H_q, int H_kv, int D,
                           int64_t bt_ld, const int32_t* seq_lens, int page_size,
                           float w_avg, float w_peak, float* scores,
                           int64_t score_ld, hipStream_t stream) {
-  SKV_REQUIRE(B >= 0 && H_kv > 0 && H_q > 0 && H_q % H_kv == 0,
-              "page_score: need H_q a positive multiple of H_kv (H_q=%d, H_kv=%d)", H_q, H_kv);
-  const int G = H_q / H_kv;
-  SKV_REQUIRE(G <= 16, "page_score: group size %d > 16", G);
-  SKV_REQUIRE(D == 64 || D == 128, "page_score: D must be 64 or 128 (got %d)", D);
-  SKV_REQUIRE(skv_supported_page_size(page_size),
-              "page_score: page_size must be 1, 2, 4, 8 or 16 (got %d)", page_size);
-  SKV_REQUIRE(bt_ld > 0 && score_ld >= bt_ld,
-              "page_score: need bt_ld > 0 and score_ld >= bt_ld");
-  SKV_REQUIRE(B <= 65535, "page_score: grid too large");
-  SKV_REQUIRE_PTR(q);
-  SKV_REQUIRE_PTR(k_min);
-  SKV_REQUIRE_PTR(k_max);
-  SKV_REQUIRE_PTR(k_mean);
-  SKV_REQUIRE_PTR(block_table);
-  SKV_REQUIRE_PTR(seq_lens);
-  SKV_REQUIRE_PTR(scores);
-  if (B == 0) { skv::clear_error(); return SKV_OK; }
-  const int64_t max_pages = bt_ld;
-  const int GS = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
-  const int slices = (G + GS - 1) / GS;
-  const int ppw = 64 / (D / 8);
-  const int tile = kIter * kWaves * ppw;
-  const int64_t tiles = (max_pages + tile - 1) / tile;
-  SKV_REQUIRE(tiles <= 65535, "page_score: bt_ld %lld too long", (long long)bt_ld);
-  dim3 grid(static_cast<unsigned>(H_kv * slices), static_cast<unsigned>(tiles),
-            static_cast<unsigned>(B));
-#define SKV_SCORE(DD, GG)                                                        \
-  launch_score<DD, GG>(grid, stream, q, H_q, H_kv, G, k_min, k_max, k_mean,       \
-                       block_table, bt_ld, seq_lens, page_size, w_avg, w_peak,   \
-                       scores, score_ld, max_pages)
-  if (D == 128) {
-    if (GS == 1) SKV_SCORE(128, 1); else if (GS == 2) SKV_SCORE(128, 2);
-    else if (GS == 4) SKV_SCORE(128, 4); else SKV_SCORE(128, 8);
-  } else {
-    if (GS == 1) SKV_SCORE(64, 1); else if (GS == 2) SKV_SCORE(64, 2);
-    else if (GS == 4) SKV_SCORE(64, 4); else SKV_SCORE(64, 8);
-  }
-#undef SKV_SCORE
-  SKV_CHECK_LAUNCH();
+  return score_pages("page_score", false, q, B, H_q, H_kv, D, k_min, k_max, k_mean,
+                     block_table, bt_ld, seq_lens, page_size, w_avg, w_peak, scores,
+                     score_ld, stream);
+}
+
+extern "C" int page_score_group(const float* q, int B, int H_q, int H_kv, int D,
+                                const uint16_t* k_min, const uint16_t* k_max,
+                                const float* k_mean, const int32_t* block_table,
+                                int64_t bt_ld, const int32_t* seq_lens,
+                                int page_size, float w_avg, float w_peak,
+                                float* scores, int64_t score_ld, hipStream_t stream) {
+  return score_pages("page_score_group", true, q, B, H_q, H_kv, D, k_min, k_max,
+                     k_mean, block_table, bt_ld, seq_lens, page_size, w_avg, w_peak,
+                     scores, score_ld, stream);
 }

@@ -36,6 +36,16 @@ void clear_error();
   } while (0)
 
 // Report a failed launch.
+// The same check for a helper shared by several entry points: `who` names
+// the entry point the caller used.
+#define SKV_REQUIRE_PTR_W(who, p)                             \
+  do {                                                       \
+    if ((p) == nullptr) {                                    \
+      skv::set_error("%s: %s must not be NULL", (who), #p);  \
+      return SKV_EFAULT;                                     \
+    }                                                        \
+  } while (0)
+
 #define SKV_CHECK_LAUNCH()                                              \
   do {                                                                  \
     hipError_t e_ = hipGetLastError();                                  \

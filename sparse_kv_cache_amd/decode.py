@@ -6,6 +6,8 @@ library's entry points in the order of a decode step:
 
   page level   [pagestats_update (append)] -> page_score -> page_topk
                -> sparse_paged_decode -> lse_merge
+  group level  as page level with page_score_group: one selection per kv
+               head, shared by its query group
   token level  pagestats_update (append + hh reset) -> h2o_accumulate
                -> page_topk (per kv head) -> sparse_paged_decode -> lse_merge
 
@@ -20,7 +22,7 @@ import math
 import torch
 
 from . import (h2o_accumulate, h2o_scratch_floats, lse_merge, page_score,
-               page_topk, pagestats_update, sparse_paged_decode)
+               page_score_group, page_topk, pagestats_update, sparse_paged_decode)
 
 
 def selection_capacity(score_ld, topk_pages, topk_frac=0.0, bos=0, eos=1):
@@ -34,12 +36,13 @@ class SparseDecoder:
     """Buffers and call order of one decode step.
 
     kv_cache: bf16 [2, num_blocks, P, H_kv, D]; block_table int32 [B, bt_ld].
-    token_level=True selects the H2O flow (page_size must be 1)."""
+    token_level=True selects the H2O flow (page_size must be 1);
+    group_select=True scores and selects once per kv head (page level)."""
 
     def __init__(self, B, H_q, H_kv, D, num_blocks, page_size, bt_ld, *,
                  topk_pages, topk_frac=0.0, bos=0, eos=1, w_avg=1.0, w_peak=1.0,
                  scale=None, num_splits=1, decay=0.984375, token_level=False,
-                 device="cuda"):
+                 group_select=False, device="cuda"):
         self.B, self.H_q, self.H_kv, self.D = B, H_q, H_kv, D
         self.num_blocks, self.P, self.bt_ld = num_blocks, page_size, bt_ld
         self.topk_pages, self.topk_frac = topk_pages, topk_frac
@@ -48,8 +51,9 @@ class SparseDecoder:
         self.scale = D ** -0.5 if scale is None else scale
         self.num_splits, self.decay = num_splits, decay
         self.token_level = token_level
+        self.group_select = bool(group_select) and not token_level
         dev = torch.device(device)
-        self.H_sel = H_kv if token_level else H_q
+        self.H_sel = H_kv if (token_level or self.group_select) else H_q
         self.k_cap = selection_capacity(bt_ld, topk_pages, topk_frac, bos, eos)
         f32, i32, bf = torch.float32, torch.int32, torch.bfloat16
         if token_level:
@@ -76,14 +80,14 @@ class SparseDecoder:
         self.lse = torch.empty((B, H_q), dtype=f32, device=dev)
 
     @classmethod
-    def for_workload(cls, wl, device="cuda", num_splits=None):
+    def for_workload(cls, wl, device="cuda", num_splits=None, group_select=False):
         return cls(wl.B, wl.H_q, wl.H_kv, wl.D, wl.num_blocks, wl.P, wl.bt_ld,
                    topk_pages=wl.topk_pages, topk_frac=wl.topk_frac, bos=wl.bos,
                    eos=wl.eos, w_avg=wl.w_avg, w_peak=wl.w_peak,
                    scale=wl.softmax_scale,
                    num_splits=wl.num_splits if num_splits is None else num_splits,
                    decay=wl.decay, token_level=(wl.name == "h2o_token"),
-                   device=device)
+                   group_select=group_select, device=device)
 
     # ------------------------------------------------------------ stages
     def rebuild_stats(self, kv_cache, block_table, seq_lens, stream=None):
@@ -98,8 +102,9 @@ class SparseDecoder:
     def score(self, q, block_table, seq_lens, stream=None):
         if self.token_level:
             raise RuntimeError("token-level scores come from h2o_accumulate")
-        page_score(q, self.k_min, self.k_max, self.k_mean, block_table, seq_lens,
-                   self.P, self.w_avg, self.w_peak, self.scores, stream=stream)
+        fn = page_score_group if self.group_select else page_score
+        fn(q, self.k_min, self.k_max, self.k_mean, block_table, seq_lens,
+           self.P, self.w_avg, self.w_peak, self.scores, stream=stream)
 
     def accumulate(self, q, kv_cache, block_table, seq_lens, stream=None):
         h2o_accumulate(q, kv_cache, block_table, seq_lens, self.hh, self.scores,

@@ -121,6 +121,27 @@ def check_scores(gpu_scores, q, stats_d, bt, sl, P, w_avg, w_peak):
     return ref
 
 
+def check_scores_group(gpu_scores, q, stats_d, bt, sl, P, w_avg, w_peak):
+    """gpu_scores [B, H_kv, ld] (group means) vs the oracle fed the same
+    statistics; the bound is the per-head one averaged over the group plus
+    the rounding of the group means of q and |q|."""
+    mn, mx, me = stats_d
+    ref = oracle.page_score_group(q, mn, mx, me, bt, sl, P, w_avg, w_peak,
+                                  ld=gpu_scores.shape[2])
+    B, H_q, D = q.shape
+    H_kv = gpu_scores.shape[1]
+    G = H_q // H_kv
+    terms = score_abs_terms(q, mn, mx, me, bt, sl, P, w_avg, w_peak)
+    terms = terms.reshape(B, H_kv, G, -1).mean(axis=2)
+    valid = ~np.isnan(ref)
+    g = gpu_scores.astype(np.float64)
+    assert not np.any(np.isnan(g[valid])), "unwritten score"
+    err = np.abs(g[valid] - ref[valid])
+    tol = (2 * D + 2 * G) * 2.0 ** -24 * terms[valid] + 1e-6
+    assert np.all(err <= tol), f"group score error {err.max()} over bound"
+    return ref
+
+
 def selection_rows(sel_idx, sel_cnt):
     out = []
     for r in range(sel_cnt.shape[0]):

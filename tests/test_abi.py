@@ -39,7 +39,8 @@ def lib():
 
 def test_header_declares_the_six_operations():
     names = _declared()
-    for n in ("pagestats_update", "page_score", "page_topk", "sparse_paged_decode",
+    for n in ("pagestats_update", "page_score", "page_score_group", "page_topk",
+              "sparse_paged_decode",
               "lse_merge", "h2o_accumulate", "h2o_scratch_floats",
               "sparsekv_last_error"):
         assert n in names
@@ -75,6 +76,15 @@ def test_validation_rejects_bad_scalars(lib):
     # score_ld < bt_ld
     assert lib.page_score(p, 1, 4, 2, 64, p, p, p, p, 8, p, 16, 1.0, 1.0, p, 4,
                           s) == EINVAL
+    # the group score validates like page_score
+    assert lib.page_score_group(p, 1, 4, 2, 96, p, p, p, p, 4, p, 16, 1.0, 1.0, p, 4,
+                                s) == EINVAL
+    assert "page_score_group" in _msg(lib)
+    assert lib.page_score_group(p, 1, 6, 4, 64, p, p, p, p, 4, p, 16, 1.0, 1.0, p, 4,
+                                s) == EINVAL
+    assert lib.page_score_group(None, 1, 4, 2, 64, p, p, p, p, 4, p, 16, 1.0, 1.0, p, 4,
+                                s) == EFAULT
+    assert "page_score_group" in _msg(lib)
     # topk < 1, k_cap too small, score_ld too long
     assert lib.page_topk(p, 64, 1, 4, p, 16, 0, 0.0, 0, 1, p, p, 8, None, 0, None, s) == EINVAL
     assert lib.page_topk(p, 64, 1, 4, p, 16, 9, 0.0, 0, 1, p, p, 8, None, 0, None, s) == EINVAL

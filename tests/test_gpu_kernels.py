@@ -12,6 +12,7 @@ from sparse_kv_cache_amd import workloads as W
 from sparse_kv_cache_amd.decode import SparseDecoder
 
 from parity import (bits, check_attention, check_partials, check_scores,
+                    check_scores_group,
                     check_selection_exact, check_selection_vs_oracle,
                     check_stats, dev, per_head_rows, poison, say,
                     selection_rows, bf16_bits_apart, check_sel_blk)
@@ -112,6 +113,78 @@ def test_page_level_step(case):
                       topk_pages=topk, topk_frac=frac, bos=bos, eos=eos,
                       w_avg=wa, w_peak=wp, num_splits=ns)
     worst, ex = run_page_case(wl, W.make_cache(wl), W.make_queries(wl))
+    say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}")
+
+
+# seed, B, H_q, H_kv, D, P, max_pages, topk, frac, bos, eos, splits, w_avg, w_peak
+GROUP_CASES = [
+    (40, 2, 8, 2, 128, 16, 20, 5, 0.0, 0, 1, 3, 1.0, 1.0),
+    (41, 3, 16, 1, 64, 16, 33, 9, 0.0, 1, 1, 4, 1.0, 0.5),
+    (42, 2, 12, 4, 128, 4, 30, 7, 0.2, 0, 1, 2, 0.5, 1.0),
+    (43, 1, 64, 8, 128, 16, 70, 16, 0.0, 0, 1, 8, 1.0, 1.0),
+    (44, 2, 4, 2, 64, 1, 150, 20, 0.0, 2, 3, 5, 1.0, 1.0),
+    (45, 2, 6, 3, 128, 16, 5, 50, 0.0, 0, 1, 2, 1.0, 1.0),
+]
+
+
+def run_group_case(wl, cache_cpu, q_cpu):
+    """Page level with one selection per kv head, shared by its query group."""
+    cache = dev(cache_cpu)
+    q = dev(q_cpu)
+    bt = dev(wl.block_table)
+    sl = dev(wl.seq_lens)
+    d = SparseDecoder(wl.B, wl.H_q, wl.H_kv, wl.D, wl.num_blocks, wl.P, wl.bt_ld,
+                      topk_pages=wl.topk_pages, topk_frac=wl.topk_frac, bos=wl.bos,
+                      eos=wl.eos, w_avg=wl.w_avg, w_peak=wl.w_peak,
+                      scale=wl.softmax_scale, num_splits=wl.num_splits,
+                      group_select=True)
+    assert d.H_sel == wl.H_kv
+    poison(d)
+    d.rebuild_stats(cache, bt, sl)
+    d.score(q, bt, sl)
+    d.select(sl, bt)
+    d.attend(q, cache, bt, sl)
+    d.merge()
+    torch.cuda.synchronize()
+
+    cb = bits(cache)
+    qd = q_cpu.double().numpy()
+    used = W.referenced_blocks(wl)
+    st = check_stats(bits(d.k_min), bits(d.k_max), d.k_mean.cpu().numpy(), cb,
+                     wl.block_table, wl.seq_lens, wl.P, used)
+    gst = (oracle.bf16_decode(bits(d.k_min)), oracle.bf16_decode(bits(d.k_max)),
+           d.k_mean.cpu().numpy().astype(np.float64))
+    gs = d.scores.cpu().numpy()
+    check_scores_group(gs, qd, gst, wl.block_table, wl.seq_lens, wl.P, wl.w_avg,
+                       wl.w_peak)
+    N = wl.pages()
+    sel_idx = d.sel_idx.cpu().numpy().reshape(-1, d.k_cap)
+    sel_cnt = d.sel_cnt.cpu().numpy().reshape(-1)
+    rowsN = np.repeat(N, wl.H_kv)
+    check_selection_exact(sel_idx, sel_cnt, gs.reshape(-1, wl.bt_ld), rowsN,
+                          wl.topk_pages, wl.topk_frac, wl.bos, wl.eos)
+    check_sel_blk(d.sel_blk.cpu().numpy(), d.sel_idx.cpu().numpy(), wl.block_table)
+    ref_scores = oracle.page_score_group(qd, *st, wl.block_table, wl.seq_lens, wl.P,
+                                         wl.w_avg, wl.w_peak)
+    rows = selection_rows(sel_idx, sel_cnt)
+    ex = check_selection_vs_oracle(rows, ref_scores.reshape(-1, wl.bt_ld), rowsN,
+                                   wl.topk_pages, wl.topk_frac, wl.bos, wl.eos)
+    per = per_head_rows(rows, wl.B, wl.H_q, wl.H_kv)
+    check_partials(d.o_part.cpu().numpy(), d.lse_part.cpu().numpy(), qd, cb,
+                   wl.block_table, wl.seq_lens, per, wl.G, wl.softmax_scale, d.k_cap)
+    worst = check_attention(d.out.cpu().numpy(), d.lse.cpu().numpy(), qd, cb,
+                            wl.block_table, wl.seq_lens, per, wl.G, wl.softmax_scale)
+    return worst, ex
+
+
+@pytest.mark.parametrize("case", GROUP_CASES, ids=[f"group{c[0]}" for c in GROUP_CASES])
+def test_group_selection_step(case):
+    (seed, B, H_q, H_kv, D, P, maxp, topk, frac, bos, eos, ns, wa, wp) = case
+    say(f"[gpu] group-selection case {case}")
+    wl = W.small_case(seed=seed, B=B, H_q=H_q, H_kv=H_kv, D=D, P=P, max_pages=maxp,
+                      topk_pages=topk, topk_frac=frac, bos=bos, eos=eos,
+                      w_avg=wa, w_peak=wp, num_splits=ns)
+    worst, ex = run_group_case(wl, W.make_cache(wl), W.make_queries(wl))
     say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}")
 
 

@@ -1,7 +1,8 @@
 """GPU parity on the five decode workloads at their real sizes, in the launch
 configuration the benchmark times (SparseDecoder, same splits).
 
-mha_tiny, gqa_ragged and long_context are compared in full; high_batch on a
+mha_tiny, gqa_ragged and long_context are compared in full (gqa_ragged and
+long_context also with one selection per kv head); high_batch on a
 sample of requests (shortest, longest and three others) after two appended
 steps; h2o_token teacher-forced at its first two steps and its last step, plus
 the probability-mass invariant after all 256 steps."""
@@ -14,7 +15,7 @@ from sparse_kv_cache_amd import workloads as W
 from sparse_kv_cache_amd.decode import SparseDecoder
 
 from parity import (bits, bf16_bits_apart, check_attention, check_partials,
-                    check_scores, check_selection_exact,
+                    check_scores, check_scores_group, check_selection_exact,
                     check_selection_vs_oracle, check_stats, dev, per_head_rows,
                     poison, say, selection_rows, sub_batch, check_sel_blk)
 
@@ -32,20 +33,23 @@ def page_level_parity(wl, cache, q_cpu, seq_lens_np, rows, d, partial_heads=4):
     gst = (oracle.bf16_decode(bits(gmin)), oracle.bf16_decode(bits(gmax)),
            gmean.numpy().astype(np.float64))
     gs = d.scores.cpu().numpy()[rows]
-    check_scores(gs, qd, gst, bt, sl, wl.P, wl.w_avg, wl.w_peak)
+    group = d.H_sel != wl.H_q
+    (check_scores_group if group else check_scores)(gs, qd, gst, bt, sl, wl.P,
+                                                    wl.w_avg, wl.w_peak)
     N = (sl.astype(np.int64) + wl.P - 1) // wl.P
-    rowsN = np.repeat(N, wl.H_q)
+    rowsN = np.repeat(N, d.H_sel)
     sel_idx = d.sel_idx.cpu().numpy()[rows].reshape(-1, d.k_cap)
     sel_cnt = d.sel_cnt.cpu().numpy()[rows].reshape(-1)
     check_selection_exact(sel_idx, sel_cnt, gs.reshape(-1, wl.bt_ld), rowsN,
                           wl.topk_pages, wl.topk_frac, wl.bos, wl.eos)
     check_sel_blk(d.sel_blk.cpu().numpy()[rows], d.sel_idx.cpu().numpy()[rows],
                   wl.block_table[list(rows)])
-    ref_scores = oracle.page_score(qd, *st, bt, sl, wl.P, wl.w_avg, wl.w_peak)
+    ref_scores = (oracle.page_score_group if group else oracle.page_score)(
+        qd, *st, bt, sl, wl.P, wl.w_avg, wl.w_peak)
     sel_rows = selection_rows(sel_idx, sel_cnt)
     ex = check_selection_vs_oracle(sel_rows, ref_scores.reshape(-1, wl.bt_ld), rowsN,
                                    wl.topk_pages, wl.topk_frac, wl.bos, wl.eos)
-    per = per_head_rows(sel_rows, len(rows), wl.H_q, wl.H_q)
+    per = per_head_rows(sel_rows, len(rows), wl.H_q, d.H_sel)
     hs = slice(0, partial_heads)
     check_partials(d.o_part.cpu().numpy()[rows][:, hs], d.lse_part.cpu().numpy()[rows][:, hs],
                    qd[:, hs], cb, bt, sl, [p[hs] for p in per], wl.G, wl.softmax_scale,
@@ -55,12 +59,12 @@ def page_level_parity(wl, cache, q_cpu, seq_lens_np, rows, d, partial_heads=4):
     return worst, ex
 
 
-def _static_workload(name):
+def _static_workload(name, group_select=False):
     wl = W.WORKLOADS[name]()
-    say(f"[gpu] workload {name}: generating")
+    say(f"[gpu] workload {name} (group selection {group_select}): generating")
     cache = W.make_cache(wl, device="cuda")
     q_cpu = W.make_queries(wl)
-    d = SparseDecoder.for_workload(wl)
+    d = SparseDecoder.for_workload(wl, group_select=group_select)
     bt, sl = dev(wl.block_table), dev(wl.seq_lens)
     poison(d)
     d.rebuild_stats(cache, bt, sl)
@@ -81,6 +85,14 @@ def test_gqa_ragged():
 
 def test_long_context():
     _static_workload("long_context")
+
+
+def test_gqa_ragged_group_selection():
+    _static_workload("gqa_ragged", group_select=True)
+
+
+def test_long_context_group_selection():
+    _static_workload("long_context", group_select=True)
 
 
 def test_high_batch_sampled_after_appends():
