@@ -9,9 +9,9 @@
 //
 // Two launches over (token chunk, request):
 //   1. logits l_t = scale * log2(e) * qbar . k_t for every kv head over
-//      64-token chunks, one token row of H_kv * D bf16 read with 16-byte loads
-//      (D/8 lanes per head row); the chunk's (max, sum 2^(l - max)) per head go
-//      to scratch.
+//      64-token chunks (16 waves per chunk, every head row read once with
+//      16-byte loads, D/8 lanes per row); the chunk's (max, sum 2^(l - max))
+//      per head go to scratch.
 //   2. merge of the chunk partials into (M, Z) per head, then per token:
 //      p = 2^(l - M) / Z, stored bf16(p), hh <- bf16(bf16(p) + decay * hh)
 //      (one fp32 fma, then round-to-nearest-even), and the new hh value is
@@ -23,8 +23,8 @@
 namespace {
 
 constexpr int kChunk = 64;      // tokens per block of the logits pass
-constexpr int kUpd = 256;       // tokens per block of the update pass
-constexpr int kUnroll = 8;      // row loads in flight per lane
+constexpr int kLWaves = 16;     // waves per block of the logits pass
+constexpr int kUpd = 64;        // tokens per block of the update pass
 
 __device__ __forceinline__ void window(int S, int64_t bt_ld, int bos, int eos,
                                        int* ntok, int* lo, int* hi) {
@@ -37,8 +37,12 @@ __device__ __forceinline__ void window(int S, int64_t bt_ld, int bos, int eos,
   *ntok = n; *lo = l; *hi = h;
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void h2o_logits_kernel(
+// Logits of one 64-token chunk of one request for every kv head.  The chunk's
+// H_kv * 64 head rows are dealt to 16 waves, 4 * H_kv rows each; a wave issues
+// all its 16-byte row loads (NLD per lane) before any arithmetic, masked rows
+// reading a placeholder so the loads stay unconditional.
+template <int D, int NLD>
+__global__ __launch_bounds__(kLWaves * 64) void h2o_logits_kernel(
     const float* __restrict__ q, int H_q, int H_kv, int G,
     const uint16_t* __restrict__ kv, const int32_t* __restrict__ bt,
     int64_t bt_ld, const int32_t* __restrict__ seq_lens, int bos, int eos,
@@ -49,6 +53,7 @@ __global__ __launch_bounds__(256) void h2o_logits_kernel(
   extern __shared__ float smem[];
   float* qs = smem;                            // [H_kv][D]
   float* lg = smem + H_kv * D;                 // [H_kv][kChunk]
+  int* sblk = reinterpret_cast<int*>(lg + H_kv * kChunk);   // [kChunk]
   const int b = blockIdx.y;
   const int c = blockIdx.x;
   int ntok, lo, hi;
@@ -58,7 +63,9 @@ __global__ __launch_bounds__(256) void h2o_logits_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int sub = lane / LPR, cc = lane % LPR;
+  const int32_t* btr = bt + static_cast<int64_t>(b) * bt_ld;
 
+  if (tid < kChunk) sblk[tid] = t0 + tid < ntok ? btr[t0 + tid] : 0;
   const float inv_g = 1.0f / static_cast<float>(G);
   for (int i = tid; i < H_kv * D; i += blockDim.x) {
     const int h = i / D, d = i % D;
@@ -68,53 +75,45 @@ __global__ __launch_bounds__(256) void h2o_logits_kernel(
   }
   __syncthreads();
 
-  const int rows = kChunk * H_kv;
-  const int32_t* btr = bt + static_cast<int64_t>(b) * bt_ld;
-  const int step = 4 * RPW;                    // rows per block load
-  for (int r0 = wave * RPW; r0 < rows; r0 += step * kUnroll) {
-    uint4 kr[kUnroll];
-    bool ok[kUnroll];
+  const int R = (kChunk / kLWaves) * H_kv;     // head rows of this wave
+  uint4 kr[NLD];
+  bool ok[NLD];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int r = r0 + u * step + sub;
-      const int t = t0 + r / H_kv;
-      ok[u] = r < rows && t >= lo && t < hi;
-      if (ok[u]) {
-        const int64_t blk = btr[t];
-        kr[u] = *reinterpret_cast<const uint4*>(
-            kv + (blk * H_kv + (r % H_kv)) * D + cc * 8);
-      } else {
-        kr[u] = make_uint4(0, 0, 0, 0);
-      }
-    }
+  for (int u = 0; u < NLD; ++u) {
+    const int rl = u * RPW + sub;
+    const int r = wave * R + rl;
+    const int tt = r / H_kv, h = r % H_kv;
+    const int t = t0 + tt;
+    ok[u] = rl < R && t >= lo && t < hi;
+    const int64_t off = ok[u] ? (static_cast<int64_t>(sblk[ok[u] ? tt : 0]) * H_kv + h) * D + cc * 8
+                              : cc * 8;
+    kr[u] = *reinterpret_cast<const uint4*>(kv + off);
+  }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int r = r0 + u * step + sub;
-      const int h = r % H_kv;
-      float x[8];
-      skv::unpack8(kr[u], x);
-      const float* qq = qs + h * D + cc * 8;
-      float dot = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dot = fmaf(qq[i], x[i], dot);
-      dot = skv::group_sum<LPR>(dot);
-      if (r < rows && cc == 0) lg[h * kChunk + r / H_kv] = ok[u] ? dot : -INFINITY;
-    }
+  for (int u = 0; u < NLD; ++u) {
+    const int rl = u * RPW + sub;
+    const int r = wave * R + rl;
+    const int tt = r / H_kv, h = r % H_kv;
+    float x[8];
+    skv::unpack8(kr[u], x);
+    const float4 qa = *reinterpret_cast<const float4*>(qs + (rl < R ? h : 0) * D + cc * 8);
+    const float4 qb = *reinterpret_cast<const float4*>(qs + (rl < R ? h : 0) * D + cc * 8 + 4);
+    float dot = qa.x * x[0];
+    dot = fmaf(qa.y, x[1], dot); dot = fmaf(qa.z, x[2], dot); dot = fmaf(qa.w, x[3], dot);
+    dot = fmaf(qb.x, x[4], dot); dot = fmaf(qb.y, x[5], dot); dot = fmaf(qb.z, x[6], dot);
+    dot = fmaf(qb.w, x[7], dot);
+    dot = skv::group_sum<LPR>(dot);
+    if (rl < R && cc == 0) lg[h * kChunk + tt] = ok[u] ? dot : -INFINITY;
   }
   __syncthreads();
 
   const int nt = min(kChunk, ntok - t0);
-  for (int h = wave; h < H_kv; h += 4) {
-    const float* row = lg + h * kChunk;
-    float m = -INFINITY;
-    for (int j = lane; j < nt; j += 64) m = fmaxf(m, row[j]);
-    m = skv::wave_max(m);
-    float s = 0.0f;
-    if (m != -INFINITY)
-      for (int j = lane; j < nt; j += 64) s += exp2f(row[j] - m);
-    s = skv::wave_sum(s);
-    float* dst = logits + (static_cast<int64_t>(b) * H_kv + h) * bt_ld + t0;
-    for (int j = lane; j < nt; j += 64) dst[j] = row[j];
+  for (int h = wave; h < H_kv; h += kLWaves) {
+    const float v = lane < nt ? lg[h * kChunk + lane] : -INFINITY;
+    const float m = skv::wave_max(v);
+    float e = (m != -INFINITY && lane < nt) ? exp2f(v - m) : 0.0f;
+    const float s = skv::wave_sum(e);
+    if (lane < nt) logits[(static_cast<int64_t>(b) * H_kv + h) * bt_ld + t0 + lane] = v;
     if (lane == 0) {
       float* pp = part + ((static_cast<int64_t>(b) * H_kv + h) * nchunk + c) * 2;
       pp[0] = m;
@@ -123,6 +122,7 @@ __global__ __launch_bounds__(256) void h2o_logits_kernel(
   }
 }
 
+// Normalise and fold into hh: block of 256 threads = 64 tokens x 4 head lanes.
 __global__ __launch_bounds__(256) void h2o_update_kernel(
     int H_kv, const int32_t* __restrict__ bt, int64_t bt_ld,
     const int32_t* __restrict__ seq_lens, int bos, int eos, float decay,
@@ -154,11 +154,11 @@ __global__ __launch_bounds__(256) void h2o_update_kernel(
     if (lane == 0) { sM[h] = m; sZ[h] = z; }
   }
   __syncthreads();
-  const int t = t0 + tid;
+  const int t = t0 + lane;
   if (t >= ntok) return;
   const int64_t slot = bt[static_cast<int64_t>(b) * bt_ld + t];
   const bool in_w = t >= lo && t < hi;
-  for (int h = 0; h < H_kv; ++h) {
+  for (int h = wave; h < H_kv; h += 4) {
     uint16_t* cell = hh + slot * H_kv + h;
     float v = skv::bf16_to_f32(*cell);
     if (in_w) {
@@ -222,19 +222,28 @@ extern "C" int h2o_accumulate(const float* q, int B, int H_q, int H_kv, int D,
   // decay is applied as its bf16 value, which is exact for 0.984375
   const float decay_b = skv_host_round_bf16(decay);
   dim3 grid(static_cast<unsigned>(nch), static_cast<unsigned>(B));
-  const size_t sm1 = sizeof(float) * (static_cast<size_t>(H_kv) * D + static_cast<size_t>(H_kv) * kChunk);
+  const size_t sm1 = sizeof(float) * (static_cast<size_t>(H_kv) * D +
+                                      static_cast<size_t>(H_kv) * kChunk + kChunk);
   const float scale_log2 = scale * skv::kLog2e;
-  if (D == 128)
-    hipLaunchKernelGGL(h2o_logits_kernel<128>, grid, dim3(256), sm1, stream, q, H_q,
-                       H_kv, H_q / H_kv, kv_cache, block_table, bt_ld, seq_lens,
-                       reserved_bos, reserved_eos, scale_log2, logits, part, nch);
-  else
-    hipLaunchKernelGGL(h2o_logits_kernel<64>, grid, dim3(256), sm1, stream, q, H_q,
-                       H_kv, H_q / H_kv, kv_cache, block_table, bt_ld, seq_lens,
-                       reserved_bos, reserved_eos, scale_log2, logits, part, nch);
+  // 16-byte row loads per lane: 4 * H_kv rows per wave over 64 / (D / 8) rows per load
+  const int rpw = 64 / (D / 8);
+  const int nld = (4 * H_kv + rpw - 1) / rpw;
+#define SKV_LOGITS(DD, NN)                                                         \
+  hipLaunchKernelGGL((h2o_logits_kernel<DD, NN>), grid, dim3(kLWaves * 64), sm1,   \
+                     stream, q, H_q, H_kv, H_q / H_kv, kv_cache, block_table,      \
+                     bt_ld, seq_lens, reserved_bos, reserved_eos, scale_log2,      \
+                     logits, part, nch)
+  if (D == 128) {
+    if (nld <= 2) SKV_LOGITS(128, 2); else if (nld <= 4) SKV_LOGITS(128, 4);
+    else if (nld <= 8) SKV_LOGITS(128, 8); else SKV_LOGITS(128, 16);
+  } else {
+    if (nld <= 2) SKV_LOGITS(64, 2); else if (nld <= 4) SKV_LOGITS(64, 4);
+    else SKV_LOGITS(64, 8);
+  }
+#undef SKV_LOGITS
   const size_t sm2 = sizeof(float) * 2 * static_cast<size_t>(H_kv);
   hipLaunchKernelGGL(h2o_update_kernel, dim3(static_cast<unsigned>(nupd), static_cast<unsigned>(B)),
-                     dim3(kUpd), sm2, stream, H_kv,
+                     dim3(256), sm2, stream, H_kv,
                      block_table, bt_ld, seq_lens, reserved_bos, reserved_eos,
                      decay_b, hh_score, scores, score_ld, logits, part, nch);
   SKV_CHECK_LAUNCH();
