@@ -138,14 +138,18 @@ __global__ __launch_bounds__(BLOCK) void page_topk_kernel(
     for (int w = 0; w < NW; ++w) { o |= s_or[w]; a &= s_and[w]; }
     const uint32_t diff = o ^ a;       // bits that vary among candidates
     int top = diff ? 31 - __clz(diff) : -1;
+    // bits below the lowest varying one are equal too (bf16-valued scores
+    // leave the low 16 bits of every key the same)
+    const int bot = diff ? __ffs(static_cast<int>(diff)) - 1 : 0;
     pmask = top >= 0 ? ~((2u << top) - 1u) : 0xffffffffu;
     if (top == 31) pmask = 0u;
     prefix = a & pmask;
     int remaining = want;
     int bin = ncand;                   // entries matching the prefix so far
     int pass = 0;
-    while (remaining < bin && top >= 0) {
-      const int shift = top >= kBits - 1 ? top - (kBits - 1) : 0;
+    while (remaining < bin && top >= bot) {
+      int shift = top >= kBits - 1 ? top - (kBits - 1) : 0;
+      if (shift < bot) shift = bot;
       const int width = top - shift + 1;
       const uint32_t dmask = (1u << width) - 1u;
       int* hp = hist[pass];
@@ -297,10 +301,12 @@ extern "C" int page_topk(const float* scores, int64_t score_ld, int B,
   launch_topk<BL, IT>(rows, stream, scores, score_ld, H_sel, seq_lens, page_size, \
                       topk_pages, frac, reserved_bos, reserved_eos, sel_idx,      \
                       sel_cnt, k_cap, block_table, bt_ld, sel_blk)
+  // the widest block that still gives each thread at least 4 entries: more
+  // threads per row shorten every pass (rows are few; each is latency-bound)
   if (score_ld <= 1024) SKV_TOPK(256, 4);
-  else if (score_ld <= 2048) SKV_TOPK(256, 8);
-  else if (score_ld <= 4096) SKV_TOPK(256, 16);
-  else if (score_ld <= 8192) SKV_TOPK(512, 16);
+  else if (score_ld <= 2048) SKV_TOPK(512, 4);
+  else if (score_ld <= 4096) SKV_TOPK(1024, 4);
+  else if (score_ld <= 8192) SKV_TOPK(1024, 8);
   else if (score_ld <= 16384) SKV_TOPK(1024, 16);
   else SKV_TOPK(1024, 32);
 #undef SKV_TOPK
