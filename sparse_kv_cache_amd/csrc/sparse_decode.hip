@@ -27,10 +27,11 @@
 //    registers to the load pipeline and 4 waves per SIMD.  A page that
 //    several heads of a group selected is fetched by each of their waves at
 //    about the same time on one CU and served by L2 after the first read.
-//  * group kernel (one selection shared by the group, the token-level flow):
-//    one block per (split, kv head, request); each wave walks part of the
-//    shared chunk once and applies every query head of the group to the rows
-//    it loaded.
+//  * group kernel (one selection shared by the group: the token-level flow
+//    and group-shared page selection): one block per (split, kv head,
+//    request); each wave walks part of the shared chunk once and applies
+//    every query head of the group to the rows it loaded, on the matrix
+//    cores.
 #include <stdlib.h>
 #include <string.h>
 
@@ -49,52 +50,12 @@ constexpr int kXcds = 8;              // accelerator complex dies of an MI355X
 #endif
 
 // One head, one group of 16 token rows: fold the rows' logits and values into
-// the lane's online-softmax state.  Rows with ok == false were loaded from a
-// placeholder address; their values are replaced, never multiplied.
-template <int LPR, int NL>
-__device__ __forceinline__ void attend_rows(const float (&qq)[8],
-                                            const uint4 (&K)[NL],
-                                            const uint4 (&V)[NL],
-                                            const bool (&ok)[NL], float& m,
-                                            float& l, float (&acc)[8]) {
-  float lg[NL];
-  float mx = m;
-#pragma unroll
-  for (int j = 0; j < NL; ++j) {
-    float x[8];
-    skv::unpack8(K[j], x);
-    float d = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) d = fmaf(qq[i], x[i], d);
-    d = skv::group_sum<LPR>(d);
-    lg[j] = ok[j] ? d : -INFINITY;
-    mx = fmaxf(mx, lg[j]);
-  }
-  if (mx == -INFINITY) return;            // none of this lane's rows yet
-  const float alpha = exp2f(m - mx);      // 0 while m == -inf
-  float pj[NL];
-  float ps = 0.0f;
-#pragma unroll
-  for (int j = 0; j < NL; ++j) { pj[j] = exp2f(lg[j] - mx); ps += pj[j]; }
-  l = fmaf(l, alpha, ps);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] *= alpha;
-#pragma unroll
-  for (int j = 0; j < NL; ++j) {
-    // masked rows: zero the packed words (never multiply a placeholder row)
-    const uint4 vw = ok[j] ? V[j] : make_uint4(0, 0, 0, 0);
-    float v[8];
-    skv::unpack8(vw, v);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = fmaf(pj[j], v[i], acc[i]);
-  }
-  m = mx;
-}
-
-// The same fold with the query split into bf16 hi + lo halves (q ~= hi + lo
-// to about 16 significant bits): each dot product runs on the packed bf16
-// key words with v_dot2c_f32_bf16 (fp32 accumulation, exact bf16 products),
-// so keys are never unpacked.  `full` (wave-uniform) says every row is valid.
+// the lane's online-softmax state.  The query is split into bf16 hi + lo
+// halves (q ~= hi + lo to about 16 significant bits): each dot product runs on
+// the packed bf16 key words with v_dot2c_f32_bf16 (fp32 accumulation, exact
+// bf16 products), so keys are never unpacked.  Rows with ok == false were
+// loaded from a placeholder address: their logits are replaced and their
+// values never multiplied.  `full` (wave-uniform) says every row is valid.
 typedef __bf16 skv_bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
@@ -371,7 +332,30 @@ void sparse_decode_wave_kernel(
 
 // ------------------------------------------------------------ group kernel
 
-template <int D, int GMAX>
+// Matrix-core operand types (gfx950 bf16 MFMA).
+typedef __bf16 skv_bf16x8 __attribute__((ext_vector_type(8)));
+typedef short skv_short4 __attribute__((ext_vector_type(4)));
+typedef float skv_f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ skv_bf16x8 as_bf16x8(uint4 v) {
+  return __builtin_bit_cast(skv_bf16x8, v);
+}
+
+// One block per (split, kv head, request) when the whole query group shares
+// one selection: every selected row is read once and serves all G heads.
+// Per 16-row group a wave computes the G x 16 logit tile and the G x D output
+// update on the matrix cores:
+//   S (16 rows x 16 heads) = K (16 x D) . Q^T (D x 16), K as read (16-byte
+//     row pieces are exactly the A operand of the 16x16x32 bf16 MFMA), Q as
+//     bf16 hi + lo halves (two MFMAs per 32 dims; about 16 significant bits);
+//   O (16 heads x D) += P (16 x 16 rows) . V (16 rows x D), P in the lanes
+//     where S left it (the S tile's layout is the A operand of the 16x16x16
+//     bf16 MFMA), split hi + lo like Q; V is staged through LDS to read it in
+//     the B operand's row-interleaved order.
+// Heads past G carry zero queries and are dropped at the end.  Online softmax
+// state per head lives in the four lanes of its S column; the waves' states
+// are merged through LDS at the end.
+template <int D>
 __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
     const float* __restrict__ q, int H_q, int H_kv, int G,
     const uint16_t* __restrict__ kv, int64_t num_blocks, int P,
@@ -380,64 +364,106 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
     const int32_t* __restrict__ sel_cnt, const int32_t* __restrict__ sel_blk,
     int k_cap, float scale_log2, int num_splits, float* __restrict__ o_part,
     float* __restrict__ lse_part) {
-  constexpr int LPR = D / 8;
-  constexpr int RPL = 64 / LPR;
-  constexpr int NL = 16 / RPL;
+  constexpr int NC = D / 32;            // 32-dim steps of the logit MFMA
+  constexpr int NB = D / 16;            // 16-column blocks of the output MFMA
   constexpr int WAVES = 4;
+  constexpr int VST = D + 4;            // staged V row stride (bf16), skews banks
 
-  __shared__ __align__(16) float qs[GMAX][D];
   __shared__ int32_t e_blk[kMaxEnt];
   __shared__ int32_t e_nv[kMaxEnt];
   __shared__ int s_start, s_len;
-  __shared__ float red_m[WAVES][GMAX], red_l[WAVES][GMAX];
-  __shared__ float red_acc[WAVES][GMAX][D];
+  __shared__ __align__(16) uint16_t vstage[WAVES][16 * VST];
+  __shared__ float red_m[WAVES][16], red_l[WAVES][16];
+  __shared__ __align__(16) float red_o[WAVES][16][D];
 
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int slot = lane / LPR, c = lane % LPR;
+  const int n = lane & 15;              // S column (head) / MFMA row of A
+  const int kq = lane >> 4;             // quarter of the wave
   const int S = seq_lens[b];
   int64_t Nb = (static_cast<int64_t>(S) + P - 1) / P;
   if (Nb > bt_ld) Nb = bt_ld;
   const int row = b * H_kv + h;
 
+  // The chunk's place in the row depends only on k_cap: its first entries
+  // (index and block id) are fetched together with the count, not after it.
+  const int cap = (k_cap + num_splits - 1) / num_splits;
+  const int start = s * cap;
+  int avail = k_cap - start;
+  avail = avail < 0 ? 0 : (avail > cap ? cap : avail);
+  int pre_p = -1, pre_b = -1;
+  if (tid < kMaxEnt && tid < avail) {
+    const int64_t at = static_cast<int64_t>(row) * k_cap + start + tid;
+    pre_p = sel_idx[at];
+    if (sel_blk != nullptr) pre_b = sel_blk[at];
+  }
   if (tid == 0) {
     const Chunk ch = split_chunk(sel_cnt[row], k_cap, num_splits, s);
     s_start = ch.start;
     s_len = ch.len;
   }
-  for (int i = tid; i < GMAX * D; i += blockDim.x) {
-    const int g = i / D, d = i % D;
-    qs[g][d] = g < G ? q[(static_cast<int64_t>(b) * H_q + h * G + g) * D + d] * scale_log2
-                     : 0.0f;
+
+  // Q^T as the B operand: lane holds head n, dims c*32 + 8*kq .. +8, scaled
+  // by scale*log2(e) and split into bf16 hi + lo.
+  uint4 qh[NC], ql[NC];
+  {
+    const bool hv = n < G;
+    const float* qr = q + (static_cast<int64_t>(b) * H_q + h * G + (hv ? n : 0)) * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const float4 xa = *reinterpret_cast<const float4*>(qr + c * 32 + 8 * kq);
+      const float4 xb = *reinterpret_cast<const float4*>(qr + c * 32 + 8 * kq + 4);
+      float x[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = hv ? x[2 * i] * scale_log2 : 0.0f;
+        const float x1 = hv ? x[2 * i + 1] * scale_log2 : 0.0f;
+        const uint16_t h0 = skv::f32_to_bf16(x0), h1 = skv::f32_to_bf16(x1);
+        const uint16_t l0 = skv::f32_to_bf16(x0 - skv::bf16_to_f32(h0));
+        const uint16_t l1 = skv::f32_to_bf16(x1 - skv::bf16_to_f32(h1));
+        hw[i] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+        lw[i] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
+      }
+      qh[c] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      ql[c] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    }
   }
   __syncthreads();
   const int rounds = (s_len + kMaxEnt - 1) / kMaxEnt;
 
-  float m[GMAX], l[GMAX], acc[GMAX][8];
+  float m = -INFINITY, l = 0.0f;       // state of head n
+  skv_f32x4 O[NB];                     // O[head 4*kq + i][blk*16 + n]
 #pragma unroll
-  for (int g = 0; g < GMAX; ++g) {
-    m[g] = -INFINITY; l[g] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[g][i] = 0.0f;
-  }
-  const int64_t head_off = static_cast<int64_t>(h) * D + c * 8;
+  for (int bk = 0; bk < NB; ++bk) O[bk] = skv_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
   const int64_t row_stride = static_cast<int64_t>(H_kv) * D;
   const int64_t v_off = num_blocks * P * row_stride;
+  const int64_t head_off = static_cast<int64_t>(h) * D;
   const int32_t* btr = bt + static_cast<int64_t>(b) * bt_ld;
   const int epg = 16 / P;
+  const int rr = lane & 15;            // row this lane loads (A operand row)
+  uint16_t* vw = vstage[wave];
 
   for (int rd = 0; rd < rounds; ++rd) {
     for (int j = tid; j < kMaxEnt; j += blockDim.x) {
       const int pos = rd * kMaxEnt + j;
       int blk = -1, nv = 0;
       if (pos < s_len) {
-        const int64_t at = static_cast<int64_t>(row) * k_cap + s_start + pos;
-        const int p = sel_idx[at];
+        int p, pb;
+        if (rd == 0) {
+          p = pre_p;                       // fetched above (256 threads: j == tid)
+          pb = pre_b;
+        } else {
+          const int64_t at = static_cast<int64_t>(row) * k_cap + s_start + pos;
+          p = sel_idx[at];
+          pb = sel_blk != nullptr ? sel_blk[at] : -1;
+        }
         if (p >= 0 && p < Nb) {
-          blk = sel_blk != nullptr ? sel_blk[at] : btr[p];
-          const int n = S - p * P;
-          nv = n < P ? n : P;
+          blk = sel_blk != nullptr ? pb : btr[p];
+          const int nn = S - p * P;
+          nv = nn < P ? nn : P;
         }
       }
       e_blk[j] = blk;
@@ -447,32 +473,87 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
     int n_here = s_len - rd * kMaxEnt;
     n_here = n_here > kMaxEnt ? kMaxEnt : n_here;
     const int ngroups = (n_here + epg - 1) / epg;
-    auto load = [&](int grp, uint4 (&K)[NL], uint4 (&V)[NL], bool (&ok)[NL]) {
+
+    // 16-byte pieces of row rr: dims c*32 + 8*kq .. +8 (the A operand layout);
+    // masked rows read row 0 of block 0 so the loads stay unconditional
+    auto load = [&](int grp, uint4 (&Kc)[NC], uint4 (&Vc)[NC], bool& ok) {
+      const int e = grp * epg + rr / P;
+      const int t = rr % P;
+      const int ec = e < kMaxEnt ? e : kMaxEnt - 1;
+      ok = grp < ngroups && e < n_here && t < e_nv[ec];
+      const int64_t off = (ok ? (static_cast<int64_t>(e_blk[ec]) * P + t) * row_stride : 0) +
+                          head_off + 8 * kq;
 #pragma unroll
-      for (int j = 0; j < NL; ++j) {
-        const int rr = slot + RPL * j;
-        const int e = grp * epg + rr / P;
-        const int t = rr % P;
-        const int ec = e < kMaxEnt ? e : kMaxEnt - 1;
-        ok[j] = grp < ngroups && e < n_here && t < e_nv[ec];
-        const int64_t off = ok[j] ? (static_cast<int64_t>(e_blk[ec]) * P + t) * row_stride + head_off
-                                  : head_off;
-        K[j] = *reinterpret_cast<const uint4*>(kv + off);
-        V[j] = *reinterpret_cast<const uint4*>(kv + v_off + off);
+      for (int c = 0; c < NC; ++c) {
+        Kc[c] = *reinterpret_cast<const uint4*>(kv + off + c * 32);
+        Vc[c] = *reinterpret_cast<const uint4*>(kv + v_off + off + c * 32);
       }
     };
-    auto apply = [&](const uint4 (&K)[NL], const uint4 (&V)[NL], const bool (&ok)[NL]) {
+    auto apply = [&](const uint4 (&Kc)[NC], const uint4 (&Vc)[NC], bool ok) {
+      // masked rows stage zeros: a placeholder row is never multiplied
 #pragma unroll
-      for (int g = 0; g < GMAX; ++g) {
-        if (g >= G) continue;
-        const float4 qa = *reinterpret_cast<const float4*>(&qs[g][c * 8]);
-        const float4 qb = *reinterpret_cast<const float4*>(&qs[g][c * 8 + 4]);
-        const float qq[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-        attend_rows<LPR, NL>(qq, K, V, ok, m[g], l[g], acc[g]);
+      for (int c = 0; c < NC; ++c)
+        *reinterpret_cast<uint4*>(vw + rr * VST + c * 32 + 8 * kq) =
+            ok ? Vc[c] : make_uint4(0u, 0u, 0u, 0u);
+      skv_f32x4 sacc = skv_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Kc[c]), as_bf16x8(qh[c]),
+                                                       sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Kc[c]), as_bf16x8(ql[c]),
+                                                       sacc, 0, 0, 0);
       }
+      // rows 4*kq + i of column n; invalid rows (bit clear) drop out
+      const uint64_t okm = __ballot(ok);
+      float sv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sv[i] = ((okm >> (4 * kq + i)) & 1ull) ? sacc[i] : -INFINITY;
+      float tm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      tm = fmaxf(tm, __shfl_xor(tm, 16));
+      tm = fmaxf(tm, __shfl_xor(tm, 32));
+      const float mn = fmaxf(m, tm);
+      float alpha = 1.0f;
+      float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (mn != -INFINITY) {
+        alpha = __builtin_amdgcn_exp2f(m - mn);          // 0 while m == -inf
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ps[i] = __builtin_amdgcn_exp2f(sv[i] - mn);
+        m = mn;
+      }
+      float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      psum += __shfl_xor(psum, 16);
+      psum += __shfl_xor(psum, 32);
+      l = fmaf(l, alpha, psum);
+      // output rows are heads 4*kq + i: their factors sit in lanes 4*kq + i
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kq + i);
+      skv_short4 ph, pl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t hb = skv::f32_to_bf16(ps[i]);
+        ph[i] = static_cast<short>(hb);
+        pl[i] = static_cast<short>(skv::f32_to_bf16(ps[i] - skv::bf16_to_f32(hb)));
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int bk = 0; bk < NB; ++bk) {
+        skv_short4 vb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          vb[i] = static_cast<short>(vw[(4 * kq + i) * VST + bk * 16 + n]);
+        skv_f32x4 o = O[bk];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] *= al[i];
+        o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vb, o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vb, o, 0, 0, 0);
+        O[bk] = o;
+      }
+      __builtin_amdgcn_wave_barrier();
     };
-    uint4 K0[NL], V0[NL], K1[NL], V1[NL];
-    bool o0[NL], o1[NL];
+    uint4 K0[NC], V0[NC], K1[NC], V1[NC];
+    bool o0, o1;
     int grp = wave;
     load(grp, K0, V0, o0);
     while (grp < ngroups) {
@@ -487,16 +568,11 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
     __syncthreads();
   }
 
+  if (lane < 16) { red_m[wave][lane] = m; red_l[wave][lane] = l; }
 #pragma unroll
-  for (int g = 0; g < GMAX; ++g) {
-    if (g >= G) continue;
-    merge_slots<LPR>(m[g], l[g], acc[g]);
-    if (slot == 0) {
+  for (int bk = 0; bk < NB; ++bk)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) red_acc[wave][g][c * 8 + i] = acc[g][i];
-      if (c == 0) { red_m[wave][g] = m[g]; red_l[wave][g] = l[g]; }
-    }
-  }
+    for (int i = 0; i < 4; ++i) red_o[wave][4 * kq + i][bk * 16 + n] = O[bk][i];
   __syncthreads();
   for (int i = tid; i < G * D; i += blockDim.x) {
     const int g = i / D, d = i % D;
@@ -512,9 +588,10 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
     float L = 0.0f, A = 0.0f;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) {
+      if (red_m[w][g] == -INFINITY) continue;
       const float e = exp2f(red_m[w][g] - M);
       L = fmaf(red_l[w][g], e, L);
-      A = fmaf(red_acc[w][g][d], e, A);
+      A = fmaf(red_o[w][g][d], e, A);
     }
     o_part[prow * D + d] = A / L;
     if (d == 0) lse_part[prow] = (M + log2f(L)) * skv::kLn2;
@@ -541,9 +618,9 @@ void launch_wave(hipStream_t st, const Args& a, int64_t n_groups) {
                      a.num_splits, a.o_part, a.lse_part, n_groups, per_group);
 }
 
-template <int D, int GMAX>
+template <int D>
 void launch_group(dim3 grid, hipStream_t st, const Args& a) {
-  hipLaunchKernelGGL((sparse_decode_group_kernel<D, GMAX>), grid, dim3(256), 0, st,
+  hipLaunchKernelGGL((sparse_decode_group_kernel<D>), grid, dim3(256), 0, st,
                      a.q, a.H_q, a.H_kv, a.G, a.kv, a.num_blocks, a.P, a.bt, a.bt_ld,
                      a.seq_lens, a.sel_idx, a.sel_cnt, a.sel_blk, a.k_cap, a.scale_log2,
                      a.num_splits, a.o_part, a.lse_part);
@@ -594,18 +671,8 @@ extern "C" int sparse_paged_decode(const float* q, int B, int H_q, int H_kv,
                seq_lens, sel_idx, sel_cnt, sel_blk, k_cap, scale * skv::kLog2e, num_splits,
                o_part, lse_part};
   if (shared_sel) {
-    const int GM = G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
-    if (D == 128) {
-      if (GM == 2) launch_group<128, 2>(grid, stream, a);
-      else if (GM == 4) launch_group<128, 4>(grid, stream, a);
-      else if (GM == 8) launch_group<128, 8>(grid, stream, a);
-      else launch_group<128, 16>(grid, stream, a);
-    } else {
-      if (GM == 2) launch_group<64, 2>(grid, stream, a);
-      else if (GM == 4) launch_group<64, 4>(grid, stream, a);
-      else if (GM == 8) launch_group<64, 8>(grid, stream, a);
-      else launch_group<64, 16>(grid, stream, a);
-    }
+    if (D == 128) launch_group<128>(grid, stream, a);
+    else launch_group<64>(grid, stream, a);
   } else {
     const int64_t n_groups = static_cast<int64_t>(B) * H_kv;
     const int64_t per_group = (static_cast<int64_t>(num_splits) * G + kWaveBlock - 1) / kWaveBlock;
