@@ -338,6 +338,14 @@ def main():
     gpu_ms = e0.elapsed_time(e1) / args.steps
     ms_per_step = wall * 1000.0 / args.steps
 
+    # algorithmic bytes from the selections of the last timed step's replica
+    # (read before the per-kernel graphs below overwrite the buffers)
+    last = (args.warmup + args.steps - 1)
+    d = decs[last % R]
+    sl_last = wl.seq_lens_at(last % wl.steps)
+    sel_idx = d.sel_idx.cpu().numpy()
+    sel_cnt = d.sel_cnt.cpu().numpy()
+
     # Per-kernel durations: each kernel alone, launched back to back over the
     # replicas inside one graph, timed with HIP events around the replay.
     per_kernel_ms = {}
@@ -355,12 +363,6 @@ def main():
         per_kernel_ms[n] = k0.elapsed_time(k1) / reps
         del g
 
-    # algorithmic bytes from the selections of the last timed step's replica
-    last = (args.warmup + args.steps - 1)
-    d = decs[last % R]
-    sl_last = wl.seq_lens_at(last % wl.steps)
-    sel_idx = d.sel_idx.cpu().numpy()
-    sel_cnt = d.sel_cnt.cpu().numpy()
     kb, upages = kernel_bytes(wl, sel_idx, sel_cnt, sl_last, wl.num_splits, token_level,
                               group)
     step_bytes = sum(kb.values())
@@ -374,7 +376,8 @@ def main():
     a = kb[focus] / (per_kernel_ms[focus] * 1e-3) / 1e9
     roofline = {"kernel": focus, "bound": "hbm", "achieved": round(a, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(a / PEAK_HBM_GBPS, 4),
-                "traffic": profiled_traffic(wl.name), "bytes_per_launch": kb[focus],
+                "traffic": profiled_traffic(wl.name + ("_group" if group else "")),
+                "bytes_per_launch": kb[focus],
                 "us_per_launch": round(per_kernel_ms[focus] * 1000, 2)}
 
     result = {

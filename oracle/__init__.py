@@ -52,12 +52,16 @@ def _load():
                                       i32, f64, f64, P, i64]
     lib.oracle_page_score_group.argtypes = [P, i32, i32, i32, i32, P, P, P, P, i64, P,
                                       i32, f64, f64, P, i64]
+    lib.oracle_page_score_alibi.argtypes = [P, i32, i32, i32, i32, P, P, P, P, i64, P,
+                                            i32, f64, f64, P, i32, P, i64]
     lib.oracle_budget.argtypes = [i32, i32, f64]
     lib.oracle_budget.restype = i32
     lib.oracle_select.argtypes = [P, i32, i32, f64, i32, i32, P]
     lib.oracle_select.restype = i32
     lib.oracle_attend.argtypes = [P, i32, P, i64, i32, i32, i32, P, i32, P, i32,
                                   f64, P, P]
+    lib.oracle_attend_alibi.argtypes = [P, i32, P, i64, i32, i32, i32, P, i32, P, i32,
+                                        f64, f64, P, P]
     lib.oracle_lse_merge.argtypes = [P, P, i32, i32, P, P]
     lib.oracle_append.argtypes = [P, i64, i32, i32, i32, P, i64, P, i32, P, P, P]
     lib.oracle_h2o_recurrence.argtypes = [P, P, i32, f64]
@@ -190,6 +194,43 @@ def attend(q_row, kv_cache, kv_head, bt_row, seq_len, pages, scale):
                       int(seq_len), _ptr(pg), pg.shape[0], float(scale),
                       _ptr(o), _ptr(lse))
     return o, float(lse[0])
+
+
+def attend_alibi(q_row, kv_cache, kv_head, bt_row, seq_len, pages, scale, slope):
+    """attend() with the ALiBi bias slope * (t - (seq_len - 1)) on each logit."""
+    lib = _load()
+    qd = _c(q_row, np.float64)
+    kv = _c(kv_cache, np.uint16)
+    _, NB, P, H_kv, D = kv.shape
+    bt = _c(bt_row, np.int32)
+    pg = _c(pages, np.int32)
+    o = np.zeros(D)
+    lse = np.zeros(1)
+    lib.oracle_attend_alibi(_ptr(qd), D, _ptr(kv), NB, P, H_kv, int(kv_head), _ptr(bt),
+                            int(seq_len), _ptr(pg), pg.shape[0], float(scale),
+                            float(slope), _ptr(o), _ptr(lse))
+    return o, float(lse[0])
+
+
+def page_score_alibi(q, kmin, kmax, kmean, block_table, seq_lens, page_size,
+                     w_avg, w_peak, alibi, aggregate=False, ld=None):
+    """ALiBi-aware page scores: [B, H_q, ld], or [B, H_kv, ld] group means when
+    aggregate; alibi [H_q] in score units (slope / softmax scale)."""
+    lib = _load()
+    qd = _c(q, np.float64)
+    B, H_q, D = qd.shape
+    mn, mx, me = (_c(a, np.float64) for a in (kmin, kmax, kmean))
+    H_kv = mn.shape[1]
+    bt = _c(block_table, np.int32)
+    sl = _c(seq_lens, np.int32)
+    al = _c(alibi, np.float64)
+    if ld is None:
+        ld = bt.shape[1]
+    s = np.full((B, H_kv if aggregate else H_q, ld), np.nan)
+    lib.oracle_page_score_alibi(_ptr(qd), B, H_q, H_kv, D, _ptr(mn), _ptr(mx), _ptr(me),
+                                _ptr(bt), bt.shape[1], _ptr(sl), page_size, float(w_avg),
+                                float(w_peak), _ptr(al), int(bool(aggregate)), _ptr(s), ld)
+    return s
 
 
 def lse_merge(o_parts, lses):

@@ -212,6 +212,61 @@ void oracle_page_score_group(const double *q, int B, int H_q, int H_kv, int D,
     }
 }
 
+/* ALiBi-aware page score.  EntmaxKV README "How it works": the page bound
+ * includes the ALiBi bias at the page's best logical position.  A key at
+ * position t of a request with S tokens gets the logit bias
+ * slope_i * (t - (S - 1)) <= 0 (the query sits at S - 1), so in the score's
+ * q.k units each term takes alibi_i = slope_i / scale times the offset of the
+ * position it describes: the peak term (a bound on the page's best logit) at
+ * the page's last valid position, the mean term (the page's mean logit) at
+ * the mean of its valid positions.
+ *   alibi     [H_q] per query head, score units (slope / softmax scale)
+ *   aggregate 0: scores [B, H_q, ld]; 1: scores [B, H_kv, ld] = the mean over
+ *             each kv head's query group (as oracle_page_score_group). */
+void oracle_page_score_alibi(const double *q, int B, int H_q, int H_kv, int D,
+                             const double *kmin, const double *kmax,
+                             const double *kmean, const int32_t *block_table,
+                             int64_t bt_ld, const int32_t *seq_lens, int P,
+                             double w_avg, double w_peak, const double *alibi,
+                             int aggregate, double *scores, int64_t ld)
+{
+    int G = H_q / H_kv;
+    for (int b = 0; b < B; ++b) {
+        int S = seq_lens[b];
+        int N = pages_of(S, P);
+        for (int h = 0; h < H_kv; ++h) {
+            for (int p = 0; p < N; ++p) {
+                int64_t blk = block_table[(int64_t)b * bt_ld + p];
+                const double *mn = kmin + (blk * H_kv + h) * D;
+                const double *mx = kmax + (blk * H_kv + h) * D;
+                const double *me = kmean + (blk * H_kv + h) * D;
+                int n = S - p * P < P ? S - p * P : P;
+                double last = (double)p * P + (n - 1) - (double)(S - 1);
+                double mid = (double)p * P + 0.5 * (n - 1) - (double)(S - 1);
+                double total = 0.0;
+                for (int g = 0; g < G; ++g) {
+                    int i = h * G + g;
+                    const double *qi = q + ((int64_t)b * H_q + i) * D;
+                    double avg = 0.0, peak = 0.0;
+                    for (int d = 0; d < D; ++d) {
+                        avg += qi[d] * me[d];
+                        double up = qi[d] * mx[d], lo = qi[d] * mn[d];
+                        peak += up > lo ? up : lo;
+                    }
+                    double s = w_avg * (avg + alibi[i] * mid) +
+                               w_peak * (peak + alibi[i] * last);
+                    if (aggregate)
+                        total += s;
+                    else
+                        scores[((int64_t)b * H_q + i) * ld + p] = s;
+                }
+                if (aggregate)
+                    scores[((int64_t)b * H_kv + h) * ld + p] = total / G;
+            }
+        }
+    }
+}
+
 /* --------------------------------------------------------- selection (O4) */
 
 struct ranked {
@@ -327,6 +382,62 @@ void oracle_attend(const double *q, int D, const uint16_t *kv_cache,
         if (logit[t] > m) m = logit[t];
     }
     /* pass 2: normaliser and weighted sum of values */
+    double Z = 0.0;
+    for (t = 0; t < ntok; ++t) {
+        double w = exp(logit[t] - m);
+        Z += w;
+        for (int d = 0; d < D; ++d)
+            o[d] += w * oracle_bf16_to_double(kv_cache[cache_index(
+                        1, blk[t], row[t], kv_head, d, num_blocks, P, H_kv, D)]);
+    }
+    for (int d = 0; d < D; ++d)
+        o[d] /= Z;
+    *lse = m + log(Z);
+    free(logit);
+    free(blk);
+    free(row);
+}
+
+/* The same attention with an ALiBi bias: logit_t = scale * q.k_t +
+ * slope * (t - (S - 1)) for a key at logical position t (EntmaxKV README "How
+ * it works" names ALiBi heads; the bias is the standard linear one, zero at
+ * the query's own position). */
+void oracle_attend_alibi(const double *q, int D, const uint16_t *kv_cache,
+                         int64_t num_blocks, int P, int H_kv, int kv_head,
+                         const int32_t *bt_row, int S, const int32_t *pages,
+                         int npages, double scale, double slope, double *o,
+                         double *lse)
+{
+    int ntok = 0;
+    for (int j = 0; j < npages; ++j) {
+        int n = S - pages[j] * P < P ? S - pages[j] * P : P;
+        ntok += n > 0 ? n : 0;
+    }
+    for (int d = 0; d < D; ++d)
+        o[d] = 0.0;
+    if (ntok == 0) {
+        *lse = -INFINITY;
+        return;
+    }
+    double *logit = malloc(sizeof *logit * ntok);
+    int64_t *blk = malloc(sizeof *blk * ntok);
+    int *row = malloc(sizeof *row * ntok);
+    int t = 0;
+    double m = -INFINITY;
+    for (int j = 0; j < npages; ++j) {
+        int n = S - pages[j] * P < P ? S - pages[j] * P : P;
+        for (int r = 0; r < n; ++r, ++t) {
+            blk[t] = bt_row[pages[j]];
+            row[t] = r;
+            double dot = 0.0;
+            for (int d = 0; d < D; ++d)
+                dot += q[d] * oracle_bf16_to_double(kv_cache[cache_index(
+                           0, blk[t], r, kv_head, d, num_blocks, P, H_kv, D)]);
+            double pos = (double)pages[j] * P + r;
+            logit[t] = scale * dot + slope * (pos - (double)(S - 1));
+            if (logit[t] > m) m = logit[t];
+        }
+    }
     double Z = 0.0;
     for (t = 0; t < ntok; ++t) {
         double w = exp(logit[t] - m);

@@ -106,7 +106,7 @@ def h2o_token(seed: int = 3, steps: int = 256, prompt: int = 4096,
     return Workload("h2o_token", B=B, H_q=32, H_kv=8, D=128, P=1,
                     num_blocks=B * ld,
                     seq_lens=np.full(B, prompt, dtype=np.int32), block_table=bt,
-                    topk_pages=512, bos=0, eos=1, num_splits=4, steps=steps,
+                    topk_pages=512, bos=0, eos=1, num_splits=8, steps=steps,
                     q_bf16=True, seed=seed)
 
 
