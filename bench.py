@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--select", default="head", choices=["head", "group"],
                     help="page level: select per query head, or once per kv head "
                          "from the group's mean score (shared by the group)")
+    ap.add_argument("--alibi", action="store_true",
+                    help="page level: standard ALiBi slopes 2^(-8(i+1)/H_q) in scoring "
+                         "and decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="enqueue kernel by kernel instead of replaying HIP graphs")
@@ -218,7 +221,7 @@ def main():
     import torch
     import sparse_kv_cache_amd  # noqa: F401  (loads lazily; fails loudly if unbuilt)
     from sparse_kv_cache_amd import workloads as W
-    from sparse_kv_cache_amd.decode import SparseDecoder
+    from sparse_kv_cache_amd.decode import SparseDecoder, alibi_slopes
 
     sparse_kv_cache_amd.load_library()
     torch.cuda.init()
@@ -239,7 +242,9 @@ def main():
         R = 1
     caches = [cache0] + [cache0.clone() for _ in range(R - 1)]
     group = args.select == "group" and not token_level
-    decs = [SparseDecoder.for_workload(wl, device=dev, group_select=group)
+    slopes = alibi_slopes(wl.H_q, dev) if (args.alibi and not token_level) else None
+    decs = [SparseDecoder.for_workload(wl, device=dev, group_select=group,
+                                       alibi_slopes=slopes)
             for _ in range(R)]
     new_kv = [W.make_new_kv(wl, s, device=dev) for s in range(min(wl.steps, 64))] \
         if wl.steps > 1 else None
@@ -376,7 +381,8 @@ def main():
     a = kb[focus] / (per_kernel_ms[focus] * 1e-3) / 1e9
     roofline = {"kernel": focus, "bound": "hbm", "achieved": round(a, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(a / PEAK_HBM_GBPS, 4),
-                "traffic": profiled_traffic(wl.name + ("_group" if group else "")),
+                "traffic": profiled_traffic(wl.name + ("_group" if group else "")
+                                            + ("_alibi" if slopes is not None else "")),
                 "bytes_per_launch": kb[focus],
                 "us_per_launch": round(per_kernel_ms[focus] * 1000, 2)}
 
@@ -394,6 +400,7 @@ def main():
                    "topk_frac": wl.topk_frac, "num_splits": wl.num_splits,
                    "mean_seq_len": float(np.mean(sl_last)), "replicas": R,
                    "selection": ("kv_head" if (group or token_level) else "query_head"),
+                   "alibi": slopes is not None,
                    "parallelism": "single-gpu"},
         "effective_GBps": round(step_bytes / (gpu_ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(step_bytes / (gpu_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),

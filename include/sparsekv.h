@@ -101,6 +101,13 @@ int pagestats_update(uint16_t *kv_cache, int64_t num_blocks, int page_size,
  *   k_min, k_max bf16 / k_mean fp32 [num_blocks, H_kv, D] (from pagestats_update)
  *   scores   fp32 [B, H_q, score_ld], logical page order; entries p >= N_b
  *            are not written.  score_ld >= bt_ld.
+ *   alibi    fp32 [H_q] or NULL.  For ALiBi heads [EKV "How it works": the
+ *            page bound includes ALiBi at each page's best logical position]:
+ *            the slope of each query head DIVIDED BY the softmax scale (the
+ *            score is in q.k units).  A key at position t of a request of S
+ *            tokens has logit bias slope * (t - (S - 1)); the peak term takes
+ *            the bias of the page's last valid position (its best), the mean
+ *            term that of the mean of its valid positions.  NULL: no bias.
  * The softmax scale is not applied (a positive factor does not change ranks).
  */
 int page_score(const float *q, int B, int H_q, int H_kv, int D,
@@ -108,7 +115,7 @@ int page_score(const float *q, int B, int H_q, int H_kv, int D,
                const float *k_mean, const int32_t *block_table, int64_t bt_ld,
                const int32_t *seq_lens, int page_size, float w_avg,
                float w_peak, float *scores, int64_t score_ld,
-               hipStream_t stream);
+               const float *alibi, hipStream_t stream);
 
 /*
  * page_score_group -- one score per (request, kv head, page): the mean, over
@@ -121,6 +128,8 @@ int page_score(const float *q, int B, int H_q, int H_kv, int D,
  *
  *   Arguments and layouts as page_score, except
  *   scores   fp32 [B, H_kv, score_ld]; entries p >= N_b are not written.
+ *   alibi    as page_score; the group's mean slope applies (the mean of the
+ *            group's biased scores).
  * The mean is formed per dim from the group's mean query and mean |q|
  * (mean_g max(q_g max, q_g min) summed over d equals the mean of the
  * per-head peaks exactly), so its cost does not grow with G.
@@ -130,7 +139,7 @@ int page_score_group(const float *q, int B, int H_q, int H_kv, int D,
                      const float *k_mean, const int32_t *block_table,
                      int64_t bt_ld, const int32_t *seq_lens, int page_size,
                      float w_avg, float w_peak, float *scores, int64_t score_ld,
-                     hipStream_t stream);
+                     const float *alibi, hipStream_t stream);
 
 /*
  * page_topk -- top-k selection per row (b, h), h < H_sel.
@@ -180,6 +189,9 @@ int page_topk(const float *scores, int64_t score_ld, int B, int H_sel,
  *                                               with o_part = 0)
  *   sel_blk (nullable) is page_topk's block-id output for the same rows;
  *   when given, the block table is not read.
+ *   alibi_slopes fp32 [H_q] or NULL: per query head ALiBi slope; the logit
+ *   of the key at position t becomes l = scale * q . k + slope * (t - (S_b - 1))
+ *   [EKV "How it works": ALiBi heads].  NULL: no bias.
  *   With H_sel == H_kv every row a block loads serves all G query heads of
  *   the group; with H_sel == H_q each query head's chunk is walked by its own
  *   wave(s), and pages shared by heads of a group are served by the caches
@@ -192,7 +204,8 @@ int sparse_paged_decode(const float *q, int B, int H_q, int H_kv, int D,
                         const int32_t *sel_idx, const int32_t *sel_cnt,
                         const int32_t *sel_blk, int k_cap, int H_sel,
                         float scale, int num_splits, float *o_part,
-                        float *lse_part, hipStream_t stream);
+                        float *lse_part, const float *alibi_slopes,
+                        hipStream_t stream);
 
 /*
  * lse_merge -- N-way log-sum-exp merge of split partials.  [MLA:

@@ -62,11 +62,11 @@ def load_library():
     lib.sparsekv_last_error.restype = ctypes.c_char_p
     lib.sparsekv_last_error.argtypes = []
     lib.pagestats_update.argtypes = [V, L, I, I, I, V, V, V, V, L, V, I, V, V, V, V]
-    lib.page_score.argtypes = [V, I, I, I, I, V, V, V, V, L, V, I, F, F, V, L, V]
+    lib.page_score.argtypes = [V, I, I, I, I, V, V, V, V, L, V, I, F, F, V, L, V, V]
     lib.page_score_group.argtypes = lib.page_score.argtypes
     lib.page_topk.argtypes = [V, L, I, I, V, I, I, F, I, I, V, V, I, V, L, V, V]
     lib.sparse_paged_decode.argtypes = [V, I, I, I, I, V, L, I, V, L, V, V, V, V, I,
-                                        I, F, I, V, V, V]
+                                        I, F, I, V, V, V, V]
     lib.lse_merge.argtypes = [V, V, I, I, I, V, V, V]
     lib.h2o_accumulate.argtypes = [V, I, I, I, I, V, L, I, V, L, V, I, I, F, F, V, V,
                                    L, V, L, V]
@@ -167,29 +167,43 @@ def _score_args(q, k_min, k_max, k_mean, block_table, seq_lens, scores, H_out):
     return B, H_q, H_kv, D
 
 
+def _alibi_arg(alibi, H_q, dev):
+    if alibi is None:
+        return None
+    _check("alibi", alibi, torch.float32, 1, dev)
+    if alibi.shape[0] != H_q:
+        raise ValueError("ALiBi slopes must be [H_q]")
+    return alibi
+
+
 def page_score(q, k_min, k_max, k_mean, block_table, seq_lens, page_size,
-               w_avg, w_peak, scores, stream=None):
-    """scores[b, i, p] ([B, H_q, score_ld]) for p < N_b from the page statistics."""
+               w_avg, w_peak, scores, alibi=None, stream=None):
+    """scores[b, i, p] ([B, H_q, score_ld]) for p < N_b from the page statistics;
+    alibi ([H_q], optional) = ALiBi slopes divided by the softmax scale."""
     lib = load_library()
     B, H_q, H_kv, D = _score_args(q, k_min, k_max, k_mean, block_table, seq_lens,
                                   scores, lambda hq, hkv: hq)
+    alibi = _alibi_arg(alibi, H_q, q.device)
     _rc("page_score", lib.page_score(
         _ptr(q), B, H_q, H_kv, D, _ptr(k_min), _ptr(k_max), _ptr(k_mean),
         _ptr(block_table), block_table.shape[1], _ptr(seq_lens), int(page_size),
-        float(w_avg), float(w_peak), _ptr(scores), scores.shape[2], _stream(stream)))
+        float(w_avg), float(w_peak), _ptr(scores), scores.shape[2], _ptr(alibi),
+        _stream(stream)))
 
 
 def page_score_group(q, k_min, k_max, k_mean, block_table, seq_lens, page_size,
-                     w_avg, w_peak, scores, stream=None):
+                     w_avg, w_peak, scores, alibi=None, stream=None):
     """scores[b, h, p] ([B, H_kv, score_ld]): the mean of the kv head's query
     group's page scores, for one selection per kv head."""
     lib = load_library()
     B, H_q, H_kv, D = _score_args(q, k_min, k_max, k_mean, block_table, seq_lens,
                                   scores, lambda hq, hkv: hkv)
+    alibi = _alibi_arg(alibi, H_q, q.device)
     _rc("page_score_group", lib.page_score_group(
         _ptr(q), B, H_q, H_kv, D, _ptr(k_min), _ptr(k_max), _ptr(k_mean),
         _ptr(block_table), block_table.shape[1], _ptr(seq_lens), int(page_size),
-        float(w_avg), float(w_peak), _ptr(scores), scores.shape[2], _stream(stream)))
+        float(w_avg), float(w_peak), _ptr(scores), scores.shape[2], _ptr(alibi),
+        _stream(stream)))
 
 
 def page_topk(scores, seq_lens, page_size, topk_pages, sel_idx, sel_cnt,
@@ -224,9 +238,11 @@ def page_topk(scores, seq_lens, page_size, topk_pages, sel_idx, sel_cnt,
 
 
 def sparse_paged_decode(q, kv_cache, block_table, seq_lens, sel_idx, sel_cnt,
-                        scale, o_part, lse_part, sel_blk=None, stream=None):
+                        scale, o_part, lse_part, sel_blk=None, alibi_slopes=None,
+                        stream=None):
     """Split-K partials over the selected pages.  H_sel = sel_idx.shape[1];
-    num_splits = o_part.shape[2]; sel_blk (optional) from page_topk."""
+    num_splits = o_part.shape[2]; sel_blk (optional) from page_topk;
+    alibi_slopes ([H_q], optional) ALiBi slopes."""
     lib = load_library()
     _check("q", q, torch.float32, 3)
     dev = q.device
@@ -250,11 +266,12 @@ def sparse_paged_decode(q, kv_cache, block_table, seq_lens, sel_idx, sel_cnt,
     _check("sel_blk", sel_blk, torch.int32, 3, dev)
     if sel_blk is not None and sel_blk.shape != sel_idx.shape:
         raise ValueError("sel_blk must have sel_idx's shape")
+    alibi_slopes = _alibi_arg(alibi_slopes, H_q, dev)
     _rc("sparse_paged_decode", lib.sparse_paged_decode(
         _ptr(q), B, H_q, H_kv, D, _ptr(kv_cache), NB, P, _ptr(block_table),
         block_table.shape[1], _ptr(seq_lens), _ptr(sel_idx), _ptr(sel_cnt),
         _ptr(sel_blk), sel_idx.shape[2], H_sel, float(scale), ns, _ptr(o_part),
-        _ptr(lse_part), _stream(stream)))
+        _ptr(lse_part), _ptr(alibi_slopes), _stream(stream)))
 
 
 def lse_merge(o_part, lse_part, out, lse_out=None, stream=None):

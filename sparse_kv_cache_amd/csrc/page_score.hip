@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void page_score_kernel(
     const float* __restrict__ kmean, const int32_t* __restrict__ bt,
     int64_t bt_ld, const int32_t* __restrict__ seq_lens, int P, float w_avg,
     float w_peak, float* __restrict__ scores, int64_t score_ld,
-    int64_t max_pages) {
+    int64_t max_pages, const float* __restrict__ alibi) {
   constexpr int LPR = D / 8;          // lanes per page-head
   constexpr int PPW = 64 / LPR;       // page-heads per wave load
   constexpr int TILE = kIter * kWaves * PPW;
@@ -55,6 +55,18 @@ __global__ __launch_bounds__(256) void page_score_kernel(
   const int wave = threadIdx.x >> 6;
   const int sub = lane / LPR;
   const int c = lane % LPR;
+
+  // ALiBi slope (score units) of the head this lane writes: the group's mean
+  // for the group score
+  float slope = 0.0f;
+  if (alibi != nullptr) {
+    if constexpr (AGG) {
+      for (int g = 0; g < G; ++g) slope += alibi[h * G + g];
+      slope /= static_cast<float>(G);
+    } else {
+      slope = c < GS && g0 + c < G ? alibi[h * G + g0 + c] : 0.0f;
+    }
+  }
 
   const int32_t* btr = bt + static_cast<int64_t>(b) * bt_ld;
   uint4 mn[kIter], mx[kIter];
@@ -113,6 +125,16 @@ __global__ __launch_bounds__(256) void page_score_kernel(
       mp[i] = fmaf(w_avg, me[i], w_peak * mid);
       hp[i] = w_peak * half;
     }
+    // ALiBi at the page's last (peak term) and mean (mean term) valid
+    // positions, relative to the query at S - 1
+    float bias = 0.0f;
+    if (alibi != nullptr) {
+      const int64_t pp = pg[it] < N ? pg[it] : p0;
+      const int64_t nn = static_cast<int64_t>(S) - pp * P;
+      const float n = static_cast<float>(nn < P ? nn : P);
+      const float first = static_cast<float>(pp * P - (S - 1));
+      bias = slope * fmaf(w_avg, first + 0.5f * (n - 1.0f), w_peak * (first + n - 1.0f));
+    }
     if constexpr (AGG) {
       const float4 qa = *reinterpret_cast<const float4*>(&qs[0][c * 8]);
       const float4 qb = *reinterpret_cast<const float4*>(&qs[0][c * 8 + 4]);
@@ -125,7 +147,7 @@ __global__ __launch_bounds__(256) void page_score_kernel(
       for (int i = 0; i < 8; ++i) s = fmaf(qv[i], mp[i], fmaf(av[i], hp[i], s));
       s = skv::group_sum<LPR>(s);
       if (pg[it] < N && c == 0)
-        scores[(static_cast<int64_t>(b) * H_kv + h) * score_ld + pg[it]] = s;
+        scores[(static_cast<int64_t>(b) * H_kv + h) * score_ld + pg[it]] = s + bias;
     } else {
       float mine = 0.0f;
 #pragma unroll
@@ -140,7 +162,7 @@ __global__ __launch_bounds__(256) void page_score_kernel(
         if (c == g) mine = s;
       }
       if (pg[it] < N && c < GS && g0 + c < G)
-        scores[(static_cast<int64_t>(b) * H_q + h * G + g0 + c) * score_ld + pg[it]] = mine;
+        scores[(static_cast<int64_t>(b) * H_q + h * G + g0 + c) * score_ld + pg[it]] = mine + bias;
     }
   }
 }
@@ -150,10 +172,11 @@ void launch_score(dim3 grid, hipStream_t stream, const float* q, int H_q,
                   int H_kv, int G, const uint16_t* kmin, const uint16_t* kmax,
                   const float* kmean, const int32_t* bt, int64_t bt_ld,
                   const int32_t* seq_lens, int P, float w_avg, float w_peak,
-                  float* scores, int64_t score_ld, int64_t max_pages) {
+                  float* scores, int64_t score_ld, int64_t max_pages,
+                  const float* alibi) {
   hipLaunchKernelGGL((page_score_kernel<D, GS, AGG>), grid, dim3(256), 0, stream, q,
                      H_q, H_kv, G, kmin, kmax, kmean, bt, bt_ld, seq_lens, P,
-                     w_avg, w_peak, scores, score_ld, max_pages);
+                     w_avg, w_peak, scores, score_ld, max_pages, alibi);
 }
 
 // Shared by both entry points: validation, grid, dispatch on (D, group size).
@@ -161,7 +184,8 @@ int score_pages(const char* who, bool group, const float* q, int B, int H_q,
                 int H_kv, int D, const uint16_t* k_min, const uint16_t* k_max,
                 const float* k_mean, const int32_t* block_table, int64_t bt_ld,
                 const int32_t* seq_lens, int page_size, float w_avg, float w_peak,
-                float* scores, int64_t score_ld, hipStream_t stream) {
+                float* scores, int64_t score_ld, const float* alibi,
+                hipStream_t stream) {
   SKV_REQUIRE(B >= 0 && H_kv > 0 && H_q > 0 && H_q % H_kv == 0,
               "%s: need H_q a positive multiple of H_kv (H_q=%d, H_kv=%d)", who, H_q, H_kv);
   const int G = H_q / H_kv;
@@ -192,7 +216,7 @@ int score_pages(const char* who, bool group, const float* q, int B, int H_q,
 #define SKV_SCORE(DD, GG, AA)                                                    \
   launch_score<DD, GG, AA>(grid, stream, q, H_q, H_kv, G, k_min, k_max, k_mean,   \
                            block_table, bt_ld, seq_lens, page_size, w_avg,      \
-                           w_peak, scores, score_ld, max_pages)
+                           w_peak, scores, score_ld, max_pages, alibi)
   if (group) {
     if (D == 128) SKV_SCORE(128, 1, true); else SKV_SCORE(64, 1, true);
   } else if (D == 128) {
@@ -213,10 +237,10 @@ extern "C" int page_score(const float* q, int B, int H_q, int H_kv, int D,
                           const float* k_mean, const int32_t* block_table,
                           int64_t bt_ld, const int32_t* seq_lens, int page_size,
                           float w_avg, float w_peak, float* scores,
-                          int64_t score_ld, hipStream_t stream) {
+                          int64_t score_ld, const float* alibi, hipStream_t stream) {
   return score_pages("page_score", false, q, B, H_q, H_kv, D, k_min, k_max, k_mean,
                      block_table, bt_ld, seq_lens, page_size, w_avg, w_peak, scores,
-                     score_ld, stream);
+                     score_ld, alibi, stream);
 }
 
 extern "C" int page_score_group(const float* q, int B, int H_q, int H_kv, int D,
@@ -224,8 +248,9 @@ extern "C" int page_score_group(const float* q, int B, int H_q, int H_kv, int D,
                                 const float* k_mean, const int32_t* block_table,
                                 int64_t bt_ld, const int32_t* seq_lens,
                                 int page_size, float w_avg, float w_peak,
-                                float* scores, int64_t score_ld, hipStream_t stream) {
+                                float* scores, int64_t score_ld, const float* alibi,
+                                hipStream_t stream) {
   return score_pages("page_score_group", true, q, B, H_q, H_kv, D, k_min, k_max,
                      k_mean, block_table, bt_ld, seq_lens, page_size, w_avg, w_peak,
-                     scores, score_ld, stream);
+                     scores, score_ld, alibi, stream);
 }

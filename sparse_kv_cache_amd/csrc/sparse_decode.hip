@@ -75,12 +75,15 @@ __device__ __forceinline__ void split_query(const float (&qq)[8], uint32_t (&qh)
   }
 }
 
-template <int LPR, int NL>
+// With AL, row j's logit also gets slope2 * pos[j] (ALiBi, base-2 units;
+// pos = key position - query position <= 0).
+template <int LPR, int NL, bool AL>
 __device__ __forceinline__ void attend_rows_split(const uint32_t (&qh)[4],
                                                   const uint32_t (&ql)[4],
                                                   const uint4 (&K)[NL],
                                                   const uint4 (&V)[NL],
                                                   const bool (&ok)[NL], bool full,
+                                                  const float (&pos)[NL], float slope2,
                                                   float& m, float& l,
                                                   float (&acc)[8]) {
   float lg[NL];
@@ -93,6 +96,7 @@ __device__ __forceinline__ void attend_rows_split(const uint32_t (&qh)[4],
     d = dot2(K[j].z, qh[2], d); d = dot2(K[j].z, ql[2], d);
     d = dot2(K[j].w, qh[3], d); d = dot2(K[j].w, ql[3], d);
     d = skv::group_sum<LPR>(d);
+    if constexpr (AL) d = fmaf(slope2, pos[j], d);   // after the row sum
     lg[j] = ok[j] ? d : -INFINITY;
     mx = fmaxf(mx, lg[j]);
   }
@@ -171,7 +175,7 @@ __device__ __forceinline__ Chunk split_chunk(int cnt, int k_cap, int num_splits,
 // share a block, and all blocks of the (request, kv head) go to one XCD:
 // pages several heads selected are fetched through one L2 at about the same
 // time.
-template <int D, int WB, int PFIX>
+template <int D, int WB, int PFIX, bool AL>
 __global__ __launch_bounds__(WB * 64)
 __attribute__((amdgpu_waves_per_eu(PFIX == 16 ? SKV_DECODE_WPE16 : SKV_DECODE_WPE)))
 void sparse_decode_wave_kernel(
@@ -181,7 +185,8 @@ void sparse_decode_wave_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_idx,
     const int32_t* __restrict__ sel_cnt, const int32_t* __restrict__ sel_blk,
     int k_cap, float scale_log2, int num_splits, float* __restrict__ o_part,
-    float* __restrict__ lse_part, int64_t n_groups, int blocks_per_group) {
+    float* __restrict__ lse_part, int64_t n_groups, int blocks_per_group,
+    const float* __restrict__ alibi) {
   constexpr int LPR = D / 8;
   constexpr int RPL = 64 / LPR;
   constexpr int NL = 16 / RPL;
@@ -231,6 +236,13 @@ void sparse_decode_wave_kernel(
   }
   uint32_t qh[4], ql[4];
   split_query(qq, qh, ql);
+  // ALiBi slope of this head in base-2 logit units.  Biases are taken
+  // relative to the chunk's last selected page (the largest bias, where the
+  // weight concentrates), so the fold works with small, exact offsets; the
+  // common offset returns in the split's lse.
+  const float slope2 = AL ? alibi[h * G + g] * skv::kLog2e : 0.0f;
+  int pref = 0;
+  if (AL && clen > 0) pref = selr[clen - 1];
   float m = -INFINITY, l = 0.0f, acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
@@ -249,14 +261,17 @@ void sparse_decode_wave_kernel(
     }
     const int nw = min(64, clen - w0);
     if (nw <= 0) break;
-    int my_blk = 0, my_nv = 0;
+    int my_blk = 0, my_nv = 0, my_pg = 0;
     if (lane < nw && p >= 0 && p < Nb) {
+      my_pg = p;
       my_blk = sblk != nullptr ? sb : btr[p];
       const int n = S - p * P;
       my_nv = n < P ? n : P;
     }
     const int ngroups = (nw + epg - 1) / epg;
-    auto load = [&](int grp, uint4 (&K)[NL], uint4 (&V)[NL], bool (&ok)[NL], bool& full) {
+    // pos (ALiBi only): key position minus the query's (S - 1), per row
+    auto load = [&](int grp, uint4 (&K)[NL], uint4 (&V)[NL], bool (&ok)[NL], bool& full,
+                    float (&pos)[NL]) {
       if constexpr (PFIX == 16) {
         // one page per group: its block id and row count are wave-uniform
         // (read from lane grp), so the row addresses are a scalar page base
@@ -265,6 +280,12 @@ void sparse_decode_wave_kernel(
         const int blk = __builtin_amdgcn_readlane(my_blk, gc);
         const int nv = grp < nw ? __builtin_amdgcn_readlane(my_nv, gc) : 0;
         full = nv == 16;
+        if constexpr (AL) {
+          const int pg = __builtin_amdgcn_readlane(my_pg, gc);
+#pragma unroll
+          for (int j = 0; j < NL; ++j)
+            pos[j] = static_cast<float>((pg - pref) * 16 + slot + RPL * j);
+        }
         const uint16_t* kp = kv + static_cast<int64_t>(blk) * 16 * row_stride;
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
@@ -285,6 +306,7 @@ void sparse_decode_wave_kernel(
         const int ec = e < 64 ? e : 63;
         const int blk = __shfl(my_blk, ec);
         const int nv = __shfl(my_nv, ec);
+        if constexpr (AL) pos[j] = static_cast<float>((__shfl(my_pg, ec) - pref) * P + t);
         ok[j] = grp < ngroups && e < nw && t < nv;
         // masked rows read row 0 of block 0: the loads are unconditional so
         // the count in flight is static and the waits stay exact
@@ -300,17 +322,18 @@ void sparse_decode_wave_kernel(
     // placeholders) so the number of loads in flight stays static.
     uint4 K0[NL], V0[NL], K1[NL], V1[NL];
     bool o0[NL], o1[NL];
+    float p0[NL], p1[NL];
     bool f0 = false, f1 = false;
     int grp = 0;
-    load(0, K0, V0, o0, f0);
-    load(1, K1, V1, o1, f1);
+    load(0, K0, V0, o0, f0, p0);
+    load(1, K1, V1, o1, f1, p1);
     while (grp < ngroups) {
-      attend_rows_split<LPR, NL>(qh, ql, K0, V0, o0, f0, m, l, acc);
+      attend_rows_split<LPR, NL, AL>(qh, ql, K0, V0, o0, f0, p0, slope2, m, l, acc);
       if (++grp >= ngroups) break;
-      load(grp + 1, K0, V0, o0, f0);
-      attend_rows_split<LPR, NL>(qh, ql, K1, V1, o1, f1, m, l, acc);
+      load(grp + 1, K0, V0, o0, f0, p0);
+      attend_rows_split<LPR, NL, AL>(qh, ql, K1, V1, o1, f1, p1, slope2, m, l, acc);
       if (++grp >= ngroups) break;
-      load(grp + 1, K1, V1, o1, f1);
+      load(grp + 1, K1, V1, o1, f1, p1);
     }
   }
 
@@ -327,7 +350,11 @@ void sparse_decode_wave_kernel(
       dst[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
     }
   }
-  if (lane == 0) lse_part[prow] = m == -INFINITY ? -INFINITY : (m + log2f(l)) * skv::kLn2;
+  if (lane == 0) {
+    float lse2 = m + log2f(l);
+    if (AL) lse2 = fmaf(slope2, static_cast<float>(pref * P - (S - 1)), lse2);
+    lse_part[prow] = m == -INFINITY ? -INFINITY : lse2 * skv::kLn2;
+  }
 }
 
 // ------------------------------------------------------------ group kernel
@@ -355,7 +382,7 @@ __device__ __forceinline__ skv_bf16x8 as_bf16x8(uint4 v) {
 // Heads past G carry zero queries and are dropped at the end.  Online softmax
 // state per head lives in the four lanes of its S column; the waves' states
 // are merged through LDS at the end.
-template <int D>
+template <int D, bool AL>
 __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
     const float* __restrict__ q, int H_q, int H_kv, int G,
     const uint16_t* __restrict__ kv, int64_t num_blocks, int P,
@@ -363,7 +390,7 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_idx,
     const int32_t* __restrict__ sel_cnt, const int32_t* __restrict__ sel_blk,
     int k_cap, float scale_log2, int num_splits, float* __restrict__ o_part,
-    float* __restrict__ lse_part) {
+    float* __restrict__ lse_part, const float* __restrict__ alibi) {
   constexpr int NC = D / 32;            // 32-dim steps of the logit MFMA
   constexpr int NB = D / 16;            // 16-column blocks of the output MFMA
   constexpr int WAVES = 4;
@@ -371,7 +398,8 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
 
   __shared__ int32_t e_blk[kMaxEnt];
   __shared__ int32_t e_nv[kMaxEnt];
-  __shared__ int s_start, s_len;
+  __shared__ int32_t e_pg[AL ? kMaxEnt : 1];
+  __shared__ int s_start, s_len, s_pref;
   __shared__ __align__(16) uint16_t vstage[WAVES][16 * VST];
   __shared__ float red_m[WAVES][16], red_l[WAVES][16];
   __shared__ __align__(16) float red_o[WAVES][16][D];
@@ -402,6 +430,9 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
     const Chunk ch = split_chunk(sel_cnt[row], k_cap, num_splits, s);
     s_start = ch.start;
     s_len = ch.len;
+    // ALiBi offsets are taken from the chunk's last selected page (see the
+    // per-head kernel); its bias returns in the lse
+    s_pref = (AL && ch.len > 0) ? sel_idx[static_cast<int64_t>(row) * k_cap + ch.start + ch.len - 1] : 0;
   }
 
   // Q^T as the B operand: lane holds head n, dims c*32 + 8*kq .. +8, scaled
@@ -433,6 +464,8 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
   __syncthreads();
   const int rounds = (s_len + kMaxEnt - 1) / kMaxEnt;
 
+  // ALiBi slope of head n in base-2 logit units
+  const float slope2 = (AL && n < G) ? alibi[h * G + n] * skv::kLog2e : 0.0f;
   float m = -INFINITY, l = 0.0f;       // state of head n
   skv_f32x4 O[NB];                     // O[head 4*kq + i][blk*16 + n]
 #pragma unroll
@@ -465,6 +498,7 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
           const int nn = S - p * P;
           nv = nn < P ? nn : P;
         }
+        if constexpr (AL) e_pg[j] = p;
       }
       e_blk[j] = blk;
       e_nv[j] = nv;
@@ -476,11 +510,13 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
 
     // 16-byte pieces of row rr: dims c*32 + 8*kq .. +8 (the A operand layout);
     // masked rows read row 0 of block 0 so the loads stay unconditional
-    auto load = [&](int grp, uint4 (&Kc)[NC], uint4 (&Vc)[NC], bool& ok) {
+    // rpos (ALiBi only): this lane's row position minus the query's (S - 1)
+    auto load = [&](int grp, uint4 (&Kc)[NC], uint4 (&Vc)[NC], bool& ok, float& rpos) {
       const int e = grp * epg + rr / P;
       const int t = rr % P;
       const int ec = e < kMaxEnt ? e : kMaxEnt - 1;
       ok = grp < ngroups && e < n_here && t < e_nv[ec];
+      if constexpr (AL) rpos = ok ? static_cast<float>((e_pg[ec] - s_pref) * P + t) : 0.0f;
       const int64_t off = (ok ? (static_cast<int64_t>(e_blk[ec]) * P + t) * row_stride : 0) +
                           head_off + 8 * kq;
 #pragma unroll
@@ -489,7 +525,7 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
         Vc[c] = *reinterpret_cast<const uint4*>(kv + v_off + off + c * 32);
       }
     };
-    auto apply = [&](const uint4 (&Kc)[NC], const uint4 (&Vc)[NC], bool ok) {
+    auto apply = [&](const uint4 (&Kc)[NC], const uint4 (&Vc)[NC], bool ok, float rpos) {
       // masked rows stage zeros: a placeholder row is never multiplied
 #pragma unroll
       for (int c = 0; c < NC; ++c)
@@ -502,6 +538,11 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
                                                        sacc, 0, 0, 0);
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Kc[c]), as_bf16x8(ql[c]),
                                                        sacc, 0, 0, 0);
+      }
+      if constexpr (AL) {
+        // row 4*kq + i's position sits in lane 4*kq + i (the A-operand row)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sacc[i] = fmaf(slope2, __shfl(rpos, 4 * kq + i), sacc[i]);
       }
       // rows 4*kq + i of column n; invalid rows (bit clear) drop out
       const uint64_t okm = __ballot(ok);
@@ -554,15 +595,16 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
     };
     uint4 K0[NC], V0[NC], K1[NC], V1[NC];
     bool o0, o1;
+    float r0 = 0.0f, r1 = 0.0f;
     int grp = wave;
-    load(grp, K0, V0, o0);
+    load(grp, K0, V0, o0, r0);
     while (grp < ngroups) {
-      load(grp + WAVES, K1, V1, o1);
-      apply(K0, V0, o0);
+      load(grp + WAVES, K1, V1, o1, r1);
+      apply(K0, V0, o0, r0);
       grp += WAVES;
       if (grp >= ngroups) break;
-      load(grp + WAVES, K0, V0, o0);
-      apply(K1, V1, o1);
+      load(grp + WAVES, K0, V0, o0, r0);
+      apply(K1, V1, o1, r1);
       grp += WAVES;
     }
     __syncthreads();
@@ -594,7 +636,12 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
       A = fmaf(red_o[w][g][d], e, A);
     }
     o_part[prow * D + d] = A / L;
-    if (d == 0) lse_part[prow] = (M + log2f(L)) * skv::kLn2;
+    if (d == 0) {
+      float lse2 = M + log2f(L);
+      if (AL) lse2 = fmaf(alibi[h * G + g] * skv::kLog2e,
+                          static_cast<float>(s_pref * P - (S - 1)), lse2);
+      lse_part[prow] = lse2 * skv::kLn2;
+    }
   }
 }
 
@@ -602,28 +649,28 @@ struct Args {
   const float* q; int H_q, H_kv, G; const uint16_t* kv; int64_t num_blocks; int P;
   const int32_t* bt; int64_t bt_ld; const int32_t* seq_lens; const int32_t* sel_idx;
   const int32_t* sel_cnt; const int32_t* sel_blk; int k_cap; float scale_log2; int num_splits;
-  float* o_part; float* lse_part;
+  float* o_part; float* lse_part; const float* alibi;
 };
 
 constexpr int kWaveBlock = 4;          // waves per block of the wave kernel
 
-template <int D, int PFIX>
+template <int D, int PFIX, bool AL>
 void launch_wave(hipStream_t st, const Args& a, int64_t n_groups) {
   const int per_group = (a.num_splits * a.G + kWaveBlock - 1) / kWaveBlock;
   const int64_t blocks = kXcds * per_group * ((n_groups + kXcds - 1) / kXcds);
-  hipLaunchKernelGGL((sparse_decode_wave_kernel<D, kWaveBlock, PFIX>),
+  hipLaunchKernelGGL((sparse_decode_wave_kernel<D, kWaveBlock, PFIX, AL>),
                      dim3(static_cast<unsigned>(blocks)), dim3(kWaveBlock * 64), 0, st,
                      a.q, a.H_q, a.H_kv, a.G, a.kv, a.num_blocks, a.P, a.bt, a.bt_ld,
                      a.seq_lens, a.sel_idx, a.sel_cnt, a.sel_blk, a.k_cap, a.scale_log2,
-                     a.num_splits, a.o_part, a.lse_part, n_groups, per_group);
+                     a.num_splits, a.o_part, a.lse_part, n_groups, per_group, a.alibi);
 }
 
-template <int D>
+template <int D, bool AL>
 void launch_group(dim3 grid, hipStream_t st, const Args& a) {
-  hipLaunchKernelGGL((sparse_decode_group_kernel<D>), grid, dim3(256), 0, st,
+  hipLaunchKernelGGL((sparse_decode_group_kernel<D, AL>), grid, dim3(256), 0, st,
                      a.q, a.H_q, a.H_kv, a.G, a.kv, a.num_blocks, a.P, a.bt, a.bt_ld,
                      a.seq_lens, a.sel_idx, a.sel_cnt, a.sel_blk, a.k_cap, a.scale_log2,
-                     a.num_splits, a.o_part, a.lse_part);
+                     a.num_splits, a.o_part, a.lse_part, a.alibi);
 }
 
 }  // namespace
@@ -638,7 +685,7 @@ extern "C" int sparse_paged_decode(const float* q, int B, int H_q, int H_kv,
                                    const int32_t* sel_blk, int k_cap,
                                    int H_sel, float scale, int num_splits,
                                    float* o_part, float* lse_part,
-                                   hipStream_t stream) {
+                                   const float* alibi_slopes, hipStream_t stream) {
   SKV_REQUIRE(B >= 0 && H_kv > 0 && H_q > 0 && H_q % H_kv == 0,
               "sparse_paged_decode: need H_q a positive multiple of H_kv");
   const int G = H_q / H_kv;
@@ -669,22 +716,27 @@ extern "C" int sparse_paged_decode(const float* q, int B, int H_q, int H_kv,
             static_cast<unsigned>(B));
   const Args a{q, H_q, H_kv, G, kv_cache, num_blocks, page_size, block_table, bt_ld,
                seq_lens, sel_idx, sel_cnt, sel_blk, k_cap, scale * skv::kLog2e, num_splits,
-               o_part, lse_part};
+               o_part, lse_part, alibi_slopes};
+  const bool al = alibi_slopes != nullptr;
   if (shared_sel) {
-    if (D == 128) launch_group<128>(grid, stream, a);
-    else launch_group<64>(grid, stream, a);
+    if (D == 128) { if (al) launch_group<128, true>(grid, stream, a); else launch_group<128, false>(grid, stream, a); }
+    else { if (al) launch_group<64, true>(grid, stream, a); else launch_group<64, false>(grid, stream, a); }
   } else {
     const int64_t n_groups = static_cast<int64_t>(B) * H_kv;
     const int64_t per_group = (static_cast<int64_t>(num_splits) * G + kWaveBlock - 1) / kWaveBlock;
     SKV_REQUIRE(per_group * (n_groups + kXcds) < 0x7fffffffLL,
                 "sparse_paged_decode: grid too large");
+#define SKV_WAVE(DD, PP)                                                   \
+  do {                                                                     \
+    if (al) launch_wave<DD, PP, true>(stream, a, n_groups);                \
+    else launch_wave<DD, PP, false>(stream, a, n_groups);                  \
+  } while (0)
     if (page_size == 16) {
-      if (D == 128) launch_wave<128, 16>(stream, a, n_groups);
-      else launch_wave<64, 16>(stream, a, n_groups);
+      if (D == 128) SKV_WAVE(128, 16); else SKV_WAVE(64, 16);
     } else {
-      if (D == 128) launch_wave<128, 0>(stream, a, n_groups);
-      else launch_wave<64, 0>(stream, a, n_groups);
+      if (D == 128) SKV_WAVE(128, 0); else SKV_WAVE(64, 0);
     }
+#undef SKV_WAVE
   }
   SKV_CHECK_LAUNCH();
 }

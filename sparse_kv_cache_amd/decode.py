@@ -25,6 +25,12 @@ from . import (h2o_accumulate, h2o_scratch_floats, lse_merge, page_score,
                page_score_group, page_topk, pagestats_update, sparse_paged_decode)
 
 
+def alibi_slopes(H, device="cuda"):
+    """The standard geometric ALiBi slopes 2^(-8 (i + 1) / H) of H heads."""
+    i = torch.arange(1, H + 1, dtype=torch.float64)
+    return torch.pow(2.0, -8.0 * i / H).to(torch.float32).to(device)
+
+
 def selection_capacity(score_ld, topk_pages, topk_frac=0.0, bos=0, eos=1):
     """Largest selection a row of at most score_ld entries can produce."""
     need = max(int(topk_pages), int(math.floor(float(topk_frac) * score_ld)),
@@ -37,12 +43,13 @@ class SparseDecoder:
 
     kv_cache: bf16 [2, num_blocks, P, H_kv, D]; block_table int32 [B, bt_ld].
     token_level=True selects the H2O flow (page_size must be 1);
-    group_select=True scores and selects once per kv head (page level)."""
+    group_select=True scores and selects once per kv head (page level);
+    alibi_slopes (fp32 [H_q] on the device) adds ALiBi to scoring and decode."""
 
     def __init__(self, B, H_q, H_kv, D, num_blocks, page_size, bt_ld, *,
                  topk_pages, topk_frac=0.0, bos=0, eos=1, w_avg=1.0, w_peak=1.0,
                  scale=None, num_splits=1, decay=0.984375, token_level=False,
-                 group_select=False, device="cuda"):
+                 group_select=False, alibi_slopes=None, device="cuda"):
         self.B, self.H_q, self.H_kv, self.D = B, H_q, H_kv, D
         self.num_blocks, self.P, self.bt_ld = num_blocks, page_size, bt_ld
         self.topk_pages, self.topk_frac = topk_pages, topk_frac
@@ -53,6 +60,11 @@ class SparseDecoder:
         self.token_level = token_level
         self.group_select = bool(group_select) and not token_level
         dev = torch.device(device)
+        if alibi_slopes is not None and token_level:
+            raise ValueError("ALiBi is not part of the token-level flow")
+        self.alibi = alibi_slopes
+        # the page score is in q.k units: slopes divided by the softmax scale
+        self.alibi_score = None if alibi_slopes is None else alibi_slopes / self.scale
         self.H_sel = H_kv if (token_level or self.group_select) else H_q
         self.k_cap = selection_capacity(bt_ld, topk_pages, topk_frac, bos, eos)
         f32, i32, bf = torch.float32, torch.int32, torch.bfloat16
@@ -80,14 +92,16 @@ class SparseDecoder:
         self.lse = torch.empty((B, H_q), dtype=f32, device=dev)
 
     @classmethod
-    def for_workload(cls, wl, device="cuda", num_splits=None, group_select=False):
+    def for_workload(cls, wl, device="cuda", num_splits=None, group_select=False,
+                     alibi_slopes=None):
         return cls(wl.B, wl.H_q, wl.H_kv, wl.D, wl.num_blocks, wl.P, wl.bt_ld,
                    topk_pages=wl.topk_pages, topk_frac=wl.topk_frac, bos=wl.bos,
                    eos=wl.eos, w_avg=wl.w_avg, w_peak=wl.w_peak,
                    scale=wl.softmax_scale,
                    num_splits=wl.num_splits if num_splits is None else num_splits,
                    decay=wl.decay, token_level=(wl.name == "h2o_token"),
-                   group_select=group_select, device=device)
+                   group_select=group_select, alibi_slopes=alibi_slopes,
+                   device=device)
 
     # ------------------------------------------------------------ stages
     def rebuild_stats(self, kv_cache, block_table, seq_lens, stream=None):
@@ -104,7 +118,8 @@ class SparseDecoder:
             raise RuntimeError("token-level scores come from h2o_accumulate")
         fn = page_score_group if self.group_select else page_score
         fn(q, self.k_min, self.k_max, self.k_mean, block_table, seq_lens,
-           self.P, self.w_avg, self.w_peak, self.scores, stream=stream)
+           self.P, self.w_avg, self.w_peak, self.scores, alibi=self.alibi_score,
+           stream=stream)
 
     def accumulate(self, q, kv_cache, block_table, seq_lens, stream=None):
         h2o_accumulate(q, kv_cache, block_table, seq_lens, self.hh, self.scores,
@@ -121,7 +136,7 @@ class SparseDecoder:
         sparse_paged_decode(q, kv_cache, block_table, seq_lens, self.sel_idx,
                             self.sel_cnt, self.scale, self.o_part, self.lse_part,
                             sel_blk=self.sel_blk if self.use_sel_blk else None,
-                            stream=stream)
+                            alibi_slopes=self.alibi, stream=stream)
 
     def merge(self, stream=None):
         lse_merge(self.o_part, self.lse_part, self.out, self.lse, stream=stream)

@@ -142,6 +142,34 @@ def check_scores_group(gpu_scores, q, stats_d, bt, sl, P, w_avg, w_peak):
     return ref
 
 
+def check_scores_alibi(gpu_scores, q, stats_d, bt, sl, P, w_avg, w_peak, alibi,
+                       aggregate):
+    """ALiBi-aware scores ([B, H_q, ld], or group means [B, H_kv, ld]) vs the
+    oracle fed the same statistics; alibi [H_q] in score units.  The bound adds
+    the fp32 rounding of the bias terms (|slope| * distance)."""
+    mn, mx, me = stats_d
+    ref = oracle.page_score_alibi(q, mn, mx, me, bt, sl, P, w_avg, w_peak, alibi,
+                                  aggregate, ld=gpu_scores.shape[2])
+    B, H_q, D = q.shape
+    terms = score_abs_terms(q, mn, mx, me, bt, sl, P, w_avg, w_peak)
+    bias = ((abs(w_avg) + abs(w_peak)) * np.abs(np.asarray(alibi))[None, :, None]
+            * np.asarray(sl, dtype=np.float64)[:, None, None])
+    tot = terms + bias
+    if aggregate:
+        H_kv = gpu_scores.shape[1]
+        tot = tot.reshape(B, H_kv, H_q // H_kv, -1).mean(axis=2)
+        G = H_q // H_kv
+    else:
+        G = 1
+    valid = ~np.isnan(ref)
+    g = gpu_scores.astype(np.float64)
+    assert not np.any(np.isnan(g[valid])), "unwritten score"
+    err = np.abs(g[valid] - ref[valid])
+    tol = (2 * D + 2 * G + 8) * 2.0 ** -24 * tot[valid] + 1e-6
+    assert np.all(err <= tol), f"ALiBi score error {err.max()} over bound"
+    return ref
+
+
 def selection_rows(sel_idx, sel_cnt):
     out = []
     for r in range(sel_cnt.shape[0]):
@@ -218,14 +246,29 @@ def check_selection_vs_oracle(gpu_rows, oracle_scores_rows, N_rows, topk, frac,
     return exempt
 
 
-def check_attention(gpu_out, gpu_lse, q, cache_bits, bt, sl, rows_sel, G, scale):
-    """gpu_out [B, H_q, D], gpu_lse [B, H_q]; rows_sel[b][i] = pages."""
+def _attend(q_row, cache_bits, h, bt_row, S, pages, scale, slopes, i):
+    if slopes is None:
+        return oracle.attend(q_row, cache_bits, h, bt_row, S, pages, scale)
+    return oracle.attend_alibi(q_row, cache_bits, h, bt_row, S, pages, scale,
+                               float(slopes[i]))
+
+
+def lse_tol(lse):
+    """1e-4 absolute, plus 8 fp32 ulps of |lse|: an ALiBi bias far from the
+    query puts |lse| near 1e5, where one fp32 ulp is about 0.01."""
+    return LSE_ATOL + 8.0 * 2.0 ** -23 * abs(lse)
+
+
+def check_attention(gpu_out, gpu_lse, q, cache_bits, bt, sl, rows_sel, G, scale,
+                    slopes=None):
+    """gpu_out [B, H_q, D], gpu_lse [B, H_q]; rows_sel[b][i] = pages;
+    slopes [H_q] = ALiBi slopes (or None)."""
     B, H_q, D = q.shape
     worst = 0.0
     for b in range(B):
         for i in range(H_q):
-            o, lse = oracle.attend(q[b, i], cache_bits, i // G, bt[b], sl[b],
-                                   rows_sel[b][i], scale)
+            o, lse = _attend(q[b, i], cache_bits, i // G, bt[b], sl[b],
+                             rows_sel[b][i], scale, slopes, i)
             go = gpu_out[b, i].astype(np.float64)
             assert not np.any(np.isnan(go)), f"NaN output at ({b},{i})"
             e = np.abs(go - o).max()
@@ -234,13 +277,13 @@ def check_attention(gpu_out, gpu_lse, q, cache_bits, bt, sl, rows_sel, G, scale)
             if np.isinf(lse):
                 assert np.isinf(gpu_lse[b, i]) and gpu_lse[b, i] < 0
             else:
-                assert abs(float(gpu_lse[b, i]) - lse) <= LSE_ATOL, \
+                assert abs(float(gpu_lse[b, i]) - lse) <= lse_tol(lse), \
                     f"lse ({b},{i}) {gpu_lse[b, i]} vs {lse}"
     return worst
 
 
 def check_partials(o_part, lse_part, q, cache_bits, bt, sl, rows_sel, G, scale,
-                   k_cap):
+                   k_cap, slopes=None):
     """Split s of a row holds entries [s*c, (s+1)*c), c = ceil(k_cap/splits)."""
     B, H_q, ns, D = o_part.shape
     c = -(-k_cap // ns)
@@ -249,15 +292,16 @@ def check_partials(o_part, lse_part, q, cache_bits, bt, sl, rows_sel, G, scale,
             pages = list(rows_sel[b][i])
             for s in range(ns):
                 chunk = pages[s * c:(s + 1) * c] if c else []
-                o, lse = oracle.attend(q[b, i], cache_bits, i // G, bt[b], sl[b],
-                                       chunk, scale)
+                o, lse = _attend(q[b, i], cache_bits, i // G, bt[b], sl[b], chunk,
+                                 scale, slopes, i)
                 if np.isinf(lse):
                     assert np.isinf(lse_part[b, i, s]) and lse_part[b, i, s] < 0
                     assert np.all(o_part[b, i, s] == 0)
                     continue
                 e = np.abs(o_part[b, i, s].astype(np.float64) - o).max()
                 assert e <= OUT_ATOL, f"partial ({b},{i},{s}) err {e}"
-                assert abs(float(lse_part[b, i, s]) - lse) <= LSE_ATOL
+                assert abs(float(lse_part[b, i, s]) - lse) <= lse_tol(lse), \
+                    f"partial lse ({b},{i},{s}) {lse_part[b, i, s]} vs {lse}"
 
 
 def per_head_rows(sel_rows, B, H_q, H_sel):

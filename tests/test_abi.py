@@ -69,21 +69,21 @@ def test_validation_rejects_bad_scalars(lib):
     assert "D must be" in _msg(lib)
     # page_size 3 unsupported
     assert lib.page_score(p, 1, 4, 2, 64, p, p, p, p, 4, p, 3, 1.0, 1.0, p, 4,
-                          s) == EINVAL
+                          None, s) == EINVAL
     # H_q not a multiple of H_kv
     assert lib.page_score(p, 1, 5, 2, 64, p, p, p, p, 4, p, 16, 1.0, 1.0, p, 4,
-                          s) == EINVAL
+                          None, s) == EINVAL
     # score_ld < bt_ld
     assert lib.page_score(p, 1, 4, 2, 64, p, p, p, p, 8, p, 16, 1.0, 1.0, p, 4,
-                          s) == EINVAL
+                          None, s) == EINVAL
     # the group score validates like page_score
     assert lib.page_score_group(p, 1, 4, 2, 96, p, p, p, p, 4, p, 16, 1.0, 1.0, p, 4,
-                                s) == EINVAL
+                                None, s) == EINVAL
     assert "page_score_group" in _msg(lib)
     assert lib.page_score_group(p, 1, 6, 4, 64, p, p, p, p, 4, p, 16, 1.0, 1.0, p, 4,
-                                s) == EINVAL
+                                None, s) == EINVAL
     assert lib.page_score_group(None, 1, 4, 2, 64, p, p, p, p, 4, p, 16, 1.0, 1.0, p, 4,
-                                s) == EFAULT
+                                None, s) == EFAULT
     assert "page_score_group" in _msg(lib)
     # topk < 1, k_cap too small, score_ld too long
     assert lib.page_topk(p, 64, 1, 4, p, 16, 0, 0.0, 0, 1, p, p, 8, None, 0, None, s) == EINVAL
@@ -95,9 +95,9 @@ def test_validation_rejects_bad_scalars(lib):
     assert lib.page_topk(p, 64, 1, 4, p, 16, 4, 0.0, 0, 1, p, p, 8, None, 4, p, s) == EFAULT
     # H_sel neither H_q nor H_kv; splits < 1
     assert lib.sparse_paged_decode(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p, None, 4,
-                                   3, 0.1, 2, p, p, s) == EINVAL
+                                   3, 0.1, 2, p, p, None, s) == EINVAL
     assert lib.sparse_paged_decode(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p, None, 4,
-                                   8, 0.1, 0, p, p, s) == EINVAL
+                                   8, 0.1, 0, p, p, None, s) == EINVAL
     # h2o: page size must be 1, decay in (0, 1]
     assert lib.h2o_accumulate(p, 1, 8, 2, 128, p, 8, 16, p, 8, p, 0, 1, 0.1, 0.98,
                               p, p, 8, p, 10 ** 6, s) == EINVAL
@@ -117,7 +117,7 @@ def test_validation_rejects_null_pointers(lib):
     assert "o_part" in _msg(lib)
     assert lib.page_topk(p, 64, 1, 4, p, 16, 4, 0.0, 0, 1, None, p, 8, None, 0, None, s) == EFAULT
     assert lib.sparse_paged_decode(p, 1, 8, 2, 128, None, 8, 16, p, 4, p, p, p, None,
-                                   4, 8, 0.1, 2, p, p, s) == EFAULT
+                                   4, 8, 0.1, 2, p, p, None, s) == EFAULT
     assert lib.pagestats_update(None, 8, 16, 2, 64, p, p, p, p, 4, p, 1, None,
                                 None, None, s) == EFAULT
     # statistics buffers must be all given or all NULL

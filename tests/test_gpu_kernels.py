@@ -12,7 +12,7 @@ from sparse_kv_cache_amd import workloads as W
 from sparse_kv_cache_amd.decode import SparseDecoder
 
 from parity import (bits, check_attention, check_partials, check_scores,
-                    check_scores_group,
+                    check_scores_alibi, check_scores_group,
                     check_selection_exact, check_selection_vs_oracle,
                     check_stats, dev, per_head_rows, poison, say,
                     selection_rows, bf16_bits_apart, check_sel_blk)
@@ -185,6 +185,81 @@ def test_group_selection_step(case):
                       topk_pages=topk, topk_frac=frac, bos=bos, eos=eos,
                       w_avg=wa, w_peak=wp, num_splits=ns)
     worst, ex = run_group_case(wl, W.make_cache(wl), W.make_queries(wl))
+    say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}")
+
+
+# seed, B, H_q, H_kv, D, P, max_pages, topk, splits, group_select
+ALIBI_CASES = [
+    (80, 2, 8, 2, 128, 16, 30, 6, 3, False),
+    (81, 2, 4, 4, 64, 4, 40, 7, 4, False),
+    (82, 1, 16, 2, 128, 16, 50, 9, 5, True),
+    (83, 2, 6, 3, 64, 1, 120, 20, 2, True),
+]
+
+
+def run_alibi_case(wl, cache_cpu, q_cpu, group, slopes_np):
+    """Page level with ALiBi slopes, per-head or group-shared selection."""
+    from sparse_kv_cache_amd.decode import alibi_slopes  # noqa: F401 (API presence)
+    cache = dev(cache_cpu)
+    q = dev(q_cpu)
+    bt = dev(wl.block_table)
+    sl = dev(wl.seq_lens)
+    slopes = torch.from_numpy(slopes_np.astype(np.float32)).cuda()
+    d = SparseDecoder(wl.B, wl.H_q, wl.H_kv, wl.D, wl.num_blocks, wl.P, wl.bt_ld,
+                      topk_pages=wl.topk_pages, topk_frac=wl.topk_frac, bos=wl.bos,
+                      eos=wl.eos, w_avg=wl.w_avg, w_peak=wl.w_peak,
+                      scale=wl.softmax_scale, num_splits=wl.num_splits,
+                      group_select=group, alibi_slopes=slopes)
+    poison(d)
+    d.rebuild_stats(cache, bt, sl)
+    d.score(q, bt, sl)
+    d.select(sl, bt)
+    d.attend(q, cache, bt, sl)
+    d.merge()
+    torch.cuda.synchronize()
+    cb = bits(cache)
+    qd = q_cpu.double().numpy()
+    st = check_stats(bits(d.k_min), bits(d.k_max), d.k_mean.cpu().numpy(), cb,
+                     wl.block_table, wl.seq_lens, wl.P, W.referenced_blocks(wl))
+    gst = (oracle.bf16_decode(bits(d.k_min)), oracle.bf16_decode(bits(d.k_max)),
+           d.k_mean.cpu().numpy().astype(np.float64))
+    # the score in q.k units takes slope / scale, as the decoder passes it
+    a_score = d.alibi_score.cpu().numpy().astype(np.float64)
+    gs = d.scores.cpu().numpy()
+    check_scores_alibi(gs, qd, gst, wl.block_table, wl.seq_lens, wl.P, wl.w_avg,
+                       wl.w_peak, a_score, group)
+    H_sel = d.H_sel
+    N = wl.pages()
+    sel_idx = d.sel_idx.cpu().numpy().reshape(-1, d.k_cap)
+    sel_cnt = d.sel_cnt.cpu().numpy().reshape(-1)
+    rowsN = np.repeat(N, H_sel)
+    check_selection_exact(sel_idx, sel_cnt, gs.reshape(-1, wl.bt_ld), rowsN,
+                          wl.topk_pages, wl.topk_frac, wl.bos, wl.eos)
+    ref_scores = oracle.page_score_alibi(qd, *st, wl.block_table, wl.seq_lens, wl.P,
+                                         wl.w_avg, wl.w_peak, a_score, group)
+    rows = selection_rows(sel_idx, sel_cnt)
+    ex = check_selection_vs_oracle(rows, ref_scores.reshape(-1, wl.bt_ld), rowsN,
+                                   wl.topk_pages, wl.topk_frac, wl.bos, wl.eos)
+    per = per_head_rows(rows, wl.B, wl.H_q, H_sel)
+    sl64 = slopes.cpu().numpy().astype(np.float64)
+    check_partials(d.o_part.cpu().numpy(), d.lse_part.cpu().numpy(), qd, cb,
+                   wl.block_table, wl.seq_lens, per, wl.G, wl.softmax_scale, d.k_cap,
+                   slopes=sl64)
+    worst = check_attention(d.out.cpu().numpy(), d.lse.cpu().numpy(), qd, cb,
+                            wl.block_table, wl.seq_lens, per, wl.G, wl.softmax_scale,
+                            slopes=sl64)
+    return worst, ex
+
+
+@pytest.mark.parametrize("case", ALIBI_CASES, ids=[f"alibi{c[0]}" for c in ALIBI_CASES])
+def test_alibi_step(case):
+    (seed, B, H_q, H_kv, D, P, maxp, topk, ns, group) = case
+    say(f"[gpu] ALiBi case {case}")
+    wl = W.small_case(seed=seed, B=B, H_q=H_q, H_kv=H_kv, D=D, P=P, max_pages=maxp,
+                      topk_pages=topk, num_splits=ns)
+    from sparse_kv_cache_amd.decode import alibi_slopes
+    slopes = alibi_slopes(H_q, device="cpu").numpy()
+    worst, ex = run_alibi_case(wl, W.make_cache(wl), W.make_queries(wl), group, slopes)
     say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}")
 
 

@@ -95,6 +95,19 @@ def test_long_context_group_selection():
     _static_workload("long_context", group_select=True)
 
 
+def test_long_context_alibi():
+    """long_context with the standard ALiBi slopes: the bias reaches about
+    -0.5 * 131071 at the far end, so selection concentrates near the tail."""
+    from test_gpu_kernels import run_alibi_case
+    from sparse_kv_cache_amd.decode import alibi_slopes
+    wl = W.long_context()
+    say("[gpu] workload long_context with ALiBi: generating")
+    cache = W.make_cache(wl, device="cuda")
+    slopes = alibi_slopes(wl.H_q, device="cpu").numpy()
+    worst, ex = run_alibi_case(wl, cache, W.make_queries(wl), False, slopes)
+    say(f"  long_context ALiBi: max |out - oracle| {worst:.2e}, near-tie rows {ex}")
+
+
 def test_high_batch_sampled_after_appends():
     wl = W.high_batch()
     say("[gpu] workload high_batch: generating 300k-block pool")
