@@ -301,14 +301,24 @@ extern "C" int page_topk(const float* scores, int64_t score_ld, int B,
   launch_topk<BL, IT>(rows, stream, scores, score_ld, H_sel, seq_lens, page_size, \
                       topk_pages, frac, reserved_bos, reserved_eos, sel_idx,      \
                       sel_cnt, k_cap, block_table, bt_ld, sel_blk)
-  // the widest block that still gives each thread at least 4 entries: more
-  // threads per row shorten every pass (rows are few; each is latency-bound)
-  if (score_ld <= 1024) SKV_TOPK(256, 4);
-  else if (score_ld <= 2048) SKV_TOPK(512, 4);
-  else if (score_ld <= 4096) SKV_TOPK(1024, 4);
-  else if (score_ld <= 8192) SKV_TOPK(1024, 8);
-  else if (score_ld <= 16384) SKV_TOPK(1024, 16);
-  else SKV_TOPK(1024, 32);
+  if (rows < 1024) {
+    // few rows, each latency-bound: the widest block that still gives each
+    // thread at least 4 entries, so every pass is short
+    if (score_ld <= 1024) SKV_TOPK(256, 4);
+    else if (score_ld <= 2048) SKV_TOPK(512, 4);
+    else if (score_ld <= 4096) SKV_TOPK(1024, 4);
+    else if (score_ld <= 8192) SKV_TOPK(1024, 8);
+    else if (score_ld <= 16384) SKV_TOPK(1024, 16);
+    else SKV_TOPK(1024, 32);
+  } else {
+    // rows enough to fill the chip: 256-thread blocks, several per CU
+    if (score_ld <= 1024) SKV_TOPK(256, 4);
+    else if (score_ld <= 2048) SKV_TOPK(256, 8);
+    else if (score_ld <= 4096) SKV_TOPK(256, 16);
+    else if (score_ld <= 8192) SKV_TOPK(512, 16);
+    else if (score_ld <= 16384) SKV_TOPK(1024, 16);
+    else SKV_TOPK(1024, 32);
+  }
 #undef SKV_TOPK
   SKV_CHECK_LAUNCH();
 }
