@@ -4,6 +4,8 @@
 One step = one pass of the whole hot path over the batch:
   page level (default gqa_ragged, also mha_tiny / long_context):
       page_score -> page_topk -> sparse_paged_decode -> lse_merge
+      (with one selection per query head and at most 8 splits the merge runs
+      inside the decode launch: sparse_paged_decode_merged)
       (statistics built once beforehand, timed separately)
   high_batch: pagestats_update (append + refresh) -> the four above
   h2o_token:  pagestats_update (append + reset) -> h2o_accumulate ->
@@ -53,6 +55,9 @@ def parse():
     ap.add_argument("--alibi", action="store_true",
                     help="page level: standard ALiBi slopes 2^(-8(i+1)/H_q) in scoring "
                          "and decode")
+    ap.add_argument("--no-fuse", action="store_true",
+                    help="keep lse_merge as its own launch even where the decode "
+                         "can merge its splits in-block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="enqueue kernel by kernel instead of replaying HIP graphs")
@@ -87,7 +92,7 @@ def unique_kv_bytes(wl, sel_idx, sel_cnt, seq_lens, H_sel):
 
 
 def kernel_bytes(wl, sel_idx, sel_cnt, seq_lens, num_splits, token_level,
-                 group_select=False):
+                 group_select=False, fused=False):
     """Algorithmic HBM bytes of each kernel of one step: the bytes the
     operation must move at least (unique selected K/V once, statistics, scores,
     indices, partials)."""
@@ -110,9 +115,12 @@ def kernel_bytes(wl, sel_idx, sel_cnt, seq_lens, num_splits, token_level,
                                           + B * Hkv * D * 8)
         out["page_score"] = int((N * (Hkv * 8 * D + H_sel * 4 + 4)).sum() + B * Hq * D * 4)
     out["page_topk"] = int((N * H_sel * 4).sum() + cnt * 4)
-    out["sparse_paged_decode"] = int(kv + B * Hq * D * 4 + cnt * 4
-                                     + B * Hq * num_splits * (D + 1) * 4)
-    out["lse_merge"] = int(B * Hq * num_splits * (D + 1) * 4 + B * Hq * (D + 1) * 4)
+    if fused:   # merged in-block: the merged output instead of the partials
+        out["sparse_paged_decode"] = int(kv + B * Hq * D * 4 + cnt * 4 + B * Hq * (D + 1) * 4)
+    else:
+        out["sparse_paged_decode"] = int(kv + B * Hq * D * 4 + cnt * 4
+                                         + B * Hq * num_splits * (D + 1) * 4)
+        out["lse_merge"] = int(B * Hq * num_splits * (D + 1) * 4 + B * Hq * (D + 1) * 4)
     return out, upages
 
 
@@ -244,8 +252,9 @@ def main():
     group = args.select == "group" and not token_level
     slopes = alibi_slopes(wl.H_q, dev) if (args.alibi and not token_level) else None
     decs = [SparseDecoder.for_workload(wl, device=dev, group_select=group,
-                                       alibi_slopes=slopes)
+                                       alibi_slopes=slopes, fuse_merge=not args.no_fuse)
             for _ in range(R)]
+    fused = decs[0].fused
     new_kv = [W.make_new_kv(wl, s, device=dev) for s in range(min(wl.steps, 64))] \
         if wl.steps > 1 else None
     if token_level:
@@ -284,7 +293,7 @@ def main():
 
     names = (["pagestats_update"] if wl.steps > 1 else []) + \
         (["h2o_accumulate"] if token_level else ["page_score"]) + \
-        ["page_topk", "sparse_paged_decode", "lse_merge"]
+        ["page_topk", "sparse_paged_decode"] + ([] if fused else ["lse_merge"])
 
     def enqueue(i, name):
         """Enqueue kernel `name` of step i (replica i % R, sequence step i % steps)."""
@@ -369,7 +378,7 @@ def main():
         del g
 
     kb, upages = kernel_bytes(wl, sel_idx, sel_cnt, sl_last, wl.num_splits, token_level,
-                              group)
+                              group, fused)
     step_bytes = sum(kb.values())
     kern = {}
     for n in names:
@@ -400,7 +409,7 @@ def main():
                    "topk_frac": wl.topk_frac, "num_splits": wl.num_splits,
                    "mean_seq_len": float(np.mean(sl_last)), "replicas": R,
                    "selection": ("kv_head" if (group or token_level) else "query_head"),
-                   "alibi": slopes is not None,
+                   "alibi": slopes is not None, "merge_in_decode": fused,
                    "parallelism": "single-gpu"},
         "effective_GBps": round(step_bytes / (gpu_ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(step_bytes / (gpu_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),

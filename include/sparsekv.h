@@ -208,6 +208,30 @@ int sparse_paged_decode(const float *q, int B, int H_q, int H_kv, int D,
                         hipStream_t stream);
 
 /*
+ * sparse_paged_decode_merged -- sparse_paged_decode for one selection per
+ * query head (H_sel = H_q) with the split merge done in the same launch: one
+ * block per query head, one wave per split, merged in LDS by lse_merge's
+ * algebra.  [Same sources as sparse_paged_decode and lse_merge.]
+ *
+ *   Arguments as sparse_paged_decode (H_sel is H_q), plus
+ *   out      fp32 [B, H_q, D]   merged attention output (required)
+ *   lse_out  fp32 [B, H_q] or NULL
+ *   o_part, lse_part  both NULL, or both given to also receive the partials.
+ *   Requires num_splits <= 8 (-EINVAL otherwise).
+ * The result equals sparse_paged_decode followed by lse_merge up to fp32
+ * rounding order.
+ */
+int sparse_paged_decode_merged(const float *q, int B, int H_q, int H_kv, int D,
+                               const uint16_t *kv_cache, int64_t num_blocks,
+                               int page_size, const int32_t *block_table,
+                               int64_t bt_ld, const int32_t *seq_lens,
+                               const int32_t *sel_idx, const int32_t *sel_cnt,
+                               const int32_t *sel_blk, int k_cap, float scale,
+                               int num_splits, float *o_part, float *lse_part,
+                               const float *alibi_slopes, float *out,
+                               float *lse_out, hipStream_t stream);
+
+/*
  * lse_merge -- N-way log-sum-exp merge of split partials.  [MLA:
  * MergeAttnStates algebra; a +inf lse is read as -inf; if every partial is
  * -inf the first partial is emitted with lse -inf.]

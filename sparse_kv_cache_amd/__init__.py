@@ -18,8 +18,8 @@ import torch
 
 __all__ = [
     "pagestats_update", "page_score", "page_score_group", "page_topk",
-    "sparse_paged_decode", "lse_merge", "h2o_accumulate", "h2o_scratch_floats",
-    "library_path",
+    "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
+    "h2o_accumulate", "h2o_scratch_floats", "library_path",
     "load_library", "SparseKVError", "EXPORTED_SYMBOLS",
 ]
 
@@ -29,11 +29,12 @@ _lib = None
 
 EXPORTED_SYMBOLS = (
     "pagestats_update", "page_score", "page_score_group", "page_topk",
-    "sparse_paged_decode", "lse_merge", "h2o_accumulate", "h2o_scratch_floats",
-    "sparsekv_last_error",
+    "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
+    "h2o_accumulate", "h2o_scratch_floats", "sparsekv_last_error",
 )
 _INT_RETURNING = ("pagestats_update", "page_score", "page_score_group", "page_topk",
-                  "sparse_paged_decode", "lse_merge", "h2o_accumulate")
+                  "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
+                  "h2o_accumulate")
 
 
 class SparseKVError(RuntimeError):
@@ -67,6 +68,8 @@ def load_library():
     lib.page_topk.argtypes = [V, L, I, I, V, I, I, F, I, I, V, V, I, V, L, V, V]
     lib.sparse_paged_decode.argtypes = [V, I, I, I, I, V, L, I, V, L, V, V, V, V, I,
                                         I, F, I, V, V, V, V]
+    lib.sparse_paged_decode_merged.argtypes = [V, I, I, I, I, V, L, I, V, L, V, V, V, V,
+                                               I, F, I, V, V, V, V, V, V]
     lib.lse_merge.argtypes = [V, V, I, I, I, V, V, V]
     lib.h2o_accumulate.argtypes = [V, I, I, I, I, V, L, I, V, L, V, I, I, F, F, V, V,
                                    L, V, L, V]
@@ -272,6 +275,46 @@ def sparse_paged_decode(q, kv_cache, block_table, seq_lens, sel_idx, sel_cnt,
         block_table.shape[1], _ptr(seq_lens), _ptr(sel_idx), _ptr(sel_cnt),
         _ptr(sel_blk), sel_idx.shape[2], H_sel, float(scale), ns, _ptr(o_part),
         _ptr(lse_part), _ptr(alibi_slopes), _stream(stream)))
+
+
+def sparse_paged_decode_merged(q, kv_cache, block_table, seq_lens, sel_idx, sel_cnt,
+                               scale, num_splits, out, lse_out=None, o_part=None,
+                               lse_part=None, sel_blk=None, alibi_slopes=None,
+                               stream=None):
+    """Decode with one selection per query head and the split merge in the same
+    launch: out [B, H_q, D] (and lse_out [B, H_q]); num_splits <= 8."""
+    lib = load_library()
+    _check("q", q, torch.float32, 3)
+    dev = q.device
+    B, H_q, D = q.shape
+    _check("kv_cache", kv_cache, torch.bfloat16, 5, dev)
+    _, NB, P, H_kv, D2 = kv_cache.shape
+    if D2 != D:
+        raise ValueError("q and kv_cache head dims differ")
+    _check("block_table", block_table, torch.int32, 2, dev)
+    _check("seq_lens", seq_lens, torch.int32, 1, dev)
+    _check("sel_idx", sel_idx, torch.int32, 3, dev)
+    _check("sel_cnt", sel_cnt, torch.int32, 2, dev)
+    _check("out", out, torch.float32, 3, dev)
+    _check("lse_out", lse_out, torch.float32, 2, dev)
+    if tuple(sel_idx.shape[:2]) != (B, H_q) or tuple(sel_cnt.shape) != (B, H_q):
+        raise ValueError("sel_idx must be [B, H_q, k_cap] and sel_cnt [B, H_q]")
+    if tuple(out.shape) != (B, H_q, D):
+        raise ValueError("out must be [B, H_q, D]")
+    if (o_part is None) != (lse_part is None):
+        raise ValueError("o_part and lse_part go together")
+    if o_part is not None:
+        _check("o_part", o_part, torch.float32, 4, dev)
+        _check("lse_part", lse_part, torch.float32, 3, dev)
+        if tuple(o_part.shape) != (B, H_q, num_splits, D):
+            raise ValueError("o_part must be [B, H_q, num_splits, D]")
+    _check("sel_blk", sel_blk, torch.int32, 3, dev)
+    alibi_slopes = _alibi_arg(alibi_slopes, H_q, dev)
+    _rc("sparse_paged_decode_merged", lib.sparse_paged_decode_merged(
+        _ptr(q), B, H_q, H_kv, D, _ptr(kv_cache), NB, P, _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), _ptr(sel_idx), _ptr(sel_cnt),
+        _ptr(sel_blk), sel_idx.shape[2], float(scale), int(num_splits), _ptr(o_part),
+        _ptr(lse_part), _ptr(alibi_slopes), _ptr(out), _ptr(lse_out), _stream(stream)))
 
 
 def lse_merge(o_part, lse_part, out, lse_out=None, stream=None):

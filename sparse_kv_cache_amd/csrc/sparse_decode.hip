@@ -175,7 +175,12 @@ __device__ __forceinline__ Chunk split_chunk(int cnt, int k_cap, int num_splits,
 // share a block, and all blocks of the (request, kv head) go to one XCD:
 // pages several heads selected are fetched through one L2 at about the same
 // time.
-template <int D, int WB, int PFIX, bool AL>
+//
+// FUSE: one block per query head, wave w = split w (num_splits <= WB); the
+// block merges its splits' states through LDS and writes the merged output
+// and lse itself (the lse_merge algebra), so no separate merge launch is
+// needed.  Partials are still written when o_part / lse_part are given.
+template <int D, int WB, int PFIX, bool AL, bool FUSE>
 __global__ __launch_bounds__(WB * 64)
 __attribute__((amdgpu_waves_per_eu(PFIX == 16 ? SKV_DECODE_WPE16 : SKV_DECODE_WPE)))
 void sparse_decode_wave_kernel(
@@ -186,21 +191,25 @@ void sparse_decode_wave_kernel(
     const int32_t* __restrict__ sel_cnt, const int32_t* __restrict__ sel_blk,
     int k_cap, float scale_log2, int num_splits, float* __restrict__ o_part,
     float* __restrict__ lse_part, int64_t n_groups, int blocks_per_group,
-    const float* __restrict__ alibi) {
+    const float* __restrict__ alibi, float* __restrict__ out,
+    float* __restrict__ lse_out) {
   constexpr int LPR = D / 8;
   constexpr int RPL = 64 / LPR;
   constexpr int NL = 16 / RPL;
   const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   // Blocks are dealt to the 8 XCDs round-robin by id; block id -> (xcd, k)
   // -> (request/kv-head group, block within the group) so that every block of
   // one (request, kv head) runs on the same XCD and shares its L2.
   const int xcd = blockIdx.x % kXcds;
   const int64_t k = blockIdx.x / kXcds;
   const int64_t grp_bh = xcd + kXcds * (k / blocks_per_group);
-  const int local = static_cast<int>(k % blocks_per_group) * WB + (threadIdx.x >> 6);
-  if (grp_bh >= n_groups || local >= num_splits * G) return;
-  const int g = local % G;
-  const int s = local / G;
+  const int local = static_cast<int>(k % blocks_per_group) * WB + wave;
+  // (FUSE: whole blocks return together; waves past num_splits stay for the
+  // block merge with an empty chunk)
+  if (grp_bh >= n_groups || (!FUSE && local >= num_splits * G)) return;
+  const int g = FUSE ? static_cast<int>(k % blocks_per_group) : local % G;
+  const int s = FUSE ? wave : local / G;
   const int h = static_cast<int>(grp_bh % H_kv);
   const int b = static_cast<int>(grp_bh / H_kv);
   const int64_t qrow = static_cast<int64_t>(b) * H_q + h * G + g;
@@ -338,6 +347,40 @@ void sparse_decode_wave_kernel(
   }
 
   merge_slots<LPR>(m, l, acc);
+  if constexpr (FUSE) {
+    // the split's state in absolute base-2 units, then the block merge
+    __shared__ float f_m[WB], f_l[WB];
+    __shared__ __align__(16) float f_acc[WB][D];
+    float mabs = m;
+    if (AL && m != -INFINITY) mabs = fmaf(slope2, static_cast<float>(pref * P - (S - 1)), m);
+    if (slot == 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f_acc[wave][c * 8 + i] = acc[i];
+    }
+    if (lane == 0) { f_m[wave] = mabs; f_l[wave] = l; }
+    __syncthreads();
+    for (int d = threadIdx.x; d < D; d += WB * 64) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < WB; ++w) M = fmaxf(M, f_m[w]);
+      if (M == -INFINITY) {
+        out[qrow * D + d] = 0.0f;
+        if (d == 0 && lse_out != nullptr) lse_out[qrow] = -INFINITY;
+        continue;
+      }
+      float L = 0.0f, A = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WB; ++w) {
+        if (f_m[w] == -INFINITY) continue;
+        const float e = exp2f(f_m[w] - M);
+        L = fmaf(f_l[w], e, L);
+        A = fmaf(f_acc[w][d], e, A);
+      }
+      out[qrow * D + d] = A / L;
+      if (d == 0 && lse_out != nullptr) lse_out[qrow] = (M + log2f(L)) * skv::kLn2;
+    }
+    if (o_part == nullptr || s >= num_splits) return;
+  }
   const int64_t prow = qrow * num_splits + s;
   if (slot == 0) {
     float4* dst = reinterpret_cast<float4*>(o_part + prow * D + c * 8);
@@ -658,11 +701,28 @@ template <int D, int PFIX, bool AL>
 void launch_wave(hipStream_t st, const Args& a, int64_t n_groups) {
   const int per_group = (a.num_splits * a.G + kWaveBlock - 1) / kWaveBlock;
   const int64_t blocks = kXcds * per_group * ((n_groups + kXcds - 1) / kXcds);
-  hipLaunchKernelGGL((sparse_decode_wave_kernel<D, kWaveBlock, PFIX, AL>),
+  hipLaunchKernelGGL((sparse_decode_wave_kernel<D, kWaveBlock, PFIX, AL, false>),
                      dim3(static_cast<unsigned>(blocks)), dim3(kWaveBlock * 64), 0, st,
                      a.q, a.H_q, a.H_kv, a.G, a.kv, a.num_blocks, a.P, a.bt, a.bt_ld,
                      a.seq_lens, a.sel_idx, a.sel_cnt, a.sel_blk, a.k_cap, a.scale_log2,
-                     a.num_splits, a.o_part, a.lse_part, n_groups, per_group, a.alibi);
+                     a.num_splits, a.o_part, a.lse_part, n_groups, per_group, a.alibi,
+                     nullptr, nullptr);
+}
+
+// One block per query head, kFuseWaves waves = splits, merged in the block.
+constexpr int kFuseWaves = 8;
+
+template <int D, int PFIX, bool AL>
+void launch_wave_fused(hipStream_t st, const Args& a, int64_t n_groups, float* out,
+                       float* lse_out) {
+  const int per_group = a.G;
+  const int64_t blocks = kXcds * per_group * ((n_groups + kXcds - 1) / kXcds);
+  hipLaunchKernelGGL((sparse_decode_wave_kernel<D, kFuseWaves, PFIX, AL, true>),
+                     dim3(static_cast<unsigned>(blocks)), dim3(kFuseWaves * 64), 0, st,
+                     a.q, a.H_q, a.H_kv, a.G, a.kv, a.num_blocks, a.P, a.bt, a.bt_ld,
+                     a.seq_lens, a.sel_idx, a.sel_cnt, a.sel_blk, a.k_cap, a.scale_log2,
+                     a.num_splits, a.o_part, a.lse_part, n_groups, per_group, a.alibi,
+                     out, lse_out);
 }
 
 template <int D, bool AL>
@@ -671,6 +731,95 @@ void launch_group(dim3 grid, hipStream_t st, const Args& a) {
                      a.q, a.H_q, a.H_kv, a.G, a.kv, a.num_blocks, a.P, a.bt, a.bt_ld,
                      a.seq_lens, a.sel_idx, a.sel_cnt, a.sel_blk, a.k_cap, a.scale_log2,
                      a.num_splits, a.o_part, a.lse_part, a.alibi);
+}
+
+}  // namespace
+
+namespace {
+
+// Validation and dispatch shared by both entry points.  out == nullptr: the
+// split partials only; otherwise the in-block merge as well (per-head
+// selection with num_splits <= kFuseWaves, checked by the caller).
+int decode_impl(const char* who, const float* q, int B, int H_q, int H_kv, int D,
+                const uint16_t* kv_cache, int64_t num_blocks, int page_size,
+                const int32_t* block_table, int64_t bt_ld, const int32_t* seq_lens,
+                const int32_t* sel_idx, const int32_t* sel_cnt, const int32_t* sel_blk,
+                int k_cap, int H_sel, float scale, int num_splits, float* o_part,
+                float* lse_part, const float* alibi_slopes, float* out, float* lse_out,
+                hipStream_t stream) {
+  SKV_REQUIRE(B >= 0 && H_kv > 0 && H_q > 0 && H_q % H_kv == 0,
+              "%s: need H_q a positive multiple of H_kv", who);
+  const int G = H_q / H_kv;
+  SKV_REQUIRE(G <= 16, "%s: group size %d > 16", who, G);
+  SKV_REQUIRE(D == 64 || D == 128, "%s: D must be 64 or 128 (got %d)", who, D);
+  SKV_REQUIRE(skv_supported_page_size(page_size),
+              "%s: page_size must be 1, 2, 4, 8 or 16 (got %d)", who, page_size);
+  SKV_REQUIRE(H_sel == H_q || H_sel == H_kv,
+              "%s: H_sel must be H_q or H_kv (got %d)", who, H_sel);
+  SKV_REQUIRE(num_splits >= 1 && num_splits <= 65535,
+              "%s: num_splits must be in [1, 65535]", who);
+  SKV_REQUIRE(k_cap >= 1 && num_blocks > 0 && bt_ld > 0,
+              "%s: need k_cap >= 1, num_blocks > 0, bt_ld > 0", who);
+  SKV_REQUIRE(num_blocks <= 0x7fffffffLL, "%s: pool too large for 32-bit block ids", who);
+  SKV_REQUIRE(B <= 65535 && H_kv <= 65535, "%s: grid too large", who);
+  SKV_REQUIRE_PTR_W(who, q);
+  SKV_REQUIRE_PTR_W(who, kv_cache);
+  SKV_REQUIRE_PTR_W(who, block_table);
+  SKV_REQUIRE_PTR_W(who, seq_lens);
+  SKV_REQUIRE_PTR_W(who, sel_idx);
+  SKV_REQUIRE_PTR_W(who, sel_cnt);
+  const bool shared_sel = (H_sel == H_kv && G > 1);
+  if (out == nullptr) {
+    SKV_REQUIRE_PTR_W(who, o_part);
+    SKV_REQUIRE_PTR_W(who, lse_part);
+  } else {
+    SKV_REQUIRE(!shared_sel, "%s: the merged output needs one selection per query head", who);
+    SKV_REQUIRE(num_splits <= kFuseWaves, "%s: num_splits must be <= %d (got %d)", who,
+                kFuseWaves, num_splits);
+    SKV_REQUIRE((o_part == nullptr) == (lse_part == nullptr),
+                "%s: o_part and lse_part must both be given or both be NULL", who);
+  }
+  const int64_t n_groups = static_cast<int64_t>(B) * H_kv;
+  const int64_t per_group = out != nullptr
+      ? G : (static_cast<int64_t>(num_splits) * G + kWaveBlock - 1) / kWaveBlock;
+  SKV_REQUIRE(shared_sel || per_group * (n_groups + kXcds) < 0x7fffffffLL,
+              "%s: grid too large", who);
+  if (B == 0) { skv::clear_error(); return SKV_OK; }
+  dim3 grid(static_cast<unsigned>(num_splits), static_cast<unsigned>(H_kv),
+            static_cast<unsigned>(B));
+  const Args a{q, H_q, H_kv, G, kv_cache, num_blocks, page_size, block_table, bt_ld,
+               seq_lens, sel_idx, sel_cnt, sel_blk, k_cap, scale * skv::kLog2e, num_splits,
+               o_part, lse_part, alibi_slopes};
+  const bool al = alibi_slopes != nullptr;
+  if (shared_sel) {
+    if (D == 128) { if (al) launch_group<128, true>(grid, stream, a); else launch_group<128, false>(grid, stream, a); }
+    else { if (al) launch_group<64, true>(grid, stream, a); else launch_group<64, false>(grid, stream, a); }
+  } else if (out != nullptr) {
+#define SKV_FUSED(DD, PP)                                                          \
+  do {                                                                             \
+    if (al) launch_wave_fused<DD, PP, true>(stream, a, n_groups, out, lse_out);    \
+    else launch_wave_fused<DD, PP, false>(stream, a, n_groups, out, lse_out);      \
+  } while (0)
+    if (page_size == 16) {
+      if (D == 128) SKV_FUSED(128, 16); else SKV_FUSED(64, 16);
+    } else {
+      if (D == 128) SKV_FUSED(128, 0); else SKV_FUSED(64, 0);
+    }
+#undef SKV_FUSED
+  } else {
+#define SKV_WAVE(DD, PP)                                                   \
+  do {                                                                     \
+    if (al) launch_wave<DD, PP, true>(stream, a, n_groups);                \
+    else launch_wave<DD, PP, false>(stream, a, n_groups);                  \
+  } while (0)
+    if (page_size == 16) {
+      if (D == 128) SKV_WAVE(128, 16); else SKV_WAVE(64, 16);
+    } else {
+      if (D == 128) SKV_WAVE(128, 0); else SKV_WAVE(64, 0);
+    }
+#undef SKV_WAVE
+  }
+  SKV_CHECK_LAUNCH();
 }
 
 }  // namespace
@@ -686,57 +835,27 @@ extern "C" int sparse_paged_decode(const float* q, int B, int H_q, int H_kv,
                                    int H_sel, float scale, int num_splits,
                                    float* o_part, float* lse_part,
                                    const float* alibi_slopes, hipStream_t stream) {
-  SKV_REQUIRE(B >= 0 && H_kv > 0 && H_q > 0 && H_q % H_kv == 0,
-              "sparse_paged_decode: need H_q a positive multiple of H_kv");
-  const int G = H_q / H_kv;
-  SKV_REQUIRE(G <= 16, "sparse_paged_decode: group size %d > 16", G);
-  SKV_REQUIRE(D == 64 || D == 128, "sparse_paged_decode: D must be 64 or 128 (got %d)", D);
-  SKV_REQUIRE(skv_supported_page_size(page_size),
-              "sparse_paged_decode: page_size must be 1, 2, 4, 8 or 16 (got %d)", page_size);
-  SKV_REQUIRE(H_sel == H_q || H_sel == H_kv,
-              "sparse_paged_decode: H_sel must be H_q or H_kv (got %d)", H_sel);
-  SKV_REQUIRE(num_splits >= 1 && num_splits <= 65535,
-              "sparse_paged_decode: num_splits must be in [1, 65535]");
-  SKV_REQUIRE(k_cap >= 1 && num_blocks > 0 && bt_ld > 0,
-              "sparse_paged_decode: need k_cap >= 1, num_blocks > 0, bt_ld > 0");
-  SKV_REQUIRE(num_blocks <= 0x7fffffffLL,
-              "sparse_paged_decode: pool too large for 32-bit block ids");
-  SKV_REQUIRE(B <= 65535 && H_kv <= 65535, "sparse_paged_decode: grid too large");
-  SKV_REQUIRE_PTR(q);
-  SKV_REQUIRE_PTR(kv_cache);
-  SKV_REQUIRE_PTR(block_table);
-  SKV_REQUIRE_PTR(seq_lens);
-  SKV_REQUIRE_PTR(sel_idx);
-  SKV_REQUIRE_PTR(sel_cnt);
-  SKV_REQUIRE_PTR(o_part);
-  SKV_REQUIRE_PTR(lse_part);
-  if (B == 0) { skv::clear_error(); return SKV_OK; }
-  const bool shared_sel = (H_sel == H_kv && G > 1);
-  dim3 grid(static_cast<unsigned>(num_splits), static_cast<unsigned>(H_kv),
-            static_cast<unsigned>(B));
-  const Args a{q, H_q, H_kv, G, kv_cache, num_blocks, page_size, block_table, bt_ld,
-               seq_lens, sel_idx, sel_cnt, sel_blk, k_cap, scale * skv::kLog2e, num_splits,
-               o_part, lse_part, alibi_slopes};
-  const bool al = alibi_slopes != nullptr;
-  if (shared_sel) {
-    if (D == 128) { if (al) launch_group<128, true>(grid, stream, a); else launch_group<128, false>(grid, stream, a); }
-    else { if (al) launch_group<64, true>(grid, stream, a); else launch_group<64, false>(grid, stream, a); }
-  } else {
-    const int64_t n_groups = static_cast<int64_t>(B) * H_kv;
-    const int64_t per_group = (static_cast<int64_t>(num_splits) * G + kWaveBlock - 1) / kWaveBlock;
-    SKV_REQUIRE(per_group * (n_groups + kXcds) < 0x7fffffffLL,
-                "sparse_paged_decode: grid too large");
-#define SKV_WAVE(DD, PP)                                                   \
-  do {                                                                     \
-    if (al) launch_wave<DD, PP, true>(stream, a, n_groups);                \
-    else launch_wave<DD, PP, false>(stream, a, n_groups);                  \
-  } while (0)
-    if (page_size == 16) {
-      if (D == 128) SKV_WAVE(128, 16); else SKV_WAVE(64, 16);
-    } else {
-      if (D == 128) SKV_WAVE(128, 0); else SKV_WAVE(64, 0);
-    }
-#undef SKV_WAVE
-  }
-  SKV_CHECK_LAUNCH();
+  return decode_impl("sparse_paged_decode", q, B, H_q, H_kv, D, kv_cache, num_blocks,
+                     page_size, block_table, bt_ld, seq_lens, sel_idx, sel_cnt, sel_blk,
+                     k_cap, H_sel, scale, num_splits, o_part, lse_part, alibi_slopes,
+                     nullptr, nullptr, stream);
+}
+
+extern "C" int sparse_paged_decode_merged(const float* q, int B, int H_q, int H_kv,
+                                          int D, const uint16_t* kv_cache,
+                                          int64_t num_blocks, int page_size,
+                                          const int32_t* block_table, int64_t bt_ld,
+                                          const int32_t* seq_lens,
+                                          const int32_t* sel_idx,
+                                          const int32_t* sel_cnt,
+                                          const int32_t* sel_blk, int k_cap,
+                                          float scale, int num_splits, float* o_part,
+                                          float* lse_part, const float* alibi_slopes,
+                                          float* out, float* lse_out,
+                                          hipStream_t stream) {
+  SKV_REQUIRE_PTR(out);
+  return decode_impl("sparse_paged_decode_merged", q, B, H_q, H_kv, D, kv_cache,
+                     num_blocks, page_size, block_table, bt_ld, seq_lens, sel_idx, sel_cnt,
+                     sel_blk, k_cap, H_q, scale, num_splits, o_part, lse_part, alibi_slopes,
+                     out, lse_out, stream);
 }

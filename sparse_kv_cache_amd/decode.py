@@ -22,7 +22,8 @@ import math
 import torch
 
 from . import (h2o_accumulate, h2o_scratch_floats, lse_merge, page_score,
-               page_score_group, page_topk, pagestats_update, sparse_paged_decode)
+               page_score_group, page_topk, pagestats_update, sparse_paged_decode,
+               sparse_paged_decode_merged)
 
 
 def alibi_slopes(H, device="cuda"):
@@ -44,12 +45,15 @@ class SparseDecoder:
     kv_cache: bf16 [2, num_blocks, P, H_kv, D]; block_table int32 [B, bt_ld].
     token_level=True selects the H2O flow (page_size must be 1);
     group_select=True scores and selects once per kv head (page level);
-    alibi_slopes (fp32 [H_q] on the device) adds ALiBi to scoring and decode."""
+    alibi_slopes (fp32 [H_q] on the device) adds ALiBi to scoring and decode.
+    With one selection per query head and num_splits <= 8 the split merge runs
+    inside the decode launch (fused); keep_partials also writes the partials."""
 
     def __init__(self, B, H_q, H_kv, D, num_blocks, page_size, bt_ld, *,
                  topk_pages, topk_frac=0.0, bos=0, eos=1, w_avg=1.0, w_peak=1.0,
                  scale=None, num_splits=1, decay=0.984375, token_level=False,
-                 group_select=False, alibi_slopes=None, device="cuda"):
+                 group_select=False, alibi_slopes=None, fuse_merge=True,
+                 device="cuda"):
         self.B, self.H_q, self.H_kv, self.D = B, H_q, H_kv, D
         self.num_blocks, self.P, self.bt_ld = num_blocks, page_size, bt_ld
         self.topk_pages, self.topk_frac = topk_pages, topk_frac
@@ -90,10 +94,12 @@ class SparseDecoder:
         self.lse_part = torch.empty((B, H_q, num_splits), dtype=f32, device=dev)
         self.out = torch.empty((B, H_q, D), dtype=f32, device=dev)
         self.lse = torch.empty((B, H_q), dtype=f32, device=dev)
+        self.fused = bool(fuse_merge) and self.H_sel == H_q and num_splits <= 8
+        self.keep_partials = False
 
     @classmethod
     def for_workload(cls, wl, device="cuda", num_splits=None, group_select=False,
-                     alibi_slopes=None):
+                     alibi_slopes=None, fuse_merge=True):
         return cls(wl.B, wl.H_q, wl.H_kv, wl.D, wl.num_blocks, wl.P, wl.bt_ld,
                    topk_pages=wl.topk_pages, topk_frac=wl.topk_frac, bos=wl.bos,
                    eos=wl.eos, w_avg=wl.w_avg, w_peak=wl.w_peak,
@@ -101,7 +107,7 @@ class SparseDecoder:
                    num_splits=wl.num_splits if num_splits is None else num_splits,
                    decay=wl.decay, token_level=(wl.name == "h2o_token"),
                    group_select=group_select, alibi_slopes=alibi_slopes,
-                   device=device)
+                   fuse_merge=fuse_merge, device=device)
 
     # ------------------------------------------------------------ stages
     def rebuild_stats(self, kv_cache, block_table, seq_lens, stream=None):
@@ -133,12 +139,22 @@ class SparseDecoder:
                   block_table=block_table, sel_blk=blk, stream=stream)
 
     def attend(self, q, kv_cache, block_table, seq_lens, stream=None):
+        if self.fused:
+            parts = (self.o_part, self.lse_part) if self.keep_partials else (None, None)
+            sparse_paged_decode_merged(
+                q, kv_cache, block_table, seq_lens, self.sel_idx, self.sel_cnt,
+                self.scale, self.num_splits, self.out, self.lse, o_part=parts[0],
+                lse_part=parts[1], sel_blk=self.sel_blk if self.use_sel_blk else None,
+                alibi_slopes=self.alibi, stream=stream)
+            return
         sparse_paged_decode(q, kv_cache, block_table, seq_lens, self.sel_idx,
                             self.sel_cnt, self.scale, self.o_part, self.lse_part,
                             sel_blk=self.sel_blk if self.use_sel_blk else None,
                             alibi_slopes=self.alibi, stream=stream)
 
     def merge(self, stream=None):
+        if self.fused:
+            return                      # merged inside attend()
         lse_merge(self.o_part, self.lse_part, self.out, self.lse, stream=stream)
 
     # -------------------------------------------------------------- step

@@ -40,7 +40,7 @@ def lib():
 def test_header_declares_the_six_operations():
     names = _declared()
     for n in ("pagestats_update", "page_score", "page_score_group", "page_topk",
-              "sparse_paged_decode",
+              "sparse_paged_decode", "sparse_paged_decode_merged",
               "lse_merge", "h2o_accumulate", "h2o_scratch_floats",
               "sparsekv_last_error"):
         assert n in names
@@ -98,6 +98,14 @@ def test_validation_rejects_bad_scalars(lib):
                                    3, 0.1, 2, p, p, None, s) == EINVAL
     assert lib.sparse_paged_decode(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p, None, 4,
                                    8, 0.1, 0, p, p, None, s) == EINVAL
+    # merged decode: at most 8 splits; out required; partials both or neither
+    assert lib.sparse_paged_decode_merged(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p, None,
+                                          4, 0.1, 9, None, None, None, p, None, s) == EINVAL
+    assert "num_splits" in _msg(lib)
+    assert lib.sparse_paged_decode_merged(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p, None,
+                                          4, 0.1, 4, p, None, None, p, None, s) == EINVAL
+    assert lib.sparse_paged_decode_merged(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p, None,
+                                          4, 0.1, 4, None, None, None, None, None, s) == EFAULT
     # h2o: page size must be 1, decay in (0, 1]
     assert lib.h2o_accumulate(p, 1, 8, 2, 128, p, 8, 16, p, 8, p, 0, 1, 0.1, 0.98,
                               p, p, 8, p, 10 ** 6, s) == EINVAL

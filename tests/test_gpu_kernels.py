@@ -50,6 +50,7 @@ def run_page_case(wl, cache_cpu, q_cpu, exact_ties=False):
     bt = dev(wl.block_table)
     sl = dev(wl.seq_lens)
     d = _decoder(wl)
+    d.keep_partials = True
     poison(d)
     d.k_min.fill_(float("nan")); d.k_max.fill_(float("nan")); d.k_mean.fill_(float("nan"))
     d.rebuild_stats(cache, bt, sl)
@@ -68,6 +69,20 @@ def run_page_case(wl, cache_cpu, q_cpu, exact_ties=False):
     # (the two paths may use different kernels and summation orders)
     assert torch.allclose(o_with, d.out, rtol=0, atol=1e-5), \
         "decode differs with / without sel_blk"
+    d.use_sel_blk = True
+    if d.fused:
+        # the in-block merge against the separate merge launch
+        lse_f = d.lse.clone()
+        d.fused = False
+        d.out.fill_(float("nan"))
+        d.lse.fill_(float("nan"))
+        d.attend(q, cache, bt, sl)
+        d.merge()
+        torch.cuda.synchronize()
+        assert torch.allclose(o_with, d.out, rtol=0, atol=1e-5), "merged decode differs"
+        assert torch.allclose(lse_f, d.lse, rtol=0, atol=1e-5, equal_nan=False), \
+            "merged decode lse differs"
+        d.fused = True
 
     cb = bits(cache)
     qd = q_cpu.double().numpy()
@@ -210,6 +225,7 @@ def run_alibi_case(wl, cache_cpu, q_cpu, group, slopes_np):
                       eos=wl.eos, w_avg=wl.w_avg, w_peak=wl.w_peak,
                       scale=wl.softmax_scale, num_splits=wl.num_splits,
                       group_select=group, alibi_slopes=slopes)
+    d.keep_partials = True
     poison(d)
     d.rebuild_stats(cache, bt, sl)
     d.score(q, bt, sl)

@@ -65,6 +65,7 @@ def _static_workload(name, group_select=False):
     cache = W.make_cache(wl, device="cuda")
     q_cpu = W.make_queries(wl)
     d = SparseDecoder.for_workload(wl, group_select=group_select)
+    d.keep_partials = True
     bt, sl = dev(wl.block_table), dev(wl.seq_lens)
     poison(d)
     d.rebuild_stats(cache, bt, sl)
@@ -113,6 +114,7 @@ def test_high_batch_sampled_after_appends():
     say("[gpu] workload high_batch: generating 300k-block pool")
     cache = W.make_cache(wl, device="cuda")
     d = SparseDecoder.for_workload(wl)
+    d.keep_partials = True
     bt = dev(wl.block_table)
     sl0 = dev(wl.seq_lens)
     d.rebuild_stats(cache, bt, sl0)
