@@ -63,6 +63,10 @@ def _load():
     lib.oracle_attend_alibi.argtypes = [P, i32, P, i64, i32, i32, i32, P, i32, P, i32,
                                         f64, f64, P, P]
     lib.oracle_lse_merge.argtypes = [P, P, i32, i32, P, P]
+    lib.oracle_entmax15_tau.argtypes = [P, i32]
+    lib.oracle_entmax15_tau.restype = f64
+    lib.oracle_attend_entmax15.argtypes = [P, i32, P, i64, i32, i32, i32, P, i32, P, i32,
+                                           f64, P, P]
     lib.oracle_append.argtypes = [P, i64, i32, i32, i32, P, i64, P, i32, P, P, P]
     lib.oracle_h2o_recurrence.argtypes = [P, P, i32, f64]
     lib.oracle_h2o_step.argtypes = [P, i32, i32, i32, i32, P, i64, P, i64, P,
@@ -231,6 +235,29 @@ def page_score_alibi(q, kmin, kmax, kmean, block_table, seq_lens, page_size,
                                 _ptr(bt), bt.shape[1], _ptr(sl), page_size, float(w_avg),
                                 float(w_peak), _ptr(al), int(bool(aggregate)), _ptr(s), ld)
     return s
+
+
+def entmax15_tau(z):
+    """tau of 1.5-entmax over the logits z (bisection in float64)."""
+    zz = _c(z, np.float64)
+    return float(_load().oracle_entmax15_tau(_ptr(zz), zz.shape[0]))
+
+
+def attend_entmax15(q_row, kv_cache, kv_head, bt_row, seq_len, pages, scale):
+    """(o [D], tau) of 1.5-entmax attention of one query row over the tokens
+    of the given pages."""
+    lib = _load()
+    qd = _c(q_row, np.float64)
+    kv = _c(kv_cache, np.uint16)
+    _, NB, P, H_kv, D = kv.shape
+    bt = _c(bt_row, np.int32)
+    pg = _c(pages, np.int32)
+    o = np.zeros(D)
+    tau = np.zeros(1)
+    lib.oracle_attend_entmax15(_ptr(qd), D, _ptr(kv), NB, P, H_kv, int(kv_head),
+                               _ptr(bt), int(seq_len), _ptr(pg), pg.shape[0],
+                               float(scale), _ptr(o), _ptr(tau))
+    return o, float(tau[0])
 
 
 def lse_merge(o_parts, lses):

@@ -454,6 +454,84 @@ void oracle_attend_alibi(const double *q, int D, const uint16_t *kv_cache,
     free(row);
 }
 
+/* ------------------------------------------------- 1.5-entmax (NEXT row) */
+
+/* alpha-entmax with alpha = 1.5 (EntmaxKV README, "Quick start": alpha=1.5;
+ * the mapping is the published one of Peters, Niculae and Martins, 2019):
+ *   p_t = [ (alpha - 1) z_t - tau ]_+ ^ (1 / (alpha - 1)) = [ z_t / 2 - tau ]_+ ^ 2
+ * with tau the unique value making sum_t p_t = 1.  f(tau) = sum [u - tau]_+^2
+ * - 1 (u = z / 2) falls strictly from f(max u - 1) >= 0 to f(max u) = -1, so
+ * tau is found by bisection on [max u - 1, max u] (200 halvings: the bracket
+ * ends far below one ulp of the double). */
+double oracle_entmax15_tau(const double *z, int n)
+{
+    double umax = -INFINITY;
+    for (int t = 0; t < n; ++t)
+        if (z[t] / 2.0 > umax) umax = z[t] / 2.0;
+    double lo = umax - 1.0, hi = umax;
+    for (int it = 0; it < 200; ++it) {
+        double mid = 0.5 * (lo + hi);
+        double f = -1.0;
+        for (int t = 0; t < n; ++t) {
+            double d = z[t] / 2.0 - mid;
+            if (d > 0.0) f += d * d;
+        }
+        if (f >= 0.0) lo = mid; else hi = mid;
+    }
+    return 0.5 * (lo + hi);
+}
+
+/* 1.5-entmax attention of one query row over the tokens of the selected
+ * pages: z_t = scale * q.k_t, p = entmax15(z), o = sum_t p_t v_t.  Writes o
+ * [D] and tau; an empty selection gives o = 0 and tau = -inf. */
+void oracle_attend_entmax15(const double *q, int D, const uint16_t *kv_cache,
+                            int64_t num_blocks, int P, int H_kv, int kv_head,
+                            const int32_t *bt_row, int S, const int32_t *pages,
+                            int npages, double scale, double *o, double *tau)
+{
+    int ntok = 0;
+    for (int j = 0; j < npages; ++j) {
+        int n = S - pages[j] * P < P ? S - pages[j] * P : P;
+        ntok += n > 0 ? n : 0;
+    }
+    for (int d = 0; d < D; ++d)
+        o[d] = 0.0;
+    if (ntok == 0) {
+        *tau = -INFINITY;
+        return;
+    }
+    double *z = malloc(sizeof *z * ntok);
+    int64_t *blk = malloc(sizeof *blk * ntok);
+    int *row = malloc(sizeof *row * ntok);
+    int t = 0;
+    for (int j = 0; j < npages; ++j) {
+        int n = S - pages[j] * P < P ? S - pages[j] * P : P;
+        for (int r = 0; r < n; ++r, ++t) {
+            blk[t] = bt_row[pages[j]];
+            row[t] = r;
+            double dot = 0.0;
+            for (int d = 0; d < D; ++d)
+                dot += q[d] * oracle_bf16_to_double(kv_cache[cache_index(
+                           0, blk[t], r, kv_head, d, num_blocks, P, H_kv, D)]);
+            z[t] = scale * dot;
+        }
+    }
+    double tu = oracle_entmax15_tau(z, ntok);
+    for (t = 0; t < ntok; ++t) {
+        double d = z[t] / 2.0 - tu;
+        if (d <= 0.0)
+            continue;
+        double p = d * d;
+        for (int c = 0; c < D; ++c)
+            o[c] += p * oracle_bf16_to_double(kv_cache[cache_index(
+                        1, blk[t], row[t], kv_head, c, num_blocks, P, H_kv, D)]);
+    }
+    *tau = tu;
+    free(z);
+    free(blk);
+    free(row);
+}
+
 /* ------------------------------------------------------ LSE merge (O6) */
 
 /* N-way merge of normalised partial outputs by their log-sum-exps [MLA:
