@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--alibi", action="store_true",
                     help="page level: standard ALiBi slopes 2^(-8(i+1)/H_q) in scoring "
                          "and decode")
+    ap.add_argument("--attention", default="softmax", choices=["softmax", "entmax15"],
+                    help="page level: softmax, or 1.5-entmax over the same selection")
     ap.add_argument("--no-fuse", action="store_true",
                     help="keep lse_merge as its own launch even where the decode "
                          "can merge its splits in-block")
@@ -92,7 +94,7 @@ def unique_kv_bytes(wl, sel_idx, sel_cnt, seq_lens, H_sel):
 
 
 def kernel_bytes(wl, sel_idx, sel_cnt, seq_lens, num_splits, token_level,
-                 group_select=False, fused=False):
+                 group_select=False, fused=False, entmax=False, k_cap=0):
     """Algorithmic HBM bytes of each kernel of one step: the bytes the
     operation must move at least (unique selected K/V once, statistics, scores,
     indices, partials)."""
@@ -115,7 +117,15 @@ def kernel_bytes(wl, sel_idx, sel_cnt, seq_lens, num_splits, token_level,
                                           + B * Hkv * D * 8)
         out["page_score"] = int((N * (Hkv * 8 * D + H_sel * 4 + 4)).sum() + B * Hq * D * 4)
     out["page_topk"] = int((N * H_sel * 4).sum() + cnt * 4)
-    if fused:   # merged in-block: the merged output instead of the partials
+    if entmax:
+        # K of the selected pages once, the logits scratch written and read,
+        # the partials; V is read only for 16-row groups in the support, which
+        # depends on the data and is left out (the GB/s is a lower bound)
+        out["sparse_paged_decode"] = int(kv // 2 + B * Hq * D * 4 + cnt * 4
+                                         + 2 * B * Hq * k_cap * P * 4
+                                         + B * Hq * num_splits * (D + 1) * 4)
+        out["lse_merge"] = int(B * Hq * num_splits * (D + 1) * 4 + B * Hq * (D + 1) * 4)
+    elif fused:   # merged in-block: the merged output instead of the partials
         out["sparse_paged_decode"] = int(kv + B * Hq * D * 4 + cnt * 4 + B * Hq * (D + 1) * 4)
     else:
         out["sparse_paged_decode"] = int(kv + B * Hq * D * 4 + cnt * 4
@@ -251,8 +261,10 @@ def main():
     caches = [cache0] + [cache0.clone() for _ in range(R - 1)]
     group = args.select == "group" and not token_level
     slopes = alibi_slopes(wl.H_q, dev) if (args.alibi and not token_level) else None
+    entmax = args.attention == "entmax15" and not token_level
     decs = [SparseDecoder.for_workload(wl, device=dev, group_select=group,
-                                       alibi_slopes=slopes, fuse_merge=not args.no_fuse)
+                                       alibi_slopes=slopes, fuse_merge=not args.no_fuse,
+                                       attention="entmax15" if entmax else "softmax")
             for _ in range(R)]
     fused = decs[0].fused
     new_kv = [W.make_new_kv(wl, s, device=dev) for s in range(min(wl.steps, 64))] \
@@ -378,7 +390,7 @@ def main():
         del g
 
     kb, upages = kernel_bytes(wl, sel_idx, sel_cnt, sl_last, wl.num_splits, token_level,
-                              group, fused)
+                              group, fused, entmax, decs[0].k_cap)
     step_bytes = sum(kb.values())
     kern = {}
     for n in names:
@@ -390,8 +402,9 @@ def main():
     a = kb[focus] / (per_kernel_ms[focus] * 1e-3) / 1e9
     roofline = {"kernel": focus, "bound": "hbm", "achieved": round(a, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(a / PEAK_HBM_GBPS, 4),
-                "traffic": profiled_traffic(wl.name + ("_group" if group else "")
-                                            + ("_alibi" if slopes is not None else "")),
+                "traffic": (None if entmax else
+                            profiled_traffic(wl.name + ("_group" if group else "")
+                                             + ("_alibi" if slopes is not None else ""))),
                 "bytes_per_launch": kb[focus],
                 "us_per_launch": round(per_kernel_ms[focus] * 1000, 2)}
 
@@ -410,6 +423,7 @@ def main():
                    "mean_seq_len": float(np.mean(sl_last)), "replicas": R,
                    "selection": ("kv_head" if (group or token_level) else "query_head"),
                    "alibi": slopes is not None, "merge_in_decode": fused,
+                   "attention": "entmax15" if entmax else "softmax",
                    "parallelism": "single-gpu"},
         "effective_GBps": round(step_bytes / (gpu_ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(step_bytes / (gpu_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),

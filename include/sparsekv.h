@@ -232,6 +232,34 @@ int sparse_paged_decode_merged(const float *q, int B, int H_q, int H_kv, int D,
                                float *lse_out, hipStream_t stream);
 
 /*
+ * entmax15_paged_decode -- 1.5-entmax attention over the tokens of the
+ * selected pages, as split partials for lse_merge.  [EKV "Quick start"
+ * (alpha=1.5) and the component list (decode over selected pages, alpha 1.5);
+ * the mapping is the published 1.5-entmax: p_t = [z_t / 2 - tau]_+^2 with
+ * z_t = scale * q . k_t and tau such that sum p_t = 1.]
+ *
+ *   Arguments as sparse_paged_decode (same selection rows, H_sel, splits of
+ *   c = ceil(k_cap / num_splits) entries), plus
+ *   scratch  fp32 device buffer of at least entmax_scratch_floats(B, H_q,
+ *            k_cap, page_size) floats (logits, then tau per query head).
+ *   Per (b, i, s):  m = sum of p over the split's rows,
+ *     o_part = sum p v / m,  lse_part = ln m   (o = 0, lse = -inf if m = 0),
+ *   so lse_merge over the splits returns sum_t p_t v_t (total mass 1).
+ *   Three launches: logits (K read once), tau (Newton from below), values
+ *   (V read only for 16-row groups holding a row with p > 0).
+ */
+int64_t entmax_scratch_floats(int B, int H_q, int k_cap, int page_size);
+int entmax15_paged_decode(const float *q, int B, int H_q, int H_kv, int D,
+                          const uint16_t *kv_cache, int64_t num_blocks,
+                          int page_size, const int32_t *block_table,
+                          int64_t bt_ld, const int32_t *seq_lens,
+                          const int32_t *sel_idx, const int32_t *sel_cnt,
+                          const int32_t *sel_blk, int k_cap, int H_sel,
+                          float scale, int num_splits, float *o_part,
+                          float *lse_part, float *scratch,
+                          int64_t scratch_floats, hipStream_t stream);
+
+/*
  * lse_merge -- N-way log-sum-exp merge of split partials.  [MLA:
  * MergeAttnStates algebra; a +inf lse is read as -inf; if every partial is
  * -inf the first partial is emitted with lse -inf.]

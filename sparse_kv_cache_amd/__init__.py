@@ -19,7 +19,8 @@ import torch
 __all__ = [
     "pagestats_update", "page_score", "page_score_group", "page_topk",
     "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
-    "h2o_accumulate", "h2o_scratch_floats", "library_path",
+    "h2o_accumulate", "h2o_scratch_floats", "entmax15_paged_decode",
+    "entmax_scratch_floats", "library_path",
     "load_library", "SparseKVError", "EXPORTED_SYMBOLS",
 ]
 
@@ -30,11 +31,12 @@ _lib = None
 EXPORTED_SYMBOLS = (
     "pagestats_update", "page_score", "page_score_group", "page_topk",
     "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
-    "h2o_accumulate", "h2o_scratch_floats", "sparsekv_last_error",
+    "h2o_accumulate", "h2o_scratch_floats", "entmax15_paged_decode",
+    "entmax_scratch_floats", "sparsekv_last_error",
 )
 _INT_RETURNING = ("pagestats_update", "page_score", "page_score_group", "page_topk",
                   "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
-                  "h2o_accumulate")
+                  "h2o_accumulate", "entmax15_paged_decode")
 
 
 class SparseKVError(RuntimeError):
@@ -75,6 +77,10 @@ def load_library():
                                    L, V, L, V]
     lib.h2o_scratch_floats.argtypes = [I, I, L]
     lib.h2o_scratch_floats.restype = ctypes.c_int64
+    lib.entmax15_paged_decode.argtypes = [V, I, I, I, I, V, L, I, V, L, V, V, V, V, I, I,
+                                          F, I, V, V, V, L, V]
+    lib.entmax_scratch_floats.argtypes = [I, I, I, I]
+    lib.entmax_scratch_floats.restype = ctypes.c_int64
     for name in _INT_RETURNING:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -315,6 +321,46 @@ def sparse_paged_decode_merged(q, kv_cache, block_table, seq_lens, sel_idx, sel_
         block_table.shape[1], _ptr(seq_lens), _ptr(sel_idx), _ptr(sel_cnt),
         _ptr(sel_blk), sel_idx.shape[2], float(scale), int(num_splits), _ptr(o_part),
         _ptr(lse_part), _ptr(alibi_slopes), _ptr(out), _ptr(lse_out), _stream(stream)))
+
+
+def entmax_scratch_floats(B, H_q, k_cap, page_size):
+    """Floats of scratch entmax15_paged_decode needs."""
+    n = load_library().entmax_scratch_floats(int(B), int(H_q), int(k_cap), int(page_size))
+    if n < 0:
+        raise ValueError("bad arguments to entmax_scratch_floats")
+    return int(n)
+
+
+def entmax15_paged_decode(q, kv_cache, block_table, seq_lens, sel_idx, sel_cnt, scale,
+                          o_part, lse_part, scratch, sel_blk=None, stream=None):
+    """1.5-entmax attention over the selected pages as split partials
+    (o_part [B, H_q, splits, D], lse_part = ln of each split's mass), to be
+    combined by lse_merge."""
+    lib = load_library()
+    _check("q", q, torch.float32, 3)
+    dev = q.device
+    B, H_q, D = q.shape
+    _check("kv_cache", kv_cache, torch.bfloat16, 5, dev)
+    _, NB, P, H_kv, D2 = kv_cache.shape
+    if D2 != D:
+        raise ValueError("q and kv_cache head dims differ")
+    _check("block_table", block_table, torch.int32, 2, dev)
+    _check("seq_lens", seq_lens, torch.int32, 1, dev)
+    _check("sel_idx", sel_idx, torch.int32, 3, dev)
+    _check("sel_cnt", sel_cnt, torch.int32, 2, dev)
+    _check("o_part", o_part, torch.float32, 4, dev)
+    _check("lse_part", lse_part, torch.float32, 3, dev)
+    _check("scratch", scratch, torch.float32, 1, dev)
+    _check("sel_blk", sel_blk, torch.int32, 3, dev)
+    ns = o_part.shape[2]
+    H_sel = sel_idx.shape[1]
+    if tuple(o_part.shape) != (B, H_q, ns, D) or tuple(lse_part.shape) != (B, H_q, ns):
+        raise ValueError("o_part must be [B, H_q, splits, D] and lse_part [B, H_q, splits]")
+    _rc("entmax15_paged_decode", lib.entmax15_paged_decode(
+        _ptr(q), B, H_q, H_kv, D, _ptr(kv_cache), NB, P, _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), _ptr(sel_idx), _ptr(sel_cnt), _ptr(sel_blk),
+        sel_idx.shape[2], H_sel, float(scale), ns, _ptr(o_part), _ptr(lse_part),
+        _ptr(scratch), scratch.numel(), _stream(stream)))
 
 
 def lse_merge(o_part, lse_part, out, lse_out=None, stream=None):

@@ -21,9 +21,9 @@ import math
 
 import torch
 
-from . import (h2o_accumulate, h2o_scratch_floats, lse_merge, page_score,
-               page_score_group, page_topk, pagestats_update, sparse_paged_decode,
-               sparse_paged_decode_merged)
+from . import (entmax15_paged_decode, entmax_scratch_floats, h2o_accumulate,
+               h2o_scratch_floats, lse_merge, page_score, page_score_group, page_topk,
+               pagestats_update, sparse_paged_decode, sparse_paged_decode_merged)
 
 
 def alibi_slopes(H, device="cuda"):
@@ -47,13 +47,15 @@ class SparseDecoder:
     group_select=True scores and selects once per kv head (page level);
     alibi_slopes (fp32 [H_q] on the device) adds ALiBi to scoring and decode.
     With one selection per query head and num_splits <= 8 the split merge runs
-    inside the decode launch (fused); keep_partials also writes the partials."""
+    inside the decode launch (fused); keep_partials also writes the partials.
+    attention="entmax15" attends with 1.5-entmax instead of softmax (page
+    level; three decode launches, then lse_merge)."""
 
     def __init__(self, B, H_q, H_kv, D, num_blocks, page_size, bt_ld, *,
                  topk_pages, topk_frac=0.0, bos=0, eos=1, w_avg=1.0, w_peak=1.0,
                  scale=None, num_splits=1, decay=0.984375, token_level=False,
                  group_select=False, alibi_slopes=None, fuse_merge=True,
-                 device="cuda"):
+                 attention="softmax", device="cuda"):
         self.B, self.H_q, self.H_kv, self.D = B, H_q, H_kv, D
         self.num_blocks, self.P, self.bt_ld = num_blocks, page_size, bt_ld
         self.topk_pages, self.topk_frac = topk_pages, topk_frac
@@ -66,6 +68,11 @@ class SparseDecoder:
         dev = torch.device(device)
         if alibi_slopes is not None and token_level:
             raise ValueError("ALiBi is not part of the token-level flow")
+        if attention not in ("softmax", "entmax15"):
+            raise ValueError("attention must be 'softmax' or 'entmax15'")
+        if attention == "entmax15" and (token_level or alibi_slopes is not None):
+            raise ValueError("1.5-entmax is built for the page-level flow without ALiBi")
+        self.attention = attention
         self.alibi = alibi_slopes
         # the page score is in q.k units: slopes divided by the softmax scale
         self.alibi_score = None if alibi_slopes is None else alibi_slopes / self.scale
@@ -94,12 +101,17 @@ class SparseDecoder:
         self.lse_part = torch.empty((B, H_q, num_splits), dtype=f32, device=dev)
         self.out = torch.empty((B, H_q, D), dtype=f32, device=dev)
         self.lse = torch.empty((B, H_q), dtype=f32, device=dev)
-        self.fused = bool(fuse_merge) and self.H_sel == H_q and num_splits <= 8
+        self.fused = (bool(fuse_merge) and self.H_sel == H_q and num_splits <= 8
+                      and attention == "softmax")
         self.keep_partials = False
+        self.entmax_scratch = None
+        if attention == "entmax15":
+            n = entmax_scratch_floats(B, H_q, self.k_cap, page_size)
+            self.entmax_scratch = torch.empty(n, dtype=f32, device=dev)
 
     @classmethod
     def for_workload(cls, wl, device="cuda", num_splits=None, group_select=False,
-                     alibi_slopes=None, fuse_merge=True):
+                     alibi_slopes=None, fuse_merge=True, attention="softmax"):
         return cls(wl.B, wl.H_q, wl.H_kv, wl.D, wl.num_blocks, wl.P, wl.bt_ld,
                    topk_pages=wl.topk_pages, topk_frac=wl.topk_frac, bos=wl.bos,
                    eos=wl.eos, w_avg=wl.w_avg, w_peak=wl.w_peak,
@@ -107,7 +119,7 @@ class SparseDecoder:
                    num_splits=wl.num_splits if num_splits is None else num_splits,
                    decay=wl.decay, token_level=(wl.name == "h2o_token"),
                    group_select=group_select, alibi_slopes=alibi_slopes,
-                   fuse_merge=fuse_merge, device=device)
+                   fuse_merge=fuse_merge, attention=attention, device=device)
 
     # ------------------------------------------------------------ stages
     def rebuild_stats(self, kv_cache, block_table, seq_lens, stream=None):
@@ -139,6 +151,13 @@ class SparseDecoder:
                   block_table=block_table, sel_blk=blk, stream=stream)
 
     def attend(self, q, kv_cache, block_table, seq_lens, stream=None):
+        if self.attention == "entmax15":
+            entmax15_paged_decode(q, kv_cache, block_table, seq_lens, self.sel_idx,
+                                  self.sel_cnt, self.scale, self.o_part, self.lse_part,
+                                  self.entmax_scratch,
+                                  sel_blk=self.sel_blk if self.use_sel_blk else None,
+                                  stream=stream)
+            return
         if self.fused:
             parts = (self.o_part, self.lse_part) if self.keep_partials else (None, None)
             sparse_paged_decode_merged(
@@ -171,3 +190,8 @@ class SparseDecoder:
         self.attend(q, kv_cache, block_table, seq_lens, stream)
         self.merge(stream)
         return self.out, self.lse
+
+    def entmax_tau(self):
+        """tau per query head [B, H_q] of the last 1.5-entmax decode."""
+        n = self.B * self.H_q
+        return self.entmax_scratch[-n:].view(self.B, self.H_q)

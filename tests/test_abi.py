@@ -41,6 +41,7 @@ def test_header_declares_the_six_operations():
     names = _declared()
     for n in ("pagestats_update", "page_score", "page_score_group", "page_topk",
               "sparse_paged_decode", "sparse_paged_decode_merged",
+              "entmax15_paged_decode", "entmax_scratch_floats",
               "lse_merge", "h2o_accumulate", "h2o_scratch_floats",
               "sparsekv_last_error"):
         assert n in names
@@ -106,6 +107,13 @@ def test_validation_rejects_bad_scalars(lib):
                                           4, 0.1, 4, p, None, None, p, None, s) == EINVAL
     assert lib.sparse_paged_decode_merged(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p, None,
                                           4, 0.1, 4, None, None, None, None, None, s) == EFAULT
+    # entmax: scratch too small, splits < 1
+    assert lib.entmax15_paged_decode(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p, None, 4, 8,
+                                     0.1, 2, p, p, p, 3, s) == EINVAL
+    assert "scratch" in _msg(lib)
+    assert lib.entmax15_paged_decode(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p, None, 4, 8,
+                                     0.1, 0, p, p, p, 10 ** 6, s) == EINVAL
+    assert lib.entmax_scratch_floats(2, 8, 4, 16) == 2 * 8 * 4 * 16 + 2 * 8
     # h2o: page size must be 1, decay in (0, 1]
     assert lib.h2o_accumulate(p, 1, 8, 2, 128, p, 8, 16, p, 8, p, 0, 1, 0.1, 0.98,
                               p, p, 8, p, 10 ** 6, s) == EINVAL

@@ -279,6 +279,70 @@ def test_alibi_step(case):
     say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}")
 
 
+# seed, B, H_q, H_kv, D, P, max_pages, topk, splits, group_select, scale
+ENTMAX_CASES = [
+    (95, 2, 8, 2, 128, 16, 30, 6, 3, False, None),
+    (96, 2, 4, 4, 64, 4, 40, 7, 4, False, 1.0),
+    (97, 1, 16, 2, 128, 16, 50, 9, 5, True, None),
+    (98, 2, 6, 3, 64, 1, 120, 20, 2, True, 0.5),
+]
+
+
+def run_entmax_case(wl, cache_cpu, q_cpu, group):
+    """Page level with 1.5-entmax attention over the GPU's own selection."""
+    cache = dev(cache_cpu)
+    q = dev(q_cpu)
+    bt = dev(wl.block_table)
+    sl = dev(wl.seq_lens)
+    d = SparseDecoder(wl.B, wl.H_q, wl.H_kv, wl.D, wl.num_blocks, wl.P, wl.bt_ld,
+                      topk_pages=wl.topk_pages, topk_frac=wl.topk_frac, bos=wl.bos,
+                      eos=wl.eos, w_avg=wl.w_avg, w_peak=wl.w_peak,
+                      scale=wl.softmax_scale, num_splits=wl.num_splits,
+                      group_select=group, attention="entmax15")
+    poison(d)
+    d.entmax_scratch.fill_(float("nan"))
+    d.rebuild_stats(cache, bt, sl)
+    d.score(q, bt, sl)
+    d.select(sl, bt)
+    d.attend(q, cache, bt, sl)
+    d.merge()
+    torch.cuda.synchronize()
+    cb = bits(cache)
+    qd = q_cpu.double().numpy()
+    sel_idx = d.sel_idx.cpu().numpy().reshape(-1, d.k_cap)
+    sel_cnt = d.sel_cnt.cpu().numpy().reshape(-1)
+    per = per_head_rows(selection_rows(sel_idx, sel_cnt), wl.B, wl.H_q, d.H_sel)
+    out = d.out.cpu().numpy()
+    gtau = d.entmax_tau().cpu().numpy()
+    worst = 0.0
+    for b in range(wl.B):
+        for i in range(wl.H_q):
+            o, tau = oracle.attend_entmax15(qd[b, i], cb, i // wl.G, wl.block_table[b],
+                                            int(wl.seq_lens[b]), per[b][i], wl.softmax_scale)
+            assert not np.any(np.isnan(out[b, i])), f"NaN output ({b},{i})"
+            e = np.abs(out[b, i].astype(np.float64) - o).max()
+            worst = max(worst, e)
+            assert e <= 2e-3, f"entmax out ({b},{i}) err {e}"
+            if np.isinf(tau):
+                assert np.isinf(gtau[b, i])
+            else:
+                assert abs(float(gtau[b, i]) - tau) <= 1e-4 * max(1.0, abs(tau)), \
+                    f"tau ({b},{i}) {gtau[b, i]} vs {tau}"
+    return worst
+
+
+@pytest.mark.parametrize("case", ENTMAX_CASES, ids=[f"entmax{c[0]}" for c in ENTMAX_CASES])
+def test_entmax_step(case):
+    (seed, B, H_q, H_kv, D, P, maxp, topk, ns, group, scale) = case
+    say(f"[gpu] 1.5-entmax case {case}")
+    wl = W.small_case(seed=seed, B=B, H_q=H_q, H_kv=H_kv, D=D, P=P, max_pages=maxp,
+                      topk_pages=topk, num_splits=ns)
+    if scale is not None:
+        wl.scale = scale
+    worst = run_entmax_case(wl, W.make_cache(wl), W.make_queries(wl), group)
+    say(f"  max |out - oracle| = {worst:.2e}")
+
+
 def test_all_equal_scores_tie_break_to_lower_index():
     say("[gpu] zero cache: every score ties")
     wl = W.small_case(seed=20, B=2, H_q=4, H_kv=2, D=128, P=16, max_pages=30,

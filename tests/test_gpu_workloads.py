@@ -109,6 +109,16 @@ def test_long_context_alibi():
     say(f"  long_context ALiBi: max |out - oracle| {worst:.2e}, near-tie rows {ex}")
 
 
+def test_long_context_entmax():
+    """long_context attended with 1.5-entmax over its 256 pages per head."""
+    from test_gpu_kernels import run_entmax_case
+    wl = W.long_context()
+    say("[gpu] workload long_context with 1.5-entmax: generating")
+    cache = W.make_cache(wl, device="cuda")
+    worst = run_entmax_case(wl, cache, W.make_queries(wl), False)
+    say(f"  long_context 1.5-entmax: max |out - oracle| {worst:.2e}")
+
+
 def test_high_batch_sampled_after_appends():
     wl = W.high_batch()
     say("[gpu] workload high_batch: generating 300k-block pool")
