@@ -58,8 +58,8 @@ def parse():
     ap.add_argument("--attention", default="softmax", choices=["softmax", "entmax15"],
                     help="page level: softmax, or 1.5-entmax over the same selection")
     ap.add_argument("--no-fuse", action="store_true",
-                    help="keep lse_merge as its own launch even where the decode "
-                         "can merge its splits in-block")
+                    help="keep page_topk and lse_merge as their own launches even "
+                         "where the decode can select and merge in-block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="enqueue kernel by kernel instead of replaying HIP graphs")
@@ -267,6 +267,7 @@ def main():
                                        attention="entmax15" if entmax else "softmax")
             for _ in range(R)]
     fused = decs[0].fused
+    in_decode = decs[0].select_in_decode
     new_kv = [W.make_new_kv(wl, s, device=dev) for s in range(min(wl.steps, 64))] \
         if wl.steps > 1 else None
     if token_level:
@@ -305,7 +306,8 @@ def main():
 
     names = (["pagestats_update"] if wl.steps > 1 else []) + \
         (["h2o_accumulate"] if token_level else ["page_score"]) + \
-        ["page_topk", "sparse_paged_decode"] + ([] if fused else ["lse_merge"])
+        (["sparse_select_decode"] if in_decode else
+         ["page_topk", "sparse_paged_decode"] + ([] if fused else ["lse_merge"]))
 
     def enqueue(i, name):
         """Enqueue kernel `name` of step i (replica i % R, sequence step i % steps)."""
@@ -324,6 +326,8 @@ def main():
             d.select(sl, bt)
         elif name == "sparse_paged_decode":
             d.attend(q, c, bt, sl)
+        elif name == "sparse_select_decode":
+            d.select_attend(q, c, bt, sl)
         else:
             d.merge()
 
@@ -369,6 +373,9 @@ def main():
     last = (args.warmup + args.steps - 1)
     d = decs[last % R]
     sl_last = wl.seq_lens_at(last % wl.steps)
+    if in_decode:   # the selection stays in LDS; recompute it for the byte count
+        d.select(seq_steps[last % wl.steps], bt)
+        torch.cuda.synchronize()
     sel_idx = d.sel_idx.cpu().numpy()
     sel_cnt = d.sel_cnt.cpu().numpy()
 
@@ -391,6 +398,9 @@ def main():
 
     kb, upages = kernel_bytes(wl, sel_idx, sel_cnt, sl_last, wl.num_splits, token_level,
                               group, fused, entmax, decs[0].k_cap)
+    if in_decode:   # one launch: the top-k's score read plus the merged decode
+        kb["sparse_select_decode"] = kb.pop("page_topk") - int(sel_cnt.sum()) * 4 \
+            + kb.pop("sparse_paged_decode")
     step_bytes = sum(kb.values())
     kern = {}
     for n in names:
@@ -398,7 +408,7 @@ def main():
         kern[n] = {"us": round(t * 1000, 2), "bytes": kb[n],
                    "GBps": round(kb[n] / (t * 1e-3) / 1e9, 1) if t > 0 else None}
     dominant = max(names, key=lambda n: per_kernel_ms[n])
-    focus = "sparse_paged_decode"
+    focus = "sparse_select_decode" if in_decode else "sparse_paged_decode"
     a = kb[focus] / (per_kernel_ms[focus] * 1e-3) / 1e9
     roofline = {"kernel": focus, "bound": "hbm", "achieved": round(a, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(a / PEAK_HBM_GBPS, 4),
@@ -423,6 +433,7 @@ def main():
                    "mean_seq_len": float(np.mean(sl_last)), "replicas": R,
                    "selection": ("kv_head" if (group or token_level) else "query_head"),
                    "alibi": slopes is not None, "merge_in_decode": fused,
+                   "select_in_decode": in_decode,
                    "attention": "entmax15" if entmax else "softmax",
                    "parallelism": "single-gpu"},
         "effective_GBps": round(step_bytes / (gpu_ms * 1e-3) / 1e9, 1),

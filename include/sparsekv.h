@@ -232,6 +232,34 @@ int sparse_paged_decode_merged(const float *q, int B, int H_q, int H_kv, int D,
                                float *lse_out, hipStream_t stream);
 
 /*
+ * sparse_select_decode -- page_topk and sparse_paged_decode_merged in one
+ * launch, for one selection per query head: one block per query head first
+ * selects from its score row into LDS, then its waves (one per split) attend
+ * over the selection and merge.  [Same sources as page_topk and
+ * sparse_paged_decode_merged.]
+ *
+ *   scores   fp32 [B, H_q, score_ld] (page_score's output), score_ld <= 4096
+ *   topk_pages, topk_frac, reserved_bos, reserved_eos, k_cap: as page_topk
+ *            (k_cap <= 4096)
+ *   q ... seq_lens, scale, num_splits (<= 8), alibi_slopes: as
+ *            sparse_paged_decode (H_sel = H_q)
+ *   out      fp32 [B, H_q, D];  lse_out fp32 [B, H_q] or NULL
+ *   sel_idx, sel_cnt (both or neither), sel_blk (needs sel_idx): when given,
+ *            receive the selection exactly as page_topk writes it.
+ * The result equals page_topk followed by sparse_paged_decode and lse_merge
+ * up to fp32 rounding order.
+ */
+int sparse_select_decode(const float *scores, int64_t score_ld, int topk_pages,
+                         float topk_frac, int reserved_bos, int reserved_eos,
+                         const float *q, int B, int H_q, int H_kv, int D,
+                         const uint16_t *kv_cache, int64_t num_blocks, int page_size,
+                         const int32_t *block_table, int64_t bt_ld,
+                         const int32_t *seq_lens, int k_cap, float scale,
+                         int num_splits, const float *alibi_slopes, float *out,
+                         float *lse_out, int32_t *sel_idx, int32_t *sel_cnt,
+                         int32_t *sel_blk, hipStream_t stream);
+
+/*
  * entmax15_paged_decode -- 1.5-entmax attention over the tokens of the
  * selected pages, as split partials for lse_merge.  [EKV "Quick start"
  * (alpha=1.5) and the component list (decode over selected pages, alpha 1.5);

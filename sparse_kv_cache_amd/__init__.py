@@ -20,7 +20,7 @@ __all__ = [
     "pagestats_update", "page_score", "page_score_group", "page_topk",
     "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
     "h2o_accumulate", "h2o_scratch_floats", "entmax15_paged_decode",
-    "entmax_scratch_floats", "library_path",
+    "entmax_scratch_floats", "sparse_select_decode", "library_path",
     "load_library", "SparseKVError", "EXPORTED_SYMBOLS",
 ]
 
@@ -32,11 +32,11 @@ EXPORTED_SYMBOLS = (
     "pagestats_update", "page_score", "page_score_group", "page_topk",
     "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
     "h2o_accumulate", "h2o_scratch_floats", "entmax15_paged_decode",
-    "entmax_scratch_floats", "sparsekv_last_error",
+    "entmax_scratch_floats", "sparse_select_decode", "sparsekv_last_error",
 )
 _INT_RETURNING = ("pagestats_update", "page_score", "page_score_group", "page_topk",
                   "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
-                  "h2o_accumulate", "entmax15_paged_decode")
+                  "h2o_accumulate", "entmax15_paged_decode", "sparse_select_decode")
 
 
 class SparseKVError(RuntimeError):
@@ -80,6 +80,8 @@ def load_library():
     lib.entmax15_paged_decode.argtypes = [V, I, I, I, I, V, L, I, V, L, V, V, V, V, I, I,
                                           F, I, V, V, V, L, V]
     lib.entmax_scratch_floats.argtypes = [I, I, I, I]
+    lib.sparse_select_decode.argtypes = [V, L, I, F, I, I, V, I, I, I, I, V, L, I, V, L, V,
+                                         I, F, I, V, V, V, V, V, V, V]
     lib.entmax_scratch_floats.restype = ctypes.c_int64
     for name in _INT_RETURNING:
         getattr(lib, name).restype = ctypes.c_int
@@ -361,6 +363,42 @@ def entmax15_paged_decode(q, kv_cache, block_table, seq_lens, sel_idx, sel_cnt, 
         block_table.shape[1], _ptr(seq_lens), _ptr(sel_idx), _ptr(sel_cnt), _ptr(sel_blk),
         sel_idx.shape[2], H_sel, float(scale), ns, _ptr(o_part), _ptr(lse_part),
         _ptr(scratch), scratch.numel(), _stream(stream)))
+
+
+def sparse_select_decode(scores, q, kv_cache, block_table, seq_lens, topk_pages, k_cap,
+                         scale, num_splits, out, lse_out=None, topk_frac=0.0,
+                         reserved_bos=0, reserved_eos=1, sel_idx=None, sel_cnt=None,
+                         sel_blk=None, alibi_slopes=None, stream=None):
+    """page_topk + sparse_paged_decode_merged in one launch (one selection per
+    query head, score_ld <= 4096, num_splits <= 8); optionally writes the
+    selection like page_topk."""
+    lib = load_library()
+    _check("scores", scores, torch.float32, 3)
+    _check("q", q, torch.float32, 3)
+    dev = q.device
+    B, H_q, D = q.shape
+    _check("kv_cache", kv_cache, torch.bfloat16, 5, dev)
+    _, NB, P, H_kv, D2 = kv_cache.shape
+    if D2 != D:
+        raise ValueError("q and kv_cache head dims differ")
+    if tuple(scores.shape[:2]) != (B, H_q):
+        raise ValueError("scores must be [B, H_q, score_ld]")
+    _check("block_table", block_table, torch.int32, 2, dev)
+    _check("seq_lens", seq_lens, torch.int32, 1, dev)
+    _check("out", out, torch.float32, 3, dev)
+    _check("lse_out", lse_out, torch.float32, 2, dev)
+    for n, t in (("sel_idx", sel_idx), ("sel_blk", sel_blk)):
+        _check(n, t, torch.int32, 3, dev)
+        if t is not None and tuple(t.shape) != (B, H_q, k_cap):
+            raise ValueError(f"{n} must be [B, H_q, k_cap]")
+    _check("sel_cnt", sel_cnt, torch.int32, 2, dev)
+    alibi_slopes = _alibi_arg(alibi_slopes, H_q, dev)
+    _rc("sparse_select_decode", lib.sparse_select_decode(
+        _ptr(scores), scores.shape[2], int(topk_pages), float(topk_frac), int(reserved_bos),
+        int(reserved_eos), _ptr(q), B, H_q, H_kv, D, _ptr(kv_cache), NB, P,
+        _ptr(block_table), block_table.shape[1], _ptr(seq_lens), int(k_cap), float(scale),
+        int(num_splits), _ptr(alibi_slopes), _ptr(out), _ptr(lse_out), _ptr(sel_idx),
+        _ptr(sel_cnt), _ptr(sel_blk), _stream(stream)))
 
 
 def lse_merge(o_part, lse_part, out, lse_out=None, stream=None):

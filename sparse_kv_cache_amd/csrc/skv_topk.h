@@ -1,0 +1,248 @@
+// skv_topk.h -- block-wide top-k selection of one score row, shared by the
+// page_topk kernel and the decode kernel that selects in-block.  Internal to
+// the library; not part of the C ABI.
+//
+// Selection: EntmaxKV README "How it works" (keep topk_pages per query head;
+// the budget counts pages and includes the always-attended tail page);
+// vortex_torch pull request "flow: add H2O sparse attention", hardware
+// follow-up (the reserved leading bos and trailing eos entries are kept and
+// only the window between them is ranked).
+//
+// Method.  Scores become order-preserving uint32 keys (-0.0 folded onto
+// +0.0) held in registers, ITEMS contiguous entries per thread.  A
+// most-significant-digit radix select finds the key prefix of the m-th best
+// candidate: the bits every candidate shares are skipped (block OR / AND),
+// each pass histograms the next 8 bits of the keys still matching the prefix
+// into its own LDS histogram (atomics; every wave then finds the digit
+// itself, so a pass costs one barrier), and the select stops as soon as the
+// chosen bin is taken whole.  Keys above the prefix are taken; when equal keys
+// must be split, the lowest indices are taken, ranked by a block-wide prefix
+// count in index order.  A prefix count over the final flags writes the
+// indices in ascending order with no sort.
+#pragma once
+
+#include <limits.h>
+
+#include "skv_device.h"
+
+namespace skv {
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;                        // -0.0 == +0.0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Select within one row of N scores (srow, 16-byte aligned when aligned16)
+// with the whole block: writes the ascending selection to out[0, k_cap)
+// (padded with -1) and, when bout is given, the selected pages' physical
+// blocks btr[p] to bout; returns the selected count (every thread).  out and
+// bout may point to global or LDS memory.  Ends with a block barrier.
+template <int BLOCK, int ITEMS>
+__device__ int topk_row(const float* __restrict__ srow, bool aligned16, int N,
+                        int topk_pages, double topk_frac, int bos, int eos,
+                        const int32_t* __restrict__ btr, int64_t bt_ld,
+                        int32_t* out, int32_t* bout, int k_cap) {
+  constexpr int NW = BLOCK / 64;
+  constexpr int kBits = 8;                       // digit width
+  constexpr int kBins = 1 << kBits;
+  constexpr int kPasses = 4;                     // 32 / 8
+  constexpr int kPerLane = kBins / 64;           // bins a lane scans
+  __shared__ __align__(16) int hist[kPasses][kBins];   // one histogram per pass
+  __shared__ int scan_smem[NW + 1];
+  __shared__ uint32_t s_or[NW], s_and[NW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  int k = topk_pages;
+  const double f = floor(topk_frac * static_cast<double>(N));
+  if (f > static_cast<double>(k)) k = static_cast<int>(f);
+  if (k > N) k = N;
+  const int lo = bos < N ? bos : N;
+  int hi = N - eos > 0 ? N - eos : 0;
+  if (hi < lo) hi = lo;
+  const int nres = N - (hi - lo);
+  const int want = k - nres > 0 ? k - nres : 0;
+  const int ncand = hi - lo;
+
+  const int base = tid * ITEMS;
+  uint32_t key[ITEMS];
+  constexpr bool kVec = ITEMS % 4 == 0;          // 16-byte pieces per thread
+  const bool vec = kVec && aligned16 && (base + ITEMS <= hi) && (base >= lo);
+  if (vec) {
+    if constexpr (kVec) {
+#pragma unroll
+      for (int i = 0; i < ITEMS; i += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(srow + base + i);
+        key[i] = order_key(v.x); key[i + 1] = order_key(v.y);
+        key[i + 2] = order_key(v.z); key[i + 3] = order_key(v.w);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      const int p = base + i;
+      key[i] = (p >= lo && p < hi) ? order_key(srow[p]) : 0u;
+    }
+  }
+  // block ids of this thread's entries, fetched alongside the keys
+  int32_t bid[ITEMS];
+  if (bout != nullptr) {
+    if (kVec && ((bt_ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(btr) & 15) == 0) &&
+        base + ITEMS <= N && base + ITEMS <= bt_ld) {
+      if constexpr (kVec) {
+#pragma unroll
+        for (int i = 0; i < ITEMS; i += 4) {
+          const int4 v = *reinterpret_cast<const int4*>(btr + base + i);
+          bid[i] = v.x; bid[i + 1] = v.y; bid[i + 2] = v.z; bid[i + 3] = v.w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < ITEMS; ++i) {
+        const int p = base + i;
+        bid[i] = (p < N && p < bt_ld) ? btr[p] : -1;
+      }
+    }
+  }
+  for (int j = tid; j < kPasses * kBins; j += BLOCK) (&hist[0][0])[j] = 0;
+
+  // Selection state: candidates whose (key & pmask) exceeds prefix are taken;
+  // among those equal to prefix under pmask, the r_eq lowest indices.
+  uint32_t prefix, pmask;
+  int r_eq;
+  bool ties = false;                   // r_eq < number equal to the prefix
+  if (want == 0) {
+    prefix = 0xffffffffu; pmask = 0xffffffffu; r_eq = 0;   // reserved only
+  } else if (want >= ncand) {
+    prefix = 0u; pmask = 0u; r_eq = INT_MAX;               // every candidate
+  } else {
+    // Bits shared by every candidate need no radix pass: start the digits at
+    // the highest bit where two candidates differ.
+    uint32_t o = 0u, a = 0xffffffffu;
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      const int p = base + i;
+      if (p >= lo && p < hi) { o |= key[i]; a &= key[i]; }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      o |= __shfl_xor(o, off);
+      a &= __shfl_xor(a, off);
+    }
+    if (lane == 0) { s_or[wave] = o; s_and[wave] = a; }
+    __syncthreads();                   // also orders the histogram clearing
+    o = 0u; a = 0xffffffffu;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) { o |= s_or[w]; a &= s_and[w]; }
+    const uint32_t diff = o ^ a;       // bits that vary among candidates
+    int top = diff ? 31 - __clz(diff) : -1;
+    // bits below the lowest varying one are equal too (bf16-valued scores
+    // leave the low 16 bits of every key the same)
+    const int bot = diff ? __ffs(static_cast<int>(diff)) - 1 : 0;
+    pmask = top >= 0 ? ~((2u << top) - 1u) : 0xffffffffu;
+    if (top == 31) pmask = 0u;
+    prefix = a & pmask;
+    int remaining = want;
+    int bin = ncand;                   // entries matching the prefix so far
+    int pass = 0;
+    while (remaining < bin && top >= bot) {
+      int shift = top >= kBits - 1 ? top - (kBits - 1) : 0;
+      if (shift < bot) shift = bot;
+      const int width = top - shift + 1;
+      const uint32_t dmask = (1u << width) - 1u;
+      int* hp = hist[pass];
+#pragma unroll
+      for (int i = 0; i < ITEMS; ++i) {
+        const int p = base + i;
+        if (p >= lo && p < hi && (key[i] & pmask) == prefix)
+          atomicAdd(&hp[(key[i] >> shift) & dmask], 1);
+      }
+      __syncthreads();
+      // every wave finds the digit itself: no broadcast, no second barrier.
+      // Lane l scans bins [kPerLane * l, kPerLane * (l + 1)).
+      int cs[kPerLane];
+#pragma unroll
+      for (int j = 0; j < kPerLane; j += 4) {
+        const int4 v = *reinterpret_cast<const int4*>(&hp[kPerLane * lane + j]);
+        cs[j] = v.x; cs[j + 1] = v.y; cs[j + 2] = v.z; cs[j + 3] = v.w;
+      }
+      int sum = 0;
+#pragma unroll
+      for (int j = 0; j < kPerLane; ++j) sum += cs[j];
+      const int incl = skv::wave_inclusive_scan(sum);
+      int above = __builtin_amdgcn_readlane(incl, 63) - incl;   // in higher digits
+      int my_digit = 0, my_rem = 0, my_bin = 0;
+      bool found = false;
+#pragma unroll
+      for (int j = kPerLane - 1; j >= 0; --j) {
+        if (above < remaining && above + cs[j] >= remaining) {
+          my_digit = kPerLane * lane + j;
+          my_rem = remaining - above;
+          my_bin = cs[j];
+          found = true;
+        }
+        above += cs[j];
+      }
+      const unsigned long long ball = __ballot(found);
+      const int src = __ffsll(static_cast<long long>(ball)) - 1;   // wave-uniform
+      const uint32_t dg = static_cast<uint32_t>(__builtin_amdgcn_readlane(my_digit, src));
+      remaining = __builtin_amdgcn_readlane(my_rem, src);
+      bin = __builtin_amdgcn_readlane(my_bin, src);
+      prefix |= dg << shift;
+      pmask |= dmask << shift;
+      top = shift - 1;
+      ++pass;
+    }
+    r_eq = remaining;
+    ties = remaining < bin;            // fully resolved with equal keys left
+  }
+
+  // ranks among the entries equal to the prefix (only needed for ties)
+  int er = 0;
+  if (ties) {
+    int eq = 0;
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      const int p = base + i;
+      eq += (p >= lo && p < hi && (key[i] & pmask) == prefix) ? 1 : 0;
+    }
+    int total_eq;
+    er = skv::block_exclusive_scan(eq, &total_eq, scan_smem);
+  }
+
+  uint32_t flags = 0u;
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int p = base + i;
+    const uint32_t km = key[i] & pmask;
+    bool take;
+    if (p >= N) take = false;
+    else if (p < lo || p >= hi) take = true;
+    else if (km > prefix) take = true;
+    else if (km == prefix) { take = er < r_eq; ++er; }
+    else take = false;
+    if (take) { flags |= 1u << i; ++cnt; }
+  }
+  int total;
+  int pos = skv::block_exclusive_scan(cnt, &total, scan_smem);
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    if (flags & (1u << i)) {
+      if (pos >= 0 && pos < k_cap) {
+        out[pos] = base + i;
+        if (bout != nullptr) bout[pos] = bid[i];
+      }
+      ++pos;
+    }
+  }
+  for (int j = total + tid; j < k_cap; j += BLOCK) {
+    out[j] = -1;
+    if (bout != nullptr) bout[j] = -1;
+  }
+  __syncthreads();
+  return total < k_cap ? total : k_cap;
+}
+
+}  // namespace skv

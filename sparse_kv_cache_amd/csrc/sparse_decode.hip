@@ -37,6 +37,7 @@
 
 #include "skv_device.h"
 #include "skv_host.h"
+#include "skv_topk.h"
 
 namespace {
 
@@ -180,7 +181,15 @@ __device__ __forceinline__ Chunk split_chunk(int cnt, int k_cap, int num_splits,
 // block merges its splits' states through LDS and writes the merged output
 // and lse itself (the lse_merge algebra), so no separate merge launch is
 // needed.  Partials are still written when o_part / lse_part are given.
-template <int D, int WB, int PFIX, bool AL, bool FUSE>
+// In-block selection (TKI > 0, with FUSE): the block first runs the top-k of
+// its query head's score row (TKI entries per thread) into LDS, then decodes
+// from there; the selection is copied out only when asked.
+struct TopkArgs {
+  const float* scores; int64_t score_ld; int topk_pages; double topk_frac;
+  int bos, eos; int32_t* sel_idx; int32_t* sel_cnt; int32_t* sel_blk;
+};
+
+template <int D, int WB, int PFIX, bool AL, bool FUSE, int TKI>
 __global__ __launch_bounds__(WB * 64)
 __attribute__((amdgpu_waves_per_eu(PFIX == 16 ? SKV_DECODE_WPE16 : SKV_DECODE_WPE)))
 void sparse_decode_wave_kernel(
@@ -192,7 +201,8 @@ void sparse_decode_wave_kernel(
     int k_cap, float scale_log2, int num_splits, float* __restrict__ o_part,
     float* __restrict__ lse_part, int64_t n_groups, int blocks_per_group,
     const float* __restrict__ alibi, float* __restrict__ out,
-    float* __restrict__ lse_out) {
+    float* __restrict__ lse_out, TopkArgs ta) {
+  static_assert(TKI == 0 || FUSE, "in-block selection merges in-block");
   constexpr int LPR = D / 8;
   constexpr int RPL = 64 / LPR;
   constexpr int NL = 16 / RPL;
@@ -227,10 +237,34 @@ void sparse_decode_wave_kernel(
   // shorter or empty, and nothing past the row's k_cap entries is read
   int avail = k_cap - start;
   avail = avail < 0 ? 0 : (avail > cap ? cap : avail);
-  const int32_t* selr = sel_idx + qrow * k_cap + start;
-  const int32_t* sblk = sel_blk != nullptr ? sel_blk + qrow * k_cap + start : nullptr;
-  int cnt = sel_cnt[qrow];
-  cnt = cnt < 0 ? 0 : (cnt > k_cap ? k_cap : cnt);
+  const int32_t* selr;
+  const int32_t* sblk;
+  int cnt;
+  if constexpr (TKI > 0) {
+    extern __shared__ int32_t sel_lds[];          // [k_cap] indices, [k_cap] blocks
+    int64_t Nt = (static_cast<int64_t>(S) + P - 1) / P;
+    if (Nt > ta.score_ld) Nt = ta.score_ld;
+    const bool aligned = ((ta.score_ld & 3) == 0) &&
+                         ((reinterpret_cast<uintptr_t>(ta.scores) & 15) == 0);
+    cnt = skv::topk_row<WB * 64, TKI>(
+        ta.scores + qrow * ta.score_ld, aligned, static_cast<int>(Nt), ta.topk_pages,
+        ta.topk_frac, ta.bos, ta.eos, bt + static_cast<int64_t>(b) * bt_ld, bt_ld,
+        sel_lds, sel_lds + k_cap, k_cap);
+    if (ta.sel_idx != nullptr) {
+      for (int j = threadIdx.x; j < k_cap; j += WB * 64) {
+        ta.sel_idx[qrow * k_cap + j] = sel_lds[j];
+        if (ta.sel_blk != nullptr) ta.sel_blk[qrow * k_cap + j] = sel_lds[k_cap + j];
+      }
+      if (threadIdx.x == 0) ta.sel_cnt[qrow] = cnt;
+    }
+    selr = sel_lds + start;
+    sblk = sel_lds + k_cap + start;
+  } else {
+    selr = sel_idx + qrow * k_cap + start;
+    sblk = sel_blk != nullptr ? sel_blk + qrow * k_cap + start : nullptr;
+    cnt = sel_cnt[qrow];
+    cnt = cnt < 0 ? 0 : (cnt > k_cap ? k_cap : cnt);
+  }
   int clen = cnt - start;
   clen = clen < 0 ? 0 : (clen > cap ? cap : clen);
 
@@ -701,28 +735,29 @@ template <int D, int PFIX, bool AL>
 void launch_wave(hipStream_t st, const Args& a, int64_t n_groups) {
   const int per_group = (a.num_splits * a.G + kWaveBlock - 1) / kWaveBlock;
   const int64_t blocks = kXcds * per_group * ((n_groups + kXcds - 1) / kXcds);
-  hipLaunchKernelGGL((sparse_decode_wave_kernel<D, kWaveBlock, PFIX, AL, false>),
+  hipLaunchKernelGGL((sparse_decode_wave_kernel<D, kWaveBlock, PFIX, AL, false, 0>),
                      dim3(static_cast<unsigned>(blocks)), dim3(kWaveBlock * 64), 0, st,
                      a.q, a.H_q, a.H_kv, a.G, a.kv, a.num_blocks, a.P, a.bt, a.bt_ld,
                      a.seq_lens, a.sel_idx, a.sel_cnt, a.sel_blk, a.k_cap, a.scale_log2,
                      a.num_splits, a.o_part, a.lse_part, n_groups, per_group, a.alibi,
-                     nullptr, nullptr);
+                     nullptr, nullptr, TopkArgs{});
 }
 
 // One block per query head, kFuseWaves waves = splits, merged in the block.
 constexpr int kFuseWaves = 8;
 
-template <int D, int PFIX, bool AL>
+template <int D, int PFIX, bool AL, int TKI>
 void launch_wave_fused(hipStream_t st, const Args& a, int64_t n_groups, float* out,
-                       float* lse_out) {
+                       float* lse_out, const TopkArgs& ta) {
   const int per_group = a.G;
   const int64_t blocks = kXcds * per_group * ((n_groups + kXcds - 1) / kXcds);
-  hipLaunchKernelGGL((sparse_decode_wave_kernel<D, kFuseWaves, PFIX, AL, true>),
-                     dim3(static_cast<unsigned>(blocks)), dim3(kFuseWaves * 64), 0, st,
+  const size_t lds = TKI > 0 ? sizeof(int32_t) * 2 * static_cast<size_t>(a.k_cap) : 0;
+  hipLaunchKernelGGL((sparse_decode_wave_kernel<D, kFuseWaves, PFIX, AL, true, TKI>),
+                     dim3(static_cast<unsigned>(blocks)), dim3(kFuseWaves * 64), lds, st,
                      a.q, a.H_q, a.H_kv, a.G, a.kv, a.num_blocks, a.P, a.bt, a.bt_ld,
                      a.seq_lens, a.sel_idx, a.sel_cnt, a.sel_blk, a.k_cap, a.scale_log2,
                      a.num_splits, a.o_part, a.lse_part, n_groups, per_group, a.alibi,
-                     out, lse_out);
+                     out, lse_out, ta);
 }
 
 template <int D, bool AL>
@@ -797,8 +832,10 @@ int decode_impl(const char* who, const float* q, int B, int H_q, int H_kv, int D
   } else if (out != nullptr) {
 #define SKV_FUSED(DD, PP)                                                          \
   do {                                                                             \
-    if (al) launch_wave_fused<DD, PP, true>(stream, a, n_groups, out, lse_out);    \
-    else launch_wave_fused<DD, PP, false>(stream, a, n_groups, out, lse_out);      \
+    if (al) launch_wave_fused<DD, PP, true, 0>(stream, a, n_groups, out, lse_out,  \
+                                               TopkArgs{});                      \
+    else launch_wave_fused<DD, PP, false, 0>(stream, a, n_groups, out, lse_out,    \
+                                             TopkArgs{});                        \
   } while (0)
     if (page_size == 16) {
       if (D == 128) SKV_FUSED(128, 16); else SKV_FUSED(64, 16);
@@ -858,4 +895,84 @@ extern "C" int sparse_paged_decode_merged(const float* q, int B, int H_q, int H_
                      num_blocks, page_size, block_table, bt_ld, seq_lens, sel_idx, sel_cnt,
                      sel_blk, k_cap, H_q, scale, num_splits, o_part, lse_part, alibi_slopes,
                      out, lse_out, stream);
+}
+
+extern "C" int sparse_select_decode(const float* scores, int64_t score_ld, int topk_pages,
+                                    float topk_frac, int reserved_bos, int reserved_eos,
+                                    const float* q, int B, int H_q, int H_kv, int D,
+                                    const uint16_t* kv_cache, int64_t num_blocks,
+                                    int page_size, const int32_t* block_table,
+                                    int64_t bt_ld, const int32_t* seq_lens, int k_cap,
+                                    float scale, int num_splits, const float* alibi_slopes,
+                                    float* out, float* lse_out, int32_t* sel_idx,
+                                    int32_t* sel_cnt, int32_t* sel_blk,
+                                    hipStream_t stream) {
+  const char* who = "sparse_select_decode";
+  SKV_REQUIRE(B >= 0 && H_kv > 0 && H_q > 0 && H_q % H_kv == 0,
+              "%s: need H_q a positive multiple of H_kv", who);
+  const int G = H_q / H_kv;
+  SKV_REQUIRE(G <= 16, "%s: group size %d > 16", who, G);
+  SKV_REQUIRE(D == 64 || D == 128, "%s: D must be 64 or 128 (got %d)", who, D);
+  SKV_REQUIRE(skv_supported_page_size(page_size),
+              "%s: page_size must be 1, 2, 4, 8 or 16 (got %d)", who, page_size);
+  SKV_REQUIRE(num_splits >= 1 && num_splits <= kFuseWaves,
+              "%s: num_splits must be in [1, %d] (got %d)", who, kFuseWaves, num_splits);
+  SKV_REQUIRE(score_ld > 0 && score_ld <= 8 * kFuseWaves * 64,
+              "%s: score_ld must be in [1, %d] (got %lld)", who, 8 * kFuseWaves * 64,
+              (long long)score_ld);
+  SKV_REQUIRE(topk_pages >= 1, "%s: topk_pages must be >= 1 (got %d)", who, topk_pages);
+  SKV_REQUIRE(topk_frac >= 0.0f && topk_frac <= 1.0f, "%s: topk_frac must be in [0, 1]", who);
+  SKV_REQUIRE(reserved_bos >= 0 && reserved_eos >= 0,
+              "%s: reserved_bos / reserved_eos must be >= 0", who);
+  SKV_REQUIRE(num_blocks > 0 && num_blocks <= 0x7fffffffLL && bt_ld > 0,
+              "%s: need 0 < num_blocks < 2^31 and bt_ld > 0", who);
+  const double frac = static_cast<double>(topk_frac);
+  int64_t need = topk_pages;
+  const int64_t fk = static_cast<int64_t>(floor(frac * static_cast<double>(score_ld)));
+  if (fk > need) need = fk;
+  if (static_cast<int64_t>(reserved_bos) + reserved_eos > need)
+    need = static_cast<int64_t>(reserved_bos) + reserved_eos;
+  if (need > score_ld) need = score_ld;
+  SKV_REQUIRE(k_cap >= need && k_cap <= 4096,
+              "%s: k_cap %d must cover the largest selection %lld (and be <= 4096)", who,
+              k_cap, (long long)need);
+  SKV_REQUIRE(B <= 65535, "%s: grid too large", who);
+  SKV_REQUIRE_PTR_W(who, scores);
+  SKV_REQUIRE_PTR_W(who, q);
+  SKV_REQUIRE_PTR_W(who, kv_cache);
+  SKV_REQUIRE_PTR_W(who, block_table);
+  SKV_REQUIRE_PTR_W(who, seq_lens);
+  SKV_REQUIRE_PTR_W(who, out);
+  SKV_REQUIRE((sel_idx == nullptr) == (sel_cnt == nullptr),
+              "%s: sel_idx and sel_cnt must both be given or both be NULL", who);
+  SKV_REQUIRE(sel_blk == nullptr || sel_idx != nullptr,
+              "%s: sel_blk needs sel_idx", who);
+  if (B == 0) { skv::clear_error(); return SKV_OK; }
+  const int64_t n_groups = static_cast<int64_t>(B) * H_kv;
+  const Args a{q, H_q, H_kv, G, kv_cache, num_blocks, page_size, block_table, bt_ld,
+               seq_lens, nullptr, nullptr, nullptr, k_cap, scale * skv::kLog2e, num_splits,
+               nullptr, nullptr, alibi_slopes};
+  const TopkArgs ta{scores, score_ld, topk_pages, frac, reserved_bos, reserved_eos,
+                    sel_idx, sel_cnt, sel_blk};
+  const bool al = alibi_slopes != nullptr;
+  const int tki = score_ld <= 512 ? 1 : score_ld <= 2048 ? 4 : 8;
+#define SKV_SEL(DD, PP, TT)                                                            \
+  do {                                                                                 \
+    if (al) launch_wave_fused<DD, PP, true, TT>(stream, a, n_groups, out, lse_out, ta); \
+    else launch_wave_fused<DD, PP, false, TT>(stream, a, n_groups, out, lse_out, ta);   \
+  } while (0)
+#define SKV_SEL_T(DD, PP)                                                              \
+  do {                                                                                 \
+    if (tki == 1) SKV_SEL(DD, PP, 1);                                                  \
+    else if (tki == 4) SKV_SEL(DD, PP, 4);                                             \
+    else SKV_SEL(DD, PP, 8);                                                           \
+  } while (0)
+  if (page_size == 16) {
+    if (D == 128) SKV_SEL_T(128, 16); else SKV_SEL_T(64, 16);
+  } else {
+    if (D == 128) SKV_SEL_T(128, 0); else SKV_SEL_T(64, 0);
+  }
+#undef SKV_SEL_T
+#undef SKV_SEL
+  SKV_CHECK_LAUNCH();
 }

@@ -23,7 +23,8 @@ import torch
 
 from . import (entmax15_paged_decode, entmax_scratch_floats, h2o_accumulate,
                h2o_scratch_floats, lse_merge, page_score, page_score_group, page_topk,
-               pagestats_update, sparse_paged_decode, sparse_paged_decode_merged)
+               pagestats_update, sparse_paged_decode, sparse_paged_decode_merged,
+               sparse_select_decode)
 
 
 def alibi_slopes(H, device="cuda"):
@@ -104,6 +105,9 @@ class SparseDecoder:
         self.fused = (bool(fuse_merge) and self.H_sel == H_q and num_splits <= 8
                       and attention == "softmax")
         self.keep_partials = False
+        # selection inside the decode launch as well (score rows <= 4096)
+        self.select_in_decode = self.fused and bt_ld <= 4096 and self.k_cap <= 4096
+        self.keep_selection = False
         self.entmax_scratch = None
         if attention == "entmax15":
             n = entmax_scratch_floats(B, H_q, self.k_cap, page_size)
@@ -171,6 +175,16 @@ class SparseDecoder:
                             sel_blk=self.sel_blk if self.use_sel_blk else None,
                             alibi_slopes=self.alibi, stream=stream)
 
+    def select_attend(self, q, kv_cache, block_table, seq_lens, stream=None):
+        """Selection, decode and merge in one launch (select_in_decode)."""
+        keep = self.keep_selection
+        sparse_select_decode(
+            self.scores, q, kv_cache, block_table, seq_lens, self.topk_pages, self.k_cap,
+            self.scale, self.num_splits, self.out, self.lse, topk_frac=self.topk_frac,
+            reserved_bos=self.bos, reserved_eos=self.eos,
+            sel_idx=self.sel_idx if keep else None, sel_cnt=self.sel_cnt if keep else None,
+            sel_blk=self.sel_blk if keep else None, alibi_slopes=self.alibi, stream=stream)
+
     def merge(self, stream=None):
         if self.fused:
             return                      # merged inside attend()
@@ -186,6 +200,9 @@ class SparseDecoder:
             self.accumulate(q, kv_cache, block_table, seq_lens, stream)
         else:
             self.score(q, block_table, seq_lens, stream)
+        if self.select_in_decode:
+            self.select_attend(q, kv_cache, block_table, seq_lens, stream)
+            return self.out, self.lse
         self.select(seq_lens, block_table, stream)
         self.attend(q, kv_cache, block_table, seq_lens, stream)
         self.merge(stream)

@@ -41,7 +41,7 @@ def test_header_declares_the_six_operations():
     names = _declared()
     for n in ("pagestats_update", "page_score", "page_score_group", "page_topk",
               "sparse_paged_decode", "sparse_paged_decode_merged",
-              "entmax15_paged_decode", "entmax_scratch_floats",
+              "entmax15_paged_decode", "entmax_scratch_floats", "sparse_select_decode",
               "lse_merge", "h2o_accumulate", "h2o_scratch_floats",
               "sparsekv_last_error"):
         assert n in names
@@ -107,6 +107,15 @@ def test_validation_rejects_bad_scalars(lib):
                                           4, 0.1, 4, p, None, None, p, None, s) == EINVAL
     assert lib.sparse_paged_decode_merged(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p, None,
                                           4, 0.1, 4, None, None, None, None, None, s) == EFAULT
+    # select+decode: at most 8 splits, rows of at most 4096, selection outputs paired
+    assert lib.sparse_select_decode(p, 64, 4, 0.0, 0, 1, p, 1, 8, 2, 128, p, 8, 16, p, 4, p,
+                                    8, 0.1, 9, None, p, None, None, None, None, s) == EINVAL
+    assert lib.sparse_select_decode(p, 5000, 4, 0.0, 0, 1, p, 1, 8, 2, 128, p, 8, 16, p, 4,
+                                    p, 8, 0.1, 2, None, p, None, None, None, None, s) == EINVAL
+    assert lib.sparse_select_decode(p, 64, 4, 0.0, 0, 1, p, 1, 8, 2, 128, p, 8, 16, p, 4, p,
+                                    8, 0.1, 2, None, p, None, p, None, None, s) == EINVAL
+    assert lib.sparse_select_decode(p, 64, 4, 0.0, 0, 1, p, 1, 8, 2, 128, p, 8, 16, p, 4, p,
+                                    8, 0.1, 2, None, None, None, None, None, None, s) == EFAULT
     # entmax: scratch too small, splits < 1
     assert lib.entmax15_paged_decode(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p, None, 4, 8,
                                      0.1, 2, p, p, p, 3, s) == EINVAL

@@ -83,6 +83,20 @@ def run_page_case(wl, cache_cpu, q_cpu, exact_ties=False):
         assert torch.allclose(lse_f, d.lse, rtol=0, atol=1e-5, equal_nan=False), \
             "merged decode lse differs"
         d.fused = True
+    if d.select_in_decode:
+        # selection inside the decode launch: the same selection as page_topk
+        # and the same output
+        ref_idx, ref_cnt, ref_blk = d.sel_idx.clone(), d.sel_cnt.clone(), d.sel_blk.clone()
+        o_ref, l_ref = d.out.clone(), d.lse.clone()
+        d.keep_selection = True
+        d.sel_idx.fill_(-7); d.sel_cnt.fill_(-7); d.sel_blk.fill_(-7)
+        d.out.fill_(float("nan")); d.lse.fill_(float("nan"))
+        d.select_attend(q, cache, bt, sl)
+        torch.cuda.synchronize()
+        assert torch.equal(d.sel_idx, ref_idx) and torch.equal(d.sel_cnt, ref_cnt)
+        assert torch.equal(d.sel_blk, ref_blk)
+        assert torch.allclose(o_ref, d.out, rtol=0, atol=1e-5), "select+decode differs"
+        assert torch.allclose(l_ref, d.lse, rtol=0, atol=1e-5), "select+decode lse differs"
 
     cb = bits(cache)
     qd = q_cpu.double().numpy()

@@ -51,9 +51,10 @@ def page_level_parity(wl, cache, q_cpu, seq_lens_np, rows, d, partial_heads=4):
                                    wl.topk_pages, wl.topk_frac, wl.bos, wl.eos)
     per = per_head_rows(sel_rows, len(rows), wl.H_q, d.H_sel)
     hs = slice(0, partial_heads)
-    check_partials(d.o_part.cpu().numpy()[rows][:, hs], d.lse_part.cpu().numpy()[rows][:, hs],
-                   qd[:, hs], cb, bt, sl, [p[hs] for p in per], wl.G, wl.softmax_scale,
-                   d.k_cap)
+    if not d.select_in_decode:   # (selection + decode + merge in one launch: no partials)
+        check_partials(d.o_part.cpu().numpy()[rows][:, hs],
+                       d.lse_part.cpu().numpy()[rows][:, hs], qd[:, hs], cb, bt, sl,
+                       [p[hs] for p in per], wl.G, wl.softmax_scale, d.k_cap)
     worst = check_attention(d.out.cpu().numpy()[rows], d.lse.cpu().numpy()[rows], qd,
                             cb, bt, sl, per, wl.G, wl.softmax_scale)
     return worst, ex
@@ -66,6 +67,7 @@ def _static_workload(name, group_select=False):
     q_cpu = W.make_queries(wl)
     d = SparseDecoder.for_workload(wl, group_select=group_select)
     d.keep_partials = True
+    d.keep_selection = True     # the step may select inside the decode launch
     bt, sl = dev(wl.block_table), dev(wl.seq_lens)
     poison(d)
     d.rebuild_stats(cache, bt, sl)
