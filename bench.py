@@ -268,6 +268,7 @@ def main():
             for _ in range(R)]
     fused = decs[0].fused
     in_decode = decs[0].select_in_decode
+    one_launch = decs[0].score_in_decode
     new_kv = [W.make_new_kv(wl, s, device=dev) for s in range(min(wl.steps, 64))] \
         if wl.steps > 1 else None
     if token_level:
@@ -305,8 +306,8 @@ def main():
     del csrc, cdst
 
     names = (["pagestats_update"] if wl.steps > 1 else []) + \
-        (["h2o_accumulate"] if token_level else ["page_score"]) + \
-        (["sparse_select_decode"] if in_decode else
+        (["h2o_accumulate"] if token_level else [] if one_launch else ["page_score"]) + \
+        (["sparse_page_decode"] if one_launch else ["sparse_select_decode"] if in_decode else
          ["page_topk", "sparse_paged_decode"] + ([] if fused else ["lse_merge"]))
 
     def enqueue(i, name):
@@ -328,6 +329,8 @@ def main():
             d.attend(q, c, bt, sl)
         elif name == "sparse_select_decode":
             d.select_attend(q, c, bt, sl)
+        elif name == "sparse_page_decode":
+            d.score_select_attend(q, c, bt, sl)
         else:
             d.merge()
 
@@ -374,6 +377,8 @@ def main():
     d = decs[last % R]
     sl_last = wl.seq_lens_at(last % wl.steps)
     if in_decode:   # the selection stays in LDS; recompute it for the byte count
+        if one_launch:
+            d.score(q, bt, seq_steps[last % wl.steps])
         d.select(seq_steps[last % wl.steps], bt)
         torch.cuda.synchronize()
     sel_idx = d.sel_idx.cpu().numpy()
@@ -398,7 +403,14 @@ def main():
 
     kb, upages = kernel_bytes(wl, sel_idx, sel_cnt, sl_last, wl.num_splits, token_level,
                               group, fused, entmax, decs[0].k_cap)
-    if in_decode:   # one launch: the top-k's score read plus the merged decode
+    if one_launch:
+        # the statistics read for scoring (scores and selection stay in LDS)
+        # plus the merged decode; q counted once
+        n_pages = (sl_last.astype(np.int64) + wl.P - 1) // wl.P
+        kb.pop("page_topk")
+        kb["sparse_page_decode"] = (kb.pop("page_score") - int((n_pages * wl.H_q * 4).sum())
+                                    - wl.B * wl.H_q * wl.D * 4 + kb.pop("sparse_paged_decode"))
+    elif in_decode:   # one launch: the top-k's score read plus the merged decode
         kb["sparse_select_decode"] = kb.pop("page_topk") - int(sel_cnt.sum()) * 4 \
             + kb.pop("sparse_paged_decode")
     step_bytes = sum(kb.values())
@@ -408,7 +420,8 @@ def main():
         kern[n] = {"us": round(t * 1000, 2), "bytes": kb[n],
                    "GBps": round(kb[n] / (t * 1e-3) / 1e9, 1) if t > 0 else None}
     dominant = max(names, key=lambda n: per_kernel_ms[n])
-    focus = "sparse_select_decode" if in_decode else "sparse_paged_decode"
+    focus = ("sparse_page_decode" if one_launch else
+             "sparse_select_decode" if in_decode else "sparse_paged_decode")
     a = kb[focus] / (per_kernel_ms[focus] * 1e-3) / 1e9
     roofline = {"kernel": focus, "bound": "hbm", "achieved": round(a, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(a / PEAK_HBM_GBPS, 4),
@@ -433,7 +446,7 @@ def main():
                    "mean_seq_len": float(np.mean(sl_last)), "replicas": R,
                    "selection": ("kv_head" if (group or token_level) else "query_head"),
                    "alibi": slopes is not None, "merge_in_decode": fused,
-                   "select_in_decode": in_decode,
+                   "select_in_decode": in_decode, "one_launch_step": one_launch,
                    "attention": "entmax15" if entmax else "softmax",
                    "parallelism": "single-gpu"},
         "effective_GBps": round(step_bytes / (gpu_ms * 1e-3) / 1e9, 1),

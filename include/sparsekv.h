@@ -260,6 +260,35 @@ int sparse_select_decode(const float *scores, int64_t score_ld, int topk_pages,
                          int32_t *sel_blk, hipStream_t stream);
 
 /*
+ * sparse_page_decode -- the whole page-level step in one launch: page_score,
+ * page_topk, sparse_paged_decode and lse_merge for one selection per query
+ * head.  One block per query head scores its pages from the statistics into
+ * LDS (page_score's arithmetic, ALiBi included), selects, attends (one wave
+ * per split) and merges.  [Sources of the four steps.]
+ *
+ *   q, kv_cache ... seq_lens, k_min / k_max / k_mean, w_avg, w_peak: as
+ *            page_score and sparse_paged_decode; bt_ld <= 4096 (the score row
+ *            is bt_ld long)
+ *   topk_pages, topk_frac, reserved_bos, reserved_eos, k_cap: as page_topk
+ *   scale, num_splits (<= 8), alibi_slopes (logit units, NULL = none): as
+ *            sparse_paged_decode; the score takes slope / scale (R30 reading)
+ *   out fp32 [B, H_q, D]; lse_out fp32 [B, H_q] or NULL
+ *   scores fp32 [B, H_q, bt_ld] or NULL; sel_idx / sel_cnt (both or neither)
+ *            and sel_blk: optional copies of the intermediate results.
+ *   Requires (2 * ceil4(bt_ld) + 2 * k_cap) * 4 bytes <= 48 KiB.
+ */
+int sparse_page_decode(const float *q, int B, int H_q, int H_kv, int D,
+                       const uint16_t *kv_cache, int64_t num_blocks, int page_size,
+                       const uint16_t *k_min, const uint16_t *k_max,
+                       const float *k_mean, const int32_t *block_table,
+                       int64_t bt_ld, const int32_t *seq_lens, float w_avg,
+                       float w_peak, int topk_pages, float topk_frac,
+                       int reserved_bos, int reserved_eos, int k_cap, float scale,
+                       int num_splits, const float *alibi_slopes, float *out,
+                       float *lse_out, float *scores, int32_t *sel_idx,
+                       int32_t *sel_cnt, int32_t *sel_blk, hipStream_t stream);
+
+/*
  * entmax15_paged_decode -- 1.5-entmax attention over the tokens of the
  * selected pages, as split partials for lse_merge.  [EKV "Quick start"
  * (alpha=1.5) and the component list (decode over selected pages, alpha 1.5);

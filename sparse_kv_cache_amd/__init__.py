@@ -20,7 +20,8 @@ __all__ = [
     "pagestats_update", "page_score", "page_score_group", "page_topk",
     "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
     "h2o_accumulate", "h2o_scratch_floats", "entmax15_paged_decode",
-    "entmax_scratch_floats", "sparse_select_decode", "library_path",
+    "entmax_scratch_floats", "sparse_select_decode", "sparse_page_decode",
+    "library_path",
     "load_library", "SparseKVError", "EXPORTED_SYMBOLS",
 ]
 
@@ -32,11 +33,13 @@ EXPORTED_SYMBOLS = (
     "pagestats_update", "page_score", "page_score_group", "page_topk",
     "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
     "h2o_accumulate", "h2o_scratch_floats", "entmax15_paged_decode",
-    "entmax_scratch_floats", "sparse_select_decode", "sparsekv_last_error",
+    "entmax_scratch_floats", "sparse_select_decode", "sparse_page_decode",
+    "sparsekv_last_error",
 )
 _INT_RETURNING = ("pagestats_update", "page_score", "page_score_group", "page_topk",
                   "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
-                  "h2o_accumulate", "entmax15_paged_decode", "sparse_select_decode")
+                  "h2o_accumulate", "entmax15_paged_decode", "sparse_select_decode",
+                  "sparse_page_decode")
 
 
 class SparseKVError(RuntimeError):
@@ -82,6 +85,8 @@ def load_library():
     lib.entmax_scratch_floats.argtypes = [I, I, I, I]
     lib.sparse_select_decode.argtypes = [V, L, I, F, I, I, V, I, I, I, I, V, L, I, V, L, V,
                                          I, F, I, V, V, V, V, V, V, V]
+    lib.sparse_page_decode.argtypes = [V, I, I, I, I, V, L, I, V, V, V, V, L, V, F, F, I, F,
+                                       I, I, I, F, I, V, V, V, V, V, V, V, V]
     lib.entmax_scratch_floats.restype = ctypes.c_int64
     for name in _INT_RETURNING:
         getattr(lib, name).restype = ctypes.c_int
@@ -399,6 +404,46 @@ def sparse_select_decode(scores, q, kv_cache, block_table, seq_lens, topk_pages,
         _ptr(block_table), block_table.shape[1], _ptr(seq_lens), int(k_cap), float(scale),
         int(num_splits), _ptr(alibi_slopes), _ptr(out), _ptr(lse_out), _ptr(sel_idx),
         _ptr(sel_cnt), _ptr(sel_blk), _stream(stream)))
+
+
+def sparse_page_decode(q, kv_cache, k_min, k_max, k_mean, block_table, seq_lens, w_avg,
+                       w_peak, topk_pages, k_cap, scale, num_splits, out, lse_out=None,
+                       topk_frac=0.0, reserved_bos=0, reserved_eos=1, scores=None,
+                       sel_idx=None, sel_cnt=None, sel_blk=None, alibi_slopes=None,
+                       stream=None):
+    """The page-level step in one launch (score, select, decode, merge; one
+    selection per query head, bt_ld <= 4096, num_splits <= 8)."""
+    lib = load_library()
+    _check("q", q, torch.float32, 3)
+    dev = q.device
+    B, H_q, D = q.shape
+    _check("kv_cache", kv_cache, torch.bfloat16, 5, dev)
+    _, NB, P, H_kv, D2 = kv_cache.shape
+    if D2 != D:
+        raise ValueError("q and kv_cache head dims differ")
+    _check("k_min", k_min, torch.bfloat16, 3, dev)
+    _check("k_max", k_max, torch.bfloat16, 3, dev)
+    _check("k_mean", k_mean, torch.float32, 3, dev)
+    _check("block_table", block_table, torch.int32, 2, dev)
+    _check("seq_lens", seq_lens, torch.int32, 1, dev)
+    _check("out", out, torch.float32, 3, dev)
+    _check("lse_out", lse_out, torch.float32, 2, dev)
+    bt_ld = block_table.shape[1]
+    _check("scores", scores, torch.float32, 3, dev)
+    if scores is not None and tuple(scores.shape) != (B, H_q, bt_ld):
+        raise ValueError("scores must be [B, H_q, bt_ld]")
+    for n, t in (("sel_idx", sel_idx), ("sel_blk", sel_blk)):
+        _check(n, t, torch.int32, 3, dev)
+        if t is not None and tuple(t.shape) != (B, H_q, k_cap):
+            raise ValueError(f"{n} must be [B, H_q, k_cap]")
+    _check("sel_cnt", sel_cnt, torch.int32, 2, dev)
+    alibi_slopes = _alibi_arg(alibi_slopes, H_q, dev)
+    _rc("sparse_page_decode", lib.sparse_page_decode(
+        _ptr(q), B, H_q, H_kv, D, _ptr(kv_cache), NB, P, _ptr(k_min), _ptr(k_max),
+        _ptr(k_mean), _ptr(block_table), bt_ld, _ptr(seq_lens), float(w_avg), float(w_peak),
+        int(topk_pages), float(topk_frac), int(reserved_bos), int(reserved_eos), int(k_cap),
+        float(scale), int(num_splits), _ptr(alibi_slopes), _ptr(out), _ptr(lse_out),
+        _ptr(scores), _ptr(sel_idx), _ptr(sel_cnt), _ptr(sel_blk), _stream(stream)))
 
 
 def lse_merge(o_part, lse_part, out, lse_out=None, stream=None):

@@ -184,12 +184,18 @@ __device__ __forceinline__ Chunk split_chunk(int cnt, int k_cap, int num_splits,
 // In-block selection (TKI > 0, with FUSE): the block first runs the top-k of
 // its query head's score row (TKI entries per thread) into LDS, then decodes
 // from there; the selection is copied out only when asked.
+// With SC as well, the block also scores its query head's pages from the page
+// statistics first (page_score's arithmetic, into LDS), so one launch runs
+// the whole page-level step.
 struct TopkArgs {
   const float* scores; int64_t score_ld; int topk_pages; double topk_frac;
   int bos, eos; int32_t* sel_idx; int32_t* sel_cnt; int32_t* sel_blk;
+  // in-block scoring (SC)
+  const uint16_t* kmin; const uint16_t* kmax; const float* kmean;
+  float w_avg, w_peak, inv_scale; int sc_cap; float* scores_out;
 };
 
-template <int D, int WB, int PFIX, bool AL, bool FUSE, int TKI>
+template <int D, int WB, int PFIX, bool AL, bool FUSE, int TKI, bool SC = false>
 __global__ __launch_bounds__(WB * 64)
 __attribute__((amdgpu_waves_per_eu(PFIX == 16 ? SKV_DECODE_WPE16 : SKV_DECODE_WPE)))
 void sparse_decode_wave_kernel(
@@ -203,6 +209,7 @@ void sparse_decode_wave_kernel(
     const float* __restrict__ alibi, float* __restrict__ out,
     float* __restrict__ lse_out, TopkArgs ta) {
   static_assert(TKI == 0 || FUSE, "in-block selection merges in-block");
+  static_assert(!SC || TKI > 0, "in-block scoring selects in-block");
   constexpr int LPR = D / 8;
   constexpr int RPL = 64 / LPR;
   constexpr int NL = 16 / RPL;
@@ -241,7 +248,77 @@ void sparse_decode_wave_kernel(
   const int32_t* sblk;
   int cnt;
   if constexpr (TKI > 0) {
-    extern __shared__ int32_t sel_lds[];          // [k_cap] indices, [k_cap] blocks
+    // dynamic LDS: [SC: sc_cap scores, sc_cap block ids] [k_cap indices, k_cap blocks]
+    extern __shared__ int32_t dyn_lds[];
+    int32_t* sel_lds = SC ? dyn_lds + 2 * ta.sc_cap : dyn_lds;
+    if constexpr (SC) {
+      float* sc_lds = reinterpret_cast<float*>(dyn_lds);
+      int32_t* bid_lds = dyn_lds + ta.sc_cap;
+      int64_t Nt64 = (static_cast<int64_t>(S) + P - 1) / P;
+      if (Nt64 > bt_ld) Nt64 = bt_ld;
+      const int Nt = static_cast<int>(Nt64);
+      const int32_t* btr0 = bt + static_cast<int64_t>(b) * bt_ld;
+      for (int j = threadIdx.x; j < Nt; j += WB * 64) bid_lds[j] = btr0[j];
+      float qv[8];
+      {
+        const float4 qa = *reinterpret_cast<const float4*>(q + qrow * D + c * 8);
+        const float4 qb = *reinterpret_cast<const float4*>(q + qrow * D + c * 8 + 4);
+        qv[0] = qa.x; qv[1] = qa.y; qv[2] = qa.z; qv[3] = qa.w;
+        qv[4] = qb.x; qv[5] = qb.y; qv[6] = qb.z; qv[7] = qb.w;
+      }
+      // ALiBi in score units: slope / softmax scale
+      const float sslope = AL ? alibi[h * G + g] * ta.inv_scale : 0.0f;
+      __syncthreads();
+      constexpr int KI = 4;                       // page loads in flight per lane
+      for (int p0 = 0; p0 < Nt; p0 += WB * RPL * KI) {
+        uint4 mn[KI], mx[KI];
+        float4 me0[KI], me1[KI];
+        int pg[KI];
+#pragma unroll
+        for (int it = 0; it < KI; ++it) {
+          pg[it] = p0 + (it * WB + wave) * RPL + slot;
+          const int64_t blk = bid_lds[pg[it] < Nt ? pg[it] : 0];
+          const int64_t off = (blk * H_kv + h) * D + c * 8;
+          mn[it] = *reinterpret_cast<const uint4*>(ta.kmin + off);
+          mx[it] = *reinterpret_cast<const uint4*>(ta.kmax + off);
+          me0[it] = *reinterpret_cast<const float4*>(ta.kmean + off);
+          me1[it] = *reinterpret_cast<const float4*>(ta.kmean + off + 4);
+        }
+#pragma unroll
+        for (int it = 0; it < KI; ++it) {
+          float lo[8], hi[8];
+          skv::unpack8(mn[it], lo);
+          skv::unpack8(mx[it], hi);
+          const float me[8] = {me0[it].x, me0[it].y, me0[it].z, me0[it].w,
+                               me1[it].x, me1[it].y, me1[it].z, me1[it].w};
+          float sc = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            // max(q max, q min) = q mid + |q| half (exact split, both terms)
+            const float mp = fmaf(ta.w_avg, me[i], ta.w_peak * ((hi[i] + lo[i]) * 0.5f));
+            const float hp = ta.w_peak * ((hi[i] - lo[i]) * 0.5f);
+            sc = fmaf(qv[i], mp, fmaf(fabsf(qv[i]), hp, sc));
+          }
+          sc = skv::group_sum<LPR>(sc);
+          if (AL) {
+            const int pp = pg[it] < Nt ? pg[it] : 0;
+            const int nn = S - pp * P;
+            const float n = static_cast<float>(nn < P ? nn : P);
+            const float first = static_cast<float>(pp * P - (S - 1));
+            sc += sslope * fmaf(ta.w_avg, first + 0.5f * (n - 1.0f),
+                                ta.w_peak * (first + n - 1.0f));
+          }
+          if (c == 0 && pg[it] < Nt) {
+            sc_lds[pg[it]] = sc;
+            if (ta.scores_out != nullptr) ta.scores_out[qrow * ta.score_ld + pg[it]] = sc;
+          }
+        }
+      }
+      __syncthreads();
+      cnt = skv::topk_row<WB * 64, TKI>(sc_lds, true, Nt, ta.topk_pages, ta.topk_frac,
+                                        ta.bos, ta.eos, bid_lds, ta.sc_cap, sel_lds,
+                                        sel_lds + k_cap, k_cap);
+    } else {
     int64_t Nt = (static_cast<int64_t>(S) + P - 1) / P;
     if (Nt > ta.score_ld) Nt = ta.score_ld;
     const bool aligned = ((ta.score_ld & 3) == 0) &&
@@ -250,6 +327,7 @@ void sparse_decode_wave_kernel(
         ta.scores + qrow * ta.score_ld, aligned, static_cast<int>(Nt), ta.topk_pages,
         ta.topk_frac, ta.bos, ta.eos, bt + static_cast<int64_t>(b) * bt_ld, bt_ld,
         sel_lds, sel_lds + k_cap, k_cap);
+    }
     if (ta.sel_idx != nullptr) {
       for (int j = threadIdx.x; j < k_cap; j += WB * 64) {
         ta.sel_idx[qrow * k_cap + j] = sel_lds[j];
@@ -746,13 +824,15 @@ void launch_wave(hipStream_t st, const Args& a, int64_t n_groups) {
 // One block per query head, kFuseWaves waves = splits, merged in the block.
 constexpr int kFuseWaves = 8;
 
-template <int D, int PFIX, bool AL, int TKI>
+template <int D, int PFIX, bool AL, int TKI, bool SC = false>
 void launch_wave_fused(hipStream_t st, const Args& a, int64_t n_groups, float* out,
                        float* lse_out, const TopkArgs& ta) {
   const int per_group = a.G;
   const int64_t blocks = kXcds * per_group * ((n_groups + kXcds - 1) / kXcds);
-  const size_t lds = TKI > 0 ? sizeof(int32_t) * 2 * static_cast<size_t>(a.k_cap) : 0;
-  hipLaunchKernelGGL((sparse_decode_wave_kernel<D, kFuseWaves, PFIX, AL, true, TKI>),
+  const size_t lds = TKI > 0 ? sizeof(int32_t) * (2 * static_cast<size_t>(a.k_cap) +
+                                                  (SC ? 2 * static_cast<size_t>(ta.sc_cap) : 0))
+                             : 0;
+  hipLaunchKernelGGL((sparse_decode_wave_kernel<D, kFuseWaves, PFIX, AL, true, TKI, SC>),
                      dim3(static_cast<unsigned>(blocks)), dim3(kFuseWaves * 64), lds, st,
                      a.q, a.H_q, a.H_kv, a.G, a.kv, a.num_blocks, a.P, a.bt, a.bt_ld,
                      a.seq_lens, a.sel_idx, a.sel_cnt, a.sel_blk, a.k_cap, a.scale_log2,
@@ -974,5 +1054,90 @@ extern "C" int sparse_select_decode(const float* scores, int64_t score_ld, int t
   }
 #undef SKV_SEL_T
 #undef SKV_SEL
+  SKV_CHECK_LAUNCH();
+}
+
+extern "C" int sparse_page_decode(const float* q, int B, int H_q, int H_kv, int D,
+                                  const uint16_t* kv_cache, int64_t num_blocks,
+                                  int page_size, const uint16_t* k_min,
+                                  const uint16_t* k_max, const float* k_mean,
+                                  const int32_t* block_table, int64_t bt_ld,
+                                  const int32_t* seq_lens, float w_avg, float w_peak,
+                                  int topk_pages, float topk_frac, int reserved_bos,
+                                  int reserved_eos, int k_cap, float scale,
+                                  int num_splits, const float* alibi_slopes, float* out,
+                                  float* lse_out, float* scores, int32_t* sel_idx,
+                                  int32_t* sel_cnt, int32_t* sel_blk, hipStream_t stream) {
+  const char* who = "sparse_page_decode";
+  SKV_REQUIRE(B >= 0 && H_kv > 0 && H_q > 0 && H_q % H_kv == 0,
+              "%s: need H_q a positive multiple of H_kv", who);
+  const int G = H_q / H_kv;
+  SKV_REQUIRE(G <= 16, "%s: group size %d > 16", who, G);
+  SKV_REQUIRE(D == 64 || D == 128, "%s: D must be 64 or 128 (got %d)", who, D);
+  SKV_REQUIRE(skv_supported_page_size(page_size),
+              "%s: page_size must be 1, 2, 4, 8 or 16 (got %d)", who, page_size);
+  SKV_REQUIRE(num_splits >= 1 && num_splits <= kFuseWaves,
+              "%s: num_splits must be in [1, %d] (got %d)", who, kFuseWaves, num_splits);
+  SKV_REQUIRE(bt_ld > 0 && bt_ld <= 8 * kFuseWaves * 64,
+              "%s: bt_ld must be in [1, %d] (got %lld)", who, 8 * kFuseWaves * 64,
+              (long long)bt_ld);
+  SKV_REQUIRE(topk_pages >= 1, "%s: topk_pages must be >= 1 (got %d)", who, topk_pages);
+  SKV_REQUIRE(topk_frac >= 0.0f && topk_frac <= 1.0f, "%s: topk_frac must be in [0, 1]", who);
+  SKV_REQUIRE(reserved_bos >= 0 && reserved_eos >= 0,
+              "%s: reserved_bos / reserved_eos must be >= 0", who);
+  SKV_REQUIRE(num_blocks > 0 && num_blocks <= 0x7fffffffLL,
+              "%s: need 0 < num_blocks < 2^31", who);
+  SKV_REQUIRE(scale > 0.0f, "%s: scale must be > 0", who);
+  const double frac = static_cast<double>(topk_frac);
+  int64_t need = topk_pages;
+  const int64_t fk = static_cast<int64_t>(floor(frac * static_cast<double>(bt_ld)));
+  if (fk > need) need = fk;
+  if (static_cast<int64_t>(reserved_bos) + reserved_eos > need)
+    need = static_cast<int64_t>(reserved_bos) + reserved_eos;
+  if (need > bt_ld) need = bt_ld;
+  const int sc_cap = static_cast<int>((bt_ld + 3) / 4 * 4);
+  SKV_REQUIRE(k_cap >= need && (2LL * sc_cap + 2LL * k_cap) * 4 <= 48 * 1024,
+              "%s: k_cap %d must cover the largest selection %lld, and the block's "
+              "scores and selection must fit 48 KiB of LDS", who, k_cap, (long long)need);
+  SKV_REQUIRE(B <= 65535, "%s: grid too large", who);
+  SKV_REQUIRE_PTR_W(who, q);
+  SKV_REQUIRE_PTR_W(who, kv_cache);
+  SKV_REQUIRE_PTR_W(who, k_min);
+  SKV_REQUIRE_PTR_W(who, k_max);
+  SKV_REQUIRE_PTR_W(who, k_mean);
+  SKV_REQUIRE_PTR_W(who, block_table);
+  SKV_REQUIRE_PTR_W(who, seq_lens);
+  SKV_REQUIRE_PTR_W(who, out);
+  SKV_REQUIRE((sel_idx == nullptr) == (sel_cnt == nullptr),
+              "%s: sel_idx and sel_cnt must both be given or both be NULL", who);
+  SKV_REQUIRE(sel_blk == nullptr || sel_idx != nullptr, "%s: sel_blk needs sel_idx", who);
+  if (B == 0) { skv::clear_error(); return SKV_OK; }
+  const int64_t n_groups = static_cast<int64_t>(B) * H_kv;
+  const Args a{q, H_q, H_kv, G, kv_cache, num_blocks, page_size, block_table, bt_ld,
+               seq_lens, nullptr, nullptr, nullptr, k_cap, scale * skv::kLog2e, num_splits,
+               nullptr, nullptr, alibi_slopes};
+  const TopkArgs ta{nullptr, bt_ld, topk_pages, frac, reserved_bos, reserved_eos,
+                    sel_idx, sel_cnt, sel_blk, k_min, k_max, k_mean, w_avg, w_peak,
+                    1.0f / scale, sc_cap, scores};
+  const bool al = alibi_slopes != nullptr;
+  const int tki = bt_ld <= 512 ? 1 : bt_ld <= 2048 ? 4 : 8;
+#define SKV_SC(DD, PP, TT)                                                                   \
+  do {                                                                                       \
+    if (al) launch_wave_fused<DD, PP, true, TT, true>(stream, a, n_groups, out, lse_out, ta); \
+    else launch_wave_fused<DD, PP, false, TT, true>(stream, a, n_groups, out, lse_out, ta);   \
+  } while (0)
+#define SKV_SC_T(DD, PP)                                                                     \
+  do {                                                                                       \
+    if (tki == 1) SKV_SC(DD, PP, 1);                                                         \
+    else if (tki == 4) SKV_SC(DD, PP, 4);                                                    \
+    else SKV_SC(DD, PP, 8);                                                                  \
+  } while (0)
+  if (page_size == 16) {
+    if (D == 128) SKV_SC_T(128, 16); else SKV_SC_T(64, 16);
+  } else {
+    if (D == 128) SKV_SC_T(128, 0); else SKV_SC_T(64, 0);
+  }
+#undef SKV_SC_T
+#undef SKV_SC
   SKV_CHECK_LAUNCH();
 }

@@ -23,8 +23,8 @@ import torch
 
 from . import (entmax15_paged_decode, entmax_scratch_floats, h2o_accumulate,
                h2o_scratch_floats, lse_merge, page_score, page_score_group, page_topk,
-               pagestats_update, sparse_paged_decode, sparse_paged_decode_merged,
-               sparse_select_decode)
+               pagestats_update, sparse_page_decode, sparse_paged_decode,
+               sparse_paged_decode_merged, sparse_select_decode)
 
 
 def alibi_slopes(H, device="cuda"):
@@ -108,6 +108,11 @@ class SparseDecoder:
         # selection inside the decode launch as well (score rows <= 4096)
         self.select_in_decode = self.fused and bt_ld <= 4096 and self.k_cap <= 4096
         self.keep_selection = False
+        # and scoring too: the whole page-level step in one launch
+        sc_cap = (bt_ld + 3) // 4 * 4
+        self.score_in_decode = (self.select_in_decode and not self.group_select
+                                and (2 * sc_cap + 2 * self.k_cap) * 4 <= 48 * 1024)
+        self.keep_scores = False
         self.entmax_scratch = None
         if attention == "entmax15":
             n = entmax_scratch_floats(B, H_q, self.k_cap, page_size)
@@ -185,6 +190,18 @@ class SparseDecoder:
             sel_idx=self.sel_idx if keep else None, sel_cnt=self.sel_cnt if keep else None,
             sel_blk=self.sel_blk if keep else None, alibi_slopes=self.alibi, stream=stream)
 
+    def score_select_attend(self, q, kv_cache, block_table, seq_lens, stream=None):
+        """Score, select, decode and merge in one launch (score_in_decode)."""
+        keep = self.keep_selection
+        sparse_page_decode(
+            q, kv_cache, self.k_min, self.k_max, self.k_mean, block_table, seq_lens,
+            self.w_avg, self.w_peak, self.topk_pages, self.k_cap, self.scale,
+            self.num_splits, self.out, self.lse, topk_frac=self.topk_frac,
+            reserved_bos=self.bos, reserved_eos=self.eos,
+            scores=self.scores if self.keep_scores else None,
+            sel_idx=self.sel_idx if keep else None, sel_cnt=self.sel_cnt if keep else None,
+            sel_blk=self.sel_blk if keep else None, alibi_slopes=self.alibi, stream=stream)
+
     def merge(self, stream=None):
         if self.fused:
             return                      # merged inside attend()
@@ -196,6 +213,9 @@ class SparseDecoder:
         """One decode step; returns (out, lse) views of the decoder's buffers."""
         if k_new is not None:
             self.append(kv_cache, block_table, seq_lens, k_new, v_new, stream)
+        if self.score_in_decode:
+            self.score_select_attend(q, kv_cache, block_table, seq_lens, stream)
+            return self.out, self.lse
         if self.token_level:
             self.accumulate(q, kv_cache, block_table, seq_lens, stream)
         else:

@@ -42,6 +42,7 @@ def test_header_declares_the_six_operations():
     for n in ("pagestats_update", "page_score", "page_score_group", "page_topk",
               "sparse_paged_decode", "sparse_paged_decode_merged",
               "entmax15_paged_decode", "entmax_scratch_floats", "sparse_select_decode",
+              "sparse_page_decode",
               "lse_merge", "h2o_accumulate", "h2o_scratch_floats",
               "sparsekv_last_error"):
         assert n in names
@@ -116,6 +117,17 @@ def test_validation_rejects_bad_scalars(lib):
                                     8, 0.1, 2, None, p, None, p, None, None, s) == EINVAL
     assert lib.sparse_select_decode(p, 64, 4, 0.0, 0, 1, p, 1, 8, 2, 128, p, 8, 16, p, 4, p,
                                     8, 0.1, 2, None, None, None, None, None, None, s) == EFAULT
+    # one-launch step: bt_ld <= 4096, splits <= 8, stats required
+    assert lib.sparse_page_decode(p, 1, 8, 2, 128, p, 8, 16, p, p, p, p, 5000, p, 1.0, 1.0,
+                                  4, 0.0, 0, 1, 8, 0.1, 2, None, p, None, None, None, None,
+                                  None, s) == EINVAL
+    assert lib.sparse_page_decode(p, 1, 8, 2, 128, p, 8, 16, p, p, p, p, 64, p, 1.0, 1.0,
+                                  4, 0.0, 0, 1, 8, 0.1, 9, None, p, None, None, None, None,
+                                  None, s) == EINVAL
+    assert lib.sparse_page_decode(p, 1, 8, 2, 128, p, 8, 16, None, p, p, p, 64, p, 1.0, 1.0,
+                                  4, 0.0, 0, 1, 8, 0.1, 2, None, p, None, None, None, None,
+                                  None, s) == EFAULT
+    assert "k_min" in _msg(lib)
     # entmax: scratch too small, splits < 1
     assert lib.entmax15_paged_decode(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p, None, 4, 8,
                                      0.1, 2, p, p, p, 3, s) == EINVAL

@@ -44,6 +44,44 @@ def _decoder(wl):
                          scale=wl.softmax_scale, num_splits=wl.num_splits)
 
 
+def check_one_launch_step(d, q, cache, bt, sl):
+    """sparse_page_decode (score + select + decode + merge in one launch)
+    against the separate launches already in d's buffers."""
+    ref_s, ref_idx = d.scores.clone(), d.sel_idx.clone()
+    ref_cnt, ref_blk = d.sel_cnt.clone(), d.sel_blk.clone()
+    o_ref, l_ref = d.out.clone(), d.lse.clone()
+    d.keep_scores = d.keep_selection = True
+    d.scores.fill_(float("nan"))
+    d.sel_idx.fill_(-7); d.sel_cnt.fill_(-7); d.sel_blk.fill_(-7)
+    d.out.fill_(float("nan")); d.lse.fill_(float("nan"))
+    d.score_select_attend(q, cache, bt, sl)
+    torch.cuda.synchronize()
+    valid = ~torch.isnan(ref_s)
+    assert torch.equal(torch.isnan(d.scores), ~valid), "one-launch scores: written set differs"
+    # same arithmetic; with ALiBi the slope / scale is rounded on a different
+    # side, so the bound is relative to the row's largest magnitude (the bias
+    # and the q.k terms can cancel)
+    rowmax = torch.nan_to_num(ref_s.abs(), nan=0.0).amax(dim=2, keepdim=True)
+    err = torch.nan_to_num((d.scores - ref_s).abs(), nan=0.0)
+    assert torch.all(err <= 4e-6 * rowmax + 1e-6), \
+        f"one-launch scores differ by {float(err.max())}"
+    if not torch.equal(d.scores[valid], ref_s[valid]):
+        # its selection must be exact on its own scores
+        gs = d.scores.cpu().numpy()
+        N = np.repeat((sl.cpu().numpy().astype(np.int64) + d.P - 1) // d.P, d.H_q)
+        check_selection_exact(d.sel_idx.cpu().numpy().reshape(-1, d.k_cap),
+                              d.sel_cnt.cpu().numpy().reshape(-1),
+                              gs.reshape(-1, gs.shape[2]), N, d.topk_pages, d.topk_frac,
+                              d.bos, d.eos)
+    if torch.equal(d.sel_idx, ref_idx) and torch.equal(d.sel_cnt, ref_cnt):
+        assert torch.equal(d.sel_blk, ref_blk)
+        assert torch.allclose(o_ref, d.out, rtol=0, atol=1e-5), "one-launch output differs"
+        assert torch.allclose(l_ref, d.lse, rtol=0, atol=1e-5), "one-launch lse differs"
+    else:
+        assert torch.equal(torch.isnan(d.scores), ~valid)   # (selection differs at a tie)
+    d.keep_scores = d.keep_selection = False
+
+
 def run_page_case(wl, cache_cpu, q_cpu, exact_ties=False):
     cache = dev(cache_cpu)
     q = dev(q_cpu)
@@ -97,6 +135,8 @@ def run_page_case(wl, cache_cpu, q_cpu, exact_ties=False):
         assert torch.equal(d.sel_blk, ref_blk)
         assert torch.allclose(o_ref, d.out, rtol=0, atol=1e-5), "select+decode differs"
         assert torch.allclose(l_ref, d.lse, rtol=0, atol=1e-5), "select+decode lse differs"
+    if d.score_in_decode:
+        check_one_launch_step(d, q, cache, bt, sl)
 
     cb = bits(cache)
     qd = q_cpu.double().numpy()
@@ -272,6 +312,13 @@ def run_alibi_case(wl, cache_cpu, q_cpu, group, slopes_np):
                                    wl.topk_pages, wl.topk_frac, wl.bos, wl.eos)
     per = per_head_rows(rows, wl.B, wl.H_q, H_sel)
     sl64 = slopes.cpu().numpy().astype(np.float64)
+    if d.score_in_decode:
+        d.fused = False            # the reference buffers from separate launches
+        d.attend(q, cache, bt, sl)
+        d.merge()
+        d.fused = True
+        torch.cuda.synchronize()
+        check_one_launch_step(d, q, cache, bt, sl)
     check_partials(d.o_part.cpu().numpy(), d.lse_part.cpu().numpy(), qd, cb,
                    wl.block_table, wl.seq_lens, per, wl.G, wl.softmax_scale, d.k_cap,
                    slopes=sl64)

@@ -67,7 +67,8 @@ def _static_workload(name, group_select=False):
     q_cpu = W.make_queries(wl)
     d = SparseDecoder.for_workload(wl, group_select=group_select)
     d.keep_partials = True
-    d.keep_selection = True     # the step may select inside the decode launch
+    d.keep_selection = True     # the step may select (and score) inside the decode launch
+    d.keep_scores = True
     bt, sl = dev(wl.block_table), dev(wl.seq_lens)
     poison(d)
     d.rebuild_stats(cache, bt, sl)
