@@ -42,6 +42,9 @@
 namespace {
 
 constexpr int kMaxEnt = 256;          // LDS entries per round (group kernel)
+#ifndef SKV_SCORE_KI
+#define SKV_SCORE_KI 2                // pages in flight per lane, in-block scoring
+#endif
 constexpr int kXcds = 8;              // accelerator complex dies of an MI355X
 #ifndef SKV_DECODE_WPE
 #define SKV_DECODE_WPE 3              // waves per SIMD the wave kernel is sized for
@@ -269,7 +272,7 @@ void sparse_decode_wave_kernel(
       // ALiBi in score units: slope / softmax scale
       const float sslope = AL ? alibi[h * G + g] * ta.inv_scale : 0.0f;
       __syncthreads();
-      constexpr int KI = 4;                       // page loads in flight per lane
+      constexpr int KI = SKV_SCORE_KI;            // page loads in flight per lane
       for (int p0 = 0; p0 < Nt; p0 += WB * RPL * KI) {
         uint4 mn[KI], mx[KI];
         float4 me0[KI], me1[KI];
