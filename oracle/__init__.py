@@ -63,10 +63,19 @@ def _load():
     lib.oracle_attend_alibi.argtypes = [P, i32, P, i64, i32, i32, i32, P, i32, P, i32,
                                         f64, f64, P, P]
     lib.oracle_lse_merge.argtypes = [P, P, i32, i32, P, P]
+    lib.oracle_page_var.argtypes = [P, i64, i32, i32, i32, P, i64, P, i32, P]
+    lib.oracle_gauss_moments.argtypes = [P, i32, i32, i32, i32, P, P, P, i64, P, i32, f64,
+                                         P, P, P, i64]
+    lib.oracle_gauss_tau.argtypes = [P, P, P, i32, i32]
+    lib.oracle_gauss_tau.restype = f64
+    lib.oracle_gauss_select.argtypes = [P, P, P, i32, f64, i32, i32, i32, P]
+    lib.oracle_gauss_select.restype = i32
     lib.oracle_entmax15_tau.argtypes = [P, i32]
     lib.oracle_entmax15_tau.restype = f64
     lib.oracle_attend_entmax15.argtypes = [P, i32, P, i64, i32, i32, i32, P, i32, P, i32,
                                            f64, P, P]
+    lib.oracle_attend_entmax15_alibi.argtypes = [P, i32, P, i64, i32, i32, i32, P, i32, P,
+                                                 i32, f64, f64, P, P]
     lib.oracle_append.argtypes = [P, i64, i32, i32, i32, P, i64, P, i32, P, P, P]
     lib.oracle_h2o_recurrence.argtypes = [P, P, i32, f64]
     lib.oracle_h2o_step.argtypes = [P, i32, i32, i32, i32, P, i64, P, i64, P,
@@ -243,9 +252,10 @@ def entmax15_tau(z):
     return float(_load().oracle_entmax15_tau(_ptr(zz), zz.shape[0]))
 
 
-def attend_entmax15(q_row, kv_cache, kv_head, bt_row, seq_len, pages, scale):
+def attend_entmax15(q_row, kv_cache, kv_head, bt_row, seq_len, pages, scale, slope=None):
     """(o [D], tau) of 1.5-entmax attention of one query row over the tokens
-    of the given pages."""
+    of the given pages; slope (logit units) adds the ALiBi bias
+    slope * (pos - (S - 1))."""
     lib = _load()
     qd = _c(q_row, np.float64)
     kv = _c(kv_cache, np.uint16)
@@ -254,10 +264,69 @@ def attend_entmax15(q_row, kv_cache, kv_head, bt_row, seq_len, pages, scale):
     pg = _c(pages, np.int32)
     o = np.zeros(D)
     tau = np.zeros(1)
-    lib.oracle_attend_entmax15(_ptr(qd), D, _ptr(kv), NB, P, H_kv, int(kv_head),
-                               _ptr(bt), int(seq_len), _ptr(pg), pg.shape[0],
-                               float(scale), _ptr(o), _ptr(tau))
+    if slope is None:
+        lib.oracle_attend_entmax15(_ptr(qd), D, _ptr(kv), NB, P, H_kv, int(kv_head),
+                                   _ptr(bt), int(seq_len), _ptr(pg), pg.shape[0],
+                                   float(scale), _ptr(o), _ptr(tau))
+    else:
+        lib.oracle_attend_entmax15_alibi(_ptr(qd), D, _ptr(kv), NB, P, H_kv, int(kv_head),
+                                         _ptr(bt), int(seq_len), _ptr(pg), pg.shape[0],
+                                         float(scale), float(slope), _ptr(o), _ptr(tau))
     return o, float(tau[0])
+
+
+def page_var(kv_cache, block_table, seq_lens, page_size):
+    """Population variance per (block, kv head, d) over each page's valid rows
+    (float64 [num_blocks, H_kv, D]; unused blocks stay NaN)."""
+    lib = _load()
+    kv = _c(kv_cache, np.uint16)
+    _, NB, P, H_kv, D = kv.shape
+    bt = _c(block_table, np.int32)
+    sl = _c(seq_lens, np.int32)
+    out = np.full((NB, H_kv, D), np.nan)
+    lib.oracle_page_var(_ptr(kv), NB, P, H_kv, D, _ptr(bt), bt.shape[1], _ptr(sl),
+                        sl.shape[0], _ptr(out))
+    return out
+
+
+def gauss_moments(q, kmean, kvar, block_table, seq_lens, page_size, scale, alibi=None,
+                  ld=None):
+    """(mu, var) [B, H_q, ld] of each page's logits z = scale q.k."""
+    lib = _load()
+    qd = _c(q, np.float64)
+    B, H_q, D = qd.shape
+    me, va = _c(kmean, np.float64), _c(kvar, np.float64)
+    H_kv = me.shape[1]
+    bt = _c(block_table, np.int32)
+    sl = _c(seq_lens, np.int32)
+    if ld is None:
+        ld = bt.shape[1]
+    mu = np.full((B, H_q, ld), np.nan)
+    var = np.full((B, H_q, ld), np.nan)
+    al = None if alibi is None else _c(alibi, np.float64)
+    lib.oracle_gauss_moments(_ptr(qd), B, H_q, H_kv, D, _ptr(me), _ptr(va), _ptr(bt),
+                             bt.shape[1], _ptr(sl), page_size, float(scale),
+                             None if al is None else _ptr(al), _ptr(mu), _ptr(var), ld)
+    return mu, var
+
+
+def gauss_tau(mu, var, n, mixture):
+    """tau-hat of one row from its pages' (mu, var) and valid-row counts n."""
+    m, v = _c(mu, np.float64), _c(var, np.float64)
+    nn = _c(n, np.int32)
+    return float(_load().oracle_gauss_tau(_ptr(m), _ptr(v), _ptr(nn), m.shape[0],
+                                          int(bool(mixture))))
+
+
+def gauss_select(mu, var, n, tau, bos, eos, k_cap):
+    """Ascending pages of one row selected against tau-hat."""
+    m, v = _c(mu, np.float64), _c(var, np.float64)
+    nn = _c(n, np.int32)
+    N = m.shape[0]
+    out = np.full(max(N, 1), -1, dtype=np.int32)
+    c = _load().oracle_gauss_select(_ptr(m), _ptr(v), _ptr(nn), N, float(tau), int(bos),
+                                    int(eos), int(k_cap), _ptr(out))
+    return out[:c].copy()
 
 
 def lse_merge(o_parts, lses):

@@ -484,10 +484,11 @@ double oracle_entmax15_tau(const double *z, int n)
 /* 1.5-entmax attention of one query row over the tokens of the selected
  * pages: z_t = scale * q.k_t, p = entmax15(z), o = sum_t p_t v_t.  Writes o
  * [D] and tau; an empty selection gives o = 0 and tau = -inf. */
-void oracle_attend_entmax15(const double *q, int D, const uint16_t *kv_cache,
-                            int64_t num_blocks, int P, int H_kv, int kv_head,
-                            const int32_t *bt_row, int S, const int32_t *pages,
-                            int npages, double scale, double *o, double *tau)
+void oracle_attend_entmax15_alibi(const double *q, int D, const uint16_t *kv_cache,
+                                  int64_t num_blocks, int P, int H_kv, int kv_head,
+                                  const int32_t *bt_row, int S, const int32_t *pages,
+                                  int npages, double scale, double slope, double *o,
+                                  double *tau)
 {
     int ntok = 0;
     for (int j = 0; j < npages; ++j) {
@@ -513,7 +514,8 @@ void oracle_attend_entmax15(const double *q, int D, const uint16_t *kv_cache,
             for (int d = 0; d < D; ++d)
                 dot += q[d] * oracle_bf16_to_double(kv_cache[cache_index(
                            0, blk[t], r, kv_head, d, num_blocks, P, H_kv, D)]);
-            z[t] = scale * dot;
+            /* ALiBi bias of a key at position pos: slope * (pos - (S - 1)) */
+            z[t] = scale * dot + slope * ((double)pages[j] * P + r - (double)(S - 1));
         }
     }
     double tu = oracle_entmax15_tau(z, ntok);
@@ -530,6 +532,178 @@ void oracle_attend_entmax15(const double *q, int D, const uint16_t *kv_cache,
     free(z);
     free(blk);
     free(row);
+}
+
+void oracle_attend_entmax15(const double *q, int D, const uint16_t *kv_cache,
+                            int64_t num_blocks, int P, int H_kv, int kv_head,
+                            const int32_t *bt_row, int S, const int32_t *pages,
+                            int npages, double scale, double *o, double *tau)
+{
+    oracle_attend_entmax15_alibi(q, D, kv_cache, num_blocks, P, H_kv, kv_head, bt_row,
+                                 S, pages, npages, scale, 0.0, o, tau);
+}
+
+/* ------------------------------------- Gaussian-aware selection (NEXT row) */
+
+/* EntmaxKV README "How it works": for the Gaussian-aware strategy pages keep
+ * mean and std key statistics, each page's scores are modelled as a Gaussian,
+ * the distributional entmax constraint gives a threshold tau-hat (a page
+ * mixture for ALiBi heads, a single Gaussian otherwise), and every page whose
+ * estimated maximum can cross tau-hat is selected, so the page count adapts.
+ * The pages give no formulas; the plain readings taken here:
+ *   page statistic  population variance per dim over the page's valid rows;
+ *   page moments    z = scale q.k (+ the ALiBi bias): mu_p = scale q.mean_p
+ *                   (+ the bias at the page's mean position), var_p =
+ *                   scale^2 sum_d q_d^2 var_pd (+ slope^2 (n_p^2 - 1) / 12,
+ *                   the variance of the bias over n_p consecutive positions):
+ *                   key dimensions and position taken as independent;
+ *   constraint      with u = z / 2 (alpha = 1.5), sum over the request's
+ *                   tokens of E[(u - tau)_+^2] = 1: each page contributes
+ *                   n_p E[(X - tau)_+^2], X ~ N(mu_p / 2, var_p / 4)
+ *                   (mixture), or all S tokens share N(mu, var) with the
+ *                   pooled mean and variance (single);
+ *   estimated max   mu_p + sqrt(var_p) sqrt(2 ln n_p) (the usual estimate of
+ *                   the largest of n_p Gaussian draws);
+ *   selection       reserved pages, plus every other page with est_max / 2 >
+ *                   tau-hat; above k_cap entries the largest estimates win,
+ *                   ties to the lower index.  The qualifying pages are the
+ *                   ones of largest estimate, so this is the top-k selection
+ *                   over the estimates with the budget (reserved + qualifying,
+ *                   at most k_cap, at least one page). */
+
+void oracle_page_var(const uint16_t *kv_cache, int64_t num_blocks, int P, int H_kv,
+                     int D, const int32_t *block_table, int64_t bt_ld,
+                     const int32_t *seq_lens, int B, double *kvar)
+{
+    for (int b = 0; b < B; ++b) {
+        int S = seq_lens[b];
+        int N = pages_of(S, P);
+        for (int p = 0; p < N; ++p) {
+            int64_t blk = block_table[(int64_t)b * bt_ld + p];
+            int n = S - p * P < P ? S - p * P : P;
+            for (int h = 0; h < H_kv; ++h)
+                for (int d = 0; d < D; ++d) {
+                    double mean = 0.0, ss = 0.0;
+                    for (int t = 0; t < n; ++t)
+                        mean += oracle_bf16_to_double(kv_cache[cache_index(
+                            0, blk, t, h, d, num_blocks, P, H_kv, D)]);
+                    mean /= n;
+                    for (int t = 0; t < n; ++t) {
+                        double k = oracle_bf16_to_double(kv_cache[cache_index(
+                            0, blk, t, h, d, num_blocks, P, H_kv, D)]);
+                        ss += (k - mean) * (k - mean);
+                    }
+                    kvar[(blk * H_kv + h) * D + d] = ss / n;
+                }
+        }
+    }
+}
+
+/* mu, var [B, H_q, ld] for p < N_b.  alibi [H_q] (logit units) or NULL. */
+void oracle_gauss_moments(const double *q, int B, int H_q, int H_kv, int D,
+                          const double *kmean, const double *kvar,
+                          const int32_t *block_table, int64_t bt_ld,
+                          const int32_t *seq_lens, int P, double scale,
+                          const double *alibi, double *mu, double *var, int64_t ld)
+{
+    int G = H_q / H_kv;
+    for (int b = 0; b < B; ++b) {
+        int S = seq_lens[b];
+        int N = pages_of(S, P);
+        for (int i = 0; i < H_q; ++i) {
+            const double *qi = q + ((int64_t)b * H_q + i) * D;
+            for (int p = 0; p < N; ++p) {
+                int64_t blk = block_table[(int64_t)b * bt_ld + p];
+                const double *me = kmean + (blk * H_kv + i / G) * D;
+                const double *va = kvar + (blk * H_kv + i / G) * D;
+                double m = 0.0, v = 0.0;
+                for (int d = 0; d < D; ++d) {
+                    m += qi[d] * me[d];
+                    v += qi[d] * qi[d] * va[d];
+                }
+                m *= scale;
+                v *= scale * scale;
+                if (alibi != NULL) {
+                    int n = S - p * P < P ? S - p * P : P;
+                    m += alibi[i] * ((double)p * P + 0.5 * (n - 1) - (double)(S - 1));
+                    v += alibi[i] * alibi[i] * ((double)n * n - 1.0) / 12.0;
+                }
+                mu[((int64_t)b * H_q + i) * ld + p] = m;
+                var[((int64_t)b * H_q + i) * ld + p] = v;
+            }
+        }
+    }
+}
+
+/* E[(X - tau)_+^2] for X ~ N(m, s^2). */
+static double gauss_excess2(double m, double s, double tau)
+{
+    double d = m - tau;
+    if (s <= 0.0)
+        return d > 0.0 ? d * d : 0.0;
+    double a = d / s;
+    double Phi = 0.5 * erfc(-a / sqrt(2.0));
+    double phi = exp(-0.5 * a * a) / 2.5066282746310002;   /* sqrt(2 pi) */
+    return (d * d + s * s) * Phi + d * s * phi;
+}
+
+/* tau-hat of one row: mu, var, n over N pages; mixture != 0 sums the page
+ * Gaussians, else the pooled single Gaussian.  Bisection on [max m - 2,
+ * max (m + 12 s)] where the constraint is >= 2 and ~0 respectively. */
+double oracle_gauss_tau(const double *mu, const double *var, const int *n, int N,
+                        int mixture)
+{
+    double S = 0.0, sm = 0.0, sq = 0.0;
+    for (int p = 0; p < N; ++p) {
+        S += n[p];
+        sm += n[p] * mu[p];
+        sq += n[p] * (var[p] + mu[p] * mu[p]);
+    }
+    double gm = sm / S, gv = sq / S - gm * gm;
+    if (gv < 0.0) gv = 0.0;
+    double mmax = -INFINITY, hi = -INFINITY;
+    for (int p = 0; p < N; ++p) {
+        double m = mixture ? mu[p] / 2.0 : gm / 2.0;
+        double s = sqrt(mixture ? var[p] : gv) / 2.0;
+        if (m > mmax) mmax = m;
+        if (m + 12.0 * s > hi) hi = m + 12.0 * s;
+    }
+    double lo = mmax - 2.0;
+    for (int it = 0; it < 200; ++it) {
+        double mid = 0.5 * (lo + hi), f = 0.0;
+        if (mixture) {
+            for (int p = 0; p < N; ++p)
+                f += n[p] * gauss_excess2(mu[p] / 2.0, sqrt(var[p]) / 2.0, mid);
+        } else {
+            f = S * gauss_excess2(gm / 2.0, sqrt(gv) / 2.0, mid);
+        }
+        if (f >= 1.0) lo = mid; else hi = mid;
+    }
+    return 0.5 * (lo + hi);
+}
+
+/* Pages of one row whose estimated max can cross tau (see above); writes the
+ * ascending selection to sel and returns its size. */
+int oracle_gauss_select(const double *mu, const double *var, const int *n, int N,
+                        double tau, int bos, int eos, int k_cap, int32_t *sel)
+{
+    double *est = malloc(sizeof *est * (N > 0 ? N : 1));
+    int lo = bos < N ? bos : N;
+    int hi = N - eos > 0 ? N - eos : 0;
+    if (hi < lo) hi = lo;
+    int qual = 0;
+    for (int p = 0; p < N; ++p) {
+        double e = mu[p] + (n[p] > 1 ? sqrt(var[p]) * sqrt(2.0 * log((double)n[p])) : 0.0);
+        est[p] = e;
+        if (e / 2.0 > tau && p >= lo && p < hi) ++qual;
+    }
+    int nres = N - (hi - lo);
+    int budget = qual + nres;
+    if (budget > k_cap) budget = k_cap;
+    if (budget < 1) budget = 1;
+    int cnt = oracle_select(est, N, budget, 0.0, bos, eos, sel);
+    free(est);
+    return cnt;
 }
 
 /* ------------------------------------------------------ LSE merge (O6) */

@@ -115,3 +115,27 @@ def test_single_token_returns_its_value_and_empty_is_zero():
     o, t = oracle.attend_entmax15(q[0, 0], cache, 0, wl.block_table[0], S,
                                   np.array([], dtype=np.int32), wl.softmax_scale)
     assert np.all(o == 0) and t == -np.inf
+
+
+def test_alibi_attention_over_all_pages_is_dense_entmax_with_the_bias():
+    wl = W.small_case(seed=92, H_q=2, H_kv=1, min_len=5)
+    cache = W.bf16_bits(W.make_cache(wl))
+    q = W.make_queries(wl).double().numpy()
+    for b in range(wl.B):
+        S = int(wl.seq_lens[b])
+        N = int(wl.pages()[b])
+        pages = np.arange(N, dtype=np.int32)
+        ks, vs = [], []
+        for p in range(N):
+            n = min(wl.P, S - p * wl.P)
+            blk = int(wl.block_table[b, p])
+            ks.append(oracle.bf16_decode(cache[0, blk, :n, 0]))
+            vs.append(oracle.bf16_decode(cache[1, blk, :n, 0]))
+        K, V = np.concatenate(ks), np.concatenate(vs)
+        for slope in (0.0, 0.0625, 0.5):
+            z = wl.softmax_scale * (K @ q[b, 0]) + slope * (np.arange(S) - (S - 1))
+            rt = tau_by_sort(z)
+            o, t = oracle.attend_entmax15(q[b, 0], cache, 0, wl.block_table[b], S, pages,
+                                          wl.softmax_scale, slope=slope)
+            np.testing.assert_allclose(o, probs(z, rt) @ V, rtol=1e-11, atol=1e-11)
+            assert abs(t - rt) < 1e-11
