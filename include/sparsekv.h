@@ -295,8 +295,11 @@ int sparse_page_decode(const float *q, int B, int H_q, int H_kv, int D,
  * the mapping is the published 1.5-entmax: p_t = [z_t / 2 - tau]_+^2 with
  * z_t = scale * q . k_t and tau such that sum p_t = 1.]
  *
- *   Arguments as sparse_paged_decode (same selection rows, H_sel, splits of
- *   c = ceil(k_cap / num_splits) entries), plus
+ *   Arguments as sparse_paged_decode (same selection rows and H_sel), except
+ *   that split s takes the entries [s c, (s + 1) c) of the row's sel_cnt
+ *   entries with c = ceil(sel_cnt / num_splits); plus
+ *   alibi_slopes fp32 [H_q] or NULL: ALiBi slope of each query head in
+ *            logit units; a key at position t gets z_t += slope * (t - (S - 1)).
  *   scratch  fp32 device buffer of at least entmax_scratch_floats(B, H_q,
  *            k_cap, page_size) floats (logits, then tau per query head).
  *   Per (b, i, s):  m = sum of p over the split's rows,
@@ -312,9 +315,78 @@ int entmax15_paged_decode(const float *q, int B, int H_q, int H_kv, int D,
                           int64_t bt_ld, const int32_t *seq_lens,
                           const int32_t *sel_idx, const int32_t *sel_cnt,
                           const int32_t *sel_blk, int k_cap, int H_sel,
-                          float scale, int num_splits, float *o_part,
+                          float scale, int num_splits,
+                          const float *alibi_slopes, float *o_part,
                           float *lse_part, float *scratch,
                           int64_t scratch_floats, hipStream_t stream);
+
+/*
+ * Gaussian-aware adaptive selection.  [EKV "How it works": pages keep mean /
+ * std key statistics; each page's scores are modelled as a Gaussian; the
+ * distributional entmax constraint gives the threshold tau-hat (a page
+ * mixture for ALiBi heads, one Gaussian for NoPE heads); every page whose
+ * estimated maximum can cross tau-hat is selected, so the number of pages
+ * adapts.  EKV "Quick start": the Gaussian-aware decode runs alpha = 1.5.]
+ * A step: pagestats_update, page_var_update, gauss_moments, gauss_select,
+ * entmax15_paged_decode over the selection (H_sel = H_q), lse_merge.
+ *
+ * page_var_update -- population variance of the keys of a page per (kv head,
+ * dim), over its n = min(P, S_b - p P) valid rows, around k_mean.
+ *   k_mean   fp32 [num_blocks, H_kv, D] in (from pagestats_update, which must
+ *            have run first on the same stream)
+ *   k_var    fp32 [num_blocks, H_kv, D] out
+ *   tail_only 0: every page p < N_b of every request (rebuild);
+ *            nonzero: only the page holding token S_b - 1 (after an append).
+ */
+int page_var_update(const uint16_t *kv_cache, int64_t num_blocks, int page_size,
+                    int H_kv, int D, const float *k_mean, float *k_var,
+                    const int32_t *block_table, int64_t bt_ld,
+                    const int32_t *seq_lens, int B, int tail_only,
+                    hipStream_t stream);
+
+/*
+ * gauss_moments -- mean and variance of each page's logits z = scale q . k
+ * for every query head (key dimensions, and the position, taken as
+ * independent):
+ *   mu  = scale q . k_mean + slope * (mean valid position - (S_b - 1)),
+ *   var = scale^2 sum_d q_d^2 k_var_d + slope^2 (n^2 - 1) / 12.
+ *   q            fp32 [B, H_q, D];  k_mean, k_var fp32 [num_blocks, H_kv, D]
+ *   alibi_slopes fp32 [H_q] (logit units) or NULL (no bias terms)
+ *   mu, var      fp32 [B, H_q, ld], ld >= bt_ld; entries p >= N_b untouched.
+ */
+int gauss_moments(const float *q, int B, int H_q, int H_kv, int D,
+                  const float *k_mean, const float *k_var,
+                  const int32_t *block_table, int64_t bt_ld,
+                  const int32_t *seq_lens, int page_size, float scale,
+                  const float *alibi_slopes, float *mu, float *var, int64_t ld,
+                  hipStream_t stream);
+
+/*
+ * gauss_select -- tau-hat and the adaptive selection of every (request,
+ * query head) row.
+ *   With u = z / 2 and n_p valid rows per page, tau-hat solves
+ *     mixture != 0:  sum_p n_p E[(X_p - tau)_+^2] = 1, X_p ~ N(mu_p/2, var_p/4);
+ *     mixture == 0:  S E[(X - tau)_+^2] = 1, X ~ N(m/2, v/4) with m, v the
+ *                    pooled mean and variance of the S tokens of the pages;
+ *   (Newton in fp64 from below).  est_p = mu_p + sqrt(var_p) sqrt(2 ln n_p)
+ *   (mu_p for n_p = 1), fp32.  Selected: the reserved first reserved_bos and
+ *   last reserved_eos pages, and every other page with est_p / 2 > tau-hat
+ *   (fp32 comparison); at most k_cap pages (largest estimates, ties to the
+ *   lower index), at least one.
+ *   mu, var  fp32 [B, H_q, ld] (from gauss_moments); bt_ld <= 32768.
+ *   tau      fp32 [B * H_q] out, or NULL;  est fp32 [B, H_q, ld] out
+ *            (required: the selection reads it back).
+ *   sel_idx  int32 [B * H_q, k_cap] out, ascending, padded with -1;
+ *   sel_cnt  int32 [B * H_q] out;  sel_blk int32 [B * H_q, k_cap] out or NULL
+ *            (block_table[b][p] of each selected page).
+ *   k_cap must hold the reserved pages (>= min(bt_ld, bos + eos)).
+ */
+int gauss_select(const float *mu, const float *var, int64_t ld, int B, int H_q,
+                 const int32_t *seq_lens, int page_size,
+                 const int32_t *block_table, int64_t bt_ld, int mixture,
+                 int reserved_bos, int reserved_eos, int k_cap, float *tau,
+                 float *est, int32_t *sel_idx, int32_t *sel_cnt, int32_t *sel_blk,
+                 hipStream_t stream);
 
 /*
  * lse_merge -- N-way log-sum-exp merge of split partials.  [MLA:

@@ -21,7 +21,7 @@ __all__ = [
     "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
     "h2o_accumulate", "h2o_scratch_floats", "entmax15_paged_decode",
     "entmax_scratch_floats", "sparse_select_decode", "sparse_page_decode",
-    "library_path",
+    "page_var_update", "gauss_moments", "gauss_select", "library_path",
     "load_library", "SparseKVError", "EXPORTED_SYMBOLS",
 ]
 
@@ -34,12 +34,12 @@ EXPORTED_SYMBOLS = (
     "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
     "h2o_accumulate", "h2o_scratch_floats", "entmax15_paged_decode",
     "entmax_scratch_floats", "sparse_select_decode", "sparse_page_decode",
-    "sparsekv_last_error",
+    "page_var_update", "gauss_moments", "gauss_select", "sparsekv_last_error",
 )
 _INT_RETURNING = ("pagestats_update", "page_score", "page_score_group", "page_topk",
                   "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
                   "h2o_accumulate", "entmax15_paged_decode", "sparse_select_decode",
-                  "sparse_page_decode")
+                  "sparse_page_decode", "page_var_update", "gauss_moments", "gauss_select")
 
 
 class SparseKVError(RuntimeError):
@@ -81,7 +81,10 @@ def load_library():
     lib.h2o_scratch_floats.argtypes = [I, I, L]
     lib.h2o_scratch_floats.restype = ctypes.c_int64
     lib.entmax15_paged_decode.argtypes = [V, I, I, I, I, V, L, I, V, L, V, V, V, V, I, I,
-                                          F, I, V, V, V, L, V]
+                                          F, I, V, V, V, V, L, V]
+    lib.page_var_update.argtypes = [V, L, I, I, I, V, V, V, L, V, I, I, V]
+    lib.gauss_moments.argtypes = [V, I, I, I, I, V, V, V, L, V, I, F, V, V, V, L, V]
+    lib.gauss_select.argtypes = [V, V, L, I, I, V, I, V, L, I, I, I, I, V, V, V, V, V, V]
     lib.entmax_scratch_floats.argtypes = [I, I, I, I]
     lib.sparse_select_decode.argtypes = [V, L, I, F, I, I, V, I, I, I, I, V, L, I, V, L, V,
                                          I, F, I, V, V, V, V, V, V, V]
@@ -339,10 +342,12 @@ def entmax_scratch_floats(B, H_q, k_cap, page_size):
 
 
 def entmax15_paged_decode(q, kv_cache, block_table, seq_lens, sel_idx, sel_cnt, scale,
-                          o_part, lse_part, scratch, sel_blk=None, stream=None):
+                          o_part, lse_part, scratch, sel_blk=None, alibi_slopes=None,
+                          stream=None):
     """1.5-entmax attention over the selected pages as split partials
     (o_part [B, H_q, splits, D], lse_part = ln of each split's mass), to be
-    combined by lse_merge."""
+    combined by lse_merge.  alibi_slopes ([H_q], logit units) adds
+    slope * (pos - (S - 1)) to each logit."""
     lib = load_library()
     _check("q", q, torch.float32, 3)
     dev = q.device
@@ -363,11 +368,91 @@ def entmax15_paged_decode(q, kv_cache, block_table, seq_lens, sel_idx, sel_cnt, 
     H_sel = sel_idx.shape[1]
     if tuple(o_part.shape) != (B, H_q, ns, D) or tuple(lse_part.shape) != (B, H_q, ns):
         raise ValueError("o_part must be [B, H_q, splits, D] and lse_part [B, H_q, splits]")
+    alibi_slopes = _alibi_arg(alibi_slopes, H_q, dev)
     _rc("entmax15_paged_decode", lib.entmax15_paged_decode(
         _ptr(q), B, H_q, H_kv, D, _ptr(kv_cache), NB, P, _ptr(block_table),
         block_table.shape[1], _ptr(seq_lens), _ptr(sel_idx), _ptr(sel_cnt), _ptr(sel_blk),
-        sel_idx.shape[2], H_sel, float(scale), ns, _ptr(o_part), _ptr(lse_part),
-        _ptr(scratch), scratch.numel(), _stream(stream)))
+        sel_idx.shape[2], H_sel, float(scale), ns, _ptr(alibi_slopes), _ptr(o_part),
+        _ptr(lse_part), _ptr(scratch), scratch.numel(), _stream(stream)))
+
+
+def page_var_update(kv_cache, k_mean, k_var, block_table, seq_lens, tail_only=False,
+                    stream=None):
+    """Per-page key variance around k_mean ([num_blocks, H_kv, D] fp32), for
+    every page (rebuild) or only the page holding each request's last token."""
+    lib = load_library()
+    _check("kv_cache", kv_cache, torch.bfloat16, 5)
+    dev = kv_cache.device
+    _, NB, P, H_kv, D = kv_cache.shape
+    for n, t in (("k_mean", k_mean), ("k_var", k_var)):
+        _check(n, t, torch.float32, 3, dev)
+        if t is not None and tuple(t.shape) != (NB, H_kv, D):
+            raise ValueError(f"{n} must be [num_blocks, H_kv, D]")
+    _check("block_table", block_table, torch.int32, 2, dev)
+    _check("seq_lens", seq_lens, torch.int32, 1, dev)
+    B = seq_lens.shape[0]
+    if block_table.shape[0] != B:
+        raise ValueError("block_table rows must equal len(seq_lens)")
+    _rc("page_var_update", lib.page_var_update(
+        _ptr(kv_cache), NB, P, H_kv, D, _ptr(k_mean), _ptr(k_var), _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), B, 1 if tail_only else 0, _stream(stream)))
+
+
+def gauss_moments(q, k_mean, k_var, block_table, seq_lens, page_size, scale, mu, var,
+                  alibi_slopes=None, stream=None):
+    """mu, var [B, H_q, ld] of each page's logits (Gaussian page model);
+    alibi_slopes [H_q] in logit units."""
+    lib = load_library()
+    _check("q", q, torch.float32, 3)
+    dev = q.device
+    B, H_q, D = q.shape
+    _check("k_mean", k_mean, torch.float32, 3, dev)
+    _check("k_var", k_var, torch.float32, 3, dev)
+    _check("block_table", block_table, torch.int32, 2, dev)
+    _check("seq_lens", seq_lens, torch.int32, 1, dev)
+    _check("mu", mu, torch.float32, 3, dev)
+    _check("var", var, torch.float32, 3, dev)
+    H_kv = k_mean.shape[1]
+    if tuple(mu.shape[:2]) != (B, H_q) or mu.shape != var.shape:
+        raise ValueError("mu and var must be [B, H_q, ld]")
+    alibi_slopes = _alibi_arg(alibi_slopes, H_q, dev)
+    _rc("gauss_moments", lib.gauss_moments(
+        _ptr(q), B, H_q, H_kv, D, _ptr(k_mean), _ptr(k_var), _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), int(page_size), float(scale),
+        _ptr(alibi_slopes), _ptr(mu), _ptr(var), mu.shape[2], _stream(stream)))
+
+
+def gauss_select(mu, var, seq_lens, page_size, block_table, mixture, k_cap, est, sel_idx,
+                 sel_cnt, tau=None, sel_blk=None, reserved_bos=0, reserved_eos=1,
+                 stream=None):
+    """tau-hat and the adaptive page selection of every (request, query head):
+    est [B, H_q, ld] receives the estimated page maxima, sel_idx
+    [B, H_q, k_cap] / sel_cnt [B, H_q] the selection (as page_topk's)."""
+    lib = load_library()
+    _check("mu", mu, torch.float32, 3)
+    dev = mu.device
+    B, H_q, ld = mu.shape
+    _check("var", var, torch.float32, 3, dev)
+    _check("est", est, torch.float32, 3, dev)
+    _check("seq_lens", seq_lens, torch.int32, 1, dev)
+    _check("block_table", block_table, torch.int32, 2, dev)
+    _check("sel_idx", sel_idx, torch.int32, 3, dev)
+    _check("sel_cnt", sel_cnt, torch.int32, 2, dev)
+    _check("tau", tau, torch.float32, 2, dev)
+    _check("sel_blk", sel_blk, torch.int32, 3, dev)
+    if var.shape != mu.shape or est.shape != mu.shape:
+        raise ValueError("mu, var and est must share the shape [B, H_q, ld]")
+    if tuple(sel_idx.shape) != (B, H_q, int(k_cap)) or tuple(sel_cnt.shape) != (B, H_q):
+        raise ValueError("sel_idx must be [B, H_q, k_cap] and sel_cnt [B, H_q]")
+    if sel_blk is not None and sel_blk.shape != sel_idx.shape:
+        raise ValueError("sel_blk must match sel_idx")
+    if tau is not None and tuple(tau.shape) != (B, H_q):
+        raise ValueError("tau must be [B, H_q]")
+    _rc("gauss_select", lib.gauss_select(
+        _ptr(mu), _ptr(var), ld, B, H_q, _ptr(seq_lens), int(page_size), _ptr(block_table),
+        block_table.shape[1], 1 if mixture else 0, int(reserved_bos), int(reserved_eos),
+        int(k_cap), _ptr(tau), _ptr(est), _ptr(sel_idx), _ptr(sel_cnt), _ptr(sel_blk),
+        _stream(stream)))
 
 
 def sparse_select_decode(scores, q, kv_cache, block_table, seq_lens, topk_pages, k_cap,

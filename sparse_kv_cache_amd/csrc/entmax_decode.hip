@@ -18,6 +18,7 @@
 //      writes the chunk's (o = sum p v / m, lse = ln m) with its mass m, so
 //      lse_merge's algebra returns sum over chunks of p v (total mass 1).
 // Scratch: logits [B, H_q, k_cap * P] then tau [B, H_q].
+// ALiBi heads add slope * (pos - (S - 1)) to each logit in pass 1.
 #include "skv_device.h"
 #include "skv_host.h"
 
@@ -49,9 +50,11 @@ __device__ __forceinline__ bool chunk_of(int64_t w, int H_q, int H_kv, int G, in
   c.h = h;
   c.srow = H_sel == H_q ? static_cast<int>(qrow) : b * H_kv + h;
   c.S = seq_lens[b];
-  const int cap = (k_cap + num_splits - 1) / num_splits;
   int cnt = sel_cnt[c.srow];
   cnt = cnt < 0 ? 0 : (cnt > k_cap ? k_cap : cnt);
+  // the row's actual entries split evenly (a selection of adaptive size
+  // would leave the trailing splits of a k_cap-sized grid empty)
+  const int cap = (cnt + num_splits - 1) / num_splits;
   c.start = s * cap;
   int len = cnt - c.start;
   c.len = len < 0 ? 0 : (len > cap ? cap : len);
@@ -74,7 +77,7 @@ __global__ __launch_bounds__(kWaves * 64) void entmax_logits_kernel(
     const int32_t* __restrict__ bt, int64_t bt_ld, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt,
     const int32_t* __restrict__ sel_blk, int k_cap, int H_sel, float scale,
-    int num_splits, float* __restrict__ logits) {
+    int num_splits, const float* __restrict__ alibi, float* __restrict__ logits) {
   constexpr int LPR = D / 8;
   constexpr int RPL = 64 / LPR;
   constexpr int NL = 16 / RPL;
@@ -85,6 +88,7 @@ __global__ __launch_bounds__(kWaves * 64) void entmax_logits_kernel(
   const int slot = lane / LPR, cc = lane % LPR;
   int64_t Nb = (static_cast<int64_t>(c.S) + P - 1) / P;
   if (Nb > bt_ld) Nb = bt_ld;
+  const float slope = alibi != nullptr ? alibi[c.qrow % H_q] : 0.0f;
   // q split into bf16 hi + lo halves: exact bf16 products on the packed keys
   uint32_t qh[4], ql[4];
   {
@@ -109,20 +113,21 @@ __global__ __launch_bounds__(kWaves * 64) void entmax_logits_kernel(
   const int epg = 16 / P;
   for (int w0 = 0; w0 < c.len; w0 += 64) {
     const int nw = min(64, c.len - w0);
-    int my_blk = 0, my_nv = 0;
+    int my_blk = 0, my_nv = 0, my_off = 0;
     if (lane < nw) {
       const int p = selr[c.start + w0 + lane];
       if (p >= 0 && p < Nb) {
         my_blk = sblk != nullptr ? sblk[c.start + w0 + lane] : btr[p];
         const int n = c.S - p * P;
         my_nv = n < P ? n : P;
+        my_off = p * P - (c.S - 1);        // first row's offset from the query
       }
     }
     const int ngroups = (nw + epg - 1) / epg;
     for (int grp = 0; grp < ngroups; ++grp) {
       uint4 K[NL];
       bool ok[NL];
-      int ent[NL], tt[NL];
+      int ent[NL], tt[NL], rel[NL];
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
         const int rr = slot + RPL * j;
@@ -134,6 +139,7 @@ __global__ __launch_bounds__(kWaves * 64) void entmax_logits_kernel(
         ok[j] = e < nw && t < nv;
         ent[j] = e;
         tt[j] = t;
+        rel[j] = __shfl(my_off, ec) + t;
         const int64_t off = ok[j] ? (static_cast<int64_t>(blk) * P + t) * row_stride + head_off
                                   : head_off;
         K[j] = *reinterpret_cast<const uint4*>(kv + off);
@@ -146,6 +152,8 @@ __global__ __launch_bounds__(kWaves * 64) void entmax_logits_kernel(
         d = dot2e(K[j].z, qh[2], d); d = dot2e(K[j].z, ql[2], d);
         d = dot2e(K[j].w, qh[3], d); d = dot2e(K[j].w, ql[3], d);
         d = skv::group_sum<LPR>(d);
+        // ALiBi: slope * (pos - (S - 1)), the integer offset exact in fp32
+        if (alibi != nullptr) d = fmaf(slope, static_cast<float>(rel[j]), d);
         if (cc == 0 && ent[j] < nw)
           lrow[static_cast<int64_t>(c.start + w0 + ent[j]) * P + tt[j]] = ok[j] ? d : -INFINITY;
       }
@@ -332,7 +340,8 @@ extern "C" int entmax15_paged_decode(const float* q, int B, int H_q, int H_kv, i
                                      int64_t bt_ld, const int32_t* seq_lens,
                                      const int32_t* sel_idx, const int32_t* sel_cnt,
                                      const int32_t* sel_blk, int k_cap, int H_sel,
-                                     float scale, int num_splits, float* o_part,
+                                     float scale, int num_splits,
+                                     const float* alibi_slopes, float* o_part,
                                      float* lse_part, float* scratch,
                                      int64_t scratch_floats, hipStream_t stream) {
   SKV_REQUIRE(B >= 0 && H_kv > 0 && H_q > 0 && H_q % H_kv == 0,
@@ -373,12 +382,12 @@ extern "C" int entmax15_paged_decode(const float* q, int B, int H_q, int H_kv, i
     hipLaunchKernelGGL(entmax_logits_kernel<128>, g13, dim3(kWaves * 64), 0, stream, q, B,
                        H_q, H_kv, G, kv_cache, num_blocks, page_size, block_table, bt_ld,
                        seq_lens, sel_idx, sel_cnt, sel_blk, k_cap, H_sel, scale, num_splits,
-                       logits);
+                       alibi_slopes, logits);
   else
     hipLaunchKernelGGL(entmax_logits_kernel<64>, g13, dim3(kWaves * 64), 0, stream, q, B,
                        H_q, H_kv, G, kv_cache, num_blocks, page_size, block_table, bt_ld,
                        seq_lens, sel_idx, sel_cnt, sel_blk, k_cap, H_sel, scale, num_splits,
-                       logits);
+                       alibi_slopes, logits);
   hipLaunchKernelGGL(entmax_tau_kernel, dim3(static_cast<unsigned>(rows)), dim3(kTauThreads),
                      0, stream, B, H_q, H_kv, G, page_size, sel_cnt, k_cap, H_sel, logits,
                      tau);

@@ -10,6 +10,9 @@ library's entry points in the order of a decode step:
                head, shared by its query group
   token level  pagestats_update (append + hh reset) -> h2o_accumulate
                -> page_topk (per kv head) -> sparse_paged_decode -> lse_merge
+  Gaussian     [pagestats_update + page_var_update (tail page)]
+               -> gauss_moments -> gauss_select -> entmax15_paged_decode
+               -> lse_merge
 
 This mirrors the decode call of the EntmaxKV README ("Quick start": score,
 select, attend and append in one call) cut at kernel granularity.  Nothing
@@ -21,10 +24,11 @@ import math
 
 import torch
 
-from . import (entmax15_paged_decode, entmax_scratch_floats, h2o_accumulate,
-               h2o_scratch_floats, lse_merge, page_score, page_score_group, page_topk,
-               pagestats_update, sparse_page_decode, sparse_paged_decode,
-               sparse_paged_decode_merged, sparse_select_decode)
+from . import (entmax15_paged_decode, entmax_scratch_floats, gauss_moments, gauss_select,
+               h2o_accumulate, h2o_scratch_floats, lse_merge, page_score,
+               page_score_group, page_topk, page_var_update, pagestats_update,
+               sparse_page_decode, sparse_paged_decode, sparse_paged_decode_merged,
+               sparse_select_decode)
 
 
 def alibi_slopes(H, device="cuda"):
@@ -50,13 +54,18 @@ class SparseDecoder:
     With one selection per query head and num_splits <= 8 the split merge runs
     inside the decode launch (fused); keep_partials also writes the partials.
     attention="entmax15" attends with 1.5-entmax instead of softmax (page
-    level; three decode launches, then lse_merge)."""
+    level; three decode launches, then lse_merge).
+    selection="gauss" selects per query head with the Gaussian-aware rule
+    (adaptive page count, at most gauss_cap pages, default every page) and
+    attends with 1.5-entmax; the page-mixture tau-hat is used for ALiBi heads
+    and the single Gaussian otherwise, unless gauss_mixture says which."""
 
     def __init__(self, B, H_q, H_kv, D, num_blocks, page_size, bt_ld, *,
                  topk_pages, topk_frac=0.0, bos=0, eos=1, w_avg=1.0, w_peak=1.0,
                  scale=None, num_splits=1, decay=0.984375, token_level=False,
                  group_select=False, alibi_slopes=None, fuse_merge=True,
-                 attention="softmax", device="cuda"):
+                 attention=None, selection="topk", gauss_cap=None, gauss_mixture=None,
+                 device="cuda"):
         self.B, self.H_q, self.H_kv, self.D = B, H_q, H_kv, D
         self.num_blocks, self.P, self.bt_ld = num_blocks, page_size, bt_ld
         self.topk_pages, self.topk_frac = topk_pages, topk_frac
@@ -69,16 +78,29 @@ class SparseDecoder:
         dev = torch.device(device)
         if alibi_slopes is not None and token_level:
             raise ValueError("ALiBi is not part of the token-level flow")
+        if selection not in ("topk", "gauss"):
+            raise ValueError("selection must be 'topk' or 'gauss'")
+        if attention is None:
+            attention = "entmax15" if selection == "gauss" else "softmax"
         if attention not in ("softmax", "entmax15"):
             raise ValueError("attention must be 'softmax' or 'entmax15'")
-        if attention == "entmax15" and (token_level or alibi_slopes is not None):
-            raise ValueError("1.5-entmax is built for the page-level flow without ALiBi")
+        if attention == "entmax15" and token_level:
+            raise ValueError("1.5-entmax is built for the page-level flow")
+        if selection == "gauss" and (token_level or group_select or attention != "entmax15"):
+            raise ValueError("Gaussian-aware selection is per query head, page level, "
+                             "with 1.5-entmax attention")
         self.attention = attention
+        self.selection = selection
+        self.gauss = selection == "gauss"
+        self.mixture = (alibi_slopes is not None) if gauss_mixture is None else bool(gauss_mixture)
         self.alibi = alibi_slopes
         # the page score is in q.k units: slopes divided by the softmax scale
         self.alibi_score = None if alibi_slopes is None else alibi_slopes / self.scale
         self.H_sel = H_kv if (token_level or self.group_select) else H_q
         self.k_cap = selection_capacity(bt_ld, topk_pages, topk_frac, bos, eos)
+        if self.gauss:
+            cap = bt_ld if gauss_cap is None else int(gauss_cap)
+            self.k_cap = max(1, min(bt_ld, max(cap, bos + eos)))
         f32, i32, bf = torch.float32, torch.int32, torch.bfloat16
         if token_level:
             if page_size != 1:
@@ -113,6 +135,13 @@ class SparseDecoder:
         self.score_in_decode = (self.select_in_decode and not self.group_select
                                 and (2 * sc_cap + 2 * self.k_cap) * 4 <= 48 * 1024)
         self.keep_scores = False
+        self.k_var = self.mu = self.var = self.est = self.tau_hat = None
+        if self.gauss:
+            self.k_var = torch.empty((num_blocks, H_kv, D), dtype=f32, device=dev)
+            self.mu = torch.empty((B, H_q, bt_ld), dtype=f32, device=dev)
+            self.var = torch.empty((B, H_q, bt_ld), dtype=f32, device=dev)
+            self.est = self.scores            # the estimates are the ranking scores
+            self.tau_hat = torch.empty((B, H_q), dtype=f32, device=dev)
         self.entmax_scratch = None
         if attention == "entmax15":
             n = entmax_scratch_floats(B, H_q, self.k_cap, page_size)
@@ -120,7 +149,8 @@ class SparseDecoder:
 
     @classmethod
     def for_workload(cls, wl, device="cuda", num_splits=None, group_select=False,
-                     alibi_slopes=None, fuse_merge=True, attention="softmax"):
+                     alibi_slopes=None, fuse_merge=True, attention=None,
+                     selection="topk", gauss_cap=None, gauss_mixture=None):
         return cls(wl.B, wl.H_q, wl.H_kv, wl.D, wl.num_blocks, wl.P, wl.bt_ld,
                    topk_pages=wl.topk_pages, topk_frac=wl.topk_frac, bos=wl.bos,
                    eos=wl.eos, w_avg=wl.w_avg, w_peak=wl.w_peak,
@@ -128,17 +158,34 @@ class SparseDecoder:
                    num_splits=wl.num_splits if num_splits is None else num_splits,
                    decay=wl.decay, token_level=(wl.name == "h2o_token"),
                    group_select=group_select, alibi_slopes=alibi_slopes,
-                   fuse_merge=fuse_merge, attention=attention, device=device)
+                   fuse_merge=fuse_merge, attention=attention, selection=selection,
+                   gauss_cap=gauss_cap, gauss_mixture=gauss_mixture, device=device)
 
     # ------------------------------------------------------------ stages
     def rebuild_stats(self, kv_cache, block_table, seq_lens, stream=None):
         pagestats_update(kv_cache, self.k_min, self.k_max, self.k_mean,
                          block_table, seq_lens, stream=stream)
+        if self.gauss:
+            page_var_update(kv_cache, self.k_mean, self.k_var, block_table, seq_lens,
+                            stream=stream)
 
     def append(self, kv_cache, block_table, seq_lens, k_new, v_new, stream=None):
         pagestats_update(kv_cache, self.k_min, self.k_max, self.k_mean,
                          block_table, seq_lens, k_new, v_new, self.hh,
                          stream=stream)
+        if self.gauss:
+            page_var_update(kv_cache, self.k_mean, self.k_var, block_table, seq_lens,
+                            tail_only=True, stream=stream)
+
+    def gauss_select(self, q, block_table, seq_lens, stream=None):
+        """Moments, tau-hat and the adaptive selection (Gaussian-aware)."""
+        gauss_moments(q, self.k_mean, self.k_var, block_table, seq_lens, self.P,
+                      self.scale, self.mu, self.var, alibi_slopes=self.alibi,
+                      stream=stream)
+        gauss_select(self.mu, self.var, seq_lens, self.P, block_table, self.mixture,
+                     self.k_cap, self.est, self.sel_idx, self.sel_cnt, tau=self.tau_hat,
+                     sel_blk=self.sel_blk if self.use_sel_blk else None,
+                     reserved_bos=self.bos, reserved_eos=self.eos, stream=stream)
 
     def score(self, q, block_table, seq_lens, stream=None):
         if self.token_level:
@@ -165,7 +212,7 @@ class SparseDecoder:
                                   self.sel_cnt, self.scale, self.o_part, self.lse_part,
                                   self.entmax_scratch,
                                   sel_blk=self.sel_blk if self.use_sel_blk else None,
-                                  stream=stream)
+                                  alibi_slopes=self.alibi, stream=stream)
             return
         if self.fused:
             parts = (self.o_part, self.lse_part) if self.keep_partials else (None, None)
@@ -213,6 +260,11 @@ class SparseDecoder:
         """One decode step; returns (out, lse) views of the decoder's buffers."""
         if k_new is not None:
             self.append(kv_cache, block_table, seq_lens, k_new, v_new, stream)
+        if self.gauss:
+            self.gauss_select(q, block_table, seq_lens, stream)
+            self.attend(q, kv_cache, block_table, seq_lens, stream)
+            self.merge(stream)
+            return self.out, self.lse
         if self.score_in_decode:
             self.score_select_attend(q, kv_cache, block_table, seq_lens, stream)
             return self.out, self.lse

@@ -315,3 +315,65 @@ def per_head_rows(sel_rows, B, H_q, H_sel):
 
 def bf16_bits_apart(a_bits, b_bits):
     return np.abs(a_bits.astype(np.int64) - b_bits.astype(np.int64))
+
+
+# ------------------------------------------------- Gaussian-aware selection
+
+def page_rows(S, P, N):
+    """Valid rows of each of the N pages of a request of S tokens."""
+    return np.array([min(P, S - p * P) for p in range(N)], dtype=np.int32)
+
+
+def check_gauss_row(g_mu, g_var, g_est, g_tau, g_sel, n, mixture, bos, eos, k_cap,
+                    mu_o, var_o, k1, q2, bias, row):
+    """One (request, query head) row of the Gaussian-aware path.
+
+    g_*   the GPU's moments, estimates, tau-hat (fp32) and selection;
+    mu_o, var_o  the oracle's moments from the oracle's statistics;
+    k1    scale * sum_d |q_d| (|mean_d| + sd_d): the magnitude the fp32 mean
+          and dot product round against; q2 = scale^2 sum_d q_d^2;
+    bias  the ALiBi part of mu_o (0 without ALiBi).
+    Returns True when the end-to-end selection differs from the oracle's only
+    at pages within the tolerance band of tau-hat (an exempt row)."""
+    N = n.shape[0]
+    # moments against the oracle
+    e_mu = np.abs(g_mu - mu_o)
+    tol_mu = 8e-6 * k1 + 2e-7 * np.abs(bias) + 1e-7
+    assert np.all(e_mu <= tol_mu), f"row {row}: mu err {e_mu.max()} (tol {tol_mu.min()})"
+    e_var = np.abs(g_var - var_o)
+    tol_var = 1e-5 * var_o + 1e-8 * (1.0 + q2)
+    assert np.all(e_var <= tol_var), f"row {row}: var err {e_var.max()}"
+    # tau-hat: the oracle's solve on the GPU's own moments (fp32 result)
+    t_o = oracle.gauss_tau(g_mu.astype(np.float64), g_var.astype(np.float64), n, mixture)
+    assert abs(float(g_tau) - t_o) <= 1e-6 * max(1.0, abs(t_o)), \
+        f"row {row}: tau-hat {g_tau} vs oracle {t_o} on the same moments"
+    # estimates from the GPU's moments
+    c = np.where(n > 1, np.sqrt(2.0 * np.log(np.maximum(n, 1))), 0.0)
+    e_o = g_mu.astype(np.float64) + np.sqrt(np.maximum(g_var.astype(np.float64), 0)) * c
+    tol_e = 1e-6 * (np.abs(g_mu) + np.sqrt(np.maximum(g_var, 0)) * c) + 1e-7
+    assert np.all(np.abs(g_est - e_o) <= tol_e), f"row {row}: estimate error"
+    # the selection is exact on the GPU's fp32 estimates and tau-hat
+    lo, hi = min(bos, N), max(N - eos, 0)
+    hi = max(hi, lo)
+    half = np.float32(0.5) * g_est.astype(np.float32)
+    qual = int(np.count_nonzero(half[lo:hi] > np.float32(g_tau)))
+    budget = max(1, min(k_cap, qual + N - (hi - lo)))
+    want = oracle.select(g_est.astype(np.float64), budget, 0.0, bos, eos).tolist()[:k_cap]
+    assert list(g_sel) == want, f"row {row}: selection differs on the GPU's own values"
+    # end to end: the oracle's tau-hat and selection from its own moments
+    t_full = oracle.gauss_tau(mu_o, var_o, n, mixture)
+    assert abs(float(g_tau) - t_full) <= 1e-4 * max(1.0, abs(t_full)), \
+        f"row {row}: tau-hat {g_tau} vs end-to-end oracle {t_full}"
+    full = oracle.gauss_select(mu_o, var_o, n, t_full, bos, eos, k_cap).tolist()
+    if full == list(g_sel):
+        return False
+    est_full = mu_o + np.sqrt(var_o) * c
+    band = 1e-4 * max(1.0, abs(t_full)) + 1e-5 * np.abs(est_full)
+    if len(full) >= k_cap or len(g_sel) >= k_cap:
+        # the cap ranks by estimate: near-equal estimates may trade places
+        assert len(full) == len(g_sel), f"row {row}: capped counts differ"
+        return True
+    for p in set(full) ^ set(g_sel):
+        assert abs(est_full[p] / 2 - t_full) <= band[p], \
+            f"row {row}: page {p} selected differently away from tau-hat"
+    return True

@@ -42,7 +42,7 @@ def test_header_declares_the_six_operations():
     for n in ("pagestats_update", "page_score", "page_score_group", "page_topk",
               "sparse_paged_decode", "sparse_paged_decode_merged",
               "entmax15_paged_decode", "entmax_scratch_floats", "sparse_select_decode",
-              "sparse_page_decode",
+              "sparse_page_decode", "page_var_update", "gauss_moments", "gauss_select",
               "lse_merge", "h2o_accumulate", "h2o_scratch_floats",
               "sparsekv_last_error"):
         assert n in names
@@ -130,10 +130,26 @@ def test_validation_rejects_bad_scalars(lib):
     assert "k_min" in _msg(lib)
     # entmax: scratch too small, splits < 1
     assert lib.entmax15_paged_decode(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p, None, 4, 8,
-                                     0.1, 2, p, p, p, 3, s) == EINVAL
+                                     0.1, 2, None, p, p, p, 3, s) == EINVAL
     assert "scratch" in _msg(lib)
     assert lib.entmax15_paged_decode(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p, None, 4, 8,
-                                     0.1, 0, p, p, p, 10 ** 6, s) == EINVAL
+                                     0.1, 0, None, p, p, p, 10 ** 6, s) == EINVAL
+    # Gaussian-aware: bad page size, head shape, scale, capacity below the
+    # reserved pages, too long a row
+    assert lib.page_var_update(p, 8, 3, 2, 128, p, p, p, 4, p, 1, 0, s) == EINVAL
+    assert lib.page_var_update(p, 8, 16, 2, 96, p, p, p, 4, p, 1, 0, s) == EINVAL
+    assert lib.gauss_moments(p, 1, 8, 3, 128, p, p, p, 4, p, 16, 0.1, None, p, p, 4,
+                             s) == EINVAL
+    assert lib.gauss_moments(p, 1, 8, 2, 128, p, p, p, 4, p, 16, 0.0, None, p, p, 4,
+                             s) == EINVAL
+    assert lib.gauss_moments(p, 1, 8, 2, 128, p, p, p, 8, p, 16, 0.1, None, p, p, 4,
+                             s) == EINVAL
+    assert "ld" in _msg(lib)
+    assert lib.gauss_select(p, p, 64, 1, 8, p, 16, p, 64, 1, 2, 3, 4, None, p, p, p, None,
+                            s) == EINVAL
+    assert "reserved" in _msg(lib)
+    assert lib.gauss_select(p, p, 40000, 1, 8, p, 16, p, 40000, 1, 0, 1, 4, None, p, p, p,
+                            None, s) == EINVAL
     assert lib.entmax_scratch_floats(2, 8, 4, 16) == 2 * 8 * 4 * 16 + 2 * 8
     # h2o: page size must be 1, decay in (0, 1]
     assert lib.h2o_accumulate(p, 1, 8, 2, 128, p, 8, 16, p, 8, p, 0, 1, 0.1, 0.98,
@@ -163,6 +179,15 @@ def test_validation_rejects_null_pointers(lib):
     # rebuild mode needs them
     assert lib.pagestats_update(p, 8, 16, 2, 64, None, None, None, p, 4, p, 1,
                                 None, None, None, s) == EINVAL
+    assert lib.page_var_update(p, 8, 16, 2, 128, None, p, p, 4, p, 1, 0, s) == EFAULT
+    assert "k_mean" in _msg(lib)
+    assert lib.gauss_moments(p, 1, 8, 2, 128, p, None, p, 4, p, 16, 0.1, None, p, p, 4,
+                             s) == EFAULT
+    assert "k_var" in _msg(lib)
+    # the estimates are required: the selection reads them back
+    assert lib.gauss_select(p, p, 64, 1, 8, p, 16, p, 64, 1, 0, 1, 4, None, None, p, p,
+                            None, s) == EFAULT
+    assert "est" in _msg(lib)
 
 
 def test_scratch_size_query(lib):

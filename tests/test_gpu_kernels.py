@@ -11,8 +11,8 @@ import sparse_kv_cache_amd as skv
 from sparse_kv_cache_amd import workloads as W
 from sparse_kv_cache_amd.decode import SparseDecoder
 
-from parity import (bits, check_attention, check_partials, check_scores,
-                    check_scores_alibi, check_scores_group,
+from parity import (OUT_ATOL, bits, check_attention, check_gauss_row, check_partials,
+                    check_scores, check_scores_alibi, check_scores_group, page_rows,
                     check_selection_exact, check_selection_vs_oracle,
                     check_stats, dev, per_head_rows, poison, say,
                     selection_rows, bf16_bits_apart, check_sel_blk)
@@ -402,6 +402,128 @@ def test_entmax_step(case):
         wl.scale = scale
     worst = run_entmax_case(wl, W.make_cache(wl), W.make_queries(wl), group)
     say(f"  max |out - oracle| = {worst:.2e}")
+
+
+# seed, B, H_q, H_kv, D, P, max_pages, bos, eos, splits, alibi, mixture, cap, scale
+GAUSS_CASES = [
+    (130, 2, 4, 2, 64, 16, 9, 0, 1, 2, False, None, None, None),
+    (131, 3, 8, 2, 128, 16, 40, 0, 1, 4, True, None, None, None),
+    (132, 2, 8, 2, 128, 16, 40, 0, 1, 4, False, True, None, None),
+    (133, 2, 8, 2, 128, 16, 40, 0, 1, 4, True, False, None, None),
+    (134, 2, 6, 2, 128, 8, 60, 1, 2, 3, False, None, 5, 1.0),
+    (135, 1, 4, 1, 64, 16, 3, 0, 1, 1, True, None, None, None),
+    (136, 2, 16, 2, 128, 16, 300, 0, 1, 8, True, None, None, None),
+    (137, 1, 8, 8, 128, 16, 1100, 0, 1, 8, False, None, None, 0.25),
+    (138, 2, 8, 4, 64, 4, 90, 2, 1, 5, True, None, 12, None),
+]
+
+
+def run_gauss_case(wl, cache_in, q_cpu, slopes_np=None, mixture=None, cap=None, rows=None):
+    """Gaussian-aware step: variance statistics, moments, tau-hat, selection
+    and the 1.5-entmax decode over it, each against the oracle.  rows limits
+    the checked (request, query head) rows (default all)."""
+    cache = cache_in if cache_in.is_cuda else dev(cache_in)
+    q = dev(q_cpu)
+    bt = dev(wl.block_table)
+    sl = dev(wl.seq_lens)
+    slopes = None if slopes_np is None else dev(np.asarray(slopes_np, dtype=np.float32))
+    d = SparseDecoder(wl.B, wl.H_q, wl.H_kv, wl.D, wl.num_blocks, wl.P, wl.bt_ld,
+                      topk_pages=wl.topk_pages, bos=wl.bos, eos=wl.eos,
+                      scale=wl.softmax_scale, num_splits=wl.num_splits,
+                      selection="gauss", alibi_slopes=slopes, gauss_cap=cap,
+                      gauss_mixture=mixture)
+    poison(d)
+    for t in (d.k_var, d.mu, d.var, d.tau_hat, d.entmax_scratch):
+        t.fill_(float("nan"))
+    d.rebuild_stats(cache, bt, sl)
+    d.gauss_select(q, bt, sl)
+    d.attend(q, cache, bt, sl)
+    d.merge()
+    torch.cuda.synchronize()
+    cb = bits(cache)
+    qd = q_cpu.double().numpy()
+    scale = wl.softmax_scale
+    _, _, kmean = oracle.page_stats(cb, wl.block_table, wl.seq_lens, wl.P)
+    kvar = oracle.page_var(cb, wl.block_table, wl.seq_lens, wl.P)
+    used = W.referenced_blocks(wl)
+    gv = d.k_var.cpu().numpy()[used].astype(np.float64)
+    ov = kvar[used]
+    assert np.all(np.abs(gv - ov) <= 1e-5 * ov + 1e-6), \
+        f"page variance err {np.abs(gv - ov).max()}"
+    sl64 = None if slopes_np is None else np.asarray(slopes_np, np.float32).astype(np.float64)
+    mu_o, var_o = oracle.gauss_moments(qd, kmean, kvar, wl.block_table, wl.seq_lens, wl.P,
+                                       scale, alibi=sl64, ld=wl.bt_ld)
+    g_mu, g_var = d.mu.cpu().numpy(), d.var.cpu().numpy()
+    g_est, g_tau = d.est.cpu().numpy(), d.tau_hat.cpu().numpy()
+    sel_idx, sel_cnt = d.sel_idx.cpu().numpy(), d.sel_cnt.cpu().numpy()
+    check_sel_blk(d.sel_blk.cpu().numpy(), sel_idx, wl.block_table)
+    out, etau = d.out.cpu().numpy(), d.entmax_tau().cpu().numpy()
+    N_all = wl.pages()
+    if rows is None:
+        rows = [(b, i) for b in range(wl.B) for i in range(wl.H_q)]
+    exempt, worst, counts = 0, 0.0, []
+    for b, i in rows:
+        S, N = int(wl.seq_lens[b]), int(N_all[b])
+        h = i // wl.G
+        cnt = int(sel_cnt[b, i])
+        assert 0 < cnt <= d.k_cap and np.all(sel_idx[b, i, cnt:] == -1), f"({b},{i}) count"
+        counts.append(cnt)
+        n = page_rows(S, wl.P, N)
+        blk = wl.block_table[b, :N]
+        sd = np.sqrt(kvar[blk, h])
+        k1 = scale * ((np.abs(kmean[blk, h]) + sd) @ np.abs(qd[b, i]))
+        q2 = scale * scale * float(qd[b, i] @ qd[b, i])
+        bias = np.zeros(N)
+        if sl64 is not None:
+            bias = sl64[i] * (np.arange(N) * wl.P + 0.5 * (n - 1) - (S - 1))
+        exempt += check_gauss_row(g_mu[b, i, :N], g_var[b, i, :N], g_est[b, i, :N],
+                                  g_tau[b, i], sel_idx[b, i, :cnt], n, d.mixture, wl.bos,
+                                  wl.eos, d.k_cap, mu_o[b, i, :N], var_o[b, i, :N], k1, q2,
+                                  bias, (b, i))
+        o, t = oracle.attend_entmax15(qd[b, i], cb, h, wl.block_table[b], S,
+                                      sel_idx[b, i, :cnt], scale,
+                                      slope=None if sl64 is None else sl64[i])
+        assert not np.any(np.isnan(out[b, i])), f"NaN output ({b},{i})"
+        e = np.abs(out[b, i].astype(np.float64) - o).max()
+        worst = max(worst, e)
+        assert e <= OUT_ATOL, f"gauss out ({b},{i}) err {e}"
+        assert abs(float(etau[b, i]) - t) <= 1e-4 * max(1.0, abs(t)), \
+            f"entmax tau ({b},{i}) {etau[b, i]} vs {t}"
+    return worst, exempt, counts
+
+
+@pytest.mark.parametrize("case", GAUSS_CASES, ids=[f"gauss{c[0]}" for c in GAUSS_CASES])
+def test_gauss_step(case):
+    (seed, B, H_q, H_kv, D, P, maxp, bos, eos, ns, alibi, mixture, cap, scale) = case
+    say(f"[gpu] Gaussian-aware case {case}")
+    wl = W.small_case(seed=seed, B=B, H_q=H_q, H_kv=H_kv, D=D, P=P, max_pages=maxp,
+                      bos=bos, eos=eos, num_splits=ns)
+    if scale is not None:
+        wl.scale = scale
+    from sparse_kv_cache_amd.decode import alibi_slopes
+    slopes = alibi_slopes(H_q, device="cpu").numpy() if alibi else None
+    worst, ex, counts = run_gauss_case(wl, W.make_cache(wl), W.make_queries(wl), slopes,
+                                       mixture, cap)
+    say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}, pages selected "
+        f"{min(counts)}..{max(counts)} of up to {int(wl.pages().max())}")
+
+
+@pytest.mark.parametrize("alibi", [False, True])
+def test_gauss_degenerate_pages(alibi):
+    """A zero cache (every variance 0, every mean 0: equal estimates without
+    ALiBi), one-token and exactly-full requests."""
+    say(f"[gpu] Gaussian-aware degenerate pages, alibi={alibi}")
+    wl = W.small_case(seed=139, B=3, H_q=4, H_kv=2, D=128, P=16, max_pages=6,
+                      num_splits=2, min_len=20)
+    wl.seq_lens = np.array([1, 16, 81], dtype=np.int32)
+    perm = np.random.default_rng(139).permutation(wl.num_blocks).astype(np.int32)
+    wl.block_table = perm[:wl.B * 6].reshape(wl.B, 6).copy()
+    from sparse_kv_cache_amd.decode import alibi_slopes
+    slopes = alibi_slopes(wl.H_q, device="cpu").numpy() if alibi else None
+    cache = torch.zeros((2, wl.num_blocks, 16, 2, 128), dtype=torch.bfloat16)
+    cache[1].normal_(generator=torch.Generator().manual_seed(5))
+    run_gauss_case(wl, cache, W.make_queries(wl), slopes)
+    run_gauss_case(wl, W.make_cache(wl), W.make_queries(wl), slopes)
 
 
 def test_all_equal_scores_tie_break_to_lower_index():

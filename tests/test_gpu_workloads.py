@@ -122,6 +122,32 @@ def test_long_context_entmax():
     say(f"  long_context 1.5-entmax: max |out - oracle| {worst:.2e}")
 
 
+def test_gqa_ragged_gauss():
+    """gqa_ragged with Gaussian-aware selection (NoPE heads: one Gaussian)."""
+    from test_gpu_kernels import run_gauss_case
+    wl = W.gqa_ragged()
+    say("[gpu] workload gqa_ragged, Gaussian-aware: generating")
+    cache = W.make_cache(wl, device="cuda")
+    rows = [(b, i) for b in range(wl.B) for i in range(0, wl.H_q, 3)]
+    worst, ex, counts = run_gauss_case(wl, cache, W.make_queries(wl), rows=rows)
+    say(f"  gqa_ragged Gaussian: max |out - oracle| {worst:.2e}, exempt rows {ex}, "
+        f"pages selected {min(counts)}..{max(counts)}")
+
+
+def test_long_context_gauss_alibi():
+    """long_context with ALiBi heads: page-mixture tau-hat, sampled heads."""
+    from test_gpu_kernels import run_gauss_case
+    from sparse_kv_cache_amd.decode import alibi_slopes
+    wl = W.long_context()
+    say("[gpu] workload long_context, Gaussian-aware with ALiBi: generating")
+    cache = W.make_cache(wl, device="cuda")
+    slopes = alibi_slopes(wl.H_q, device="cpu").numpy()
+    rows = [(0, i) for i in (0, 1, 9, 31, 40, 63)]
+    worst, ex, counts = run_gauss_case(wl, cache, W.make_queries(wl), slopes, rows=rows)
+    say(f"  long_context Gaussian ALiBi: max |out - oracle| {worst:.2e}, exempt rows {ex}, "
+        f"pages selected {min(counts)}..{max(counts)}")
+
+
 def test_high_batch_sampled_after_appends():
     wl = W.high_batch()
     say("[gpu] workload high_batch: generating 300k-block pool")
