@@ -49,9 +49,11 @@ def parse():
     ap.add_argument("--replicas", type=int, default=0,
                     help="rotation depth (0 = enough to exceed 1 GiB per cycle)")
     ap.add_argument("--splits", type=int, default=0, help="override num_splits")
-    ap.add_argument("--select", default="head", choices=["head", "group"],
-                    help="page level: select per query head, or once per kv head "
-                         "from the group's mean score (shared by the group)")
+    ap.add_argument("--select", default="head", choices=["head", "group", "gauss"],
+                    help="page level: top-k per query head, or once per kv head "
+                         "from the group's mean score (shared by the group), or the "
+                         "Gaussian-aware adaptive selection per query head (attends "
+                         "with 1.5-entmax)")
     ap.add_argument("--alibi", action="store_true",
                     help="page level: standard ALiBi slopes 2^(-8(i+1)/H_q) in scoring "
                          "and decode")
@@ -94,7 +96,7 @@ def unique_kv_bytes(wl, sel_idx, sel_cnt, seq_lens, H_sel):
 
 
 def kernel_bytes(wl, sel_idx, sel_cnt, seq_lens, num_splits, token_level,
-                 group_select=False, fused=False, entmax=False, k_cap=0):
+                 group_select=False, fused=False, entmax=False, gauss=False):
     """Algorithmic HBM bytes of each kernel of one step: the bytes the
     operation must move at least (unique selected K/V once, statistics, scores,
     indices, partials)."""
@@ -115,14 +117,26 @@ def kernel_bytes(wl, sel_idx, sel_cnt, seq_lens, num_splits, token_level,
             out["pagestats_update"] = int(B * Hkv * D * 2 * 2 * 2
                                           + B * Hkv * D * 2 * (P - 1)
                                           + B * Hkv * D * 8)
-        out["page_score"] = int((N * (Hkv * 8 * D + H_sel * 4 + 4)).sum() + B * Hq * D * 4)
-    out["page_topk"] = int((N * H_sel * 4).sum() + cnt * 4)
+            if gauss:      # the tail page's rows again, its mean, its variance
+                out["pagestats_update"] += int(B * Hkv * D * (2 * P + 8))
+        if gauss:
+            # mean + variance rows (fp32) once per page-head, q, mu + var out
+            out["gauss_moments"] = int((N * (Hkv * 8 * D + Hq * 8)).sum() + B * Hq * D * 4)
+        else:
+            out["page_score"] = int((N * (Hkv * 8 * D + H_sel * 4 + 4)).sum()
+                                    + B * Hq * D * 4)
+    if gauss:
+        # mu + var in, estimates out, tau-hat, selection (indices and blocks)
+        out["gauss_select"] = int((N * Hq * 12).sum() + B * Hq * 4 + cnt * 8 + B * Hq * 4)
+    else:
+        out["page_topk"] = int((N * H_sel * 4).sum() + cnt * 4)
     if entmax:
-        # K of the selected pages once, the logits scratch written and read,
-        # the partials; V is read only for 16-row groups in the support, which
-        # depends on the data and is left out (the GB/s is a lower bound)
+        # K of the selected pages once, the logits of the selected rows written
+        # and read, the partials; V is read only for 16-row groups in the
+        # support, which depends on the data and is left out (the GB/s is a
+        # lower bound)
         out["sparse_paged_decode"] = int(kv // 2 + B * Hq * D * 4 + cnt * 4
-                                         + 2 * B * Hq * k_cap * P * 4
+                                         + 2 * cnt * P * 4
                                          + B * Hq * num_splits * (D + 1) * 4)
         out["lse_merge"] = int(B * Hq * num_splits * (D + 1) * 4 + B * Hq * (D + 1) * 4)
     elif fused:   # merged in-block: the merged output instead of the partials
@@ -172,7 +186,8 @@ def profiled_traffic(workload):
 
 # ------------------------------------------------------------ cpu baseline
 
-def cpu_baseline(wl, cache_bits, q, seq_lens, seconds, token_level, hh_bits=None):
+def cpu_baseline(wl, cache_bits, q, seq_lens, seconds, token_level, hh_bits=None,
+                 gauss=False, slopes=None, k_cap=0):
     """The float64 oracle on a bounded sample of requests (whole step for
     those requests), scaled to steps/s of the full batch."""
     import oracle
@@ -201,6 +216,34 @@ def cpu_baseline(wl, cache_bits, q, seq_lens, seconds, token_level, hh_bits=None
             rows_done += 1
             b += 1
         sample = f"{rows_done} request-steps of the token-level step (1 of {wl.B} requests each)"
+    elif gauss:
+        st_cache = {}
+        sl64 = None if slopes is None else np.asarray(slopes, np.float32).astype(np.float64)
+        while t_used < seconds and reps < 10_000:
+            bb = b % wl.B
+            bt, sl = wl.block_table[bb:bb + 1], seq_lens[bb:bb + 1]
+            if bb not in st_cache:
+                st_cache[bb] = (oracle.page_stats(cache_bits, bt, sl, wl.P)[2],
+                                oracle.page_var(cache_bits, bt, sl, wl.P))
+            t0 = time.perf_counter()
+            S = int(sl[0])
+            N = (S + wl.P - 1) // wl.P
+            n = np.array([min(wl.P, S - p * wl.P) for p in range(N)], dtype=np.int32)
+            mu, var = oracle.gauss_moments(qd[bb:bb + 1], *st_cache[bb], bt, sl, wl.P,
+                                           wl.softmax_scale, alibi=sl64)
+            for i in range(wl.H_q):
+                tau = oracle.gauss_tau(mu[0, i, :N], var[0, i, :N], n, sl64 is not None)
+                sel = oracle.gauss_select(mu[0, i, :N], var[0, i, :N], n, tau, wl.bos,
+                                          wl.eos, k_cap)
+                oracle.attend_entmax15(qd[bb, i], cache_bits, i // wl.G, bt[0], S, sel,
+                                       wl.softmax_scale,
+                                       slope=None if sl64 is None else sl64[i])
+            t_used += time.perf_counter() - t0
+            reps += 1
+            rows_done += 1
+            b += 1
+        sample = (f"{rows_done} request-steps of moments+tau-hat+select+entmax attend "
+                  f"(1 of {wl.B} requests each, statistics prebuilt)")
     else:
         st_cache = {}
         while t_used < seconds and reps < 10_000:
@@ -260,11 +303,13 @@ def main():
         R = 1
     caches = [cache0] + [cache0.clone() for _ in range(R - 1)]
     group = args.select == "group" and not token_level
+    gauss = args.select == "gauss" and not token_level
     slopes = alibi_slopes(wl.H_q, dev) if (args.alibi and not token_level) else None
-    entmax = args.attention == "entmax15" and not token_level
+    entmax = (args.attention == "entmax15" or gauss) and not token_level
     decs = [SparseDecoder.for_workload(wl, device=dev, group_select=group,
                                        alibi_slopes=slopes, fuse_merge=not args.no_fuse,
-                                       attention="entmax15" if entmax else "softmax")
+                                       attention="entmax15" if entmax else "softmax",
+                                       selection="gauss" if gauss else "topk")
             for _ in range(R)]
     fused = decs[0].fused
     in_decode = decs[0].select_in_decode
@@ -305,10 +350,14 @@ def main():
     copy_gbps = 2 * copy_bytes / (min(copy_ms) * 1e-3) / 1e9
     del csrc, cdst
 
-    names = (["pagestats_update"] if wl.steps > 1 else []) + \
-        (["h2o_accumulate"] if token_level else [] if one_launch else ["page_score"]) + \
-        (["sparse_page_decode"] if one_launch else ["sparse_select_decode"] if in_decode else
-         ["page_topk", "sparse_paged_decode"] + ([] if fused else ["lse_merge"]))
+    if gauss:
+        names = (["pagestats_update"] if wl.steps > 1 else []) + \
+            ["gauss_moments", "gauss_select", "sparse_paged_decode", "lse_merge"]
+    else:
+        names = (["pagestats_update"] if wl.steps > 1 else []) + \
+            (["h2o_accumulate"] if token_level else [] if one_launch else ["page_score"]) + \
+            (["sparse_page_decode"] if one_launch else ["sparse_select_decode"] if in_decode
+             else ["page_topk", "sparse_paged_decode"] + ([] if fused else ["lse_merge"]))
 
     def enqueue(i, name):
         """Enqueue kernel `name` of step i (replica i % R, sequence step i % steps)."""
@@ -325,6 +374,10 @@ def main():
             d.score(q, bt, sl)
         elif name == "page_topk":
             d.select(sl, bt)
+        elif name == "gauss_moments":
+            d.moments(q, bt, sl)
+        elif name == "gauss_select":
+            d.select_gauss(sl, bt)
         elif name == "sparse_paged_decode":
             d.attend(q, c, bt, sl)
         elif name == "sparse_select_decode":
@@ -402,7 +455,7 @@ def main():
         del g
 
     kb, upages = kernel_bytes(wl, sel_idx, sel_cnt, sl_last, wl.num_splits, token_level,
-                              group, fused, entmax, decs[0].k_cap)
+                              group, fused, entmax, gauss)
     if one_launch:
         # the statistics read for scoring (scores and selection stay in LDS)
         # plus the merged decode; q counted once
@@ -444,11 +497,15 @@ def main():
                    "D": wl.D, "page_size": wl.P, "topk_pages": wl.topk_pages,
                    "topk_frac": wl.topk_frac, "num_splits": wl.num_splits,
                    "mean_seq_len": float(np.mean(sl_last)), "replicas": R,
-                   "selection": ("kv_head" if (group or token_level) else "query_head"),
+                   "selection": ("kv_head" if (group or token_level) else
+                                 "gauss_query_head" if gauss else "query_head"),
+                   "gauss_tau": (None if not gauss else
+                                 "page_mixture" if decs[0].mixture else "single"),
                    "alibi": slopes is not None, "merge_in_decode": fused,
                    "select_in_decode": in_decode, "one_launch_step": one_launch,
                    "attention": "entmax15" if entmax else "softmax",
                    "parallelism": "single-gpu"},
+        "selected_pages_per_head": round(float(sel_cnt.mean()), 2),
         "effective_GBps": round(step_bytes / (gpu_ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(step_bytes / (gpu_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "step_bytes": int(step_bytes), "unique_page_heads": int(upages),
@@ -462,8 +519,10 @@ def main():
         from sparse_kv_cache_amd.workloads import bf16_bits
         cb = bf16_bits(caches[last % R])
         hb = bf16_bits(hh0) if token_level else None
-        result["cpu_baseline"] = cpu_baseline(wl, cb, q.cpu(), sl_last,
-                                              args.cpu_seconds, token_level, hb)
+        result["cpu_baseline"] = cpu_baseline(
+            wl, cb, q.cpu(), sl_last, args.cpu_seconds, token_level, hb,
+            gauss=gauss, slopes=None if slopes is None else slopes.cpu().numpy(),
+            k_cap=decs[0].k_cap)
     print(json.dumps(result), flush=True)
     return 0
 

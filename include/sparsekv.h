@@ -368,8 +368,8 @@ int gauss_moments(const float *q, int B, int H_q, int H_kv, int D,
  *     mixture != 0:  sum_p n_p E[(X_p - tau)_+^2] = 1, X_p ~ N(mu_p/2, var_p/4);
  *     mixture == 0:  S E[(X - tau)_+^2] = 1, X ~ N(m/2, v/4) with m, v the
  *                    pooled mean and variance of the S tokens of the pages;
- *   (Newton in fp64 from below).  est_p = mu_p + sqrt(var_p) sqrt(2 ln n_p)
- *   (mu_p for n_p = 1), fp32.  Selected: the reserved first reserved_bos and
+ *   (safeguarded Newton steps on log F in fp64).
+ *   est_p = mu_p + sqrt(var_p) sqrt(2 ln n_p) (mu_p for n_p = 1), fp32.  Selected: the reserved first reserved_bos and
  *   last reserved_eos pages, and every other page with est_p / 2 > tau-hat
  *   (fp32 comparison); at most k_cap pages (largest estimates, ties to the
  *   lower index), at least one.

@@ -31,11 +31,11 @@
 // Arithmetic.  For X ~ N(m, s^2) and d = m - tau, a = d / s:
 //   E[(X - tau)_+^2] = (d^2 + s^2) Phi(a) + d s phi(a),
 //   E[(X - tau)_+]   = d Phi(a) + s phi(a)   (minus half the derivative).
-// f(tau) = sum n_p E[(X_p - tau)_+^2] - 1 is convex and falling, and
-// tau0 = max_p (m_p - 1 / sqrt(n_p)) has f(tau0) >= 0 (Jensen), so Newton
-// steps from tau0 rise monotonically to the root.  The solve runs in fp64
-// (the two terms of the tail expectation cancel); the estimates and the
-// comparison with tau-hat are fp32.
+// F(tau) = sum n_p E[(X_p - tau)_+^2] falls with tau, and tau0 =
+// max_p (m_p - 1 / sqrt(n_p)) has F(tau0) >= 1 (Jensen); the root of F = 1 is
+// found by safeguarded Newton steps on log F from tau0 (solve_tau).  The solve
+// runs in fp64 (the two terms of the tail expectation cancel); the estimates
+// and the comparison with tau-hat are fp32.
 #include <math.h>
 
 #include "skv_device.h"
@@ -184,17 +184,20 @@ __global__ __launch_bounds__(256) void gauss_moments_kernel(
 
 // -------------------------------------------------------- tau-hat + select
 
-__device__ __forceinline__ double block_sum_d(double x, double* red) {
+// Sums of two doubles over the block; red holds 2 * (waves) doubles.
+__device__ __forceinline__ void block_sum2_d(double& x, double& y, double* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  if (lane == 0) red[wave] = x;
+  for (int o = 32; o > 0; o >>= 1) {
+    x += __shfl_xor(x, o);
+    y += __shfl_xor(y, o);
+  }
+  if (lane == 0) { red[2 * wave] = x; red[2 * wave + 1] = y; }
   __syncthreads();
-  double t = 0.0;
-  for (int w = 0; w < nw; ++w) t += red[w];
+  x = 0.0; y = 0.0;
+  for (int w = 0; w < nw; ++w) { x += red[2 * w]; y += red[2 * w + 1]; }
   __syncthreads();
-  return t;
 }
 
 __device__ __forceinline__ double block_max_d(double x, double* red) {
@@ -210,16 +213,19 @@ __device__ __forceinline__ double block_max_d(double x, double* red) {
   return t;
 }
 
-// (E[(X - tau)_+^2], E[(X - tau)_+]) for X ~ N(m, s^2).
+// (E[(X - tau)_+^2], E[(X - tau)_+]) for X ~ N(m, s^2).  Beyond 9 standard
+// deviations the Gaussian tail (below 1e-18 of the scale) is dropped: a page
+// far below tau adds nothing, one far above adds d^2 + s^2 and d.
 __device__ __forceinline__ void gauss_excess(double m, double s, double tau, double& e2,
                                              double& e1) {
   const double d = m - tau;
-  if (!(s > 0.0)) {
+  if (!(s > 0.0) || d >= 9.0 * s) {
     const double dp = d > 0.0 ? d : 0.0;
-    e2 = dp * dp;
+    e2 = dp * dp + (dp > 0.0 ? s * s : 0.0);
     e1 = dp;
     return;
   }
+  if (d <= -9.0 * s) { e2 = 0.0; e1 = 0.0; return; }
   const double a = d / s;
   const double Phi = 0.5 * erfc(-a * 0.70710678118654752440);     // 1 / sqrt(2)
   const double phi = exp(-0.5 * a * a) * 0.39894228040143267794;  // 1 / sqrt(2 pi)
@@ -229,6 +235,30 @@ __device__ __forceinline__ void gauss_excess(double m, double s, double tau, dou
   if (e1 < 0.0) e1 = 0.0;
 }
 
+// Root of F(tau) = 1, F(tau) = sum n E[(X - tau)_+^2] with F' = -2 sum n
+// E[(X - tau)_+] (eval returns F and that sum), from lo with F(lo) >= 1.
+// Newton steps on log F: for one Gaussian log F is concave (the threshold
+// moments of a log-concave density are log-concave), so after the first
+// step the iterates fall monotonically onto the root in a few steps; a
+// bracket [lo, hi] with F(lo) >= 1 > F(hi) catches anything else (a
+// mixture, an underflowed F) with a bisection.  The result is uniform across
+// the callers when eval is.
+template <class Eval>
+__device__ double solve_tau(double lo, Eval eval) {
+  double hi = INFINITY, tau = lo;
+  for (int it = 0; it < kMaxNewton; ++it) {
+    double F, G;
+    eval(tau, F, G);
+    if (F >= 1.0) lo = tau; else hi = tau;
+    double next = (F > 0.0 && G > 0.0) ? tau + log(F) * F / (2.0 * G) : NAN;
+    if (!(next >= lo && next <= hi))
+      next = hi < INFINITY ? 0.5 * (lo + hi) : lo + fmax(1.0, fabs(lo));
+    if (!(fabs(next - tau) > 1e-13 * fmax(1.0, fabs(tau)))) return next;
+    tau = next;
+  }
+  return tau;
+}
+
 template <int BLOCK, int ITEMS>
 __global__ __launch_bounds__(BLOCK) void gauss_select_kernel(
     const float* __restrict__ mu, const float* __restrict__ var, int64_t ld, int H_q,
@@ -236,7 +266,7 @@ __global__ __launch_bounds__(BLOCK) void gauss_select_kernel(
     int64_t bt_ld, int mixture, int bos, int eos, int k_cap, float* __restrict__ tau_out,
     float* est, int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt,
     int32_t* __restrict__ sel_blk) {
-  __shared__ double red[BLOCK / 64];
+  __shared__ double red[2 * (BLOCK / 64)];
   __shared__ int ired[BLOCK / 64];
   const int64_t row = blockIdx.x;
   const int b = static_cast<int>(row / H_q);
@@ -254,31 +284,27 @@ __global__ __launch_bounds__(BLOCK) void gauss_select_kernel(
   auto m_of = [&](int p) { return 0.5 * static_cast<double>(mr[p]); };
   auto s_of = [&](int p) { return 0.5 * sqrt(static_cast<double>(fmaxf(vr[p], 0.0f))); };
 
+  __shared__ double s_tau;
   double tau = -INFINITY;
   if (N > 0) {
     if (mixture) {
       double t0 = -INFINITY;
       for (int p = tid; p < N; p += BLOCK)
         t0 = fmax(t0, m_of(p) - 1.0 / sqrt(static_cast<double>(rows_of(p))));
-      tau = block_max_d(t0, red);
-      for (int it = 0; it < kMaxNewton; ++it) {
+      t0 = block_max_d(t0, red);
+      tau = solve_tau(t0, [&](double t, double& F, double& G) {
         double f = 0.0, g = 0.0;
         for (int p = tid; p < N; p += BLOCK) {
           double e2, e1;
-          gauss_excess(m_of(p), s_of(p), tau, e2, e1);
+          gauss_excess(m_of(p), s_of(p), t, e2, e1);
           const double n = static_cast<double>(rows_of(p));
           f = fma(n, e2, f);
           g = fma(n, e1, g);
         }
-        f = block_sum_d(f, red);
-        g = block_sum_d(g, red);
-        const double step = (f - 1.0) / (2.0 * g);
-        if (!(step > 1e-13 * fmax(1.0, fabs(tau)))) {
-          if (step > 0.0) tau += step;
-          break;
-        }
-        tau += step;
-      }
+        block_sum2_d(f, g, red);
+        F = f;
+        G = g;
+      });
     } else {
       // pooled mean, then the pooled variance around it (law of total
       // variance, no cancellation)
@@ -288,28 +314,29 @@ __global__ __launch_bounds__(BLOCK) void gauss_select_kernel(
         sn += n;
         sm = fma(n, static_cast<double>(mr[p]), sm);
       }
-      sm = block_sum_d(sm, red);
-      const double Sd = block_sum_d(sn, red);          // valid tokens of the N pages
+      block_sum2_d(sn, sm, red);
+      const double Sd = sn;                             // valid tokens of the N pages
       const double gm = sm / Sd;
-      double sv = 0.0;
+      double sv = 0.0, unused = 0.0;
       for (int p = tid; p < N; p += BLOCK) {
         const double dm = static_cast<double>(mr[p]) - gm;
         sv = fma(static_cast<double>(rows_of(p)),
                  static_cast<double>(fmaxf(vr[p], 0.0f)) + dm * dm, sv);
       }
-      sv = block_sum_d(sv, red);
-      const double m = 0.5 * gm, s = 0.5 * sqrt(sv / Sd);
-      tau = m - 1.0 / sqrt(Sd);
-      for (int it = 0; it < kMaxNewton; ++it) {       // uniform across the block
-        double e2, e1;
-        gauss_excess(m, s, tau, e2, e1);
-        const double step = (Sd * e2 - 1.0) / (2.0 * Sd * e1);
-        if (!(step > 1e-13 * fmax(1.0, fabs(tau)))) {
-          if (step > 0.0) tau += step;
-          break;
-        }
-        tau += step;
+      block_sum2_d(sv, unused, red);
+      // one scalar solve: wave 0 runs it, the block reads the result
+      if (tid < 64) {
+        const double m = 0.5 * gm, s = 0.5 * sqrt(sv / Sd);
+        const double t = solve_tau(m - 1.0 / sqrt(Sd), [&](double t, double& F, double& G) {
+          double e2, e1;
+          gauss_excess(m, s, t, e2, e1);
+          F = Sd * e2;
+          G = Sd * e1;
+        });
+        if (tid == 0) s_tau = t;
       }
+      __syncthreads();
+      tau = s_tau;
     }
   }
   const float tau_f = static_cast<float>(tau);
@@ -467,12 +494,23 @@ extern "C" int gauss_select(const float* mu, const float* var, int64_t ld, int B
   launch_select<BL, IT>(rows, stream, mu, var, ld, H_q, seq_lens, page_size,           \
                         block_table, bt_ld, mix, reserved_bos, reserved_eos, k_cap, tau, \
                         est, sel_idx, sel_cnt, sel_blk)
-  if (bt_ld <= 1024) SKV_GSEL(256, 4);
-  else if (bt_ld <= 2048) SKV_GSEL(512, 4);
-  else if (bt_ld <= 4096) SKV_GSEL(1024, 4);
-  else if (bt_ld <= 8192) SKV_GSEL(1024, 8);
-  else if (bt_ld <= 16384) SKV_GSEL(1024, 16);
-  else SKV_GSEL(1024, 32);
+  if (rows < 1024) {
+    // few rows, each latency-bound: wide blocks, short loops per thread
+    if (bt_ld <= 1024) SKV_GSEL(256, 4);
+    else if (bt_ld <= 2048) SKV_GSEL(512, 4);
+    else if (bt_ld <= 4096) SKV_GSEL(1024, 4);
+    else if (bt_ld <= 8192) SKV_GSEL(1024, 8);
+    else if (bt_ld <= 16384) SKV_GSEL(1024, 16);
+    else SKV_GSEL(1024, 32);
+  } else {
+    // rows enough to fill the chip: 256-thread blocks, several per CU
+    if (bt_ld <= 1024) SKV_GSEL(256, 4);
+    else if (bt_ld <= 2048) SKV_GSEL(256, 8);
+    else if (bt_ld <= 4096) SKV_GSEL(256, 16);
+    else if (bt_ld <= 8192) SKV_GSEL(512, 16);
+    else if (bt_ld <= 16384) SKV_GSEL(1024, 16);
+    else SKV_GSEL(1024, 32);
+  }
 #undef SKV_GSEL
   SKV_CHECK_LAUNCH();
 }

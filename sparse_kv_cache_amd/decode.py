@@ -177,15 +177,23 @@ class SparseDecoder:
             page_var_update(kv_cache, self.k_mean, self.k_var, block_table, seq_lens,
                             tail_only=True, stream=stream)
 
-    def gauss_select(self, q, block_table, seq_lens, stream=None):
-        """Moments, tau-hat and the adaptive selection (Gaussian-aware)."""
+    def moments(self, q, block_table, seq_lens, stream=None):
+        """Gaussian moments of every page's logits."""
         gauss_moments(q, self.k_mean, self.k_var, block_table, seq_lens, self.P,
                       self.scale, self.mu, self.var, alibi_slopes=self.alibi,
                       stream=stream)
+
+    def select_gauss(self, seq_lens, block_table, stream=None):
+        """tau-hat and the adaptive selection from the moments."""
         gauss_select(self.mu, self.var, seq_lens, self.P, block_table, self.mixture,
                      self.k_cap, self.est, self.sel_idx, self.sel_cnt, tau=self.tau_hat,
                      sel_blk=self.sel_blk if self.use_sel_blk else None,
                      reserved_bos=self.bos, reserved_eos=self.eos, stream=stream)
+
+    def gauss_select(self, q, block_table, seq_lens, stream=None):
+        """Moments, tau-hat and the adaptive selection (Gaussian-aware)."""
+        self.moments(q, block_table, seq_lens, stream)
+        self.select_gauss(seq_lens, block_table, stream)
 
     def score(self, q, block_table, seq_lens, stream=None):
         if self.token_level:
