@@ -130,11 +130,15 @@ def kernel_bytes(wl, sel_idx, sel_cnt, seq_lens, num_splits, token_level,
         out["gauss_select"] = int((N * Hq * 12).sum() + B * Hq * 4 + cnt * 8 + B * Hq * 4)
     else:
         out["page_topk"] = int((N * H_sel * 4).sum() + cnt * 4)
-    if entmax:
-        # K of the selected pages once, the logits of the selected rows written
-        # and read, the partials; V is read only for 16-row groups in the
-        # support, which depends on the data and is left out (the GB/s is a
-        # lower bound)
+    if entmax and fused:
+        # K of the selected pages once and the merged output; V is read only
+        # for 16-row groups in the support, which depends on the data and is
+        # left out (the GB/s is a lower bound)
+        out["sparse_paged_decode"] = int(kv // 2 + B * Hq * D * 4 + cnt * 4
+                                         + B * Hq * (D + 1) * 4)
+    elif entmax:
+        # as above, plus the logits of the selected rows written and read and
+        # the partials
         out["sparse_paged_decode"] = int(kv // 2 + B * Hq * D * 4 + cnt * 4
                                          + 2 * cnt * P * 4
                                          + B * Hq * num_splits * (D + 1) * 4)
@@ -311,7 +315,7 @@ def main():
                                        attention="entmax15" if entmax else "softmax",
                                        selection="gauss" if gauss else "topk")
             for _ in range(R)]
-    fused = decs[0].fused
+    fused = decs[0].fused or decs[0].entmax_fused
     in_decode = decs[0].select_in_decode
     one_launch = decs[0].score_in_decode
     new_kv = [W.make_new_kv(wl, s, device=dev) for s in range(min(wl.steps, 64))] \
@@ -352,7 +356,8 @@ def main():
 
     if gauss:
         names = (["pagestats_update"] if wl.steps > 1 else []) + \
-            ["gauss_moments", "gauss_select", "sparse_paged_decode", "lse_merge"]
+            ["gauss_moments", "gauss_select", "sparse_paged_decode"] + \
+            ([] if fused else ["lse_merge"])
     else:
         names = (["pagestats_update"] if wl.steps > 1 else []) + \
             (["h2o_accumulate"] if token_level else [] if one_launch else ["page_score"]) + \

@@ -321,6 +321,27 @@ int entmax15_paged_decode(const float *q, int B, int H_q, int H_kv, int D,
                           int64_t scratch_floats, hipStream_t stream);
 
 /*
+ * entmax15_paged_decode_merged -- the same attention in one launch, merged:
+ * one block per query row computes the logits of its selected rows (kept in
+ * LDS when k_cap * page_size <= 8192, else in scratch), tau, and
+ * out = sum_t p_t v_t / sum_t p_t, with lse_out = ln sum_t p_t (about 0).
+ *   Arguments as entmax15_paged_decode, without the partials and splits;
+ *   out      fp32 [B, H_q, D];  lse_out fp32 [B, H_q] or NULL;
+ *   tau_out  fp32 [B, H_q] or NULL (tau of each row, -inf with no valid row);
+ *   scratch  fp32 device buffer of >= B * H_q * k_cap * page_size floats when
+ *            k_cap * page_size > 8192, else ignored (may be NULL).
+ */
+int entmax15_paged_decode_merged(const float *q, int B, int H_q, int H_kv, int D,
+                                 const uint16_t *kv_cache, int64_t num_blocks,
+                                 int page_size, const int32_t *block_table,
+                                 int64_t bt_ld, const int32_t *seq_lens,
+                                 const int32_t *sel_idx, const int32_t *sel_cnt,
+                                 const int32_t *sel_blk, int k_cap, int H_sel,
+                                 float scale, const float *alibi_slopes, float *out,
+                                 float *lse_out, float *tau_out, float *scratch,
+                                 int64_t scratch_floats, hipStream_t stream);
+
+/*
  * Gaussian-aware adaptive selection.  [EKV "How it works": pages keep mean /
  * std key statistics; each page's scores are modelled as a Gaussian; the
  * distributional entmax constraint gives the threshold tau-hat (a page
@@ -328,7 +349,8 @@ int entmax15_paged_decode(const float *q, int B, int H_q, int H_kv, int D,
  * estimated maximum can cross tau-hat is selected, so the number of pages
  * adapts.  EKV "Quick start": the Gaussian-aware decode runs alpha = 1.5.]
  * A step: pagestats_update, page_var_update, gauss_moments, gauss_select,
- * entmax15_paged_decode over the selection (H_sel = H_q), lse_merge.
+ * entmax15_paged_decode_merged over the selection (H_sel = H_q) (or
+ * entmax15_paged_decode, then lse_merge).
  *
  * page_var_update -- population variance of the keys of a page per (kv head,
  * dim), over its n = min(P, S_b - p P) valid rows, around k_mean.

@@ -21,7 +21,8 @@ __all__ = [
     "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
     "h2o_accumulate", "h2o_scratch_floats", "entmax15_paged_decode",
     "entmax_scratch_floats", "sparse_select_decode", "sparse_page_decode",
-    "page_var_update", "gauss_moments", "gauss_select", "library_path",
+    "page_var_update", "gauss_moments", "gauss_select", "entmax15_paged_decode_merged",
+    "library_path",
     "load_library", "SparseKVError", "EXPORTED_SYMBOLS",
 ]
 
@@ -34,12 +35,14 @@ EXPORTED_SYMBOLS = (
     "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
     "h2o_accumulate", "h2o_scratch_floats", "entmax15_paged_decode",
     "entmax_scratch_floats", "sparse_select_decode", "sparse_page_decode",
-    "page_var_update", "gauss_moments", "gauss_select", "sparsekv_last_error",
+    "page_var_update", "gauss_moments", "gauss_select", "entmax15_paged_decode_merged",
+    "sparsekv_last_error",
 )
 _INT_RETURNING = ("pagestats_update", "page_score", "page_score_group", "page_topk",
                   "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
                   "h2o_accumulate", "entmax15_paged_decode", "sparse_select_decode",
-                  "sparse_page_decode", "page_var_update", "gauss_moments", "gauss_select")
+                  "sparse_page_decode", "page_var_update", "gauss_moments", "gauss_select",
+                  "entmax15_paged_decode_merged")
 
 
 class SparseKVError(RuntimeError):
@@ -82,6 +85,8 @@ def load_library():
     lib.h2o_scratch_floats.restype = ctypes.c_int64
     lib.entmax15_paged_decode.argtypes = [V, I, I, I, I, V, L, I, V, L, V, V, V, V, I, I,
                                           F, I, V, V, V, V, L, V]
+    lib.entmax15_paged_decode_merged.argtypes = [V, I, I, I, I, V, L, I, V, L, V, V, V, V,
+                                                 I, I, F, V, V, V, V, V, L, V]
     lib.page_var_update.argtypes = [V, L, I, I, I, V, V, V, L, V, I, I, V]
     lib.gauss_moments.argtypes = [V, I, I, I, I, V, V, V, L, V, I, F, V, V, V, L, V]
     lib.gauss_select.argtypes = [V, V, L, I, I, V, I, V, L, I, I, I, I, V, V, V, V, V, V]
@@ -374,6 +379,43 @@ def entmax15_paged_decode(q, kv_cache, block_table, seq_lens, sel_idx, sel_cnt, 
         block_table.shape[1], _ptr(seq_lens), _ptr(sel_idx), _ptr(sel_cnt), _ptr(sel_blk),
         sel_idx.shape[2], H_sel, float(scale), ns, _ptr(alibi_slopes), _ptr(o_part),
         _ptr(lse_part), _ptr(scratch), scratch.numel(), _stream(stream)))
+
+
+def entmax15_paged_decode_merged(q, kv_cache, block_table, seq_lens, sel_idx, sel_cnt,
+                                 scale, out, lse_out=None, tau_out=None, scratch=None,
+                                 sel_blk=None, alibi_slopes=None, stream=None):
+    """1.5-entmax attention over the selected pages in one launch: out
+    [B, H_q, D] = sum p v / sum p; lse_out, tau_out [B, H_q] optional; scratch
+    (fp32, B * H_q * k_cap * P floats) only when k_cap * P > 8192."""
+    lib = load_library()
+    _check("q", q, torch.float32, 3)
+    dev = q.device
+    B, H_q, D = q.shape
+    _check("kv_cache", kv_cache, torch.bfloat16, 5, dev)
+    _, NB, P, H_kv, D2 = kv_cache.shape
+    if D2 != D:
+        raise ValueError("q and kv_cache head dims differ")
+    _check("block_table", block_table, torch.int32, 2, dev)
+    _check("seq_lens", seq_lens, torch.int32, 1, dev)
+    _check("sel_idx", sel_idx, torch.int32, 3, dev)
+    _check("sel_cnt", sel_cnt, torch.int32, 2, dev)
+    _check("sel_blk", sel_blk, torch.int32, 3, dev)
+    _check("out", out, torch.float32, 3, dev)
+    _check("lse_out", lse_out, torch.float32, 2, dev)
+    _check("tau_out", tau_out, torch.float32, 2, dev)
+    _check("scratch", scratch, torch.float32, 1, dev)
+    if tuple(out.shape) != (B, H_q, D):
+        raise ValueError("out must be [B, H_q, D]")
+    for n, t in (("lse_out", lse_out), ("tau_out", tau_out)):
+        if t is not None and tuple(t.shape) != (B, H_q):
+            raise ValueError(f"{n} must be [B, H_q]")
+    alibi_slopes = _alibi_arg(alibi_slopes, H_q, dev)
+    _rc("entmax15_paged_decode_merged", lib.entmax15_paged_decode_merged(
+        _ptr(q), B, H_q, H_kv, D, _ptr(kv_cache), NB, P, _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), _ptr(sel_idx), _ptr(sel_cnt), _ptr(sel_blk),
+        sel_idx.shape[2], sel_idx.shape[1], float(scale), _ptr(alibi_slopes), _ptr(out),
+        _ptr(lse_out), _ptr(tau_out), _ptr(scratch),
+        0 if scratch is None else scratch.numel(), _stream(stream)))
 
 
 def page_var_update(kv_cache, k_mean, k_var, block_table, seq_lens, tail_only=False,

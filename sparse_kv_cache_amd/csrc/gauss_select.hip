@@ -235,6 +235,34 @@ __device__ __forceinline__ void gauss_excess(double m, double s, double tau, dou
   if (e1 < 0.0) e1 = 0.0;
 }
 
+// A first guess of the single-Gaussian root: with a = (m - tau) / s the
+// constraint reads S s^2 psi(a) = 1, psi(a) = (1 + a^2) Phi(a) + a phi(a),
+// which behaves as 1 + a^2 for a >= 1, runs from 0.5 to about 1.9 on [0, 1],
+// and as 2 phi(a) / |a|^3 far below 0.  Newton steps correct the guess; it
+// only saves steps, and it never lies below the Jensen start.
+__device__ __forceinline__ double start_single(double m, double s, double S) {
+  if (!(s > 0.0)) return m - 1.0 / sqrt(S);
+  const double r = 1.0 / (S * s * s);
+  double a;
+  if (r >= 2.0) {
+    a = sqrt(r - 1.0);
+  } else if (r >= 0.5) {
+    a = (r - 0.5) / 1.42;
+  } else {
+    // 2 phi(x) / x^3 = r  ->  x^2 = 2 ln(2 / (sqrt(2 pi) r)) - 6 ln x
+    const double c = 2.0 * log(0.79788456080286535588 / r);   // 2 / sqrt(2 pi)
+    double x = sqrt(c > 1.0 ? c : 1.0);
+    for (int k = 0; k < 3; ++k) {
+      const double x2 = c - 6.0 * log(x > 1.0 ? x : 1.0);
+      x = sqrt(x2 > 0.0 ? x2 : 0.0);
+    }
+    a = -x;
+  }
+  const double t = m - a * s;
+  const double lo = m - 1.0 / sqrt(S);
+  return t > lo ? t : lo;
+}
+
 // Root of F(tau) = 1, F(tau) = sum n E[(X - tau)_+^2] with F' = -2 sum n
 // E[(X - tau)_+] (eval returns F and that sum), from lo with F(lo) >= 1.
 // Newton steps on log F: for one Gaussian log F is concave (the threshold
@@ -244,8 +272,8 @@ __device__ __forceinline__ void gauss_excess(double m, double s, double tau, dou
 // mixture, an underflowed F) with a bisection.  The result is uniform across
 // the callers when eval is.
 template <class Eval>
-__device__ double solve_tau(double lo, Eval eval) {
-  double hi = INFINITY, tau = lo;
+__device__ double solve_tau(double lo, double start, Eval eval) {
+  double hi = INFINITY, tau = start > lo ? start : lo;
   for (int it = 0; it < kMaxNewton; ++it) {
     double F, G;
     eval(tau, F, G);
@@ -259,6 +287,14 @@ __device__ double solve_tau(double lo, Eval eval) {
   return tau;
 }
 
+// Pages a mixture solve keeps in LDS: those whose Gaussian reaches within 9
+// standard deviations of the lower start tau0 (tau-hat never goes below it,
+// so the rest add nothing at any step).  Rows with more read the whole row
+// from memory at every step instead.
+constexpr int kAliveCap = 2048;
+
+// One block per (request, query head) row; entry p is handled by thread
+// p mod BLOCK in every pass.
 template <int BLOCK, int ITEMS>
 __global__ __launch_bounds__(BLOCK) void gauss_select_kernel(
     const float* __restrict__ mu, const float* __restrict__ var, int64_t ld, int H_q,
@@ -267,7 +303,8 @@ __global__ __launch_bounds__(BLOCK) void gauss_select_kernel(
     float* est, int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt,
     int32_t* __restrict__ sel_blk) {
   __shared__ double red[2 * (BLOCK / 64)];
-  __shared__ int ired[BLOCK / 64];
+  __shared__ int ired[BLOCK / 64 + 1];
+  __shared__ float al_m[kAliveCap], al_v[kAliveCap], al_n[kAliveCap];
   const int64_t row = blockIdx.x;
   const int b = static_cast<int>(row / H_q);
   const int S = seq_lens[b];
@@ -279,8 +316,8 @@ __global__ __launch_bounds__(BLOCK) void gauss_select_kernel(
   const float* vr = var + row * ld;
   float* er = est + row * ld;
   auto rows_of = [&](int p) { return S - p * P < P ? S - p * P : P; };
-  // The row (8 bytes a page) is re-read from cache on every Newton step: the
-  // fp64 tail expectations dominate, and registers stay free for them.
+  // The row (8 bytes a page) is read from cache by each pass (strided,
+  // coalesced): registers stay free for the fp64 tail expectations.
   auto m_of = [&](int p) { return 0.5 * static_cast<double>(mr[p]); };
   auto s_of = [&](int p) { return 0.5 * sqrt(static_cast<double>(fmaxf(vr[p], 0.0f))); };
 
@@ -292,14 +329,35 @@ __global__ __launch_bounds__(BLOCK) void gauss_select_kernel(
       for (int p = tid; p < N; p += BLOCK)
         t0 = fmax(t0, m_of(p) - 1.0 / sqrt(static_cast<double>(rows_of(p))));
       t0 = block_max_d(t0, red);
-      tau = solve_tau(t0, [&](double t, double& F, double& G) {
-        double f = 0.0, g = 0.0;
-        for (int p = tid; p < N; p += BLOCK) {
-          double e2, e1;
-          gauss_excess(m_of(p), s_of(p), t, e2, e1);
-          const double n = static_cast<double>(rows_of(p));
-          f = fma(n, e2, f);
-          g = fma(n, e1, g);
+      // the pages that can matter at any tau >= t0 go to an LDS list
+      auto alive = [&](int p) { return m_of(p) + 9.0 * s_of(p) > t0; };
+      int na = 0;
+      for (int p = tid; p < N; p += BLOCK) na += alive(p) ? 1 : 0;
+      int total;
+      int pos = skv::block_exclusive_scan(na, &total, ired);
+      const bool in_lds = total <= kAliveCap;
+      if (in_lds)
+        for (int p = tid; p < N; p += BLOCK)
+          if (alive(p)) {
+            al_m[pos] = mr[p];
+            al_v[pos] = fmaxf(vr[p], 0.0f);
+            al_n[pos] = static_cast<float>(rows_of(p));
+            ++pos;
+          }
+      __syncthreads();
+      const int count = in_lds ? total : N;
+      tau = solve_tau(t0, t0, [&](double t, double& F, double& G) {
+        double f = 0.0, g = 0.0, e2, e1;
+        for (int j = tid; j < count; j += BLOCK) {
+          // the LDS list, or the whole row from memory
+          const float mj = in_lds ? al_m[j] : mr[j];
+          const float vj = in_lds ? al_v[j] : fmaxf(vr[j], 0.0f);
+          const double nj = in_lds ? static_cast<double>(al_n[j])
+                                   : static_cast<double>(rows_of(j));
+          gauss_excess(0.5 * static_cast<double>(mj), 0.5 * sqrt(static_cast<double>(vj)), t,
+                       e2, e1);
+          f = fma(nj, e2, f);
+          g = fma(nj, e1, g);
         }
         block_sum2_d(f, g, red);
         F = f;
@@ -327,7 +385,8 @@ __global__ __launch_bounds__(BLOCK) void gauss_select_kernel(
       // one scalar solve: wave 0 runs it, the block reads the result
       if (tid < 64) {
         const double m = 0.5 * gm, s = 0.5 * sqrt(sv / Sd);
-        const double t = solve_tau(m - 1.0 / sqrt(Sd), [&](double t, double& F, double& G) {
+        const double t = solve_tau(m - 1.0 / sqrt(Sd), start_single(m, s, Sd),
+                                   [&](double t, double& F, double& G) {
           double e2, e1;
           gauss_excess(m, s, t, e2, e1);
           F = Sd * e2;

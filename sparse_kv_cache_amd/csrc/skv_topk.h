@@ -38,11 +38,51 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // (padded with -1) and, when bout is given, the selected pages' physical
 // blocks btr[p] to bout; returns the selected count (every thread).  out and
 // bout may point to global or LDS memory.  Ends with a block barrier.
+// The selection from keys already in registers: key[i] is the order key of
+// entry tid * ITEMS + i (entries outside the ranked window are ignored).
+template <int BLOCK, int ITEMS>
+__device__ int topk_row_keys(const uint32_t (&key)[ITEMS], int N, int topk_pages,
+                             double topk_frac, int bos, int eos,
+                             const int32_t* __restrict__ btr, int64_t bt_ld,
+                             int32_t* out, int32_t* bout, int k_cap);
+
 template <int BLOCK, int ITEMS>
 __device__ int topk_row(const float* __restrict__ srow, bool aligned16, int N,
                         int topk_pages, double topk_frac, int bos, int eos,
                         const int32_t* __restrict__ btr, int64_t bt_ld,
                         int32_t* out, int32_t* bout, int k_cap) {
+  const int lo = bos < N ? bos : N;
+  int hi = N - eos > 0 ? N - eos : 0;
+  if (hi < lo) hi = lo;
+  const int base = threadIdx.x * ITEMS;
+  uint32_t key[ITEMS];
+  constexpr bool kVec = ITEMS % 4 == 0;          // 16-byte pieces per thread
+  const bool vec = kVec && aligned16 && (base + ITEMS <= hi) && (base >= lo);
+  if (vec) {
+    if constexpr (kVec) {
+#pragma unroll
+      for (int i = 0; i < ITEMS; i += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(srow + base + i);
+        key[i] = order_key(v.x); key[i + 1] = order_key(v.y);
+        key[i + 2] = order_key(v.z); key[i + 3] = order_key(v.w);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      const int p = base + i;
+      key[i] = (p >= lo && p < hi) ? order_key(srow[p]) : 0u;
+    }
+  }
+  return topk_row_keys<BLOCK, ITEMS>(key, N, topk_pages, topk_frac, bos, eos, btr, bt_ld,
+                                     out, bout, k_cap);
+}
+
+template <int BLOCK, int ITEMS>
+__device__ int topk_row_keys(const uint32_t (&key)[ITEMS], int N, int topk_pages,
+                             double topk_frac, int bos, int eos,
+                             const int32_t* __restrict__ btr, int64_t bt_ld,
+                             int32_t* out, int32_t* bout, int k_cap) {
   constexpr int NW = BLOCK / 64;
   constexpr int kBits = 8;                       // digit width
   constexpr int kBins = 1 << kBits;
@@ -66,25 +106,7 @@ __device__ int topk_row(const float* __restrict__ srow, bool aligned16, int N,
   const int ncand = hi - lo;
 
   const int base = tid * ITEMS;
-  uint32_t key[ITEMS];
-  constexpr bool kVec = ITEMS % 4 == 0;          // 16-byte pieces per thread
-  const bool vec = kVec && aligned16 && (base + ITEMS <= hi) && (base >= lo);
-  if (vec) {
-    if constexpr (kVec) {
-#pragma unroll
-      for (int i = 0; i < ITEMS; i += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(srow + base + i);
-        key[i] = order_key(v.x); key[i + 1] = order_key(v.y);
-        key[i + 2] = order_key(v.z); key[i + 3] = order_key(v.w);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-      const int p = base + i;
-      key[i] = (p >= lo && p < hi) ? order_key(srow[p]) : 0u;
-    }
-  }
+  constexpr bool kVec = ITEMS % 4 == 0;
   // block ids of this thread's entries, fetched alongside the keys
   int32_t bid[ITEMS];
   if (bout != nullptr) {

@@ -24,7 +24,8 @@ import math
 
 import torch
 
-from . import (entmax15_paged_decode, entmax_scratch_floats, gauss_moments, gauss_select,
+from . import (entmax15_paged_decode, entmax15_paged_decode_merged, entmax_scratch_floats,
+               gauss_moments, gauss_select,
                h2o_accumulate, h2o_scratch_floats, lse_merge, page_score,
                page_score_group, page_topk, page_var_update, pagestats_update,
                sparse_page_decode, sparse_paged_decode, sparse_paged_decode_merged,
@@ -143,9 +144,16 @@ class SparseDecoder:
             self.est = self.scores            # the estimates are the ranking scores
             self.tau_hat = torch.empty((B, H_q), dtype=f32, device=dev)
         self.entmax_scratch = None
+        # 1.5-entmax in one merged launch (else three launches and lse_merge)
+        # (a batch of fewer than 128 query rows keeps the three launches and
+        # their num_splits chunks per row: one block per row would leave the
+        # chip mostly idle)
+        self.entmax_fused = (bool(fuse_merge) and attention == "entmax15"
+                             and B * H_q >= 128)
         if attention == "entmax15":
             n = entmax_scratch_floats(B, H_q, self.k_cap, page_size)
             self.entmax_scratch = torch.empty(n, dtype=f32, device=dev)
+            self.entmax_tau_buf = torch.empty((B, H_q), dtype=f32, device=dev)
 
     @classmethod
     def for_workload(cls, wl, device="cuda", num_splits=None, group_select=False,
@@ -215,6 +223,14 @@ class SparseDecoder:
                   block_table=block_table, sel_blk=blk, stream=stream)
 
     def attend(self, q, kv_cache, block_table, seq_lens, stream=None):
+        if self.attention == "entmax15" and self.entmax_fused:
+            entmax15_paged_decode_merged(
+                q, kv_cache, block_table, seq_lens, self.sel_idx, self.sel_cnt, self.scale,
+                self.out, lse_out=self.lse, tau_out=self.entmax_tau_buf,
+                scratch=self.entmax_scratch,
+                sel_blk=self.sel_blk if self.use_sel_blk else None,
+                alibi_slopes=self.alibi, stream=stream)
+            return
         if self.attention == "entmax15":
             entmax15_paged_decode(q, kv_cache, block_table, seq_lens, self.sel_idx,
                                   self.sel_cnt, self.scale, self.o_part, self.lse_part,
@@ -258,7 +274,7 @@ class SparseDecoder:
             sel_blk=self.sel_blk if keep else None, alibi_slopes=self.alibi, stream=stream)
 
     def merge(self, stream=None):
-        if self.fused:
+        if self.fused or (self.attention == "entmax15" and self.entmax_fused):
             return                      # merged inside attend()
         lse_merge(self.o_part, self.lse_part, self.out, self.lse, stream=stream)
 
@@ -290,5 +306,7 @@ class SparseDecoder:
 
     def entmax_tau(self):
         """tau per query head [B, H_q] of the last 1.5-entmax decode."""
+        if self.entmax_fused:
+            return self.entmax_tau_buf
         n = self.B * self.H_q
         return self.entmax_scratch[-n:].view(self.B, self.H_q)

@@ -43,6 +43,7 @@ def test_header_declares_the_six_operations():
               "sparse_paged_decode", "sparse_paged_decode_merged",
               "entmax15_paged_decode", "entmax_scratch_floats", "sparse_select_decode",
               "sparse_page_decode", "page_var_update", "gauss_moments", "gauss_select",
+              "entmax15_paged_decode_merged",
               "lse_merge", "h2o_accumulate", "h2o_scratch_floats",
               "sparsekv_last_error"):
         assert n in names
@@ -134,6 +135,14 @@ def test_validation_rejects_bad_scalars(lib):
     assert "scratch" in _msg(lib)
     assert lib.entmax15_paged_decode(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p, None, 4, 8,
                                      0.1, 0, None, p, p, p, 10 ** 6, s) == EINVAL
+    # merged entmax: rows too long for LDS need the scratch
+    assert lib.entmax15_paged_decode_merged(p, 1, 8, 2, 128, p, 8, 16, p, 1024, p, p, p,
+                                            None, 1024, 8, 0.1, None, p, None, None, None,
+                                            0, s) == EINVAL
+    assert "scratch" in _msg(lib)
+    assert lib.entmax15_paged_decode_merged(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p,
+                                            None, 4, 8, 0.1, None, None, None, None, None,
+                                            0, s) == EFAULT
     # Gaussian-aware: bad page size, head shape, scale, capacity below the
     # reserved pages, too long a row
     assert lib.page_var_update(p, 8, 3, 2, 128, p, p, p, 4, p, 1, 0, s) == EINVAL

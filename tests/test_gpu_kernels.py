@@ -365,30 +365,39 @@ def run_entmax_case(wl, cache_cpu, q_cpu, group):
     d.rebuild_stats(cache, bt, sl)
     d.score(q, bt, sl)
     d.select(sl, bt)
-    d.attend(q, cache, bt, sl)
-    d.merge()
     torch.cuda.synchronize()
     cb = bits(cache)
     qd = q_cpu.double().numpy()
     sel_idx = d.sel_idx.cpu().numpy().reshape(-1, d.k_cap)
     sel_cnt = d.sel_cnt.cpu().numpy().reshape(-1)
     per = per_head_rows(selection_rows(sel_idx, sel_cnt), wl.B, wl.H_q, d.H_sel)
-    out = d.out.cpu().numpy()
-    gtau = d.entmax_tau().cpu().numpy()
-    worst = 0.0
+    ref = {}
     for b in range(wl.B):
         for i in range(wl.H_q):
-            o, tau = oracle.attend_entmax15(qd[b, i], cb, i // wl.G, wl.block_table[b],
-                                            int(wl.seq_lens[b]), per[b][i], wl.softmax_scale)
-            assert not np.any(np.isnan(out[b, i])), f"NaN output ({b},{i})"
+            ref[b, i] = oracle.attend_entmax15(qd[b, i], cb, i // wl.G, wl.block_table[b],
+                                               int(wl.seq_lens[b]), per[b][i],
+                                               wl.softmax_scale)
+    worst = 0.0
+    # one merged launch, then the three launches + lse_merge
+    for fused in (True, False):
+        d.entmax_fused = fused
+        d.out.fill_(float("nan"))
+        d.entmax_tau().fill_(float("nan"))
+        d.attend(q, cache, bt, sl)
+        d.merge()
+        torch.cuda.synchronize()
+        out = d.out.cpu().numpy()
+        gtau = d.entmax_tau().cpu().numpy()
+        for (b, i), (o, tau) in ref.items():
+            assert not np.any(np.isnan(out[b, i])), f"NaN output ({b},{i}) fused={fused}"
             e = np.abs(out[b, i].astype(np.float64) - o).max()
             worst = max(worst, e)
-            assert e <= 2e-3, f"entmax out ({b},{i}) err {e}"
+            assert e <= 2e-3, f"entmax out ({b},{i}) err {e} fused={fused}"
             if np.isinf(tau):
                 assert np.isinf(gtau[b, i])
             else:
                 assert abs(float(gtau[b, i]) - tau) <= 1e-4 * max(1.0, abs(tau)), \
-                    f"tau ({b},{i}) {gtau[b, i]} vs {tau}"
+                    f"tau ({b},{i}) {gtau[b, i]} vs {tau} fused={fused}"
     return worst
 
 
@@ -437,6 +446,14 @@ def run_gauss_case(wl, cache_in, q_cpu, slopes_np=None, mixture=None, cap=None, 
         t.fill_(float("nan"))
     d.rebuild_stats(cache, bt, sl)
     d.gauss_select(q, bt, sl)
+    # the three-launch decode first, kept for comparison with the merged one
+    d.entmax_fused = False
+    d.attend(q, cache, bt, sl)
+    d.merge()
+    torch.cuda.synchronize()
+    out3 = d.out.cpu().numpy()
+    d.entmax_fused = True
+    d.out.fill_(float("nan"))
     d.attend(q, cache, bt, sl)
     d.merge()
     torch.cuda.synchronize()
@@ -484,7 +501,8 @@ def run_gauss_case(wl, cache_in, q_cpu, slopes_np=None, mixture=None, cap=None, 
                                       sel_idx[b, i, :cnt], scale,
                                       slope=None if sl64 is None else sl64[i])
         assert not np.any(np.isnan(out[b, i])), f"NaN output ({b},{i})"
-        e = np.abs(out[b, i].astype(np.float64) - o).max()
+        e = max(np.abs(out[b, i].astype(np.float64) - o).max(),
+                np.abs(out3[b, i].astype(np.float64) - o).max())
         worst = max(worst, e)
         assert e <= OUT_ATOL, f"gauss out ({b},{i}) err {e}"
         assert abs(float(etau[b, i]) - t) <= 1e-4 * max(1.0, abs(t)), \
