@@ -154,27 +154,34 @@ def kernel_bytes(wl, sel_idx, sel_cnt, seq_lens, num_splits, token_level,
 
 # ------------------------------------------------------ measured traffic
 
-DECODE_SOURCES = ("sparse_kv_cache_amd/csrc/sparse_decode.hip",
-                  "sparse_kv_cache_amd/csrc/skv_device.h")
+# The sources each decode kernel is built from: a counter record stays valid
+# while they hash the same.
+DECODE_SOURCES = {
+    "softmax": ("sparse_kv_cache_amd/csrc/sparse_decode.hip",
+                "sparse_kv_cache_amd/csrc/skv_device.h",
+                "sparse_kv_cache_amd/csrc/skv_topk.h"),
+    "entmax": ("sparse_kv_cache_amd/csrc/entmax_decode.hip",
+               "sparse_kv_cache_amd/csrc/skv_device.h"),
+}
 
 
-def decode_source_hash():
+def decode_source_hash(kind="softmax"):
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     h = hashlib.sha1()
-    for f in DECODE_SOURCES:
+    for f in DECODE_SOURCES[kind]:
         with open(os.path.join(root, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def profiled_traffic(workload):
+def profiled_traffic(tag, kind="softmax"):
     """HBM bytes per decode launch from the committed counter summary of this
-    workload (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy's reading),
-    or None when there is none or the decode kernel's sources have changed
-    since the counters were taken."""
+    workload and mode (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy's
+    reading), or None when there is none or the decode kernel's sources have
+    changed since the counters were taken."""
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                        f"traffic_{workload}.md")
+                        f"traffic_{tag}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -183,7 +190,7 @@ def profiled_traffic(workload):
         return None
     body = text[start + 7:text.find("```", start + 7)].strip()
     rec = json.loads(body)
-    if rec.get("source_sha1") != decode_source_hash():
+    if rec is None or rec.get("source_sha1") != decode_source_hash(kind):
         return None
     return int(rec["traffic"])
 
@@ -483,9 +490,12 @@ def main():
     a = kb[focus] / (per_kernel_ms[focus] * 1e-3) / 1e9
     roofline = {"kernel": focus, "bound": "hbm", "achieved": round(a, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(a / PEAK_HBM_GBPS, 4),
-                "traffic": (None if entmax else
+                "traffic": (None if (entmax and not fused) else
                             profiled_traffic(wl.name + ("_group" if group else "")
-                                             + ("_alibi" if slopes is not None else ""))),
+                                             + ("_gauss" if gauss else
+                                                "_entmax" if entmax else "")
+                                             + ("_alibi" if slopes is not None else ""),
+                                             "entmax" if entmax else "softmax")),
                 "bytes_per_launch": kb[focus],
                 "us_per_launch": round(per_kernel_ms[focus] * 1000, 2)}
 
