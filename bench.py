@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true",
                     help="enqueue kernel by kernel instead of replaying HIP graphs")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="extra replays of the timed steps for the p10/p50/p90 spread")
     return ap.parse_args()
 
 
@@ -278,7 +280,20 @@ def cpu_baseline(wl, cache_bits, q, seq_lens, seconds, token_level, hh_bits=None
     per_request = t_used / rows_done
     steps_per_s = 1.0 / (per_request * wl.B)
     return {"value": steps_per_s, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "host_cpu": host_cpu(),
             "sample": sample, "seconds": round(t_used, 2)}
+
+
+def host_cpu():
+    """The host CPU's model name (Linux), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 # -------------------------------------------------------------------- main
@@ -436,6 +451,19 @@ def main():
     gpu_ms = e0.elapsed_time(e1) / args.steps
     ms_per_step = wall * 1000.0 / args.steps
 
+    # spread: the timed sequence replayed a few more times (HIP events), for
+    # the median and p10 / p90 of the per-step time; value stays the first,
+    # barrier-bracketed run above
+    spread = []
+    if not args.no_graph:
+        for _ in range(args.repeats):
+            r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            r0.record()
+            g_timed.replay()
+            r1.record()
+            torch.cuda.synchronize()
+            spread.append(r0.elapsed_time(r1) / args.steps)
+
     # algorithmic bytes from the selections of the last timed step's replica
     # (read before the per-kernel graphs below overwrite the buffers)
     last = (args.warmup + args.steps - 1)
@@ -529,6 +557,14 @@ def main():
         "roofline": roofline,
         "copy_GBps": round(copy_gbps, 1),
         "setup_s": round(gen_s, 1),
+        "gpu_ms_per_step_spread": (None if not spread else {
+            "runs": len(spread),
+            "p10": round(float(np.percentile(spread, 10)), 4),
+            "p50": round(float(np.percentile(spread, 50)), 4),
+            "p90": round(float(np.percentile(spread, 90)), 4)}),
+        "env": {"torch": torch.__version__, "hip": torch.version.hip,
+                "gpu": torch.cuda.get_device_name(0),
+                "host_cpu": host_cpu(), "host_threads": os.cpu_count()},
     }
     if not args.no_cpu_baseline:
         from sparse_kv_cache_amd.workloads import bf16_bits
