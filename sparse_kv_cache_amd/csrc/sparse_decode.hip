@@ -372,7 +372,7 @@ void sparse_decode_wave_kernel(
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 
   const int32_t* btr = bt + static_cast<int64_t>(b) * bt_ld;
-  const int64_t head_off = static_cast<int64_t>(h) * D + c * 8;
+  const int head_off = h * D + c * 8;   // < H_kv * D: 32 bits
   const int64_t row_stride = static_cast<int64_t>(H_kv) * D;
   const int64_t v_off = num_blocks * P * row_stride;
   const int epg = 16 / P;
@@ -410,15 +410,17 @@ void sparse_decode_wave_kernel(
           for (int j = 0; j < NL; ++j)
             pos[j] = static_cast<float>((pg - pref) * 16 + slot + RPL * j);
         }
+        // masked rows read row 0 of the same page (every page listed has
+        // one, and an invalid entry reads block 0): the base stays scalar
         const uint16_t* kp = kv + static_cast<int64_t>(blk) * 16 * row_stride;
+        const uint16_t* vp = kp + v_off;
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
           const int t = slot + RPL * j;
           ok[j] = t < nv;
-          const uint32_t off = ok[j] ? static_cast<uint32_t>(t * row_stride + head_off) : 0u;
-          const uint16_t* base = ok[j] ? kp : kv + head_off;
-          K[j] = *reinterpret_cast<const uint4*>(base + off);
-          V[j] = *reinterpret_cast<const uint4*>(base + v_off + off);
+          const uint32_t off = static_cast<uint32_t>((ok[j] ? t * static_cast<int>(row_stride) : 0) + head_off);
+          K[j] = *reinterpret_cast<const uint4*>(kp + off);
+          V[j] = *reinterpret_cast<const uint4*>(vp + off);
         }
       } else {
       full = false;
