@@ -708,3 +708,46 @@ def test_invalid_arguments_raise_before_launch():
     assert e.value.code == -22
     with pytest.raises(TypeError):
         skv.page_score(q.double(), None, None, None, None, None, 16, 1, 1, None)
+
+
+@pytest.mark.parametrize("mode", ["one_launch", "separate", "group", "gauss", "entmax",
+                                  "gauss_merged", "entmax_merged"])
+def test_graph_replays_match_eager(mode):
+    """bench.py times HIP-graph replays of the step: each replay, with eager
+    work and new queries in between, must give the eager step's bits."""
+    say(f"[gpu] graph replay vs eager, {mode}")
+    wl = W.small_case(seed=150, B=3, H_q=8, H_kv=2, D=128, P=16, max_pages=40,
+                      topk_pages=6, num_splits=4, min_len=40)
+    kw = {}
+    if mode == "separate":
+        kw["fuse_merge"] = False
+    elif mode == "group":
+        kw["group_select"] = True
+    elif mode.startswith("gauss"):
+        kw["selection"] = "gauss"
+    elif mode.startswith("entmax"):
+        kw["attention"] = "entmax15"
+    d = SparseDecoder.for_workload(wl, device="cuda", **kw)
+    # the one-launch 1.5-entmax decode, also for this small batch
+    d.entmax_fused = mode.endswith("_merged")
+    cache = dev(W.make_cache(wl))
+    bt, sl = dev(wl.block_table), dev(wl.seq_lens)
+    q = dev(W.make_queries(wl, 0))
+    d.rebuild_stats(cache, bt, sl)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        d.step(q, cache, bt, sl)
+    torch.cuda.synchronize()
+    for step in range(3):
+        q.copy_(dev(W.make_queries(wl, step + 1)))
+        scratch = torch.randn(1 << 20, device="cuda").sum()     # eager work between
+        g.replay()
+        torch.cuda.synchronize()
+        got = (d.out.clone(), d.lse.clone())
+        d.out.fill_(float("nan"))
+        d.step(q, cache, bt, sl)
+        torch.cuda.synchronize()
+        assert torch.isfinite(scratch)
+        assert torch.equal(got[0], d.out), f"replay {step}: out differs from eager"
+        assert torch.equal(got[1], d.lse), f"replay {step}: lse differs from eager"
