@@ -145,11 +145,12 @@ class SparseDecoder:
             self.tau_hat = torch.empty((B, H_q), dtype=f32, device=dev)
         self.entmax_scratch = None
         # 1.5-entmax in one merged launch (else three launches and lse_merge)
-        # (a batch of fewer than 128 query rows keeps the three launches and
-        # their num_splits chunks per row: one block per row would leave the
-        # chip mostly idle)
+        # (a batch of fewer than 128 query rows with a fixed top-k budget
+        # keeps the three launches and their num_splits chunks per row: one
+        # block per row would leave the chip mostly idle; Gaussian-aware
+        # selections are small, and the one launch wins there too)
         self.entmax_fused = (bool(fuse_merge) and attention == "entmax15"
-                             and B * H_q >= 128)
+                             and (B * H_q >= 128 or selection == "gauss"))
         if attention == "entmax15":
             n = entmax_scratch_floats(B, H_q, self.k_cap, page_size)
             self.entmax_scratch = torch.empty(n, dtype=f32, device=dev)
