@@ -12,7 +12,7 @@
 //   2. tau: one block per (request, query head) finds tau by Newton steps on
 //      f(tau) = sum [u - tau]_+^2 - 1 (u = z / 2) from tau = max u - 1, where
 //      f >= 0; f is convex and falling there, so the steps rise monotonically
-//      to the root;
+//      to the root (the row held in registers when it fits);
 //   3. values: one wave per chunk again folds p_t v_t over the rows with
 //      p_t > 0 only (16-row groups with no such row load no V at all) and
 //      writes the chunk's (o = sum p v / m, lse = ln m) with its mass m, so
@@ -161,11 +161,16 @@ __global__ __launch_bounds__(kWaves * 64) void entmax_logits_kernel(
   }
 }
 
-// Pass 2: tau of one query row over its cnt * P logits.
-__global__ __launch_bounds__(kTauThreads) void entmax_tau_kernel(
+// Pass 2: tau of one query row over its cnt * P logits.  With R > 0 the
+// row (at most THREADS * R logits) is read once into registers, so the
+// Newton steps cost no memory round trips; with R == 0 every step re-reads
+// the row.
+template <int THREADS, int R>
+__global__ __launch_bounds__(THREADS) void entmax_tau_kernel(
     int B, int H_q, int H_kv, int G, int P, const int32_t* __restrict__ sel_cnt,
     int k_cap, int H_sel, const float* __restrict__ logits, float* __restrict__ tau) {
-  __shared__ float red[2][kTauThreads / 64];
+  constexpr int NW = THREADS / 64;
+  __shared__ float red[2][NW];
   const int64_t qrow = blockIdx.x;
   const int b = static_cast<int>(qrow / H_q);
   const int i = static_cast<int>(qrow % H_q);
@@ -175,7 +180,6 @@ __global__ __launch_bounds__(kTauThreads) void entmax_tau_kernel(
   const int n = cnt * P;
   const float* z = logits + qrow * (static_cast<int64_t>(k_cap) * P);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int NW = kTauThreads / 64;
 
   auto block_sum2 = [&](float& a, float& c2) {
     a = skv::wave_sum(a);
@@ -188,8 +192,19 @@ __global__ __launch_bounds__(kTauThreads) void entmax_tau_kernel(
     __syncthreads();
   };
 
+  // u = z / 2 of this thread's entries (-inf past the row)
+  float u[R > 0 ? R : 1];
   float um = -INFINITY;
-  for (int t = tid; t < n; t += kTauThreads) um = fmaxf(um, 0.5f * z[t]);
+  if constexpr (R > 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int t = tid + r * THREADS;
+      u[r] = t < n ? 0.5f * z[t] : -INFINITY;
+      um = fmaxf(um, u[r]);
+    }
+  } else {
+    for (int t = tid; t < n; t += THREADS) um = fmaxf(um, 0.5f * z[t]);
+  }
   um = skv::wave_max(um);
   if (lane == 0) red[0][wave] = um;
   __syncthreads();
@@ -206,9 +221,17 @@ __global__ __launch_bounds__(kTauThreads) void entmax_tau_kernel(
   float t0 = um - 1.0f;
   for (int it = 0; it < 30; ++it) {
     float f = 0.0f, g = 0.0f;
-    for (int t = tid; t < n; t += kTauThreads) {
-      const float d = 0.5f * z[t] - t0;
-      if (d > 0.0f) { f = fmaf(d, d, f); g += d; }
+    if constexpr (R > 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float d = u[r] - t0;
+        if (d > 0.0f) { f = fmaf(d, d, f); g += d; }
+      }
+    } else {
+      for (int t = tid; t < n; t += THREADS) {
+        const float d = 0.5f * z[t] - t0;
+        if (d > 0.0f) { f = fmaf(d, d, f); g += d; }
+      }
     }
     block_sum2(f, g);
     f -= 1.0f;
@@ -637,9 +660,17 @@ extern "C" int entmax15_paged_decode(const float* q, int B, int H_q, int H_kv, i
                        H_q, H_kv, G, kv_cache, num_blocks, page_size, block_table, bt_ld,
                        seq_lens, sel_idx, sel_cnt, sel_blk, k_cap, H_sel, scale, num_splits,
                        alibi_slopes, logits);
-  hipLaunchKernelGGL(entmax_tau_kernel, dim3(static_cast<unsigned>(rows)), dim3(kTauThreads),
-                     0, stream, B, H_q, H_kv, G, page_size, sel_cnt, k_cap, H_sel, logits,
-                     tau);
+  // few rows: wide blocks; rows of up to 8 logits a thread stay in registers
+  const int64_t row_logits = static_cast<int64_t>(k_cap) * page_size;
+  const bool wide = rows < 256;
+  const int64_t in_regs = (wide ? 1024 : kTauThreads) * 8;
+#define SKV_TAU(TH, RR)                                                                  \
+  hipLaunchKernelGGL((entmax_tau_kernel<TH, RR>), dim3(static_cast<unsigned>(rows)),      \
+                     dim3(TH), 0, stream, B, H_q, H_kv, G, page_size, sel_cnt, k_cap,    \
+                     H_sel, logits, tau)
+  if (wide) { if (row_logits <= in_regs) SKV_TAU(1024, 8); else SKV_TAU(1024, 0); }
+  else { if (row_logits <= in_regs) SKV_TAU(kTauThreads, 8); else SKV_TAU(kTauThreads, 0); }
+#undef SKV_TAU
   if (D == 128)
     hipLaunchKernelGGL(entmax_values_kernel<128>, g13, dim3(kWaves * 64), 0, stream, B, H_q,
                        H_kv, G, kv_cache, num_blocks, page_size, block_table, bt_ld,
