@@ -72,16 +72,20 @@ __device__ __forceinline__ float group_max(float x) {
   return x;
 }
 
+// Whole-wave sum / max, the same value in every lane: DPP row reductions
+// (no LDS permutes), then the four row results read into scalars.
+__device__ __forceinline__ float row_lane(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  x = group_sum<16>(x);
+  return (row_lane(x, 0) + row_lane(x, 16)) + (row_lane(x, 32) + row_lane(x, 48));
 }
 
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+  x = group_max<16>(x);
+  return fmaxf(fmaxf(row_lane(x, 0), row_lane(x, 16)), fmaxf(row_lane(x, 32), row_lane(x, 48)));
 }
 
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
