@@ -184,15 +184,51 @@ __global__ __launch_bounds__(256) void gauss_moments_kernel(
 
 // -------------------------------------------------------- tau-hat + select
 
+// fp64 wave reductions: DPP moves of both 32-bit halves inside each 16-lane
+// row (no LDS permutes), then the four row results read into scalars; every
+// lane gets the same value.
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double x) {
+  const unsigned long long u = static_cast<unsigned long long>(__double_as_longlong(x));
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u & 0xffffffffull), CTRL,
+                                             0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), CTRL, 0xF, 0xF,
+                                             true);
+  return __longlong_as_double(static_cast<long long>(
+      (static_cast<unsigned long long>(static_cast<unsigned int>(hi)) << 32) |
+      static_cast<unsigned int>(lo)));
+}
+
+__device__ __forceinline__ double lane_d(double x, int l) {
+  const unsigned long long u = static_cast<unsigned long long>(__double_as_longlong(x));
+  const unsigned int lo = __builtin_amdgcn_readlane(static_cast<int>(u & 0xffffffffull), l);
+  const unsigned int hi = __builtin_amdgcn_readlane(static_cast<int>(u >> 32), l);
+  return __longlong_as_double(static_cast<long long>(
+      (static_cast<unsigned long long>(hi) << 32) | lo));
+}
+
+__device__ __forceinline__ double wave_sum_d(double x) {
+  x += dpp_d<0xB1>(x);
+  x += dpp_d<0x4E>(x);
+  x += dpp_d<0x141>(x);
+  x += dpp_d<0x140>(x);
+  return (lane_d(x, 0) + lane_d(x, 16)) + (lane_d(x, 32) + lane_d(x, 48));
+}
+
+__device__ __forceinline__ double wave_max_d(double x) {
+  x = fmax(x, dpp_d<0xB1>(x));
+  x = fmax(x, dpp_d<0x4E>(x));
+  x = fmax(x, dpp_d<0x141>(x));
+  x = fmax(x, dpp_d<0x140>(x));
+  return fmax(fmax(lane_d(x, 0), lane_d(x, 16)), fmax(lane_d(x, 32), lane_d(x, 48)));
+}
+
 // Sums of two doubles over the block; red holds 2 * (waves) doubles.
 __device__ __forceinline__ void block_sum2_d(double& x, double& y, double* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    x += __shfl_xor(x, o);
-    y += __shfl_xor(y, o);
-  }
+  x = wave_sum_d(x);
+  y = wave_sum_d(y);
   if (lane == 0) { red[2 * wave] = x; red[2 * wave + 1] = y; }
   __syncthreads();
   x = 0.0; y = 0.0;
@@ -203,8 +239,7 @@ __device__ __forceinline__ void block_sum2_d(double& x, double& y, double* red) 
 __device__ __forceinline__ double block_max_d(double x, double* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmax(x, __shfl_xor(x, o));
+  x = wave_max_d(x);
   if (lane == 0) red[wave] = x;
   __syncthreads();
   double t = -INFINITY;
