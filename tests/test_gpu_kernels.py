@@ -424,6 +424,10 @@ GAUSS_CASES = [
     (136, 2, 16, 2, 128, 16, 300, 0, 1, 8, True, None, None, None),
     (137, 1, 8, 8, 128, 16, 1100, 0, 1, 8, False, None, None, 0.25),
     (138, 2, 8, 4, 64, 4, 90, 2, 1, 5, True, None, 12, None),
+    # page size 1 (every variance 0), D 64, no reserved tail page
+    (140, 2, 4, 4, 64, 1, 120, 0, 0, 2, False, None, None, None),
+    # D 64 with ALiBi, a binding cap, no reserved page, a sharper scale
+    (141, 2, 8, 2, 64, 16, 50, 0, 0, 3, True, None, 4, 2.0),
 ]
 
 
