@@ -755,3 +755,31 @@ def test_graph_replays_match_eager(mode):
         assert torch.isfinite(scratch)
         assert torch.equal(got[0], d.out), f"replay {step}: out differs from eager"
         assert torch.equal(got[1], d.lse), f"replay {step}: lse differs from eager"
+
+
+def test_gauss_append_refreshes_tail_variance():
+    """Gaussian-aware decoder over appends: pagestats_update's tail refresh
+    and page_var_update(tail_only) keep every page's mean and variance equal
+    to the oracle's statistics of the grown cache (pages crossing a boundary
+    included)."""
+    say("[gpu] Gaussian-aware statistics over 20 appends")
+    wl = W.high_batch(seed=160, steps=20, B=3, num_blocks=120, smin=17, smax=150)
+    d = SparseDecoder.for_workload(wl, device="cuda", selection="gauss")
+    cache = dev(W.make_cache(wl))
+    bt = dev(wl.block_table)
+    d.k_var.fill_(float("nan"))
+    d.rebuild_stats(cache, bt, dev(wl.seq_lens))
+    for step in range(wl.steps):
+        kn, vn = W.make_new_kv(wl, step)
+        d.append(cache, bt, dev(wl.seq_lens_at(step)), dev(kn), dev(vn))
+    torch.cuda.synchronize()
+    sl = wl.seq_lens_at(wl.steps - 1)
+    cb = bits(cache)
+    used = np.unique(np.concatenate(
+        [wl.block_table[b, :(int(sl[b]) + wl.P - 1) // wl.P] for b in range(wl.B)]))
+    check_stats(bits(d.k_min), bits(d.k_max), d.k_mean.cpu().numpy(), cb, wl.block_table,
+                sl, wl.P, used)
+    ov = oracle.page_var(cb, wl.block_table, sl, wl.P)[used]
+    gv = d.k_var.cpu().numpy()[used].astype(np.float64)
+    assert np.all(np.abs(gv - ov) <= 1e-5 * ov + 1e-6), \
+        f"variance after appends off by {np.abs(gv - ov).max()}"
