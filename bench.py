@@ -494,8 +494,8 @@ def main():
         per_kernel_ms[n] = k0.elapsed_time(k1) / reps
         del g
 
-    kb, upages = kernel_bytes(wl, sel_idx, sel_cnt, sl_last, wl.num_splits, token_level,
-                              group, fused, entmax, gauss)
+    kb, upages = kernel_bytes(wl, sel_idx, sel_cnt, sl_last, decs[0].decode_splits,
+                              token_level, group, fused, entmax, gauss)
     if one_launch:
         # the statistics read for scoring (scores and selection stay in LDS)
         # plus the merged decode; q counted once
@@ -538,7 +538,7 @@ def main():
         "dtype": "f32", "kv_dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H_q": wl.H_q, "H_kv": wl.H_kv,
                    "D": wl.D, "page_size": wl.P, "topk_pages": wl.topk_pages,
-                   "topk_frac": wl.topk_frac, "num_splits": wl.num_splits,
+                   "topk_frac": wl.topk_frac, "num_splits": decs[0].decode_splits,
                    "mean_seq_len": float(np.mean(sl_last)), "replicas": R,
                    "selection": ("kv_head" if (group or token_level) else
                                  "gauss_query_head" if gauss else "query_head"),

@@ -121,8 +121,16 @@ class SparseDecoder:
         self.sel_cnt = torch.empty((B, self.H_sel), dtype=i32, device=dev)
         self.sel_blk = torch.empty((B, self.H_sel, self.k_cap), dtype=i32, device=dev)
         self.use_sel_blk = True
-        self.o_part = torch.empty((B, H_q, num_splits, D), dtype=f32, device=dev)
-        self.lse_part = torch.empty((B, H_q, num_splits), dtype=f32, device=dev)
+        # A selection shared by a kv head's group is decoded by the matrix-core
+        # group kernel, one block per (split, request, kv head): it runs best
+        # with about one block per CU (256), so its split count follows the
+        # grid, at most num_splits and at most one split per selected page.
+        self.decode_splits = num_splits
+        if self.H_sel == H_kv and H_q > H_kv:
+            per = max(1, 256 // max(1, B * H_kv))
+            self.decode_splits = max(1, min(num_splits, per, self.k_cap))
+        self.o_part = torch.empty((B, H_q, self.decode_splits, D), dtype=f32, device=dev)
+        self.lse_part = torch.empty((B, H_q, self.decode_splits), dtype=f32, device=dev)
         self.out = torch.empty((B, H_q, D), dtype=f32, device=dev)
         self.lse = torch.empty((B, H_q), dtype=f32, device=dev)
         self.fused = (bool(fuse_merge) and self.H_sel == H_q and num_splits <= 8
