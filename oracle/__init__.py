@@ -80,6 +80,7 @@ def _load():
     lib.oracle_h2o_recurrence.argtypes = [P, P, i32, f64]
     lib.oracle_h2o_step.argtypes = [P, i32, i32, i32, i32, P, i64, P, i64, P,
                                     i32, i32, f64, f64, P, P, i64]
+    lib.oracle_h2o_step_heads.argtypes = lib.oracle_h2o_step.argtypes
     lib.oracle_decode_step.argtypes = [P, i32, i32, i32, i32, P, i64, i32, P, i64,
                                        P, P, P, P, f64, f64, i32, f64, i32, i32,
                                        f64, P, i64, P, P, i32, P, P]
@@ -367,9 +368,11 @@ def h2o_recurrence(p, hh, decay):
 
 
 def h2o_step(q, kv_cache, block_table, seq_lens, hh, bos, eos, scale, decay,
-             ld=None):
+             ld=None, per_head=False):
     """Token-level H2O step (page_size 1).  Updates hh ([num_blocks, H_kv] bf16
-    bits) in place and returns scores [B, H_kv, ld] (float64, NaN beyond S_b)."""
+    bits) in place and returns scores [B, H_kv, ld] (float64, NaN beyond S_b).
+    per_head=False: softmax of the group-mean query; True: every query head's
+    own softmax, averaged over the group."""
     lib = _load()
     qd = _c(q, np.float64)
     B, H_q, D = qd.shape
@@ -382,9 +385,9 @@ def h2o_step(q, kv_cache, block_table, seq_lens, hh, bos, eos, scale, decay,
     if ld is None:
         ld = bt.shape[1]
     s = np.full((B, H_kv, ld), np.nan)
-    lib.oracle_h2o_step(_ptr(qd), B, H_q, H_kv, D, _ptr(kv), NB, _ptr(bt),
-                        bt.shape[1], _ptr(sl), int(bos), int(eos), float(scale),
-                        float(decay), _ptr(hh), _ptr(s), ld)
+    fn = lib.oracle_h2o_step_heads if per_head else lib.oracle_h2o_step
+    fn(_ptr(qd), B, H_q, H_kv, D, _ptr(kv), NB, _ptr(bt), bt.shape[1], _ptr(sl),
+       int(bos), int(eos), float(scale), float(decay), _ptr(hh), _ptr(s), ld)
     return s
 
 

@@ -856,6 +856,71 @@ void oracle_h2o_step(const double *q, int B, int H_q, int H_kv, int D,
     free(qbar);
 }
 
+/* Per-head reading of the GQA token flow [VTX description: the GQA variants
+ * run the product and the softmax with the query-group axis kept]: per request
+ * b and kv head h, every query head g of the group takes its own softmax over
+ * the window W = [bos, S_b - eos),
+ *   p_g = softmax_W(scale * q_g . k_t),
+ * the group's probabilities are averaged, p = (1/G) sum_g p_g (one unit of
+ * mass per step, as in the group-mean reading), and every t in W gets the
+ * recurrence above.  Layouts and untouched entries as oracle_h2o_step. */
+void oracle_h2o_step_heads(const double *q, int B, int H_q, int H_kv, int D,
+                           const uint16_t *kv_cache, int64_t num_blocks,
+                           const int32_t *block_table, int64_t bt_ld,
+                           const int32_t *seq_lens, int bos, int eos,
+                           double scale, double decay, uint16_t *hh,
+                           double *scores, int64_t ld)
+{
+    int G = H_q / H_kv;
+    for (int b = 0; b < B; ++b) {
+        int S = seq_lens[b];
+        int lo = bos < S ? bos : S;
+        int hi = S - eos > 0 ? S - eos : 0;
+        if (hi < lo) hi = lo;
+        int n = hi - lo;
+        int nn = n > 0 ? n : 1;
+        const int32_t *bt = block_table + (int64_t)b * bt_ld;
+        double *l = malloc(sizeof *l * nn);
+        double *pr = malloc(sizeof *pr * nn);
+        uint16_t *slot = malloc(sizeof *slot * nn);
+        for (int h = 0; h < H_kv; ++h) {
+            for (int j = 0; j < n; ++j)
+                pr[j] = 0.0;
+            for (int g = 0; g < G; ++g) {
+                const double *qg = q + ((int64_t)b * H_q + h * G + g) * D;
+                double m = -INFINITY;
+                for (int j = 0; j < n; ++j) {
+                    int64_t blk = bt[lo + j];
+                    double dot = 0.0;
+                    for (int d = 0; d < D; ++d)
+                        dot += qg[d] * oracle_bf16_to_double(kv_cache[cache_index(
+                                   0, blk, 0, h, d, num_blocks, 1, H_kv, D)]);
+                    l[j] = scale * dot;
+                    if (l[j] > m) m = l[j];
+                }
+                double Z = 0.0;
+                for (int j = 0; j < n; ++j) {
+                    l[j] = exp(l[j] - m);
+                    Z += l[j];
+                }
+                for (int j = 0; j < n; ++j)
+                    pr[j] += l[j] / Z / G;
+            }
+            for (int j = 0; j < n; ++j)
+                slot[j] = hh[(int64_t)bt[lo + j] * H_kv + h];
+            oracle_h2o_recurrence(pr, slot, n, decay);
+            for (int j = 0; j < n; ++j)
+                hh[(int64_t)bt[lo + j] * H_kv + h] = slot[j];
+            for (int t = 0; t < S; ++t)
+                scores[((int64_t)b * H_kv + h) * ld + t] =
+                    oracle_bf16_to_double(hh[(int64_t)bt[t] * H_kv + h]);
+        }
+        free(l);
+        free(pr);
+        free(slot);
+    }
+}
+
 /* ------------------------------------------------ whole decode step */
 
 /* One page-level decode step for the whole batch, used as the CPU baseline

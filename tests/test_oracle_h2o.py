@@ -13,6 +13,12 @@
   the queries lean towards), re-run on CPU-drawn inputs against its
   thresholds and an unrounded float64 recurrence written here.
 * Append writes exactly the new bytes and zeroes the written hh slots only.
+* The per-head reading of the GQA token flow (each query head's softmax,
+  averaged over the group): a three-token closed form where it differs from
+  the group-mean query, exact rational weights on tiny inputs, G = 1 and
+  identical group queries reduce it to the group-mean step, one unit of mass
+  per step inside the window only, head order within a group is irrelevant and
+  a group reaches only its own kv head.
 """
 import json
 import os
@@ -202,3 +208,140 @@ def test_append_writes_bytes_and_resets_only_written_slots():
         before[0, blk, pos % 16] = kn[b]
         before[1, blk, pos % 16] = vn[b]
     np.testing.assert_array_equal(cache, before)
+
+
+# --------------------------------------------------------------------------
+# per-head reading of the GQA token flow: each query head's own softmax over
+# the window, averaged over the group
+
+
+def _token_case(keys, H_kv=1):
+    """Cache [2, S, 1, H_kv, D] holding `keys` ([S, H_kv, D] bf16-exact floats)
+    under a contiguous block table, one request."""
+    keys = np.asarray(keys, dtype=np.float64)
+    S, _, D = keys.shape
+    cache = np.zeros((2, S, 1, H_kv, D), dtype=np.uint16)
+    cache[0, :, 0] = oracle.double_to_bf16(keys)
+    assert np.array_equal(oracle.bf16_decode(cache[0, :, 0]), keys)
+    bt = np.arange(S, dtype=np.int32)[None, :]
+    sl = np.array([S], dtype=np.int32)
+    return cache, bt, sl
+
+
+def test_per_head_closed_form_three_tokens():
+    # keys e1, e2, 0; head 0 asks along e1, head 1 along e2 (q = c e_i, scale 1)
+    D, c = 8, 2.0
+    keys = np.zeros((3, 1, D))
+    keys[0, 0, 0] = 1.0
+    keys[1, 0, 1] = 1.0
+    cache, bt, sl = _token_case(keys)
+    q = np.zeros((1, 2, D))
+    q[0, 0, 0] = c
+    q[0, 1, 1] = c
+    e = np.exp(c)
+    # each head: (e, 1, 1) / (e + 2) and (1, e, 1) / (e + 2); their mean
+    heads = np.array([(e + 1) / 2, (e + 1) / 2, 1.0]) / (e + 2)
+    # the group-mean query c/2 (e1 + e2) gives softmax(c/2, c/2, 0)
+    mean_q = np.array([np.exp(c / 2), np.exp(c / 2), 1.0]) / (2 * np.exp(c / 2) + 1)
+    assert np.abs(heads - mean_q).max() > 0.02          # the readings differ here
+    d = 0.984375
+    for per_head, want in ((True, heads), (False, mean_q)):
+        hh = np.zeros((3, 1), dtype=np.uint16)
+        sc = oracle.h2o_step(q, cache, bt, sl, hh, 0, 0, 1.0, d, per_head=per_head)
+        np.testing.assert_array_equal(hh[:, 0], oracle.double_to_bf16(want))
+        np.testing.assert_array_equal(sc[0, 0, :3], oracle.bf16_decode(hh[:, 0]))
+        # second step: bf16(bf16(p) + bf16(d) * hh)
+        first = oracle.bf16_decode(hh[:, 0]).copy()
+        oracle.h2o_step(q, cache, bt, sl, hh, 0, 0, 1.0, d, per_head=per_head)
+        pb = oracle.bf16_decode(oracle.double_to_bf16(want))
+        np.testing.assert_array_equal(hh[:, 0], oracle.double_to_bf16(pb + d * first))
+
+
+def _random_token_case(seed, B=2, H_q=8, H_kv=2, D=16, S=40):
+    rng = np.random.default_rng(seed)
+    cache = oracle.double_to_bf16(rng.standard_normal((2, B * S, 1, H_kv, D)))
+    bt = rng.permutation(B * S).astype(np.int32).reshape(B, S)
+    sl = np.array([S, S - 13][:B], dtype=np.int32)
+    q = rng.standard_normal((B, H_q, D))
+    hh = oracle.double_to_bf16(rng.random((B * S, H_kv)) * 4)
+    return cache, bt, sl, q, hh
+
+
+def test_per_head_reduces_to_group_mean_cases():
+    # G = 1: both readings are the same step, bit for bit
+    cache, bt, sl, q, hh0 = _random_token_case(80, H_q=2, H_kv=2)
+    a, b = hh0.copy(), hh0.copy()
+    sa = oracle.h2o_step(q, cache, bt, sl, a, 2, 3, 0.25, 0.984375, per_head=True)
+    sb = oracle.h2o_step(q, cache, bt, sl, b, 2, 3, 0.25, 0.984375)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(sa, sb)
+    # identical queries within each group: the same probabilities (up to the
+    # float64 rounding of the two averages, so at most one bf16 step apart)
+    cache, bt, sl, q, hh0 = _random_token_case(81, H_q=8, H_kv=2)
+    q[:, 1:4] = q[:, 0:1]
+    q[:, 5:8] = q[:, 4:5]
+    a, b = hh0.copy(), hh0.copy()
+    oracle.h2o_step(q, cache, bt, sl, a, 2, 3, 0.25, 0.984375, per_head=True)
+    oracle.h2o_step(q, cache, bt, sl, b, 2, 3, 0.25, 0.984375)
+    apart = np.abs(a.astype(np.int64) - b.astype(np.int64))
+    assert apart.max() <= 1 and (apart == 0).mean() > 0.95
+
+
+def test_per_head_window_mass_order_and_groups():
+    B, H_q, H_kv, S, bos, eos = 2, 8, 2, 40, 2, 3
+    cache, bt, sl, q, hh0 = _random_token_case(82, B, H_q, H_kv, S=S)
+    # one unit of mass per (request, kv head), only inside [bos, S - eos)
+    hh = np.zeros_like(hh0)
+    oracle.h2o_step(q, cache, bt, sl, hh, bos, eos, 0.25, 0.984375, per_head=True)
+    for b in range(B):
+        n = int(sl[b])
+        v = oracle.bf16_decode(hh[bt[b, :n]])
+        assert np.all(v[:bos] == 0) and np.all(v[n - eos:] == 0)
+        assert np.all(v[bos:n - eos] > 0)
+        assert np.all(np.abs(v.sum(0) - 1) <= (n - bos - eos) * 2.0 ** -9)
+    # mass after n steps from zero: (1 - d^n) / (1 - d) within the 10 % bound
+    d, steps = 0.984375, 200
+    hh = np.zeros_like(hh0)
+    rng = np.random.default_rng(3)
+    for _ in range(steps):
+        qq = rng.standard_normal(q.shape)
+        oracle.h2o_step(qq, cache, bt, sl, hh, bos, eos, 0.25, d, per_head=True)
+    exact = (1 - d ** steps) / (1 - d)
+    for b in range(B):
+        mass = oracle.bf16_decode(hh[bt[b, :int(sl[b])]]).sum(0)
+        assert np.all(np.abs(mass / exact - 1) <= 0.10), mass
+    # the head order within a group does not matter
+    perm = np.array([2, 0, 3, 1, 5, 7, 4, 6])
+    a, b = hh0.copy(), hh0.copy()
+    oracle.h2o_step(q, cache, bt, sl, a, bos, eos, 0.25, d, per_head=True)
+    oracle.h2o_step(q[:, perm], cache, bt, sl, b, bos, eos, 0.25, d, per_head=True)
+    assert np.abs(a.astype(np.int64) - b.astype(np.int64)).max() <= 1
+    # a group's queries reach only its own kv head
+    q2 = q.copy()
+    q2[:, 4:] = rng.standard_normal((B, 4, q.shape[2])) * 3
+    c = hh0.copy()
+    oracle.h2o_step(q2, cache, bt, sl, c, bos, eos, 0.25, d, per_head=True)
+    np.testing.assert_array_equal(c[:, 0], a[:, 0])
+    assert not np.array_equal(c[:, 1], a[:, 1])
+
+
+def test_per_head_matches_brute_force_on_tiny_inputs():
+    # the definition written out with exact rational weights: logits chosen so
+    # every head's softmax is a ratio of small integers (exp of log-integers)
+    D = 4
+    keys = np.zeros((4, 1, D))
+    keys[:, 0, 0] = [1.0, 0.0, 0.0, 0.0]
+    keys[:, 0, 1] = [0.0, 1.0, 0.0, 0.0]
+    keys[:, 0, 2] = [0.0, 0.0, 1.0, 0.0]
+    cache, bt, sl = _token_case(keys)
+    q = np.zeros((1, 4, D))
+    q[0, 0, :3] = np.log([3.0, 1.0, 1.0])      # exp logits 3, 1, 1, 1 -> /6
+    q[0, 1, :3] = np.log([1.0, 5.0, 1.0])      # 1, 5, 1, 1 -> /8
+    q[0, 2, :3] = np.log([1.0, 1.0, 7.0])      # 1, 1, 7, 1 -> /10
+    q[0, 3, :3] = np.log([2.0, 2.0, 2.0])      # 2, 2, 2, 1 -> /7
+    probs = np.array([[3, 1, 1, 1], [1, 5, 1, 1], [1, 1, 7, 1], [2, 2, 2, 1]], float)
+    probs /= probs.sum(1, keepdims=True)
+    want = probs.mean(0)
+    hh = np.zeros((4, 1), dtype=np.uint16)
+    oracle.h2o_step(q, cache, bt, sl, hh, 0, 0, 1.0, 0.984375, per_head=True)
+    np.testing.assert_array_equal(hh[:, 0], oracle.double_to_bf16(want))
