@@ -59,6 +59,9 @@ def parse():
                          "and decode")
     ap.add_argument("--attention", default="softmax", choices=["softmax", "entmax15"],
                     help="page level: softmax, or 1.5-entmax over the same selection")
+    ap.add_argument("--h2o-softmax", default="group_mean", choices=["group_mean", "per_head"],
+                    help="token level: softmax of the group-mean query, or every query "
+                         "head's own softmax averaged over the group")
     ap.add_argument("--no-fuse", action="store_true",
                     help="keep page_topk and lse_merge as their own launches even "
                          "where the decode can select and merge in-block")
@@ -200,7 +203,7 @@ def profiled_traffic(tag, kind="softmax"):
 # ------------------------------------------------------------ cpu baseline
 
 def cpu_baseline(wl, cache_bits, q, seq_lens, seconds, token_level, hh_bits=None,
-                 gauss=False, slopes=None, k_cap=0):
+                 gauss=False, slopes=None, k_cap=0, h2o_per_head=False):
     """The float64 oracle on a bounded sample of requests (whole step for
     those requests), scaled to steps/s of the full batch."""
     import oracle
@@ -217,7 +220,8 @@ def cpu_baseline(wl, cache_bits, q, seq_lens, seconds, token_level, hh_bits=None
             hh = hh_bits.copy()
             t0 = time.perf_counter()
             sc = oracle.h2o_step(qd[bb:bb + 1], cache_bits, bt, sl, hh, wl.bos,
-                                 wl.eos, wl.softmax_scale, wl.decay)
+                                 wl.eos, wl.softmax_scale, wl.decay,
+                                 per_head=h2o_per_head)
             for h in range(wl.H_kv):
                 sel = oracle.select(sc[0, h, :int(sl[0])], wl.topk_pages, 0.0,
                                     wl.bos, wl.eos)
@@ -335,7 +339,8 @@ def main():
     decs = [SparseDecoder.for_workload(wl, device=dev, group_select=group,
                                        alibi_slopes=slopes, fuse_merge=not args.no_fuse,
                                        attention="entmax15" if entmax else "softmax",
-                                       selection="gauss" if gauss else "topk")
+                                       selection="gauss" if gauss else "topk",
+                                       h2o_softmax=args.h2o_softmax)
             for _ in range(R)]
     fused = decs[0].fused or decs[0].entmax_fused
     in_decode = decs[0].select_in_decode
@@ -522,7 +527,8 @@ def main():
                             profiled_traffic(wl.name + ("_group" if group else "")
                                              + ("_gauss" if gauss else
                                                 "_entmax" if entmax else "")
-                                             + ("_alibi" if slopes is not None else ""),
+                                             + ("_alibi" if slopes is not None else "")
+                                             + ("_heads" if decs[0].h2o_per_head else ""),
                                              "entmax" if entmax else "softmax")),
                 "bytes_per_launch": kb[focus],
                 "us_per_launch": round(per_kernel_ms[focus] * 1000, 2)}
@@ -547,6 +553,7 @@ def main():
                    "alibi": slopes is not None, "merge_in_decode": fused,
                    "select_in_decode": in_decode, "one_launch_step": one_launch,
                    "attention": "entmax15" if entmax else "softmax",
+                   "h2o_softmax": args.h2o_softmax if token_level else None,
                    "parallelism": "single-gpu"},
         "selected_pages_per_head": round(float(sel_cnt.mean()), 2),
         "effective_GBps": round(step_bytes / (gpu_ms * 1e-3) / 1e9, 1),
@@ -573,7 +580,7 @@ def main():
         result["cpu_baseline"] = cpu_baseline(
             wl, cb, q.cpu(), sl_last, args.cpu_seconds, token_level, hb,
             gauss=gauss, slopes=None if slopes is None else slopes.cpu().numpy(),
-            k_cap=decs[0].k_cap)
+            k_cap=decs[0].k_cap, h2o_per_head=decs[0].h2o_per_head)
     print(json.dumps(result), flush=True)
     return 0
 

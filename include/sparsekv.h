@@ -456,6 +456,35 @@ int h2o_accumulate(const float *q, int B, int H_q, int H_kv, int D,
  * rows of at most max_tokens tokens.  No device work; -1 on bad arguments. */
 int64_t h2o_scratch_floats(int B, int H_kv, int64_t max_tokens);
 
+/*
+ * h2o_accumulate_heads -- the same step with the query-group axis kept through
+ * the softmax.  [VTX description: the GQA variants compute the product and
+ * the softmax over the query-group axis; VTX "Token-level variants" for the
+ * accumulator.]
+ *
+ *   Per (b, kv head h): every query head g of the group takes its own
+ *   p_g = softmax_W(scale * q_g . k_t) over W = [bos, S_b - eos), and
+ *   p = (1/G) sum_g p_g (still one unit of mass per step) feeds the same
+ *   recurrence, hh_t <- bf16( bf16(p_t) + bf16(decay) * hh_t ) for t in W.
+ *   Arguments, layouts and errors as h2o_accumulate, except that the scratch
+ *   holds h2o_heads_scratch_floats(B, H_q, bt_ld) floats and H_q * (D + 64)
+ *   must stay within 16320 (the query rows and one chunk's logits of a request
+ *   sit in one block's 64 KiB of LDS; SKV_EINVAL otherwise).
+ */
+int h2o_accumulate_heads(const float *q, int B, int H_q, int H_kv, int D,
+                         const uint16_t *kv_cache, int64_t num_blocks,
+                         int page_size, const int32_t *block_table,
+                         int64_t bt_ld, const int32_t *seq_lens,
+                         int reserved_bos, int reserved_eos, float scale,
+                         float decay, uint16_t *hh_score, float *scores,
+                         int64_t score_ld, float *scratch,
+                         int64_t scratch_floats, hipStream_t stream);
+
+/* Scratch size (floats) h2o_accumulate_heads needs for B requests, H_q query
+ * heads and rows of at most max_tokens tokens.  No device work; -1 on bad
+ * arguments. */
+int64_t h2o_heads_scratch_floats(int B, int H_q, int64_t max_tokens);
+
 #ifdef __cplusplus
 }
 #endif

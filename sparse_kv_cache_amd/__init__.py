@@ -19,7 +19,8 @@ import torch
 __all__ = [
     "pagestats_update", "page_score", "page_score_group", "page_topk",
     "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
-    "h2o_accumulate", "h2o_scratch_floats", "entmax15_paged_decode",
+    "h2o_accumulate", "h2o_scratch_floats", "h2o_accumulate_heads",
+    "h2o_heads_scratch_floats", "entmax15_paged_decode",
     "entmax_scratch_floats", "sparse_select_decode", "sparse_page_decode",
     "page_var_update", "gauss_moments", "gauss_select", "entmax15_paged_decode_merged",
     "library_path",
@@ -33,14 +34,16 @@ _lib = None
 EXPORTED_SYMBOLS = (
     "pagestats_update", "page_score", "page_score_group", "page_topk",
     "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
-    "h2o_accumulate", "h2o_scratch_floats", "entmax15_paged_decode",
+    "h2o_accumulate", "h2o_scratch_floats", "h2o_accumulate_heads",
+    "h2o_heads_scratch_floats", "entmax15_paged_decode",
     "entmax_scratch_floats", "sparse_select_decode", "sparse_page_decode",
     "page_var_update", "gauss_moments", "gauss_select", "entmax15_paged_decode_merged",
     "sparsekv_last_error",
 )
 _INT_RETURNING = ("pagestats_update", "page_score", "page_score_group", "page_topk",
                   "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
-                  "h2o_accumulate", "entmax15_paged_decode", "sparse_select_decode",
+                  "h2o_accumulate", "h2o_accumulate_heads", "entmax15_paged_decode",
+                  "sparse_select_decode",
                   "sparse_page_decode", "page_var_update", "gauss_moments", "gauss_select",
                   "entmax15_paged_decode_merged")
 
@@ -83,6 +86,9 @@ def load_library():
                                    L, V, L, V]
     lib.h2o_scratch_floats.argtypes = [I, I, L]
     lib.h2o_scratch_floats.restype = ctypes.c_int64
+    lib.h2o_accumulate_heads.argtypes = lib.h2o_accumulate.argtypes
+    lib.h2o_heads_scratch_floats.argtypes = [I, I, L]
+    lib.h2o_heads_scratch_floats.restype = ctypes.c_int64
     lib.entmax15_paged_decode.argtypes = [V, I, I, I, I, V, L, I, V, L, V, V, V, V, I, I,
                                           F, I, V, V, V, V, L, V]
     lib.entmax15_paged_decode_merged.argtypes = [V, I, I, I, I, V, L, I, V, L, V, V, V, V,
@@ -596,11 +602,12 @@ def h2o_scratch_floats(B, H_kv, max_tokens) -> int:
     return int(load_library().h2o_scratch_floats(int(B), int(H_kv), int(max_tokens)))
 
 
-def h2o_accumulate(q, kv_cache, block_table, seq_lens, hh_score, scores, scratch,
-                   scale, decay=0.984375, reserved_bos=0, reserved_eos=1,
-                   stream=None):
-    """Token-level H2O step (page_size 1): updates hh_score in place and writes
-    the new values as scores [B, H_kv, score_ld]."""
+def h2o_heads_scratch_floats(B, H_q, max_tokens) -> int:
+    return int(load_library().h2o_heads_scratch_floats(int(B), int(H_q), int(max_tokens)))
+
+
+def _h2o(name, q, kv_cache, block_table, seq_lens, hh_score, scores, scratch, scale,
+         decay, reserved_bos, reserved_eos, stream):
     lib = load_library()
     _check("q", q, torch.float32, 3)
     dev = q.device
@@ -616,8 +623,26 @@ def h2o_accumulate(q, kv_cache, block_table, seq_lens, hh_score, scores, scratch
         raise ValueError("hh_score must be [num_blocks, H_kv]")
     if tuple(scores.shape[:2]) != (B, H_kv):
         raise ValueError("scores must be [B, H_kv, score_ld]")
-    _rc("h2o_accumulate", lib.h2o_accumulate(
+    _rc(name, getattr(lib, name)(
         _ptr(q), B, H_q, H_kv, D, _ptr(kv_cache), NB, P, _ptr(block_table),
         block_table.shape[1], _ptr(seq_lens), int(reserved_bos), int(reserved_eos),
         float(scale), float(decay), _ptr(hh_score), _ptr(scores), scores.shape[2],
         _ptr(scratch), scratch.numel(), _stream(stream)))
+
+
+def h2o_accumulate(q, kv_cache, block_table, seq_lens, hh_score, scores, scratch,
+                   scale, decay=0.984375, reserved_bos=0, reserved_eos=1,
+                   stream=None):
+    """Token-level H2O step (page_size 1), group-mean query: updates hh_score in
+    place and writes the new values as scores [B, H_kv, score_ld]."""
+    _h2o("h2o_accumulate", q, kv_cache, block_table, seq_lens, hh_score, scores,
+         scratch, scale, decay, reserved_bos, reserved_eos, stream)
+
+
+def h2o_accumulate_heads(q, kv_cache, block_table, seq_lens, hh_score, scores, scratch,
+                         scale, decay=0.984375, reserved_bos=0, reserved_eos=1,
+                         stream=None):
+    """The same step with every query head's own softmax, averaged over its
+    group; scratch of h2o_heads_scratch_floats(B, H_q, bt_ld) floats."""
+    _h2o("h2o_accumulate_heads", q, kv_cache, block_table, seq_lens, hh_score, scores,
+         scratch, scale, decay, reserved_bos, reserved_eos, stream)

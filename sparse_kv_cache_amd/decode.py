@@ -8,7 +8,8 @@ library's entry points in the order of a decode step:
                -> sparse_paged_decode -> lse_merge
   group level  as page level with page_score_group: one selection per kv
                head, shared by its query group
-  token level  pagestats_update (append + hh reset) -> h2o_accumulate
+  token level  pagestats_update (append + hh reset) -> h2o_accumulate (or
+               h2o_accumulate_heads: per-head softmax averaged over the group)
                -> page_topk (per kv head) -> sparse_paged_decode -> lse_merge
   Gaussian     [pagestats_update + page_var_update (tail page)]
                -> gauss_moments -> gauss_select -> entmax15_paged_decode
@@ -26,7 +27,8 @@ import torch
 
 from . import (entmax15_paged_decode, entmax15_paged_decode_merged, entmax_scratch_floats,
                gauss_moments, gauss_select,
-               h2o_accumulate, h2o_scratch_floats, lse_merge, page_score,
+               h2o_accumulate, h2o_accumulate_heads, h2o_heads_scratch_floats,
+               h2o_scratch_floats, lse_merge, page_score,
                page_score_group, page_topk, page_var_update, pagestats_update,
                sparse_page_decode, sparse_paged_decode, sparse_paged_decode_merged,
                sparse_select_decode)
@@ -49,7 +51,10 @@ class SparseDecoder:
     """Buffers and call order of one decode step.
 
     kv_cache: bf16 [2, num_blocks, P, H_kv, D]; block_table int32 [B, bt_ld].
-    token_level=True selects the H2O flow (page_size must be 1);
+    token_level=True selects the H2O flow (page_size must be 1); its query
+    group enters the accumulator through the group-mean query
+    (h2o_softmax="group_mean") or through every head's own softmax, averaged
+    over the group (h2o_softmax="per_head");
     group_select=True scores and selects once per kv head (page level);
     alibi_slopes (fp32 [H_q] on the device) adds ALiBi to scoring and decode.
     With one selection per query head and num_splits <= 8 the split merge runs
@@ -66,7 +71,7 @@ class SparseDecoder:
                  scale=None, num_splits=1, decay=0.984375, token_level=False,
                  group_select=False, alibi_slopes=None, fuse_merge=True,
                  attention=None, selection="topk", gauss_cap=None, gauss_mixture=None,
-                 device="cuda"):
+                 h2o_softmax="group_mean", device="cuda"):
         self.B, self.H_q, self.H_kv, self.D = B, H_q, H_kv, D
         self.num_blocks, self.P, self.bt_ld = num_blocks, page_size, bt_ld
         self.topk_pages, self.topk_frac = topk_pages, topk_frac
@@ -79,6 +84,9 @@ class SparseDecoder:
         dev = torch.device(device)
         if alibi_slopes is not None and token_level:
             raise ValueError("ALiBi is not part of the token-level flow")
+        if h2o_softmax not in ("group_mean", "per_head"):
+            raise ValueError("h2o_softmax must be 'group_mean' or 'per_head'")
+        self.h2o_per_head = token_level and h2o_softmax == "per_head"
         if selection not in ("topk", "gauss"):
             raise ValueError("selection must be 'topk' or 'gauss'")
         if attention is None:
@@ -108,7 +116,8 @@ class SparseDecoder:
                 raise ValueError("the token-level flow needs page_size 1")
             self.k_min = self.k_max = self.k_mean = None
             self.hh = torch.zeros((num_blocks, H_kv), dtype=bf, device=dev)
-            n = h2o_scratch_floats(B, H_kv, bt_ld)
+            n = (h2o_heads_scratch_floats(B, H_q, bt_ld) if self.h2o_per_head
+                 else h2o_scratch_floats(B, H_kv, bt_ld))
             self.scratch = torch.empty(n, dtype=f32, device=dev)
         else:
             self.k_min = torch.empty((num_blocks, H_kv, D), dtype=bf, device=dev)
@@ -167,7 +176,8 @@ class SparseDecoder:
     @classmethod
     def for_workload(cls, wl, device="cuda", num_splits=None, group_select=False,
                      alibi_slopes=None, fuse_merge=True, attention=None,
-                     selection="topk", gauss_cap=None, gauss_mixture=None):
+                     selection="topk", gauss_cap=None, gauss_mixture=None,
+                     h2o_softmax="group_mean"):
         return cls(wl.B, wl.H_q, wl.H_kv, wl.D, wl.num_blocks, wl.P, wl.bt_ld,
                    topk_pages=wl.topk_pages, topk_frac=wl.topk_frac, bos=wl.bos,
                    eos=wl.eos, w_avg=wl.w_avg, w_peak=wl.w_peak,
@@ -176,7 +186,8 @@ class SparseDecoder:
                    decay=wl.decay, token_level=(wl.name == "h2o_token"),
                    group_select=group_select, alibi_slopes=alibi_slopes,
                    fuse_merge=fuse_merge, attention=attention, selection=selection,
-                   gauss_cap=gauss_cap, gauss_mixture=gauss_mixture, device=device)
+                   gauss_cap=gauss_cap, gauss_mixture=gauss_mixture,
+                   h2o_softmax=h2o_softmax, device=device)
 
     # ------------------------------------------------------------ stages
     def rebuild_stats(self, kv_cache, block_table, seq_lens, stream=None):
@@ -221,7 +232,8 @@ class SparseDecoder:
            stream=stream)
 
     def accumulate(self, q, kv_cache, block_table, seq_lens, stream=None):
-        h2o_accumulate(q, kv_cache, block_table, seq_lens, self.hh, self.scores,
+        fn = h2o_accumulate_heads if self.h2o_per_head else h2o_accumulate
+        fn(q, kv_cache, block_table, seq_lens, self.hh, self.scores,
                        self.scratch, self.scale, self.decay, self.bos, self.eos,
                        stream=stream)
 

@@ -45,6 +45,7 @@ def test_header_declares_the_six_operations():
               "sparse_page_decode", "page_var_update", "gauss_moments", "gauss_select",
               "entmax15_paged_decode_merged",
               "lse_merge", "h2o_accumulate", "h2o_scratch_floats",
+              "h2o_accumulate_heads", "h2o_heads_scratch_floats",
               "sparsekv_last_error"):
         assert n in names
     assert set(names) == set(skv.EXPORTED_SYMBOLS)
@@ -169,6 +170,20 @@ def test_validation_rejects_bad_scalars(lib):
     assert lib.h2o_accumulate(p, 1, 8, 2, 128, p, 8, 1, p, 8, p, 0, 1, 0.1, 0.98,
                               p, p, 8, p, 3, s) == EINVAL
     assert "scratch" in _msg(lib)
+    # per-head reading: its scratch holds H_q logit rows, not H_kv
+    small = lib.h2o_scratch_floats(1, 2, 8)
+    assert lib.h2o_accumulate_heads(p, 1, 8, 2, 128, p, 8, 1, p, 8, p, 0, 1, 0.1, 0.98,
+                                    p, p, 8, p, small, s) == EINVAL
+    assert "h2o_accumulate_heads" in _msg(lib) and "scratch" in _msg(lib)
+    assert lib.h2o_accumulate_heads(p, 1, 8, 2, 128, p, 8, 16, p, 8, p, 0, 1, 0.1, 0.98,
+                                    p, p, 8, p, 10 ** 6, s) == EINVAL
+    # the request's query rows and one chunk's logits must fit one block's LDS
+    assert lib.h2o_accumulate_heads(p, 1, 128, 8, 128, p, 8, 1, p, 8, p, 0, 1, 0.1, 0.98,
+                                    p, p, 8, p, 10 ** 7, s) == EINVAL
+    assert "LDS" in _msg(lib)
+    assert lib.h2o_accumulate_heads(None, 1, 8, 2, 128, p, 8, 1, p, 8, p, 0, 1, 0.1, 0.98,
+                                    p, p, 8, p, 10 ** 6, s) == EFAULT
+    assert "h2o_accumulate_heads: q" in _msg(lib)
     assert lib.lse_merge(p, p, 4, 0, 128, p, None, s) == EINVAL
 
 
@@ -205,6 +220,8 @@ def test_scratch_size_query(lib):
     assert n == 4 * 8 * 4352 + 4 * 8 * chunks * 2
     assert lib.h2o_scratch_floats(1, 0, 10) == -1
     assert skv.h2o_scratch_floats(4, 8, 4352) == n
+    assert lib.h2o_heads_scratch_floats(4, 32, 4352) == 4 * 32 * 4352 + 4 * 32 * chunks * 2
+    assert skv.h2o_heads_scratch_floats(4, 32, 4352) == lib.h2o_heads_scratch_floats(4, 32, 4352)
 
 
 def test_product_package_never_imports_the_oracle():

@@ -641,9 +641,12 @@ def test_append_refresh_and_reset(P):
                 wl.seq_lens, P, used)
 
 
-def test_token_level_step_teacher_forced():
-    say("[gpu] h2o small, teacher forced")
-    S0, B, H_q, H_kv, D = 300, 3, 8, 2, 128
+@pytest.mark.parametrize("reading,H_q,H_kv,D", [
+    ("group_mean", 8, 2, 128), ("per_head", 8, 2, 128), ("per_head", 80, 16, 128),
+    ("per_head", 12, 4, 64), ("group_mean", 12, 4, 64)])
+def test_token_level_step_teacher_forced(reading, H_q, H_kv, D):
+    say(f"[gpu] h2o small, teacher forced, {reading} H_q {H_q} H_kv {H_kv} D {D}")
+    S0, B = 300, 3
     wl = W.h2o_token(seed=40, steps=6, prompt=S0, B=B)
     wl.H_q, wl.H_kv, wl.D = H_q, H_kv, D
     wl.bos, wl.eos, wl.topk_pages, wl.num_splits = 4, 8, 40, 5
@@ -653,7 +656,7 @@ def test_token_level_step_teacher_forced():
     d = SparseDecoder(B, H_q, H_kv, D, wl.num_blocks, 1, wl.bt_ld,
                       topk_pages=wl.topk_pages, bos=wl.bos, eos=wl.eos,
                       scale=wl.softmax_scale, num_splits=wl.num_splits,
-                      token_level=True)
+                      token_level=True, h2o_softmax=reading)
     d.hh.copy_(W.make_hh(wl).cuda())
     for step in range(wl.steps):
         sl_np = wl.seq_lens_at(step)
@@ -676,7 +679,8 @@ def test_token_level_step_teacher_forced():
         hh_ref = pre_hh.copy()
         qd = q_cpu.double().numpy()
         ref_scores = oracle.h2o_step(qd, pre_cache, wl.block_table, sl_np, hh_ref,
-                                     wl.bos, wl.eos, wl.softmax_scale, wl.decay)
+                                     wl.bos, wl.eos, wl.softmax_scale, wl.decay,
+                                     per_head=(reading == "per_head"))
         gh = bits(d.hh)
         apart = bf16_bits_apart(gh, hh_ref)
         assert apart.max() <= 1, f"step {step}: hh more than one ulp off"

@@ -5,7 +5,8 @@ mha_tiny, gqa_ragged and long_context are compared in full (gqa_ragged and
 long_context also with one selection per kv head); high_batch on a
 sample of requests (shortest, longest and three others) after two appended
 steps; h2o_token teacher-forced at its first two steps and its last step, plus
-the probability-mass invariant after all 256 steps."""
+the probability-mass invariant after all 256 steps, in both readings of the
+query group (group-mean query and per-head softmax)."""
 import numpy as np
 import pytest
 import torch
@@ -172,11 +173,12 @@ def test_high_batch_sampled_after_appends():
     say(f"  high_batch: max |out - oracle| {worst:.2e}, near-tie rows {ex}")
 
 
-def test_h2o_token_sequence():
+@pytest.mark.parametrize("reading", ["group_mean", "per_head"])
+def test_h2o_token_sequence(reading):
     wl = W.h2o_token()
-    say("[gpu] workload h2o_token: generating")
+    say(f"[gpu] workload h2o_token ({reading}): generating")
     cache = W.make_cache(wl, device="cuda")
-    d = SparseDecoder.for_workload(wl)
+    d = SparseDecoder.for_workload(wl, h2o_softmax=reading)
     d.hh.copy_(W.make_hh(wl, device="cuda"))
     bt = dev(wl.block_table)
     checked = {0, 1, wl.steps - 1}
@@ -203,7 +205,8 @@ def test_h2o_token_sequence():
         qd = q_cpu.double().numpy()
         hh_ref = pre_hh.copy()
         ref = oracle.h2o_step(qd, pre_cache, wl.block_table, sl_np, hh_ref, wl.bos,
-                              wl.eos, wl.softmax_scale, wl.decay)
+                              wl.eos, wl.softmax_scale, wl.decay,
+                              per_head=(reading == "per_head"))
         gh = bits(d.hh)
         apart = bf16_bits_apart(gh, hh_ref)
         assert apart.max() <= 1
