@@ -117,13 +117,13 @@ __global__ __launch_bounds__(256) void page_score_kernel(
     skv::unpack8(mx[it], hi);
     const float me[8] = {me0[it].x, me0[it].y, me0[it].z, me0[it].w,
                          me1[it].x, me1[it].y, me1[it].z, me1[it].w};
+    // w_peak / 2 is exact, so folding it saves the two halvings
+    const float wp2 = 0.5f * w_peak;
     float mp[8], hp[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float mid = (hi[i] + lo[i]) * 0.5f;
-      const float half = (hi[i] - lo[i]) * 0.5f;
-      mp[i] = fmaf(w_avg, me[i], w_peak * mid);
-      hp[i] = w_peak * half;
+      mp[i] = fmaf(wp2, hi[i] + lo[i], w_avg * me[i]);
+      hp[i] = wp2 * (hi[i] - lo[i]);
     }
     // ALiBi at the page's last (peak term) and mean (mean term) valid
     // positions, relative to the query at S - 1

@@ -188,8 +188,9 @@ __device__ __forceinline__ Chunk split_chunk(int cnt, int k_cap, int num_splits,
 // its query head's score row (TKI entries per thread) into LDS, then decodes
 // from there; the selection is copied out only when asked.
 // With SC as well, the block also scores its query head's pages from the page
-// statistics first (page_score's arithmetic, into LDS), so one launch runs
-// the whole page-level step.
+// statistics first (the page score, into LDS; one query head per block, so
+// the peak term picks each dim's envelope by the query's sign), so one launch
+// runs the whole page-level step.
 struct TopkArgs {
   const float* scores; int64_t score_ld; int topk_pages; double topk_frac;
   int bos, eos; int32_t* sel_idx; int32_t* sel_cnt; int32_t* sel_blk;
@@ -271,6 +272,21 @@ void sparse_decode_wave_kernel(
       }
       // ALiBi in score units: slope / softmax scale
       const float sslope = AL ? alibi[h * G + g] * ta.inv_scale : 0.0f;
+      // The peak term taken as written: dim d contributes q_d * max_d where
+      // q_d >= 0 and q_d * min_d elsewhere.  This lane's dims are fixed, so
+      // the choice is a bit mask per packed pair of bf16 envelope values (one
+      // bitfield select per two dims), and the weights fold into the query.
+      float qa[8], qp[8];
+      uint32_t env_mask[4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        qa[i] = ta.w_avg * qv[i];
+        qp[i] = ta.w_peak * qv[i];
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        env_mask[k] = (qv[2 * k] >= 0.0f ? 0x0000ffffu : 0u) |
+                      (qv[2 * k + 1] >= 0.0f ? 0xffff0000u : 0u);
       __syncthreads();
       constexpr int KI = SKV_SCORE_KI;            // page loads in flight per lane
       for (int p0 = 0; p0 < Nt; p0 += WB * RPL * KI) {
@@ -289,20 +305,20 @@ void sparse_decode_wave_kernel(
         }
 #pragma unroll
         for (int it = 0; it < KI; ++it) {
-          float lo[8], hi[8];
-          skv::unpack8(mn[it], lo);
-          skv::unpack8(mx[it], hi);
           const float me[8] = {me0[it].x, me0[it].y, me0[it].z, me0[it].w,
                                me1[it].x, me1[it].y, me1[it].z, me1[it].w};
-          float sc = 0.0f;
+          const uint32_t mnw[4] = {mn[it].x, mn[it].y, mn[it].z, mn[it].w};
+          const uint32_t mxw[4] = {mx[it].x, mx[it].y, mx[it].z, mx[it].w};
+          float s_env = 0.0f, s_avg = 0.0f;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            // max(q max, q min) = q mid + |q| half (exact split, both terms)
-            const float mp = fmaf(ta.w_avg, me[i], ta.w_peak * ((hi[i] + lo[i]) * 0.5f));
-            const float hp = ta.w_peak * ((hi[i] - lo[i]) * 0.5f);
-            sc = fmaf(qv[i], mp, fmaf(fabsf(qv[i]), hp, sc));
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t e = (mxw[k] & env_mask[k]) | (mnw[k] & ~env_mask[k]);
+            s_env = fmaf(qp[2 * k], __uint_as_float(e << 16), s_env);
+            s_env = fmaf(qp[2 * k + 1], __uint_as_float(e & 0xffff0000u), s_env);
+            s_avg = fmaf(qa[2 * k], me[2 * k], s_avg);
+            s_avg = fmaf(qa[2 * k + 1], me[2 * k + 1], s_avg);
           }
-          sc = skv::group_sum<LPR>(sc);
+          float sc = skv::group_sum<LPR>(s_env + s_avg);
           if (AL) {
             const int pp = pg[it] < Nt ? pg[it] : 0;
             const int nn = S - pp * P;
