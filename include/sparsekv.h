@@ -467,9 +467,11 @@ int64_t h2o_scratch_floats(int B, int H_kv, int64_t max_tokens);
  *   p = (1/G) sum_g p_g (still one unit of mass per step) feeds the same
  *   recurrence, hh_t <- bf16( bf16(p_t) + bf16(decay) * hh_t ) for t in W.
  *   Arguments, layouts and errors as h2o_accumulate, except that the scratch
- *   holds h2o_heads_scratch_floats(B, H_q, bt_ld) floats and H_q * (D + 64)
- *   must stay within 16320 (the query rows and one chunk's logits of a request
- *   sit in one block's 64 KiB of LDS; SKV_EINVAL otherwise).
+ *   holds h2o_heads_scratch_floats(B, H_q, bt_ld) floats and
+ *   H_q * (D + 72) + 64 must stay within 16384 (a request's query rows as
+ *   bf16 halves and one 64-token chunk's logits sit in one block's 64 KiB of
+ *   LDS; SKV_EINVAL otherwise).  The logits run on the matrix cores with the
+ *   query as bf16 hi + lo halves (about 16 significant bits).
  */
 int h2o_accumulate_heads(const float *q, int B, int H_q, int H_kv, int D,
                          const uint16_t *kv_cache, int64_t num_blocks,

@@ -12,11 +12,11 @@
 //
 // Two launches over (token chunk, request):
 //   1. logits l_t = scale * log2(e) * q_r . k_t over 64-token chunks for every
-//      logit row r: one per kv head (q_r = the group-mean query) or one per
-//      query head (its own query).  16 waves per chunk, every kv-head row read
-//      once with 16-byte loads, D/8 lanes per row, dotted with each of the
-//      head's logit-row queries; the chunk's (max, sum 2^(l - max)) per logit
-//      row go to scratch.
+//      logit row r: one per kv head (q_r = the group-mean query: fp32 dot
+//      products, D/8 lanes per row) or one per query head (its own query: the
+//      group's rows at once on the matrix cores).  16 waves per chunk, every
+//      kv-head row read once with 16-byte loads; the chunk's
+//      (max, sum 2^(l - max)) per logit row go to scratch.
 //   2. merge of the chunk partials into (M, Z) per logit row, then per token
 //      and kv head: p = 2^(l - M) / Z (per-head reading: the mean of that over
 //      the group's rows), hh <- bf16(bf16(p) + decay * hh) (one fp32 fma, then
@@ -44,15 +44,14 @@ __device__ __forceinline__ void window(int S, int64_t bt_ld, int bos, int eos,
   *ntok = n; *lo = l; *hi = h;
 }
 
-// Logits of one 64-token chunk of one request for every logit row.  The
-// chunk's H_kv * 64 kv-head rows are dealt to 16 waves, 4 * H_kv rows each; a
-// wave issues all its 16-byte row loads (NLD per lane) before any arithmetic,
-// masked rows reading a placeholder so the loads stay unconditional.  PH: GR =
-// G logit rows per kv head (the group's own queries), else GR = 1 (the mean).
-// HM (H_kv divides 16): the rows are dealt head-major, so every row of a wave
-// belongs to one kv head and each lane reads that head's query slices from
-// LDS once per four logit rows, not once per key row.
-template <int D, int NLD, bool PH, bool HM>
+// Logits of one 64-token chunk of one request, one logit row per kv head (the
+// group-mean query).  The chunk's H_kv * 64 kv-head rows are dealt to 16
+// waves, 4 * H_kv rows each; a wave issues all its 16-byte row loads (NLD per
+// lane) before any arithmetic, masked rows reading a placeholder so the loads
+// stay unconditional.  HM (H_kv divides 16): the rows are dealt head-major,
+// so every row of a wave belongs to one kv head and each lane reads that
+// head's query slice from LDS once, not once per key row.
+template <int D, int NLD, bool HM>
 __global__ __launch_bounds__(kLWaves * 64) void h2o_logits_kernel(
     const float* __restrict__ q, int H_q, int H_kv, int G,
     const uint16_t* __restrict__ kv, const int32_t* __restrict__ bt,
@@ -61,12 +60,10 @@ __global__ __launch_bounds__(kLWaves * 64) void h2o_logits_kernel(
     int nchunk) {
   constexpr int LPR = D / 8;
   constexpr int RPW = 64 / LPR;                // head rows per wave load
-  const int GR = PH ? G : 1;                   // logit rows per kv head
-  const int HR = H_kv * GR;                    // logit rows per request
   extern __shared__ float smem[];
-  float* qs = smem;                            // [HR][D]
-  float* lg = smem + HR * D;                   // [HR][kChunk]
-  int* sblk = reinterpret_cast<int*>(lg + HR * kChunk);     // [kChunk]
+  float* qs = smem;                            // [H_kv][D]
+  float* lg = smem + H_kv * D;                 // [H_kv][kChunk]
+  int* sblk = reinterpret_cast<int*>(lg + H_kv * kChunk);   // [kChunk]
   const int b = blockIdx.y;
   const int c = blockIdx.x;
   int ntok, lo, hi;
@@ -79,17 +76,12 @@ __global__ __launch_bounds__(kLWaves * 64) void h2o_logits_kernel(
   const int32_t* btr = bt + static_cast<int64_t>(b) * bt_ld;
 
   if (tid < kChunk) sblk[tid] = t0 + tid < ntok ? btr[t0 + tid] : 0;
-  if constexpr (PH) {
-    for (int i = tid; i < H_q * D; i += blockDim.x)
-      qs[i] = q[static_cast<int64_t>(b) * H_q * D + i] * scale_log2;
-  } else {
-    const float inv_g = 1.0f / static_cast<float>(G);
-    for (int i = tid; i < H_kv * D; i += blockDim.x) {
-      const int h = i / D, d = i % D;
-      float s = 0.0f;
-      for (int g = 0; g < G; ++g) s += q[(static_cast<int64_t>(b) * H_q + h * G + g) * D + d];
-      qs[i] = s * inv_g * scale_log2;
-    }
+  const float inv_g = 1.0f / static_cast<float>(G);
+  for (int i = tid; i < H_kv * D; i += blockDim.x) {
+    const int h = i / D, d = i % D;
+    float s = 0.0f;
+    for (int g = 0; g < G; ++g) s += q[(static_cast<int64_t>(b) * H_q + h * G + g) * D + d];
+    qs[i] = s * inv_g * scale_log2;
   }
   __syncthreads();
 
@@ -113,70 +105,149 @@ __global__ __launch_bounds__(kLWaves * 64) void h2o_logits_kernel(
                               : cc * 8;
     kr[u] = *reinterpret_cast<const uint4*>(kv + off);
   }
-  auto dot8 = [](const float* qr, const float (&x)[8]) {
-    const float4 qa = *reinterpret_cast<const float4*>(qr);
-    const float4 qb = *reinterpret_cast<const float4*>(qr + 4);
-    float dot = qa.x * x[0];
-    dot = fmaf(qa.y, x[1], dot); dot = fmaf(qa.z, x[2], dot); dot = fmaf(qa.w, x[3], dot);
-    dot = fmaf(qb.x, x[4], dot); dot = fmaf(qb.y, x[5], dot); dot = fmaf(qb.z, x[6], dot);
-    return fmaf(qb.w, x[7], dot);
-  };
+  // HM: the wave's kv head and its query slice in registers
+  float qv[8];
   if constexpr (HM) {
-    // the wave's kv head; four of its logit rows' query slices in registers
-    const int hw = (wave * R) / kChunk;
-    for (int g0 = 0; g0 < GR; g0 += 4) {
-      float qv[4][8];
+    const float* qr = qs + ((wave * R) / kChunk) * D + cc * 8;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int g = g0 + j < GR ? g0 + j : GR - 1;
-        const float* qr = qs + (hw * GR + g) * D + cc * 8;
+    for (int i = 0; i < 8; ++i) qv[i] = qr[i];
+  }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) qv[j][i] = qr[i];
-      }
+  for (int u = 0; u < NLD; ++u) {
+    const int rl = u * RPW + sub;
+    int tt, h;
+    row_of(rl, tt, h);
+    float x[8];
+    skv::unpack8(kr[u], x);
+    if constexpr (!HM) {
+      const float* qr = qs + (rl < R ? h : 0) * D + cc * 8;
 #pragma unroll
-      for (int u = 0; u < NLD; ++u) {
-        const int rl = u * RPW + sub;
-        int tt, h;
-        row_of(rl, tt, h);
-        float x[8];
-        skv::unpack8(kr[u], x);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (g0 + j >= GR) break;
-          float dot = qv[j][0] * x[0];
-#pragma unroll
-          for (int i = 1; i < 8; ++i) dot = fmaf(qv[j][i], x[i], dot);
-          dot = skv::group_sum<LPR>(dot);
-          if (rl < R && cc == 0) lg[(hw * GR + g0 + j) * kChunk + tt] = ok[u] ? dot : -INFINITY;
-        }
-      }
+      for (int i = 0; i < 8; ++i) qv[i] = qr[i];
     }
-  } else {
+    float dot = qv[0] * x[0];
 #pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const int rl = u * RPW + sub;
-      int tt, h;
-      row_of(rl, tt, h);
-      float x[8];
-      skv::unpack8(kr[u], x);
-      for (int gi = 0; gi < GR; ++gi) {
-        float dot = dot8(qs + (rl < R ? h * GR + gi : 0) * D + cc * 8, x);
-        dot = skv::group_sum<LPR>(dot);
-        if (rl < R && cc == 0) lg[(h * GR + gi) * kChunk + tt] = ok[u] ? dot : -INFINITY;
+    for (int i = 1; i < 8; ++i) dot = fmaf(qv[i], x[i], dot);
+    dot = skv::group_sum<LPR>(dot);
+    if (rl < R && cc == 0) lg[h * kChunk + tt] = ok[u] ? dot : -INFINITY;
+  }
+  __syncthreads();
+
+  const int nt = min(kChunk, ntok - t0);
+  for (int h = wave; h < H_kv; h += kLWaves) {
+    const float v = lane < nt ? lg[h * kChunk + lane] : -INFINITY;
+    const float m = skv::wave_max(v);
+    float e = (m != -INFINITY && lane < nt) ? exp2f(v - m) : 0.0f;
+    const float s = skv::wave_sum(e);
+    if (lane < nt) logits[(static_cast<int64_t>(b) * H_kv + h) * bt_ld + t0 + lane] = v;
+    if (lane == 0) {
+      float* pp = part + ((static_cast<int64_t>(b) * H_kv + h) * nchunk + c) * 2;
+      pp[0] = m;
+      pp[1] = s;
+    }
+  }
+}
+
+// Per-head logits on the matrix cores (the per-head reading).  A chunk's
+// kv-head rows form 4 * H_kv tiles of (kv head h, 16 tokens), dealt to the 16
+// waves (up to TPW each).  Per tile
+//   S (16 tokens x 16 query heads) = K (16 x D) . Q^T (D x 16)
+// with 16x16x32 bf16 MFMAs: the 16-byte row pieces a lane loads are exactly
+// its A operand (row lane & 15, dims c*32 + 8*(lane >> 4) .. +8), the group's
+// queries (scaled by scale * log2(e)) are the B operand as bf16 hi + lo
+// halves (two MFMAs per 32 dims, about 16 significant bits), columns past G
+// are zero, and lane (n, kq) ends with rows 4*kq .. 4*kq + 3 of column n.
+// The query halves sit in LDS with rows padded by 8 bf16 so that the 16 rows
+// a quarter-wave reads fall in different banks.
+template <int D, int TPW>
+__global__ __launch_bounds__(kLWaves * 64) void h2o_logits_heads_kernel(
+    const float* __restrict__ q, int H_q, int H_kv, int G,
+    const uint16_t* __restrict__ kv, const int32_t* __restrict__ bt,
+    int64_t bt_ld, const int32_t* __restrict__ seq_lens, int bos, int eos,
+    float scale_log2, float* __restrict__ logits, float* __restrict__ part,
+    int nchunk) {
+  constexpr int NC = D / 32;                   // 32-dim steps of the MFMA
+  constexpr int QS = D + 8;                    // padded query row (bf16)
+  constexpr int LGS = kChunk + 4;              // padded logit row (floats)
+  extern __shared__ float smem[];
+  uint16_t* qh = reinterpret_cast<uint16_t*>(smem);          // [H_q][QS]
+  uint16_t* ql = qh + H_q * QS;                              // [H_q][QS]
+  float* lg = smem + H_q * QS;                               // [H_q][LGS]
+  int* sblk = reinterpret_cast<int*>(lg + H_q * LGS);        // [kChunk]
+  const int b = blockIdx.y;
+  const int c = blockIdx.x;
+  int ntok, lo, hi;
+  window(seq_lens[b], bt_ld, bos, eos, &ntok, &lo, &hi);
+  const int t0 = c * kChunk;
+  if (t0 >= ntok) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, kq = lane >> 4;
+  const int32_t* btr = bt + static_cast<int64_t>(b) * bt_ld;
+
+  if (tid < kChunk) sblk[tid] = t0 + tid < ntok ? btr[t0 + tid] : 0;
+  for (int i = tid; i < H_q * D; i += blockDim.x) {
+    const int r = i / D, d = i % D;
+    const float x = q[static_cast<int64_t>(b) * H_q * D + i] * scale_log2;
+    const uint16_t hb = skv::f32_to_bf16(x);
+    qh[r * QS + d] = hb;
+    ql[r * QS + d] = skv::f32_to_bf16(x - skv::bf16_to_f32(hb));
+  }
+  __syncthreads();
+
+  const int ntile = 4 * H_kv;
+  uint4 kt[TPW][NC];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int t = wave + kLWaves * j;
+    const int h = t < ntile ? t / 4 : 0;
+    const int tt = (t % 4) * 16 + n;           // the row this lane loads
+    const int tok = t0 + tt;
+    const bool ok = t < ntile && tok >= lo && tok < hi;
+    const int64_t off = (ok ? (static_cast<int64_t>(sblk[tt]) * H_kv + h) * D : 0) + 8 * kq;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+      kt[j][cc] = *reinterpret_cast<const uint4*>(kv + off + cc * 32);
+  }
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int t = wave + kLWaves * j;
+    if (t >= ntile) break;
+    const int h = t / 4, tb = (t % 4) * 16;
+    const bool col = n < G;
+    const int qr = (h * G + (col ? n : 0)) * QS + 8 * kq;
+    skv_f32x4 sacc = skv_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      uint4 bh = *reinterpret_cast<const uint4*>(qh + qr + cc * 32);
+      uint4 bl = *reinterpret_cast<const uint4*>(ql + qr + cc * 32);
+      if (!col) { bh = make_uint4(0u, 0u, 0u, 0u); bl = bh; }
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(skv::as_bf16x8(kt[j][cc]),
+                                                     skv::as_bf16x8(bh), sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(skv::as_bf16x8(kt[j][cc]),
+                                                     skv::as_bf16x8(bl), sacc, 0, 0, 0);
+    }
+    if (col) {
+      float4 v;
+      float* vv = reinterpret_cast<float*>(&v);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = t0 + tb + 4 * kq + i;
+        vv[i] = (tok >= lo && tok < hi) ? sacc[i] : -INFINITY;
       }
+      *reinterpret_cast<float4*>(lg + (h * G + n) * LGS + tb + 4 * kq) = v;
     }
   }
   __syncthreads();
 
   const int nt = min(kChunk, ntok - t0);
-  for (int h = wave; h < HR; h += kLWaves) {
-    const float v = lane < nt ? lg[h * kChunk + lane] : -INFINITY;
+  for (int r = wave; r < H_q; r += kLWaves) {
+    const float v = lane < nt ? lg[r * LGS + lane] : -INFINITY;
     const float m = skv::wave_max(v);
     float e = (m != -INFINITY && lane < nt) ? exp2f(v - m) : 0.0f;
     const float s = skv::wave_sum(e);
-    if (lane < nt) logits[(static_cast<int64_t>(b) * HR + h) * bt_ld + t0 + lane] = v;
+    if (lane < nt) logits[(static_cast<int64_t>(b) * H_q + r) * bt_ld + t0 + lane] = v;
     if (lane == 0) {
-      float* pp = part + ((static_cast<int64_t>(b) * HR + h) * nchunk + c) * 2;
+      float* pp = part + ((static_cast<int64_t>(b) * H_q + r) * nchunk + c) * 2;
       pp[0] = m;
       pp[1] = s;
     }
@@ -295,11 +366,13 @@ int64_t scratch_floats(int B, int rows, int64_t max_tokens) {
   return r * max_tokens + r * nchunks(max_tokens) * 2;
 }
 
-// Logits pass LDS: the logit-row queries, their chunk logits and the chunk's
-// block ids.
-size_t logits_lds(int rows, int D) {
-  return sizeof(float) * (static_cast<size_t>(rows) * D + static_cast<size_t>(rows) * kChunk +
-                          kChunk);
+// Logits pass LDS: the logit-row queries (fp32, or bf16 hi + lo with rows
+// padded by 8 for the per-head pass), their chunk logits (rows padded by 4 for
+// the per-head pass) and the chunk's block ids.
+size_t logits_lds(bool per_head, int rows, int D) {
+  const size_t r = static_cast<size_t>(rows);
+  return per_head ? sizeof(float) * (r * (D + 8) + r * (kChunk + 4) + kChunk)
+                  : sizeof(float) * (r * D + r * kChunk + kChunk);
 }
 constexpr size_t kMaxLogitsLds = 64 * 1024;
 
@@ -319,8 +392,9 @@ int accumulate(const char* fn, const float* q, int B, int H_q, int H_kv, int D,
   const int rows = PH ? H_q : H_kv;
   // (the update pass merges every logit row's partials with at least one of
   // its 256 threads per row; the LDS bound below keeps rows under 128)
-  SKV_REQUIRE(logits_lds(rows, D) <= kMaxLogitsLds,
-              "%s: H_q * (D + 64) too large for one block's LDS (H_q %d, D %d)", fn, H_q, D);
+  SKV_REQUIRE(logits_lds(PH, rows, D) <= kMaxLogitsLds,
+              "%s: the request's query rows and chunk logits exceed one block's LDS "
+              "(%d rows, D %d)", fn, rows, D);
   SKV_REQUIRE(num_blocks > 0 && bt_ld > 0 && score_ld >= bt_ld,
               "%s: need num_blocks > 0, bt_ld > 0, score_ld >= bt_ld", fn);
   SKV_REQUIRE(reserved_bos >= 0 && reserved_eos >= 0,
@@ -347,36 +421,51 @@ int accumulate(const char* fn, const float* q, int B, int H_q, int H_kv, int D,
   // decay is applied as its bf16 value, which is exact for 0.984375
   const float decay_b = skv_host_round_bf16(decay);
   dim3 grid(static_cast<unsigned>(nch), static_cast<unsigned>(B));
-  const size_t sm1 = logits_lds(rows, D);
+  const size_t sm1 = logits_lds(PH, rows, D);
   const float scale_log2 = scale * skv::kLog2e;
-  // 16-byte row loads per lane: 4 * H_kv rows per wave over 64 / (D / 8) rows per load
-  const int rpw = 64 / (D / 8);
-  const int nld = (4 * H_kv + rpw - 1) / rpw;
-  // head-major rows when every wave's rows belong to one kv head (per-head
-  // logits with 16 loads per lane would not fit their query slices beside
-  // the loads in 128 VGPRs)
-  const bool hm = 16 % H_kv == 0 && (!PH || nld <= 8);
+  if constexpr (PH) {
+    // tiles of (kv head, 16 tokens) per wave
+    const int tpw = (4 * H_kv + kLWaves - 1) / kLWaves;
+#define SKV_HEADS(DD, TT)                                                                \
+  hipLaunchKernelGGL((h2o_logits_heads_kernel<DD, TT>), grid, dim3(kLWaves * 64), sm1,   \
+                     stream, q, H_q, H_kv, G, kv_cache, block_table, bt_ld, seq_lens,     \
+                     reserved_bos, reserved_eos, scale_log2, logits, part, nch)
+    if (D == 128) {
+      if (tpw <= 1) SKV_HEADS(128, 1); else if (tpw == 2) SKV_HEADS(128, 2);
+      else if (tpw == 3) SKV_HEADS(128, 3); else SKV_HEADS(128, 4);
+    } else {
+      if (tpw <= 1) SKV_HEADS(64, 1); else if (tpw == 2) SKV_HEADS(64, 2);
+      else if (tpw == 3) SKV_HEADS(64, 3); else SKV_HEADS(64, 4);
+    }
+#undef SKV_HEADS
+  } else {
+    // 16-byte row loads per lane: 4 * H_kv rows per wave over 64 / (D / 8) rows per load
+    const int rpw = 64 / (D / 8);
+    const int nld = (4 * H_kv + rpw - 1) / rpw;
+    // head-major rows when every wave's rows belong to one kv head
+    const bool hm = 16 % H_kv == 0;
 #define SKV_LOGITS(DD, NN)                                                               \
   do {                                                                                   \
     if (hm)                                                                              \
-      hipLaunchKernelGGL((h2o_logits_kernel<DD, NN, PH, true>), grid, dim3(kLWaves * 64), \
+      hipLaunchKernelGGL((h2o_logits_kernel<DD, NN, true>), grid, dim3(kLWaves * 64),     \
                          sm1, stream, q, H_q, H_kv, G, kv_cache, block_table, bt_ld,      \
                          seq_lens, reserved_bos, reserved_eos, scale_log2, logits, part,  \
                          nch);                                                           \
     else                                                                                 \
-      hipLaunchKernelGGL((h2o_logits_kernel<DD, NN, PH, false>), grid, dim3(kLWaves * 64),\
+      hipLaunchKernelGGL((h2o_logits_kernel<DD, NN, false>), grid, dim3(kLWaves * 64),    \
                          sm1, stream, q, H_q, H_kv, G, kv_cache, block_table, bt_ld,      \
                          seq_lens, reserved_bos, reserved_eos, scale_log2, logits, part,  \
                          nch);                                                           \
   } while (0)
-  if (D == 128) {
-    if (nld <= 2) SKV_LOGITS(128, 2); else if (nld <= 4) SKV_LOGITS(128, 4);
-    else if (nld <= 8) SKV_LOGITS(128, 8); else SKV_LOGITS(128, 16);
-  } else {
-    if (nld <= 2) SKV_LOGITS(64, 2); else if (nld <= 4) SKV_LOGITS(64, 4);
-    else SKV_LOGITS(64, 8);
-  }
+    if (D == 128) {
+      if (nld <= 2) SKV_LOGITS(128, 2); else if (nld <= 4) SKV_LOGITS(128, 4);
+      else if (nld <= 8) SKV_LOGITS(128, 8); else SKV_LOGITS(128, 16);
+    } else {
+      if (nld <= 2) SKV_LOGITS(64, 2); else if (nld <= 4) SKV_LOGITS(64, 4);
+      else SKV_LOGITS(64, 8);
+    }
 #undef SKV_LOGITS
+  }
   const size_t sm2 = sizeof(float) * 2 * static_cast<size_t>(rows);
   hipLaunchKernelGGL(h2o_update_kernel<PH>,
                      dim3(static_cast<unsigned>(nupd), static_cast<unsigned>(B)), dim3(256), sm2,

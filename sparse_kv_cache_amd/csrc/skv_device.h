@@ -5,6 +5,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Matrix-core operand types (gfx950 bf16 MFMA).
+typedef __bf16 skv_bf16x8 __attribute__((ext_vector_type(8)));
+typedef short skv_short4 __attribute__((ext_vector_type(4)));
+typedef float skv_f32x4 __attribute__((ext_vector_type(4)));
+
 namespace skv {
 
 constexpr int kWave = 64;
@@ -128,5 +133,10 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* total,
 // log2(e) and ln(2) for base-2 exponentials.
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+// Matrix-core operand of the 16x16x32 bf16 MFMA from 16 loaded bytes.
+__device__ __forceinline__ skv_bf16x8 as_bf16x8(uint4 v) {
+  return __builtin_bit_cast(skv_bf16x8, v);
+}
 
 }  // namespace skv

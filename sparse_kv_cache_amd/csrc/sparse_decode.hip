@@ -535,14 +535,7 @@ void sparse_decode_wave_kernel(
 
 // ------------------------------------------------------------ group kernel
 
-// Matrix-core operand types (gfx950 bf16 MFMA).
-typedef __bf16 skv_bf16x8 __attribute__((ext_vector_type(8)));
-typedef short skv_short4 __attribute__((ext_vector_type(4)));
-typedef float skv_f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ skv_bf16x8 as_bf16x8(uint4 v) {
-  return __builtin_bit_cast(skv_bf16x8, v);
-}
+using skv::as_bf16x8;
 
 // One block per (split, kv head, request) when the whole query group shares
 // one selection: every selected row is read once and serves all G heads.
