@@ -29,8 +29,16 @@
 
 namespace {
 
-constexpr int kChunk = 64;      // tokens per block of the logits pass
-constexpr int kLWaves = 16;     // waves per block of the logits pass
+#ifndef SKV_H2O_CHUNK
+#define SKV_H2O_CHUNK 64
+#endif
+// tokens per block of the logits pass (64 measured best against 32 and 16:
+// the merge of more, smaller chunk partials costs more than the finer grid
+// gains)
+constexpr int kChunk = SKV_H2O_CHUNK;
+constexpr int kLWaves = kChunk / 4;     // waves per block: 4 tokens' rows each
+constexpr int kTiles = kChunk / 16;     // 16-token MFMA tiles per kv head
+static_assert(kChunk % 16 == 0 && kChunk <= 64, "chunk of 16, 32, 48 or 64 tokens");
 constexpr int kUpd = 64;        // tokens per block of the update pass
 
 __device__ __forceinline__ void window(int S, int64_t bt_ld, int bos, int eos,
@@ -44,13 +52,14 @@ __device__ __forceinline__ void window(int S, int64_t bt_ld, int bos, int eos,
   *ntok = n; *lo = l; *hi = h;
 }
 
-// Logits of one 64-token chunk of one request, one logit row per kv head (the
-// group-mean query).  The chunk's H_kv * 64 kv-head rows are dealt to 16
-// waves, 4 * H_kv rows each; a wave issues all its 16-byte row loads (NLD per
-// lane) before any arithmetic, masked rows reading a placeholder so the loads
-// stay unconditional.  HM (H_kv divides 16): the rows are dealt head-major,
-// so every row of a wave belongs to one kv head and each lane reads that
-// head's query slice from LDS once, not once per key row.
+// Logits of one chunk of kChunk tokens of one request, one logit row per kv
+// head (the group-mean query).  The chunk's H_kv * kChunk kv-head rows are
+// dealt to kChunk / 4 waves, 4 * H_kv rows each; a wave issues all its 16-byte
+// row loads (NLD per lane) before any arithmetic, masked rows reading a
+// placeholder so the loads stay unconditional.  HM (4 * H_kv divides the
+// chunk): the rows are dealt head-major, so every row of a wave belongs to one
+// kv head and each lane reads that head's query slice from LDS once, not once
+// per key row.
 template <int D, int NLD, bool HM>
 __global__ __launch_bounds__(kLWaves * 64) void h2o_logits_kernel(
     const float* __restrict__ q, int H_q, int H_kv, int G,
@@ -148,8 +157,8 @@ __global__ __launch_bounds__(kLWaves * 64) void h2o_logits_kernel(
 }
 
 // Per-head logits on the matrix cores (the per-head reading).  A chunk's
-// kv-head rows form 4 * H_kv tiles of (kv head h, 16 tokens), dealt to the 16
-// waves (up to TPW each).  Per tile
+// kv-head rows form kTiles * H_kv tiles of (kv head h, 16 tokens), dealt to
+// the kLWaves waves (up to TPW each).  Per tile
 //   S (16 tokens x 16 query heads) = K (16 x D) . Q^T (D x 16)
 // with 16x16x32 bf16 MFMAs: the 16-byte row pieces a lane loads are exactly
 // its A operand (row lane & 15, dims c*32 + 8*(lane >> 4) .. +8), the group's
@@ -194,13 +203,13 @@ __global__ __launch_bounds__(kLWaves * 64) void h2o_logits_heads_kernel(
   }
   __syncthreads();
 
-  const int ntile = 4 * H_kv;
+  const int ntile = kTiles * H_kv;
   uint4 kt[TPW][NC];
 #pragma unroll
   for (int j = 0; j < TPW; ++j) {
     const int t = wave + kLWaves * j;
-    const int h = t < ntile ? t / 4 : 0;
-    const int tt = (t % 4) * 16 + n;           // the row this lane loads
+    const int h = t < ntile ? t / kTiles : 0;
+    const int tt = (t % kTiles) * 16 + n;      // the row this lane loads
     const int tok = t0 + tt;
     const bool ok = t < ntile && tok >= lo && tok < hi;
     const int64_t off = (ok ? (static_cast<int64_t>(sblk[tt]) * H_kv + h) * D : 0) + 8 * kq;
@@ -212,7 +221,7 @@ __global__ __launch_bounds__(kLWaves * 64) void h2o_logits_heads_kernel(
   for (int j = 0; j < TPW; ++j) {
     const int t = wave + kLWaves * j;
     if (t >= ntile) break;
-    const int h = t / 4, tb = (t % 4) * 16;
+    const int h = t / kTiles, tb = (t % kTiles) * 16;
     const bool col = n < G;
     const int qr = (h * G + (col ? n : 0)) * QS + 8 * kq;
     skv_f32x4 sacc = skv_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -425,7 +434,7 @@ int accumulate(const char* fn, const float* q, int B, int H_q, int H_kv, int D,
   const float scale_log2 = scale * skv::kLog2e;
   if constexpr (PH) {
     // tiles of (kv head, 16 tokens) per wave
-    const int tpw = (4 * H_kv + kLWaves - 1) / kLWaves;
+    const int tpw = (kTiles * H_kv + kLWaves - 1) / kLWaves;
 #define SKV_HEADS(DD, TT)                                                                \
   hipLaunchKernelGGL((h2o_logits_heads_kernel<DD, TT>), grid, dim3(kLWaves * 64), sm1,   \
                      stream, q, H_q, H_kv, G, kv_cache, block_table, bt_ld, seq_lens,     \
@@ -443,7 +452,7 @@ int accumulate(const char* fn, const float* q, int B, int H_q, int H_kv, int D,
     const int rpw = 64 / (D / 8);
     const int nld = (4 * H_kv + rpw - 1) / rpw;
     // head-major rows when every wave's rows belong to one kv head
-    const bool hm = 16 % H_kv == 0;
+    const bool hm = (kChunk / 4) % H_kv == 0;
 #define SKV_LOGITS(DD, NN)                                                               \
   do {                                                                                   \
     if (hm)                                                                              \
