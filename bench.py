@@ -101,7 +101,8 @@ def unique_kv_bytes(wl, sel_idx, sel_cnt, seq_lens, H_sel):
 
 
 def kernel_bytes(wl, sel_idx, sel_cnt, seq_lens, num_splits, token_level,
-                 group_select=False, fused=False, entmax=False, gauss=False):
+                 group_select=False, fused=False, entmax=False, gauss=False,
+                 h2o_per_head=False):
     """Algorithmic HBM bytes of each kernel of one step: the bytes the
     operation must move at least (unique selected K/V once, statistics, scores,
     indices, partials)."""
@@ -114,8 +115,11 @@ def kernel_bytes(wl, sel_idx, sel_cnt, seq_lens, num_splits, token_level,
     if token_level:
         S = seq_lens.astype(np.int64)
         out["pagestats_update"] = B * Hkv * D * 2 * 2 * 2 + B * Hkv * 2 + B * 8
+        # the logit scratch holds one row per kv head (group-mean query) or
+        # per query head (per-head reading)
+        rows = Hq if h2o_per_head else Hkv
         out["h2o_accumulate"] = int((S * Hkv * D * 2).sum() + (S * Hkv * 2 * 2).sum()
-                                    + (S * Hkv * 4 * 2).sum() + (S * Hkv * 4).sum()
+                                    + (S * rows * 4 * 2).sum() + (S * Hkv * 4).sum()
                                     + B * Hq * D * 4 + S.sum() * 4 * 2)
     else:
         if wl.steps > 1:   # append + tail refresh
@@ -180,11 +184,12 @@ def decode_source_hash(kind="softmax"):
     return h.hexdigest()
 
 
-def profiled_traffic(tag, kind="softmax"):
+def profiled_traffic(tag, kind="softmax", kernel=None):
     """HBM bytes per decode launch from the committed counter summary of this
     workload and mode (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy's
-    reading), or None when there is none or the decode kernel's sources have
-    changed since the counters were taken."""
+    reading), or None when there is none, when it was taken for another kernel
+    (e.g. the one-launch step's record for the separate decode), or when the
+    decode kernel's sources have changed since the counters were taken."""
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                         f"traffic_{tag}.md")
     if not os.path.exists(path):
@@ -196,6 +201,8 @@ def profiled_traffic(tag, kind="softmax"):
     body = text[start + 7:text.find("```", start + 7)].strip()
     rec = json.loads(body)
     if rec is None or rec.get("source_sha1") != decode_source_hash(kind):
+        return None
+    if kernel is not None and rec.get("kernel") != kernel:
         return None
     return int(rec["traffic"])
 
@@ -500,7 +507,8 @@ def main():
         del g
 
     kb, upages = kernel_bytes(wl, sel_idx, sel_cnt, sl_last, decs[0].decode_splits,
-                              token_level, group, fused, entmax, gauss)
+                              token_level, group, fused, entmax, gauss,
+                              h2o_per_head=decs[0].h2o_per_head)
     if one_launch:
         # the statistics read for scoring (scores and selection stay in LDS)
         # plus the merged decode; q counted once
@@ -529,7 +537,7 @@ def main():
                                                 "_entmax" if entmax else "")
                                              + ("_alibi" if slopes is not None else "")
                                              + ("_heads" if decs[0].h2o_per_head else ""),
-                                             "entmax" if entmax else "softmax")),
+                                             "entmax" if entmax else "softmax", focus)),
                 "bytes_per_launch": kb[focus],
                 "us_per_launch": round(per_kernel_ms[focus] * 1000, 2)}
 
