@@ -33,6 +33,9 @@
  *     h2o_accumulate also needs H_kv <= 16.
  *   - Device-side contents (block ids, lengths, selections) are trusted: they
  *     must lie inside the caller's buffers.
+ *   - A call with no rows (B = 0, or rows = 0 for lse_merge) checks its scalar
+ *     arguments and returns SKV_OK without reading or writing anything, so its
+ *     pointers may be NULL then (an empty batch is a no-op).
  *
  * Return value of every int entry point
  *   SKV_OK (0) on success.  SKV_EINVAL (-22) for a bad scalar argument,

@@ -629,6 +629,8 @@ extern "C" int entmax15_paged_decode(const float* q, int B, int H_q, int H_kv, i
   SKV_REQUIRE(k_cap >= 1 && num_blocks > 0 && bt_ld > 0,
               "entmax15_paged_decode: need k_cap >= 1, num_blocks > 0, bt_ld > 0");
   SKV_REQUIRE(scale > 0.0f, "entmax15_paged_decode: scale must be > 0");
+  // no rows: nothing is read or written, so no pointer is needed
+  if (B == 0) { skv::clear_error(); return SKV_OK; }
   SKV_REQUIRE_PTR(q);
   SKV_REQUIRE_PTR(kv_cache);
   SKV_REQUIRE_PTR(block_table);
@@ -646,7 +648,6 @@ extern "C" int entmax15_paged_decode(const float* q, int B, int H_q, int H_kv, i
   const int64_t waves = rows * num_splits;
   SKV_REQUIRE((waves + kWaves - 1) / kWaves <= 0x7fffffffLL && rows <= 0x7fffffffLL,
               "entmax15_paged_decode: grid too large");
-  if (B == 0) { skv::clear_error(); return SKV_OK; }
   float* logits = scratch;
   float* tau = scratch + rows * k_cap * page_size;
   const dim3 g13(static_cast<unsigned>((waves + kWaves - 1) / kWaves));
@@ -704,6 +705,8 @@ extern "C" int entmax15_paged_decode_merged(
   SKV_REQUIRE(k_cap >= 1 && num_blocks > 0 && bt_ld > 0,
               "entmax15_paged_decode_merged: need k_cap >= 1, num_blocks > 0, bt_ld > 0");
   SKV_REQUIRE(scale > 0.0f, "entmax15_paged_decode_merged: scale must be > 0");
+  // no rows: nothing is read or written, so no pointer is needed
+  if (B == 0) { skv::clear_error(); return SKV_OK; }
   SKV_REQUIRE_PTR(q);
   SKV_REQUIRE_PTR(kv_cache);
   SKV_REQUIRE_PTR(block_table);
@@ -721,7 +724,6 @@ extern "C" int entmax15_paged_decode_merged(
   const int64_t groups = static_cast<int64_t>(B) * H_kv;
   const int64_t blocks = (groups + kXcds - 1) / kXcds * kXcds * G;
   SKV_REQUIRE(blocks <= 0x7fffffffLL, "entmax15_paged_decode_merged: grid too large");
-  if (B == 0) { skv::clear_error(); return SKV_OK; }
   // few rows: 16 waves per row keep more loads in flight
   const bool wide = rows * 8 < 2048;
 #define SKV_EMF(DD, NWW)                                                                \

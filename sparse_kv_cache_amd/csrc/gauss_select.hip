@@ -494,12 +494,13 @@ extern "C" int page_var_update(const uint16_t* kv_cache, int64_t num_blocks, int
   SKV_REQUIRE(skv_supported_page_size(page_size),
               "page_var_update: page_size must be 1, 2, 4, 8 or 16 (got %d)", page_size);
   SKV_REQUIRE(bt_ld <= 0x7fffffff && B <= 65535, "page_var_update: grid too large");
+  // no rows: nothing is read or written, so no pointer is needed
+  if (B == 0) { skv::clear_error(); return SKV_OK; }
   SKV_REQUIRE_PTR(kv_cache);
   SKV_REQUIRE_PTR(k_mean);
   SKV_REQUIRE_PTR(k_var);
   SKV_REQUIRE_PTR(block_table);
   SKV_REQUIRE_PTR(seq_lens);
-  if (B == 0) { skv::clear_error(); return SKV_OK; }
   const int row_vecs = H_kv * D / 8;
   const int threads = row_vecs >= 256 ? 256 : ((row_vecs + 63) / 64) * 64;
   const dim3 grid(tail_only ? 1u : static_cast<unsigned>(bt_ld), static_cast<unsigned>(B));
@@ -525,6 +526,8 @@ extern "C" int gauss_moments(const float* q, int B, int H_q, int H_kv, int D,
   SKV_REQUIRE(bt_ld > 0 && ld >= bt_ld, "gauss_moments: need bt_ld > 0 and ld >= bt_ld");
   SKV_REQUIRE(scale > 0.0f, "gauss_moments: scale must be > 0");
   SKV_REQUIRE(B <= 65535, "gauss_moments: grid too large");
+  // no rows: nothing is read or written, so no pointer is needed
+  if (B == 0) { skv::clear_error(); return SKV_OK; }
   SKV_REQUIRE_PTR(q);
   SKV_REQUIRE_PTR(k_mean);
   SKV_REQUIRE_PTR(k_var);
@@ -537,7 +540,6 @@ extern "C" int gauss_moments(const float* q, int B, int H_q, int H_kv, int D,
   const int tile = kIter * kWaves * (64 / (D / 8));
   const int64_t tiles = (bt_ld + tile - 1) / tile;
   SKV_REQUIRE(tiles <= 65535, "gauss_moments: bt_ld %lld too long", (long long)bt_ld);
-  if (B == 0) { skv::clear_error(); return SKV_OK; }
   const dim3 grid(static_cast<unsigned>(H_kv * slices), static_cast<unsigned>(tiles),
                   static_cast<unsigned>(B));
 #define SKV_MOM(DD, GG)                                                                  \
@@ -573,6 +575,8 @@ extern "C" int gauss_select(const float* mu, const float* var, int64_t ld, int B
   if (nres > bt_ld) nres = bt_ld;
   SKV_REQUIRE(k_cap >= nres, "gauss_select: k_cap %d < reserved pages %lld", k_cap,
               (long long)nres);
+  // no rows: nothing is read or written, so no pointer is needed
+  if (B == 0) { skv::clear_error(); return SKV_OK; }
   SKV_REQUIRE_PTR(mu);
   SKV_REQUIRE_PTR(var);
   SKV_REQUIRE_PTR(seq_lens);
@@ -582,7 +586,6 @@ extern "C" int gauss_select(const float* mu, const float* var, int64_t ld, int B
   SKV_REQUIRE_PTR(sel_cnt);
   const int64_t rows = static_cast<int64_t>(B) * H_q;
   SKV_REQUIRE(rows <= 0x7fffffff, "gauss_select: too many rows");
-  if (rows == 0) { skv::clear_error(); return SKV_OK; }
   const int mix = mixture ? 1 : 0;
 #define SKV_GSEL(BL, IT)                                                               \
   launch_select<BL, IT>(rows, stream, mu, var, ld, H_q, seq_lens, page_size,           \

@@ -411,6 +411,8 @@ int accumulate(const char* fn, const float* q, int B, int H_q, int H_kv, int D,
   SKV_REQUIRE(decay > 0.0f && decay <= 1.0f, "%s: decay must lie in (0, 1]", fn);
   SKV_REQUIRE(scale > 0.0f, "%s: scale must be > 0", fn);
   SKV_REQUIRE(B <= 65535 && nchunks(bt_ld) <= 0x7fffffff, "%s: grid too large", fn);
+  // no rows: nothing is read or written, so no pointer is needed
+  if (B == 0) { skv::clear_error(); return SKV_OK; }
   SKV_REQUIRE_PTR_W(fn, q);
   SKV_REQUIRE_PTR_W(fn, kv_cache);
   SKV_REQUIRE_PTR_W(fn, block_table);
@@ -421,7 +423,6 @@ int accumulate(const char* fn, const float* q, int B, int H_q, int H_kv, int D,
   const int64_t need = scratch_floats(B, rows, bt_ld);
   SKV_REQUIRE(scratch_floats_have >= need, "%s: scratch has %lld floats, needs %lld", fn,
               (long long)scratch_floats_have, (long long)need);
-  if (B == 0) { skv::clear_error(); return SKV_OK; }
   const int G = H_q / H_kv;
   const int nch = static_cast<int>(nchunks(bt_ld));
   const int nupd = static_cast<int>((bt_ld + kUpd - 1) / kUpd);

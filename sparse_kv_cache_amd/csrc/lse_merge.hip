@@ -90,10 +90,11 @@ extern "C" int lse_merge(const float* o_part, const float* lse_part, int rows,
   SKV_REQUIRE(rows >= 0, "lse_merge: rows must be >= 0");
   SKV_REQUIRE(num_splits >= 1, "lse_merge: num_splits must be >= 1 (got %d)", num_splits);
   SKV_REQUIRE(D == 64 || D == 128, "lse_merge: D must be 64 or 128 (got %d)", D);
+  // no rows: nothing is read or written, so no pointer is needed
+  if (rows == 0) { skv::clear_error(); return SKV_OK; }
   SKV_REQUIRE_PTR(o_part);
   SKV_REQUIRE_PTR(lse_part);
   SKV_REQUIRE_PTR(out);
-  if (rows == 0) { skv::clear_error(); return SKV_OK; }
   dim3 grid(static_cast<unsigned>(rows));
   if (D == 128)
     hipLaunchKernelGGL(lse_merge_kernel<128>, grid, dim3(256), 0, stream, o_part,

@@ -196,6 +196,8 @@ int score_pages(const char* who, bool group, const float* q, int B, int H_q,
   SKV_REQUIRE(bt_ld > 0 && score_ld >= bt_ld,
               "%s: need bt_ld > 0 and score_ld >= bt_ld", who);
   SKV_REQUIRE(B <= 65535, "%s: grid too large", who);
+  // no rows: nothing is read or written, so no pointer is needed
+  if (B == 0) { skv::clear_error(); return SKV_OK; }
   SKV_REQUIRE_PTR_W(who, q);
   SKV_REQUIRE_PTR_W(who, k_min);
   SKV_REQUIRE_PTR_W(who, k_max);
@@ -210,7 +212,6 @@ int score_pages(const char* who, bool group, const float* q, int B, int H_q,
   const int tile = kIter * kWaves * ppw;
   const int64_t tiles = (max_pages + tile - 1) / tile;
   SKV_REQUIRE(tiles <= 65535, "%s: bt_ld %lld too long", who, (long long)bt_ld);
-  if (B == 0) { skv::clear_error(); return SKV_OK; }
   dim3 grid(static_cast<unsigned>(H_kv * slices), static_cast<unsigned>(tiles),
             static_cast<unsigned>(B));
 #define SKV_SCORE(DD, GG, AA)                                                    \

@@ -74,6 +74,8 @@ extern "C" int page_topk(const float* scores, int64_t score_ld, int B,
   if (need > score_ld) need = score_ld;
   SKV_REQUIRE(k_cap >= need, "page_topk: k_cap %d < largest possible selection %lld",
               k_cap, (long long)need);
+  // no rows: nothing is read or written, so no pointer is needed
+  if (B == 0) { skv::clear_error(); return SKV_OK; }
   SKV_REQUIRE_PTR(scores);
   SKV_REQUIRE_PTR(seq_lens);
   SKV_REQUIRE_PTR(sel_idx);
@@ -84,7 +86,6 @@ extern "C" int page_topk(const float* scores, int64_t score_ld, int B,
   }
   const int64_t rows = static_cast<int64_t>(B) * H_sel;
   SKV_REQUIRE(rows <= 0x7fffffff, "page_topk: too many rows");
-  if (rows == 0) { skv::clear_error(); return SKV_OK; }
 #define SKV_TOPK(BL, IT)                                                          \
   launch_topk<BL, IT>(rows, stream, scores, score_ld, H_sel, seq_lens, page_size, \
                       topk_pages, frac, reserved_bos, reserved_eos, sel_idx,      \

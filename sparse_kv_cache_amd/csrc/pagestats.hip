@@ -153,11 +153,12 @@ extern "C" int pagestats_update(uint16_t* kv_cache, int64_t num_blocks,
               "pagestats_update: k_min, k_max, k_mean must be all given or all NULL");
   SKV_REQUIRE((k_new == nullptr) == (v_new == nullptr),
               "pagestats_update: k_new and v_new must be both given or both NULL");
+  // no rows: nothing is read or written, so no pointer is needed
+  if (B == 0) { skv::clear_error(); return SKV_OK; }
   SKV_REQUIRE_PTR(kv_cache);
   SKV_REQUIRE_PTR(block_table);
   SKV_REQUIRE_PTR(seq_lens);
   const int row_vecs = H_kv * D / 8;
-  if (B == 0) { skv::clear_error(); return SKV_OK; }
   const int threads = row_vecs >= 256 ? 256 : ((row_vecs + 63) / 64) * 64;
   if (k_new == nullptr) {
     SKV_REQUIRE(all_stats, "pagestats_update: rebuild mode needs the statistics buffers");

@@ -891,6 +891,8 @@ int decode_impl(const char* who, const float* q, int B, int H_q, int H_kv, int D
               "%s: need k_cap >= 1, num_blocks > 0, bt_ld > 0", who);
   SKV_REQUIRE(num_blocks <= 0x7fffffffLL, "%s: pool too large for 32-bit block ids", who);
   SKV_REQUIRE(B <= 65535 && H_kv <= 65535, "%s: grid too large", who);
+  // no rows: nothing is read or written, so no pointer is needed
+  if (B == 0) { skv::clear_error(); return SKV_OK; }
   SKV_REQUIRE_PTR_W(who, q);
   SKV_REQUIRE_PTR_W(who, kv_cache);
   SKV_REQUIRE_PTR_W(who, block_table);
@@ -913,7 +915,6 @@ int decode_impl(const char* who, const float* q, int B, int H_q, int H_kv, int D
       ? G : (static_cast<int64_t>(num_splits) * G + kWaveBlock - 1) / kWaveBlock;
   SKV_REQUIRE(shared_sel || per_group * (n_groups + kXcds) < 0x7fffffffLL,
               "%s: grid too large", who);
-  if (B == 0) { skv::clear_error(); return SKV_OK; }
   dim3 grid(static_cast<unsigned>(num_splits), static_cast<unsigned>(H_kv),
             static_cast<unsigned>(B));
   const Args a{q, H_q, H_kv, G, kv_cache, num_blocks, page_size, block_table, bt_ld,
@@ -1031,6 +1032,8 @@ extern "C" int sparse_select_decode(const float* scores, int64_t score_ld, int t
               "%s: k_cap %d must cover the largest selection %lld (and be <= 4096)", who,
               k_cap, (long long)need);
   SKV_REQUIRE(B <= 65535, "%s: grid too large", who);
+  // no rows: nothing is read or written, so no pointer is needed
+  if (B == 0) { skv::clear_error(); return SKV_OK; }
   SKV_REQUIRE_PTR_W(who, scores);
   SKV_REQUIRE_PTR_W(who, q);
   SKV_REQUIRE_PTR_W(who, kv_cache);
@@ -1041,7 +1044,6 @@ extern "C" int sparse_select_decode(const float* scores, int64_t score_ld, int t
               "%s: sel_idx and sel_cnt must both be given or both be NULL", who);
   SKV_REQUIRE(sel_blk == nullptr || sel_idx != nullptr,
               "%s: sel_blk needs sel_idx", who);
-  if (B == 0) { skv::clear_error(); return SKV_OK; }
   const int64_t n_groups = static_cast<int64_t>(B) * H_kv;
   const Args a{q, H_q, H_kv, G, kv_cache, num_blocks, page_size, block_table, bt_ld,
                seq_lens, nullptr, nullptr, nullptr, k_cap, scale * skv::kLog2e, num_splits,
@@ -1114,6 +1116,8 @@ extern "C" int sparse_page_decode(const float* q, int B, int H_q, int H_kv, int 
               "%s: k_cap %d must cover the largest selection %lld, and the block's "
               "scores and selection must fit 48 KiB of LDS", who, k_cap, (long long)need);
   SKV_REQUIRE(B <= 65535, "%s: grid too large", who);
+  // no rows: nothing is read or written, so no pointer is needed
+  if (B == 0) { skv::clear_error(); return SKV_OK; }
   SKV_REQUIRE_PTR_W(who, q);
   SKV_REQUIRE_PTR_W(who, kv_cache);
   SKV_REQUIRE_PTR_W(who, k_min);
@@ -1125,7 +1129,6 @@ extern "C" int sparse_page_decode(const float* q, int B, int H_q, int H_kv, int 
   SKV_REQUIRE((sel_idx == nullptr) == (sel_cnt == nullptr),
               "%s: sel_idx and sel_cnt must both be given or both be NULL", who);
   SKV_REQUIRE(sel_blk == nullptr || sel_idx != nullptr, "%s: sel_blk needs sel_idx", who);
-  if (B == 0) { skv::clear_error(); return SKV_OK; }
   const int64_t n_groups = static_cast<int64_t>(B) * H_kv;
   const Args a{q, H_q, H_kv, G, kv_cache, num_blocks, page_size, block_table, bt_ld,
                seq_lens, nullptr, nullptr, nullptr, k_cap, scale * skv::kLog2e, num_splits,

@@ -787,3 +787,47 @@ def test_gauss_append_refreshes_tail_variance():
     gv = d.k_var.cpu().numpy()[used].astype(np.float64)
     assert np.all(np.abs(gv - ov) <= 1e-5 * ov + 1e-6), \
         f"variance after appends off by {np.abs(gv - ov).max()}"
+
+
+@pytest.mark.parametrize("mode", ["one_launch", "separate", "group", "entmax", "gauss",
+                                  "token_group_mean", "token_per_head"])
+def test_empty_batch_is_a_no_op(mode):
+    """B = 0 through every entry point of a step: each call returns OK without
+    touching memory (empty tensors carry NULL data pointers), and the cache
+    is left as it was."""
+    say(f"[gpu] empty batch, {mode}")
+    token = mode.startswith("token")
+    P, H_q, H_kv, D, NB, ld = (1 if token else 16), 8, 2, 128, 64, 32
+    kw = dict(topk_pages=4, num_splits=2, token_level=token)
+    if mode == "separate":
+        kw["fuse_merge"] = False
+    if mode == "group":
+        kw["group_select"] = True
+    if mode == "entmax":
+        kw["attention"] = "entmax15"
+    if mode == "gauss":
+        kw["selection"] = "gauss"
+    if token:
+        kw["h2o_softmax"] = "per_head" if mode == "token_per_head" else "group_mean"
+    d = SparseDecoder(0, H_q, H_kv, D, NB, P, ld, **kw)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    cache = torch.randn((2, NB, P, H_kv, D), generator=g, device="cuda").to(torch.bfloat16)
+    before = cache.clone()
+    q = torch.empty((0, H_q, D), device="cuda")
+    bt = torch.empty((0, ld), dtype=torch.int32, device="cuda")
+    sl = torch.empty((0,), dtype=torch.int32, device="cuda")
+    kn = torch.empty((0, H_kv, D), dtype=torch.bfloat16, device="cuda")
+    if not token:
+        d.rebuild_stats(cache, bt, sl)
+    if token:
+        d.append(cache, bt, sl, kn, kn.clone())
+        d.accumulate(q, cache, bt, sl)
+        d.select(sl, bt)
+        d.attend(q, cache, bt, sl)
+        d.merge()
+        out = d.out
+    else:
+        out, _ = d.step(q, cache, bt, sl, kn, kn.clone())
+    torch.cuda.synchronize()
+    assert out.shape[0] == 0
+    assert torch.equal(cache, before)
