@@ -643,7 +643,10 @@ def test_append_refresh_and_reset(P):
 
 @pytest.mark.parametrize("reading,H_q,H_kv,D", [
     ("group_mean", 8, 2, 128), ("per_head", 8, 2, 128), ("per_head", 80, 16, 128),
-    ("per_head", 12, 4, 64), ("group_mean", 12, 4, 64)])
+    ("per_head", 12, 4, 64), ("group_mean", 12, 4, 64),
+    # G = 16 (every column of the matrix-core tile), one kv head, and three kv
+    # heads (rows dealt token-major in the group-mean pass)
+    ("per_head", 16, 1, 64), ("per_head", 48, 3, 128), ("group_mean", 48, 3, 128)])
 def test_token_level_step_teacher_forced(reading, H_q, H_kv, D):
     say(f"[gpu] h2o small, teacher forced, {reading} H_q {H_q} H_kv {H_kv} D {D}")
     S0, B = 300, 3
