@@ -212,45 +212,42 @@ def profiled_traffic(tag, kind="softmax", kernel=None):
 def cpu_baseline(wl, cache_bits, q, seq_lens, seconds, token_level, hh_bits=None,
                  gauss=False, slopes=None, k_cap=0, h2o_per_head=False):
     """The float64 oracle on a bounded sample of requests (whole step for
-    those requests), scaled to steps/s of the full batch."""
+    those requests), scaled to steps/s of the full batch: (i) one thread, then
+    (ii) the same request-steps on a pool of threads (the oracle's C calls
+    release the GIL), one request-step per thread at a time.  Returns both."""
     import oracle
     oracle.build() if not os.path.exists(os.path.join(
         os.path.dirname(os.path.abspath(oracle.__file__)), "liboracle.so")) else None
     qd = q.double().numpy()
-    reps, rows_done, t_used = 0, 0, 0.0
-    b = 0
-    if token_level:
-        while t_used < seconds and reps < 10_000:
-            bb = b % wl.B
-            bt = wl.block_table[bb:bb + 1]
-            sl = seq_lens[bb:bb + 1]
+    st_cache = {}
+    sl64 = None if slopes is None else np.asarray(slopes, np.float32).astype(np.float64)
+
+    def prepare(bb):
+        """Per-request inputs built outside the timed region."""
+        if token_level or bb in st_cache:
+            return
+        bt, sl = wl.block_table[bb:bb + 1], seq_lens[bb:bb + 1]
+        if gauss:
+            st_cache[bb] = (oracle.page_stats(cache_bits, bt, sl, wl.P)[2],
+                            oracle.page_var(cache_bits, bt, sl, wl.P))
+        else:
+            st_cache[bb] = oracle.page_stats(cache_bits, bt, sl, wl.P)
+
+    def request_step(bb):
+        """One request's whole step through the oracle."""
+        bt, sl = wl.block_table[bb:bb + 1], seq_lens[bb:bb + 1]
+        S = int(sl[0])
+        if token_level:
             hh = hh_bits.copy()
-            t0 = time.perf_counter()
             sc = oracle.h2o_step(qd[bb:bb + 1], cache_bits, bt, sl, hh, wl.bos,
                                  wl.eos, wl.softmax_scale, wl.decay,
                                  per_head=h2o_per_head)
             for h in range(wl.H_kv):
-                sel = oracle.select(sc[0, h, :int(sl[0])], wl.topk_pages, 0.0,
-                                    wl.bos, wl.eos)
+                sel = oracle.select(sc[0, h, :S], wl.topk_pages, 0.0, wl.bos, wl.eos)
                 for g in range(wl.G):
-                    oracle.attend(qd[bb, h * wl.G + g], cache_bits, h, bt[0],
-                                  int(sl[0]), sel, wl.softmax_scale)
-            t_used += time.perf_counter() - t0
-            reps += 1
-            rows_done += 1
-            b += 1
-        sample = f"{rows_done} request-steps of the token-level step (1 of {wl.B} requests each)"
-    elif gauss:
-        st_cache = {}
-        sl64 = None if slopes is None else np.asarray(slopes, np.float32).astype(np.float64)
-        while t_used < seconds and reps < 10_000:
-            bb = b % wl.B
-            bt, sl = wl.block_table[bb:bb + 1], seq_lens[bb:bb + 1]
-            if bb not in st_cache:
-                st_cache[bb] = (oracle.page_stats(cache_bits, bt, sl, wl.P)[2],
-                                oracle.page_var(cache_bits, bt, sl, wl.P))
-            t0 = time.perf_counter()
-            S = int(sl[0])
+                    oracle.attend(qd[bb, h * wl.G + g], cache_bits, h, bt[0], S, sel,
+                                  wl.softmax_scale)
+        elif gauss:
             N = (S + wl.P - 1) // wl.P
             n = np.array([min(wl.P, S - p * wl.P) for p in range(N)], dtype=np.int32)
             mu, var = oracle.gauss_moments(qd[bb:bb + 1], *st_cache[bb], bt, sl, wl.P,
@@ -262,37 +259,59 @@ def cpu_baseline(wl, cache_bits, q, seq_lens, seconds, token_level, hh_bits=None
                 oracle.attend_entmax15(qd[bb, i], cache_bits, i // wl.G, bt[0], S, sel,
                                        wl.softmax_scale,
                                        slope=None if sl64 is None else sl64[i])
-            t_used += time.perf_counter() - t0
-            reps += 1
-            rows_done += 1
-            b += 1
-        sample = (f"{rows_done} request-steps of moments+tau-hat+select+entmax attend "
-                  f"(1 of {wl.B} requests each, statistics prebuilt)")
-    else:
-        st_cache = {}
-        while t_used < seconds and reps < 10_000:
-            bb = b % wl.B
-            if bb not in st_cache:
-                st_cache[bb] = oracle.page_stats(cache_bits, wl.block_table[bb:bb + 1],
-                                                 seq_lens[bb:bb + 1], wl.P)
-            t0 = time.perf_counter()
-            k_cap = min(max(wl.topk_pages, int(math.floor(wl.topk_frac * wl.bt_ld)),
-                            wl.bos + wl.eos), wl.bt_ld)
-            oracle.decode_step(qd[bb:bb + 1], cache_bits, wl.block_table[bb:bb + 1],
-                               seq_lens[bb:bb + 1], st_cache[bb], wl.w_avg, wl.w_peak,
-                               wl.topk_pages, wl.topk_frac, wl.bos, wl.eos,
-                               wl.softmax_scale, k_cap)
-            t_used += time.perf_counter() - t0
-            reps += 1
-            rows_done += 1
-            b += 1
-        sample = (f"{rows_done} request-steps of score+select+attend "
-                  f"(1 of {wl.B} requests each, statistics prebuilt)")
-    per_request = t_used / rows_done
-    steps_per_s = 1.0 / (per_request * wl.B)
-    return {"value": steps_per_s, "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "host_cpu": host_cpu(),
-            "sample": sample, "seconds": round(t_used, 2)}
+        else:
+            kc = min(max(wl.topk_pages, int(math.floor(wl.topk_frac * wl.bt_ld)),
+                         wl.bos + wl.eos), wl.bt_ld)
+            oracle.decode_step(qd[bb:bb + 1], cache_bits, bt, sl, st_cache[bb], wl.w_avg,
+                               wl.w_peak, wl.topk_pages, wl.topk_frac, wl.bos, wl.eos,
+                               wl.softmax_scale, kc)
+
+    # (i) one thread
+    rows_done, t_used, b = 0, 0.0, 0
+    while t_used < seconds and rows_done < 10_000:
+        bb = b % wl.B
+        prepare(bb)
+        t0 = time.perf_counter()
+        request_step(bb)
+        t_used += time.perf_counter() - t0
+        rows_done += 1
+        b += 1
+    covered = min(rows_done, wl.B)
+    what = ("the token-level step" if token_level else
+            "moments+tau-hat+select+entmax attend (statistics prebuilt)" if gauss else
+            "score+select+attend (statistics prebuilt)")
+    single = {"value": 1.0 / (t_used / rows_done * wl.B), "unit": "steps/s", "cores": 1,
+              "kind": "oracle", "host_cpu": host_cpu(),
+              "sample": f"{rows_done} request-steps of {what}, {covered} of {wl.B} requests",
+              "seconds": round(t_used, 2)}
+
+    # (ii) a pool of threads over the same requests, for about as long
+    import concurrent.futures as cf
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    threads = max(1, min(16, avail))
+    deadline = time.perf_counter() + max(1.0, seconds / 2)
+
+    def worker(w):
+        done, k = 0, w
+        while time.perf_counter() < deadline:
+            request_step(k % covered)
+            done += 1
+            k += threads
+        return done
+
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        total = sum(ex.map(worker, range(threads)))
+    wall = time.perf_counter() - t0
+    parallel = {"value": total / wall / wl.B, "unit": "steps/s", "cores": threads,
+                "kind": "oracle", "host_cpu": host_cpu(),
+                "sample": (f"{total} request-steps of {what} on {threads} threads over the "
+                           f"same {covered} requests"),
+                "seconds": round(wall, 2)}
+    return single, parallel
 
 
 def host_cpu():
@@ -585,7 +604,7 @@ def main():
         from sparse_kv_cache_amd.workloads import bf16_bits
         cb = bf16_bits(caches[last % R])
         hb = bf16_bits(hh0) if token_level else None
-        result["cpu_baseline"] = cpu_baseline(
+        result["cpu_baseline"], result["cpu_baseline_parallel"] = cpu_baseline(
             wl, cb, q.cpu(), sl_last, args.cpu_seconds, token_level, hb,
             gauss=gauss, slopes=None if slopes is None else slopes.cpu().numpy(),
             k_cap=decs[0].k_cap, h2o_per_head=decs[0].h2o_per_head)
