@@ -557,6 +557,8 @@ def main():
                                              + ("_alibi" if slopes is not None else "")
                                              + ("_heads" if decs[0].h2o_per_head else ""),
                                              "entmax" if entmax else "softmax", focus)),
+                # the same rate against a plain device copy measured in this run
+                "copy_frac": round(a / copy_gbps, 4) if copy_gbps > 0 else None,
                 "bytes_per_launch": kb[focus],
                 "us_per_launch": round(per_kernel_ms[focus] * 1000, 2)}
 
