@@ -14,7 +14,12 @@
 
 namespace {
 
-template <int BLOCK, int ITEMS>
+// EAGER: the block reads its whole stored row (score_ld entries) before the
+// request's length arrives, so the key loads overlap that round trip; for a
+// launch of few rows that latency is the cost that matters.  Otherwise only
+// the N valid entries are read (ragged rows of a large batch would read up
+// to twice the bytes).
+template <int BLOCK, int ITEMS, bool EAGER>
 __global__ __launch_bounds__(BLOCK) void page_topk_kernel(
     const float* __restrict__ scores, int64_t score_ld, int H_sel,
     const int32_t* __restrict__ seq_lens, int P, int topk_pages,
@@ -23,17 +28,33 @@ __global__ __launch_bounds__(BLOCK) void page_topk_kernel(
     int64_t bt_ld, int32_t* __restrict__ sel_blk) {
   const int64_t row = blockIdx.x;
   const int b = static_cast<int>(row / H_sel);
+  const float* srow = scores + row * score_ld;
+  const bool aligned = ((score_ld & 3) == 0) &&
+                       ((reinterpret_cast<uintptr_t>(scores) & 15) == 0);
+  uint32_t key[ITEMS];
+  if constexpr (EAGER) skv::load_row_keys<ITEMS>(srow, aligned, score_ld, key);
   int64_t N64 = (static_cast<int64_t>(seq_lens[b]) + P - 1) / P;
   if (N64 > score_ld) N64 = score_ld;
   if (N64 < 0) N64 = 0;
-  const bool aligned = ((score_ld & 3) == 0) &&
-                       ((reinterpret_cast<uintptr_t>(scores) & 15) == 0);
-  const int total = skv::topk_row<BLOCK, ITEMS>(
-      scores + row * score_ld, aligned, static_cast<int>(N64), topk_pages, topk_frac,
-      bos, eos, sel_blk != nullptr ? bt + static_cast<int64_t>(b) * bt_ld : nullptr, bt_ld,
-      sel_idx + row * k_cap, sel_blk != nullptr ? sel_blk + row * k_cap : nullptr, k_cap);
+  const int N = static_cast<int>(N64);
+  const int32_t* btr = sel_blk != nullptr ? bt + static_cast<int64_t>(b) * bt_ld : nullptr;
+  int32_t* bout = sel_blk != nullptr ? sel_blk + row * k_cap : nullptr;
+  // 8-bit digits; the outputs go to global memory only, so no closing barrier
+  int total;
+  if constexpr (EAGER) {
+    total = skv::topk_row_keys<BLOCK, ITEMS, 8, false>(key, N, topk_pages, topk_frac, bos,
+                                                       eos, btr, bt_ld, sel_idx + row * k_cap,
+                                                       bout, k_cap);
+  } else {
+    total = skv::topk_row<BLOCK, ITEMS, 8, false>(srow, aligned, N, topk_pages, topk_frac,
+                                                  bos, eos, btr, bt_ld, sel_idx + row * k_cap,
+                                                  bout, k_cap);
+  }
   if (threadIdx.x == 0) sel_cnt[row] = total;
 }
+
+// launches of up to this many rows read their rows eagerly
+constexpr int64_t kEagerRows = 1024;
 
 template <int BLOCK, int ITEMS>
 void launch_topk(int64_t rows, hipStream_t stream, const float* scores,
@@ -41,10 +62,16 @@ void launch_topk(int64_t rows, hipStream_t stream, const float* scores,
                  int topk_pages, double topk_frac, int bos, int eos,
                  int32_t* sel_idx, int32_t* sel_cnt, int k_cap, const int32_t* bt,
                  int64_t bt_ld, int32_t* sel_blk) {
-  hipLaunchKernelGGL((page_topk_kernel<BLOCK, ITEMS>), dim3(static_cast<unsigned>(rows)),
-                     dim3(BLOCK), 0, stream, scores, score_ld, H_sel, seq_lens, P,
-                     topk_pages, topk_frac, bos, eos, sel_idx, sel_cnt, k_cap, bt,
-                     bt_ld, sel_blk);
+  if (rows <= kEagerRows)
+    hipLaunchKernelGGL((page_topk_kernel<BLOCK, ITEMS, true>), dim3(static_cast<unsigned>(rows)),
+                       dim3(BLOCK), 0, stream, scores, score_ld, H_sel, seq_lens, P,
+                       topk_pages, topk_frac, bos, eos, sel_idx, sel_cnt, k_cap, bt,
+                       bt_ld, sel_blk);
+  else
+    hipLaunchKernelGGL((page_topk_kernel<BLOCK, ITEMS, false>), dim3(static_cast<unsigned>(rows)),
+                       dim3(BLOCK), 0, stream, scores, score_ld, H_sel, seq_lens, P,
+                       topk_pages, topk_frac, bos, eos, sel_idx, sel_cnt, k_cap, bt,
+                       bt_ld, sel_blk);
 }
 
 }  // namespace

@@ -130,6 +130,34 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* total,
   return r;
 }
 
+// Two exclusive prefix sums over the block at the cost of one (the same three
+// barriers).  smem needs 2 * (nwaves + 1) ints.  Every thread must call it.
+__device__ __forceinline__ void block_exclusive_scan2(int x, int y, int* ex, int* ey,
+                                                      int* tx, int* ty, int* smem) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int nwaves = (blockDim.x + kWave - 1) / kWave;
+  int* sy = smem + nwaves + 1;
+  const int ix = wave_inclusive_scan(x);
+  const int iy = wave_inclusive_scan(y);
+  if (lane == kWave - 1) { smem[wave] = ix; sy[wave] = iy; }
+  __syncthreads();
+  if (wave == 0) {
+    const int wx = lane < nwaves ? smem[lane] : 0;
+    const int wy = lane < nwaves ? sy[lane] : 0;
+    const int jx = wave_inclusive_scan(wx);
+    const int jy = wave_inclusive_scan(wy);
+    if (lane < nwaves) { smem[lane] = jx - wx; sy[lane] = jy - wy; }
+    if (lane == nwaves - 1) { smem[nwaves] = jx; sy[nwaves] = jy; }
+  }
+  __syncthreads();
+  *ex = ix - x + smem[wave];
+  *ey = iy - y + sy[wave];
+  *tx = smem[nwaves];
+  *ty = sy[nwaves];
+  __syncthreads();
+}
+
 // log2(e) and ln(2) for base-2 exponentials.
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

@@ -12,13 +12,14 @@
 // +0.0) held in registers, ITEMS contiguous entries per thread.  A
 // most-significant-digit radix select finds the key prefix of the m-th best
 // candidate: the bits every candidate shares are skipped (block OR / AND),
-// each pass histograms the next 8 bits of the keys still matching the prefix
-// into its own LDS histogram (atomics; every wave then finds the digit
+// each pass histograms the next BITS bits of the keys still matching the
+// prefix into its own LDS histogram (atomics; every wave then finds the digit
 // itself, so a pass costs one barrier), and the select stops as soon as the
 // chosen bin is taken whole.  Keys above the prefix are taken; when equal keys
-// must be split, the lowest indices are taken, ranked by a block-wide prefix
-// count in index order.  A prefix count over the final flags writes the
-// indices in ascending order with no sort.
+// must be split, the lowest indices are taken.  One block-wide prefix count of
+// two values per thread (entries taken outright, entries equal to the prefix)
+// gives every entry its place, so the indices are written in ascending order
+// with no sort.
 #pragma once
 
 #include <limits.h>
@@ -37,16 +38,17 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // with the whole block: writes the ascending selection to out[0, k_cap)
 // (padded with -1) and, when bout is given, the selected pages' physical
 // blocks btr[p] to bout; returns the selected count (every thread).  out and
-// bout may point to global or LDS memory.  Ends with a block barrier.
+// bout may point to global or LDS memory.  Ends with a block barrier unless
+// SYNC_END is false (outputs that no thread of the block reads back).
 // The selection from keys already in registers: key[i] is the order key of
 // entry tid * ITEMS + i (entries outside the ranked window are ignored).
-template <int BLOCK, int ITEMS>
+template <int BLOCK, int ITEMS, int BITS = 8, bool SYNC_END = true>
 __device__ int topk_row_keys(const uint32_t (&key)[ITEMS], int N, int topk_pages,
                              double topk_frac, int bos, int eos,
                              const int32_t* __restrict__ btr, int64_t bt_ld,
                              int32_t* out, int32_t* bout, int k_cap);
 
-template <int BLOCK, int ITEMS>
+template <int BLOCK, int ITEMS, int BITS = 8, bool SYNC_END = true>
 __device__ int topk_row(const float* __restrict__ srow, bool aligned16, int N,
                         int topk_pages, double topk_frac, int bos, int eos,
                         const int32_t* __restrict__ btr, int64_t bt_ld,
@@ -74,22 +76,49 @@ __device__ int topk_row(const float* __restrict__ srow, bool aligned16, int N,
       key[i] = (p >= lo && p < hi) ? order_key(srow[p]) : 0u;
     }
   }
-  return topk_row_keys<BLOCK, ITEMS>(key, N, topk_pages, topk_frac, bos, eos, btr, bt_ld,
-                                     out, bout, k_cap);
+  return topk_row_keys<BLOCK, ITEMS, BITS, SYNC_END>(key, N, topk_pages, topk_frac, bos,
+                                                     eos, btr, bt_ld, out, bout, k_cap);
 }
 
-template <int BLOCK, int ITEMS>
+// Keys of the first row_len stored entries of srow, whatever the row's valid
+// length (the selection masks by N), so the loads need not wait for N.
+template <int ITEMS>
+__device__ __forceinline__ void load_row_keys(const float* __restrict__ srow,
+                                              bool aligned16, int64_t row_len,
+                                              uint32_t (&key)[ITEMS]) {
+  const int base = threadIdx.x * ITEMS;
+  constexpr bool kVec = ITEMS % 4 == 0;
+  if (kVec && aligned16 && base + ITEMS <= row_len) {
+    if constexpr (kVec) {
+#pragma unroll
+      for (int i = 0; i < ITEMS; i += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(srow + base + i);
+        key[i] = order_key(v.x); key[i + 1] = order_key(v.y);
+        key[i + 2] = order_key(v.z); key[i + 3] = order_key(v.w);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      const int p = base + i;
+      key[i] = p < row_len ? order_key(srow[p]) : 0u;
+    }
+  }
+}
+
+template <int BLOCK, int ITEMS, int BITS, bool SYNC_END>
 __device__ int topk_row_keys(const uint32_t (&key)[ITEMS], int N, int topk_pages,
                              double topk_frac, int bos, int eos,
                              const int32_t* __restrict__ btr, int64_t bt_ld,
                              int32_t* out, int32_t* bout, int k_cap) {
   constexpr int NW = BLOCK / 64;
-  constexpr int kBits = 8;                       // digit width
+  constexpr int kBits = BITS;                    // digit width
   constexpr int kBins = 1 << kBits;
-  constexpr int kPasses = 4;                     // 32 / 8
+  constexpr int kPasses = (32 + kBits - 1) / kBits;
   constexpr int kPerLane = kBins / 64;           // bins a lane scans
+  static_assert(kPerLane % 4 == 0, "a lane scans its bins 16 bytes at a time");
   __shared__ __align__(16) int hist[kPasses][kBins];   // one histogram per pass
-  __shared__ int scan_smem[NW + 1];
+  __shared__ int scan_smem[2 * (NW + 1)];
   __shared__ uint32_t s_or[NW], s_and[NW];
 
   const int tid = threadIdx.x;
@@ -133,7 +162,6 @@ __device__ int topk_row_keys(const uint32_t (&key)[ITEMS], int N, int topk_pages
   // among those equal to prefix under pmask, the r_eq lowest indices.
   uint32_t prefix, pmask;
   int r_eq;
-  bool ties = false;                   // r_eq < number equal to the prefix
   if (want == 0) {
     prefix = 0xffffffffu; pmask = 0xffffffffu; r_eq = 0;   // reserved only
   } else if (want >= ncand) {
@@ -217,43 +245,39 @@ __device__ int topk_row_keys(const uint32_t (&key)[ITEMS], int N, int topk_pages
       ++pass;
     }
     r_eq = remaining;
-    ties = remaining < bin;            // fully resolved with equal keys left
   }
 
-  // ranks among the entries equal to the prefix (only needed for ties)
-  int er = 0;
-  if (ties) {
-    int eq = 0;
-#pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-      const int p = base + i;
-      eq += (p >= lo && p < hi && (key[i] & pmask) == prefix) ? 1 : 0;
-    }
-    int total_eq;
-    er = skv::block_exclusive_scan(eq, &total_eq, scan_smem);
-  }
-
-  uint32_t flags = 0u;
-  int cnt = 0;
+  // Entries taken outright (reserved, or above the prefix) and entries equal
+  // to the prefix, counted per thread and prefix-summed together: the
+  // r_eq lowest-index equal entries are taken, so an entry's place is the
+  // outright count before it plus min(equal count before it, r_eq).
+  int n_out = 0, n_eq = 0;
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
     const int p = base + i;
+    if (p >= N) continue;
     const uint32_t km = key[i] & pmask;
-    bool take;
-    if (p >= N) take = false;
-    else if (p < lo || p >= hi) take = true;
-    else if (km > prefix) take = true;
-    else if (km == prefix) { take = er < r_eq; ++er; }
-    else take = false;
-    if (take) { flags |= 1u << i; ++cnt; }
+    if (p < lo || p >= hi || km > prefix) ++n_out;
+    else if (km == prefix) ++n_eq;
   }
-  int total;
-  int pos = skv::block_exclusive_scan(cnt, &total, scan_smem);
+  int out_before, eq_before, out_total, eq_total;
+  skv::block_exclusive_scan2(n_out, n_eq, &out_before, &eq_before, &out_total, &eq_total,
+                             scan_smem);
+  const int total = out_total + (eq_total < r_eq ? eq_total : r_eq);
+  int er = eq_before;
+  int pos = out_before + (eq_before < r_eq ? eq_before : r_eq);
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
-    if (flags & (1u << i)) {
+    const int p = base + i;
+    if (p >= N) continue;
+    const uint32_t km = key[i] & pmask;
+    bool take;
+    if (p < lo || p >= hi || km > prefix) take = true;
+    else if (km == prefix) { take = er < r_eq; ++er; }
+    else take = false;
+    if (take) {
       if (pos >= 0 && pos < k_cap) {
-        out[pos] = base + i;
+        out[pos] = p;
         if (bout != nullptr) bout[pos] = bid[i];
       }
       ++pos;
@@ -263,7 +287,7 @@ __device__ int topk_row_keys(const uint32_t (&key)[ITEMS], int N, int topk_pages
     out[j] = -1;
     if (bout != nullptr) bout[j] = -1;
   }
-  __syncthreads();
+  if constexpr (SYNC_END) __syncthreads();
   return total < k_cap ? total : k_cap;
 }
 
