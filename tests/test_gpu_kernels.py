@@ -583,18 +583,22 @@ def test_topk_rows_against_oracle_all_sizes():
                                   np.repeat(sl, H), topk, frac, bos, eos)
 
 
-def test_lse_merge_edge_cases_and_random():
-    say("[gpu] lse_merge")
-    rng = np.random.default_rng(1)
+@pytest.mark.parametrize("ns", [1, 9, 16, 17, 32, 33, 64, 300])
+def test_lse_merge_edge_cases_and_random(ns):
+    """Up to 8 splits per thread (16 at D = 128, 32 at D = 64) take the
+    register-resident kernel, in both of its widths; more take the LDS-staged
+    passes."""
+    say(f"[gpu] lse_merge, {ns} splits")
+    rng = np.random.default_rng(1 + ns)
     for D in (64, 128):
-        rows, ns = 37, 9
+        rows = 37
         o = rng.standard_normal((rows, ns, D)).astype(np.float32)
         l = (rng.standard_normal((rows, ns)) * 3).astype(np.float32)
         l[0, :] = -np.inf                     # every split empty
-        l[1, :4] = -np.inf
-        l[2, 2] = np.inf                      # +inf is read as -inf
+        l[1, :min(4, ns - 1)] = -np.inf
+        l[2, min(2, ns - 1)] = np.inf         # +inf is read as -inf
         l[3, :] = -np.inf
-        l[3, 5] = np.inf
+        l[3, min(5, ns - 1)] = np.inf
         l[4, 0] = 80.0                        # large spread
         out = torch.full((rows, D), float("nan"), device="cuda")
         lse = torch.full((rows,), float("nan"), device="cuda")
