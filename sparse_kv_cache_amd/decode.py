@@ -47,6 +47,31 @@ def selection_capacity(score_ld, topk_pages, topk_frac=0.0, bos=0, eos=1):
     return min(need, int(score_ld))
 
 
+def validate_tables(block_table, seq_lens, num_blocks, page_size):
+    """Debug check of the device-side contents the kernels trust: every
+    request's length fits its block-table row (ceil(S / P) <= bt_ld) and every
+    block id it uses lies in [0, num_blocks).  Copies both tensors to the host
+    (a synchronising read); raises ValueError naming the first bad request.
+    Not part of the step: call it, or pass validate=True to SparseDecoder,
+    while debugging a caller."""
+    bt = block_table.detach().cpu()
+    sl = seq_lens.detach().cpu()
+    if bt.dim() != 2 or sl.dim() != 1 or bt.shape[0] != sl.shape[0]:
+        raise ValueError("block_table must be [B, bt_ld] and seq_lens [B]")
+    ld = bt.shape[1]
+    for b in range(sl.shape[0]):
+        S = int(sl[b])
+        if S < 0:
+            raise ValueError(f"request {b}: seq_len {S} < 0")
+        n = (S + page_size - 1) // page_size
+        if n > ld:
+            raise ValueError(f"request {b}: {S} tokens need {n} pages, the row holds {ld}")
+        ids = bt[b, :n]
+        if n and (int(ids.min()) < 0 or int(ids.max()) >= num_blocks):
+            bad = int(ids[(ids < 0) | (ids >= num_blocks)][0])
+            raise ValueError(f"request {b}: block id {bad} outside [0, {num_blocks})")
+
+
 class SparseDecoder:
     """Buffers and call order of one decode step.
 
@@ -56,6 +81,8 @@ class SparseDecoder:
     (h2o_softmax="group_mean") or through every head's own softmax, averaged
     over the group (h2o_softmax="per_head");
     group_select=True scores and selects once per kv head (page level);
+    validate=True checks the block table and lengths on the host before each
+    step (validate_tables; a debugging aid that synchronises);
     alibi_slopes (fp32 [H_q] on the device) adds ALiBi to scoring and decode.
     With one selection per query head and num_splits <= 8 the split merge runs
     inside the decode launch (fused); keep_partials also writes the partials.
@@ -71,7 +98,7 @@ class SparseDecoder:
                  scale=None, num_splits=1, decay=0.984375, token_level=False,
                  group_select=False, alibi_slopes=None, fuse_merge=True,
                  attention=None, selection="topk", gauss_cap=None, gauss_mixture=None,
-                 h2o_softmax="group_mean", device="cuda"):
+                 h2o_softmax="group_mean", validate=False, device="cuda"):
         self.B, self.H_q, self.H_kv, self.D = B, H_q, H_kv, D
         self.num_blocks, self.P, self.bt_ld = num_blocks, page_size, bt_ld
         self.topk_pages, self.topk_frac = topk_pages, topk_frac
@@ -80,6 +107,7 @@ class SparseDecoder:
         self.scale = D ** -0.5 if scale is None else scale
         self.num_splits, self.decay = num_splits, decay
         self.token_level = token_level
+        self.validate = bool(validate)
         self.group_select = bool(group_select) and not token_level
         dev = torch.device(device)
         if alibi_slopes is not None and token_level:
@@ -303,6 +331,8 @@ class SparseDecoder:
     def step(self, q, kv_cache, block_table, seq_lens, k_new=None, v_new=None,
              stream=None):
         """One decode step; returns (out, lse) views of the decoder's buffers."""
+        if self.validate:
+            validate_tables(block_table, seq_lens, self.num_blocks, self.P)
         if k_new is not None:
             self.append(kv_cache, block_table, seq_lens, k_new, v_new, stream)
         if self.gauss:

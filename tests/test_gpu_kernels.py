@@ -185,6 +185,28 @@ def test_page_level_step(case):
     say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}")
 
 
+def test_page_level_step_with_empty_and_one_token_requests():
+    """A batch holding an empty request (S = 0: no page, nothing selected,
+    output 0 with lse -inf), a one-token request and a full one, through
+    every launch form of the page-level step."""
+    say("[gpu] page-level step with S = 0 and S = 1 requests")
+    wl = W.small_case(seed=90, B=4, H_q=8, H_kv=2, D=128, P=16, max_pages=12,
+                      topk_pages=5, num_splits=4)
+    wl.seq_lens = np.array([0, 1, 17, 12 * 16], dtype=np.int32)
+    wl.block_table[3] = np.arange(12, dtype=np.int32) + 30
+    worst, ex = run_page_case(wl, W.make_cache(wl), W.make_queries(wl))
+    say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}")
+
+
+def test_page_level_step_with_128_query_heads():
+    """128 query heads over 8 kv heads (G = 16) at D = 64."""
+    say("[gpu] page-level step, 128 query heads")
+    wl = W.small_case(seed=91, B=2, H_q=128, H_kv=8, D=64, P=16, max_pages=10,
+                      topk_pages=4, num_splits=2)
+    worst, ex = run_page_case(wl, W.make_cache(wl), W.make_queries(wl))
+    say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}")
+
+
 # seed, B, H_q, H_kv, D, P, max_pages, topk, frac, bos, eos, splits, w_avg, w_peak
 GROUP_CASES = [
     (40, 2, 8, 2, 128, 16, 20, 5, 0.0, 0, 1, 3, 1.0, 1.0),
