@@ -790,6 +790,49 @@ def test_graph_replays_match_eager(mode):
         assert torch.equal(got[1], d.lse), f"replay {step}: lse differs from eager"
 
 
+@pytest.mark.parametrize("reading", ["group_mean", "per_head"])
+def test_token_level_graph_replays_match_eager(reading):
+    """The token-level step (accumulate, select, attend, merge) captured in a
+    graph: from the same hh, every replay must give the eager step's output,
+    lse and updated hh, bit for bit."""
+    say(f"[gpu] token-level graph replay vs eager, {reading}")
+    S0, B = 300, 3
+    wl = W.h2o_token(seed=41, steps=4, prompt=S0, B=B)
+    wl.H_q, wl.H_kv, wl.D = 8, 2, 128
+    wl.topk_pages, wl.num_splits = 40, 4
+    wl.seq_lens = np.array([S0, S0 - 37, 11], dtype=np.int32)
+    d = SparseDecoder(B, wl.H_q, wl.H_kv, wl.D, wl.num_blocks, 1, wl.bt_ld,
+                      topk_pages=wl.topk_pages, bos=wl.bos, eos=wl.eos,
+                      scale=wl.softmax_scale, num_splits=wl.num_splits,
+                      token_level=True, h2o_softmax=reading)
+    d.hh.copy_(W.make_hh(wl).cuda())
+    cache = dev(W.make_cache(wl))
+    bt, sl = dev(wl.block_table), dev(wl.seq_lens)
+    q = dev(W.make_queries(wl, 0))
+    torch.cuda.synchronize()
+    hh0 = d.hh.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        d.step(q, cache, bt, sl)
+    torch.cuda.synchronize()
+    for step in range(3):
+        q.copy_(dev(W.make_queries(wl, step + 1)))
+        d.hh.copy_(hh0)
+        scratch = torch.randn(1 << 20, device="cuda").sum()     # eager work between
+        g.replay()
+        torch.cuda.synchronize()
+        got = (d.out.clone(), d.lse.clone(), d.hh.clone())
+        d.hh.copy_(hh0)
+        d.out.fill_(float("nan"))
+        d.step(q, cache, bt, sl)
+        torch.cuda.synchronize()
+        assert torch.isfinite(scratch)
+        assert torch.equal(got[0], d.out), f"replay {step}: out differs from eager"
+        assert torch.equal(got[1], d.lse), f"replay {step}: lse differs from eager"
+        assert torch.equal(got[2], d.hh), f"replay {step}: hh differs from eager"
+        hh0 = d.hh.clone()
+
+
 def test_gauss_append_refreshes_tail_variance():
     """Gaussian-aware decoder over appends: pagestats_update's tail refresh
     and page_var_update(tail_only) keep every page's mean and variance equal
