@@ -198,6 +198,30 @@ def test_page_level_step_with_empty_and_one_token_requests():
     say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}")
 
 
+# Rows past 512 and past 2048 pages take the 4- and 8-entry-per-thread top-k
+# of the in-block selection (select + decode, and the one launch); 4096 pages
+# is the longest row the one launch takes.
+# seed, B, H_q, H_kv, D, max_pages, min_pages, topk, splits
+LONG_ROW_CASES = [
+    (70, 2, 8, 2, 128, 1500, 600, 300, 8),
+    (71, 1, 4, 1, 64, 4096, 2500, 2000, 8),
+]
+
+
+@pytest.mark.parametrize("case", LONG_ROW_CASES, ids=[f"rows{c[5]}" for c in LONG_ROW_CASES])
+def test_page_level_step_long_rows(case):
+    (seed, B, H_q, H_kv, D, maxp, minp, topk, ns) = case
+    say(f"[gpu] page-level long rows {case}")
+    wl = W.small_case(seed=seed, B=B, H_q=H_q, H_kv=H_kv, D=D, P=16, max_pages=maxp,
+                      topk_pages=topk, num_splits=ns, min_len=minp * 16)
+    d = _decoder(wl)
+    assert d.select_in_decode and d.score_in_decode
+    assert int(wl.pages().max()) > (2048 if maxp > 2048 else 512)
+    del d
+    worst, ex = run_page_case(wl, W.make_cache(wl), W.make_queries(wl))
+    say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}")
+
+
 def test_page_level_step_with_128_query_heads():
     """128 query heads over 8 kv heads (G = 16) at D = 64."""
     say("[gpu] page-level step, 128 query heads")
