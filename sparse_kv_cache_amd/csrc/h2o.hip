@@ -454,27 +454,24 @@ int accumulate(const char* fn, const float* q, int B, int H_q, int H_kv, int D,
     const int nld = (4 * H_kv + rpw - 1) / rpw;
     // head-major rows when every wave's rows belong to one kv head
     const bool hm = (kChunk / 4) % H_kv == 0;
+#define SKV_LOGITS_HM(DD, NN, HM)                                                        \
+  hipLaunchKernelGGL((h2o_logits_kernel<DD, NN, HM>), grid, dim3(kLWaves * 64), sm1,      \
+                     stream, q, H_q, H_kv, G, kv_cache, block_table, bt_ld, seq_lens,     \
+                     reserved_bos, reserved_eos, scale_log2, logits, part, nch)
 #define SKV_LOGITS(DD, NN)                                                               \
   do {                                                                                   \
-    if (hm)                                                                              \
-      hipLaunchKernelGGL((h2o_logits_kernel<DD, NN, true>), grid, dim3(kLWaves * 64),     \
-                         sm1, stream, q, H_q, H_kv, G, kv_cache, block_table, bt_ld,      \
-                         seq_lens, reserved_bos, reserved_eos, scale_log2, logits, part,  \
-                         nch);                                                           \
-    else                                                                                 \
-      hipLaunchKernelGGL((h2o_logits_kernel<DD, NN, false>), grid, dim3(kLWaves * 64),    \
-                         sm1, stream, q, H_q, H_kv, G, kv_cache, block_table, bt_ld,      \
-                         seq_lens, reserved_bos, reserved_eos, scale_log2, logits, part,  \
-                         nch);                                                           \
+    if (hm) SKV_LOGITS_HM(DD, NN, true); else SKV_LOGITS_HM(DD, NN, false);              \
   } while (0)
     if (D == 128) {
-      if (nld <= 2) SKV_LOGITS(128, 2); else if (nld <= 4) SKV_LOGITS(128, 4);
+      // (one or two kv heads: 2 loads, and H_kv divides 16, so head-major)
+      if (nld <= 2) SKV_LOGITS_HM(128, 2, true); else if (nld <= 4) SKV_LOGITS(128, 4);
       else if (nld <= 8) SKV_LOGITS(128, 8); else SKV_LOGITS(128, 16);
     } else {
       if (nld <= 2) SKV_LOGITS(64, 2); else if (nld <= 4) SKV_LOGITS(64, 4);
       else SKV_LOGITS(64, 8);
     }
 #undef SKV_LOGITS
+#undef SKV_LOGITS_HM
   }
   const size_t sm2 = sizeof(float) * 2 * static_cast<size_t>(rows);
   hipLaunchKernelGGL(h2o_update_kernel<PH>,

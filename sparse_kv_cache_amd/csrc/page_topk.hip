@@ -53,25 +53,21 @@ __global__ __launch_bounds__(BLOCK) void page_topk_kernel(
   if (threadIdx.x == 0) sel_cnt[row] = total;
 }
 
-// launches of up to this many rows read their rows eagerly
+// Launches of up to this many rows take the wide-block mapping and read their
+// rows eagerly; larger launches take 256-thread blocks and read only the
+// valid entries.
 constexpr int64_t kEagerRows = 1024;
 
-template <int BLOCK, int ITEMS>
+template <int BLOCK, int ITEMS, bool EAGER>
 void launch_topk(int64_t rows, hipStream_t stream, const float* scores,
                  int64_t score_ld, int H_sel, const int32_t* seq_lens, int P,
                  int topk_pages, double topk_frac, int bos, int eos,
                  int32_t* sel_idx, int32_t* sel_cnt, int k_cap, const int32_t* bt,
                  int64_t bt_ld, int32_t* sel_blk) {
-  if (rows <= kEagerRows)
-    hipLaunchKernelGGL((page_topk_kernel<BLOCK, ITEMS, true>), dim3(static_cast<unsigned>(rows)),
-                       dim3(BLOCK), 0, stream, scores, score_ld, H_sel, seq_lens, P,
-                       topk_pages, topk_frac, bos, eos, sel_idx, sel_cnt, k_cap, bt,
-                       bt_ld, sel_blk);
-  else
-    hipLaunchKernelGGL((page_topk_kernel<BLOCK, ITEMS, false>), dim3(static_cast<unsigned>(rows)),
-                       dim3(BLOCK), 0, stream, scores, score_ld, H_sel, seq_lens, P,
-                       topk_pages, topk_frac, bos, eos, sel_idx, sel_cnt, k_cap, bt,
-                       bt_ld, sel_blk);
+  hipLaunchKernelGGL((page_topk_kernel<BLOCK, ITEMS, EAGER>), dim3(static_cast<unsigned>(rows)),
+                     dim3(BLOCK), 0, stream, scores, score_ld, H_sel, seq_lens, P,
+                     topk_pages, topk_frac, bos, eos, sel_idx, sel_cnt, k_cap, bt,
+                     bt_ld, sel_blk);
 }
 
 }  // namespace
@@ -113,27 +109,27 @@ extern "C" int page_topk(const float* scores, int64_t score_ld, int B,
   }
   const int64_t rows = static_cast<int64_t>(B) * H_sel;
   SKV_REQUIRE(rows <= 0x7fffffff, "page_topk: too many rows");
-#define SKV_TOPK(BL, IT)                                                          \
-  launch_topk<BL, IT>(rows, stream, scores, score_ld, H_sel, seq_lens, page_size, \
-                      topk_pages, frac, reserved_bos, reserved_eos, sel_idx,      \
-                      sel_cnt, k_cap, block_table, bt_ld, sel_blk)
-  if (rows < 1024) {
+#define SKV_TOPK(BL, IT, EA)                                                          \
+  launch_topk<BL, IT, EA>(rows, stream, scores, score_ld, H_sel, seq_lens, page_size, \
+                          topk_pages, frac, reserved_bos, reserved_eos, sel_idx,      \
+                          sel_cnt, k_cap, block_table, bt_ld, sel_blk)
+  if (rows <= kEagerRows) {
     // few rows, each latency-bound: the widest block that still gives each
     // thread at least 4 entries, so every pass is short
-    if (score_ld <= 1024) SKV_TOPK(256, 4);
-    else if (score_ld <= 2048) SKV_TOPK(512, 4);
-    else if (score_ld <= 4096) SKV_TOPK(1024, 4);
-    else if (score_ld <= 8192) SKV_TOPK(1024, 8);
-    else if (score_ld <= 16384) SKV_TOPK(1024, 16);
-    else SKV_TOPK(1024, 32);
+    if (score_ld <= 1024) SKV_TOPK(256, 4, true);
+    else if (score_ld <= 2048) SKV_TOPK(512, 4, true);
+    else if (score_ld <= 4096) SKV_TOPK(1024, 4, true);
+    else if (score_ld <= 8192) SKV_TOPK(1024, 8, true);
+    else if (score_ld <= 16384) SKV_TOPK(1024, 16, true);
+    else SKV_TOPK(1024, 32, true);
   } else {
     // rows enough to fill the chip: 256-thread blocks, several per CU
-    if (score_ld <= 1024) SKV_TOPK(256, 4);
-    else if (score_ld <= 2048) SKV_TOPK(256, 8);
-    else if (score_ld <= 4096) SKV_TOPK(256, 16);
-    else if (score_ld <= 8192) SKV_TOPK(512, 16);
-    else if (score_ld <= 16384) SKV_TOPK(1024, 16);
-    else SKV_TOPK(1024, 32);
+    if (score_ld <= 1024) SKV_TOPK(256, 4, false);
+    else if (score_ld <= 2048) SKV_TOPK(256, 8, false);
+    else if (score_ld <= 4096) SKV_TOPK(256, 16, false);
+    else if (score_ld <= 8192) SKV_TOPK(512, 16, false);
+    else if (score_ld <= 16384) SKV_TOPK(1024, 16, false);
+    else SKV_TOPK(1024, 32, false);
   }
 #undef SKV_TOPK
   SKV_CHECK_LAUNCH();

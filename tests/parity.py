@@ -324,6 +324,29 @@ def page_rows(S, P, N):
     return np.array([min(P, S - p * P) for p in range(N)], dtype=np.int32)
 
 
+def check_gauss_select_row(g_mu, g_var, g_est, g_tau, g_sel, n, mixture, bos, eos, k_cap,
+                           row):
+    """The selection step of one row given the moments it was fed (g_mu,
+    g_var fp32): tau-hat against the oracle's solve on those moments, the
+    estimates mu + sigma sqrt(2 ln n), and the selection exact on the GPU's
+    own fp32 estimates and tau-hat."""
+    N = n.shape[0]
+    t_o = oracle.gauss_tau(g_mu.astype(np.float64), g_var.astype(np.float64), n, mixture)
+    assert abs(float(g_tau) - t_o) <= 1e-6 * max(1.0, abs(t_o)), \
+        f"row {row}: tau-hat {g_tau} vs oracle {t_o} on the same moments"
+    c = np.where(n > 1, np.sqrt(2.0 * np.log(np.maximum(n, 1))), 0.0)
+    e_o = g_mu.astype(np.float64) + np.sqrt(np.maximum(g_var.astype(np.float64), 0)) * c
+    tol_e = 1e-6 * (np.abs(g_mu) + np.sqrt(np.maximum(g_var, 0)) * c) + 1e-7
+    assert np.all(np.abs(g_est - e_o) <= tol_e), f"row {row}: estimate error"
+    lo, hi = min(bos, N), max(N - eos, 0)
+    hi = max(hi, lo)
+    half = np.float32(0.5) * g_est.astype(np.float32)
+    qual = int(np.count_nonzero(half[lo:hi] > np.float32(g_tau)))
+    budget = max(1, min(k_cap, qual + N - (hi - lo)))
+    want = oracle.select(g_est.astype(np.float64), budget, 0.0, bos, eos).tolist()[:k_cap]
+    assert list(g_sel) == want, f"row {row}: selection differs on the GPU's own values"
+
+
 def check_gauss_row(g_mu, g_var, g_est, g_tau, g_sel, n, mixture, bos, eos, k_cap,
                     mu_o, var_o, k1, q2, bias, row):
     """One (request, query head) row of the Gaussian-aware path.
@@ -343,23 +366,9 @@ def check_gauss_row(g_mu, g_var, g_est, g_tau, g_sel, n, mixture, bos, eos, k_ca
     e_var = np.abs(g_var - var_o)
     tol_var = 1e-5 * var_o + 1e-8 * (1.0 + q2)
     assert np.all(e_var <= tol_var), f"row {row}: var err {e_var.max()}"
-    # tau-hat: the oracle's solve on the GPU's own moments (fp32 result)
-    t_o = oracle.gauss_tau(g_mu.astype(np.float64), g_var.astype(np.float64), n, mixture)
-    assert abs(float(g_tau) - t_o) <= 1e-6 * max(1.0, abs(t_o)), \
-        f"row {row}: tau-hat {g_tau} vs oracle {t_o} on the same moments"
-    # estimates from the GPU's moments
+    check_gauss_select_row(g_mu, g_var, g_est, g_tau, g_sel, n, mixture, bos, eos, k_cap,
+                           row)
     c = np.where(n > 1, np.sqrt(2.0 * np.log(np.maximum(n, 1))), 0.0)
-    e_o = g_mu.astype(np.float64) + np.sqrt(np.maximum(g_var.astype(np.float64), 0)) * c
-    tol_e = 1e-6 * (np.abs(g_mu) + np.sqrt(np.maximum(g_var, 0)) * c) + 1e-7
-    assert np.all(np.abs(g_est - e_o) <= tol_e), f"row {row}: estimate error"
-    # the selection is exact on the GPU's fp32 estimates and tau-hat
-    lo, hi = min(bos, N), max(N - eos, 0)
-    hi = max(hi, lo)
-    half = np.float32(0.5) * g_est.astype(np.float32)
-    qual = int(np.count_nonzero(half[lo:hi] > np.float32(g_tau)))
-    budget = max(1, min(k_cap, qual + N - (hi - lo)))
-    want = oracle.select(g_est.astype(np.float64), budget, 0.0, bos, eos).tolist()[:k_cap]
-    assert list(g_sel) == want, f"row {row}: selection differs on the GPU's own values"
     # end to end: the oracle's tau-hat and selection from its own moments
     t_full = oracle.gauss_tau(mu_o, var_o, n, mixture)
     assert abs(float(g_tau) - t_full) <= 1e-4 * max(1.0, abs(t_full)), \

@@ -198,27 +198,52 @@ def test_page_level_step_with_empty_and_one_token_requests():
     say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}")
 
 
-# Rows past 512 and past 2048 pages take the 4- and 8-entry-per-thread top-k
-# of the in-block selection (select + decode, and the one launch); 4096 pages
-# is the longest row the one launch takes.
-# seed, B, H_q, H_kv, D, max_pages, min_pages, topk, splits
+# The in-block selection (select + decode, and the one launch) holds 1, 4 or 8
+# entries per thread for rows of up to 512, 2048 and 4096 pages (the longest
+# row the one launch takes); its decode has a page-size-16 form and a generic
+# one, with and without ALiBi, at D = 64 and 128.  One case per combination.
+# seed, B, H_q, H_kv, D, P, max_pages, min_pages, topk, splits, alibi
 LONG_ROW_CASES = [
-    (70, 2, 8, 2, 128, 1500, 600, 300, 8),
-    (71, 1, 4, 1, 64, 4096, 2500, 2000, 8),
+    (70, 2, 8, 2, 128, 16, 1500, 600, 300, 8, False),
+    (71, 1, 4, 1, 64, 16, 4096, 2500, 2000, 8, False),
+    (72, 2, 8, 2, 128, 16, 4096, 2300, 700, 6, False),
+    (73, 2, 4, 2, 64, 16, 1200, 600, 200, 4, False),
+    (74, 2, 8, 2, 128, 8, 300, 100, 40, 8, False),
+    (75, 2, 8, 2, 128, 4, 1800, 700, 250, 8, False),
+    (76, 1, 8, 2, 128, 2, 4096, 2200, 900, 5, False),
+    (77, 2, 4, 1, 64, 4, 1500, 600, 300, 8, False),
+    (78, 1, 4, 2, 64, 8, 4000, 2100, 1000, 3, False),
+    (79, 2, 6, 3, 64, 8, 400, 100, 30, 7, False),
+    (84, 2, 8, 2, 128, 16, 1500, 600, 300, 8, True),
+    (85, 1, 8, 2, 128, 16, 4096, 2300, 700, 6, True),
+    (86, 2, 4, 2, 64, 16, 300, 100, 40, 4, True),
+    (87, 2, 4, 2, 64, 16, 1200, 600, 200, 8, True),
+    (88, 1, 4, 1, 64, 16, 4096, 2500, 2000, 8, True),
+    (89, 2, 8, 2, 128, 8, 300, 100, 40, 8, True),
+    (90, 2, 8, 2, 128, 4, 1800, 700, 250, 8, True),
+    (91, 1, 8, 2, 128, 2, 4096, 2200, 900, 5, True),
+    (92, 2, 6, 3, 64, 8, 400, 100, 30, 7, True),
+    (93, 2, 4, 1, 64, 4, 1500, 600, 300, 8, True),
+    (94, 1, 4, 2, 64, 8, 4000, 2100, 1000, 3, True),
 ]
 
 
-@pytest.mark.parametrize("case", LONG_ROW_CASES, ids=[f"rows{c[5]}" for c in LONG_ROW_CASES])
+@pytest.mark.parametrize("case", LONG_ROW_CASES, ids=[f"rows{c[0]}" for c in LONG_ROW_CASES])
 def test_page_level_step_long_rows(case):
-    (seed, B, H_q, H_kv, D, maxp, minp, topk, ns) = case
-    say(f"[gpu] page-level long rows {case}")
-    wl = W.small_case(seed=seed, B=B, H_q=H_q, H_kv=H_kv, D=D, P=16, max_pages=maxp,
-                      topk_pages=topk, num_splits=ns, min_len=minp * 16)
+    (seed, B, H_q, H_kv, D, P, maxp, minp, topk, ns, al) = case
+    say(f"[gpu] page-level rows {case}")
+    wl = W.small_case(seed=seed, B=B, H_q=H_q, H_kv=H_kv, D=D, P=P, max_pages=maxp,
+                      topk_pages=topk, num_splits=ns, min_len=minp * P)
     d = _decoder(wl)
-    assert d.select_in_decode and d.score_in_decode
-    assert int(wl.pages().max()) > (2048 if maxp > 2048 else 512)
+    assert d.fused and d.select_in_decode and d.score_in_decode
     del d
-    worst, ex = run_page_case(wl, W.make_cache(wl), W.make_queries(wl))
+    cache, q = W.make_cache(wl), W.make_queries(wl)
+    if al:
+        from sparse_kv_cache_amd.decode import alibi_slopes
+        slopes = alibi_slopes(H_q, device="cpu").numpy()
+        worst, ex = run_alibi_case(wl, cache, q, False, slopes)
+    else:
+        worst, ex = run_page_case(wl, cache, q)
     say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}")
 
 
@@ -358,6 +383,21 @@ def run_alibi_case(wl, cache_cpu, q_cpu, group, slopes_np):
                                    wl.topk_pages, wl.topk_frac, wl.bos, wl.eos)
     per = per_head_rows(rows, wl.B, wl.H_q, H_sel)
     sl64 = slopes.cpu().numpy().astype(np.float64)
+    if d.select_in_decode:
+        # selection inside the decode launch: page_topk's selection and the
+        # same output as the separate launches
+        ref_idx, ref_cnt, ref_blk = d.sel_idx.clone(), d.sel_cnt.clone(), d.sel_blk.clone()
+        o_ref, l_ref = d.out.clone(), d.lse.clone()
+        d.keep_selection = True
+        d.sel_idx.fill_(-7); d.sel_cnt.fill_(-7); d.sel_blk.fill_(-7)
+        d.out.fill_(float("nan")); d.lse.fill_(float("nan"))
+        d.select_attend(q, cache, bt, sl)
+        torch.cuda.synchronize()
+        assert torch.equal(d.sel_idx, ref_idx) and torch.equal(d.sel_cnt, ref_cnt)
+        assert torch.equal(d.sel_blk, ref_blk)
+        assert torch.allclose(o_ref, d.out, rtol=0, atol=1e-5), "select+decode differs"
+        assert torch.allclose(l_ref, d.lse, rtol=0, atol=1e-5), "select+decode lse differs"
+        d.keep_selection = False
     if d.score_in_decode:
         d.fused = False            # the reference buffers from separate launches
         d.attend(q, cache, bt, sl)
@@ -392,6 +432,9 @@ ENTMAX_CASES = [
     (96, 2, 4, 4, 64, 4, 40, 7, 4, False, 1.0),
     (97, 1, 16, 2, 128, 16, 50, 9, 5, True, None),
     (98, 2, 6, 3, 64, 1, 120, 20, 2, True, 0.5),
+    # 256 query rows: the merged launch's 8-wave blocks and the three-launch
+    # tau pass's 256-thread blocks with the row in registers
+    (99, 16, 16, 4, 64, 16, 12, 5, 3, False, None),
 ]
 
 
@@ -474,6 +517,8 @@ GAUSS_CASES = [
     (140, 2, 4, 4, 64, 1, 120, 0, 0, 2, False, None, None, None),
     # D 64 with ALiBi, a binding cap, no reserved page, a sharper scale
     (141, 2, 8, 2, 64, 16, 50, 0, 0, 3, True, None, 4, 2.0),
+    # D 64 with a group of 8 (the moments pass's widest head slice)
+    (142, 2, 16, 2, 64, 16, 40, 0, 1, 4, False, None, None, None),
 ]
 
 
@@ -629,6 +674,67 @@ def test_topk_rows_against_oracle_all_sizes():
                                   np.repeat(sl, H), topk, frac, bos, eos)
 
 
+def test_topk_many_rows_all_sizes():
+    """Launches of more than 1024 rows (256-thread blocks and wider, reading
+    only a row's valid entries) at every row-length class, and a launch of
+    exactly 1024 rows (the last that reads whole rows eagerly)."""
+    rng = np.random.default_rng(1)
+    for B, H, ld in ((33, 32, 1000), (33, 32, 2000), (33, 32, 4000), (33, 32, 8000),
+                     (33, 32, 16000), (33, 32, 32768), (32, 32, 3000)):
+        say(f"[gpu] page_topk {B * H} rows, score_ld={ld}")
+        sl = rng.integers(1, ld, size=B, endpoint=True).astype(np.int32)
+        sc = rng.standard_normal((B, H, ld)).astype(np.float32)
+        sc[::2, :, ::5] = np.round(sc[::2, :, ::5])          # ties in half the requests
+        sc[1::4] = rng.integers(-3, 4, size=sc[1::4].shape)   # and whole rows of them
+        topk, frac, bos, eos = max(1, ld // 10), 0.0, 1, 2
+        k_cap = min(max(topk, bos + eos), ld)
+        scores = dev(sc)
+        idx = torch.full((B, H, k_cap), -7, dtype=torch.int32, device="cuda")
+        cnt = torch.full((B, H), -7, dtype=torch.int32, device="cuda")
+        skv.page_topk(scores, dev(sl), 1, topk, idx, cnt, frac, bos, eos)
+        torch.cuda.synchronize()
+        check_selection_exact(idx.cpu().numpy().reshape(-1, k_cap),
+                              cnt.cpu().numpy().reshape(-1), sc.reshape(-1, ld),
+                              np.repeat(sl, H), topk, frac, bos, eos)
+
+
+def test_gauss_select_rows_all_sizes():
+    """gauss_select on synthetic moment rows at every launch shape: under 1024
+    rows at the row lengths of the 1024-thread blocks (4, 16 and 32 pages a
+    thread), 1024 and more rows at the lengths of the 256- and 512-thread
+    blocks; single Gaussian and mixture, with and without a binding cap."""
+    from parity import check_gauss_select_row
+    rng = np.random.default_rng(3)
+    P = 16
+    for B, H, ld, mixture, cap in ((2, 3, 3000, False, None), (2, 3, 12000, True, None),
+                                   (1, 2, 20000, False, 64), (33, 32, 1500, True, None),
+                                   (33, 32, 3000, False, 40), (33, 32, 6000, True, None)):
+        say(f"[gpu] gauss_select {B * H} rows, ld={ld}, mixture={mixture}, cap={cap}")
+        sl = rng.integers(1, ld * P, size=B, endpoint=True).astype(np.int32)
+        mu = rng.normal(0.0, 0.5, size=(B, H, ld)).astype(np.float32)
+        mu += (rng.random((B, H, ld)) < 0.01) * np.float32(3.0)      # a few strong pages
+        var = rng.gamma(2.0, 0.05, size=(B, H, ld)).astype(np.float32)
+        var[..., ::13] = 0.0
+        k_cap = ld if cap is None else cap
+        bt = np.tile(np.arange(ld, dtype=np.int32), (B, 1))
+        est = torch.full((B, H, ld), float("nan"), device="cuda")
+        tau = torch.full((B, H), float("nan"), device="cuda")
+        idx = torch.full((B, H, k_cap), -7, dtype=torch.int32, device="cuda")
+        cnt = torch.full((B, H), -7, dtype=torch.int32, device="cuda")
+        skv.gauss_select(dev(mu), dev(var), dev(sl), P, dev(bt), mixture, k_cap, est, idx,
+                         cnt, tau=tau, reserved_bos=0, reserved_eos=1)
+        torch.cuda.synchronize()
+        g_est, g_tau = est.cpu().numpy(), tau.cpu().numpy()
+        g_idx, g_cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+        for b in range(B):
+            N = (int(sl[b]) + P - 1) // P
+            n = np.minimum(P, int(sl[b]) - np.arange(N) * P).astype(np.int32)
+            for h in range(H):
+                check_gauss_select_row(mu[b, h, :N], var[b, h, :N], g_est[b, h, :N],
+                                       g_tau[b, h], g_idx[b, h, :g_cnt[b, h]], n, mixture,
+                                       0, 1, k_cap, (b, h))
+
+
 @pytest.mark.parametrize("ns", [1, 9, 16, 17, 32, 33, 64, 300])
 def test_lse_merge_edge_cases_and_random(ns):
     """Up to 8 splits per thread (16 at D = 128, 32 at D = 64) take the
@@ -696,7 +802,15 @@ def test_append_refresh_and_reset(P):
     ("per_head", 12, 4, 64), ("group_mean", 12, 4, 64),
     # G = 16 (every column of the matrix-core tile), one kv head, and three kv
     # heads (rows dealt token-major in the group-mean pass)
-    ("per_head", 16, 1, 64), ("per_head", 48, 3, 128), ("group_mean", 48, 3, 128)])
+    ("per_head", 16, 1, 64), ("per_head", 48, 3, 128), ("group_mean", 48, 3, 128),
+    # every key-row load depth of the group-mean pass (rows of 4 * H_kv tokens
+    # per wave, head-major where H_kv divides 16, else token-major) and every
+    # tile count per wave of the per-head pass, at both head sizes
+    ("group_mean", 8, 4, 128), ("group_mean", 12, 6, 128), ("group_mean", 24, 12, 128),
+    ("group_mean", 32, 16, 128), ("group_mean", 6, 3, 64), ("group_mean", 16, 8, 64),
+    ("group_mean", 12, 6, 64), ("group_mean", 20, 10, 64), ("group_mean", 32, 16, 64),
+    ("per_head", 40, 10, 128), ("per_head", 16, 8, 64), ("per_head", 24, 12, 64),
+    ("per_head", 32, 16, 64)])
 def test_token_level_step_teacher_forced(reading, H_q, H_kv, D):
     say(f"[gpu] h2o small, teacher forced, {reading} H_q {H_q} H_kv {H_kv} D {D}")
     S0, B = 300, 3
