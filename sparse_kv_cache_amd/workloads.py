@@ -136,7 +136,7 @@ def high_batch(seed: int = 5, steps: int = 32, B: int = 128,
     return Workload("high_batch", B=B, H_q=32, H_kv=8, D=128, P=16,
                     num_blocks=num_blocks, seq_lens=seq, block_table=bt,
                     topk_pages=4, topk_frac=0.1, w_avg=1.0, w_peak=1.0,
-                    num_splits=16, steps=steps, seed=seed)
+                    num_splits=8, steps=steps, seed=seed)
 
 
 WORKLOADS = {

@@ -155,6 +155,7 @@ def test_high_batch_sampled_after_appends():
     cache = W.make_cache(wl, device="cuda")
     d = SparseDecoder.for_workload(wl)
     d.keep_partials = True
+    d.keep_selection = True     # the step selects inside the decode launch
     bt = dev(wl.block_table)
     sl0 = dev(wl.seq_lens)
     d.rebuild_stats(cache, bt, sl0)
