@@ -228,7 +228,7 @@ int score_pages(const char* who, bool group, const float* q, int B, int H_q,
     else if (GS == 4) SKV_SCORE(64, 4, false); else SKV_SCORE(64, 8, false);
   }
 #undef SKV_SCORE
-  SKV_CHECK_LAUNCH();
+  SKV_CHECK_LAUNCH_W(who);
 }
 
 }  // namespace

@@ -35,7 +35,6 @@ void clear_error();
     }                                                        \
   } while (0)
 
-// Report a failed launch.
 // The same check for a helper shared by several entry points: `who` names
 // the entry point the caller used.
 #define SKV_REQUIRE_PTR_W(who, p)                             \
@@ -46,11 +45,15 @@ void clear_error();
     }                                                        \
   } while (0)
 
-#define SKV_CHECK_LAUNCH()                                              \
+// Report a failed launch (or success) and return from the entry point.
+#define SKV_CHECK_LAUNCH() SKV_CHECK_LAUNCH_W(__func__)
+
+// The same for a helper shared by several entry points.
+#define SKV_CHECK_LAUNCH_W(who)                                         \
   do {                                                                  \
     hipError_t e_ = hipGetLastError();                                  \
     if (e_ != hipSuccess) {                                             \
-      skv::set_error("%s: launch failed: %s", __func__,                 \
+      skv::set_error("%s: launch failed: %s", (who),                    \
                      hipGetErrorString(e_));                            \
       return SKV_EIO;                                                   \
     }                                                                   \
@@ -67,12 +70,6 @@ static inline float skv_host_round_bf16(float f) {
   float r;
   memcpy(&r, &u, sizeof r);
   return r;
-}
-
-// A tuning switch read from the environment (set and not "0").
-static inline bool skv_env_flag(const char* name) {
-  const char* v = getenv(name);
-  return v != nullptr && v[0] != '\0' && !(v[0] == '0' && v[1] == '\0');
 }
 
 static inline bool skv_supported_page_size(int p) {

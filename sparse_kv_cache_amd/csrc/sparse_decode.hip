@@ -951,7 +951,7 @@ int decode_impl(const char* who, const float* q, int B, int H_q, int H_kv, int D
     }
 #undef SKV_WAVE
   }
-  SKV_CHECK_LAUNCH();
+  SKV_CHECK_LAUNCH_W(who);
 }
 
 }  // namespace
