@@ -2,7 +2,7 @@
  * ragged and degenerate inputs, with every buffer sized exactly, so that a
  * build with -fsanitize=address,undefined reports any out-of-bounds access,
  * use after free, leak or undefined operation.  Values are not checked here
- * (the pytest pins do that); the exit status is the sanitizers' verdict.
+ * (the pytest pins do that); the exit status carries the sanitizers' findings.
  * Test infrastructure: built and run by tests/test_oracle_sanitized.py. */
 #include <math.h>
 #include <stdint.h>
