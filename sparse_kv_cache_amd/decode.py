@@ -15,6 +15,13 @@ library's entry points in the order of a decode step:
                -> gauss_moments -> gauss_select -> entmax15_paged_decode
                -> lse_merge
 
+With one selection per query head and at most 8 splits the decoder fuses
+launches: the merge runs inside the decode (sparse_paged_decode_merged), the
+selection too when rows fit (sparse_select_decode, after page_score), and up
+to ONE_LAUNCH_ROWS query rows the whole page-level step is one launch
+(sparse_page_decode).  Past that row count scoring stays a launch of its own,
+since it reads each kv head's statistics once for the whole query group.
+
 This mirrors the decode call of the EntmaxKV README ("Quick start": score,
 select, attend and append in one call) cut at kernel granularity.  Nothing
 here computes: it allocates once and marshals arguments.
