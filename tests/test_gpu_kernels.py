@@ -885,8 +885,8 @@ def test_invalid_arguments_raise_before_launch():
         skv.page_score(q.double(), None, None, None, None, None, 16, 1, 1, None)
 
 
-@pytest.mark.parametrize("mode", ["one_launch", "separate", "group", "gauss", "entmax",
-                                  "gauss_merged", "entmax_merged"])
+@pytest.mark.parametrize("mode", ["one_launch", "select_decode", "separate", "group", "gauss",
+                                  "entmax", "gauss_merged", "entmax_merged"])
 def test_graph_replays_match_eager(mode):
     """bench.py times HIP-graph replays of the step: each replay, with eager
     work and new queries in between, must give the eager step's bits."""
@@ -905,6 +905,11 @@ def test_graph_replays_match_eager(mode):
     d = SparseDecoder.for_workload(wl, device="cuda", **kw)
     # the one-launch 1.5-entmax decode, also for this small batch
     d.entmax_fused = mode.endswith("_merged")
+    if mode == "select_decode":
+        # the form batches past the one-launch row limit take: page_score,
+        # then selection, decode and merge in one launch
+        assert d.score_in_decode and d.select_in_decode
+        d.score_in_decode = False
     cache = dev(W.make_cache(wl))
     bt, sl = dev(wl.block_table), dev(wl.seq_lens)
     q = dev(W.make_queries(wl, 0))
