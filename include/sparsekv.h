@@ -102,36 +102,47 @@ int pagestats_update(uint16_t *kv_cache, int64_t num_blocks, int page_size,
  *
  *   q        fp32 [B, H_q, D]
  *   k_min, k_max bf16 / k_mean fp32 [num_blocks, H_kv, D] (from pagestats_update)
+ *   block_table int32 [B, bt_ld], seq_lens int32 [B]
  *   scores   fp32 [B, H_q, score_ld], logical page order; entries p >= N_b
  *            are not written.  score_ld >= bt_ld.
- *   alibi    fp32 [H_q] or NULL.  For ALiBi heads [EKV "How it works": the
- *            page bound includes ALiBi at each page's best logical position]:
- *            the slope of each query head DIVIDED BY the softmax scale (the
- *            score is in q.k units).  A key at position t of a request of S
- *            tokens has logit bias slope * (t - (S - 1)); the peak term takes
- *            the bias of the page's last valid position (its best), the mean
- *            term that of the mean of its valid positions.  NULL: no bias.
  * The softmax scale is not applied (a positive factor does not change ranks).
  */
 int page_score(const float *q, int B, int H_q, int H_kv, int D,
-               const uint16_t *k_min, const uint16_t *k_max,
-               const float *k_mean, const int32_t *block_table, int64_t bt_ld,
-               const int32_t *seq_lens, int page_size, float w_avg,
-               float w_peak, float *scores, int64_t score_ld,
-               const float *alibi, hipStream_t stream);
+               const uint16_t *k_min, const uint16_t *k_max, const float *k_mean,
+               const int32_t *block_table, int64_t bt_ld, const int32_t *seq_lens, int page_size,
+               float w_avg, float w_peak, float *scores, int64_t score_ld, hipStream_t stream);
+
+/*
+ * page_score_ex -- page_score with ALiBi heads.  [EKV "How it works": the page
+ * bound includes ALiBi at each page's best logical position.]
+ *
+ *   Arguments as page_score, plus
+ *   alibi    fp32 [H_q] or NULL: the slope of each query head DIVIDED BY the
+ *            softmax scale (the score is in q.k units).  A key at position t
+ *            of a request of S tokens has logit bias slope * (t - (S - 1)); the
+ *            peak term takes the bias of the page's last valid position (its
+ *            best), the mean term that of the mean of its valid positions.
+ *            NULL: no bias, the same result as page_score.
+ */
+int page_score_ex(const float *q, int B, int H_q, int H_kv, int D,
+                  const uint16_t *k_min, const uint16_t *k_max,
+                  const float *k_mean, const int32_t *block_table, int64_t bt_ld,
+                  const int32_t *seq_lens, int page_size, float w_avg,
+                  float w_peak, float *scores, int64_t score_ld,
+                  const float *alibi, hipStream_t stream);
 
 /*
  * page_score_group -- one score per (request, kv head, page): the mean, over
- * the G = H_q / H_kv query heads that read kv head h, of page_score's value.
+ * the G = H_q / H_kv query heads that read kv head h, of page_score_ex's value.
  * [VTX: the GQA variants of the page-level flow reduce over the query-group
  * axis; the reduction is read as the plain mean of the group's scores, which
  * ranks pages as their sum does.  Selecting once per kv head (page_topk with
  * H_sel = H_kv) lets sparse_paged_decode read each selected page once for the
  * whole group.]
  *
- *   Arguments and layouts as page_score, except
+ *   Arguments and layouts as page_score_ex, except
  *   scores   fp32 [B, H_kv, score_ld]; entries p >= N_b are not written.
- *   alibi    as page_score; the group's mean slope applies (the mean of the
+ *   alibi    as page_score_ex; the group's mean slope applies (the mean of the
  *            group's biased scores).
  * The mean is formed per dim from the group's mean query and mean |q|
  * (mean_g max(q_g max, q_g min) summed over d equals the mean of the
@@ -151,6 +162,8 @@ int page_score_group(const float *q, int B, int H_q, int H_kv, int D,
  * reserved leading bos and trailing eos entries are kept unconditionally and
  * only the window between them is ranked.]
  *
+ *   scores   fp32 [B, H_sel, score_ld] (page_score, page_score_group or
+ *            h2o_accumulate output)
  *   N = min(ceil(seq_lens[b] / page_size), score_ld) candidates per row.
  *   k = min(N, max(topk_pages, floor(topk_frac * N))), floor taken in double
  *       of the fp32 topk_frac.
@@ -159,19 +172,31 @@ int page_score_group(const float *q, int B, int H_q, int H_kv, int D,
  *   ties going to the lower index (-0.0 equals +0.0; scores must not be NaN).
  *   sel_idx  int32 [B, H_sel, k_cap]: ascending indices, padded with -1.
  *   sel_cnt  int32 [B, H_sel]: number selected (= max(|R|, k)).
- *   sel_blk  int32 [B, H_sel, k_cap] or NULL: when given, the physical block
- *            block_table[b * bt_ld + p] of every selected page p (-1 padded,
- *            -1 for p >= bt_ld), so the decode needs no block-table lookup.
- *            block_table / bt_ld are read only when sel_blk is given.
  *   Requires k_cap >= max(topk_pages, floor(topk_frac * score_ld), bos + eos)
  *   and score_ld <= 32768.
  */
 int page_topk(const float *scores, int64_t score_ld, int B, int H_sel,
-              const int32_t *seq_lens, int page_size, int topk_pages,
-              float topk_frac, int reserved_bos, int reserved_eos,
-              int32_t *sel_idx, int32_t *sel_cnt, int k_cap,
-              const int32_t *block_table, int64_t bt_ld, int32_t *sel_blk,
-              hipStream_t stream);
+              const int32_t *seq_lens, int page_size,
+              int topk_pages, float topk_frac, int reserved_bos, int reserved_eos,
+              int32_t *sel_idx, int32_t *sel_cnt, int k_cap, hipStream_t stream);
+
+/*
+ * page_topk_blk -- page_topk that also writes the physical block of every
+ * selected page, so the decode needs no block-table lookup.  [Sources of
+ * page_topk; EKV "How it works": the block table maps logical pages to blocks.]
+ *
+ *   Arguments as page_topk, plus
+ *   block_table int32 [B, bt_ld] and bt_ld: read only when sel_blk is given.
+ *   sel_blk  int32 [B, H_sel, k_cap] or NULL: block_table[b * bt_ld + p] of
+ *            every selected page p (-1 padded, -1 for p >= bt_ld).  NULL: the
+ *            same result as page_topk.
+ */
+int page_topk_blk(const float *scores, int64_t score_ld, int B, int H_sel,
+                  const int32_t *seq_lens, int page_size, int topk_pages,
+                  float topk_frac, int reserved_bos, int reserved_eos,
+                  int32_t *sel_idx, int32_t *sel_cnt, int k_cap,
+                  const int32_t *block_table, int64_t bt_ld, int32_t *sel_blk,
+                  hipStream_t stream);
 
 /*
  * sparse_paged_decode -- split-K exact softmax attention over the tokens of
@@ -179,6 +204,9 @@ int page_topk(const float *scores, int64_t score_ld, int B, int H_sel,
  * attended and the attention is exact over that selection; MLA: chunked
  * partials merged by log-sum-exp equal single-shot attention.]
  *
+ *   q        fp32 [B, H_q, D];  kv_cache bf16 [2, num_blocks, page_size, H_kv, D]
+ *   block_table int32 [B, bt_ld], seq_lens int32 [B]
+ *   sel_idx  int32 [B, H_sel, k_cap], sel_cnt int32 [B, H_sel] (page_topk's)
  *   H_sel == H_q : row (b, i) of sel_idx is query head i's own selection.
  *   H_sel == H_kv: the G query heads of kv head h share row (b, h) (the
  *                  token-level flow selects per kv head).
@@ -190,33 +218,48 @@ int page_topk(const float *scores, int64_t score_ld, int B, int H_sel,
  *     o_part   fp32 [B, H_q, num_splits, D]  = sum softmax(l) v over the split
  *     lse_part fp32 [B, H_q, num_splits]     = ln sum exp(l)  (-inf if empty,
  *                                               with o_part = 0)
- *   sel_blk (nullable) is page_topk's block-id output for the same rows;
- *   when given, the block table is not read.
- *   alibi_slopes fp32 [H_q] or NULL: per query head ALiBi slope; the logit
- *   of the key at position t becomes l = scale * q . k + slope * (t - (S_b - 1))
- *   [EKV "How it works": ALiBi heads].  NULL: no bias.
  *   With H_sel == H_kv every row a block loads serves all G query heads of
  *   the group; with H_sel == H_q each query head's chunk is walked by its own
  *   wave(s), and pages shared by heads of a group are served by the caches
  *   after their first read.
  */
 int sparse_paged_decode(const float *q, int B, int H_q, int H_kv, int D,
-                        const uint16_t *kv_cache, int64_t num_blocks,
-                        int page_size, const int32_t *block_table,
-                        int64_t bt_ld, const int32_t *seq_lens,
-                        const int32_t *sel_idx, const int32_t *sel_cnt,
-                        const int32_t *sel_blk, int k_cap, int H_sel,
-                        float scale, int num_splits, float *o_part,
-                        float *lse_part, const float *alibi_slopes,
+                        const uint16_t *kv_cache, int64_t num_blocks, int page_size,
+                        const int32_t *block_table, int64_t bt_ld, const int32_t *seq_lens,
+                        const int32_t *sel_idx, const int32_t *sel_cnt, int k_cap, int H_sel,
+                        float scale, int num_splits, float *o_part, float *lse_part,
                         hipStream_t stream);
 
 /*
- * sparse_paged_decode_merged -- sparse_paged_decode for one selection per
+ * sparse_paged_decode_ex -- sparse_paged_decode with block ids from
+ * page_topk_blk and ALiBi heads.  [Sources of sparse_paged_decode; EKV
+ * "How it works": ALiBi heads.]
+ *
+ *   Arguments as sparse_paged_decode, plus
+ *   sel_blk  int32 [B, H_sel, k_cap] or NULL: page_topk_blk's block ids for
+ *            the same rows; when given, the block table is not read.
+ *   alibi_slopes fp32 [H_q] or NULL: per query head ALiBi slope; the logit
+ *            of the key at position t becomes
+ *            l = scale * q . k + slope * (t - (S_b - 1)).
+ *   Both NULL: the same result as sparse_paged_decode.
+ */
+int sparse_paged_decode_ex(const float *q, int B, int H_q, int H_kv, int D,
+                           const uint16_t *kv_cache, int64_t num_blocks,
+                           int page_size, const int32_t *block_table,
+                           int64_t bt_ld, const int32_t *seq_lens,
+                           const int32_t *sel_idx, const int32_t *sel_cnt,
+                           const int32_t *sel_blk, int k_cap, int H_sel,
+                           float scale, int num_splits, float *o_part,
+                           float *lse_part, const float *alibi_slopes,
+                           hipStream_t stream);
+
+/*
+ * sparse_paged_decode_merged -- sparse_paged_decode_ex for one selection per
  * query head (H_sel = H_q) with the split merge done in the same launch: one
  * block per query head, one wave per split, merged in LDS by lse_merge's
  * algebra.  [Same sources as sparse_paged_decode and lse_merge.]
  *
- *   Arguments as sparse_paged_decode (H_sel is H_q), plus
+ *   Arguments as sparse_paged_decode_ex (H_sel is H_q), plus
  *   out      fp32 [B, H_q, D]   merged attention output (required)
  *   lse_out  fp32 [B, H_q] or NULL
  *   o_part, lse_part  both NULL, or both given to also receive the partials.

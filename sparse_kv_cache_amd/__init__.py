@@ -17,8 +17,9 @@ import os
 import torch
 
 __all__ = [
-    "pagestats_update", "page_score", "page_score_group", "page_topk",
-    "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
+    "pagestats_update", "page_score", "page_score_ex", "page_score_group", "page_topk",
+    "page_topk_blk", "sparse_paged_decode", "sparse_paged_decode_ex",
+    "sparse_paged_decode_merged", "lse_merge",
     "h2o_accumulate", "h2o_scratch_floats", "h2o_accumulate_heads",
     "h2o_heads_scratch_floats", "entmax15_paged_decode",
     "entmax_scratch_floats", "sparse_select_decode", "sparse_page_decode",
@@ -32,16 +33,18 @@ _LIB_PATH = os.path.join(_HERE, "libsparsekv.so")
 _lib = None
 
 EXPORTED_SYMBOLS = (
-    "pagestats_update", "page_score", "page_score_group", "page_topk",
-    "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
+    "pagestats_update", "page_score", "page_score_ex", "page_score_group", "page_topk",
+    "page_topk_blk", "sparse_paged_decode", "sparse_paged_decode_ex",
+    "sparse_paged_decode_merged", "lse_merge",
     "h2o_accumulate", "h2o_scratch_floats", "h2o_accumulate_heads",
     "h2o_heads_scratch_floats", "entmax15_paged_decode",
     "entmax_scratch_floats", "sparse_select_decode", "sparse_page_decode",
     "page_var_update", "gauss_moments", "gauss_select", "entmax15_paged_decode_merged",
     "sparsekv_last_error",
 )
-_INT_RETURNING = ("pagestats_update", "page_score", "page_score_group", "page_topk",
-                  "sparse_paged_decode", "sparse_paged_decode_merged", "lse_merge",
+_INT_RETURNING = ("pagestats_update", "page_score", "page_score_ex", "page_score_group",
+                  "page_topk", "page_topk_blk", "sparse_paged_decode",
+                  "sparse_paged_decode_ex", "sparse_paged_decode_merged", "lse_merge",
                   "h2o_accumulate", "h2o_accumulate_heads", "entmax15_paged_decode",
                   "sparse_select_decode",
                   "sparse_page_decode", "page_var_update", "gauss_moments", "gauss_select",
@@ -74,11 +77,15 @@ def load_library():
     lib.sparsekv_last_error.restype = ctypes.c_char_p
     lib.sparsekv_last_error.argtypes = []
     lib.pagestats_update.argtypes = [V, L, I, I, I, V, V, V, V, L, V, I, V, V, V, V]
-    lib.page_score.argtypes = [V, I, I, I, I, V, V, V, V, L, V, I, F, F, V, L, V, V]
-    lib.page_score_group.argtypes = lib.page_score.argtypes
-    lib.page_topk.argtypes = [V, L, I, I, V, I, I, F, I, I, V, V, I, V, L, V, V]
-    lib.sparse_paged_decode.argtypes = [V, I, I, I, I, V, L, I, V, L, V, V, V, V, I,
-                                        I, F, I, V, V, V, V]
+    lib.page_score.argtypes = [V, I, I, I, I, V, V, V, V, L, V, I, F, F, V, L, V]
+    lib.page_score_ex.argtypes = [V, I, I, I, I, V, V, V, V, L, V, I, F, F, V, L, V, V]
+    lib.page_score_group.argtypes = lib.page_score_ex.argtypes
+    lib.page_topk.argtypes = [V, L, I, I, V, I, I, F, I, I, V, V, I, V]
+    lib.page_topk_blk.argtypes = [V, L, I, I, V, I, I, F, I, I, V, V, I, V, L, V, V]
+    lib.sparse_paged_decode.argtypes = [V, I, I, I, I, V, L, I, V, L, V, V, V, I, I, F, I,
+                                        V, V, V]
+    lib.sparse_paged_decode_ex.argtypes = [V, I, I, I, I, V, L, I, V, L, V, V, V, V, I,
+                                           I, F, I, V, V, V, V]
     lib.sparse_paged_decode_merged.argtypes = [V, I, I, I, I, V, L, I, V, L, V, V, V, V,
                                                I, F, I, V, V, V, V, V, V]
     lib.lse_merge.argtypes = [V, V, I, I, I, V, V, V]
@@ -181,19 +188,77 @@ def pagestats_update(kv_cache, k_min, k_max, k_mean, block_table, seq_lens,
         _ptr(v_new), _ptr(hh_score), _stream(stream)))
 
 
+def _shape(name, t, shape):
+    """t (if given) must have exactly `shape`."""
+    if t is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(x) for x in shape)}, "
+                         f"got {tuple(t.shape)}")
+
+
+def _batch(B, block_table, seq_lens):
+    """seq_lens is [B] and block_table (if given) has B rows."""
+    if seq_lens.shape[0] != B:
+        raise ValueError(f"seq_lens must be [B] = [{B}], got {tuple(seq_lens.shape)}")
+    if block_table is not None and block_table.shape[0] != B:
+        raise ValueError(f"block_table must have B = {B} rows, got {tuple(block_table.shape)}")
+
+
+def _stats(k_min, k_max, k_mean, D, dev, NB=None):
+    """The three page statistics share [num_blocks, H_kv, D]; returns (NB, H_kv)."""
+    _check("k_min", k_min, torch.bfloat16, 3, dev)
+    _check("k_max", k_max, torch.bfloat16, 3, dev)
+    _check("k_mean", k_mean, torch.float32, 3, dev)
+    nb, H_kv, d = k_min.shape
+    if d != D:
+        raise ValueError(f"page statistics have head dim {d}, the query {D}")
+    if NB is not None and nb != NB:
+        raise ValueError(f"page statistics cover {nb} blocks, the cache {NB}")
+    _shape("k_max", k_max, (nb, H_kv, D))
+    _shape("k_mean", k_mean, (nb, H_kv, D))
+    return nb, H_kv
+
+
+def _selection(sel_idx, sel_cnt, sel_blk, B, H_sel, dev, k_cap=None):
+    """sel_idx [B, H_sel, k_cap], sel_cnt [B, H_sel], sel_blk like sel_idx."""
+    _check("sel_idx", sel_idx, torch.int32, 3, dev)
+    _check("sel_cnt", sel_cnt, torch.int32, 2, dev)
+    _check("sel_blk", sel_blk, torch.int32, 3, dev)
+    if sel_idx is not None:
+        if tuple(sel_idx.shape[:2]) != (B, H_sel):
+            raise ValueError(f"sel_idx must be [B, H_sel, k_cap] = [{B}, {H_sel}, k_cap], "
+                             f"got {tuple(sel_idx.shape)}")
+        if k_cap is not None and sel_idx.shape[2] != k_cap:
+            raise ValueError(f"sel_idx must have k_cap = {k_cap} columns")
+    _shape("sel_cnt", sel_cnt, (B, H_sel))
+    if sel_blk is not None:
+        if sel_idx is None:
+            raise ValueError("sel_blk needs sel_idx")
+        _shape("sel_blk", sel_blk, sel_idx.shape)
+
+
+def _cache(kv_cache, D, dev):
+    """kv_cache bf16 [2, num_blocks, P, H_kv, D]; returns (NB, P, H_kv)."""
+    _check("kv_cache", kv_cache, torch.bfloat16, 5, dev)
+    two, NB, P, H_kv, D2 = kv_cache.shape
+    if two != 2:
+        raise ValueError("kv_cache must be [2, num_blocks, page_size, H_kv, D]")
+    if D2 != D:
+        raise ValueError("q and kv_cache head dims differ")
+    return NB, P, H_kv
+
+
 def _score_args(q, k_min, k_max, k_mean, block_table, seq_lens, scores, H_out):
     _check("q", q, torch.float32, 3)
     dev = q.device
     B, H_q, D = q.shape
-    _check("k_min", k_min, torch.bfloat16, 3, dev)
-    _check("k_max", k_max, torch.bfloat16, 3, dev)
-    _check("k_mean", k_mean, torch.float32, 3, dev)
+    _, H_kv = _stats(k_min, k_max, k_mean, D, dev)
     _check("block_table", block_table, torch.int32, 2, dev)
     _check("seq_lens", seq_lens, torch.int32, 1, dev)
+    _batch(B, block_table, seq_lens)
     _check("scores", scores, torch.float32, 3, dev)
-    H_kv = k_min.shape[1]
     if tuple(scores.shape[:2]) != (B, H_out(H_q, H_kv)):
-        raise ValueError("scores has the wrong leading shape")
+        raise ValueError(f"scores must be [{B}, {H_out(H_q, H_kv)}, score_ld], "
+                         f"got {tuple(scores.shape)}")
     return B, H_q, H_kv, D
 
 
@@ -207,14 +272,26 @@ def _alibi_arg(alibi, H_q, dev):
 
 
 def page_score(q, k_min, k_max, k_mean, block_table, seq_lens, page_size,
-               w_avg, w_peak, scores, alibi=None, stream=None):
-    """scores[b, i, p] ([B, H_q, score_ld]) for p < N_b from the page statistics;
-    alibi ([H_q], optional) = ALiBi slopes divided by the softmax scale."""
+               w_avg, w_peak, scores, stream=None):
+    """scores[b, i, p] ([B, H_q, score_ld]) for p < N_b from the page statistics."""
+    lib = load_library()
+    B, H_q, H_kv, D = _score_args(q, k_min, k_max, k_mean, block_table, seq_lens,
+                                  scores, lambda hq, hkv: hq)
+    _rc("page_score", lib.page_score(
+        _ptr(q), B, H_q, H_kv, D, _ptr(k_min), _ptr(k_max), _ptr(k_mean),
+        _ptr(block_table), block_table.shape[1], _ptr(seq_lens), int(page_size),
+        float(w_avg), float(w_peak), _ptr(scores), scores.shape[2], _stream(stream)))
+
+
+def page_score_ex(q, k_min, k_max, k_mean, block_table, seq_lens, page_size,
+                  w_avg, w_peak, scores, alibi=None, stream=None):
+    """page_score with ALiBi heads: alibi ([H_q], optional) = ALiBi slopes
+    divided by the softmax scale."""
     lib = load_library()
     B, H_q, H_kv, D = _score_args(q, k_min, k_max, k_mean, block_table, seq_lens,
                                   scores, lambda hq, hkv: hq)
     alibi = _alibi_arg(alibi, H_q, q.device)
-    _rc("page_score", lib.page_score(
+    _rc("page_score_ex", lib.page_score_ex(
         _ptr(q), B, H_q, H_kv, D, _ptr(k_min), _ptr(k_max), _ptr(k_mean),
         _ptr(block_table), block_table.shape[1], _ptr(seq_lens), int(page_size),
         float(w_avg), float(w_peak), _ptr(scores), scores.shape[2], _ptr(alibi),
@@ -236,68 +313,112 @@ def page_score_group(q, k_min, k_max, k_mean, block_table, seq_lens, page_size,
         _stream(stream)))
 
 
-def page_topk(scores, seq_lens, page_size, topk_pages, sel_idx, sel_cnt,
-              topk_frac=0.0, reserved_bos=0, reserved_eos=1, block_table=None,
-              sel_blk=None, stream=None):
-    """Top-k rows of scores [B, H_sel, score_ld] into sel_idx [B, H_sel, k_cap];
-    with sel_blk (and block_table) also the selected pages' physical blocks."""
-    lib = load_library()
+def _topk_args(scores, seq_lens, sel_idx, sel_cnt):
     _check("scores", scores, torch.float32, 3)
     dev = scores.device
     B, H_sel, ld = scores.shape
     _check("seq_lens", seq_lens, torch.int32, 1, dev)
-    _check("sel_idx", sel_idx, torch.int32, 3, dev)
-    _check("sel_cnt", sel_cnt, torch.int32, 2, dev)
-    if tuple(sel_idx.shape[:2]) != (B, H_sel) or tuple(sel_cnt.shape) != (B, H_sel):
-        raise ValueError("sel_idx must be [B, H_sel, k_cap] and sel_cnt [B, H_sel]")
-    _check("sel_blk", sel_blk, torch.int32, 3, dev)
-    bt_ld = 0
-    if sel_blk is not None:
-        if block_table is None:
-            raise ValueError("sel_blk needs block_table")
-        _check("block_table", block_table, torch.int32, 2, dev)
-        if sel_blk.shape != sel_idx.shape:
-            raise ValueError("sel_blk must have sel_idx's shape")
-        bt_ld = block_table.shape[1]
+    _batch(B, None, seq_lens)
+    if sel_idx is None or sel_cnt is None:
+        raise ValueError("sel_idx and sel_cnt are required")
+    _selection(sel_idx, sel_cnt, None, B, H_sel, dev)
+    return dev, B, H_sel, ld
+
+
+def page_topk(scores, seq_lens, page_size, topk_pages, sel_idx, sel_cnt,
+              topk_frac=0.0, reserved_bos=0, reserved_eos=1, stream=None):
+    """Top-k rows of scores [B, H_sel, score_ld] into sel_idx [B, H_sel, k_cap]
+    and sel_cnt [B, H_sel]."""
+    lib = load_library()
+    _, B, H_sel, ld = _topk_args(scores, seq_lens, sel_idx, sel_cnt)
     _rc("page_topk", lib.page_topk(
         _ptr(scores), ld, B, H_sel, _ptr(seq_lens), int(page_size), int(topk_pages),
         float(topk_frac), int(reserved_bos), int(reserved_eos), _ptr(sel_idx),
-        _ptr(sel_cnt), sel_idx.shape[2],
-        _ptr(block_table) if sel_blk is not None else None, bt_ld, _ptr(sel_blk),
-        _stream(stream)))
+        _ptr(sel_cnt), sel_idx.shape[2], _stream(stream)))
 
 
-def sparse_paged_decode(q, kv_cache, block_table, seq_lens, sel_idx, sel_cnt,
-                        scale, o_part, lse_part, sel_blk=None, alibi_slopes=None,
-                        stream=None):
-    """Split-K partials over the selected pages.  H_sel = sel_idx.shape[1];
-    num_splits = o_part.shape[2]; sel_blk (optional) from page_topk;
-    alibi_slopes ([H_q], optional) ALiBi slopes."""
+def page_topk_blk(scores, seq_lens, page_size, topk_pages, sel_idx, sel_cnt,
+                  block_table, sel_blk, topk_frac=0.0, reserved_bos=0, reserved_eos=1,
+                  stream=None):
+    """page_topk that also writes the selected pages' physical blocks
+    (sel_blk, like sel_idx; None = page_topk's result only)."""
     lib = load_library()
+    dev, B, H_sel, ld = _topk_args(scores, seq_lens, sel_idx, sel_cnt)
+    _check("block_table", block_table, torch.int32, 2, dev)
+    _batch(B, block_table, seq_lens)
+    _selection(sel_idx, sel_cnt, sel_blk, B, H_sel, dev)
+    _rc("page_topk_blk", lib.page_topk_blk(
+        _ptr(scores), ld, B, H_sel, _ptr(seq_lens), int(page_size), int(topk_pages),
+        float(topk_frac), int(reserved_bos), int(reserved_eos), _ptr(sel_idx),
+        _ptr(sel_cnt), sel_idx.shape[2], _ptr(block_table), block_table.shape[1],
+        _ptr(sel_blk), _stream(stream)))
+
+
+def _decode_args(q, kv_cache, block_table, seq_lens, sel_idx, sel_cnt, sel_blk,
+                 H_sel=None):
     _check("q", q, torch.float32, 3)
     dev = q.device
     B, H_q, D = q.shape
-    _check("kv_cache", kv_cache, torch.bfloat16, 5, dev)
-    _, NB, P, H_kv, D2 = kv_cache.shape
-    if D2 != D:
-        raise ValueError("q and kv_cache head dims differ")
+    NB, P, H_kv = _cache(kv_cache, D, dev)
     _check("block_table", block_table, torch.int32, 2, dev)
     _check("seq_lens", seq_lens, torch.int32, 1, dev)
+    _batch(B, block_table, seq_lens)
+    if sel_idx is None or sel_cnt is None:
+        raise ValueError("sel_idx and sel_cnt are required")
     _check("sel_idx", sel_idx, torch.int32, 3, dev)
-    _check("sel_cnt", sel_cnt, torch.int32, 2, dev)
+    if H_sel is None:
+        H_sel = sel_idx.shape[1]
+    if H_sel not in (H_q, H_kv):
+        raise ValueError(f"the selection must have H_q = {H_q} or H_kv = {H_kv} rows "
+                         f"per request, got {H_sel}")
+    _selection(sel_idx, sel_cnt, sel_blk, B, H_sel, dev)
+    return dev, B, H_q, D, NB, P, H_kv, H_sel
+
+
+def _partials(o_part, lse_part, B, H_q, D, dev, num_splits=None):
     _check("o_part", o_part, torch.float32, 4, dev)
     _check("lse_part", lse_part, torch.float32, 3, dev)
-    ns = o_part.shape[2]
-    H_sel = sel_idx.shape[1]
-    if tuple(o_part.shape) != (B, H_q, ns, D) or tuple(lse_part.shape) != (B, H_q, ns):
-        raise ValueError("o_part must be [B, H_q, splits, D] and lse_part [B, H_q, splits]")
-    if sel_idx.shape[0] != B or tuple(sel_cnt.shape) != (B, H_sel):
-        raise ValueError("sel_idx must be [B, H_sel, k_cap] and sel_cnt [B, H_sel]")
-    _check("sel_blk", sel_blk, torch.int32, 3, dev)
-    if sel_blk is not None and sel_blk.shape != sel_idx.shape:
-        raise ValueError("sel_blk must have sel_idx's shape")
-    alibi_slopes = _alibi_arg(alibi_slopes, H_q, dev)
+    ns = o_part.shape[2] if num_splits is None else int(num_splits)
+    _shape("o_part", o_part, (B, H_q, ns, D))
+    _shape("lse_part", lse_part, (B, H_q, ns))
+    return ns
+
+
+def _outputs(out, lse_out, B, H_q, D, dev, required=True):
+    if required and out is None:
+        raise ValueError("out is required")
+    _check("out", out, torch.float32, 3, dev)
+    _check("lse_out", lse_out, torch.float32, 2, dev)
+    _shape("out", out, (B, H_q, D))
+    _shape("lse_out", lse_out, (B, H_q))
+
+
+def sparse_paged_decode(q, kv_cache, block_table, seq_lens, sel_idx, sel_cnt,
+                        scale, o_part, lse_part, stream=None):
+    """Split-K partials over the selected pages.  H_sel = sel_idx.shape[1];
+    num_splits = o_part.shape[2]."""
+    lib = load_library()
+    dev, B, H_q, D, NB, P, H_kv, H_sel = _decode_args(q, kv_cache, block_table, seq_lens,
+                                                      sel_idx, sel_cnt, None)
+    ns = _partials(o_part, lse_part, B, H_q, D, dev)
     _rc("sparse_paged_decode", lib.sparse_paged_decode(
+        _ptr(q), B, H_q, H_kv, D, _ptr(kv_cache), NB, P, _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), _ptr(sel_idx), _ptr(sel_cnt),
+        sel_idx.shape[2], H_sel, float(scale), ns, _ptr(o_part), _ptr(lse_part),
+        _stream(stream)))
+
+
+def sparse_paged_decode_ex(q, kv_cache, block_table, seq_lens, sel_idx, sel_cnt,
+                           scale, o_part, lse_part, sel_blk=None, alibi_slopes=None,
+                           stream=None):
+    """sparse_paged_decode with page_topk_blk's block ids (sel_blk) and ALiBi
+    slopes ([H_q], logit units); both optional."""
+    lib = load_library()
+    dev, B, H_q, D, NB, P, H_kv, H_sel = _decode_args(q, kv_cache, block_table, seq_lens,
+                                                      sel_idx, sel_cnt, sel_blk)
+    ns = _partials(o_part, lse_part, B, H_q, D, dev)
+    alibi_slopes = _alibi_arg(alibi_slopes, H_q, dev)
+    _rc("sparse_paged_decode_ex", lib.sparse_paged_decode_ex(
         _ptr(q), B, H_q, H_kv, D, _ptr(kv_cache), NB, P, _ptr(block_table),
         block_table.shape[1], _ptr(seq_lens), _ptr(sel_idx), _ptr(sel_cnt),
         _ptr(sel_blk), sel_idx.shape[2], H_sel, float(scale), ns, _ptr(o_part),
@@ -311,31 +432,13 @@ def sparse_paged_decode_merged(q, kv_cache, block_table, seq_lens, sel_idx, sel_
     """Decode with one selection per query head and the split merge in the same
     launch: out [B, H_q, D] (and lse_out [B, H_q]); num_splits <= 8."""
     lib = load_library()
-    _check("q", q, torch.float32, 3)
-    dev = q.device
-    B, H_q, D = q.shape
-    _check("kv_cache", kv_cache, torch.bfloat16, 5, dev)
-    _, NB, P, H_kv, D2 = kv_cache.shape
-    if D2 != D:
-        raise ValueError("q and kv_cache head dims differ")
-    _check("block_table", block_table, torch.int32, 2, dev)
-    _check("seq_lens", seq_lens, torch.int32, 1, dev)
-    _check("sel_idx", sel_idx, torch.int32, 3, dev)
-    _check("sel_cnt", sel_cnt, torch.int32, 2, dev)
-    _check("out", out, torch.float32, 3, dev)
-    _check("lse_out", lse_out, torch.float32, 2, dev)
-    if tuple(sel_idx.shape[:2]) != (B, H_q) or tuple(sel_cnt.shape) != (B, H_q):
-        raise ValueError("sel_idx must be [B, H_q, k_cap] and sel_cnt [B, H_q]")
-    if tuple(out.shape) != (B, H_q, D):
-        raise ValueError("out must be [B, H_q, D]")
+    dev, B, H_q, D, NB, P, H_kv, _ = _decode_args(q, kv_cache, block_table, seq_lens,
+                                                  sel_idx, sel_cnt, sel_blk, H_sel=q.shape[1])
+    _outputs(out, lse_out, B, H_q, D, dev)
     if (o_part is None) != (lse_part is None):
         raise ValueError("o_part and lse_part go together")
     if o_part is not None:
-        _check("o_part", o_part, torch.float32, 4, dev)
-        _check("lse_part", lse_part, torch.float32, 3, dev)
-        if tuple(o_part.shape) != (B, H_q, num_splits, D):
-            raise ValueError("o_part must be [B, H_q, num_splits, D]")
-    _check("sel_blk", sel_blk, torch.int32, 3, dev)
+        _partials(o_part, lse_part, B, H_q, D, dev, num_splits)
     alibi_slopes = _alibi_arg(alibi_slopes, H_q, dev)
     _rc("sparse_paged_decode_merged", lib.sparse_paged_decode_merged(
         _ptr(q), B, H_q, H_kv, D, _ptr(kv_cache), NB, P, _ptr(block_table),
@@ -360,25 +463,12 @@ def entmax15_paged_decode(q, kv_cache, block_table, seq_lens, sel_idx, sel_cnt, 
     combined by lse_merge.  alibi_slopes ([H_q], logit units) adds
     slope * (pos - (S - 1)) to each logit."""
     lib = load_library()
-    _check("q", q, torch.float32, 3)
-    dev = q.device
-    B, H_q, D = q.shape
-    _check("kv_cache", kv_cache, torch.bfloat16, 5, dev)
-    _, NB, P, H_kv, D2 = kv_cache.shape
-    if D2 != D:
-        raise ValueError("q and kv_cache head dims differ")
-    _check("block_table", block_table, torch.int32, 2, dev)
-    _check("seq_lens", seq_lens, torch.int32, 1, dev)
-    _check("sel_idx", sel_idx, torch.int32, 3, dev)
-    _check("sel_cnt", sel_cnt, torch.int32, 2, dev)
-    _check("o_part", o_part, torch.float32, 4, dev)
-    _check("lse_part", lse_part, torch.float32, 3, dev)
+    dev, B, H_q, D, NB, P, H_kv, H_sel = _decode_args(q, kv_cache, block_table, seq_lens,
+                                                      sel_idx, sel_cnt, sel_blk)
+    ns = _partials(o_part, lse_part, B, H_q, D, dev)
+    if scratch is None:
+        raise ValueError("scratch is required")
     _check("scratch", scratch, torch.float32, 1, dev)
-    _check("sel_blk", sel_blk, torch.int32, 3, dev)
-    ns = o_part.shape[2]
-    H_sel = sel_idx.shape[1]
-    if tuple(o_part.shape) != (B, H_q, ns, D) or tuple(lse_part.shape) != (B, H_q, ns):
-        raise ValueError("o_part must be [B, H_q, splits, D] and lse_part [B, H_q, splits]")
     alibi_slopes = _alibi_arg(alibi_slopes, H_q, dev)
     _rc("entmax15_paged_decode", lib.entmax15_paged_decode(
         _ptr(q), B, H_q, H_kv, D, _ptr(kv_cache), NB, P, _ptr(block_table),
@@ -394,32 +484,17 @@ def entmax15_paged_decode_merged(q, kv_cache, block_table, seq_lens, sel_idx, se
     [B, H_q, D] = sum p v / sum p; lse_out, tau_out [B, H_q] optional; scratch
     (fp32, B * H_q * k_cap * P floats) only when k_cap * P > 8192."""
     lib = load_library()
-    _check("q", q, torch.float32, 3)
-    dev = q.device
-    B, H_q, D = q.shape
-    _check("kv_cache", kv_cache, torch.bfloat16, 5, dev)
-    _, NB, P, H_kv, D2 = kv_cache.shape
-    if D2 != D:
-        raise ValueError("q and kv_cache head dims differ")
-    _check("block_table", block_table, torch.int32, 2, dev)
-    _check("seq_lens", seq_lens, torch.int32, 1, dev)
-    _check("sel_idx", sel_idx, torch.int32, 3, dev)
-    _check("sel_cnt", sel_cnt, torch.int32, 2, dev)
-    _check("sel_blk", sel_blk, torch.int32, 3, dev)
-    _check("out", out, torch.float32, 3, dev)
-    _check("lse_out", lse_out, torch.float32, 2, dev)
+    dev, B, H_q, D, NB, P, H_kv, H_sel = _decode_args(q, kv_cache, block_table, seq_lens,
+                                                      sel_idx, sel_cnt, sel_blk)
+    _outputs(out, lse_out, B, H_q, D, dev)
     _check("tau_out", tau_out, torch.float32, 2, dev)
+    _shape("tau_out", tau_out, (B, H_q))
     _check("scratch", scratch, torch.float32, 1, dev)
-    if tuple(out.shape) != (B, H_q, D):
-        raise ValueError("out must be [B, H_q, D]")
-    for n, t in (("lse_out", lse_out), ("tau_out", tau_out)):
-        if t is not None and tuple(t.shape) != (B, H_q):
-            raise ValueError(f"{n} must be [B, H_q]")
     alibi_slopes = _alibi_arg(alibi_slopes, H_q, dev)
     _rc("entmax15_paged_decode_merged", lib.entmax15_paged_decode_merged(
         _ptr(q), B, H_q, H_kv, D, _ptr(kv_cache), NB, P, _ptr(block_table),
         block_table.shape[1], _ptr(seq_lens), _ptr(sel_idx), _ptr(sel_cnt), _ptr(sel_blk),
-        sel_idx.shape[2], sel_idx.shape[1], float(scale), _ptr(alibi_slopes), _ptr(out),
+        sel_idx.shape[2], H_sel, float(scale), _ptr(alibi_slopes), _ptr(out),
         _ptr(lse_out), _ptr(tau_out), _ptr(scratch),
         0 if scratch is None else scratch.numel(), _stream(stream)))
 
@@ -456,11 +531,19 @@ def gauss_moments(q, k_mean, k_var, block_table, seq_lens, page_size, scale, mu,
     B, H_q, D = q.shape
     _check("k_mean", k_mean, torch.float32, 3, dev)
     _check("k_var", k_var, torch.float32, 3, dev)
+    NB, H_kv, d = k_mean.shape
+    if d != D:
+        raise ValueError("k_mean and q head dims differ")
+    _shape("k_var", k_var, (NB, H_kv, D))
+    if H_q % H_kv:
+        raise ValueError("H_q must be a multiple of H_kv")
     _check("block_table", block_table, torch.int32, 2, dev)
     _check("seq_lens", seq_lens, torch.int32, 1, dev)
+    _batch(B, block_table, seq_lens)
     _check("mu", mu, torch.float32, 3, dev)
     _check("var", var, torch.float32, 3, dev)
-    H_kv = k_mean.shape[1]
+    if mu is None or var is None:
+        raise ValueError("mu and var are required")
     if tuple(mu.shape[:2]) != (B, H_q) or mu.shape != var.shape:
         raise ValueError("mu and var must be [B, H_q, ld]")
     alibi_slopes = _alibi_arg(alibi_slopes, H_q, dev)
@@ -484,23 +567,27 @@ def gauss_select(mu, var, seq_lens, page_size, block_table, mixture, k_cap, est,
     _check("est", est, torch.float32, 3, dev)
     _check("seq_lens", seq_lens, torch.int32, 1, dev)
     _check("block_table", block_table, torch.int32, 2, dev)
-    _check("sel_idx", sel_idx, torch.int32, 3, dev)
-    _check("sel_cnt", sel_cnt, torch.int32, 2, dev)
+    _batch(B, block_table, seq_lens)
     _check("tau", tau, torch.float32, 2, dev)
-    _check("sel_blk", sel_blk, torch.int32, 3, dev)
-    if var.shape != mu.shape or est.shape != mu.shape:
+    if var is None or est is None or var.shape != mu.shape or est.shape != mu.shape:
         raise ValueError("mu, var and est must share the shape [B, H_q, ld]")
-    if tuple(sel_idx.shape) != (B, H_q, int(k_cap)) or tuple(sel_cnt.shape) != (B, H_q):
-        raise ValueError("sel_idx must be [B, H_q, k_cap] and sel_cnt [B, H_q]")
-    if sel_blk is not None and sel_blk.shape != sel_idx.shape:
-        raise ValueError("sel_blk must match sel_idx")
-    if tau is not None and tuple(tau.shape) != (B, H_q):
-        raise ValueError("tau must be [B, H_q]")
+    if sel_idx is None or sel_cnt is None:
+        raise ValueError("sel_idx and sel_cnt are required")
+    _selection(sel_idx, sel_cnt, sel_blk, B, H_q, dev, int(k_cap))
+    _shape("tau", tau, (B, H_q))
     _rc("gauss_select", lib.gauss_select(
         _ptr(mu), _ptr(var), ld, B, H_q, _ptr(seq_lens), int(page_size), _ptr(block_table),
         block_table.shape[1], 1 if mixture else 0, int(reserved_bos), int(reserved_eos),
         int(k_cap), _ptr(tau), _ptr(est), _ptr(sel_idx), _ptr(sel_cnt), _ptr(sel_blk),
         _stream(stream)))
+
+
+def _optional_selection(sel_idx, sel_cnt, sel_blk, B, H_q, k_cap, dev):
+    if (sel_idx is None) != (sel_cnt is None):
+        raise ValueError("sel_idx and sel_cnt go together")
+    if sel_blk is not None and sel_idx is None:
+        raise ValueError("sel_blk needs sel_idx")
+    _selection(sel_idx, sel_cnt, sel_blk, B, H_q, dev, int(k_cap))
 
 
 def sparse_select_decode(scores, q, kv_cache, block_table, seq_lens, topk_pages, k_cap,
@@ -509,27 +596,20 @@ def sparse_select_decode(scores, q, kv_cache, block_table, seq_lens, topk_pages,
                          sel_blk=None, alibi_slopes=None, stream=None):
     """page_topk + sparse_paged_decode_merged in one launch (one selection per
     query head, score_ld <= 4096, num_splits <= 8); optionally writes the
-    selection like page_topk."""
+    selection like page_topk_blk."""
     lib = load_library()
-    _check("scores", scores, torch.float32, 3)
     _check("q", q, torch.float32, 3)
     dev = q.device
     B, H_q, D = q.shape
-    _check("kv_cache", kv_cache, torch.bfloat16, 5, dev)
-    _, NB, P, H_kv, D2 = kv_cache.shape
-    if D2 != D:
-        raise ValueError("q and kv_cache head dims differ")
-    if tuple(scores.shape[:2]) != (B, H_q):
+    _check("scores", scores, torch.float32, 3, dev)
+    NB, P, H_kv = _cache(kv_cache, D, dev)
+    if scores is None or tuple(scores.shape[:2]) != (B, H_q):
         raise ValueError("scores must be [B, H_q, score_ld]")
     _check("block_table", block_table, torch.int32, 2, dev)
     _check("seq_lens", seq_lens, torch.int32, 1, dev)
-    _check("out", out, torch.float32, 3, dev)
-    _check("lse_out", lse_out, torch.float32, 2, dev)
-    for n, t in (("sel_idx", sel_idx), ("sel_blk", sel_blk)):
-        _check(n, t, torch.int32, 3, dev)
-        if t is not None and tuple(t.shape) != (B, H_q, k_cap):
-            raise ValueError(f"{n} must be [B, H_q, k_cap]")
-    _check("sel_cnt", sel_cnt, torch.int32, 2, dev)
+    _batch(B, block_table, seq_lens)
+    _outputs(out, lse_out, B, H_q, D, dev)
+    _optional_selection(sel_idx, sel_cnt, sel_blk, B, H_q, k_cap, dev)
     alibi_slopes = _alibi_arg(alibi_slopes, H_q, dev)
     _rc("sparse_select_decode", lib.sparse_select_decode(
         _ptr(scores), scores.shape[2], int(topk_pages), float(topk_frac), int(reserved_bos),
@@ -550,26 +630,18 @@ def sparse_page_decode(q, kv_cache, k_min, k_max, k_mean, block_table, seq_lens,
     _check("q", q, torch.float32, 3)
     dev = q.device
     B, H_q, D = q.shape
-    _check("kv_cache", kv_cache, torch.bfloat16, 5, dev)
-    _, NB, P, H_kv, D2 = kv_cache.shape
-    if D2 != D:
-        raise ValueError("q and kv_cache head dims differ")
-    _check("k_min", k_min, torch.bfloat16, 3, dev)
-    _check("k_max", k_max, torch.bfloat16, 3, dev)
-    _check("k_mean", k_mean, torch.float32, 3, dev)
+    NB, P, H_kv = _cache(kv_cache, D, dev)
+    _stats(k_min, k_max, k_mean, D, dev, NB)
+    if k_min.shape[1] != H_kv:
+        raise ValueError("page statistics and kv_cache kv-head counts differ")
     _check("block_table", block_table, torch.int32, 2, dev)
     _check("seq_lens", seq_lens, torch.int32, 1, dev)
-    _check("out", out, torch.float32, 3, dev)
-    _check("lse_out", lse_out, torch.float32, 2, dev)
+    _batch(B, block_table, seq_lens)
+    _outputs(out, lse_out, B, H_q, D, dev)
     bt_ld = block_table.shape[1]
     _check("scores", scores, torch.float32, 3, dev)
-    if scores is not None and tuple(scores.shape) != (B, H_q, bt_ld):
-        raise ValueError("scores must be [B, H_q, bt_ld]")
-    for n, t in (("sel_idx", sel_idx), ("sel_blk", sel_blk)):
-        _check(n, t, torch.int32, 3, dev)
-        if t is not None and tuple(t.shape) != (B, H_q, k_cap):
-            raise ValueError(f"{n} must be [B, H_q, k_cap]")
-    _check("sel_cnt", sel_cnt, torch.int32, 2, dev)
+    _shape("scores", scores, (B, H_q, bt_ld))
+    _optional_selection(sel_idx, sel_cnt, sel_blk, B, H_q, k_cap, dev)
     alibi_slopes = _alibi_arg(alibi_slopes, H_q, dev)
     _rc("sparse_page_decode", lib.sparse_page_decode(
         _ptr(q), B, H_q, H_kv, D, _ptr(kv_cache), NB, P, _ptr(k_min), _ptr(k_max),
@@ -587,13 +659,14 @@ def lse_merge(o_part, lse_part, out, lse_out=None, stream=None):
     _check("lse_part", lse_part, torch.float32, None, dev)
     _check("out", out, torch.float32, None, dev)
     _check("lse_out", lse_out, torch.float32, None, dev)
-    D = o_part.shape[-1]
-    ns = o_part.shape[-2]
+    if o_part.dim() < 2 or lse_part is None or out is None:
+        raise ValueError("o_part [..., splits, D], lse_part and out are required")
+    lead = tuple(o_part.shape[:-2])
+    ns, D = o_part.shape[-2], o_part.shape[-1]
+    _shape("lse_part", lse_part, lead + (ns,))
+    _shape("out", out, lead + (D,))
+    _shape("lse_out", lse_out, lead)
     rows = o_part.numel() // (ns * D) if o_part.numel() else 0
-    if lse_part.numel() != rows * ns or out.numel() != rows * D:
-        raise ValueError("inconsistent partial / output sizes")
-    if lse_out is not None and lse_out.numel() != rows:
-        raise ValueError("lse_out must hold one value per row")
     _rc("lse_merge", lib.lse_merge(_ptr(o_part), _ptr(lse_part), rows, ns, D,
                                    _ptr(out), _ptr(lse_out), _stream(stream)))
 
@@ -612,15 +685,17 @@ def _h2o(name, q, kv_cache, block_table, seq_lens, hh_score, scores, scratch, sc
     _check("q", q, torch.float32, 3)
     dev = q.device
     B, H_q, D = q.shape
-    _check("kv_cache", kv_cache, torch.bfloat16, 5, dev)
-    _, NB, P, H_kv, _ = kv_cache.shape
+    NB, P, H_kv = _cache(kv_cache, D, dev)
     _check("block_table", block_table, torch.int32, 2, dev)
     _check("seq_lens", seq_lens, torch.int32, 1, dev)
+    _batch(B, block_table, seq_lens)
+    for n, t in (("hh_score", hh_score), ("scores", scores), ("scratch", scratch)):
+        if t is None:
+            raise ValueError(f"{n} is required")
     _check("hh_score", hh_score, torch.bfloat16, 2, dev)
     _check("scores", scores, torch.float32, 3, dev)
     _check("scratch", scratch, torch.float32, 1, dev)
-    if tuple(hh_score.shape) != (NB * P, H_kv):
-        raise ValueError("hh_score must be [num_blocks, H_kv]")
+    _shape("hh_score", hh_score, (NB * P, H_kv))
     if tuple(scores.shape[:2]) != (B, H_kv):
         raise ValueError("scores must be [B, H_kv, score_ld]")
     _rc(name, getattr(lib, name)(

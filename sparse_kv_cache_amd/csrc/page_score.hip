@@ -238,8 +238,19 @@ extern "C" int page_score(const float* q, int B, int H_q, int H_kv, int D,
                           const float* k_mean, const int32_t* block_table,
                           int64_t bt_ld, const int32_t* seq_lens, int page_size,
                           float w_avg, float w_peak, float* scores,
-                          int64_t score_ld, const float* alibi, hipStream_t stream) {
+                          int64_t score_ld, hipStream_t stream) {
   return score_pages("page_score", false, q, B, H_q, H_kv, D, k_min, k_max, k_mean,
+                     block_table, bt_ld, seq_lens, page_size, w_avg, w_peak, scores,
+                     score_ld, nullptr, stream);
+}
+
+extern "C" int page_score_ex(const float* q, int B, int H_q, int H_kv, int D,
+                             const uint16_t* k_min, const uint16_t* k_max,
+                             const float* k_mean, const int32_t* block_table,
+                             int64_t bt_ld, const int32_t* seq_lens, int page_size,
+                             float w_avg, float w_peak, float* scores,
+                             int64_t score_ld, const float* alibi, hipStream_t stream) {
+  return score_pages("page_score_ex", false, q, B, H_q, H_kv, D, k_min, k_max, k_mean,
                      block_table, bt_ld, seq_lens, page_size, w_avg, w_peak, scores,
                      score_ld, alibi, stream);
 }

@@ -72,22 +72,25 @@ void launch_topk(int64_t rows, hipStream_t stream, const float* scores,
 
 }  // namespace
 
-extern "C" int page_topk(const float* scores, int64_t score_ld, int B,
-                         int H_sel, const int32_t* seq_lens, int page_size,
-                         int topk_pages, float topk_frac, int reserved_bos,
-                         int reserved_eos, int32_t* sel_idx, int32_t* sel_cnt,
-                         int k_cap, const int32_t* block_table, int64_t bt_ld,
-                         int32_t* sel_blk, hipStream_t stream) {
-  SKV_REQUIRE(B >= 0 && H_sel > 0, "page_topk: need B >= 0 and H_sel > 0");
+namespace {
+
+// Validation and dispatch shared by page_topk and page_topk_blk.
+int topk_impl(const char* who, const float* scores, int64_t score_ld, int B, int H_sel,
+              const int32_t* seq_lens, int page_size, int topk_pages, float topk_frac,
+              int reserved_bos, int reserved_eos, int32_t* sel_idx, int32_t* sel_cnt,
+              int k_cap, const int32_t* block_table, int64_t bt_ld, int32_t* sel_blk,
+              hipStream_t stream) {
+  SKV_REQUIRE(B >= 0 && H_sel > 0, "%s: need B >= 0 and H_sel > 0", who);
   SKV_REQUIRE(score_ld > 0 && score_ld <= 32768,
-              "page_topk: score_ld must be in [1, 32768] (got %lld)", (long long)score_ld);
+              "%s: score_ld must be in [1, 32768] (got %lld)", who, (long long)score_ld);
   SKV_REQUIRE(skv_supported_page_size(page_size),
-              "page_topk: page_size must be 1, 2, 4, 8 or 16 (got %d)", page_size);
-  SKV_REQUIRE(topk_pages >= 1, "page_topk: topk_pages must be >= 1 (got %d)", topk_pages);
+              "%s: page_size must be 1, 2, 4, 8 or 16 (got %d)", who, page_size);
+  SKV_REQUIRE(topk_pages >= 1, "%s: topk_pages must be >= 1 (got %d)", who,
+              topk_pages);
   SKV_REQUIRE(topk_frac >= 0.0f && topk_frac <= 1.0f,
-              "page_topk: topk_frac must be in [0, 1]");
+              "%s: topk_frac must be in [0, 1]", who);
   SKV_REQUIRE(reserved_bos >= 0 && reserved_eos >= 0,
-              "page_topk: reserved_bos / reserved_eos must be >= 0");
+              "%s: reserved_bos / reserved_eos must be >= 0", who);
   const double frac = static_cast<double>(topk_frac);
   int64_t need = topk_pages;
   const int64_t fk = static_cast<int64_t>(floor(frac * static_cast<double>(score_ld)));
@@ -95,20 +98,20 @@ extern "C" int page_topk(const float* scores, int64_t score_ld, int B,
   if (static_cast<int64_t>(reserved_bos) + reserved_eos > need)
     need = static_cast<int64_t>(reserved_bos) + reserved_eos;
   if (need > score_ld) need = score_ld;
-  SKV_REQUIRE(k_cap >= need, "page_topk: k_cap %d < largest possible selection %lld",
+  SKV_REQUIRE(k_cap >= need, "%s: k_cap %d < largest possible selection %lld", who,
               k_cap, (long long)need);
   // no rows: nothing is read or written, so no pointer is needed
   if (B == 0) { skv::clear_error(); return SKV_OK; }
-  SKV_REQUIRE_PTR(scores);
-  SKV_REQUIRE_PTR(seq_lens);
-  SKV_REQUIRE_PTR(sel_idx);
-  SKV_REQUIRE_PTR(sel_cnt);
+  SKV_REQUIRE_PTR_W(who, scores);
+  SKV_REQUIRE_PTR_W(who, seq_lens);
+  SKV_REQUIRE_PTR_W(who, sel_idx);
+  SKV_REQUIRE_PTR_W(who, sel_cnt);
   if (sel_blk != nullptr) {
-    SKV_REQUIRE_PTR(block_table);
-    SKV_REQUIRE(bt_ld > 0, "page_topk: bt_ld must be > 0 when sel_blk is given");
+    SKV_REQUIRE_PTR_W(who, block_table);
+    SKV_REQUIRE(bt_ld > 0, "%s: bt_ld must be > 0 when sel_blk is given", who);
   }
   const int64_t rows = static_cast<int64_t>(B) * H_sel;
-  SKV_REQUIRE(rows <= 0x7fffffff, "page_topk: too many rows");
+  SKV_REQUIRE(rows <= 0x7fffffff, "%s: too many rows", who);
 #define SKV_TOPK(BL, IT, EA)                                                          \
   launch_topk<BL, IT, EA>(rows, stream, scores, score_ld, H_sel, seq_lens, page_size, \
                           topk_pages, frac, reserved_bos, reserved_eos, sel_idx,      \
@@ -132,5 +135,28 @@ extern "C" int page_topk(const float* scores, int64_t score_ld, int B,
     else SKV_TOPK(1024, 32, false);
   }
 #undef SKV_TOPK
-  SKV_CHECK_LAUNCH();
+  SKV_CHECK_LAUNCH_W(who);
+}
+
+}  // namespace
+
+extern "C" int page_topk(const float* scores, int64_t score_ld, int B, int H_sel,
+                         const int32_t* seq_lens, int page_size, int topk_pages,
+                         float topk_frac, int reserved_bos, int reserved_eos,
+                         int32_t* sel_idx, int32_t* sel_cnt, int k_cap,
+                         hipStream_t stream) {
+  return topk_impl("page_topk", scores, score_ld, B, H_sel, seq_lens, page_size,
+                   topk_pages, topk_frac, reserved_bos, reserved_eos, sel_idx, sel_cnt,
+                   k_cap, nullptr, 0, nullptr, stream);
+}
+
+extern "C" int page_topk_blk(const float* scores, int64_t score_ld, int B, int H_sel,
+                             const int32_t* seq_lens, int page_size, int topk_pages,
+                             float topk_frac, int reserved_bos, int reserved_eos,
+                             int32_t* sel_idx, int32_t* sel_cnt, int k_cap,
+                             const int32_t* block_table, int64_t bt_ld, int32_t* sel_blk,
+                             hipStream_t stream) {
+  return topk_impl("page_topk_blk", scores, score_ld, B, H_sel, seq_lens, page_size,
+                   topk_pages, topk_frac, reserved_bos, reserved_eos, sel_idx, sel_cnt,
+                   k_cap, block_table, bt_ld, sel_blk, stream);
 }

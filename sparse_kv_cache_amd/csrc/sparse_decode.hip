@@ -956,18 +956,29 @@ int decode_impl(const char* who, const float* q, int B, int H_q, int H_kv, int D
 
 }  // namespace
 
-extern "C" int sparse_paged_decode(const float* q, int B, int H_q, int H_kv,
-                                   int D, const uint16_t* kv_cache,
-                                   int64_t num_blocks, int page_size,
-                                   const int32_t* block_table, int64_t bt_ld,
-                                   const int32_t* seq_lens,
-                                   const int32_t* sel_idx,
-                                   const int32_t* sel_cnt,
-                                   const int32_t* sel_blk, int k_cap,
-                                   int H_sel, float scale, int num_splits,
-                                   float* o_part, float* lse_part,
-                                   const float* alibi_slopes, hipStream_t stream) {
+extern "C" int sparse_paged_decode(const float* q, int B, int H_q, int H_kv, int D,
+                                   const uint16_t* kv_cache, int64_t num_blocks,
+                                   int page_size, const int32_t* block_table,
+                                   int64_t bt_ld, const int32_t* seq_lens,
+                                   const int32_t* sel_idx, const int32_t* sel_cnt,
+                                   int k_cap, int H_sel, float scale, int num_splits,
+                                   float* o_part, float* lse_part, hipStream_t stream) {
   return decode_impl("sparse_paged_decode", q, B, H_q, H_kv, D, kv_cache, num_blocks,
+                     page_size, block_table, bt_ld, seq_lens, sel_idx, sel_cnt, nullptr,
+                     k_cap, H_sel, scale, num_splits, o_part, lse_part, nullptr, nullptr,
+                     nullptr, stream);
+}
+
+extern "C" int sparse_paged_decode_ex(const float* q, int B, int H_q, int H_kv, int D,
+                                      const uint16_t* kv_cache, int64_t num_blocks,
+                                      int page_size, const int32_t* block_table,
+                                      int64_t bt_ld, const int32_t* seq_lens,
+                                      const int32_t* sel_idx, const int32_t* sel_cnt,
+                                      const int32_t* sel_blk, int k_cap, int H_sel,
+                                      float scale, int num_splits, float* o_part,
+                                      float* lse_part, const float* alibi_slopes,
+                                      hipStream_t stream) {
+  return decode_impl("sparse_paged_decode_ex", q, B, H_q, H_kv, D, kv_cache, num_blocks,
                      page_size, block_table, bt_ld, seq_lens, sel_idx, sel_cnt, sel_blk,
                      k_cap, H_sel, scale, num_splits, o_part, lse_part, alibi_slopes,
                      nullptr, nullptr, stream);

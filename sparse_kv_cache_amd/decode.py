@@ -35,10 +35,10 @@ import torch
 from . import (entmax15_paged_decode, entmax15_paged_decode_merged, entmax_scratch_floats,
                gauss_moments, gauss_select,
                h2o_accumulate, h2o_accumulate_heads, h2o_heads_scratch_floats,
-               h2o_scratch_floats, lse_merge, page_score,
-               page_score_group, page_topk, page_var_update, pagestats_update,
-               sparse_page_decode, sparse_paged_decode, sparse_paged_decode_merged,
-               sparse_select_decode)
+               h2o_scratch_floats, lse_merge, page_score, page_score_ex,
+               page_score_group, page_topk, page_topk_blk, page_var_update,
+               pagestats_update, sparse_page_decode, sparse_paged_decode,
+               sparse_paged_decode_ex, sparse_paged_decode_merged, sparse_select_decode)
 
 
 def alibi_slopes(H, device="cuda"):
@@ -271,10 +271,14 @@ class SparseDecoder:
     def score(self, q, block_table, seq_lens, stream=None):
         if self.token_level:
             raise RuntimeError("token-level scores come from h2o_accumulate")
-        fn = page_score_group if self.group_select else page_score
-        fn(q, self.k_min, self.k_max, self.k_mean, block_table, seq_lens,
-           self.P, self.w_avg, self.w_peak, self.scores, alibi=self.alibi_score,
-           stream=stream)
+        args = (q, self.k_min, self.k_max, self.k_mean, block_table, seq_lens, self.P,
+                self.w_avg, self.w_peak, self.scores)
+        if self.group_select:
+            page_score_group(*args, alibi=self.alibi_score, stream=stream)
+        elif self.alibi_score is not None:
+            page_score_ex(*args, alibi=self.alibi_score, stream=stream)
+        else:
+            page_score(*args, stream=stream)
 
     def accumulate(self, q, kv_cache, block_table, seq_lens, stream=None):
         fn = h2o_accumulate_heads if self.h2o_per_head else h2o_accumulate
@@ -283,10 +287,13 @@ class SparseDecoder:
                        stream=stream)
 
     def select(self, seq_lens, block_table=None, stream=None):
-        blk = self.sel_blk if (self.use_sel_blk and block_table is not None) else None
-        page_topk(self.scores, seq_lens, self.P, self.topk_pages, self.sel_idx,
-                  self.sel_cnt, self.topk_frac, self.bos, self.eos,
-                  block_table=block_table, sel_blk=blk, stream=stream)
+        if self.use_sel_blk and block_table is not None:
+            page_topk_blk(self.scores, seq_lens, self.P, self.topk_pages, self.sel_idx,
+                          self.sel_cnt, block_table, self.sel_blk, self.topk_frac,
+                          self.bos, self.eos, stream=stream)
+        else:
+            page_topk(self.scores, seq_lens, self.P, self.topk_pages, self.sel_idx,
+                      self.sel_cnt, self.topk_frac, self.bos, self.eos, stream=stream)
 
     def attend(self, q, kv_cache, block_table, seq_lens, stream=None):
         if self.attention == "entmax15" and self.entmax_fused:
@@ -312,10 +319,15 @@ class SparseDecoder:
                 lse_part=parts[1], sel_blk=self.sel_blk if self.use_sel_blk else None,
                 alibi_slopes=self.alibi, stream=stream)
             return
-        sparse_paged_decode(q, kv_cache, block_table, seq_lens, self.sel_idx,
-                            self.sel_cnt, self.scale, self.o_part, self.lse_part,
-                            sel_blk=self.sel_blk if self.use_sel_blk else None,
-                            alibi_slopes=self.alibi, stream=stream)
+        if self.use_sel_blk or self.alibi is not None:
+            sparse_paged_decode_ex(q, kv_cache, block_table, seq_lens, self.sel_idx,
+                                   self.sel_cnt, self.scale, self.o_part, self.lse_part,
+                                   sel_blk=self.sel_blk if self.use_sel_blk else None,
+                                   alibi_slopes=self.alibi, stream=stream)
+        else:
+            sparse_paged_decode(q, kv_cache, block_table, seq_lens, self.sel_idx,
+                                self.sel_cnt, self.scale, self.o_part, self.lse_part,
+                                stream=stream)
 
     def select_attend(self, q, kv_cache, block_table, seq_lens, stream=None):
         """Selection, decode and merge in one launch (select_in_decode)."""

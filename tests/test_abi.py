@@ -2,6 +2,9 @@
 
 * libsparsekv.so loads and exports every function ``include/sparsekv.h``
   declares;
+* the header declares the seven contract entry points of
+  ``tests/golden/abi_contract.h`` token for token (extensions sit in
+  separately named entry points);
 * argument validation rejects bad scalars (-EINVAL) and NULL pointers
   (-EFAULT) before anything is enqueued, with a message;
 * the scratch-size query of the token-level step;
@@ -37,10 +40,55 @@ def lib():
     return skv.load_library()
 
 
-def test_header_declares_the_six_operations():
+CONTRACT = os.path.join(ROOT, "tests", "golden", "abi_contract.h")
+
+
+def _tokens(text):
+    return re.findall(r"[A-Za-z_0-9]+|[^\sA-Za-z_0-9]", text)
+
+
+def _prototypes(path):
+    """name -> token list of each top-level prototype (comments removed)."""
+    text = re.sub(r"/\*.*?\*/", " ", open(path).read(), flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = re.sub(r"^\s*#[^\n]*", " ", text, flags=re.M)
+    out = {}
+    for m in re.finditer(r"(?:const\s+)?[A-Za-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\([^;{]*\)\s*;",
+                         text):
+        out[m.group(1)] = _tokens(m.group(0))
+    return out
+
+
+def test_header_matches_the_contract_token_by_token():
+    want = _prototypes(CONTRACT)
+    assert set(want) == {"pagestats_update", "page_score", "page_topk",
+                         "sparse_paged_decode", "lse_merge", "h2o_accumulate",
+                         "h2o_scratch_floats"}
+    have = _prototypes(HEADER)
+    for name, toks in want.items():
+        assert name in have, name
+        assert have[name] == toks, (name, have[name], toks)
+
+
+def test_contract_comparison_catches_drift(tmp_path):
+    """The comparison fails for an inserted argument, a renamed one and a
+    swapped pair."""
+    base = open(CONTRACT).read()
+    for old, new in (("float* scores, int64_t score_ld, hipStream_t stream",
+                      "float* scores, int64_t score_ld, const float* alibi, hipStream_t stream"),
+                     ("int k_cap, hipStream_t stream", "int cap, hipStream_t stream"),
+                     ("float w_avg, float w_peak", "float w_peak, float w_avg")):
+        assert old in base
+        bad = tmp_path / "bad.h"
+        bad.write_text(base.replace(old, new, 1))
+        assert _prototypes(str(bad)) != _prototypes(CONTRACT)
+
+
+def test_header_declares_every_operation():
     names = _declared()
-    for n in ("pagestats_update", "page_score", "page_score_group", "page_topk",
-              "sparse_paged_decode", "sparse_paged_decode_merged",
+    for n in ("pagestats_update", "page_score", "page_score_ex", "page_score_group",
+              "page_topk", "page_topk_blk", "sparse_paged_decode", "sparse_paged_decode_ex",
+              "sparse_paged_decode_merged",
               "entmax15_paged_decode", "entmax_scratch_floats", "sparse_select_decode",
               "sparse_page_decode", "page_var_update", "gauss_moments", "gauss_select",
               "entmax15_paged_decode_merged",
@@ -72,14 +120,18 @@ def test_validation_rejects_bad_scalars(lib):
                                 None, s) == EINVAL
     assert "D must be" in _msg(lib)
     # page_size 3 unsupported
-    assert lib.page_score(p, 1, 4, 2, 64, p, p, p, p, 4, p, 3, 1.0, 1.0, p, 4,
-                          None, s) == EINVAL
+    assert lib.page_score(p, 1, 4, 2, 64, p, p, p, p, 4, p, 3, 1.0, 1.0, p, 4, s) == EINVAL
     # H_q not a multiple of H_kv
-    assert lib.page_score(p, 1, 5, 2, 64, p, p, p, p, 4, p, 16, 1.0, 1.0, p, 4,
-                          None, s) == EINVAL
+    assert lib.page_score(p, 1, 5, 2, 64, p, p, p, p, 4, p, 16, 1.0, 1.0, p, 4, s) == EINVAL
     # score_ld < bt_ld
-    assert lib.page_score(p, 1, 4, 2, 64, p, p, p, p, 8, p, 16, 1.0, 1.0, p, 4,
-                          None, s) == EINVAL
+    assert lib.page_score(p, 1, 4, 2, 64, p, p, p, p, 8, p, 16, 1.0, 1.0, p, 4, s) == EINVAL
+    assert "page_score" in _msg(lib)
+    # the ALiBi form validates like page_score and names itself
+    assert lib.page_score_ex(p, 1, 4, 2, 64, p, p, p, p, 8, p, 16, 1.0, 1.0, p, 4,
+                             None, s) == EINVAL
+    assert "page_score_ex" in _msg(lib)
+    assert lib.page_score_ex(None, 1, 4, 2, 64, p, p, p, p, 4, p, 16, 1.0, 1.0, p, 4,
+                             p, s) == EFAULT
     # the group score validates like page_score
     assert lib.page_score_group(p, 1, 4, 2, 96, p, p, p, p, 4, p, 16, 1.0, 1.0, p, 4,
                                 None, s) == EINVAL
@@ -90,18 +142,25 @@ def test_validation_rejects_bad_scalars(lib):
                                 None, s) == EFAULT
     assert "page_score_group" in _msg(lib)
     # topk < 1, k_cap too small, score_ld too long
-    assert lib.page_topk(p, 64, 1, 4, p, 16, 0, 0.0, 0, 1, p, p, 8, None, 0, None, s) == EINVAL
-    assert lib.page_topk(p, 64, 1, 4, p, 16, 9, 0.0, 0, 1, p, p, 8, None, 0, None, s) == EINVAL
+    assert lib.page_topk(p, 64, 1, 4, p, 16, 0, 0.0, 0, 1, p, p, 8, s) == EINVAL
+    assert lib.page_topk(p, 64, 1, 4, p, 16, 9, 0.0, 0, 1, p, p, 8, s) == EINVAL
     assert "k_cap" in _msg(lib)
-    assert lib.page_topk(p, 64, 1, 4, p, 16, 4, 0.5, 0, 1, p, p, 8, None, 0, None, s) == EINVAL
-    assert lib.page_topk(p, 40000, 1, 4, p, 16, 4, 0.0, 0, 1, p, p, 8, None, 0, None, s) == EINVAL
+    assert lib.page_topk(p, 64, 1, 4, p, 16, 4, 0.5, 0, 1, p, p, 8, s) == EINVAL
+    assert lib.page_topk(p, 40000, 1, 4, p, 16, 4, 0.0, 0, 1, p, p, 8, s) == EINVAL
+    assert lib.page_topk_blk(p, 40000, 1, 4, p, 16, 4, 0.0, 0, 1, p, p, 8, None, 0, None,
+                             s) == EINVAL
+    assert "page_topk_blk" in _msg(lib)
     # sel_blk needs the block table
-    assert lib.page_topk(p, 64, 1, 4, p, 16, 4, 0.0, 0, 1, p, p, 8, None, 4, p, s) == EFAULT
+    assert lib.page_topk_blk(p, 64, 1, 4, p, 16, 4, 0.0, 0, 1, p, p, 8, None, 4, p,
+                             s) == EFAULT
     # H_sel neither H_q nor H_kv; splits < 1
-    assert lib.sparse_paged_decode(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p, None, 4,
-                                   3, 0.1, 2, p, p, None, s) == EINVAL
-    assert lib.sparse_paged_decode(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p, None, 4,
-                                   8, 0.1, 0, p, p, None, s) == EINVAL
+    assert lib.sparse_paged_decode(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p, 4,
+                                   3, 0.1, 2, p, p, s) == EINVAL
+    assert lib.sparse_paged_decode(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p, 4,
+                                   8, 0.1, 0, p, p, s) == EINVAL
+    assert lib.sparse_paged_decode_ex(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p, None, 4,
+                                      3, 0.1, 2, p, p, None, s) == EINVAL
+    assert "sparse_paged_decode_ex" in _msg(lib)
     # merged decode: at most 8 splits; out required; partials both or neither
     assert lib.sparse_paged_decode_merged(p, 1, 8, 2, 128, p, 8, 16, p, 4, p, p, p, None,
                                           4, 0.1, 9, None, None, None, p, None, s) == EINVAL
@@ -192,9 +251,14 @@ def test_validation_rejects_null_pointers(lib):
     s = ctypes.c_void_p(0)
     assert lib.lse_merge(None, p, 4, 2, 128, p, None, s) == EFAULT
     assert "o_part" in _msg(lib)
-    assert lib.page_topk(p, 64, 1, 4, p, 16, 4, 0.0, 0, 1, None, p, 8, None, 0, None, s) == EFAULT
-    assert lib.sparse_paged_decode(p, 1, 8, 2, 128, None, 8, 16, p, 4, p, p, p, None,
-                                   4, 8, 0.1, 2, p, p, None, s) == EFAULT
+    assert lib.page_topk(p, 64, 1, 4, p, 16, 4, 0.0, 0, 1, None, p, 8, s) == EFAULT
+    assert lib.page_topk_blk(p, 64, 1, 4, p, 16, 4, 0.0, 0, 1, None, p, 8, None, 0, None,
+                             s) == EFAULT
+    assert lib.sparse_paged_decode(p, 1, 8, 2, 128, None, 8, 16, p, 4, p, p, p,
+                                   4, 8, 0.1, 2, p, p, s) == EFAULT
+    assert "kv_cache" in _msg(lib)
+    assert lib.sparse_paged_decode_ex(p, 1, 8, 2, 128, None, 8, 16, p, 4, p, p, p, None,
+                                      4, 8, 0.1, 2, p, p, None, s) == EFAULT
     assert lib.pagestats_update(None, 8, 16, 2, 64, p, p, p, p, 4, p, 1, None,
                                 None, None, s) == EFAULT
     # statistics buffers must be all given or all NULL

@@ -23,9 +23,10 @@ from parity import (bits, bf16_bits_apart, check_attention, check_partials,
 pytestmark = pytest.mark.gpu
 
 
-def page_level_parity(wl, cache, q_cpu, seq_lens_np, rows, d, partial_heads=4):
+def page_level_parity(wl, cache, q_cpu, seq_lens_np, rows, d, partial_heads=4,
+                      with_blk=True):
     """Compare decoder d's buffers (already computed for the whole batch) with
-    the oracle on requests ``rows``."""
+    the oracle on requests ``rows``; with_blk: d.sel_blk was written too."""
     cb, bt, sl, blocks, (gmin, gmax, gmean) = sub_batch(
         wl, cache, rows, seq_lens_np, extra=(d.k_min, d.k_max, d.k_mean))
     qd = q_cpu.double().numpy()[rows]
@@ -43,8 +44,9 @@ def page_level_parity(wl, cache, q_cpu, seq_lens_np, rows, d, partial_heads=4):
     sel_cnt = d.sel_cnt.cpu().numpy()[rows].reshape(-1)
     check_selection_exact(sel_idx, sel_cnt, gs.reshape(-1, wl.bt_ld), rowsN,
                           wl.topk_pages, wl.topk_frac, wl.bos, wl.eos)
-    check_sel_blk(d.sel_blk.cpu().numpy()[rows], d.sel_idx.cpu().numpy()[rows],
-                  wl.block_table[list(rows)])
+    if with_blk:
+        check_sel_blk(d.sel_blk.cpu().numpy()[rows], d.sel_idx.cpu().numpy()[rows],
+                      wl.block_table[list(rows)])
     ref_scores = (oracle.page_score_group if group else oracle.page_score)(
         qd, *st, bt, sl, wl.P, wl.w_avg, wl.w_peak)
     sel_rows = selection_rows(sel_idx, sel_cnt)
@@ -82,6 +84,35 @@ def _static_workload(name, group_select=False):
 
 def test_mha_tiny():
     _static_workload("mha_tiny")
+
+
+def test_gqa_ragged_contract_forms():
+    """One gqa_ragged step through the seven-call contract's forms only:
+    pagestats_update (rebuild), page_score, page_topk, sparse_paged_decode and
+    lse_merge, each called with exactly its contract arguments (no block-id
+    or ALiBi extension); the decoder object only holds the buffers."""
+    import sparse_kv_cache_amd as skv
+    wl = W.gqa_ragged()
+    say("[gpu] workload gqa_ragged through the contract entry points: generating")
+    cache = W.make_cache(wl, device="cuda")
+    q_cpu = W.make_queries(wl)
+    d = SparseDecoder.for_workload(wl, fuse_merge=False)
+    assert d.H_sel == wl.H_q and not d.select_in_decode
+    bt, sl, q = dev(wl.block_table), dev(wl.seq_lens), dev(q_cpu)
+    poison(d)
+    skv.pagestats_update(cache, d.k_min, d.k_max, d.k_mean, bt, sl)
+    skv.page_score(q, d.k_min, d.k_max, d.k_mean, bt, sl, wl.P, wl.w_avg, wl.w_peak,
+                   d.scores)
+    skv.page_topk(d.scores, sl, wl.P, wl.topk_pages, d.sel_idx, d.sel_cnt, wl.topk_frac,
+                  wl.bos, wl.eos)
+    skv.sparse_paged_decode(q, cache, bt, sl, d.sel_idx, d.sel_cnt, wl.softmax_scale,
+                            d.o_part, d.lse_part)
+    skv.lse_merge(d.o_part, d.lse_part, d.out, d.lse)
+    torch.cuda.synchronize()
+    say("[gpu] workload gqa_ragged (contract forms): checking")
+    worst, ex = page_level_parity(wl, cache, q_cpu, wl.seq_lens, range(wl.B), d,
+                                  with_blk=False)
+    say(f"  gqa_ragged contract forms: max |out - oracle| {worst:.2e}, near-tie rows {ex}")
 
 
 def test_gqa_ragged():
