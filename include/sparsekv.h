@@ -503,6 +503,36 @@ int h2o_accumulate(const float *q, int B, int H_q, int H_kv, int D,
 int64_t h2o_scratch_floats(int B, int H_kv, int64_t max_tokens);
 
 /*
+ * h2o_accumulate_noalloc -- h2o_accumulate for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same step, the same kernels and the same result,
+ * with the scratch taken from a fixed buffer inside the library instead of a
+ * caller argument.  The call itself allocates and frees nothing.
+ *
+ *   Arguments, layouts and errors as h2o_accumulate, without scratch and
+ *   scratch_floats.  Additionally
+ *     - h2o_scratch_floats(B, H_kv, bt_ld) must not exceed
+ *       SKV_NOALLOC_SCRATCH_FLOATS (SKV_EINVAL otherwise);
+ *     - stream must belong to the current device (SKV_EINVAL otherwise);
+ *       NULL is the current device's null stream.
+ *   The buffer is a device array of SKV_NOALLOC_SCRATCH_FLOATS floats (8 MiB)
+ *   that each GPU the library runs on holds until the process ends; its
+ *   address is looked up once per device, on the first call there.  Every
+ *   call on one GPU uses that GPU's single buffer: calls whose work overlaps
+ *   on one GPU (other streams, other threads) race and must be serialised by
+ *   the caller.  Nothing in the buffer needs to start at zero: each call
+ *   writes what it reads.
+ */
+#define SKV_NOALLOC_SCRATCH_FLOATS (2 * 1024 * 1024)
+int h2o_accumulate_noalloc(const float *q, int B, int H_q, int H_kv, int D,
+                           const uint16_t *kv_cache, int64_t num_blocks,
+                           int page_size, const int32_t *block_table,
+                           int64_t bt_ld, const int32_t *seq_lens,
+                           int reserved_bos, int reserved_eos, float scale,
+                           float decay, uint16_t *hh_score, float *scores,
+                           int64_t score_ld, hipStream_t stream);
+
+/*
  * h2o_accumulate_heads -- the same step with the query-group axis kept through
  * the softmax.  [VTX description: the GQA variants compute the product and
  * the softmax over the query-group axis; VTX "Token-level variants" for the

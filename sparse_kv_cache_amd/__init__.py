@@ -21,7 +21,8 @@ __all__ = [
     "page_topk_blk", "sparse_paged_decode", "sparse_paged_decode_ex",
     "sparse_paged_decode_merged", "lse_merge",
     "h2o_accumulate", "h2o_scratch_floats", "h2o_accumulate_heads",
-    "h2o_heads_scratch_floats", "entmax15_paged_decode",
+    "h2o_heads_scratch_floats", "h2o_accumulate_noalloc", "NOALLOC_SCRATCH_FLOATS",
+    "entmax15_paged_decode",
     "entmax_scratch_floats", "sparse_select_decode", "sparse_page_decode",
     "page_var_update", "gauss_moments", "gauss_select", "entmax15_paged_decode_merged",
     "library_path",
@@ -37,15 +38,18 @@ EXPORTED_SYMBOLS = (
     "page_topk_blk", "sparse_paged_decode", "sparse_paged_decode_ex",
     "sparse_paged_decode_merged", "lse_merge",
     "h2o_accumulate", "h2o_scratch_floats", "h2o_accumulate_heads",
-    "h2o_heads_scratch_floats", "entmax15_paged_decode",
+    "h2o_heads_scratch_floats", "h2o_accumulate_noalloc", "entmax15_paged_decode",
     "entmax_scratch_floats", "sparse_select_decode", "sparse_page_decode",
     "page_var_update", "gauss_moments", "gauss_select", "entmax15_paged_decode_merged",
     "sparsekv_last_error",
 )
+# size of the fixed scratch of h2o_accumulate_noalloc (SKV_NOALLOC_SCRATCH_FLOATS)
+NOALLOC_SCRATCH_FLOATS = 2 * 1024 * 1024
 _INT_RETURNING = ("pagestats_update", "page_score", "page_score_ex", "page_score_group",
                   "page_topk", "page_topk_blk", "sparse_paged_decode",
                   "sparse_paged_decode_ex", "sparse_paged_decode_merged", "lse_merge",
-                  "h2o_accumulate", "h2o_accumulate_heads", "entmax15_paged_decode",
+                  "h2o_accumulate", "h2o_accumulate_heads", "h2o_accumulate_noalloc",
+                  "entmax15_paged_decode",
                   "sparse_select_decode",
                   "sparse_page_decode", "page_var_update", "gauss_moments", "gauss_select",
                   "entmax15_paged_decode_merged")
@@ -94,6 +98,8 @@ def load_library():
     lib.h2o_scratch_floats.argtypes = [I, I, L]
     lib.h2o_scratch_floats.restype = ctypes.c_int64
     lib.h2o_accumulate_heads.argtypes = lib.h2o_accumulate.argtypes
+    lib.h2o_accumulate_noalloc.argtypes = [V, I, I, I, I, V, L, I, V, L, V, I, I, F, F, V, V,
+                                           L, V]
     lib.h2o_heads_scratch_floats.argtypes = [I, I, L]
     lib.h2o_heads_scratch_floats.restype = ctypes.c_int64
     lib.entmax15_paged_decode.argtypes = [V, I, I, I, I, V, L, I, V, L, V, V, V, V, I, I,
@@ -721,3 +727,32 @@ def h2o_accumulate_heads(q, kv_cache, block_table, seq_lens, hh_score, scores, s
     group; scratch of h2o_heads_scratch_floats(B, H_q, bt_ld) floats."""
     _h2o("h2o_accumulate_heads", q, kv_cache, block_table, seq_lens, hh_score, scores,
          scratch, scale, decay, reserved_bos, reserved_eos, stream)
+
+
+def h2o_accumulate_noalloc(q, kv_cache, block_table, seq_lens, hh_score, scores, scale,
+                           decay=0.984375, reserved_bos=0, reserved_eos=1, stream=None):
+    """h2o_accumulate with the library's fixed scratch buffer: no device memory
+    is allocated by the call (nor by this wrapper).  Needs
+    h2o_scratch_floats(B, H_kv, bt_ld) <= NOALLOC_SCRATCH_FLOATS; calls that
+    overlap on one GPU share that buffer and race."""
+    lib = load_library()
+    _check("q", q, torch.float32, 3)
+    dev = q.device
+    B, H_q, D = q.shape
+    NB, P, H_kv = _cache(kv_cache, D, dev)
+    _check("block_table", block_table, torch.int32, 2, dev)
+    _check("seq_lens", seq_lens, torch.int32, 1, dev)
+    _batch(B, block_table, seq_lens)
+    for n, t in (("hh_score", hh_score), ("scores", scores)):
+        if t is None:
+            raise ValueError(f"{n} is required")
+    _check("hh_score", hh_score, torch.bfloat16, 2, dev)
+    _check("scores", scores, torch.float32, 3, dev)
+    _shape("hh_score", hh_score, (NB * P, H_kv))
+    if tuple(scores.shape[:2]) != (B, H_kv):
+        raise ValueError("scores must be [B, H_kv, score_ld]")
+    _rc("h2o_accumulate_noalloc", lib.h2o_accumulate_noalloc(
+        _ptr(q), B, H_q, H_kv, D, _ptr(kv_cache), NB, P, _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), int(reserved_bos), int(reserved_eos),
+        float(scale), float(decay), _ptr(hh_score), _ptr(scores), scores.shape[2],
+        _stream(stream)))

@@ -24,6 +24,8 @@
 //      score row in logical order for the selection.
 // Scratch layout: logits [B, R, bt_ld] then partials [B, R, nchunk, 2], with
 // R = H_kv logit rows per request (group mean) or H_q (per head).
+#include <mutex>
+
 #include "skv_device.h"
 #include "skv_host.h"
 
@@ -487,6 +489,52 @@ int accumulate(const char* fn, const float* q, int B, int H_q, int H_kv, int D,
   return SKV_OK;
 }
 
+// ------------------------------------------------- no-allocation form
+// The scratch of h2o_accumulate_noalloc: a fixed array in device memory.
+// Every GPU the library runs on holds its own copy, at its own address, until
+// the process ends.  In host code the array's name is only a host-side
+// stand-in: kernels get the device address fetched once per device.
+static __device__ __align__(256) float g_noalloc_scratch[SKV_NOALLOC_SCRATCH_FLOATS];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_noalloc_mu;
+float* g_noalloc_ptr[kMaxDevices] = {};
+
+// Device address of this device's copy of the array, fetched on the first
+// call that runs on the device (with the device current) and kept.
+int noalloc_scratch(const char* fn, hipStream_t stream, float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    skv::set_error("%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+    return SKV_EIO;
+  }
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) {
+      skv::set_error("%s: hipStreamGetDevice failed: %s", fn, hipGetErrorString(e));
+      return SKV_EIO;
+    }
+    SKV_REQUIRE(sdev == dev, "%s: the stream belongs to device %d, the current device is %d",
+                fn, static_cast<int>(sdev), dev);
+  }
+  SKV_REQUIRE(dev >= 0 && dev < kMaxDevices, "%s: device %d beyond %d", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (g_noalloc_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_noalloc_scratch));
+    if (e != hipSuccess || p == nullptr) {
+      skv::set_error("%s: hipGetSymbolAddress failed on device %d: %s", fn, dev,
+                     hipGetErrorString(e));
+      return SKV_EIO;
+    }
+    g_noalloc_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_noalloc_ptr[dev];
+  return SKV_OK;
+}
+
 }  // namespace
 
 extern "C" int64_t h2o_scratch_floats(int B, int H_kv, int64_t max_tokens) {
@@ -523,4 +571,35 @@ extern "C" int h2o_accumulate_heads(const float* q, int B, int H_q, int H_kv, in
                           page_size, block_table, bt_ld, seq_lens, reserved_bos,
                           reserved_eos, scale, decay, hh_score, scores, score_ld, scratch,
                           scratch_floats, stream);
+}
+
+extern "C" int h2o_accumulate_noalloc(const float* q, int B, int H_q, int H_kv, int D,
+                                      const uint16_t* kv_cache, int64_t num_blocks,
+                                      int page_size, const int32_t* block_table,
+                                      int64_t bt_ld, const int32_t* seq_lens,
+                                      int reserved_bos, int reserved_eos, float scale,
+                                      float decay, uint16_t* hh_score, float* scores,
+                                      int64_t score_ld, hipStream_t stream) {
+  const char* fn = "h2o_accumulate_noalloc";
+  SKV_REQUIRE(B >= 0 && H_kv > 0 && bt_ld > 0, "%s: need B >= 0, H_kv > 0, bt_ld > 0", fn);
+  const int64_t need = scratch_floats(B, H_kv, bt_ld);
+  SKV_REQUIRE(need <= SKV_NOALLOC_SCRATCH_FLOATS,
+              "%s: the step needs %lld scratch floats, the fixed buffer holds %lld "
+              "(use h2o_accumulate with a caller buffer)", fn, (long long)need,
+              (long long)SKV_NOALLOC_SCRATCH_FLOATS);
+  float* scratch = nullptr;
+  if (B > 0) {
+    // (scalar checks first, so that a bad argument is reported as such)
+    const int rc = accumulate<false>(fn, q, 0, H_q, H_kv, D, kv_cache, num_blocks,
+                                     page_size, block_table, bt_ld, seq_lens, reserved_bos,
+                                     reserved_eos, scale, decay, hh_score, scores, score_ld,
+                                     nullptr, 0, stream);
+    if (rc != SKV_OK) return rc;
+    const int rs = noalloc_scratch(fn, stream, &scratch);
+    if (rs != SKV_OK) return rs;
+  }
+  return accumulate<false>(fn, q, B, H_q, H_kv, D, kv_cache, num_blocks, page_size,
+                           block_table, bt_ld, seq_lens, reserved_bos, reserved_eos, scale,
+                           decay, hh_score, scores, score_ld, scratch,
+                           SKV_NOALLOC_SCRATCH_FLOATS, stream);
 }

@@ -93,7 +93,7 @@ def test_header_declares_every_operation():
               "sparse_page_decode", "page_var_update", "gauss_moments", "gauss_select",
               "entmax15_paged_decode_merged",
               "lse_merge", "h2o_accumulate", "h2o_scratch_floats",
-              "h2o_accumulate_heads", "h2o_heads_scratch_floats",
+              "h2o_accumulate_heads", "h2o_heads_scratch_floats", "h2o_accumulate_noalloc",
               "sparsekv_last_error"):
         assert n in names
     assert set(names) == set(skv.EXPORTED_SYMBOLS)
@@ -276,6 +276,25 @@ def test_validation_rejects_null_pointers(lib):
     assert lib.gauss_select(p, p, 64, 1, 8, p, 16, p, 64, 1, 0, 1, 4, None, None, p, p,
                             None, s) == EFAULT
     assert "est" in _msg(lib)
+
+
+def test_noalloc_step_checks_its_fixed_buffer_first(lib):
+    """The no-allocation accumulator step refuses, before any HIP call, a step
+    whose scratch exceeds its fixed buffer; an empty batch is a no-op."""
+    p = ctypes.c_void_p(16)
+    s = ctypes.c_void_p(0)
+    ld = 262144
+    assert lib.h2o_scratch_floats(1, 8, ld) > skv.NOALLOC_SCRATCH_FLOATS
+    assert lib.h2o_accumulate_noalloc(p, 1, 32, 8, 128, p, 4, 1, p, ld, p, 0, 1, 0.1, 0.98,
+                                      p, p, ld, s) == EINVAL
+    assert "fixed buffer" in _msg(lib)
+    assert lib.h2o_accumulate_noalloc(p, 0, 32, 8, 128, p, 4, 1, p, 64, p, 0, 1, 0.1, 0.98,
+                                      None, None, 64, s) == 0
+    assert lib.h2o_accumulate_noalloc(p, 0, 32, 8, 128, p, 4, 16, p, 64, p, 0, 1, 0.1, 0.98,
+                                      None, None, 64, s) == EINVAL
+    hdr = open(HEADER).read()
+    assert re.search(r"#define SKV_NOALLOC_SCRATCH_FLOATS \(2 \* 1024 \* 1024\)", hdr)
+    assert skv.NOALLOC_SCRATCH_FLOATS == 2 * 1024 * 1024
 
 
 def test_scratch_size_query(lib):
