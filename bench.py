@@ -23,6 +23,15 @@ each kernel (algorithmic bytes / kernel time; each kernel is timed alone,
 launched back to back over the replicas in a graph, with HIP events on the
 launch stream), the roofline entry of the decode kernel, and the float64
 oracle timed on a bounded sample on the host cores (cpu_baseline).
+
+The roofline entry also places the decode kernel against two references of
+the library that carry no arithmetic, timed the same way in the same run:
+the streaming read of the kernel's byte count (stream_ref / stream_frac) and
+the gather-only read of the decode's own page-heads (gather_ref /
+gather_frac).  Unless --no-north-star (or --workload long_context), the line
+also carries a "north_star" record: the long-context workload's step rate and
+its decode kernel's time, bytes, fraction of peak, counter traffic and
+references.
 """
 from __future__ import annotations
 
@@ -66,6 +75,8 @@ def parse():
                     help="keep page_topk and lse_merge as their own launches even "
                          "where the decode can select and merge in-block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-north-star", action="store_true",
+                    help="skip the long_context sub-record that the default run adds")
     ap.add_argument("--no-graph", action="store_true",
                     help="enqueue kernel by kernel instead of replaying HIP graphs")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -328,6 +339,65 @@ def host_cpu():
 
 # -------------------------------------------------------------------- main
 
+def unique_page_heads(wl, sel_idx, sel_cnt, seq_lens, H_sel):
+    """int32 [n, 3] (block, kv head, valid rows) of every distinct (request,
+    kv head, page) the selection reads, in (request, kv head, page) order."""
+    out = []
+    for b in range(wl.B):
+        S = int(seq_lens[b])
+        for h in range(wl.H_kv):
+            rows = range(h * wl.G, (h + 1) * wl.G) if H_sel == wl.H_q else [h]
+            u = set()
+            for r in rows:
+                u.update(sel_idx[b, r, :sel_cnt[b, r]].tolist())
+            for p in sorted(u):
+                out.append((int(wl.block_table[b, p]), h, min(wl.P, S - p * wl.P)))
+    return np.asarray(out, dtype=np.int32).reshape(-1, 3)
+
+
+def reference_rates(torch, dev, nbytes, caches=None, items=None, reps=16):
+    """The library's bandwidth references, timed like the kernels (a graph of
+    back-to-back launches, HIP events around one replay): a streaming read of
+    nbytes at rotating offsets of a buffer 16x larger (so the memory-side cache
+    cannot serve it), and, given the decode's page-heads, the gather-only read
+    of exactly those rows rotating over the replica caches."""
+    import sparse_kv_cache_amd as skv
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    out = {}
+    n16 = max(16, int(nbytes) // 16 * 16)
+    pool = torch.empty(n16 * 16 + (1 << 20), dtype=torch.uint8, device=dev)
+    pool.fill_(3)
+    views = [pool[(i * n16) % (pool.numel() - n16):][:n16] for i in range(reps)]
+
+    def timed(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(reps):
+                fn(i)
+        g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms = timed(lambda i: skv.skv_ref_stream_read(views[i], sink))
+    out["stream"] = {"bytes": n16, "us": round(ms * 1000, 2),
+                     "GBps": round(n16 / (ms * 1e-3) / 1e9, 1)}
+    del pool, views
+    if caches is not None and items is not None and len(items):
+        it = torch.from_numpy(items).to(dev)
+        rows = int(items[:, 2].sum())
+        gbytes = rows * caches[0].shape[4] * 2 * 2
+        ms = timed(lambda i: skv.skv_ref_gather_read(caches[i % len(caches)], it, sink))
+        out["gather"] = {"bytes": gbytes, "page_heads": int(len(items)),
+                         "us": round(ms * 1000, 2),
+                         "GBps": round(gbytes / (ms * 1e-3) / 1e9, 1)}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -337,13 +407,42 @@ def main():
         return 2
     import torch
     import sparse_kv_cache_amd  # noqa: F401  (loads lazily; fails loudly if unbuilt)
-    from sparse_kv_cache_amd import workloads as W
-    from sparse_kv_cache_amd.decode import SparseDecoder, alibi_slopes
 
     sparse_kv_cache_amd.load_library()
     torch.cuda.init()
+    result = measure(args, args.workload, cpu=not args.no_cpu_baseline)
+    if args.workload != "long_context" and not args.no_north_star:
+        import copy
+        torch.cuda.empty_cache()
+        a2 = copy.copy(args)
+        a2.select, a2.alibi, a2.attention, a2.no_fuse, a2.splits = "head", False, "softmax", \
+            False, 0
+        a2.steps, a2.repeats = min(args.steps, 50), 0
+        ns = measure(a2, "long_context", cpu=False)
+        rf = ns["roofline"]
+        result["north_star"] = {
+            "workload": "long_context", "steps_per_s": ns["value"],
+            "gpu_ms_per_step": ns["gpu_ms_per_step"], "launches": len(ns["kernels"]),
+            "kernel": rf["kernel"], "us_per_launch": rf["us_per_launch"],
+            "bytes_per_launch": rf["bytes_per_launch"], "achieved_GBps": rf["achieved"],
+            "frac": rf["frac"], "traffic": rf["traffic"],
+            "traffic_ratio": (None if rf["traffic"] is None else
+                              round(rf["traffic"] / rf["bytes_per_launch"], 3)),
+            "stream_ref": rf.get("stream_ref"), "stream_frac": rf.get("stream_frac"),
+            "gather_ref": rf.get("gather_ref"), "gather_frac": rf.get("gather_frac"),
+            "kernels": ns["kernels"]}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def measure(args, workload, cpu=True):
+    """One workload's bench record (the dict printed as the JSON line)."""
+    import torch
+    from sparse_kv_cache_amd import workloads as W
+    from sparse_kv_cache_amd.decode import SparseDecoder, alibi_slopes
+
     dev = torch.device("cuda:0")
-    wl = W.WORKLOADS[args.workload]()
+    wl = W.WORKLOADS[workload]()
     token_level = wl.name == "h2o_token"
     if args.splits:
         wl.num_splits = args.splits
@@ -561,6 +660,18 @@ def main():
                 "copy_frac": round(a / copy_gbps, 4) if copy_gbps > 0 else None,
                 "bytes_per_launch": kb[focus],
                 "us_per_launch": round(per_kernel_ms[focus] * 1000, 2)}
+    # against the library's streaming read of the same byte count, and (page
+    # size 16) the gather-only read of the decode's own page-heads
+    items = None
+    if wl.P == 16 and not (entmax and not fused):
+        H_sel = wl.H_kv if (group or token_level) else wl.H_q
+        items = unique_page_heads(wl, sel_idx, sel_cnt, sl_last, H_sel)
+    refs = reference_rates(torch, dev, kb[focus], caches, items)
+    roofline["stream_ref"] = refs["stream"]
+    roofline["stream_frac"] = round(a / refs["stream"]["GBps"], 4)
+    if "gather" in refs:
+        roofline["gather_ref"] = refs["gather"]
+        roofline["gather_frac"] = round(a / refs["gather"]["GBps"], 4)
 
     result = {
         "metric": "sparse decode steps/s + effective HBM GB/s (% of peak), GQA 32/8 D=128",
@@ -602,7 +713,7 @@ def main():
                 "gpu": torch.cuda.get_device_name(0),
                 "host_cpu": host_cpu(), "host_threads": os.cpu_count()},
     }
-    if not args.no_cpu_baseline:
+    if cpu:
         from sparse_kv_cache_amd.workloads import bf16_bits
         cb = bf16_bits(caches[last % R])
         hb = bf16_bits(hh0) if token_level else None
@@ -610,8 +721,7 @@ def main():
             wl, cb, q.cpu(), sl_last, args.cpu_seconds, token_level, hb,
             gauss=gauss, slopes=None if slopes is None else slopes.cpu().numpy(),
             k_cap=decs[0].k_cap, h2o_per_head=decs[0].h2o_per_head)
-    print(json.dumps(result), flush=True)
-    return 0
+    return result
 
 
 if __name__ == "__main__":

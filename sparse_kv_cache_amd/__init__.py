@@ -25,7 +25,7 @@ __all__ = [
     "entmax15_paged_decode",
     "entmax_scratch_floats", "sparse_select_decode", "sparse_page_decode",
     "page_var_update", "gauss_moments", "gauss_select", "entmax15_paged_decode_merged",
-    "library_path",
+    "skv_ref_stream_read", "skv_ref_gather_read", "library_path",
     "load_library", "SparseKVError", "EXPORTED_SYMBOLS",
 ]
 
@@ -41,7 +41,7 @@ EXPORTED_SYMBOLS = (
     "h2o_heads_scratch_floats", "h2o_accumulate_noalloc", "entmax15_paged_decode",
     "entmax_scratch_floats", "sparse_select_decode", "sparse_page_decode",
     "page_var_update", "gauss_moments", "gauss_select", "entmax15_paged_decode_merged",
-    "sparsekv_last_error",
+    "skv_ref_stream_read", "skv_ref_gather_read", "sparsekv_last_error",
 )
 # size of the fixed scratch of h2o_accumulate_noalloc (SKV_NOALLOC_SCRATCH_FLOATS)
 NOALLOC_SCRATCH_FLOATS = 2 * 1024 * 1024
@@ -52,7 +52,8 @@ _INT_RETURNING = ("pagestats_update", "page_score", "page_score_ex", "page_score
                   "entmax15_paged_decode",
                   "sparse_select_decode",
                   "sparse_page_decode", "page_var_update", "gauss_moments", "gauss_select",
-                  "entmax15_paged_decode_merged")
+                  "entmax15_paged_decode_merged", "skv_ref_stream_read",
+                  "skv_ref_gather_read")
 
 
 class SparseKVError(RuntimeError):
@@ -115,6 +116,8 @@ def load_library():
     lib.sparse_page_decode.argtypes = [V, I, I, I, I, V, L, I, V, V, V, V, L, V, F, F, I, F,
                                        I, I, I, F, I, V, V, V, V, V, V, V, V]
     lib.entmax_scratch_floats.restype = ctypes.c_int64
+    lib.skv_ref_stream_read.argtypes = [V, L, V, V]
+    lib.skv_ref_gather_read.argtypes = [V, L, I, I, I, V, L, V, V]
     for name in _INT_RETURNING:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -755,4 +758,40 @@ def h2o_accumulate_noalloc(q, kv_cache, block_table, seq_lens, hh_score, scores,
         _ptr(q), B, H_q, H_kv, D, _ptr(kv_cache), NB, P, _ptr(block_table),
         block_table.shape[1], _ptr(seq_lens), int(reserved_bos), int(reserved_eos),
         float(scale), float(decay), _ptr(hh_score), _ptr(scores), scores.shape[2],
+        _stream(stream)))
+
+
+# ------------------------------------------------------ bandwidth references
+
+def skv_ref_stream_read(buf, sink, nbytes=None, stream=None):
+    """Read nbytes (default: all) of the device tensor buf once, streaming
+    (skv_reference.h); sink is a uint32-sized device buffer of >= 1024 words."""
+    lib = load_library()
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    _check("sink", sink, torch.int32, 1, buf.device)
+    if sink.numel() < 1024:
+        raise ValueError("sink must hold 1024 words")
+    n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    if n > buf.numel() * buf.element_size():
+        raise ValueError("nbytes exceeds the buffer")
+    _rc("skv_ref_stream_read", lib.skv_ref_stream_read(_ptr(buf), n, _ptr(sink),
+                                                       _stream(stream)))
+
+
+def skv_ref_gather_read(kv_cache, items, sink, stream=None):
+    """Read the K and V rows of the page-heads items [n, 3] = (block, kv head,
+    valid rows) of kv_cache (skv_reference.h); sink >= 256 words."""
+    lib = load_library()
+    _check("kv_cache", kv_cache, torch.bfloat16, 5)
+    dev = kv_cache.device
+    _, NB, P, H_kv, D = kv_cache.shape
+    _check("items", items, torch.int32, 2, dev)
+    if items.shape[1] != 3:
+        raise ValueError("items must be [n, 3]")
+    _check("sink", sink, torch.int32, 1, dev)
+    if sink.numel() < 256:
+        raise ValueError("sink must hold 256 words")
+    _rc("skv_ref_gather_read", lib.skv_ref_gather_read(
+        _ptr(kv_cache), NB, P, H_kv, D, _ptr(items), items.shape[0], _ptr(sink),
         _stream(stream)))

@@ -19,6 +19,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sparsekv.h")
+REF_HEADER = os.path.join(ROOT, "include", "skv_reference.h")
 
 import sparse_kv_cache_amd as skv  # noqa: E402
 
@@ -26,10 +27,12 @@ EINVAL, EFAULT = -22, -14
 
 
 def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z0-9_]+\s*\*?\s*([a-z_0-9]+)\s*\(",
-                                 text, flags=re.M)))
+    names = set()
+    for h in (HEADER, REF_HEADER):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"^\s*(?:const\s+)?[a-z0-9_]+\s*\*?\s*([a-z_0-9]+)\s*\(",
+                                text, flags=re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -94,7 +97,7 @@ def test_header_declares_every_operation():
               "entmax15_paged_decode_merged",
               "lse_merge", "h2o_accumulate", "h2o_scratch_floats",
               "h2o_accumulate_heads", "h2o_heads_scratch_floats", "h2o_accumulate_noalloc",
-              "sparsekv_last_error"):
+              "skv_ref_stream_read", "skv_ref_gather_read", "sparsekv_last_error"):
         assert n in names
     assert set(names) == set(skv.EXPORTED_SYMBOLS)
 
@@ -295,6 +298,19 @@ def test_noalloc_step_checks_its_fixed_buffer_first(lib):
     hdr = open(HEADER).read()
     assert re.search(r"#define SKV_NOALLOC_SCRATCH_FLOATS \(2 \* 1024 \* 1024\)", hdr)
     assert skv.NOALLOC_SCRATCH_FLOATS == 2 * 1024 * 1024
+
+
+def test_bandwidth_references_validate(lib):
+    p = ctypes.c_void_p(16)
+    s = ctypes.c_void_p(0)
+    assert lib.skv_ref_stream_read(p, 17, p, s) == EINVAL
+    assert lib.skv_ref_stream_read(p, 0, p, s) == EINVAL
+    assert lib.skv_ref_stream_read(None, 32, p, s) == EFAULT
+    assert lib.skv_ref_stream_read(ctypes.c_void_p(24), 32, p, s) == EINVAL
+    assert lib.skv_ref_gather_read(p, 8, 4, 8, 128, p, 4, p, s) == EINVAL
+    assert lib.skv_ref_gather_read(p, 8, 16, 8, 96, p, 4, p, s) == EINVAL
+    assert lib.skv_ref_gather_read(p, 8, 16, 8, 128, None, 4, p, s) == EFAULT
+    assert lib.skv_ref_gather_read(p, 8, 16, 8, 128, None, 0, None, s) == 0
 
 
 def test_scratch_size_query(lib):
