@@ -469,6 +469,8 @@ def measure(args, workload, cpu=True):
             for _ in range(R)]
     fused = decs[0].fused or decs[0].entmax_fused
     in_decode = decs[0].select_in_decode
+    in_group_decode = decs[0].select_in_group_decode and not gauss and not token_level
+    token_fused = decs[0].token_fused
     one_launch = decs[0].score_in_decode
     new_kv = [W.make_new_kv(wl, s, device=dev) for s in range(min(wl.steps, 64))] \
         if wl.steps > 1 else None
@@ -512,9 +514,11 @@ def measure(args, workload, cpu=True):
             ([] if fused else ["lse_merge"])
     else:
         names = (["pagestats_update"] if wl.steps > 1 else []) + \
-            (["h2o_accumulate"] if token_level else [] if one_launch else ["page_score"]) + \
+            (["h2o_select_decode", "lse_merge"] if token_fused else
+             (["h2o_accumulate"] if token_level else [] if one_launch else ["page_score"]) +
             (["sparse_page_decode"] if one_launch else ["sparse_select_decode"] if in_decode
-             else ["page_topk", "sparse_paged_decode"] + ([] if fused else ["lse_merge"]))
+             else ["sparse_select_decode_group", "lse_merge"] if in_group_decode
+             else ["page_topk", "sparse_paged_decode"] + ([] if fused else ["lse_merge"])))
 
     def enqueue(i, name):
         """Enqueue kernel `name` of step i (replica i % R, sequence step i % steps)."""
@@ -527,6 +531,8 @@ def measure(args, workload, cpu=True):
             d.append(c, bt, sl, kn, vn)
         elif name == "h2o_accumulate":
             d.accumulate(q, c, bt, sl)
+        elif name == "h2o_select_decode":
+            d.accumulate_select_attend(q, c, bt, sl)
         elif name == "page_score":
             d.score(q, bt, sl)
         elif name == "page_topk":
@@ -539,6 +545,8 @@ def measure(args, workload, cpu=True):
             d.attend(q, c, bt, sl)
         elif name == "sparse_select_decode":
             d.select_attend(q, c, bt, sl)
+        elif name == "sparse_select_decode_group":
+            d.select_attend_group(q, c, bt, sl)
         elif name == "sparse_page_decode":
             d.score_select_attend(q, c, bt, sl)
         else:
@@ -599,7 +607,12 @@ def measure(args, workload, cpu=True):
     last = (args.warmup + args.steps - 1)
     d = decs[last % R]
     sl_last = wl.seq_lens_at(last % wl.steps)
-    if in_decode:   # the selection stays in LDS; recompute it for the byte count
+    if token_fused:   # the selection stays on chip: one more step that writes it out
+        d.keep_selection = True
+        d.accumulate_select_attend(q, caches[last % R], bt, seq_steps[last % wl.steps])
+        d.keep_selection = False
+        torch.cuda.synchronize()
+    elif in_decode or in_group_decode:   # the selection stays in LDS; recompute it
         if one_launch:
             d.score(q, bt, seq_steps[last % wl.steps])
         d.select(seq_steps[last % wl.steps], bt)
@@ -637,6 +650,14 @@ def measure(args, workload, cpu=True):
     elif in_decode:   # one launch: the top-k's score read plus the merged decode
         kb["sparse_select_decode"] = kb.pop("page_topk") - int(sel_cnt.sum()) * 4 \
             + kb.pop("sparse_paged_decode")
+    elif token_fused:   # the accumulator step without its score rows, plus the decode
+        S_sum = int(sl_last.astype(np.int64).sum())
+        kb["h2o_select_decode"] = (kb.pop("h2o_accumulate") - S_sum * wl.H_kv * 4
+                                   + kb.pop("sparse_paged_decode") - int(sel_cnt.sum()) * 4)
+        kb.pop("page_topk")
+    elif in_group_decode:   # the top-k's score read plus the decode's partials
+        kb["sparse_select_decode_group"] = kb.pop("page_topk") - int(sel_cnt.sum()) * 4 \
+            + kb.pop("sparse_paged_decode")
     step_bytes = sum(kb.values())
     kern = {}
     for n in names:
@@ -645,7 +666,9 @@ def measure(args, workload, cpu=True):
                    "GBps": round(kb[n] / (t * 1e-3) / 1e9, 1) if t > 0 else None}
     dominant = max(names, key=lambda n: per_kernel_ms[n])
     focus = ("sparse_page_decode" if one_launch else
-             "sparse_select_decode" if in_decode else "sparse_paged_decode")
+             "sparse_select_decode" if in_decode else
+             "sparse_select_decode_group" if in_group_decode else
+             "h2o_select_decode" if token_fused else "sparse_paged_decode")
     a = kb[focus] / (per_kernel_ms[focus] * 1e-3) / 1e9
     roofline = {"kernel": focus, "bound": "hbm", "achieved": round(a, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(a / PEAK_HBM_GBPS, 4),
@@ -691,7 +714,8 @@ def measure(args, workload, cpu=True):
                    "gauss_tau": (None if not gauss else
                                  "page_mixture" if decs[0].mixture else "single"),
                    "alibi": slopes is not None, "merge_in_decode": fused,
-                   "select_in_decode": in_decode, "one_launch_step": one_launch,
+                   "select_in_decode": in_decode or in_group_decode or token_fused,
+                   "one_launch_step": one_launch,
                    "attention": "entmax15" if entmax else "softmax",
                    "h2o_softmax": args.h2o_softmax if token_level else None,
                    "parallelism": "single-gpu"},

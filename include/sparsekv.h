@@ -306,6 +306,41 @@ int sparse_select_decode(const float *scores, int64_t score_ld, int topk_pages,
                          int32_t *sel_blk, hipStream_t stream);
 
 /*
+ * sparse_select_decode_group -- page_topk and sparse_paged_decode in one
+ * launch for a selection shared by each kv head's query group (H_sel = H_kv:
+ * the token-level flow, page_score_group).  One block per (split, kv head,
+ * request) first selects its row from the scores into LDS (the top-k of
+ * page_topk; every split block of a row derives the same selection), then
+ * attends over its chunk of it for the G query heads of the group.  [Same
+ * sources as page_topk and sparse_paged_decode; VTX "Token-level variants":
+ * the token flow selects once per kv head.]
+ *
+ *   scores   fp32 [B, H_kv, score_ld] (h2o_accumulate's or page_score_group's
+ *            output), score_ld <= 8192
+ *   topk_pages, topk_frac, reserved_bos, reserved_eos, k_cap: as page_topk
+ *            (k_cap <= 4096)
+ *   q ... seq_lens, scale, num_splits, alibi_slopes: as sparse_paged_decode_ex
+ *            with H_sel = H_kv (split s of a row holds the selected entries
+ *            [s c, min((s + 1) c, cnt)), c = ceil(k_cap / num_splits))
+ *   o_part   fp32 [B, H_q, num_splits, D], lse_part fp32 [B, H_q, num_splits]:
+ *            exactly what sparse_paged_decode writes for that selection
+ *            (lse_merge combines them)
+ *   sel_idx, sel_cnt (both or neither), sel_blk (needs sel_idx):
+ *            [B, H_kv, k_cap] / [B, H_kv]; when given, receive the selection
+ *            exactly as page_topk_blk writes it.
+ */
+int sparse_select_decode_group(const float *scores, int64_t score_ld, int topk_pages,
+                               float topk_frac, int reserved_bos, int reserved_eos,
+                               const float *q, int B, int H_q, int H_kv, int D,
+                               const uint16_t *kv_cache, int64_t num_blocks,
+                               int page_size, const int32_t *block_table,
+                               int64_t bt_ld, const int32_t *seq_lens, int k_cap,
+                               float scale, int num_splits,
+                               const float *alibi_slopes, float *o_part,
+                               float *lse_part, int32_t *sel_idx, int32_t *sel_cnt,
+                               int32_t *sel_blk, hipStream_t stream);
+
+/*
  * sparse_page_decode -- the whole page-level step in one launch: page_score,
  * page_topk, sparse_paged_decode and lse_merge for one selection per query
  * head.  One block per query head scores its pages from the statistics into
@@ -531,6 +566,53 @@ int h2o_accumulate_noalloc(const float *q, int B, int H_q, int H_kv, int D,
                            int reserved_bos, int reserved_eos, float scale,
                            float decay, uint16_t *hh_score, float *scores,
                            int64_t score_ld, hipStream_t stream);
+
+/*
+ * h2o_select_decode -- the token-level step after the append, up to the split
+ * partials, in two launches: h2o_accumulate (either reading), then page_topk
+ * with H_sel = H_kv and sparse_paged_decode.  [VTX "Token-level variants":
+ * accumulate, select per kv head, attend over the selected tokens; the
+ * sources of the three steps.]
+ *   Launch 1 is the accumulator's logits pass, which also copies the
+ *   accumulator of every token it covers into the scratch.  Launch 2 runs one
+ *   block per (split, kv head, request): it applies the accumulator update to
+ *   its row from the logits and that copy (the arithmetic of h2o_accumulate's
+ *   update), selects the row's tokens in-block (page_topk's selection), and
+ *   attends over its chunk of the selection for the G query heads.  Split 0
+ *   of each row writes the new hh values (and the fp32 row, when scores is
+ *   given).  Results equal h2o_accumulate (per_head: h2o_accumulate_heads) +
+ *   page_topk_blk + sparse_paged_decode bit for bit.
+ *
+ *   q ... seq_lens, reserved_bos, reserved_eos, scale, decay, hh_score: as
+ *            h2o_accumulate (page_size 1); bt_ld <= 8192.
+ *   per_head 0: group-mean query (h2o_accumulate); nonzero: every query
+ *            head's own softmax averaged over the group (h2o_accumulate_heads).
+ *   scores   fp32 [B, H_kv, score_ld] or NULL: the new hh row, as
+ *            h2o_accumulate writes it (score_ld >= bt_ld).
+ *   topk_pages, topk_frac, k_cap: as page_topk (k_cap <= 4096); the reserved
+ *            window is reserved_bos / reserved_eos, as for the accumulator.
+ *   num_splits, o_part [B, H_q, num_splits, D], lse_part [B, H_q, num_splits]:
+ *            as sparse_paged_decode with H_sel = H_kv; lse_merge combines them.
+ *   sel_idx, sel_cnt (both or neither), sel_blk (needs sel_idx):
+ *            [B, H_kv, k_cap] / [B, H_kv] or NULL, as page_topk_blk writes them.
+ *   scratch  fp32, at least h2o_select_decode_scratch_floats(B, H_q, H_kv,
+ *            bt_ld, per_head) floats; contents on entry are ignored.
+ */
+int h2o_select_decode(const float *q, int B, int H_q, int H_kv, int D,
+                      const uint16_t *kv_cache, int64_t num_blocks, int page_size,
+                      const int32_t *block_table, int64_t bt_ld,
+                      const int32_t *seq_lens, int reserved_bos, int reserved_eos,
+                      float scale, float decay, int per_head, uint16_t *hh_score,
+                      float *scores, int64_t score_ld, int topk_pages,
+                      float topk_frac, int k_cap, int num_splits, float *o_part,
+                      float *lse_part, int32_t *sel_idx, int32_t *sel_cnt,
+                      int32_t *sel_blk, float *scratch, int64_t scratch_floats,
+                      hipStream_t stream);
+
+/* Scratch size (floats) h2o_select_decode needs; no device work; -1 on bad
+ * arguments. */
+int64_t h2o_select_decode_scratch_floats(int B, int H_q, int H_kv,
+                                         int64_t max_tokens, int per_head);
 
 /*
  * h2o_accumulate_heads -- the same step with the query-group axis kept through

@@ -21,9 +21,10 @@ __all__ = [
     "page_topk_blk", "sparse_paged_decode", "sparse_paged_decode_ex",
     "sparse_paged_decode_merged", "lse_merge",
     "h2o_accumulate", "h2o_scratch_floats", "h2o_accumulate_heads",
-    "h2o_heads_scratch_floats", "h2o_accumulate_noalloc", "NOALLOC_SCRATCH_FLOATS",
+    "h2o_heads_scratch_floats", "h2o_accumulate_noalloc", "h2o_select_decode", "h2o_select_decode_scratch_floats", "NOALLOC_SCRATCH_FLOATS",
     "entmax15_paged_decode",
-    "entmax_scratch_floats", "sparse_select_decode", "sparse_page_decode",
+    "entmax_scratch_floats", "sparse_select_decode", "sparse_select_decode_group",
+    "sparse_page_decode",
     "page_var_update", "gauss_moments", "gauss_select", "entmax15_paged_decode_merged",
     "skv_ref_stream_read", "skv_ref_gather_read", "library_path",
     "load_library", "SparseKVError", "EXPORTED_SYMBOLS",
@@ -38,8 +39,9 @@ EXPORTED_SYMBOLS = (
     "page_topk_blk", "sparse_paged_decode", "sparse_paged_decode_ex",
     "sparse_paged_decode_merged", "lse_merge",
     "h2o_accumulate", "h2o_scratch_floats", "h2o_accumulate_heads",
-    "h2o_heads_scratch_floats", "h2o_accumulate_noalloc", "entmax15_paged_decode",
-    "entmax_scratch_floats", "sparse_select_decode", "sparse_page_decode",
+    "h2o_heads_scratch_floats", "h2o_accumulate_noalloc", "h2o_select_decode", "h2o_select_decode_scratch_floats", "entmax15_paged_decode",
+    "entmax_scratch_floats", "sparse_select_decode", "sparse_select_decode_group",
+    "sparse_page_decode",
     "page_var_update", "gauss_moments", "gauss_select", "entmax15_paged_decode_merged",
     "skv_ref_stream_read", "skv_ref_gather_read", "sparsekv_last_error",
 )
@@ -49,8 +51,9 @@ _INT_RETURNING = ("pagestats_update", "page_score", "page_score_ex", "page_score
                   "page_topk", "page_topk_blk", "sparse_paged_decode",
                   "sparse_paged_decode_ex", "sparse_paged_decode_merged", "lse_merge",
                   "h2o_accumulate", "h2o_accumulate_heads", "h2o_accumulate_noalloc",
+                  "h2o_select_decode",
                   "entmax15_paged_decode",
-                  "sparse_select_decode",
+                  "sparse_select_decode", "sparse_select_decode_group",
                   "sparse_page_decode", "page_var_update", "gauss_moments", "gauss_select",
                   "entmax15_paged_decode_merged", "skv_ref_stream_read",
                   "skv_ref_gather_read")
@@ -99,6 +102,10 @@ def load_library():
     lib.h2o_scratch_floats.argtypes = [I, I, L]
     lib.h2o_scratch_floats.restype = ctypes.c_int64
     lib.h2o_accumulate_heads.argtypes = lib.h2o_accumulate.argtypes
+    lib.h2o_select_decode.argtypes = [V, I, I, I, I, V, L, I, V, L, V, I, I, F, F, I, V, V, L,
+                                      I, F, I, I, V, V, V, V, V, V, L, V]
+    lib.h2o_select_decode_scratch_floats.argtypes = [I, I, I, L, I]
+    lib.h2o_select_decode_scratch_floats.restype = ctypes.c_int64
     lib.h2o_accumulate_noalloc.argtypes = [V, I, I, I, I, V, L, I, V, L, V, I, I, F, F, V, V,
                                            L, V]
     lib.h2o_heads_scratch_floats.argtypes = [I, I, L]
@@ -113,6 +120,8 @@ def load_library():
     lib.entmax_scratch_floats.argtypes = [I, I, I, I]
     lib.sparse_select_decode.argtypes = [V, L, I, F, I, I, V, I, I, I, I, V, L, I, V, L, V,
                                          I, F, I, V, V, V, V, V, V, V]
+    lib.sparse_select_decode_group.argtypes = [V, L, I, F, I, I, V, I, I, I, I, V, L, I, V,
+                                               L, V, I, F, I, V, V, V, V, V, V, V]
     lib.sparse_page_decode.argtypes = [V, I, I, I, I, V, L, I, V, V, V, V, L, V, F, F, I, F,
                                        I, I, I, F, I, V, V, V, V, V, V, V, V]
     lib.entmax_scratch_floats.restype = ctypes.c_int64
@@ -628,6 +637,38 @@ def sparse_select_decode(scores, q, kv_cache, block_table, seq_lens, topk_pages,
         _ptr(sel_cnt), _ptr(sel_blk), _stream(stream)))
 
 
+def sparse_select_decode_group(scores, q, kv_cache, block_table, seq_lens, topk_pages,
+                               k_cap, scale, o_part, lse_part, topk_frac=0.0, reserved_bos=0,
+                               reserved_eos=1, sel_idx=None, sel_cnt=None, sel_blk=None,
+                               alibi_slopes=None, stream=None):
+    """page_topk + sparse_paged_decode in one launch for one selection per kv
+    head (scores [B, H_kv, score_ld], score_ld <= 8192): the split partials
+    o_part [B, H_q, splits, D] / lse_part [B, H_q, splits] (num_splits =
+    o_part.shape[2]); optionally writes the selection like page_topk_blk."""
+    lib = load_library()
+    _check("q", q, torch.float32, 3)
+    dev = q.device
+    B, H_q, D = q.shape
+    _check("scores", scores, torch.float32, 3, dev)
+    NB, P, H_kv = _cache(kv_cache, D, dev)
+    if scores is None or tuple(scores.shape[:2]) != (B, H_kv):
+        raise ValueError("scores must be [B, H_kv, score_ld]")
+    _check("block_table", block_table, torch.int32, 2, dev)
+    _check("seq_lens", seq_lens, torch.int32, 1, dev)
+    _batch(B, block_table, seq_lens)
+    if o_part is None or lse_part is None:
+        raise ValueError("o_part and lse_part are required")
+    ns = _partials(o_part, lse_part, B, H_q, D, dev)
+    _optional_selection(sel_idx, sel_cnt, sel_blk, B, H_kv, k_cap, dev)
+    alibi_slopes = _alibi_arg(alibi_slopes, H_q, dev)
+    _rc("sparse_select_decode_group", lib.sparse_select_decode_group(
+        _ptr(scores), scores.shape[2], int(topk_pages), float(topk_frac), int(reserved_bos),
+        int(reserved_eos), _ptr(q), B, H_q, H_kv, D, _ptr(kv_cache), NB, P,
+        _ptr(block_table), block_table.shape[1], _ptr(seq_lens), int(k_cap), float(scale),
+        ns, _ptr(alibi_slopes), _ptr(o_part), _ptr(lse_part), _ptr(sel_idx), _ptr(sel_cnt),
+        _ptr(sel_blk), _stream(stream)))
+
+
 def sparse_page_decode(q, kv_cache, k_min, k_max, k_mean, block_table, seq_lens, w_avg,
                        w_peak, topk_pages, k_cap, scale, num_splits, out, lse_out=None,
                        topk_frac=0.0, reserved_bos=0, reserved_eos=1, scores=None,
@@ -712,6 +753,48 @@ def _h2o(name, q, kv_cache, block_table, seq_lens, hh_score, scores, scratch, sc
         block_table.shape[1], _ptr(seq_lens), int(reserved_bos), int(reserved_eos),
         float(scale), float(decay), _ptr(hh_score), _ptr(scores), scores.shape[2],
         _ptr(scratch), scratch.numel(), _stream(stream)))
+
+
+def h2o_select_decode_scratch_floats(B, H_q, H_kv, max_tokens, per_head=False) -> int:
+    return int(load_library().h2o_select_decode_scratch_floats(
+        int(B), int(H_q), int(H_kv), int(max_tokens), 1 if per_head else 0))
+
+
+def h2o_select_decode(q, kv_cache, block_table, seq_lens, hh_score, scratch, scale,
+                      topk_pages, k_cap, o_part, lse_part, decay=0.984375, reserved_bos=0,
+                      reserved_eos=1, per_head=False, scores=None, topk_frac=0.0,
+                      sel_idx=None, sel_cnt=None, sel_blk=None, stream=None):
+    """Token-level accumulate + per-kv-head selection + decode in two launches:
+    hh_score updated in place, split partials o_part [B, H_q, splits, D] /
+    lse_part [B, H_q, splits] (num_splits = o_part.shape[2]) for lse_merge;
+    scores [B, H_kv, score_ld] and the selection are optional copies."""
+    lib = load_library()
+    _check("q", q, torch.float32, 3)
+    dev = q.device
+    B, H_q, D = q.shape
+    NB, P, H_kv = _cache(kv_cache, D, dev)
+    _check("block_table", block_table, torch.int32, 2, dev)
+    _check("seq_lens", seq_lens, torch.int32, 1, dev)
+    _batch(B, block_table, seq_lens)
+    for n, t in (("hh_score", hh_score), ("scratch", scratch), ("o_part", o_part),
+                 ("lse_part", lse_part)):
+        if t is None:
+            raise ValueError(f"{n} is required")
+    _check("hh_score", hh_score, torch.bfloat16, 2, dev)
+    _shape("hh_score", hh_score, (NB * P, H_kv))
+    _check("scratch", scratch, torch.float32, 1, dev)
+    ns = _partials(o_part, lse_part, B, H_q, D, dev)
+    _check("scores", scores, torch.float32, 3, dev)
+    if scores is not None and tuple(scores.shape[:2]) != (B, H_kv):
+        raise ValueError("scores must be [B, H_kv, score_ld]")
+    _optional_selection(sel_idx, sel_cnt, sel_blk, B, H_kv, k_cap, dev)
+    _rc("h2o_select_decode", lib.h2o_select_decode(
+        _ptr(q), B, H_q, H_kv, D, _ptr(kv_cache), NB, P, _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), int(reserved_bos), int(reserved_eos),
+        float(scale), float(decay), 1 if per_head else 0, _ptr(hh_score), _ptr(scores),
+        0 if scores is None else scores.shape[2], int(topk_pages), float(topk_frac),
+        int(k_cap), ns, _ptr(o_part), _ptr(lse_part), _ptr(sel_idx), _ptr(sel_cnt),
+        _ptr(sel_blk), _ptr(scratch), scratch.numel(), _stream(stream)))
 
 
 def h2o_accumulate(q, kv_cache, block_table, seq_lens, hh_score, scores, scratch,

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kLWaves * 64) void h2o_logits_kernel(
     const uint16_t* __restrict__ kv, const int32_t* __restrict__ bt,
     int64_t bt_ld, const int32_t* __restrict__ seq_lens, int bos, int eos,
     float scale_log2, float* __restrict__ logits, float* __restrict__ part,
-    int nchunk) {
+    int nchunk, const uint16_t* __restrict__ hh, uint16_t* __restrict__ hh_snap) {
   constexpr int LPR = D / 8;
   constexpr int RPW = 64 / LPR;                // head rows per wave load
   extern __shared__ float smem[];
@@ -87,6 +87,14 @@ __global__ __launch_bounds__(kLWaves * 64) void h2o_logits_kernel(
   const int32_t* btr = bt + static_cast<int64_t>(b) * bt_ld;
 
   if (tid < kChunk) sblk[tid] = t0 + tid < ntok ? btr[t0 + tid] : 0;
+  if (hh_snap != nullptr && tid < kChunk * H_kv) {
+    // the accumulator before this step, per kv head in logical order, for a
+    // consumer that must not read hh_score while it is being rewritten
+    const int tt = tid / H_kv, hd = tid % H_kv;
+    if (t0 + tt < ntok)
+      hh_snap[(static_cast<int64_t>(b) * H_kv + hd) * bt_ld + t0 + tt] =
+          hh[static_cast<int64_t>(btr[t0 + tt]) * H_kv + hd];
+  }
   const float inv_g = 1.0f / static_cast<float>(G);
   for (int i = tid; i < H_kv * D; i += blockDim.x) {
     const int h = i / D, d = i % D;
@@ -175,7 +183,7 @@ __global__ __launch_bounds__(kLWaves * 64) void h2o_logits_heads_kernel(
     const uint16_t* __restrict__ kv, const int32_t* __restrict__ bt,
     int64_t bt_ld, const int32_t* __restrict__ seq_lens, int bos, int eos,
     float scale_log2, float* __restrict__ logits, float* __restrict__ part,
-    int nchunk) {
+    int nchunk, const uint16_t* __restrict__ hh, uint16_t* __restrict__ hh_snap) {
   constexpr int NC = D / 32;                   // 32-dim steps of the MFMA
   constexpr int QS = D + 8;                    // padded query row (bf16)
   constexpr int LGS = kChunk + 4;              // padded logit row (floats)
@@ -196,6 +204,14 @@ __global__ __launch_bounds__(kLWaves * 64) void h2o_logits_heads_kernel(
   const int32_t* btr = bt + static_cast<int64_t>(b) * bt_ld;
 
   if (tid < kChunk) sblk[tid] = t0 + tid < ntok ? btr[t0 + tid] : 0;
+  if (hh_snap != nullptr && tid < kChunk * H_kv) {
+    // the accumulator before this step, per kv head in logical order, for a
+    // consumer that must not read hh_score while it is being rewritten
+    const int tt = tid / H_kv, hd = tid % H_kv;
+    if (t0 + tt < ntok)
+      hh_snap[(static_cast<int64_t>(b) * H_kv + hd) * bt_ld + t0 + tt] =
+          hh[static_cast<int64_t>(btr[t0 + tt]) * H_kv + hd];
+  }
   for (int i = tid; i < H_q * D; i += blockDim.x) {
     const int r = i / D, d = i % D;
     const float x = q[static_cast<int64_t>(b) * H_q * D + i] * scale_log2;
@@ -387,13 +403,23 @@ size_t logits_lds(bool per_head, int rows, int D) {
 }
 constexpr size_t kMaxLogitsLds = 64 * 1024;
 
+// Offset (floats) of the accumulator snapshot in the scratch of the pass that
+// feeds a fused update: after the logits and partials, 16-byte aligned.
+int64_t snap_offset(int B, int rows, int64_t max_tokens) {
+  return (scratch_floats(B, rows, max_tokens) + 3) / 4 * 4;
+}
+
+// pass == nullptr: the whole step (logits pass, then the update pass).
+// pass given: the logits pass only, with a snapshot of the accumulator for a
+// consumer that applies the update itself; scores is not used then.
 template <bool PH>
 int accumulate(const char* fn, const float* q, int B, int H_q, int H_kv, int D,
                const uint16_t* kv_cache, int64_t num_blocks, int page_size,
                const int32_t* block_table, int64_t bt_ld, const int32_t* seq_lens,
                int reserved_bos, int reserved_eos, float scale, float decay,
                uint16_t* hh_score, float* scores, int64_t score_ld, float* scratch,
-               int64_t scratch_floats_have, hipStream_t stream) {
+               int64_t scratch_floats_have, hipStream_t stream,
+               skv::H2oPass* pass = nullptr) {
   SKV_REQUIRE(page_size == 1, "%s: page_size must be 1 (got %d)", fn, page_size);
   SKV_REQUIRE(B >= 0 && H_kv > 0 && H_q > 0 && H_q % H_kv == 0,
               "%s: need H_q a positive multiple of H_kv", fn);
@@ -420,9 +446,10 @@ int accumulate(const char* fn, const float* q, int B, int H_q, int H_kv, int D,
   SKV_REQUIRE_PTR_W(fn, block_table);
   SKV_REQUIRE_PTR_W(fn, seq_lens);
   SKV_REQUIRE_PTR_W(fn, hh_score);
-  SKV_REQUIRE_PTR_W(fn, scores);
+  if (pass == nullptr) SKV_REQUIRE_PTR_W(fn, scores);
   SKV_REQUIRE_PTR_W(fn, scratch);
-  const int64_t need = scratch_floats(B, rows, bt_ld);
+  const int64_t need = pass == nullptr ? scratch_floats(B, rows, bt_ld)
+      : snap_offset(B, rows, bt_ld) + (static_cast<int64_t>(B) * H_kv * bt_ld + 1) / 2;
   SKV_REQUIRE(scratch_floats_have >= need, "%s: scratch has %lld floats, needs %lld", fn,
               (long long)scratch_floats_have, (long long)need);
   const int G = H_q / H_kv;
@@ -430,6 +457,8 @@ int accumulate(const char* fn, const float* q, int B, int H_q, int H_kv, int D,
   const int nupd = static_cast<int>((bt_ld + kUpd - 1) / kUpd);
   float* logits = scratch;
   float* part = scratch + static_cast<int64_t>(B) * rows * bt_ld;
+  uint16_t* hh_snap = pass == nullptr ? nullptr
+      : reinterpret_cast<uint16_t*>(scratch + snap_offset(B, rows, bt_ld));
   // decay is applied as its bf16 value, which is exact for 0.984375
   const float decay_b = skv_host_round_bf16(decay);
   dim3 grid(static_cast<unsigned>(nch), static_cast<unsigned>(B));
@@ -441,7 +470,8 @@ int accumulate(const char* fn, const float* q, int B, int H_q, int H_kv, int D,
 #define SKV_HEADS(DD, TT)                                                                \
   hipLaunchKernelGGL((h2o_logits_heads_kernel<DD, TT>), grid, dim3(kLWaves * 64), sm1,   \
                      stream, q, H_q, H_kv, G, kv_cache, block_table, bt_ld, seq_lens,     \
-                     reserved_bos, reserved_eos, scale_log2, logits, part, nch)
+                     reserved_bos, reserved_eos, scale_log2, logits, part, nch, hh_score,   \
+                     hh_snap)
     if (D == 128) {
       if (tpw <= 1) SKV_HEADS(128, 1); else if (tpw == 2) SKV_HEADS(128, 2);
       else if (tpw == 3) SKV_HEADS(128, 3); else SKV_HEADS(128, 4);
@@ -459,7 +489,8 @@ int accumulate(const char* fn, const float* q, int B, int H_q, int H_kv, int D,
 #define SKV_LOGITS_HM(DD, NN, HM)                                                        \
   hipLaunchKernelGGL((h2o_logits_kernel<DD, NN, HM>), grid, dim3(kLWaves * 64), sm1,      \
                      stream, q, H_q, H_kv, G, kv_cache, block_table, bt_ld, seq_lens,     \
-                     reserved_bos, reserved_eos, scale_log2, logits, part, nch)
+                     reserved_bos, reserved_eos, scale_log2, logits, part, nch, hh_score,   \
+                     hh_snap)
 #define SKV_LOGITS(DD, NN)                                                               \
   do {                                                                                   \
     if (hm) SKV_LOGITS_HM(DD, NN, true); else SKV_LOGITS_HM(DD, NN, false);              \
@@ -474,6 +505,16 @@ int accumulate(const char* fn, const float* q, int B, int H_q, int H_kv, int D,
     }
 #undef SKV_LOGITS
 #undef SKV_LOGITS_HM
+  }
+  if (pass != nullptr) {
+    *pass = skv::H2oPass{logits, part, hh_snap, nch, kChunk, decay_b};
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+      skv::set_error("%s: launch failed: %s", fn, hipGetErrorString(e));
+      return SKV_EIO;
+    }
+    skv::clear_error();
+    return SKV_OK;
   }
   const size_t sm2 = sizeof(float) * 2 * static_cast<size_t>(rows);
   hipLaunchKernelGGL(h2o_update_kernel<PH>,
@@ -536,6 +577,32 @@ int noalloc_scratch(const char* fn, hipStream_t stream, float** out) {
 }
 
 }  // namespace
+
+namespace skv {
+
+int h2o_logits_pass(const char* fn, bool per_head, const float* q, int B, int H_q, int H_kv,
+                    int D, const uint16_t* kv_cache, int64_t num_blocks, int page_size,
+                    const int32_t* block_table, int64_t bt_ld, const int32_t* seq_lens,
+                    int reserved_bos, int reserved_eos, float scale, float decay,
+                    const uint16_t* hh_score, float* scratch, int64_t scratch_floats,
+                    hipStream_t stream, H2oPass* out) {
+  // (hh_score is only read by this pass)
+  uint16_t* hh = const_cast<uint16_t*>(hh_score);
+  if (per_head)
+    return accumulate<true>(fn, q, B, H_q, H_kv, D, kv_cache, num_blocks, page_size,
+                            block_table, bt_ld, seq_lens, reserved_bos, reserved_eos, scale,
+                            decay, hh, nullptr, bt_ld, scratch, scratch_floats, stream, out);
+  return accumulate<false>(fn, q, B, H_q, H_kv, D, kv_cache, num_blocks, page_size,
+                           block_table, bt_ld, seq_lens, reserved_bos, reserved_eos, scale,
+                           decay, hh, nullptr, bt_ld, scratch, scratch_floats, stream, out);
+}
+
+int64_t h2o_pass_scratch_floats(int B, int rows, int H_kv, int64_t max_tokens) {
+  if (B < 0 || rows <= 0 || H_kv <= 0 || max_tokens <= 0) return -1;
+  return snap_offset(B, rows, max_tokens) + (static_cast<int64_t>(B) * H_kv * max_tokens + 1) / 2;
+}
+
+}  // namespace skv
 
 extern "C" int64_t h2o_scratch_floats(int B, int H_kv, int64_t max_tokens) {
   return scratch_floats(B, H_kv, max_tokens);

@@ -15,6 +15,25 @@ namespace skv {
 void set_error(const char* fmt, ...);
 void clear_error();
 
+// The token-level accumulator's first pass, for a kernel that folds the
+// update pass into itself (h2o.hip; used by sparse_decode.hip).  out
+// describes where the pass left its results in the caller's scratch.
+struct H2oPass {
+  const float* logits;      // [B, rows, bt_ld], base-2 scaled logits
+  const float* part;        // [B, rows, nchunk, 2] chunk (max, sum)
+  const uint16_t* snap;     // [B, H_kv, bt_ld] the accumulator before the step
+  int nchunk, chunk;        // chunks per row, tokens per chunk
+  float decay;              // the decay as applied (its bf16 value)
+};
+int h2o_logits_pass(const char* fn, bool per_head, const float* q, int B, int H_q, int H_kv,
+                    int D, const uint16_t* kv_cache, int64_t num_blocks, int page_size,
+                    const int32_t* block_table, int64_t bt_ld, const int32_t* seq_lens,
+                    int reserved_bos, int reserved_eos, float scale, float decay,
+                    const uint16_t* hh_score, float* scratch, int64_t scratch_floats,
+                    hipStream_t stream, H2oPass* out);
+// floats of scratch h2o_logits_pass needs (-1 on bad arguments)
+int64_t h2o_pass_scratch_floats(int B, int rows, int H_kv, int64_t max_tokens);
+
 }  // namespace skv
 
 // Reject a bad scalar before anything is enqueued.

@@ -106,11 +106,17 @@ __device__ __forceinline__ void load_row_keys(const float* __restrict__ srow,
   }
 }
 
+// Bits [0, x) set (x clipped to [0, 32]).
+__device__ __forceinline__ uint32_t low_bits(int x) {
+  return x <= 0 ? 0u : x >= 32 ? 0xffffffffu : ((1u << x) - 1u);
+}
+
 template <int BLOCK, int ITEMS, int BITS, bool SYNC_END>
 __device__ int topk_row_keys(const uint32_t (&key)[ITEMS], int N, int topk_pages,
                              double topk_frac, int bos, int eos,
                              const int32_t* __restrict__ btr, int64_t bt_ld,
                              int32_t* out, int32_t* bout, int k_cap) {
+  static_assert(ITEMS <= 32, "a thread's entries are tracked in 32-bit masks");
   constexpr int NW = BLOCK / 64;
   constexpr int kBits = BITS;                    // digit width
   constexpr int kBins = 1 << kBits;
@@ -118,7 +124,7 @@ __device__ int topk_row_keys(const uint32_t (&key)[ITEMS], int N, int topk_pages
   constexpr int kPerLane = kBins / 64;           // bins a lane scans
   static_assert(kPerLane % 4 == 0, "a lane scans its bins 16 bytes at a time");
   __shared__ __align__(16) int hist[kPasses][kBins];   // one histogram per pass
-  __shared__ int scan_smem[2 * (NW + 1)];
+  __shared__ int scan_smem[2 * NW];
   __shared__ uint32_t s_or[NW], s_and[NW];
 
   const int tid = threadIdx.x;
@@ -135,6 +141,14 @@ __device__ int topk_row_keys(const uint32_t (&key)[ITEMS], int N, int topk_pages
   const int ncand = hi - lo;
 
   const int base = tid * ITEMS;
+  // This thread's entries base + i as bit i: in the row (vm), in the ranked
+  // window (wm), reserved (rm: in the row, outside the window).  Every
+  // per-entry test below is a bit test, so the loops carry no branches.
+  const uint32_t im = low_bits(ITEMS);
+  const uint32_t vm = low_bits(N - base) & im;
+  const uint32_t wm = low_bits(hi - base) & ~low_bits(lo - base) & im;
+  const uint32_t rm = vm & ~wm;
+
   constexpr bool kVec = ITEMS % 4 == 0;
   // block ids of this thread's entries, fetched alongside the keys
   int32_t bid[ITEMS];
@@ -172,8 +186,9 @@ __device__ int topk_row_keys(const uint32_t (&key)[ITEMS], int N, int topk_pages
     uint32_t o = 0u, a = 0xffffffffu;
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
-      const int p = base + i;
-      if (p >= lo && p < hi) { o |= key[i]; a &= key[i]; }
+      const uint32_t c = 0u - ((wm >> i) & 1u);       // all ones for a candidate
+      o |= key[i] & c;
+      a &= key[i] | ~c;
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
@@ -204,8 +219,7 @@ __device__ int topk_row_keys(const uint32_t (&key)[ITEMS], int N, int topk_pages
       int* hp = hist[pass];
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i) {
-        const int p = base + i;
-        if (p >= lo && p < hi && (key[i] & pmask) == prefix)
+        if (((wm >> i) & 1u) && (key[i] & pmask) == prefix)
           atomicAdd(&hp[(key[i] >> shift) & dmask], 1);
       }
       __syncthreads();
@@ -248,36 +262,53 @@ __device__ int topk_row_keys(const uint32_t (&key)[ITEMS], int N, int topk_pages
   }
 
   // Entries taken outright (reserved, or above the prefix) and entries equal
-  // to the prefix, counted per thread and prefix-summed together: the
-  // r_eq lowest-index equal entries are taken, so an entry's place is the
+  // to the prefix, as bit masks and counts, prefix-summed together: the r_eq
+  // lowest-index equal entries are taken, so an entry's place is the
   // outright count before it plus min(equal count before it, r_eq).
-  int n_out = 0, n_eq = 0;
+  uint32_t om = rm, em = 0u;
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
-    const int p = base + i;
-    if (p >= N) continue;
     const uint32_t km = key[i] & pmask;
-    if (p < lo || p >= hi || km > prefix) ++n_out;
-    else if (km == prefix) ++n_eq;
+    om |= static_cast<uint32_t>(km > prefix) << i;
+    em |= static_cast<uint32_t>(km == prefix) << i;
   }
-  int out_before, eq_before, out_total, eq_total;
-  skv::block_exclusive_scan2(n_out, n_eq, &out_before, &eq_before, &out_total, &eq_total,
-                             scan_smem);
+  em &= wm;
+  om = (om & wm) | rm;
+  const int n_out = __popc(om), n_eq = __popc(em);
+  // exclusive scans of both counts: wave scans, one barrier for the wave
+  // totals (the selection's own closing barrier, or the caller's, keeps the
+  // totals from being overwritten before every wave has read them)
+  const int ix = skv::wave_inclusive_scan(n_out);
+  const int iy = skv::wave_inclusive_scan(n_eq);
+  if (lane == 63) { scan_smem[wave] = ix; scan_smem[NW + wave] = iy; }
+  __syncthreads();
+  int out_before = ix - n_out, eq_before = iy - n_eq, out_total = 0, eq_total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int tx = scan_smem[w], ty = scan_smem[NW + w];
+    if (w < wave) { out_before += tx; eq_before += ty; }
+    out_total += tx;
+    eq_total += ty;
+  }
   const int total = out_total + (eq_total < r_eq ? eq_total : r_eq);
-  int er = eq_before;
+  // entries taken: the outright ones, and the equal ones still within r_eq
+  const int eq_take = r_eq - eq_before;               // equal entries this thread may take
+  uint32_t tm = om;
+  if (eq_take >= n_eq) {
+    tm |= em;
+  } else if (eq_take > 0) {
+    uint32_t e = em;
+    for (int c = 0; c < eq_take; ++c) {                // lowest indices first
+      tm |= e & (0u - e);
+      e &= e - 1u;
+    }
+  }
   int pos = out_before + (eq_before < r_eq ? eq_before : r_eq);
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
-    const int p = base + i;
-    if (p >= N) continue;
-    const uint32_t km = key[i] & pmask;
-    bool take;
-    if (p < lo || p >= hi || km > prefix) take = true;
-    else if (km == prefix) { take = er < r_eq; ++er; }
-    else take = false;
-    if (take) {
-      if (pos >= 0 && pos < k_cap) {
-        out[pos] = p;
+    if ((tm >> i) & 1u) {
+      if (pos < k_cap) {
+        out[pos] = base + i;
         if (bout != nullptr) bout[pos] = bid[i];
       }
       ++pos;

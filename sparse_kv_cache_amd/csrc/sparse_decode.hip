@@ -197,7 +197,20 @@ struct TopkArgs {
   // in-block scoring (SC)
   const uint16_t* kmin; const uint16_t* kmax; const float* kmean;
   float w_avg, w_peak, inv_scale; int sc_cap; float* scores_out;
+  // in-block accumulator update (token level): the logits pass's output
+  const float* h_logits; const float* h_part; const uint16_t* h_snap; uint16_t* h_hh;
+  int h_nchunk, h_chunk; float h_decay;
 };
+
+// (max, sum) fold of two softmax partials in base 2, as the accumulator's
+// update pass folds them (same operations, same order).
+__device__ __forceinline__ void fold_max_sum(float& m, float& z, float m2, float z2) {
+  if (m2 == -INFINITY) return;
+  if (m == -INFINITY) { m = m2; z = z2; return; }
+  const float M = fmaxf(m, m2);
+  z = z * exp2f(m - M) + z2 * exp2f(m2 - M);
+  m = M;
+}
 
 template <int D, int WB, int PFIX, bool AL, bool FUSE, int TKI, bool SC = false>
 __global__ __launch_bounds__(WB * 64)
@@ -551,7 +564,19 @@ using skv::as_bf16x8;
 // Heads past G carry zero queries and are dropped at the end.  Online softmax
 // state per head lives in the four lanes of its S column; the waves' states
 // are merged through LDS at the end.
-template <int D, bool AL>
+// In-block selection (TKI > 0): the block first selects its row from the
+// row's scores (ta.scores, TKI entries per thread, the device top-k shared
+// with page_topk) into LDS and takes its chunk from there; every split block
+// of a row selects the same row, so the selection never leaves the chip
+// (block 0 of the row copies it out when ta.sel_idx is given).
+// Token level (H2O = 1 group-mean query, 2 per-head softmax): the row's
+// scores are the accumulator after this step's update, which the block
+// computes itself from the logits pass's logits and chunk (max, sum)
+// partials and the accumulator as it was before the step (the pass's
+// snapshot), with the update pass's arithmetic; split 0 of the row writes
+// the new accumulator (and, if asked, its fp32 row), so no block reads a
+// value another block rewrites.
+template <int D, bool AL, int TKI = 0, int H2O = 0>
 __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
     const float* __restrict__ q, int H_q, int H_kv, int G,
     const uint16_t* __restrict__ kv, int64_t num_blocks, int P,
@@ -559,7 +584,7 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel_idx,
     const int32_t* __restrict__ sel_cnt, const int32_t* __restrict__ sel_blk,
     int k_cap, float scale_log2, int num_splits, float* __restrict__ o_part,
-    float* __restrict__ lse_part, const float* __restrict__ alibi) {
+    float* __restrict__ lse_part, const float* __restrict__ alibi, TopkArgs ta) {
   constexpr int NC = D / 32;            // 32-dim steps of the logit MFMA
   constexpr int NB = D / 16;            // 16-column blocks of the output MFMA
   constexpr int WAVES = 4;
@@ -590,6 +615,142 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
   int avail = k_cap - start;
   avail = avail < 0 ? 0 : (avail > cap ? cap : avail);
   int pre_p = -1, pre_b = -1;
+  // with in-block selection: the row's selection in LDS (k_cap entries)
+  extern __shared__ int32_t sel_lds[];
+  if constexpr (TKI > 0) {
+    int64_t Nt;
+    uint32_t key[TKI];
+    if constexpr (H2O > 0) {
+      constexpr bool PH = H2O == 2;
+      const int GR = PH ? G : 1;              // logit rows of this kv head
+      const int HR = H_kv * GR;               // logit rows of the request
+      int ntok = S < bt_ld ? S : static_cast<int>(bt_ld);
+      if (ntok < 0) ntok = 0;
+      const int lo = ta.bos < ntok ? ta.bos : ntok;
+      int hi = ntok - ta.eos > 0 ? ntok - ta.eos : 0;
+      if (hi < lo) hi = lo;
+      Nt = ntok;
+      const int base = tid * TKI;
+      // (rows of bt_ld % 4 == 0 start 16-byte aligned in both buffers)
+      const bool vec = (bt_ld & 3) == 0 && base + TKI <= bt_ld;
+      // the old accumulator and the first logit row, issued before the
+      // normaliser so their latency overlaps it
+      const uint16_t* hrow = ta.h_snap + (static_cast<int64_t>(b) * H_kv + h) * bt_ld;
+      const float* lrow = ta.h_logits + (static_cast<int64_t>(b) * HR + h * GR) * bt_ld;
+      const int32_t* btr0 = bt + static_cast<int64_t>(b) * bt_ld;
+      float hv[TKI], lg[TKI];
+      int32_t slot[TKI];                      // split 0 only: where hh lives
+      if (vec) {
+#pragma unroll
+        for (int i = 0; i < TKI; i += 4) {
+          const uint2 w = *reinterpret_cast<const uint2*>(hrow + base + i);
+          hv[i] = skv::bf16_lo(w.x); hv[i + 1] = skv::bf16_hi(w.x);
+          hv[i + 2] = skv::bf16_lo(w.y); hv[i + 3] = skv::bf16_hi(w.y);
+          const float4 l4 = *reinterpret_cast<const float4*>(lrow + base + i);
+          lg[i] = l4.x; lg[i + 1] = l4.y; lg[i + 2] = l4.z; lg[i + 3] = l4.w;
+        }
+        if (s == 0) {
+#pragma unroll
+          for (int i = 0; i < TKI; i += 4) {
+            const int4 v4 = *reinterpret_cast<const int4*>(btr0 + base + i);
+            slot[i] = v4.x; slot[i + 1] = v4.y; slot[i + 2] = v4.z; slot[i + 3] = v4.w;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < TKI; ++i) {
+          const int t = base + i;
+          hv[i] = t < ntok ? skv::bf16_to_f32(hrow[t]) : 0.0f;
+          lg[i] = t < ntok ? lrow[t] : 0.0f;
+          slot[i] = (s == 0 && t < ntok) ? btr0[t] : 0;
+        }
+      }
+      // (max, sum) of each logit row over the row's chunks, in the update
+      // pass's lane layout: LR lanes per row fold every LR-th chunk, then a
+      // butterfly over the row's lanes
+      __shared__ float hM[16], hZ[16];
+      {
+        int LR = 64;
+        while (LR > 1 && LR * HR > 256) LR >>= 1;
+        const int r = tid / LR, sl = tid % LR;
+        const int nch_b = (ntok + ta.h_chunk - 1) / ta.h_chunk;
+        float m = -INFINITY, z = 0.0f;
+        if (r < GR) {
+          const float2* pp = reinterpret_cast<const float2*>(
+              ta.h_part + (static_cast<int64_t>(b) * HR + h * GR + r) * ta.h_nchunk * 2);
+          for (int j = sl; j < nch_b; j += LR) fold_max_sum(m, z, pp[j].x, pp[j].y);
+        }
+        for (int off = LR >> 1; off > 0; off >>= 1)
+          fold_max_sum(m, z, __shfl_xor(m, off), __shfl_xor(z, off));
+        if (r < GR && sl == 0) { hM[r] = m; hZ[r] = z; }
+      }
+      __syncthreads();
+      float pr[TKI];
+      if constexpr (PH) {
+#pragma unroll
+        for (int i = 0; i < TKI; ++i) pr[i] = exp2f(lg[i] - hM[0]) / hZ[0];
+        for (int g = 1; g < GR; ++g) {
+          const float* lr2 = lrow + static_cast<int64_t>(g) * bt_ld;
+#pragma unroll
+          for (int i = 0; i < TKI; ++i) {
+            const int t = base + i;
+            const float l2 = t < ntok ? lr2[t] : 0.0f;
+            pr[i] += exp2f(l2 - hM[g]) / hZ[g];
+          }
+        }
+        const float inv = static_cast<float>(GR);
+#pragma unroll
+        for (int i = 0; i < TKI; ++i) pr[i] /= inv;
+      } else {
+#pragma unroll
+        for (int i = 0; i < TKI; ++i) pr[i] = exp2f(lg[i] - hM[0]) / hZ[0];
+      }
+      float* srow_out = ta.scores_out != nullptr
+          ? ta.scores_out + static_cast<int64_t>(row) * ta.score_ld : nullptr;
+#pragma unroll
+      for (int i = 0; i < TKI; ++i) {
+        const int t = base + i;
+        float v = hv[i];
+        if (t >= lo && t < hi) {
+          const float pb = skv::bf16_to_f32(skv::f32_to_bf16(pr[i]));
+          const uint16_t nb = skv::f32_to_bf16(fmaf(ta.h_decay, v, pb));
+          v = skv::bf16_to_f32(nb);
+          if (s == 0) ta.h_hh[static_cast<int64_t>(slot[i]) * H_kv + h] = nb;
+        }
+        if (s == 0 && srow_out != nullptr && t < ntok) srow_out[t] = v;
+        key[i] = t < ntok ? skv::order_key(v) : 0u;
+      }
+    } else {
+    Nt = (static_cast<int64_t>(S) + P - 1) / P;
+    if (Nt > ta.score_ld) Nt = ta.score_ld;
+    const float* srow = ta.scores + static_cast<int64_t>(row) * ta.score_ld;
+    const bool aligned = ((ta.score_ld & 3) == 0) &&
+                         ((reinterpret_cast<uintptr_t>(ta.scores) & 15) == 0);
+    // the whole stored row is loaded before its length is known; entries
+    // outside [bos, N - eos) are ignored by the selection
+    skv::load_row_keys<TKI>(srow, aligned, ta.score_ld, key);
+    }
+    const int cnt = skv::topk_row_keys<256, TKI>(key, static_cast<int>(Nt), ta.topk_pages,
+                                                 ta.topk_frac, ta.bos, ta.eos, nullptr, 0,
+                                                 sel_lds, nullptr, k_cap);
+    if (ta.sel_idx != nullptr && s == 0) {
+      const int32_t* btr0 = bt + static_cast<int64_t>(b) * bt_ld;
+      for (int j = tid; j < k_cap; j += 256) {
+        const int p = sel_lds[j];
+        ta.sel_idx[static_cast<int64_t>(row) * k_cap + j] = p;
+        if (ta.sel_blk != nullptr)
+          ta.sel_blk[static_cast<int64_t>(row) * k_cap + j] = (p >= 0 && p < bt_ld) ? btr0[p] : -1;
+      }
+      if (tid == 0) ta.sel_cnt[row] = cnt;
+    }
+    if (tid < kMaxEnt && tid < avail) pre_p = sel_lds[start + tid];
+    if (tid == 0) {
+      const Chunk ch = split_chunk(cnt, k_cap, num_splits, s);
+      s_start = ch.start;
+      s_len = ch.len;
+      s_pref = (AL && ch.len > 0) ? sel_lds[ch.start + ch.len - 1] : 0;
+    }
+  } else {
   if (tid < kMaxEnt && tid < avail) {
     const int64_t at = static_cast<int64_t>(row) * k_cap + start + tid;
     pre_p = sel_idx[at];
@@ -602,6 +763,7 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
     // ALiBi offsets are taken from the chunk's last selected page (see the
     // per-head kernel); its bias returns in the lse
     s_pref = (AL && ch.len > 0) ? sel_idx[static_cast<int64_t>(row) * k_cap + ch.start + ch.len - 1] : 0;
+  }
   }
 
   // Q^T as the B operand: lane holds head n, dims c*32 + 8*kq .. +8, scaled
@@ -657,13 +819,16 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
         if (rd == 0) {
           p = pre_p;                       // fetched above (256 threads: j == tid)
           pb = pre_b;
+        } else if constexpr (TKI > 0) {
+          p = sel_lds[s_start + pos];
+          pb = -1;
         } else {
           const int64_t at = static_cast<int64_t>(row) * k_cap + s_start + pos;
           p = sel_idx[at];
           pb = sel_blk != nullptr ? sel_blk[at] : -1;
         }
         if (p >= 0 && p < Nb) {
-          blk = sel_blk != nullptr ? pb : btr[p];
+          blk = (TKI == 0 && sel_blk != nullptr) ? pb : btr[p];
           const int nn = S - p * P;
           nv = nn < P ? nn : P;
         }
@@ -854,12 +1019,13 @@ void launch_wave_fused(hipStream_t st, const Args& a, int64_t n_groups, float* o
                      out, lse_out, ta);
 }
 
-template <int D, bool AL>
-void launch_group(dim3 grid, hipStream_t st, const Args& a) {
-  hipLaunchKernelGGL((sparse_decode_group_kernel<D, AL>), grid, dim3(256), 0, st,
+template <int D, bool AL, int TKI = 0, int H2O = 0>
+void launch_group(dim3 grid, hipStream_t st, const Args& a, const TopkArgs& ta = TopkArgs{}) {
+  const size_t lds = TKI > 0 ? sizeof(int32_t) * static_cast<size_t>(a.k_cap) : 0;
+  hipLaunchKernelGGL((sparse_decode_group_kernel<D, AL, TKI, H2O>), grid, dim3(256), lds, st,
                      a.q, a.H_q, a.H_kv, a.G, a.kv, a.num_blocks, a.P, a.bt, a.bt_ld,
                      a.seq_lens, a.sel_idx, a.sel_cnt, a.sel_blk, a.k_cap, a.scale_log2,
-                     a.num_splits, a.o_part, a.lse_part, a.alibi);
+                     a.num_splits, a.o_part, a.lse_part, a.alibi, ta);
 }
 
 }  // namespace
@@ -1168,4 +1334,171 @@ extern "C" int sparse_page_decode(const float* q, int B, int H_q, int H_kv, int 
 #undef SKV_SC_T
 #undef SKV_SC
   SKV_CHECK_LAUNCH();
+}
+
+extern "C" int sparse_select_decode_group(const float* scores, int64_t score_ld,
+                                          int topk_pages, float topk_frac, int reserved_bos,
+                                          int reserved_eos, const float* q, int B, int H_q,
+                                          int H_kv, int D, const uint16_t* kv_cache,
+                                          int64_t num_blocks, int page_size,
+                                          const int32_t* block_table, int64_t bt_ld,
+                                          const int32_t* seq_lens, int k_cap, float scale,
+                                          int num_splits, const float* alibi_slopes,
+                                          float* o_part, float* lse_part, int32_t* sel_idx,
+                                          int32_t* sel_cnt, int32_t* sel_blk,
+                                          hipStream_t stream) {
+  const char* who = "sparse_select_decode_group";
+  SKV_REQUIRE(B >= 0 && H_kv > 0 && H_q > 0 && H_q % H_kv == 0,
+              "%s: need H_q a positive multiple of H_kv", who);
+  const int G = H_q / H_kv;
+  SKV_REQUIRE(G <= 16, "%s: group size %d > 16", who, G);
+  SKV_REQUIRE(D == 64 || D == 128, "%s: D must be 64 or 128 (got %d)", who, D);
+  SKV_REQUIRE(skv_supported_page_size(page_size),
+              "%s: page_size must be 1, 2, 4, 8 or 16 (got %d)", who, page_size);
+  SKV_REQUIRE(num_splits >= 1 && num_splits <= 65535,
+              "%s: num_splits must be in [1, 65535] (got %d)", who, num_splits);
+  SKV_REQUIRE(score_ld > 0 && score_ld <= 8192,
+              "%s: score_ld must be in [1, 8192] (got %lld)", who, (long long)score_ld);
+  SKV_REQUIRE(topk_pages >= 1, "%s: topk_pages must be >= 1 (got %d)", who, topk_pages);
+  SKV_REQUIRE(topk_frac >= 0.0f && topk_frac <= 1.0f, "%s: topk_frac must be in [0, 1]", who);
+  SKV_REQUIRE(reserved_bos >= 0 && reserved_eos >= 0,
+              "%s: reserved_bos / reserved_eos must be >= 0", who);
+  SKV_REQUIRE(num_blocks > 0 && num_blocks <= 0x7fffffffLL && bt_ld > 0,
+              "%s: need 0 < num_blocks < 2^31 and bt_ld > 0", who);
+  const double frac = static_cast<double>(topk_frac);
+  int64_t need = topk_pages;
+  const int64_t fk = static_cast<int64_t>(floor(frac * static_cast<double>(score_ld)));
+  if (fk > need) need = fk;
+  if (static_cast<int64_t>(reserved_bos) + reserved_eos > need)
+    need = static_cast<int64_t>(reserved_bos) + reserved_eos;
+  if (need > score_ld) need = score_ld;
+  SKV_REQUIRE(k_cap >= need && k_cap <= 4096,
+              "%s: k_cap %d must cover the largest selection %lld (and be <= 4096)", who,
+              k_cap, (long long)need);
+  SKV_REQUIRE(B <= 65535 && H_kv <= 65535, "%s: grid too large", who);
+  // no rows: nothing is read or written, so no pointer is needed
+  if (B == 0) { skv::clear_error(); return SKV_OK; }
+  SKV_REQUIRE_PTR_W(who, scores);
+  SKV_REQUIRE_PTR_W(who, q);
+  SKV_REQUIRE_PTR_W(who, kv_cache);
+  SKV_REQUIRE_PTR_W(who, block_table);
+  SKV_REQUIRE_PTR_W(who, seq_lens);
+  SKV_REQUIRE_PTR_W(who, o_part);
+  SKV_REQUIRE_PTR_W(who, lse_part);
+  SKV_REQUIRE((sel_idx == nullptr) == (sel_cnt == nullptr),
+              "%s: sel_idx and sel_cnt must both be given or both be NULL", who);
+  SKV_REQUIRE(sel_blk == nullptr || sel_idx != nullptr, "%s: sel_blk needs sel_idx", who);
+  const Args a{q, H_q, H_kv, G, kv_cache, num_blocks, page_size, block_table, bt_ld,
+               seq_lens, nullptr, nullptr, nullptr, k_cap, scale * skv::kLog2e, num_splits,
+               o_part, lse_part, alibi_slopes};
+  const TopkArgs ta{scores, score_ld, topk_pages, frac, reserved_bos, reserved_eos,
+                    sel_idx, sel_cnt, sel_blk};
+  dim3 grid(static_cast<unsigned>(num_splits), static_cast<unsigned>(H_kv),
+            static_cast<unsigned>(B));
+  const bool al = alibi_slopes != nullptr;
+  const int tki = score_ld <= 1024 ? 4 : score_ld <= 2048 ? 8 : score_ld <= 5120 ? 20 : 32;
+#define SKV_GSEL(DD, TT)                                                     \
+  do {                                                                       \
+    if (al) launch_group<DD, true, TT>(grid, stream, a, ta);                 \
+    else launch_group<DD, false, TT>(grid, stream, a, ta);                   \
+  } while (0)
+#define SKV_GSEL_T(DD)                                                       \
+  do {                                                                       \
+    if (tki == 4) SKV_GSEL(DD, 4);                                           \
+    else if (tki == 8) SKV_GSEL(DD, 8);                                      \
+    else if (tki == 20) SKV_GSEL(DD, 20);                                    \
+    else SKV_GSEL(DD, 32);                                                   \
+  } while (0)
+  if (D == 128) SKV_GSEL_T(128); else SKV_GSEL_T(64);
+#undef SKV_GSEL_T
+#undef SKV_GSEL
+  SKV_CHECK_LAUNCH();
+}
+
+extern "C" int64_t h2o_select_decode_scratch_floats(int B, int H_q, int H_kv,
+                                                    int64_t max_tokens, int per_head) {
+  if (B < 0 || H_q <= 0 || H_kv <= 0 || H_q % H_kv != 0 || max_tokens <= 0) return -1;
+  return skv::h2o_pass_scratch_floats(B, per_head ? H_q : H_kv, H_kv, max_tokens);
+}
+
+extern "C" int h2o_select_decode(const float* q, int B, int H_q, int H_kv, int D,
+                                 const uint16_t* kv_cache, int64_t num_blocks, int page_size,
+                                 const int32_t* block_table, int64_t bt_ld,
+                                 const int32_t* seq_lens, int reserved_bos, int reserved_eos,
+                                 float scale, float decay, int per_head, uint16_t* hh_score,
+                                 float* scores, int64_t score_ld, int topk_pages,
+                                 float topk_frac, int k_cap, int num_splits, float* o_part,
+                                 float* lse_part, int32_t* sel_idx, int32_t* sel_cnt,
+                                 int32_t* sel_blk, float* scratch, int64_t scratch_floats,
+                                 hipStream_t stream) {
+  const char* who = "h2o_select_decode";
+  SKV_REQUIRE(B >= 0 && H_kv > 0 && H_q > 0 && H_q % H_kv == 0,
+              "%s: need H_q a positive multiple of H_kv", who);
+  SKV_REQUIRE(H_q / H_kv <= 16, "%s: group size > 16", who);
+  SKV_REQUIRE(page_size == 1, "%s: page_size must be 1 (got %d)", who, page_size);
+  SKV_REQUIRE(bt_ld > 0 && bt_ld <= 8192, "%s: bt_ld must be in [1, 8192] (got %lld)", who,
+              (long long)bt_ld);
+  SKV_REQUIRE(scores == nullptr || score_ld >= bt_ld,
+              "%s: score_ld must be >= bt_ld when scores are written", who);
+  SKV_REQUIRE(num_splits >= 1 && num_splits <= 65535,
+              "%s: num_splits must be in [1, 65535] (got %d)", who, num_splits);
+  SKV_REQUIRE(topk_pages >= 1, "%s: topk_pages must be >= 1 (got %d)", who, topk_pages);
+  SKV_REQUIRE(topk_frac >= 0.0f && topk_frac <= 1.0f, "%s: topk_frac must be in [0, 1]", who);
+  SKV_REQUIRE(reserved_bos >= 0 && reserved_eos >= 0,
+              "%s: reserved_bos / reserved_eos must be >= 0", who);
+  SKV_REQUIRE(num_blocks > 0 && num_blocks <= 0x7fffffffLL,
+              "%s: need 0 < num_blocks < 2^31", who);
+  const double frac = static_cast<double>(topk_frac);
+  int64_t need = topk_pages;
+  const int64_t fk = static_cast<int64_t>(floor(frac * static_cast<double>(bt_ld)));
+  if (fk > need) need = fk;
+  if (static_cast<int64_t>(reserved_bos) + reserved_eos > need)
+    need = static_cast<int64_t>(reserved_bos) + reserved_eos;
+  if (need > bt_ld) need = bt_ld;
+  SKV_REQUIRE(k_cap >= need && k_cap <= 4096,
+              "%s: k_cap %d must cover the largest selection %lld (and be <= 4096)", who,
+              k_cap, (long long)need);
+  SKV_REQUIRE(B <= 65535 && H_kv <= 65535, "%s: grid too large", who);
+  SKV_REQUIRE((sel_idx == nullptr) == (sel_cnt == nullptr),
+              "%s: sel_idx and sel_cnt must both be given or both be NULL", who);
+  SKV_REQUIRE(sel_blk == nullptr || sel_idx != nullptr, "%s: sel_blk needs sel_idx", who);
+  // the logits pass validates the rest (D, window, decay, scale, scratch size)
+  skv::H2oPass pass{};
+  const int rc = skv::h2o_logits_pass(who, per_head != 0, q, B, H_q, H_kv, D, kv_cache,
+                                      num_blocks, page_size, block_table, bt_ld, seq_lens,
+                                      reserved_bos, reserved_eos, scale, decay, hh_score,
+                                      scratch, scratch_floats, stream, &pass);
+  if (rc != SKV_OK || B == 0) return rc;
+  SKV_REQUIRE_PTR_W(who, o_part);
+  SKV_REQUIRE_PTR_W(who, lse_part);
+  const int G = H_q / H_kv;
+  const Args a{q, H_q, H_kv, G, kv_cache, num_blocks, page_size, block_table, bt_ld,
+               seq_lens, nullptr, nullptr, nullptr, k_cap, scale * skv::kLog2e, num_splits,
+               o_part, lse_part, nullptr};
+  TopkArgs ta{};
+  ta.scores = nullptr; ta.score_ld = score_ld; ta.topk_pages = topk_pages; ta.topk_frac = frac;
+  ta.bos = reserved_bos; ta.eos = reserved_eos;
+  ta.sel_idx = sel_idx; ta.sel_cnt = sel_cnt; ta.sel_blk = sel_blk;
+  ta.scores_out = scores;
+  ta.h_logits = pass.logits; ta.h_part = pass.part; ta.h_snap = pass.snap; ta.h_hh = hh_score;
+  ta.h_nchunk = pass.nchunk; ta.h_chunk = pass.chunk; ta.h_decay = pass.decay;
+  dim3 grid(static_cast<unsigned>(num_splits), static_cast<unsigned>(H_kv),
+            static_cast<unsigned>(B));
+  const int tki = bt_ld <= 1024 ? 4 : bt_ld <= 2048 ? 8 : bt_ld <= 5120 ? 20 : 32;
+#define SKV_H2OSEL(DD, TT)                                                   \
+  do {                                                                       \
+    if (per_head) launch_group<DD, false, TT, 2>(grid, stream, a, ta);       \
+    else launch_group<DD, false, TT, 1>(grid, stream, a, ta);                \
+  } while (0)
+#define SKV_H2OSEL_T(DD)                                                     \
+  do {                                                                       \
+    if (tki == 4) SKV_H2OSEL(DD, 4);                                         \
+    else if (tki == 8) SKV_H2OSEL(DD, 8);                                    \
+    else if (tki == 20) SKV_H2OSEL(DD, 20);                                  \
+    else SKV_H2OSEL(DD, 32);                                                 \
+  } while (0)
+  if (D == 128) SKV_H2OSEL_T(128); else SKV_H2OSEL_T(64);
+#undef SKV_H2OSEL_T
+#undef SKV_H2OSEL
+  SKV_CHECK_LAUNCH_W(who);
 }

@@ -10,7 +10,10 @@ library's entry points in the order of a decode step:
                head, shared by its query group
   token level  pagestats_update (append + hh reset) -> h2o_accumulate (or
                h2o_accumulate_heads: per-head softmax averaged over the group)
-               -> page_topk (per kv head) -> sparse_paged_decode -> lse_merge
+               -> page_topk (per kv head) -> sparse_paged_decode -> lse_merge,
+               as two launches when rows fit (h2o_select_decode: the logits
+               pass, then the update, the selection and the decode in one
+               kernel), then lse_merge
   Gaussian     [pagestats_update + page_var_update (tail page)]
                -> gauss_moments -> gauss_select -> entmax15_paged_decode
                -> lse_merge
@@ -35,10 +38,12 @@ import torch
 from . import (entmax15_paged_decode, entmax15_paged_decode_merged, entmax_scratch_floats,
                gauss_moments, gauss_select,
                h2o_accumulate, h2o_accumulate_heads, h2o_heads_scratch_floats,
-               h2o_scratch_floats, lse_merge, page_score, page_score_ex,
+               h2o_scratch_floats, h2o_select_decode, h2o_select_decode_scratch_floats,
+               lse_merge, page_score, page_score_ex,
                page_score_group, page_topk, page_topk_blk, page_var_update,
                pagestats_update, sparse_page_decode, sparse_paged_decode,
-               sparse_paged_decode_ex, sparse_paged_decode_merged, sparse_select_decode)
+               sparse_paged_decode_ex, sparse_paged_decode_merged, sparse_select_decode,
+               sparse_select_decode_group)
 
 
 def alibi_slopes(H, device="cuda"):
@@ -157,6 +162,9 @@ class SparseDecoder:
             self.hh = torch.zeros((num_blocks, H_kv), dtype=bf, device=dev)
             n = (h2o_heads_scratch_floats(B, H_q, bt_ld) if self.h2o_per_head
                  else h2o_scratch_floats(B, H_kv, bt_ld))
+            # (room for the fused step's accumulator copy as well)
+            n = max(n, h2o_select_decode_scratch_floats(B, H_q, H_kv, bt_ld,
+                                                        self.h2o_per_head))
             self.scratch = torch.empty(n, dtype=f32, device=dev)
         else:
             self.k_min = torch.empty((num_blocks, H_kv, D), dtype=bf, device=dev)
@@ -186,6 +194,14 @@ class SparseDecoder:
         self.keep_partials = False
         # selection inside the decode launch as well (score rows <= 4096)
         self.select_in_decode = self.fused and bt_ld <= 4096 and self.k_cap <= 4096
+        # a selection shared by the group: selected inside the group decode
+        # (rows of up to 8192), partials merged by lse_merge
+        self.select_in_group_decode = (bool(fuse_merge) and self.H_sel == H_kv and H_q > H_kv
+                                       and attention == "softmax" and bt_ld <= 8192
+                                       and self.k_cap <= 4096)
+        # token level: the accumulator update, the selection and the decode in
+        # two launches (h2o_select_decode), then lse_merge
+        self.token_fused = token_level and self.select_in_group_decode
         self.keep_selection = False
         # and scoring too: the whole page-level step in one launch, while the
         # device holds every block of it at once (two 8-wave blocks per CU,
@@ -339,6 +355,29 @@ class SparseDecoder:
             sel_idx=self.sel_idx if keep else None, sel_cnt=self.sel_cnt if keep else None,
             sel_blk=self.sel_blk if keep else None, alibi_slopes=self.alibi, stream=stream)
 
+    def select_attend_group(self, q, kv_cache, block_table, seq_lens, stream=None):
+        """Selection (per kv head) and the group decode in one launch
+        (select_in_group_decode); the partials still go through merge()."""
+        keep = self.keep_selection
+        sparse_select_decode_group(
+            self.scores, q, kv_cache, block_table, seq_lens, self.topk_pages, self.k_cap,
+            self.scale, self.o_part, self.lse_part, topk_frac=self.topk_frac,
+            reserved_bos=self.bos, reserved_eos=self.eos,
+            sel_idx=self.sel_idx if keep else None, sel_cnt=self.sel_cnt if keep else None,
+            sel_blk=self.sel_blk if keep else None, alibi_slopes=self.alibi, stream=stream)
+
+    def accumulate_select_attend(self, q, kv_cache, block_table, seq_lens, stream=None):
+        """Token level (token_fused): accumulate, select and decode in two
+        launches; hh updated, partials for merge()."""
+        keep = self.keep_selection
+        h2o_select_decode(
+            q, kv_cache, block_table, seq_lens, self.hh, self.scratch, self.scale,
+            self.topk_pages, self.k_cap, self.o_part, self.lse_part, decay=self.decay,
+            reserved_bos=self.bos, reserved_eos=self.eos, per_head=self.h2o_per_head,
+            scores=self.scores if self.keep_scores else None, topk_frac=self.topk_frac,
+            sel_idx=self.sel_idx if keep else None, sel_cnt=self.sel_cnt if keep else None,
+            sel_blk=self.sel_blk if keep else None, stream=stream)
+
     def score_select_attend(self, q, kv_cache, block_table, seq_lens, stream=None):
         """Score, select, decode and merge in one launch (score_in_decode)."""
         keep = self.keep_selection
@@ -372,12 +411,20 @@ class SparseDecoder:
         if self.score_in_decode:
             self.score_select_attend(q, kv_cache, block_table, seq_lens, stream)
             return self.out, self.lse
+        if self.token_fused:
+            self.accumulate_select_attend(q, kv_cache, block_table, seq_lens, stream)
+            self.merge(stream)
+            return self.out, self.lse
         if self.token_level:
             self.accumulate(q, kv_cache, block_table, seq_lens, stream)
         else:
             self.score(q, block_table, seq_lens, stream)
         if self.select_in_decode:
             self.select_attend(q, kv_cache, block_table, seq_lens, stream)
+            return self.out, self.lse
+        if self.select_in_group_decode:
+            self.select_attend_group(q, kv_cache, block_table, seq_lens, stream)
+            self.merge(stream)
             return self.out, self.lse
         self.select(seq_lens, block_table, stream)
         self.attend(q, kv_cache, block_table, seq_lens, stream)

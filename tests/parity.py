@@ -53,6 +53,62 @@ def poison(dec):
     dec.sel_blk.fill_(-7)
 
 
+def check_group_select_decode_matches(dec, q, cache, bt, sl):
+    """With a selection shared by each kv head's group, the one-launch form
+    (selection inside the group decode) must give exactly the bits the
+    separate page_topk + sparse_paged_decode (+ lse_merge) launches just
+    wrote into dec's buffers: selection, block ids, partials, merged output."""
+    assert dec.select_in_group_decode
+    ref = [t.clone() for t in (dec.sel_idx, dec.sel_cnt, dec.sel_blk, dec.o_part,
+                               dec.lse_part, dec.out, dec.lse)]
+    for t in (dec.o_part, dec.lse_part, dec.out, dec.lse):
+        t.fill_(float("nan"))
+    for t in (dec.sel_idx, dec.sel_cnt, dec.sel_blk):
+        t.fill_(-7)
+    keep = dec.keep_selection
+    dec.keep_selection = True
+    dec.select_attend_group(q, cache, bt, sl)
+    dec.merge()
+    dec.keep_selection = keep
+    torch.cuda.synchronize()
+    names = ("sel_idx", "sel_cnt", "sel_blk", "o_part", "lse_part", "out", "lse")
+    for name, a, b in zip(names, ref, (dec.sel_idx, dec.sel_cnt, dec.sel_blk, dec.o_part,
+                                       dec.lse_part, dec.out, dec.lse)):
+        assert torch.equal(a, b), f"select-in-decode {name} differs from separate launches"
+
+
+def check_token_fused_matches(dec, q, cache, bt, sl, pre_hh):
+    """Token level: after the separate launches (h2o_accumulate or its per-head
+    form, page_topk_blk, sparse_paged_decode, lse_merge) have filled dec's
+    buffers, rerun the step from the same accumulator (pre_hh, the device
+    tensor's bytes before the step) through h2o_select_decode and require the
+    same bits: accumulator, score rows, selection, partials, merged output."""
+    assert dec.token_fused
+    names = ("hh", "scores", "sel_idx", "sel_cnt", "sel_blk", "o_part", "lse_part", "out",
+             "lse")
+    ref = {n: getattr(dec, n).clone() for n in names}
+    dec.hh.copy_(pre_hh)
+    for n in ("scores", "o_part", "lse_part", "out", "lse"):
+        getattr(dec, n).fill_(float("nan"))
+    for n in ("sel_idx", "sel_cnt", "sel_blk"):
+        getattr(dec, n).fill_(-7)
+    keep = (dec.keep_selection, dec.keep_scores)
+    dec.keep_selection = dec.keep_scores = True
+    dec.accumulate_select_attend(q, cache, bt, sl)
+    dec.merge()
+    dec.keep_selection, dec.keep_scores = keep
+    torch.cuda.synchronize()
+    N = sl.cpu().numpy()
+    for n in names:
+        a, b = ref[n], getattr(dec, n)
+        if n == "scores":   # entries past each request's length are not written
+            for r in range(a.shape[0]):
+                assert torch.equal(a[r, :, :int(N[r])], b[r, :, :int(N[r])]), \
+                    f"fused token step: scores of request {r} differ"
+            continue
+        assert torch.equal(a, b), f"fused token step: {n} differs from separate launches"
+
+
 def bits(t):
     return W.bf16_bits(t)
 

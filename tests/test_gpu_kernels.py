@@ -12,7 +12,8 @@ from sparse_kv_cache_amd import workloads as W
 from sparse_kv_cache_amd.decode import SparseDecoder
 
 from parity import (OUT_ATOL, bits, check_attention, check_gauss_row, check_partials,
-                    check_scores, check_scores_alibi, check_scores_group, page_rows,
+                    check_group_select_decode_matches, check_scores,
+                    check_token_fused_matches, check_scores_alibi, check_scores_group, page_rows,
                     check_selection_exact, check_selection_vs_oracle,
                     check_stats, dev, per_head_rows, poison, say,
                     selection_rows, bf16_bits_apart, check_sel_blk)
@@ -314,6 +315,8 @@ def run_group_case(wl, cache_cpu, q_cpu):
                    wl.block_table, wl.seq_lens, per, wl.G, wl.softmax_scale, d.k_cap)
     worst = check_attention(d.out.cpu().numpy(), d.lse.cpu().numpy(), qd, cb,
                             wl.block_table, wl.seq_lens, per, wl.G, wl.softmax_scale)
+    if d.select_in_group_decode:
+        check_group_select_decode_matches(d, q, cache, bt, sl)
     return worst, ex
 
 
@@ -838,6 +841,7 @@ def test_token_level_step_teacher_forced(reading, H_q, H_kv, D):
         oracle.append(pre_cache, wl.block_table, sl_np, bits(kn), bits(vn), pre_hh)
         assert np.array_equal(bits(cache), pre_cache)
         assert np.array_equal(bits(d.hh), pre_hh)
+        pre_hh_dev = d.hh.clone()
         d.accumulate(q, cache, bt, sl)
         d.select(sl, bt)
         d.attend(q, cache, bt, sl)
@@ -870,6 +874,8 @@ def test_token_level_step_teacher_forced(reading, H_q, H_kv, D):
                        wl.softmax_scale, d.k_cap)
         check_attention(d.out.cpu().numpy(), d.lse.cpu().numpy(), qd, bits(cache),
                         wl.block_table, sl_np, per, H_q // H_kv, wl.softmax_scale)
+        if d.token_fused:
+            check_token_fused_matches(d, q, cache, bt, sl, pre_hh_dev)
         say(f"  step {step}: hh ulps off max {apart.max()}, "
             f"{int((apart > 0).sum())} of {apart.size}")
 
