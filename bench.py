@@ -10,6 +10,8 @@ One step = one pass of the whole hot path over the batch:
   high_batch: pagestats_update (append + refresh) -> the four above
   h2o_token:  pagestats_update (append + reset) -> h2o_accumulate ->
       page_topk -> sparse_paged_decode -> lse_merge
+      (as h2o_select_decode, the append and the accumulator's logits in one
+      launch, the update, selection and decode in another, then lse_merge)
 
 Inputs are seeded synthetic tensors already resident in HBM.  To measure
 HBM rather than the 256 MB memory-side cache, the timed steps rotate over R
@@ -513,7 +515,8 @@ def measure(args, workload, cpu=True):
             ["gauss_moments", "gauss_select", "sparse_paged_decode"] + \
             ([] if fused else ["lse_merge"])
     else:
-        names = (["pagestats_update"] if wl.steps > 1 else []) + \
+        # (token_fused: the append runs inside h2o_select_decode's first launch)
+        names = (["pagestats_update"] if wl.steps > 1 and not token_fused else []) + \
             (["h2o_select_decode", "lse_merge"] if token_fused else
              (["h2o_accumulate"] if token_level else [] if one_launch else ["page_score"]) +
             (["sparse_page_decode"] if one_launch else ["sparse_select_decode"] if in_decode
@@ -532,7 +535,8 @@ def measure(args, workload, cpu=True):
         elif name == "h2o_accumulate":
             d.accumulate(q, c, bt, sl)
         elif name == "h2o_select_decode":
-            d.accumulate_select_attend(q, c, bt, sl)
+            kn, vn = new_kv[s % len(new_kv)] if new_kv is not None else (None, None)
+            d.accumulate_select_attend(q, c, bt, sl, kn, vn)
         elif name == "page_score":
             d.score(q, bt, sl)
         elif name == "page_topk":
@@ -655,6 +659,8 @@ def measure(args, workload, cpu=True):
         kb["h2o_select_decode"] = (kb.pop("h2o_accumulate") - S_sum * wl.H_kv * 4
                                    + kb.pop("sparse_paged_decode") - int(sel_cnt.sum()) * 4)
         kb.pop("page_topk")
+        if "pagestats_update" in kb:   # the append, less its table reads (counted once)
+            kb["h2o_select_decode"] += kb.pop("pagestats_update") - wl.B * 8
     elif in_group_decode:   # the top-k's score read plus the decode's partials
         kb["sparse_select_decode_group"] = kb.pop("page_topk") - int(sel_cnt.sum()) * 4 \
             + kb.pop("sparse_paged_decode")

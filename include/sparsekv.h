@@ -568,9 +568,9 @@ int h2o_accumulate_noalloc(const float *q, int B, int H_q, int H_kv, int D,
                            int64_t score_ld, hipStream_t stream);
 
 /*
- * h2o_select_decode -- the token-level step after the append, up to the split
- * partials, in two launches: h2o_accumulate (either reading), then page_topk
- * with H_sel = H_kv and sparse_paged_decode.  [VTX "Token-level variants":
+ * h2o_select_decode -- the token-level step, up to the split partials, in two
+ * launches: (optionally the append), h2o_accumulate (either reading), then
+ * page_topk with H_sel = H_kv and sparse_paged_decode.  [VTX "Token-level variants":
  * accumulate, select per kv head, attend over the selected tokens; the
  * sources of the three steps.]
  *   Launch 1 is the accumulator's logits pass, which also copies the
@@ -578,9 +578,10 @@ int h2o_accumulate_noalloc(const float *q, int B, int H_q, int H_kv, int D,
  *   block per (split, kv head, request): it applies the accumulator update to
  *   its row from the logits and that copy (the arithmetic of h2o_accumulate's
  *   update), selects the row's tokens in-block (page_topk's selection), and
- *   attends over its chunk of the selection for the G query heads.  Split 0
- *   of each row writes the new hh values (and the fp32 row, when scores is
- *   given).  Results equal h2o_accumulate (per_head: h2o_accumulate_heads) +
+ *   attends over its chunk of the selection for the G query heads; the
+ *   row's split blocks then share writing the new hh values (and the fp32
+ *   row, when scores is given).  Results equal h2o_accumulate (per_head:
+ *   h2o_accumulate_heads) +
  *   page_topk_blk + sparse_paged_decode bit for bit.
  *
  *   q ... seq_lens, reserved_bos, reserved_eos, scale, decay, hh_score: as
@@ -595,18 +596,26 @@ int h2o_accumulate_noalloc(const float *q, int B, int H_q, int H_kv, int D,
  *            as sparse_paged_decode with H_sel = H_kv; lse_merge combines them.
  *   sel_idx, sel_cnt (both or neither), sel_blk (needs sel_idx):
  *            [B, H_kv, k_cap] / [B, H_kv] or NULL, as page_topk_blk writes them.
+ *   k_new, v_new  bf16 [B, H_kv, D] (both or neither) or NULL: this step's
+ *            new token; given, launch 1 also does pagestats_update's append
+ *            with no statistics (K and V written at position S_b - 1, its hh
+ *            slot zeroed; nothing when S_b - 1 >= bt_ld) and takes that
+ *            token's key from k_new, so the results equal pagestats_update
+ *            (append, hh_score given, no statistics) followed by the call
+ *            without them.  kv_cache is written only then.
  *   scratch  fp32, at least h2o_select_decode_scratch_floats(B, H_q, H_kv,
  *            bt_ld, per_head) floats; contents on entry are ignored.
  */
 int h2o_select_decode(const float *q, int B, int H_q, int H_kv, int D,
-                      const uint16_t *kv_cache, int64_t num_blocks, int page_size,
+                      uint16_t *kv_cache, int64_t num_blocks, int page_size,
                       const int32_t *block_table, int64_t bt_ld,
                       const int32_t *seq_lens, int reserved_bos, int reserved_eos,
                       float scale, float decay, int per_head, uint16_t *hh_score,
                       float *scores, int64_t score_ld, int topk_pages,
                       float topk_frac, int k_cap, int num_splits, float *o_part,
                       float *lse_part, int32_t *sel_idx, int32_t *sel_cnt,
-                      int32_t *sel_blk, float *scratch, int64_t scratch_floats,
+                      int32_t *sel_blk, const uint16_t *k_new,
+                      const uint16_t *v_new, float *scratch, int64_t scratch_floats,
                       hipStream_t stream);
 
 /* Scratch size (floats) h2o_select_decode needs; no device work; -1 on bad

@@ -103,7 +103,7 @@ def load_library():
     lib.h2o_scratch_floats.restype = ctypes.c_int64
     lib.h2o_accumulate_heads.argtypes = lib.h2o_accumulate.argtypes
     lib.h2o_select_decode.argtypes = [V, I, I, I, I, V, L, I, V, L, V, I, I, F, F, I, V, V, L,
-                                      I, F, I, I, V, V, V, V, V, V, L, V]
+                                      I, F, I, I, V, V, V, V, V, V, V, V, L, V]
     lib.h2o_select_decode_scratch_floats.argtypes = [I, I, I, L, I]
     lib.h2o_select_decode_scratch_floats.restype = ctypes.c_int64
     lib.h2o_accumulate_noalloc.argtypes = [V, I, I, I, I, V, L, I, V, L, V, I, I, F, F, V, V,
@@ -763,11 +763,14 @@ def h2o_select_decode_scratch_floats(B, H_q, H_kv, max_tokens, per_head=False) -
 def h2o_select_decode(q, kv_cache, block_table, seq_lens, hh_score, scratch, scale,
                       topk_pages, k_cap, o_part, lse_part, decay=0.984375, reserved_bos=0,
                       reserved_eos=1, per_head=False, scores=None, topk_frac=0.0,
-                      sel_idx=None, sel_cnt=None, sel_blk=None, stream=None):
+                      sel_idx=None, sel_cnt=None, sel_blk=None, k_new=None, v_new=None,
+                      stream=None):
     """Token-level accumulate + per-kv-head selection + decode in two launches:
     hh_score updated in place, split partials o_part [B, H_q, splits, D] /
     lse_part [B, H_q, splits] (num_splits = o_part.shape[2]) for lse_merge;
-    scores [B, H_kv, score_ld] and the selection are optional copies."""
+    scores [B, H_kv, score_ld] and the selection are optional copies.  With
+    k_new / v_new [B, H_kv, D] bf16 the step's append (cache rows and hh slot
+    of token S - 1) is done in the first launch."""
     lib = load_library()
     _check("q", q, torch.float32, 3)
     dev = q.device
@@ -788,13 +791,20 @@ def h2o_select_decode(q, kv_cache, block_table, seq_lens, hh_score, scratch, sca
     if scores is not None and tuple(scores.shape[:2]) != (B, H_kv):
         raise ValueError("scores must be [B, H_kv, score_ld]")
     _optional_selection(sel_idx, sel_cnt, sel_blk, B, H_kv, k_cap, dev)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new must be given together")
+    for n, t in (("k_new", k_new), ("v_new", v_new)):
+        _check(n, t, torch.bfloat16, 3, dev)
+        if t is not None:
+            _shape(n, t, (B, H_kv, D))
     _rc("h2o_select_decode", lib.h2o_select_decode(
         _ptr(q), B, H_q, H_kv, D, _ptr(kv_cache), NB, P, _ptr(block_table),
         block_table.shape[1], _ptr(seq_lens), int(reserved_bos), int(reserved_eos),
         float(scale), float(decay), 1 if per_head else 0, _ptr(hh_score), _ptr(scores),
         0 if scores is None else scores.shape[2], int(topk_pages), float(topk_frac),
         int(k_cap), ns, _ptr(o_part), _ptr(lse_part), _ptr(sel_idx), _ptr(sel_cnt),
-        _ptr(sel_blk), _ptr(scratch), scratch.numel(), _stream(stream)))
+        _ptr(sel_blk), _ptr(k_new), _ptr(v_new), _ptr(scratch), scratch.numel(),
+        _stream(stream)))
 
 
 def h2o_accumulate(q, kv_cache, block_table, seq_lens, hh_score, scores, scratch,

@@ -68,7 +68,9 @@ __global__ __launch_bounds__(kLWaves * 64) void h2o_logits_kernel(
     const uint16_t* __restrict__ kv, const int32_t* __restrict__ bt,
     int64_t bt_ld, const int32_t* __restrict__ seq_lens, int bos, int eos,
     float scale_log2, float* __restrict__ logits, float* __restrict__ part,
-    int nchunk, const uint16_t* __restrict__ hh, uint16_t* __restrict__ hh_snap) {
+    int nchunk, const uint16_t* __restrict__ hh, uint16_t* __restrict__ hh_snap,
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    uint16_t* __restrict__ kv_w, uint16_t* __restrict__ hh_w, int64_t v_off) {
   constexpr int LPR = D / 8;
   constexpr int RPW = 64 / LPR;                // head rows per wave load
   extern __shared__ float smem[];
@@ -87,13 +89,27 @@ __global__ __launch_bounds__(kLWaves * 64) void h2o_logits_kernel(
   const int32_t* btr = bt + static_cast<int64_t>(b) * bt_ld;
 
   if (tid < kChunk) sblk[tid] = t0 + tid < ntok ? btr[t0 + tid] : 0;
+  // With k_new given, this step's append (the cache's and the accumulator's
+  // side of it) is done here: the block whose chunk holds token S - 1 writes
+  // its K and V rows, zeroes its accumulator, and takes its logit from k_new.
+  const int t_new = seq_lens[b] - 1;
+  const bool app = k_new != nullptr && t_new >= t0 && t_new < ntok && t_new - t0 < kChunk;
+  if (app && tid < H_kv * (D / 8)) {
+    const int hd = tid / (D / 8), c8 = tid % (D / 8);
+    const int64_t dst = (static_cast<int64_t>(btr[t_new]) * H_kv + hd) * D + c8 * 8;
+    const int64_t src = (static_cast<int64_t>(b) * H_kv + hd) * D + c8 * 8;
+    *reinterpret_cast<uint4*>(kv_w + dst) = *reinterpret_cast<const uint4*>(k_new + src);
+    *reinterpret_cast<uint4*>(kv_w + v_off + dst) = *reinterpret_cast<const uint4*>(v_new + src);
+    if (c8 == 0) hh_w[static_cast<int64_t>(btr[t_new]) * H_kv + hd] = 0;
+  }
   if (hh_snap != nullptr && tid < kChunk * H_kv) {
     // the accumulator before this step, per kv head in logical order, for a
     // consumer that must not read hh_score while it is being rewritten
     const int tt = tid / H_kv, hd = tid % H_kv;
     if (t0 + tt < ntok)
       hh_snap[(static_cast<int64_t>(b) * H_kv + hd) * bt_ld + t0 + tt] =
-          hh[static_cast<int64_t>(btr[t0 + tt]) * H_kv + hd];
+          (app && t0 + tt == t_new) ? static_cast<uint16_t>(0)
+                                    : hh[static_cast<int64_t>(btr[t0 + tt]) * H_kv + hd];
   }
   const float inv_g = 1.0f / static_cast<float>(G);
   for (int i = tid; i < H_kv * D; i += blockDim.x) {
@@ -122,7 +138,9 @@ __global__ __launch_bounds__(kLWaves * 64) void h2o_logits_kernel(
     ok[u] = rl < R && t >= lo && t < hi;
     const int64_t off = ok[u] ? (static_cast<int64_t>(sblk[ok[u] ? tt : 0]) * H_kv + h) * D + cc * 8
                               : cc * 8;
-    kr[u] = *reinterpret_cast<const uint4*>(kv + off);
+    const uint16_t* src = (app && ok[u] && t == t_new)
+        ? k_new + (static_cast<int64_t>(b) * H_kv + h) * D + cc * 8 : kv + off;
+    kr[u] = *reinterpret_cast<const uint4*>(src);
   }
   // HM: the wave's kv head and its query slice in registers
   float qv[8];
@@ -183,7 +201,9 @@ __global__ __launch_bounds__(kLWaves * 64) void h2o_logits_heads_kernel(
     const uint16_t* __restrict__ kv, const int32_t* __restrict__ bt,
     int64_t bt_ld, const int32_t* __restrict__ seq_lens, int bos, int eos,
     float scale_log2, float* __restrict__ logits, float* __restrict__ part,
-    int nchunk, const uint16_t* __restrict__ hh, uint16_t* __restrict__ hh_snap) {
+    int nchunk, const uint16_t* __restrict__ hh, uint16_t* __restrict__ hh_snap,
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    uint16_t* __restrict__ kv_w, uint16_t* __restrict__ hh_w, int64_t v_off) {
   constexpr int NC = D / 32;                   // 32-dim steps of the MFMA
   constexpr int QS = D + 8;                    // padded query row (bf16)
   constexpr int LGS = kChunk + 4;              // padded logit row (floats)
@@ -204,13 +224,27 @@ __global__ __launch_bounds__(kLWaves * 64) void h2o_logits_heads_kernel(
   const int32_t* btr = bt + static_cast<int64_t>(b) * bt_ld;
 
   if (tid < kChunk) sblk[tid] = t0 + tid < ntok ? btr[t0 + tid] : 0;
+  // With k_new given, this step's append (the cache's and the accumulator's
+  // side of it) is done here: the block whose chunk holds token S - 1 writes
+  // its K and V rows, zeroes its accumulator, and takes its logit from k_new.
+  const int t_new = seq_lens[b] - 1;
+  const bool app = k_new != nullptr && t_new >= t0 && t_new < ntok && t_new - t0 < kChunk;
+  if (app && tid < H_kv * (D / 8)) {
+    const int hd = tid / (D / 8), c8 = tid % (D / 8);
+    const int64_t dst = (static_cast<int64_t>(btr[t_new]) * H_kv + hd) * D + c8 * 8;
+    const int64_t src = (static_cast<int64_t>(b) * H_kv + hd) * D + c8 * 8;
+    *reinterpret_cast<uint4*>(kv_w + dst) = *reinterpret_cast<const uint4*>(k_new + src);
+    *reinterpret_cast<uint4*>(kv_w + v_off + dst) = *reinterpret_cast<const uint4*>(v_new + src);
+    if (c8 == 0) hh_w[static_cast<int64_t>(btr[t_new]) * H_kv + hd] = 0;
+  }
   if (hh_snap != nullptr && tid < kChunk * H_kv) {
     // the accumulator before this step, per kv head in logical order, for a
     // consumer that must not read hh_score while it is being rewritten
     const int tt = tid / H_kv, hd = tid % H_kv;
     if (t0 + tt < ntok)
       hh_snap[(static_cast<int64_t>(b) * H_kv + hd) * bt_ld + t0 + tt] =
-          hh[static_cast<int64_t>(btr[t0 + tt]) * H_kv + hd];
+          (app && t0 + tt == t_new) ? static_cast<uint16_t>(0)
+                                    : hh[static_cast<int64_t>(btr[t0 + tt]) * H_kv + hd];
   }
   for (int i = tid; i < H_q * D; i += blockDim.x) {
     const int r = i / D, d = i % D;
@@ -231,9 +265,11 @@ __global__ __launch_bounds__(kLWaves * 64) void h2o_logits_heads_kernel(
     const int tok = t0 + tt;
     const bool ok = t < ntile && tok >= lo && tok < hi;
     const int64_t off = (ok ? (static_cast<int64_t>(sblk[tt]) * H_kv + h) * D : 0) + 8 * kq;
+    const uint16_t* src = (app && ok && tok == t_new)
+        ? k_new + (static_cast<int64_t>(b) * H_kv + h) * D + 8 * kq : kv + off;
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc)
-      kt[j][cc] = *reinterpret_cast<const uint4*>(kv + off + cc * 32);
+      kt[j][cc] = *reinterpret_cast<const uint4*>(src + cc * 32);
   }
 #pragma unroll
   for (int j = 0; j < TPW; ++j) {
@@ -419,7 +455,8 @@ int accumulate(const char* fn, const float* q, int B, int H_q, int H_kv, int D,
                int reserved_bos, int reserved_eos, float scale, float decay,
                uint16_t* hh_score, float* scores, int64_t score_ld, float* scratch,
                int64_t scratch_floats_have, hipStream_t stream,
-               skv::H2oPass* pass = nullptr) {
+               skv::H2oPass* pass = nullptr, const uint16_t* k_new = nullptr,
+               const uint16_t* v_new = nullptr, uint16_t* kv_w = nullptr) {
   SKV_REQUIRE(page_size == 1, "%s: page_size must be 1 (got %d)", fn, page_size);
   SKV_REQUIRE(B >= 0 && H_kv > 0 && H_q > 0 && H_q % H_kv == 0,
               "%s: need H_q a positive multiple of H_kv", fn);
@@ -461,6 +498,7 @@ int accumulate(const char* fn, const float* q, int B, int H_q, int H_kv, int D,
       : reinterpret_cast<uint16_t*>(scratch + snap_offset(B, rows, bt_ld));
   // decay is applied as its bf16 value, which is exact for 0.984375
   const float decay_b = skv_host_round_bf16(decay);
+  const int64_t v_off = num_blocks * page_size * static_cast<int64_t>(H_kv) * D;
   dim3 grid(static_cast<unsigned>(nch), static_cast<unsigned>(B));
   const size_t sm1 = logits_lds(PH, rows, D);
   const float scale_log2 = scale * skv::kLog2e;
@@ -471,7 +509,7 @@ int accumulate(const char* fn, const float* q, int B, int H_q, int H_kv, int D,
   hipLaunchKernelGGL((h2o_logits_heads_kernel<DD, TT>), grid, dim3(kLWaves * 64), sm1,   \
                      stream, q, H_q, H_kv, G, kv_cache, block_table, bt_ld, seq_lens,     \
                      reserved_bos, reserved_eos, scale_log2, logits, part, nch, hh_score,   \
-                     hh_snap)
+                     hh_snap, k_new, v_new, kv_w, hh_score, v_off)
     if (D == 128) {
       if (tpw <= 1) SKV_HEADS(128, 1); else if (tpw == 2) SKV_HEADS(128, 2);
       else if (tpw == 3) SKV_HEADS(128, 3); else SKV_HEADS(128, 4);
@@ -490,7 +528,7 @@ int accumulate(const char* fn, const float* q, int B, int H_q, int H_kv, int D,
   hipLaunchKernelGGL((h2o_logits_kernel<DD, NN, HM>), grid, dim3(kLWaves * 64), sm1,      \
                      stream, q, H_q, H_kv, G, kv_cache, block_table, bt_ld, seq_lens,     \
                      reserved_bos, reserved_eos, scale_log2, logits, part, nch, hh_score,   \
-                     hh_snap)
+                     hh_snap, k_new, v_new, kv_w, hh_score, v_off)
 #define SKV_LOGITS(DD, NN)                                                               \
   do {                                                                                   \
     if (hm) SKV_LOGITS_HM(DD, NN, true); else SKV_LOGITS_HM(DD, NN, false);              \
@@ -584,17 +622,18 @@ int h2o_logits_pass(const char* fn, bool per_head, const float* q, int B, int H_
                     int D, const uint16_t* kv_cache, int64_t num_blocks, int page_size,
                     const int32_t* block_table, int64_t bt_ld, const int32_t* seq_lens,
                     int reserved_bos, int reserved_eos, float scale, float decay,
-                    const uint16_t* hh_score, float* scratch, int64_t scratch_floats,
-                    hipStream_t stream, H2oPass* out) {
-  // (hh_score is only read by this pass)
-  uint16_t* hh = const_cast<uint16_t*>(hh_score);
+                    uint16_t* hh_score, float* scratch, int64_t scratch_floats,
+                    hipStream_t stream, H2oPass* out, const uint16_t* k_new,
+                    const uint16_t* v_new, uint16_t* kv_w) {
   if (per_head)
     return accumulate<true>(fn, q, B, H_q, H_kv, D, kv_cache, num_blocks, page_size,
                             block_table, bt_ld, seq_lens, reserved_bos, reserved_eos, scale,
-                            decay, hh, nullptr, bt_ld, scratch, scratch_floats, stream, out);
+                            decay, hh_score, nullptr, bt_ld, scratch, scratch_floats, stream,
+                            out, k_new, v_new, kv_w);
   return accumulate<false>(fn, q, B, H_q, H_kv, D, kv_cache, num_blocks, page_size,
                            block_table, bt_ld, seq_lens, reserved_bos, reserved_eos, scale,
-                           decay, hh, nullptr, bt_ld, scratch, scratch_floats, stream, out);
+                           decay, hh_score, nullptr, bt_ld, scratch, scratch_floats, stream,
+                           out, k_new, v_new, kv_w);
 }
 
 int64_t h2o_pass_scratch_floats(int B, int rows, int H_kv, int64_t max_tokens) {

@@ -29,8 +29,9 @@ int h2o_logits_pass(const char* fn, bool per_head, const float* q, int B, int H_
                     int D, const uint16_t* kv_cache, int64_t num_blocks, int page_size,
                     const int32_t* block_table, int64_t bt_ld, const int32_t* seq_lens,
                     int reserved_bos, int reserved_eos, float scale, float decay,
-                    const uint16_t* hh_score, float* scratch, int64_t scratch_floats,
-                    hipStream_t stream, H2oPass* out);
+                    uint16_t* hh_score, float* scratch, int64_t scratch_floats,
+                    hipStream_t stream, H2oPass* out, const uint16_t* k_new = nullptr,
+                    const uint16_t* v_new = nullptr, uint16_t* kv_w = nullptr);
 // floats of scratch h2o_logits_pass needs (-1 on bad arguments)
 int64_t h2o_pass_scratch_floats(int B, int rows, int H_kv, int64_t max_tokens);
 

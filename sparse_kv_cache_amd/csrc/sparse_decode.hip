@@ -202,6 +202,11 @@ struct TopkArgs {
   int h_nchunk, h_chunk; float h_decay;
 };
 
+// Bits [0, x) set (x clipped to [0, 32]).
+__device__ __forceinline__ uint32_t low_bits_u(int x) {
+  return x <= 0 ? 0u : x >= 32 ? 0xffffffffu : ((1u << x) - 1u);
+}
+
 // (max, sum) fold of two softmax partials in base 2, as the accumulator's
 // update pass folds them (same operations, same order).
 __device__ __forceinline__ void fold_max_sum(float& m, float& z, float m2, float z2) {
@@ -573,11 +578,11 @@ using skv::as_bf16x8;
 // scores are the accumulator after this step's update, which the block
 // computes itself from the logits pass's logits and chunk (max, sum)
 // partials and the accumulator as it was before the step (the pass's
-// snapshot), with the update pass's arithmetic; split 0 of the row writes
-// the new accumulator (and, if asked, its fp32 row), so no block reads a
-// value another block rewrites.
-template <int D, bool AL, int TKI = 0, int H2O = 0>
-__global__ __launch_bounds__(256) void sparse_decode_group_kernel(
+// snapshot), with the update pass's arithmetic; the row's split blocks
+// share the write of the new accumulator (and, if asked, its fp32 row) after
+// their decode, so no block reads a value another block rewrites.
+template <int D, bool AL, int TKI = 0, int H2O = 0, int NWV = 4>
+__global__ __launch_bounds__(NWV * 64) void sparse_decode_group_kernel(
     const float* __restrict__ q, int H_q, int H_kv, int G,
     const uint16_t* __restrict__ kv, int64_t num_blocks, int P,
     const int32_t* __restrict__ bt, int64_t bt_ld,
@@ -587,7 +592,7 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
     float* __restrict__ lse_part, const float* __restrict__ alibi, TopkArgs ta) {
   constexpr int NC = D / 32;            // 32-dim steps of the logit MFMA
   constexpr int NB = D / 16;            // 16-column blocks of the output MFMA
-  constexpr int WAVES = 4;
+  constexpr int WAVES = NWV;            // (in-block selection: more waves share it)
   constexpr int VST = D + 4;            // staged V row stride (bf16), skews banks
 
   __shared__ int32_t e_blk[kMaxEnt];
@@ -617,6 +622,14 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
   int pre_p = -1, pre_b = -1;
   // with in-block selection: the row's selection in LDS (k_cap entries)
   extern __shared__ int32_t sel_lds[];
+  // token level: the row's new accumulator values this thread computed, and
+  // the physical slots it writes them to when it owns them (the row's write
+  // is spread over its split blocks and issued after the decode)
+  constexpr int WB = (TKI > 0 && H2O > 0) ? TKI : 1;
+  float wb_v[WB];
+  int32_t wb_slot[WB];
+  uint32_t wb_win = 0u;                 // entries inside the accumulator window
+  bool wb_own = false;
   if constexpr (TKI > 0) {
     int64_t Nt;
     uint32_t key[TKI];
@@ -639,7 +652,8 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
       const float* lrow = ta.h_logits + (static_cast<int64_t>(b) * HR + h * GR) * bt_ld;
       const int32_t* btr0 = bt + static_cast<int64_t>(b) * bt_ld;
       float hv[TKI], lg[TKI];
-      int32_t slot[TKI];                      // split 0 only: where hh lives
+      int32_t* slot = wb_slot;
+      wb_own = (tid % num_splits) == s;
       if (vec) {
 #pragma unroll
         for (int i = 0; i < TKI; i += 4) {
@@ -649,7 +663,7 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
           const float4 l4 = *reinterpret_cast<const float4*>(lrow + base + i);
           lg[i] = l4.x; lg[i + 1] = l4.y; lg[i + 2] = l4.z; lg[i + 3] = l4.w;
         }
-        if (s == 0) {
+        if (wb_own) {
 #pragma unroll
           for (int i = 0; i < TKI; i += 4) {
             const int4 v4 = *reinterpret_cast<const int4*>(btr0 + base + i);
@@ -662,7 +676,7 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
           const int t = base + i;
           hv[i] = t < ntok ? skv::bf16_to_f32(hrow[t]) : 0.0f;
           lg[i] = t < ntok ? lrow[t] : 0.0f;
-          slot[i] = (s == 0 && t < ntok) ? btr0[t] : 0;
+          slot[i] = (wb_own && t < ntok) ? btr0[t] : 0;
         }
       }
       // (max, sum) of each logit row over the row's chunks, in the update
@@ -705,19 +719,16 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
 #pragma unroll
         for (int i = 0; i < TKI; ++i) pr[i] = exp2f(lg[i] - hM[0]) / hZ[0];
       }
-      float* srow_out = ta.scores_out != nullptr
-          ? ta.scores_out + static_cast<int64_t>(row) * ta.score_ld : nullptr;
+      wb_win = low_bits_u(hi - base) & ~low_bits_u(lo - base) & low_bits_u(TKI);
 #pragma unroll
       for (int i = 0; i < TKI; ++i) {
         const int t = base + i;
         float v = hv[i];
-        if (t >= lo && t < hi) {
+        if ((wb_win >> i) & 1u) {
           const float pb = skv::bf16_to_f32(skv::f32_to_bf16(pr[i]));
-          const uint16_t nb = skv::f32_to_bf16(fmaf(ta.h_decay, v, pb));
-          v = skv::bf16_to_f32(nb);
-          if (s == 0) ta.h_hh[static_cast<int64_t>(slot[i]) * H_kv + h] = nb;
+          v = skv::bf16_to_f32(skv::f32_to_bf16(fmaf(ta.h_decay, v, pb)));
         }
-        if (s == 0 && srow_out != nullptr && t < ntok) srow_out[t] = v;
+        wb_v[i] = v;
         key[i] = t < ntok ? skv::order_key(v) : 0u;
       }
     } else {
@@ -730,12 +741,12 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
     // outside [bos, N - eos) are ignored by the selection
     skv::load_row_keys<TKI>(srow, aligned, ta.score_ld, key);
     }
-    const int cnt = skv::topk_row_keys<256, TKI>(key, static_cast<int>(Nt), ta.topk_pages,
+    const int cnt = skv::topk_row_keys<NWV * 64, TKI>(key, static_cast<int>(Nt), ta.topk_pages,
                                                  ta.topk_frac, ta.bos, ta.eos, nullptr, 0,
                                                  sel_lds, nullptr, k_cap);
     if (ta.sel_idx != nullptr && s == 0) {
       const int32_t* btr0 = bt + static_cast<int64_t>(b) * bt_ld;
-      for (int j = tid; j < k_cap; j += 256) {
+      for (int j = tid; j < k_cap; j += NWV * 64) {
         const int p = sel_lds[j];
         ta.sel_idx[static_cast<int64_t>(row) * k_cap + j] = p;
         if (ta.sel_blk != nullptr)
@@ -977,6 +988,21 @@ __global__ __launch_bounds__(256) void sparse_decode_group_kernel(
       lse_part[prow] = lse2 * skv::kLn2;
     }
   }
+  if constexpr (TKI > 0 && H2O > 0) {
+    // the new accumulator (and its fp32 row) of the entries this thread owns
+    if (wb_own) {
+      int ntok = S < bt_ld ? S : static_cast<int>(bt_ld);
+      float* srow_out = ta.scores_out != nullptr
+          ? ta.scores_out + static_cast<int64_t>(row) * ta.score_ld : nullptr;
+#pragma unroll
+      for (int i = 0; i < TKI; ++i) {
+        const int t = tid * TKI + i;
+        if ((wb_win >> i) & 1u)
+          ta.h_hh[static_cast<int64_t>(wb_slot[i]) * H_kv + h] = skv::f32_to_bf16(wb_v[i]);
+        if (srow_out != nullptr && t < ntok) srow_out[t] = wb_v[i];
+      }
+    }
+  }
 }
 
 struct Args {
@@ -1019,10 +1045,11 @@ void launch_wave_fused(hipStream_t st, const Args& a, int64_t n_groups, float* o
                      out, lse_out, ta);
 }
 
-template <int D, bool AL, int TKI = 0, int H2O = 0>
+template <int D, bool AL, int TKI = 0, int H2O = 0, int NWV = 4>
 void launch_group(dim3 grid, hipStream_t st, const Args& a, const TopkArgs& ta = TopkArgs{}) {
   const size_t lds = TKI > 0 ? sizeof(int32_t) * static_cast<size_t>(a.k_cap) : 0;
-  hipLaunchKernelGGL((sparse_decode_group_kernel<D, AL, TKI, H2O>), grid, dim3(256), lds, st,
+  hipLaunchKernelGGL((sparse_decode_group_kernel<D, AL, TKI, H2O, NWV>), grid, dim3(NWV * 64),
+                     lds, st,
                      a.q, a.H_q, a.H_kv, a.G, a.kv, a.num_blocks, a.P, a.bt, a.bt_ld,
                      a.seq_lens, a.sel_idx, a.sel_cnt, a.sel_blk, a.k_cap, a.scale_log2,
                      a.num_splits, a.o_part, a.lse_part, a.alibi, ta);
@@ -1396,18 +1423,19 @@ extern "C" int sparse_select_decode_group(const float* scores, int64_t score_ld,
   dim3 grid(static_cast<unsigned>(num_splits), static_cast<unsigned>(H_kv),
             static_cast<unsigned>(B));
   const bool al = alibi_slopes != nullptr;
-  const int tki = score_ld <= 1024 ? 4 : score_ld <= 2048 ? 8 : score_ld <= 5120 ? 20 : 32;
+  // 8 waves: the selection's entries spread over 512 threads
+  const int tki = score_ld <= 2048 ? 4 : score_ld <= 4096 ? 8 : score_ld <= 6144 ? 12 : 16;
 #define SKV_GSEL(DD, TT)                                                     \
   do {                                                                       \
-    if (al) launch_group<DD, true, TT>(grid, stream, a, ta);                 \
-    else launch_group<DD, false, TT>(grid, stream, a, ta);                   \
+    if (al) launch_group<DD, true, TT, 0, 8>(grid, stream, a, ta);           \
+    else launch_group<DD, false, TT, 0, 8>(grid, stream, a, ta);             \
   } while (0)
 #define SKV_GSEL_T(DD)                                                       \
   do {                                                                       \
     if (tki == 4) SKV_GSEL(DD, 4);                                           \
     else if (tki == 8) SKV_GSEL(DD, 8);                                      \
-    else if (tki == 20) SKV_GSEL(DD, 20);                                    \
-    else SKV_GSEL(DD, 32);                                                   \
+    else if (tki == 12) SKV_GSEL(DD, 12);                                    \
+    else SKV_GSEL(DD, 16);                                                   \
   } while (0)
   if (D == 128) SKV_GSEL_T(128); else SKV_GSEL_T(64);
 #undef SKV_GSEL_T
@@ -1422,15 +1450,16 @@ extern "C" int64_t h2o_select_decode_scratch_floats(int B, int H_q, int H_kv,
 }
 
 extern "C" int h2o_select_decode(const float* q, int B, int H_q, int H_kv, int D,
-                                 const uint16_t* kv_cache, int64_t num_blocks, int page_size,
+                                 uint16_t* kv_cache, int64_t num_blocks, int page_size,
                                  const int32_t* block_table, int64_t bt_ld,
                                  const int32_t* seq_lens, int reserved_bos, int reserved_eos,
                                  float scale, float decay, int per_head, uint16_t* hh_score,
                                  float* scores, int64_t score_ld, int topk_pages,
                                  float topk_frac, int k_cap, int num_splits, float* o_part,
                                  float* lse_part, int32_t* sel_idx, int32_t* sel_cnt,
-                                 int32_t* sel_blk, float* scratch, int64_t scratch_floats,
-                                 hipStream_t stream) {
+                                 int32_t* sel_blk, const uint16_t* k_new,
+                                 const uint16_t* v_new, float* scratch,
+                                 int64_t scratch_floats, hipStream_t stream) {
   const char* who = "h2o_select_decode";
   SKV_REQUIRE(B >= 0 && H_kv > 0 && H_q > 0 && H_q % H_kv == 0,
               "%s: need H_q a positive multiple of H_kv", who);
@@ -1462,12 +1491,15 @@ extern "C" int h2o_select_decode(const float* q, int B, int H_q, int H_kv, int D
   SKV_REQUIRE((sel_idx == nullptr) == (sel_cnt == nullptr),
               "%s: sel_idx and sel_cnt must both be given or both be NULL", who);
   SKV_REQUIRE(sel_blk == nullptr || sel_idx != nullptr, "%s: sel_blk needs sel_idx", who);
+  SKV_REQUIRE((k_new == nullptr) == (v_new == nullptr),
+              "%s: k_new and v_new must both be given or both be NULL", who);
   // the logits pass validates the rest (D, window, decay, scale, scratch size)
   skv::H2oPass pass{};
   const int rc = skv::h2o_logits_pass(who, per_head != 0, q, B, H_q, H_kv, D, kv_cache,
                                       num_blocks, page_size, block_table, bt_ld, seq_lens,
                                       reserved_bos, reserved_eos, scale, decay, hh_score,
-                                      scratch, scratch_floats, stream, &pass);
+                                      scratch, scratch_floats, stream, &pass, k_new, v_new,
+                                      kv_cache);
   if (rc != SKV_OK || B == 0) return rc;
   SKV_REQUIRE_PTR_W(who, o_part);
   SKV_REQUIRE_PTR_W(who, lse_part);
@@ -1484,18 +1516,19 @@ extern "C" int h2o_select_decode(const float* q, int B, int H_q, int H_kv, int D
   ta.h_nchunk = pass.nchunk; ta.h_chunk = pass.chunk; ta.h_decay = pass.decay;
   dim3 grid(static_cast<unsigned>(num_splits), static_cast<unsigned>(H_kv),
             static_cast<unsigned>(B));
-  const int tki = bt_ld <= 1024 ? 4 : bt_ld <= 2048 ? 8 : bt_ld <= 5120 ? 20 : 32;
+  // 8 waves: the row's update and selection spread over 512 threads
+  const int tki = bt_ld <= 2048 ? 4 : bt_ld <= 4096 ? 8 : bt_ld <= 6144 ? 12 : 16;
 #define SKV_H2OSEL(DD, TT)                                                   \
   do {                                                                       \
-    if (per_head) launch_group<DD, false, TT, 2>(grid, stream, a, ta);       \
-    else launch_group<DD, false, TT, 1>(grid, stream, a, ta);                \
+    if (per_head) launch_group<DD, false, TT, 2, 8>(grid, stream, a, ta);    \
+    else launch_group<DD, false, TT, 1, 8>(grid, stream, a, ta);             \
   } while (0)
 #define SKV_H2OSEL_T(DD)                                                     \
   do {                                                                       \
     if (tki == 4) SKV_H2OSEL(DD, 4);                                         \
     else if (tki == 8) SKV_H2OSEL(DD, 8);                                    \
-    else if (tki == 20) SKV_H2OSEL(DD, 20);                                  \
-    else SKV_H2OSEL(DD, 32);                                                 \
+    else if (tki == 12) SKV_H2OSEL(DD, 12);                                  \
+    else SKV_H2OSEL(DD, 16);                                                 \
   } while (0)
   if (D == 128) SKV_H2OSEL_T(128); else SKV_H2OSEL_T(64);
 #undef SKV_H2OSEL_T

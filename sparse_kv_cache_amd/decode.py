@@ -11,9 +11,9 @@ library's entry points in the order of a decode step:
   token level  pagestats_update (append + hh reset) -> h2o_accumulate (or
                h2o_accumulate_heads: per-head softmax averaged over the group)
                -> page_topk (per kv head) -> sparse_paged_decode -> lse_merge,
-               as two launches when rows fit (h2o_select_decode: the logits
-               pass, then the update, the selection and the decode in one
-               kernel), then lse_merge
+               as two launches when rows fit (h2o_select_decode: the append
+               and the logits pass, then the update, the selection and the
+               decode in one kernel), then lse_merge
   Gaussian     [pagestats_update + page_var_update (tail page)]
                -> gauss_moments -> gauss_select -> entmax15_paged_decode
                -> lse_merge
@@ -366,9 +366,11 @@ class SparseDecoder:
             sel_idx=self.sel_idx if keep else None, sel_cnt=self.sel_cnt if keep else None,
             sel_blk=self.sel_blk if keep else None, alibi_slopes=self.alibi, stream=stream)
 
-    def accumulate_select_attend(self, q, kv_cache, block_table, seq_lens, stream=None):
-        """Token level (token_fused): accumulate, select and decode in two
-        launches; hh updated, partials for merge()."""
+    def accumulate_select_attend(self, q, kv_cache, block_table, seq_lens, k_new=None,
+                                 v_new=None, stream=None):
+        """Token level (token_fused): the append (when k_new is given),
+        accumulate, select and decode in two launches; hh updated, partials
+        for merge()."""
         keep = self.keep_selection
         h2o_select_decode(
             q, kv_cache, block_table, seq_lens, self.hh, self.scratch, self.scale,
@@ -376,7 +378,8 @@ class SparseDecoder:
             reserved_bos=self.bos, reserved_eos=self.eos, per_head=self.h2o_per_head,
             scores=self.scores if self.keep_scores else None, topk_frac=self.topk_frac,
             sel_idx=self.sel_idx if keep else None, sel_cnt=self.sel_cnt if keep else None,
-            sel_blk=self.sel_blk if keep else None, stream=stream)
+            sel_blk=self.sel_blk if keep else None, k_new=k_new, v_new=v_new,
+            stream=stream)
 
     def score_select_attend(self, q, kv_cache, block_table, seq_lens, stream=None):
         """Score, select, decode and merge in one launch (score_in_decode)."""
@@ -401,6 +404,12 @@ class SparseDecoder:
         """One decode step; returns (out, lse) views of the decoder's buffers."""
         if self.validate:
             validate_tables(block_table, seq_lens, self.num_blocks, self.P)
+        if self.token_fused:
+            # the append runs inside the first of the two launches
+            self.accumulate_select_attend(q, kv_cache, block_table, seq_lens, k_new, v_new,
+                                          stream)
+            self.merge(stream)
+            return self.out, self.lse
         if k_new is not None:
             self.append(kv_cache, block_table, seq_lens, k_new, v_new, stream)
         if self.gauss:
@@ -410,10 +419,6 @@ class SparseDecoder:
             return self.out, self.lse
         if self.score_in_decode:
             self.score_select_attend(q, kv_cache, block_table, seq_lens, stream)
-            return self.out, self.lse
-        if self.token_fused:
-            self.accumulate_select_attend(q, kv_cache, block_table, seq_lens, stream)
-            self.merge(stream)
             return self.out, self.lse
         if self.token_level:
             self.accumulate(q, kv_cache, block_table, seq_lens, stream)

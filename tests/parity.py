@@ -77,16 +77,24 @@ def check_group_select_decode_matches(dec, q, cache, bt, sl):
         assert torch.equal(a, b), f"select-in-decode {name} differs from separate launches"
 
 
-def check_token_fused_matches(dec, q, cache, bt, sl, pre_hh):
+def check_token_fused_matches(dec, q, cache, bt, sl, pre_hh, k_new=None, v_new=None,
+                              pre_cache=None):
     """Token level: after the separate launches (h2o_accumulate or its per-head
     form, page_topk_blk, sparse_paged_decode, lse_merge) have filled dec's
     buffers, rerun the step from the same accumulator (pre_hh, the device
     tensor's bytes before the step) through h2o_select_decode and require the
-    same bits: accumulator, score rows, selection, partials, merged output."""
+    same bits: accumulator, score rows, selection, partials, merged output.
+    With k_new / v_new the rerun also does the append (pagestats_update's
+    part of the step): pre_hh and pre_cache are then the tensors before the
+    append, and the cache must come out equal as well."""
     assert dec.token_fused
     names = ("hh", "scores", "sel_idx", "sel_cnt", "sel_blk", "o_part", "lse_part", "out",
              "lse")
     ref = {n: getattr(dec, n).clone() for n in names}
+    ref_cache = None
+    if k_new is not None:
+        ref_cache = cache.clone()
+        cache.copy_(pre_cache)
     dec.hh.copy_(pre_hh)
     for n in ("scores", "o_part", "lse_part", "out", "lse"):
         getattr(dec, n).fill_(float("nan"))
@@ -94,10 +102,12 @@ def check_token_fused_matches(dec, q, cache, bt, sl, pre_hh):
         getattr(dec, n).fill_(-7)
     keep = (dec.keep_selection, dec.keep_scores)
     dec.keep_selection = dec.keep_scores = True
-    dec.accumulate_select_attend(q, cache, bt, sl)
+    dec.accumulate_select_attend(q, cache, bt, sl, k_new, v_new)
     dec.merge()
     dec.keep_selection, dec.keep_scores = keep
     torch.cuda.synchronize()
+    if ref_cache is not None:
+        assert torch.equal(ref_cache, cache), "fused token step: the appended cache differs"
     N = sl.cpu().numpy()
     for n in names:
         a, b = ref[n], getattr(dec, n)

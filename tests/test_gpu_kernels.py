@@ -800,26 +800,29 @@ def test_append_refresh_and_reset(P):
                 wl.seq_lens, P, used)
 
 
-@pytest.mark.parametrize("reading,H_q,H_kv,D", [
-    ("group_mean", 8, 2, 128), ("per_head", 8, 2, 128), ("per_head", 80, 16, 128),
-    ("per_head", 12, 4, 64), ("group_mean", 12, 4, 64),
+@pytest.mark.parametrize("reading,H_q,H_kv,D,eos", [
+    ("group_mean", 8, 2, 128, 8), ("per_head", 8, 2, 128, 8), ("per_head", 80, 16, 128, 8),
+    # no reserved tail: the newest token's logit is taken (from k_new in the
+    # fused step's append)
+    ("group_mean", 8, 2, 128, 0), ("per_head", 12, 4, 64, 0),
+    ("per_head", 12, 4, 64, 8), ("group_mean", 12, 4, 64, 8),
     # G = 16 (every column of the matrix-core tile), one kv head, and three kv
     # heads (rows dealt token-major in the group-mean pass)
-    ("per_head", 16, 1, 64), ("per_head", 48, 3, 128), ("group_mean", 48, 3, 128),
+    ("per_head", 16, 1, 64, 8), ("per_head", 48, 3, 128, 8), ("group_mean", 48, 3, 128, 8),
     # every key-row load depth of the group-mean pass (rows of 4 * H_kv tokens
     # per wave, head-major where H_kv divides 16, else token-major) and every
     # tile count per wave of the per-head pass, at both head sizes
-    ("group_mean", 8, 4, 128), ("group_mean", 12, 6, 128), ("group_mean", 24, 12, 128),
-    ("group_mean", 32, 16, 128), ("group_mean", 6, 3, 64), ("group_mean", 16, 8, 64),
-    ("group_mean", 12, 6, 64), ("group_mean", 20, 10, 64), ("group_mean", 32, 16, 64),
-    ("per_head", 40, 10, 128), ("per_head", 16, 8, 64), ("per_head", 24, 12, 64),
-    ("per_head", 32, 16, 64)])
-def test_token_level_step_teacher_forced(reading, H_q, H_kv, D):
-    say(f"[gpu] h2o small, teacher forced, {reading} H_q {H_q} H_kv {H_kv} D {D}")
+    ("group_mean", 8, 4, 128, 8), ("group_mean", 12, 6, 128, 8), ("group_mean", 24, 12, 128, 8),
+    ("group_mean", 32, 16, 128, 8), ("group_mean", 6, 3, 64, 8), ("group_mean", 16, 8, 64, 8),
+    ("group_mean", 12, 6, 64, 8), ("group_mean", 20, 10, 64, 8), ("group_mean", 32, 16, 64, 8),
+    ("per_head", 40, 10, 128, 8), ("per_head", 16, 8, 64, 8), ("per_head", 24, 12, 64, 8),
+    ("per_head", 32, 16, 64, 8)])
+def test_token_level_step_teacher_forced(reading, H_q, H_kv, D, eos):
+    say(f"[gpu] h2o small, teacher forced, {reading} H_q {H_q} H_kv {H_kv} D {D} eos {eos}")
     S0, B = 300, 3
     wl = W.h2o_token(seed=40, steps=6, prompt=S0, B=B)
     wl.H_q, wl.H_kv, wl.D = H_q, H_kv, D
-    wl.bos, wl.eos, wl.topk_pages, wl.num_splits = 4, 8, 40, 5
+    wl.bos, wl.eos, wl.topk_pages, wl.num_splits = 4, eos, 40, 5
     wl.seq_lens = np.array([S0, S0 - 37, 11], dtype=np.int32)
     cache = dev(W.make_cache(wl))
     bt = dev(wl.block_table)
@@ -835,6 +838,7 @@ def test_token_level_step_teacher_forced(reading, H_q, H_kv, D):
         q = dev(q_cpu)
         kn, vn = W.make_new_kv(wl, step)
         pre_cache, pre_hh = bits(cache).copy(), bits(d.hh).copy()
+        pre_cache_dev, pre_append_hh_dev = cache.clone(), d.hh.clone()
         poison(d)
         d.append(cache, bt, sl, dev(kn), dev(vn))
         torch.cuda.synchronize()
@@ -876,6 +880,9 @@ def test_token_level_step_teacher_forced(reading, H_q, H_kv, D):
                         wl.block_table, sl_np, per, H_q // H_kv, wl.softmax_scale)
         if d.token_fused:
             check_token_fused_matches(d, q, cache, bt, sl, pre_hh_dev)
+            # and with the append inside the first launch
+            check_token_fused_matches(d, q, cache, bt, sl, pre_append_hh_dev, dev(kn),
+                                      dev(vn), pre_cache_dev)
         say(f"  step {step}: hh ulps off max {apart.max()}, "
             f"{int((apart > 0).sum())} of {apart.size}")
 

@@ -244,22 +244,23 @@ def test_h2o_token_sequence(reading):
         q = dev(q_cpu)
         kn, vn = W.make_new_kv(wl, step, device="cuda")
         poison(d)
-        d.append(cache, bt, sl, kn, vn)
-        slots = np.array([wl.block_table[b, int(sl_np[b]) - 1] for b in range(wl.B)])
-        host_cache[0, slots, 0] = bits(kn)
-        host_cache[1, slots, 0] = bits(vn)
-        got = bits(cache.index_select(1, torch.from_numpy(slots).cuda()))
-        assert np.array_equal(got, host_cache[:, slots]), f"step {step}: appended slot"
         pre_hh = bits(d.hh).copy()
-        if d.token_fused:     # the launch form the benchmark times
+        if d.token_fused:     # the launch form the benchmark times, the append inside
             d.keep_selection = d.keep_scores = True
-            d.accumulate_select_attend(q, cache, bt, sl)
+            d.accumulate_select_attend(q, cache, bt, sl, kn, vn)
         else:
+            d.append(cache, bt, sl, kn, vn)
             d.accumulate(q, cache, bt, sl)
             d.select(sl, bt)
             d.attend(q, cache, bt, sl)
         d.merge()
         torch.cuda.synchronize()
+        # the append on the host copies: the new rows, and the zeroed hh slot
+        # the accumulator starts from
+        oracle.append(host_cache, wl.block_table, sl_np, bits(kn), bits(vn), pre_hh)
+        slots = np.array([wl.block_table[b, int(sl_np[b]) - 1] for b in range(wl.B)])
+        got = bits(cache.index_select(1, torch.from_numpy(slots).cuda()))
+        assert np.array_equal(got, host_cache[:, slots]), f"step {step}: appended slot"
         qd = q_cpu.double().numpy()
         hh_ref = pre_hh.copy()
         ref = oracle.h2o_step(qd, host_cache, wl.block_table, sl_np, hh_ref, wl.bos,
