@@ -184,6 +184,11 @@ DECODE_SOURCES = {
                 "sparse_kv_cache_amd/csrc/skv_topk.h"),
     "entmax": ("sparse_kv_cache_amd/csrc/entmax_decode.hip",
                "sparse_kv_cache_amd/csrc/skv_device.h"),
+    # h2o_select_decode: the logits pass and the group kernel
+    "token": ("sparse_kv_cache_amd/csrc/sparse_decode.hip",
+              "sparse_kv_cache_amd/csrc/skv_device.h",
+              "sparse_kv_cache_amd/csrc/skv_topk.h",
+              "sparse_kv_cache_amd/csrc/h2o.hip"),
 }
 
 
@@ -684,7 +689,8 @@ def measure(args, workload, cpu=True):
                                                 "_entmax" if entmax else "")
                                              + ("_alibi" if slopes is not None else "")
                                              + ("_heads" if decs[0].h2o_per_head else ""),
-                                             "entmax" if entmax else "softmax", focus)),
+                                             "entmax" if entmax else
+                                             "token" if token_fused else "softmax", focus)),
                 # the same rate against a plain device copy measured in this run
                 "copy_frac": round(a / copy_gbps, 4) if copy_gbps > 0 else None,
                 "bytes_per_launch": kb[focus],
