@@ -227,6 +227,17 @@ def profiled_traffic(tag, kind="softmax", kernel=None):
 
 # ------------------------------------------------------------ cpu baseline
 
+def compact_request(wl, cache_bits, seq_lens, bb):
+    """Request bb's blocks copied out of the cache bits ([2, NB, P, H_kv, D])
+    in page order, and its block-table row remapped to them: (cache, bt)."""
+    N = min((int(seq_lens[bb]) + wl.P - 1) // wl.P, wl.bt_ld)
+    blocks = wl.block_table[bb, :N]
+    cache_c = np.ascontiguousarray(cache_bits[:, blocks])
+    bt = np.zeros((1, wl.bt_ld), dtype=np.int32)
+    bt[0, :N] = np.arange(N, dtype=np.int32)
+    return cache_c, bt
+
+
 def cpu_baseline(wl, cache_bits, q, seq_lens, seconds, token_level, hh_bits=None,
                  gauss=False, slopes=None, k_cap=0, h2o_per_head=False):
     """The float64 oracle on a bounded sample of requests (whole step for
@@ -241,20 +252,29 @@ def cpu_baseline(wl, cache_bits, q, seq_lens, seconds, token_level, hh_bits=None
     sl64 = None if slopes is None else np.asarray(slopes, np.float32).astype(np.float64)
 
     def prepare(bb):
-        """Per-request inputs built outside the timed region."""
+        """Per-request inputs built outside the timed region: the request's
+        own blocks copied into a compact cache with its block table remapped
+        (the oracle's statistics are sized by the cache it is given, so the
+        whole pool would cost gigabytes per request), and its statistics."""
         if token_level or bb in st_cache:
             return
-        bt, sl = wl.block_table[bb:bb + 1], seq_lens[bb:bb + 1]
+        sl = seq_lens[bb:bb + 1]
+        cache_c, bt = compact_request(wl, cache_bits, seq_lens, bb)
         if gauss:
-            st_cache[bb] = (oracle.page_stats(cache_bits, bt, sl, wl.P)[2],
-                            oracle.page_var(cache_bits, bt, sl, wl.P))
+            st = (oracle.page_stats(cache_c, bt, sl, wl.P)[2],
+                  oracle.page_var(cache_c, bt, sl, wl.P))
         else:
-            st_cache[bb] = oracle.page_stats(cache_bits, bt, sl, wl.P)
+            st = oracle.page_stats(cache_c, bt, sl, wl.P)
+        st_cache[bb] = (cache_c, bt, st)
 
     def request_step(bb):
         """One request's whole step through the oracle."""
-        bt, sl = wl.block_table[bb:bb + 1], seq_lens[bb:bb + 1]
+        sl = seq_lens[bb:bb + 1]
         S = int(sl[0])
+        if token_level:
+            bt = wl.block_table[bb:bb + 1]
+        else:
+            cache_c, bt, st = st_cache[bb]
         if token_level:
             hh = hh_bits.copy()
             sc = oracle.h2o_step(qd[bb:bb + 1], cache_bits, bt, sl, hh, wl.bos,
@@ -268,19 +288,19 @@ def cpu_baseline(wl, cache_bits, q, seq_lens, seconds, token_level, hh_bits=None
         elif gauss:
             N = (S + wl.P - 1) // wl.P
             n = np.array([min(wl.P, S - p * wl.P) for p in range(N)], dtype=np.int32)
-            mu, var = oracle.gauss_moments(qd[bb:bb + 1], *st_cache[bb], bt, sl, wl.P,
+            mu, var = oracle.gauss_moments(qd[bb:bb + 1], *st, bt, sl, wl.P,
                                            wl.softmax_scale, alibi=sl64)
             for i in range(wl.H_q):
                 tau = oracle.gauss_tau(mu[0, i, :N], var[0, i, :N], n, sl64 is not None)
                 sel = oracle.gauss_select(mu[0, i, :N], var[0, i, :N], n, tau, wl.bos,
                                           wl.eos, k_cap)
-                oracle.attend_entmax15(qd[bb, i], cache_bits, i // wl.G, bt[0], S, sel,
+                oracle.attend_entmax15(qd[bb, i], cache_c, i // wl.G, bt[0], S, sel,
                                        wl.softmax_scale,
                                        slope=None if sl64 is None else sl64[i])
         else:
             kc = min(max(wl.topk_pages, int(math.floor(wl.topk_frac * wl.bt_ld)),
                          wl.bos + wl.eos), wl.bt_ld)
-            oracle.decode_step(qd[bb:bb + 1], cache_bits, bt, sl, st_cache[bb], wl.w_avg,
+            oracle.decode_step(qd[bb:bb + 1], cache_c, bt, sl, st, wl.w_avg,
                                wl.w_peak, wl.topk_pages, wl.topk_frac, wl.bos, wl.eos,
                                wl.softmax_scale, kc)
 

@@ -74,3 +74,31 @@ def test_counter_records_are_gated_by_kernel_and_source_hash(monkeypatch):
     assert bench.profiled_traffic("no_such_workload") is None
     monkeypatch.setattr(bench, "decode_source_hash", lambda kind="softmax": "0" * 40)
     assert bench.profiled_traffic("gqa_ragged", "softmax", rec["kernel"]) is None
+
+
+def test_cpu_baseline_request_copy_gives_the_same_step():
+    """The oracle baseline runs each sampled request on a compact copy of its
+    own blocks: the step's output must equal the step over the whole pool."""
+    import oracle
+    wl = W.small_case(seed=5, B=3, H_q=4, H_kv=2, D=64, P=16, max_pages=6,
+                      num_blocks=200, topk_pages=3)
+    rng = np.random.default_rng(1)
+    cache = rng.integers(0x3c00, 0x4100, size=(2, wl.num_blocks, wl.P, wl.H_kv, wl.D),
+                         dtype=np.uint16)
+    q = rng.standard_normal((wl.B, wl.H_q, wl.D))
+    kc = min(max(wl.topk_pages, wl.bos + wl.eos), wl.bt_ld)
+    for bb in range(wl.B):
+        sl = wl.seq_lens[bb:bb + 1]
+        bt = wl.block_table[bb:bb + 1]
+        full = oracle.decode_step(q[bb:bb + 1], cache, bt, sl,
+                                  oracle.page_stats(cache, bt, sl, wl.P), wl.w_avg,
+                                  wl.w_peak, wl.topk_pages, 0.0, wl.bos, wl.eos,
+                                  wl.softmax_scale, kc)
+        cc, bc = bench.compact_request(wl, cache, wl.seq_lens, bb)
+        assert cc.shape[1] == (int(sl[0]) + wl.P - 1) // wl.P
+        part = oracle.decode_step(q[bb:bb + 1], cc, bc, sl, oracle.page_stats(cc, bc, sl, wl.P),
+                                  wl.w_avg, wl.w_peak, wl.topk_pages, 0.0, wl.bos, wl.eos,
+                                  wl.softmax_scale, kc)
+        for a, b in zip(full, part):
+            assert np.array_equal(np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64),
+                                  equal_nan=True)
