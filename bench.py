@@ -30,10 +30,10 @@ The roofline entry also places the decode kernel against two references of
 the library that carry no arithmetic, timed the same way in the same run:
 the streaming read of the kernel's byte count (stream_ref / stream_frac) and
 the gather-only read of the decode's own page-heads (gather_ref /
-gather_frac).  Unless --no-north-star (or --workload long_context), the line
-also carries a "north_star" record: the long-context workload's step rate and
-its decode kernel's time, bytes, fraction of peak, counter traffic and
-references.
+gather_frac).  Unless --no-long-context (or --workload long_context), the
+line also carries a "long_context" record: the long-context workload's step
+rate (one request of 131,072 tokens, 64 query heads) and its decode kernel's
+time, bytes, fraction of peak, counter traffic and references.
 """
 from __future__ import annotations
 
@@ -77,7 +77,7 @@ def parse():
                     help="keep page_topk and lse_merge as their own launches even "
                          "where the decode can select and merge in-block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-north-star", action="store_true",
+    ap.add_argument("--no-long-context", action="store_true",
                     help="skip the long_context sub-record that the default run adds")
     ap.add_argument("--no-graph", action="store_true",
                     help="enqueue kernel by kernel instead of replaying HIP graphs")
@@ -438,7 +438,7 @@ def main():
     sparse_kv_cache_amd.load_library()
     torch.cuda.init()
     result = measure(args, args.workload, cpu=not args.no_cpu_baseline)
-    if args.workload != "long_context" and not args.no_north_star:
+    if args.workload != "long_context" and not args.no_long_context:
         import copy
         torch.cuda.empty_cache()
         a2 = copy.copy(args)
@@ -447,7 +447,7 @@ def main():
         a2.steps, a2.repeats = min(args.steps, 50), 0
         ns = measure(a2, "long_context", cpu=False)
         rf = ns["roofline"]
-        result["north_star"] = {
+        result["long_context"] = {
             "workload": "long_context", "steps_per_s": ns["value"],
             "gpu_ms_per_step": ns["gpu_ms_per_step"], "launches": len(ns["kernels"]),
             "kernel": rf["kernel"], "us_per_launch": rf["us_per_launch"],

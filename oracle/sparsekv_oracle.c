@@ -28,7 +28,12 @@
  *   - everything is float64; bf16 values are decoded exactly.
  *
  * Parity pins: every function below is pinned by a test against closed forms,
- * invariants, brute force or printed values; none is "parity unpinned".
+ * invariants, brute force or printed values, with one exception in kind:
+ * the Gaussian-aware selection's estimated-maximum rule (est = mu +
+ * sigma * sqrt(2 ln n), a page kept when est / 2 > tau-hat) is a reading of
+ * [EKV "How it works"], which names an estimated maximum but prints no
+ * formula.  Its tests (brute force, limit cases) pin this code to that
+ * reading; against the pages the rule is "parity unpinned".
  */
 #include <math.h>
 #include <stdint.h>
