@@ -947,6 +947,52 @@ def test_graph_replays_match_eager(mode):
 
 
 @pytest.mark.parametrize("reading", ["group_mean", "per_head"])
+def test_token_fused_append_past_the_table_writes_nothing(reading):
+    """h2o_select_decode given k_new / v_new: a request whose new token lies
+    past its block-table row (S - 1 >= bt_ld) appends nothing, as
+    pagestats_update does; the others append. The step equals
+    pagestats_update followed by the call without k_new, bit for bit."""
+    say(f"[gpu] token-level append inside the first launch, row past the table, {reading}")
+    S0, B = 300, 3
+    wl = W.h2o_token(seed=43, steps=2, prompt=S0, B=B)
+    wl.H_q, wl.H_kv, wl.D = 8, 2, 128
+    wl.bos, wl.eos, wl.topk_pages, wl.num_splits = 2, 0, 40, 4
+    wl.seq_lens = np.array([S0, wl.bt_ld + 1, 11], dtype=np.int32)
+    d = SparseDecoder(B, wl.H_q, wl.H_kv, wl.D, wl.num_blocks, 1, wl.bt_ld,
+                      topk_pages=wl.topk_pages, bos=wl.bos, eos=wl.eos,
+                      scale=wl.softmax_scale, num_splits=wl.num_splits,
+                      token_level=True, h2o_softmax=reading)
+    assert d.token_fused
+    hh0 = W.make_hh(wl).cuda()
+    cache0 = dev(W.make_cache(wl))
+    bt, sl = dev(wl.block_table), dev(wl.seq_lens)
+    q = dev(W.make_queries(wl, 0))
+    kn, vn = (dev(t) for t in W.make_new_kv(wl, 0))
+    cache_a = cache0.clone()
+    d.hh.copy_(hh0)
+    d.append(cache_a, bt, sl, kn, vn)
+    d.accumulate_select_attend(q, cache_a, bt, sl)
+    d.merge()
+    torch.cuda.synchronize()
+    ref = (d.hh.clone(), d.out.clone(), d.lse.clone())
+    cache_b = cache0.clone()
+    d.hh.copy_(hh0)
+    d.out.fill_(float("nan"))
+    d.accumulate_select_attend(q, cache_b, bt, sl, kn, vn)
+    d.merge()
+    torch.cuda.synchronize()
+    assert torch.equal(cache_a, cache_b), "appended cache differs"
+    for name, a, b in zip(("hh", "out", "lse"), ref, (d.hh, d.out, d.lse)):
+        assert torch.equal(a, b), f"{name} differs from append + separate call"
+    # only requests 0 and 2 wrote a row
+    written = [int(wl.block_table[b, int(wl.seq_lens[b]) - 1]) for b in (0, 2)]
+    keep = torch.ones(cache0.shape[1], dtype=torch.bool, device="cuda")
+    keep[written] = False
+    assert torch.equal(cache_b[:, keep], cache0[:, keep]), "a row was written past the table"
+    assert not torch.equal(cache_b[:, written], cache0[:, written])
+
+
+@pytest.mark.parametrize("reading", ["group_mean", "per_head"])
 def test_token_level_graph_replays_match_eager(reading):
     """The token-level step (accumulate, select, attend, merge) captured in a
     graph: from the same hh, every replay must give the eager step's output,
