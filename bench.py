@@ -5,7 +5,9 @@ One step = one pass of the whole hot path over the batch:
   page level (default gqa_ragged, also mha_tiny / long_context):
       page_score -> page_topk -> sparse_paged_decode -> lse_merge
       (with one selection per query head and at most 8 splits the merge runs
-      inside the decode launch: sparse_paged_decode_merged)
+      inside the decode launch: sparse_paged_decode_merged; with more splits
+      the selection runs inside the split decode, sparse_select_decode_split,
+      and lse_merge follows)
       (statistics built once beforehand, timed separately)
   high_batch: pagestats_update (append + refresh) -> the four above
   h2o_token:  pagestats_update (append + reset) -> h2o_accumulate ->
@@ -457,7 +459,7 @@ def main():
                               round(rf["traffic"] / rf["bytes_per_launch"], 3)),
             "stream_ref": rf.get("stream_ref"), "stream_frac": rf.get("stream_frac"),
             "gather_ref": rf.get("gather_ref"), "gather_frac": rf.get("gather_frac"),
-            "kernels": ns["kernels"]}
+            "decode_alone": rf.get("decode_alone"), "kernels": ns["kernels"]}
     print(json.dumps(result), flush=True)
     return 0
 
@@ -497,6 +499,7 @@ def measure(args, workload, cpu=True):
     fused = decs[0].fused or decs[0].entmax_fused
     in_decode = decs[0].select_in_decode
     in_group_decode = decs[0].select_in_group_decode and not gauss and not token_level
+    in_split_decode = decs[0].select_in_split_decode
     token_fused = decs[0].token_fused
     one_launch = decs[0].score_in_decode
     new_kv = [W.make_new_kv(wl, s, device=dev) for s in range(min(wl.steps, 64))] \
@@ -546,6 +549,7 @@ def measure(args, workload, cpu=True):
              (["h2o_accumulate"] if token_level else [] if one_launch else ["page_score"]) +
             (["sparse_page_decode"] if one_launch else ["sparse_select_decode"] if in_decode
              else ["sparse_select_decode_group", "lse_merge"] if in_group_decode
+             else ["sparse_select_decode_split", "lse_merge"] if in_split_decode
              else ["page_topk", "sparse_paged_decode"] + ([] if fused else ["lse_merge"])))
 
     def enqueue(i, name):
@@ -576,6 +580,8 @@ def measure(args, workload, cpu=True):
             d.select_attend(q, c, bt, sl)
         elif name == "sparse_select_decode_group":
             d.select_attend_group(q, c, bt, sl)
+        elif name == "sparse_select_decode_split":
+            d.select_attend_split(q, c, bt, sl)
         elif name == "sparse_page_decode":
             d.score_select_attend(q, c, bt, sl)
         else:
@@ -641,7 +647,7 @@ def measure(args, workload, cpu=True):
         d.accumulate_select_attend(q, caches[last % R], bt, seq_steps[last % wl.steps])
         d.keep_selection = False
         torch.cuda.synchronize()
-    elif in_decode or in_group_decode:   # the selection stays in LDS; recompute it
+    elif in_decode or in_group_decode or in_split_decode:   # selection in LDS: recompute it
         if one_launch:
             d.score(q, bt, seq_steps[last % wl.steps])
         d.select(seq_steps[last % wl.steps], bt)
@@ -686,9 +692,9 @@ def measure(args, workload, cpu=True):
         kb.pop("page_topk")
         if "pagestats_update" in kb:   # the append, less its table reads (counted once)
             kb["h2o_select_decode"] += kb.pop("pagestats_update") - wl.B * 8
-    elif in_group_decode:   # the top-k's score read plus the decode's partials
-        kb["sparse_select_decode_group"] = kb.pop("page_topk") - int(sel_cnt.sum()) * 4 \
-            + kb.pop("sparse_paged_decode")
+    elif in_group_decode or in_split_decode:   # the top-k's score read plus the decode
+        name = "sparse_select_decode_group" if in_group_decode else "sparse_select_decode_split"
+        kb[name] = kb.pop("page_topk") - int(sel_cnt.sum()) * 4 + kb.pop("sparse_paged_decode")
     step_bytes = sum(kb.values())
     kern = {}
     for n in names:
@@ -699,6 +705,7 @@ def measure(args, workload, cpu=True):
     focus = ("sparse_page_decode" if one_launch else
              "sparse_select_decode" if in_decode else
              "sparse_select_decode_group" if in_group_decode else
+             "sparse_select_decode_split" if in_split_decode else
              "h2o_select_decode" if token_fused else "sparse_paged_decode")
     a = kb[focus] / (per_kernel_ms[focus] * 1e-3) / 1e9
     roofline = {"kernel": focus, "bound": "hbm", "achieved": round(a, 1),
@@ -727,6 +734,37 @@ def measure(args, workload, cpu=True):
     if "gather" in refs:
         roofline["gather_ref"] = refs["gather"]
         roofline["gather_frac"] = round(a / refs["gather"]["GBps"], 4)
+    # Where the step's decode runs inside a fused launch (selection, scoring
+    # or both in the same kernel), the decode kernel is also timed on its own
+    # over the same selection, the same way: its rate is the decode's, not
+    # the fused launch's.
+    if (focus != "sparse_paged_decode" and wl.steps == 1 and not token_level
+            and not gauss and not entmax):
+        for r in range(R):
+            decs[r].score(q, bt, seq_steps[0])
+            decs[r].select(seq_steps[0], bt)
+        torch.cuda.synchronize()
+        g = captured(lambda: [decs[(base + j) % R].attend(q, caches[(base + j) % R], bt,
+                                                          seq_steps[0])
+                              for j in range(reps)])
+        g.replay()
+        k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        k0.record()
+        g.replay()
+        k1.record()
+        torch.cuda.synchronize()
+        dms = k0.elapsed_time(k1) / reps
+        del g
+        kb0, _ = kernel_bytes(wl, sel_idx, sel_cnt, sl_last, decs[0].decode_splits,
+                              token_level, group, fused, entmax, gauss)
+        da = kb0["sparse_paged_decode"] / (dms * 1e-3) / 1e9
+        roofline["decode_alone"] = {
+            "kernel": "sparse_paged_decode_merged" if fused else "sparse_paged_decode",
+            "us": round(dms * 1000, 2), "bytes": kb0["sparse_paged_decode"],
+            "achieved": round(da, 1), "frac": round(da / PEAK_HBM_GBPS, 4),
+            "gather_frac": (round(da / refs["gather"]["GBps"], 4) if "gather" in refs
+                            else None)}
 
     result = {
         "metric": "sparse decode steps/s + effective HBM GB/s (% of peak), GQA 32/8 D=128",
@@ -746,7 +784,8 @@ def measure(args, workload, cpu=True):
                    "gauss_tau": (None if not gauss else
                                  "page_mixture" if decs[0].mixture else "single"),
                    "alibi": slopes is not None, "merge_in_decode": fused,
-                   "select_in_decode": in_decode or in_group_decode or token_fused,
+                   "select_in_decode": (in_decode or in_group_decode or in_split_decode
+                                        or token_fused),
                    "one_launch_step": one_launch,
                    "attention": "entmax15" if entmax else "softmax",
                    "h2o_softmax": args.h2o_softmax if token_level else None,

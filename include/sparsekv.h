@@ -306,6 +306,42 @@ int sparse_select_decode(const float *scores, int64_t score_ld, int topk_pages,
                          int32_t *sel_blk, hipStream_t stream);
 
 /*
+ * sparse_select_decode_split -- page_topk and sparse_paged_decode in one
+ * launch for one selection per query head (H_sel = H_q) at any split count:
+ * the split partials go to lse_merge.  One 16-wave block per (query head,
+ * group of 16 splits) first selects its head's row from the scores into LDS
+ * (the top-k of page_topk; the blocks of a head derive the same selection),
+ * then each wave attends over one split's chunk of it.  This is
+ * sparse_select_decode without its in-block merge, for rows with more than
+ * 8 splits or up to 8192 entries.  [Same sources as page_topk and
+ * sparse_paged_decode; EKV "How it works": top-k pages per query head.]
+ *
+ *   scores   fp32 [B, H_q, score_ld] (page_score's output), score_ld <= 8192
+ *   topk_pages, topk_frac, reserved_bos, reserved_eos, k_cap: as page_topk
+ *            (k_cap <= 4096)
+ *   q ... seq_lens, scale, num_splits (<= 4096), alibi_slopes: as
+ *            sparse_paged_decode_ex with H_sel = H_q (split s of a row holds
+ *            the selected entries [s c, min((s + 1) c, cnt)),
+ *            c = ceil(k_cap / num_splits))
+ *   o_part   fp32 [B, H_q, num_splits, D], lse_part fp32 [B, H_q, num_splits]:
+ *            exactly what sparse_paged_decode writes for that selection
+ *   sel_idx, sel_cnt (both or neither), sel_blk (needs sel_idx):
+ *            [B, H_q, k_cap] / [B, H_q]; when given, receive the selection
+ *            exactly as page_topk_blk writes it.
+ *   Errors as sparse_paged_decode.
+ */
+int sparse_select_decode_split(const float *scores, int64_t score_ld, int topk_pages,
+                               float topk_frac, int reserved_bos, int reserved_eos,
+                               const float *q, int B, int H_q, int H_kv, int D,
+                               const uint16_t *kv_cache, int64_t num_blocks,
+                               int page_size, const int32_t *block_table,
+                               int64_t bt_ld, const int32_t *seq_lens, int k_cap,
+                               float scale, int num_splits,
+                               const float *alibi_slopes, float *o_part,
+                               float *lse_part, int32_t *sel_idx, int32_t *sel_cnt,
+                               int32_t *sel_blk, hipStream_t stream);
+
+/*
  * sparse_select_decode_group -- page_topk and sparse_paged_decode in one
  * launch for a selection shared by each kv head's query group (H_sel = H_kv:
  * the token-level flow, page_score_group).  One block per (split, kv head,

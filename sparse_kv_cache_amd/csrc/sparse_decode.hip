@@ -230,8 +230,7 @@ void sparse_decode_wave_kernel(
     float* __restrict__ lse_part, int64_t n_groups, int blocks_per_group,
     const float* __restrict__ alibi, float* __restrict__ out,
     float* __restrict__ lse_out, TopkArgs ta) {
-  static_assert(TKI == 0 || FUSE, "in-block selection merges in-block");
-  static_assert(!SC || TKI > 0, "in-block scoring selects in-block");
+  static_assert(!SC || (TKI > 0 && FUSE), "in-block scoring selects and merges in-block");
   constexpr int LPR = D / 8;
   constexpr int RPL = 64 / LPR;
   constexpr int NL = 16 / RPL;
@@ -244,11 +243,15 @@ void sparse_decode_wave_kernel(
   const int64_t k = blockIdx.x / kXcds;
   const int64_t grp_bh = xcd + kXcds * (k / blocks_per_group);
   const int local = static_cast<int>(k % blocks_per_group) * WB + wave;
-  // (FUSE: whole blocks return together; waves past num_splits stay for the
-  // block merge with an empty chunk)
-  if (grp_bh >= n_groups || (!FUSE && local >= num_splits * G)) return;
-  const int g = FUSE ? static_cast<int>(k % blocks_per_group) : local % G;
-  const int s = FUSE ? wave : local / G;
+  // In-block selection (TKI > 0): a block serves one query head, its waves
+  // consecutive splits; a head's splits take blocks_per_group / G blocks
+  // (one with FUSE).  Whole blocks return together; waves past num_splits
+  // stay for the selection's barriers (and FUSE's merge) with an empty chunk.
+  if (grp_bh >= n_groups || (!FUSE && TKI == 0 && local >= num_splits * G)) return;
+  const int nsg = TKI > 0 ? blocks_per_group / G : 1;   // blocks per query head
+  const int kb = static_cast<int>(k % blocks_per_group);
+  const int g = TKI > 0 ? kb / nsg : FUSE ? kb : local % G;
+  const int s = TKI > 0 ? (kb % nsg) * WB + wave : FUSE ? wave : local / G;
   const int h = static_cast<int>(grp_bh % H_kv);
   const int b = static_cast<int>(grp_bh / H_kv);
   const int64_t qrow = static_cast<int64_t>(b) * H_q + h * G + g;
@@ -365,7 +368,7 @@ void sparse_decode_wave_kernel(
         ta.topk_frac, ta.bos, ta.eos, bt + static_cast<int64_t>(b) * bt_ld, bt_ld,
         sel_lds, sel_lds + k_cap, k_cap);
     }
-    if (ta.sel_idx != nullptr) {
+    if (ta.sel_idx != nullptr && kb % nsg == 0) {
       for (int j = threadIdx.x; j < k_cap; j += WB * 64) {
         ta.sel_idx[qrow * k_cap + j] = sel_lds[j];
         if (ta.sel_blk != nullptr) ta.sel_blk[qrow * k_cap + j] = sel_lds[k_cap + j];
@@ -532,6 +535,7 @@ void sparse_decode_wave_kernel(
     }
     if (o_part == nullptr || s >= num_splits) return;
   }
+  if (TKI > 0 && s >= num_splits) return;
   const int64_t prow = qrow * num_splits + s;
   if (slot == 0) {
     float4* dst = reinterpret_cast<float4*>(o_part + prow * D + c * 8);
@@ -1045,6 +1049,24 @@ void launch_wave_fused(hipStream_t st, const Args& a, int64_t n_groups, float* o
                      out, lse_out, ta);
 }
 
+// In-block selection with split partials: one kSplitWaves-wave block per
+// (query head, group of kSplitWaves splits), each selecting its head's row.
+constexpr int kSplitWaves = 16;
+
+template <int D, int PFIX, bool AL, int TKI>
+void launch_wave_split(hipStream_t st, const Args& a, int64_t n_groups, const TopkArgs& ta) {
+  const int nsg = (a.num_splits + kSplitWaves - 1) / kSplitWaves;
+  const int per_group = a.G * nsg;
+  const int64_t blocks = kXcds * per_group * ((n_groups + kXcds - 1) / kXcds);
+  const size_t lds = sizeof(int32_t) * 2 * static_cast<size_t>(a.k_cap);
+  hipLaunchKernelGGL((sparse_decode_wave_kernel<D, kSplitWaves, PFIX, AL, false, TKI>),
+                     dim3(static_cast<unsigned>(blocks)), dim3(kSplitWaves * 64), lds, st,
+                     a.q, a.H_q, a.H_kv, a.G, a.kv, a.num_blocks, a.P, a.bt, a.bt_ld,
+                     a.seq_lens, a.sel_idx, a.sel_cnt, a.sel_blk, a.k_cap, a.scale_log2,
+                     a.num_splits, a.o_part, a.lse_part, n_groups, per_group, a.alibi,
+                     nullptr, nullptr, ta);
+}
+
 template <int D, bool AL, int TKI = 0, int H2O = 0, int NWV = 4>
 void launch_group(dim3 grid, hipStream_t st, const Args& a, const TopkArgs& ta = TopkArgs{}) {
   const size_t lds = TKI > 0 ? sizeof(int32_t) * static_cast<size_t>(a.k_cap) : 0;
@@ -1360,6 +1382,92 @@ extern "C" int sparse_page_decode(const float* q, int B, int H_q, int H_kv, int 
   }
 #undef SKV_SC_T
 #undef SKV_SC
+  SKV_CHECK_LAUNCH();
+}
+
+extern "C" int sparse_select_decode_split(const float* scores, int64_t score_ld,
+                                          int topk_pages, float topk_frac, int reserved_bos,
+                                          int reserved_eos, const float* q, int B, int H_q,
+                                          int H_kv, int D, const uint16_t* kv_cache,
+                                          int64_t num_blocks, int page_size,
+                                          const int32_t* block_table, int64_t bt_ld,
+                                          const int32_t* seq_lens, int k_cap, float scale,
+                                          int num_splits, const float* alibi_slopes,
+                                          float* o_part, float* lse_part, int32_t* sel_idx,
+                                          int32_t* sel_cnt, int32_t* sel_blk,
+                                          hipStream_t stream) {
+  const char* who = "sparse_select_decode_split";
+  SKV_REQUIRE(B >= 0 && H_kv > 0 && H_q > 0 && H_q % H_kv == 0,
+              "%s: need H_q a positive multiple of H_kv", who);
+  const int G = H_q / H_kv;
+  SKV_REQUIRE(G <= 16, "%s: group size %d > 16", who, G);
+  SKV_REQUIRE(D == 64 || D == 128, "%s: D must be 64 or 128 (got %d)", who, D);
+  SKV_REQUIRE(skv_supported_page_size(page_size),
+              "%s: page_size must be 1, 2, 4, 8 or 16 (got %d)", who, page_size);
+  SKV_REQUIRE(num_splits >= 1 && num_splits <= 4096,
+              "%s: num_splits must be in [1, 4096] (got %d)", who, num_splits);
+  SKV_REQUIRE(score_ld > 0 && score_ld <= 8 * kSplitWaves * 64,
+              "%s: score_ld must be in [1, %d] (got %lld)", who, 8 * kSplitWaves * 64,
+              (long long)score_ld);
+  SKV_REQUIRE(topk_pages >= 1, "%s: topk_pages must be >= 1 (got %d)", who, topk_pages);
+  SKV_REQUIRE(topk_frac >= 0.0f && topk_frac <= 1.0f, "%s: topk_frac must be in [0, 1]", who);
+  SKV_REQUIRE(reserved_bos >= 0 && reserved_eos >= 0,
+              "%s: reserved_bos / reserved_eos must be >= 0", who);
+  SKV_REQUIRE(num_blocks > 0 && num_blocks <= 0x7fffffffLL && bt_ld > 0,
+              "%s: need 0 < num_blocks < 2^31 and bt_ld > 0", who);
+  const double frac = static_cast<double>(topk_frac);
+  int64_t need = topk_pages;
+  const int64_t fk = static_cast<int64_t>(floor(frac * static_cast<double>(score_ld)));
+  if (fk > need) need = fk;
+  if (static_cast<int64_t>(reserved_bos) + reserved_eos > need)
+    need = static_cast<int64_t>(reserved_bos) + reserved_eos;
+  if (need > score_ld) need = score_ld;
+  SKV_REQUIRE(k_cap >= need && k_cap <= 4096,
+              "%s: k_cap %d must cover the largest selection %lld (and be <= 4096)", who,
+              k_cap, (long long)need);
+  const int64_t n_groups = static_cast<int64_t>(B) * H_kv;
+  const int64_t nsg = (num_splits + kSplitWaves - 1) / kSplitWaves;
+  SKV_REQUIRE(B <= 65535 && G * nsg * (n_groups + kXcds) < 0x7fffffffLL,
+              "%s: grid too large", who);
+  // no rows: nothing is read or written, so no pointer is needed
+  if (B == 0) { skv::clear_error(); return SKV_OK; }
+  SKV_REQUIRE_PTR_W(who, scores);
+  SKV_REQUIRE_PTR_W(who, q);
+  SKV_REQUIRE_PTR_W(who, kv_cache);
+  SKV_REQUIRE_PTR_W(who, block_table);
+  SKV_REQUIRE_PTR_W(who, seq_lens);
+  SKV_REQUIRE_PTR_W(who, o_part);
+  SKV_REQUIRE_PTR_W(who, lse_part);
+  SKV_REQUIRE((sel_idx == nullptr) == (sel_cnt == nullptr),
+              "%s: sel_idx and sel_cnt must both be given or both be NULL", who);
+  SKV_REQUIRE(sel_blk == nullptr || sel_idx != nullptr, "%s: sel_blk needs sel_idx", who);
+  const Args a{q, H_q, H_kv, G, kv_cache, num_blocks, page_size, block_table, bt_ld,
+               seq_lens, nullptr, nullptr, nullptr, k_cap, scale * skv::kLog2e, num_splits,
+               o_part, lse_part, alibi_slopes};
+  const TopkArgs ta{scores, score_ld, topk_pages, frac, reserved_bos, reserved_eos,
+                    sel_idx, sel_cnt, sel_blk};
+  const bool al = alibi_slopes != nullptr;
+  // entries per thread of the 1024-thread selection
+  const int tki = score_ld <= 1024 ? 1 : score_ld <= 2048 ? 2 : score_ld <= 4096 ? 4 : 8;
+#define SKV_SPL(DD, PP, TT)                                                          \
+  do {                                                                               \
+    if (al) launch_wave_split<DD, PP, true, TT>(stream, a, n_groups, ta);            \
+    else launch_wave_split<DD, PP, false, TT>(stream, a, n_groups, ta);              \
+  } while (0)
+#define SKV_SPL_T(DD, PP)                                                            \
+  do {                                                                               \
+    if (tki == 1) SKV_SPL(DD, PP, 1);                                                \
+    else if (tki == 2) SKV_SPL(DD, PP, 2);                                           \
+    else if (tki == 4) SKV_SPL(DD, PP, 4);                                           \
+    else SKV_SPL(DD, PP, 8);                                                         \
+  } while (0)
+  if (page_size == 16) {
+    if (D == 128) SKV_SPL_T(128, 16); else SKV_SPL_T(64, 16);
+  } else {
+    if (D == 128) SKV_SPL_T(128, 0); else SKV_SPL_T(64, 0);
+  }
+#undef SKV_SPL_T
+#undef SKV_SPL
   SKV_CHECK_LAUNCH();
 }
 

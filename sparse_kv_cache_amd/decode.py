@@ -24,6 +24,8 @@ selection too when rows fit (sparse_select_decode, after page_score), and up
 to ONE_LAUNCH_ROWS query rows the whole page-level step is one launch
 (sparse_page_decode).  Past that row count scoring stays a launch of its own,
 since it reads each kv head's statistics once for the whole query group.
+With more splits (rows of up to 8192 pages) the selection runs inside the
+split decode (sparse_select_decode_split) and lse_merge follows.
 
 This mirrors the decode call of the EntmaxKV README ("Quick start": score,
 select, attend and append in one call) cut at kernel granularity.  Nothing
@@ -43,7 +45,7 @@ from . import (entmax15_paged_decode, entmax15_paged_decode_merged, entmax_scrat
                page_score_group, page_topk, page_topk_blk, page_var_update,
                pagestats_update, sparse_page_decode, sparse_paged_decode,
                sparse_paged_decode_ex, sparse_paged_decode_merged, sparse_select_decode,
-               sparse_select_decode_group)
+               sparse_select_decode_group, sparse_select_decode_split)
 
 
 def alibi_slopes(H, device="cuda"):
@@ -202,6 +204,13 @@ class SparseDecoder:
         # token level: the accumulator update, the selection and the decode in
         # two launches (h2o_select_decode), then lse_merge
         self.token_fused = token_level and self.select_in_group_decode
+        # one selection per query head with more splits than a block merges:
+        # the selection inside the split decode (each block of a head derives
+        # it), partials merged by lse_merge
+        self.select_in_split_decode = (bool(fuse_merge) and self.H_sel == H_q
+                                       and not self.fused and attention == "softmax"
+                                       and selection == "topk" and bt_ld <= 8192
+                                       and self.k_cap <= 4096)
         self.keep_selection = False
         # and scoring too: the whole page-level step in one launch, while the
         # device holds every block of it at once (two 8-wave blocks per CU,
@@ -366,6 +375,17 @@ class SparseDecoder:
             sel_idx=self.sel_idx if keep else None, sel_cnt=self.sel_cnt if keep else None,
             sel_blk=self.sel_blk if keep else None, alibi_slopes=self.alibi, stream=stream)
 
+    def select_attend_split(self, q, kv_cache, block_table, seq_lens, stream=None):
+        """Selection (per query head) and the split decode in one launch
+        (select_in_split_decode); the partials go through merge()."""
+        keep = self.keep_selection
+        sparse_select_decode_split(
+            self.scores, q, kv_cache, block_table, seq_lens, self.topk_pages, self.k_cap,
+            self.scale, self.o_part, self.lse_part, topk_frac=self.topk_frac,
+            reserved_bos=self.bos, reserved_eos=self.eos,
+            sel_idx=self.sel_idx if keep else None, sel_cnt=self.sel_cnt if keep else None,
+            sel_blk=self.sel_blk if keep else None, alibi_slopes=self.alibi, stream=stream)
+
     def accumulate_select_attend(self, q, kv_cache, block_table, seq_lens, k_new=None,
                                  v_new=None, stream=None):
         """Token level (token_fused): the append (when k_new is given),
@@ -429,6 +449,10 @@ class SparseDecoder:
             return self.out, self.lse
         if self.select_in_group_decode:
             self.select_attend_group(q, kv_cache, block_table, seq_lens, stream)
+            self.merge(stream)
+            return self.out, self.lse
+        if self.select_in_split_decode:
+            self.select_attend_split(q, kv_cache, block_table, seq_lens, stream)
             self.merge(stream)
             return self.out, self.lse
         self.select(seq_lens, block_table, stream)

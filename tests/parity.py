@@ -77,6 +77,31 @@ def check_group_select_decode_matches(dec, q, cache, bt, sl):
         assert torch.equal(a, b), f"select-in-decode {name} differs from separate launches"
 
 
+def check_split_select_decode_matches(dec, q, cache, bt, sl):
+    """With one selection per query head and more splits than a block merges,
+    the one-launch form (selection inside the split decode) must give exactly
+    the bits the separate page_topk + sparse_paged_decode + lse_merge launches
+    just wrote into dec's buffers: selection, block ids, partials, merged
+    output."""
+    assert dec.select_in_split_decode
+    ref = [t.clone() for t in (dec.sel_idx, dec.sel_cnt, dec.sel_blk, dec.o_part,
+                               dec.lse_part, dec.out, dec.lse)]
+    for t in (dec.o_part, dec.lse_part, dec.out, dec.lse):
+        t.fill_(float("nan"))
+    for t in (dec.sel_idx, dec.sel_cnt, dec.sel_blk):
+        t.fill_(-7)
+    keep = dec.keep_selection
+    dec.keep_selection = True
+    dec.select_attend_split(q, cache, bt, sl)
+    dec.merge()
+    dec.keep_selection = keep
+    torch.cuda.synchronize()
+    names = ("sel_idx", "sel_cnt", "sel_blk", "o_part", "lse_part", "out", "lse")
+    for name, a, b in zip(names, ref, (dec.sel_idx, dec.sel_cnt, dec.sel_blk, dec.o_part,
+                                       dec.lse_part, dec.out, dec.lse)):
+        assert torch.equal(a, b), f"select-in-split-decode {name} differs from separate launches"
+
+
 def check_token_fused_matches(dec, q, cache, bt, sl, pre_hh, k_new=None, v_new=None,
                               pre_cache=None):
     """Token level: after the separate launches (h2o_accumulate or its per-head

@@ -22,6 +22,12 @@ def test_one_launch_up_to_the_resident_row_count():
 
 def test_launch_forms_by_splits_rows_and_selection():
     assert not _dec(8, num_splits=16).fused       # more splits than a block's waves
+    # ... then the selection runs inside the split decode, rows up to 8192
+    assert _dec(8, num_splits=16).select_in_split_decode
+    assert _dec(1, H_q=64, num_splits=64, bt_ld=8192).select_in_split_decode
+    assert not _dec(1, H_q=64, num_splits=64, bt_ld=8193).select_in_split_decode
+    assert not _dec(8).select_in_split_decode     # merged in-block instead
+    assert not _dec(8, num_splits=16, group_select=True).select_in_split_decode
     assert not _dec(8, bt_ld=5000).select_in_decode
     d = _dec(8, group_select=True)                # one selection per kv head
     assert not d.fused and not d.score_in_decode

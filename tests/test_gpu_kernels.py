@@ -13,6 +13,7 @@ from sparse_kv_cache_amd.decode import SparseDecoder
 
 from parity import (OUT_ATOL, bits, check_attention, check_gauss_row, check_partials,
                     check_group_select_decode_matches, check_scores,
+                    check_split_select_decode_matches,
                     check_token_fused_matches, check_scores_alibi, check_scores_group, page_rows,
                     check_selection_exact, check_selection_vs_oracle,
                     check_stats, dev, per_head_rows, poison, say,
@@ -35,6 +36,10 @@ PAGE_CASES = [
     (10, 1, 6, 2, 128, 2, 80, 9, 0.0, 0, 1, 16, 1.0, 1.0),
     # more splits than selection capacity: most chunks start past the row
     (11, 2, 8, 2, 128, 16, 24, 4, 0.0, 0, 1, 32, 1.0, 1.0),
+    # split counts the in-decode selection's 16-wave blocks do not divide
+    # (waves past the last split stay for the selection only)
+    (12, 2, 8, 2, 128, 16, 30, 6, 0.0, 0, 1, 20, 1.0, 1.0),
+    (13, 1, 16, 2, 64, 16, 300, 24, 0.0, 1, 1, 12, 1.0, 0.5),
 ]
 
 
@@ -138,6 +143,8 @@ def run_page_case(wl, cache_cpu, q_cpu, exact_ties=False):
         assert torch.allclose(l_ref, d.lse, rtol=0, atol=1e-5), "select+decode lse differs"
     if d.score_in_decode:
         check_one_launch_step(d, q, cache, bt, sl)
+    if d.select_in_split_decode:
+        check_split_select_decode_matches(d, q, cache, bt, sl)
 
     cb = bits(cache)
     qd = q_cpu.double().numpy()

@@ -35,6 +35,8 @@ def _buffers():
         tau=z((B, H_Q)), hh=z((NB * P, H_KV), bf), scratch=z((4096,)),
         mu=z((B, H_Q, LD)), var=z((B, H_Q, LD)), est=z((B, H_Q, LD)),
         knew=z((B, H_KV, D), bf),
+        gsel_idx=z((B, H_KV, K_CAP), i32), gsel_cnt=z((B, H_KV), i32),
+        gsel_blk=z((B, H_KV, K_CAP), i32),
     )
     return t
 
@@ -87,6 +89,17 @@ def _calls(t):
         "pagestats_update": lambda: skv.pagestats_update(t["kv"], t["kmin"], t["kmax"],
                                                          t["kmean"], t["bt"], t["sl"],
                                                          t["knew"], t["knew"]),
+        "sparse_select_decode_split": lambda: skv.sparse_select_decode_split(
+            t["scores"], t["q"], t["kv"], t["bt"], t["sl"], 2, K_CAP, s, t["o_part"],
+            t["lse_part"], sel_idx=t["sel_idx"], sel_cnt=t["sel_cnt"], sel_blk=t["sel_blk"]),
+        "sparse_select_decode_group": lambda: skv.sparse_select_decode_group(
+            t["gscores"], t["q"], t["kv"], t["bt"], t["sl"], 2, K_CAP, s, t["o_part"],
+            t["lse_part"], sel_idx=t["gsel_idx"], sel_cnt=t["gsel_cnt"],
+            sel_blk=t["gsel_blk"]),
+        "h2o_select_decode": lambda: skv.h2o_select_decode(
+            t["q"], t["kv"], t["bt"], t["sl"], t["hh"], t["scratch"], s, 2, K_CAP,
+            t["o_part"], t["lse_part"], scores=t["gscores"], sel_idx=t["gsel_idx"],
+            sel_cnt=t["gsel_cnt"], sel_blk=t["gsel_blk"], k_new=t["knew"], v_new=t["knew"]),
     }
 
 
@@ -134,6 +147,17 @@ CASES = [
     ("gauss_select", "tau", (B, H_Q - 1)), ("gauss_select", "sel_idx", (B, H_Q, K_CAP + 1)),
     ("gauss_select", "sel_blk", (B, H_Q, K_CAP - 1)), ("gauss_select", "bt", (B + 1, LD)),
     ("pagestats_update", "knew", (B, H_KV, D + 8)), ("pagestats_update", "bt", (B + 1, LD)),
+    ("sparse_select_decode_split", "scores", (B, H_KV, LD)),
+    ("sparse_select_decode_split", "o_part", (B, H_Q, NS, D + 8)),
+    ("sparse_select_decode_split", "sel_idx", (B, H_KV, K_CAP)),
+    ("sparse_select_decode_split", "sl", (B + 1,)),
+    ("sparse_select_decode_group", "gscores", (B, H_Q, LD)),
+    ("sparse_select_decode_group", "gsel_cnt", (B, H_Q)),
+    ("sparse_select_decode_group", "lse_part", (B, H_Q, NS + 1)),
+    ("h2o_select_decode", "knew", (B, H_KV + 1, D)),
+    ("h2o_select_decode", "hh", (NB * P - 1, H_KV)),
+    ("h2o_select_decode", "gsel_idx", (B, H_Q, K_CAP)),
+    ("h2o_select_decode", "gscores", (B + 1, H_KV, LD)),
 ]
 
 
