@@ -35,9 +35,10 @@ int skv_ref_stream_read(const void *buf, int64_t bytes, uint32_t *sink,
  * cache, as an attention decode over them must: item i = (block
  * items[3i], kv head items[3i+1], valid rows items[3i+2]), whose rows
  * t < valid rows are read for K and for V (D bf16 each, 16-byte loads, one
- * wave per item, four items in flight per wave; a row past the valid count
- * reads row 0 of the same page so the loads stay unconditional).  The
- * gather-only rate for a decode's own list of page-heads.
+ * wave per item, up to 4096 blocks of 4 waves, so that many short waves keep
+ * the most reads in flight; a row past the valid count reads row 0 of the
+ * same page so the loads stay unconditional).  The gather-only rate for a
+ * decode's own list of page-heads.
  *   kv_cache bf16 [2, num_blocks, page_size, H_kv, D]; page_size 16,
  *            D in {64, 128}.
  *   items    int32 [n, 3]; block < num_blocks, kv head < H_kv, rows <= 16
