@@ -52,6 +52,9 @@ constexpr int kXcds = 8;              // accelerator complex dies of an MI355X
 #ifndef SKV_DECODE_WPE16
 #define SKV_DECODE_WPE16 3            // same, page_size 16 path
 #endif
+#ifndef SKV_DECODE_WPE_ALONE
+#define SKV_DECODE_WPE_ALONE 6        // the standalone page_size 16 decode (one page in flight)
+#endif
 
 // One head, one group of 16 token rows: fold the rows' logits and values into
 // the lane's online-softmax state.  The query is split into bf16 hi + lo
@@ -219,7 +222,8 @@ __device__ __forceinline__ void fold_max_sum(float& m, float& z, float m2, float
 
 template <int D, int WB, int PFIX, bool AL, bool FUSE, int TKI, bool SC = false>
 __global__ __launch_bounds__(WB * 64)
-__attribute__((amdgpu_waves_per_eu(PFIX == 16 ? SKV_DECODE_WPE16 : SKV_DECODE_WPE)))
+__attribute__((amdgpu_waves_per_eu((!FUSE && TKI == 0 && PFIX == 16) ? SKV_DECODE_WPE_ALONE
+                                   : PFIX == 16 ? SKV_DECODE_WPE16 : SKV_DECODE_WPE)))
 void sparse_decode_wave_kernel(
     const float* __restrict__ q, int H_q, int H_kv, int G,
     const uint16_t* __restrict__ kv, int64_t num_blocks, int P,
@@ -483,6 +487,23 @@ void sparse_decode_wave_kernel(
     // Two groups in flight: while one is folded in, the next one's loads
     // are outstanding; each refill is unconditional (past the end it reads
     // placeholders) so the number of loads in flight stays static.
+    // The standalone page_size 16 decode keeps one page in flight per wave
+    // and more waves per SIMD (6, at 74 VGPRs): 25.2 against 25.5 us at
+    // long_context and 22.6 against 23.0 at gqa_ragged for the two-page ring
+    // at 4 waves (the same pages in the same order, so the same bits).  The
+    // fused forms keep the ring (their block shapes cap the waves per SIMD),
+    // and so does the generic page size (its addressing spills at 6).
+    if constexpr (!FUSE && TKI == 0 && PFIX == 16) {
+      uint4 Ks[NL], Vs[NL];
+      bool os[NL];
+      float ps[NL];
+      bool fs = false;
+      for (int grp = 0; grp < ngroups; ++grp) {
+        load(grp, Ks, Vs, os, fs, ps);
+        attend_rows_split<LPR, NL, AL>(qh, ql, Ks, Vs, os, fs, ps, slope2, m, l, acc);
+      }
+      continue;
+    }
     uint4 K0[NL], V0[NL], K1[NL], V1[NL];
     bool o0[NL], o1[NL];
     float p0[NL], p1[NL];
@@ -1049,18 +1070,23 @@ void launch_wave_fused(hipStream_t st, const Args& a, int64_t n_groups, float* o
                      out, lse_out, ta);
 }
 
-// In-block selection with split partials: one kSplitWaves-wave block per
-// (query head, group of kSplitWaves splits), each selecting its head's row.
+// In-block selection with split partials: one block per (query head, group
+// of as many splits as the block has waves), each selecting its head's row.
+// 16 waves at page_size 16; 8 for the generic page size, whose addressing
+// would spill within the 128 registers a 16-wave block allows.
 constexpr int kSplitWaves = 16;
+
+constexpr int split_waves(int pfix) { return pfix == 16 ? kSplitWaves : kSplitWaves / 2; }
 
 template <int D, int PFIX, bool AL, int TKI>
 void launch_wave_split(hipStream_t st, const Args& a, int64_t n_groups, const TopkArgs& ta) {
-  const int nsg = (a.num_splits + kSplitWaves - 1) / kSplitWaves;
+  constexpr int WB = split_waves(PFIX);
+  const int nsg = (a.num_splits + WB - 1) / WB;
   const int per_group = a.G * nsg;
   const int64_t blocks = kXcds * per_group * ((n_groups + kXcds - 1) / kXcds);
   const size_t lds = sizeof(int32_t) * 2 * static_cast<size_t>(a.k_cap);
-  hipLaunchKernelGGL((sparse_decode_wave_kernel<D, kSplitWaves, PFIX, AL, false, TKI>),
-                     dim3(static_cast<unsigned>(blocks)), dim3(kSplitWaves * 64), lds, st,
+  hipLaunchKernelGGL((sparse_decode_wave_kernel<D, WB, PFIX, AL, false, TKI>),
+                     dim3(static_cast<unsigned>(blocks)), dim3(WB * 64), lds, st,
                      a.q, a.H_q, a.H_kv, a.G, a.kv, a.num_blocks, a.P, a.bt, a.bt_ld,
                      a.seq_lens, a.sel_idx, a.sel_cnt, a.sel_blk, a.k_cap, a.scale_log2,
                      a.num_splits, a.o_part, a.lse_part, n_groups, per_group, a.alibi,
@@ -1426,7 +1452,8 @@ extern "C" int sparse_select_decode_split(const float* scores, int64_t score_ld,
               "%s: k_cap %d must cover the largest selection %lld (and be <= 4096)", who,
               k_cap, (long long)need);
   const int64_t n_groups = static_cast<int64_t>(B) * H_kv;
-  const int64_t nsg = (num_splits + kSplitWaves - 1) / kSplitWaves;
+  const int wb = split_waves(page_size == 16 ? 16 : 0);
+  const int64_t nsg = (num_splits + wb - 1) / wb;
   SKV_REQUIRE(B <= 65535 && G * nsg * (n_groups + kXcds) < 0x7fffffffLL,
               "%s: grid too large", who);
   // no rows: nothing is read or written, so no pointer is needed
@@ -1447,8 +1474,10 @@ extern "C" int sparse_select_decode_split(const float* scores, int64_t score_ld,
   const TopkArgs ta{scores, score_ld, topk_pages, frac, reserved_bos, reserved_eos,
                     sel_idx, sel_cnt, sel_blk};
   const bool al = alibi_slopes != nullptr;
-  // entries per thread of the 1024-thread selection
-  const int tki = score_ld <= 1024 ? 1 : score_ld <= 2048 ? 2 : score_ld <= 4096 ? 4 : 8;
+  // entries per thread of the block's selection (wb * 64 threads)
+  const int64_t per_thread = (score_ld + wb * 64 - 1) / (wb * 64);
+  const int tki = per_thread <= 1 ? 1 : per_thread <= 2 ? 2 : per_thread <= 4 ? 4
+                  : per_thread <= 8 ? 8 : 16;
 #define SKV_SPL(DD, PP, TT)                                                          \
   do {                                                                               \
     if (al) launch_wave_split<DD, PP, true, TT>(stream, a, n_groups, ta);            \
@@ -1459,7 +1488,8 @@ extern "C" int sparse_select_decode_split(const float* scores, int64_t score_ld,
     if (tki == 1) SKV_SPL(DD, PP, 1);                                                \
     else if (tki == 2) SKV_SPL(DD, PP, 2);                                           \
     else if (tki == 4) SKV_SPL(DD, PP, 4);                                           \
-    else SKV_SPL(DD, PP, 8);                                                         \
+    else if (tki == 8) SKV_SPL(DD, PP, 8);                                           \
+    else if (PP != 16) SKV_SPL(DD, PP, 16);                                          \
   } while (0)
   if (page_size == 16) {
     if (D == 128) SKV_SPL_T(128, 16); else SKV_SPL_T(64, 16);
