@@ -344,6 +344,10 @@ ALIBI_CASES = [
     (81, 2, 4, 4, 64, 4, 40, 7, 4, False),
     (82, 1, 16, 2, 128, 16, 50, 9, 5, True),
     (83, 2, 6, 3, 64, 1, 120, 20, 2, True),
+    # more splits than a block merges: the selection inside the split decode
+    # (8-wave blocks at page size 4, 16-wave blocks at 16)
+    (84, 2, 8, 2, 128, 4, 60, 9, 12, False),
+    (85, 1, 16, 2, 128, 16, 200, 12, 20, False),
 ]
 
 
@@ -415,6 +419,8 @@ def run_alibi_case(wl, cache_cpu, q_cpu, group, slopes_np):
         d.fused = True
         torch.cuda.synchronize()
         check_one_launch_step(d, q, cache, bt, sl)
+    if d.select_in_split_decode:
+        check_split_select_decode_matches(d, q, cache, bt, sl)
     check_partials(d.o_part.cpu().numpy(), d.lse_part.cpu().numpy(), qd, cb,
                    wl.block_table, wl.seq_lens, per, wl.G, wl.softmax_scale, d.k_cap,
                    slopes=sl64)
