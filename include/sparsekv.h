@@ -62,6 +62,12 @@ extern "C" {
 /* Message for the latest non-zero return on this thread ("" if none). */
 const char *sparsekv_last_error(void);
 
+/* Build id: the SHA-1 (hex) over the names and bytes of the sources the
+ * library was built from (these headers and the kernel sources), so that a
+ * binding can refuse a library whose entry points may differ from the
+ * declarations it marshals for.  Static string; no device work. */
+const char *sparsekv_build_id(void);
+
 /*
  * pagestats_update -- per-page key statistics, optionally fused with the KV
  * append of one decode step.   [VTX "Page-level variants": element-wise

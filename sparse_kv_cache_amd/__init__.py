@@ -44,6 +44,7 @@ EXPORTED_SYMBOLS = (
     "sparse_select_decode_split", "sparse_page_decode",
     "page_var_update", "gauss_moments", "gauss_select", "entmax15_paged_decode_merged",
     "skv_ref_stream_read", "skv_ref_gather_read", "sparsekv_last_error",
+    "sparsekv_build_id",
 )
 # size of the fixed scratch of h2o_accumulate_noalloc (SKV_NOALLOC_SCRATCH_FLOATS)
 NOALLOC_SCRATCH_FLOATS = 2 * 1024 * 1024
@@ -82,6 +83,18 @@ def load_library():
             "g.build()'` (or python sparse_kv_cache_amd/build.py) first")
     lib = ctypes.CDLL(_LIB_PATH)
     V, I, L, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    # a library built from other sources than the tree holds may take other
+    # arguments than the ones passed below: refuse it rather than call it
+    lib.sparsekv_build_id.restype = ctypes.c_char_p
+    lib.sparsekv_build_id.argtypes = []
+    from . import build as _build
+    if os.path.isdir(_build.CSRC):
+        built, now = lib.sparsekv_build_id().decode(), _build.source_digest()
+        if built != now:
+            raise RuntimeError(
+                f"{_LIB_PATH} was built from other sources (build id {built[:12]}, "
+                f"sources {now[:12]}); rebuild it: python -c 'import __graft_entry__ "
+                "as g; g.build()'")
     lib.sparsekv_last_error.restype = ctypes.c_char_p
     lib.sparsekv_last_error.argtypes = []
     lib.pagestats_update.argtypes = [V, L, I, I, I, V, V, V, V, L, V, I, V, V, V, V]

@@ -111,6 +111,24 @@ def test_library_exports_every_declared_symbol(lib):
         assert getattr(lib, n) is not None
 
 
+def test_library_carries_the_digest_of_its_sources(lib):
+    from sparse_kv_cache_amd import build
+    assert lib.sparsekv_build_id().decode() == build.source_digest()
+    # every kernel source and header is in the digest
+    names = {os.path.basename(f) for f in build.source_files()}
+    assert {"sparse_decode.hip", "skv_topk.h", "sparsekv.h", "skv_reference.h"} <= names
+
+
+def test_a_library_built_from_other_sources_is_refused(monkeypatch, lib):
+    """A stale library may take other arguments than the binding passes:
+    loading it must fail before any call."""
+    from sparse_kv_cache_amd import build
+    monkeypatch.setattr(build, "source_digest", lambda: "0" * 40)
+    monkeypatch.setattr(skv, "_lib", None)
+    with pytest.raises(RuntimeError, match="built from other sources"):
+        skv.load_library()
+
+
 def _msg(lib):
     return lib.sparsekv_last_error().decode()
 
