@@ -181,12 +181,6 @@ def _rc(name, code):
         raise SparseKVError(name, code, msg)
 
 
-def _row_len(t, name):
-    if t.dim() != 2:
-        raise ValueError(f"{name} must be 2-D")
-    return t.shape[1]
-
-
 # ------------------------------------------------------------ entry points
 
 def pagestats_update(kv_cache, k_min, k_max, k_mean, block_table, seq_lens,
