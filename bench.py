@@ -221,12 +221,17 @@ def profiled_traffic(tag, kind="softmax", kernel=None):
     if start < 0:
         return None
     body = text[start + 7:text.find("```", start + 7)].strip()
-    rec = json.loads(body)
-    if rec is None or rec.get("source_sha1") != decode_source_hash(kind):
+    recs = json.loads(body)
+    if recs is None:
         return None
-    if kernel is not None and rec.get("kernel") != kernel:
+    # one record (the main launch), or a list: the main launch, then the
+    # decode timed alone
+    recs = recs if isinstance(recs, list) else [recs]
+    if kernel is not None:
+        recs = [r for r in recs if r.get("kernel") == kernel]
+    if not recs or recs[0].get("source_sha1") != decode_source_hash(kind):
         return None
-    return int(rec["traffic"])
+    return int(recs[0]["traffic"])
 
 
 # ------------------------------------------------------------ cpu baseline
@@ -458,12 +463,15 @@ def main():
             dec = {"kernel": da["kernel"], "us_per_launch": da["us"],
                    "bytes_per_launch": da["bytes"], "achieved_GBps": da["achieved"],
                    "frac": da["frac"], "gather_frac": da["gather_frac"],
-                   "stream_frac": round(da["achieved"] / rf["stream_ref"]["GBps"], 4)}
+                   "stream_frac": round(da["achieved"] / rf["stream_ref"]["GBps"], 4),
+                   "traffic": da.get("traffic")}
         else:
             dec = {"kernel": rf["kernel"], "us_per_launch": rf["us_per_launch"],
                    "bytes_per_launch": rf["bytes_per_launch"], "achieved_GBps": rf["achieved"],
                    "frac": rf["frac"], "gather_frac": rf.get("gather_frac"),
-                   "stream_frac": rf.get("stream_frac")}
+                   "stream_frac": rf.get("stream_frac"), "traffic": rf["traffic"]}
+        dec["traffic_ratio"] = (None if dec["traffic"] is None else
+                                round(dec["traffic"] / dec["bytes_per_launch"], 3))
         result["long_context"] = {
             "workload": "long_context", "steps_per_s": ns["value"],
             "gpu_ms_per_step": ns["gpu_ms_per_step"], "launches": len(ns["kernels"]),
@@ -724,16 +732,16 @@ def measure(args, workload, cpu=True):
              "sparse_select_decode_split" if in_split_decode else
              "h2o_select_decode" if token_fused else "sparse_paged_decode")
     a = kb[focus] / (per_kernel_ms[focus] * 1e-3) / 1e9
+    # the committed counter summary of this workload and mode
+    traffic_tag = (wl.name + ("_group" if group else "")
+                   + ("_gauss" if gauss else "_entmax" if entmax else "")
+                   + ("_alibi" if slopes is not None else "")
+                   + ("_heads" if decs[0].h2o_per_head else ""))
+    traffic_kind = "entmax" if entmax else "token" if token_fused else "softmax"
     roofline = {"kernel": focus, "bound": "hbm", "achieved": round(a, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(a / PEAK_HBM_GBPS, 4),
                 "traffic": (None if (entmax and not fused) else
-                            profiled_traffic(wl.name + ("_group" if group else "")
-                                             + ("_gauss" if gauss else
-                                                "_entmax" if entmax else "")
-                                             + ("_alibi" if slopes is not None else "")
-                                             + ("_heads" if decs[0].h2o_per_head else ""),
-                                             "entmax" if entmax else
-                                             "token" if token_fused else "softmax", focus)),
+                            profiled_traffic(traffic_tag, traffic_kind, focus)),
                 # the same rate against a plain device copy measured in this run
                 "copy_frac": round(a / copy_gbps, 4) if copy_gbps > 0 else None,
                 "bytes_per_launch": kb[focus],
@@ -775,12 +783,14 @@ def measure(args, workload, cpu=True):
         kb0, _ = kernel_bytes(wl, sel_idx, sel_cnt, sl_last, decs[0].decode_splits,
                               token_level, group, fused, entmax, gauss)
         da = kb0["sparse_paged_decode"] / (dms * 1e-3) / 1e9
+        alone = "sparse_paged_decode_merged" if fused else "sparse_paged_decode"
         roofline["decode_alone"] = {
-            "kernel": "sparse_paged_decode_merged" if fused else "sparse_paged_decode",
+            "kernel": alone,
             "us": round(dms * 1000, 2), "bytes": kb0["sparse_paged_decode"],
             "achieved": round(da, 1), "frac": round(da / PEAK_HBM_GBPS, 4),
             "gather_frac": (round(da / refs["gather"]["GBps"], 4) if "gather" in refs
-                            else None)}
+                            else None),
+            "traffic": profiled_traffic(traffic_tag, traffic_kind, alone)}
 
     result = {
         "metric": "sparse decode steps/s + effective HBM GB/s (% of peak), GQA 32/8 D=128",

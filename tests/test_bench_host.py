@@ -67,13 +67,25 @@ def _record(tag):
 
 
 def test_counter_records_are_gated_by_kernel_and_source_hash(monkeypatch):
-    rec = _record("gqa_ragged")
-    monkeypatch.setattr(bench, "decode_source_hash", lambda kind="softmax": rec["source_sha1"])
-    assert bench.profiled_traffic("gqa_ragged", "softmax", rec["kernel"]) == rec["traffic"]
+    recs = _record("gqa_ragged")
+    # the step's main launch, then the decode timed alone
+    assert isinstance(recs, list) and len(recs) == 2
+    main, alone = recs
+    assert main["kernel"] == "sparse_page_decode"
+    assert alone["kernel"] == "sparse_paged_decode_merged"
+    monkeypatch.setattr(bench, "decode_source_hash", lambda kind="softmax": main["source_sha1"])
+    assert bench.profiled_traffic("gqa_ragged", "softmax", main["kernel"]) == main["traffic"]
+    assert bench.profiled_traffic("gqa_ragged", "softmax", alone["kernel"]) == alone["traffic"]
+    assert bench.profiled_traffic("gqa_ragged", "softmax") == main["traffic"]
     assert bench.profiled_traffic("gqa_ragged", "softmax", "some_other_kernel") is None
     assert bench.profiled_traffic("no_such_workload") is None
+    # a single record (workloads whose step has no separately timed decode)
+    one = _record("high_batch")
+    assert isinstance(one, dict)
+    assert bench.profiled_traffic("high_batch", "softmax", one["kernel"]) == one["traffic"]
     monkeypatch.setattr(bench, "decode_source_hash", lambda kind="softmax": "0" * 40)
-    assert bench.profiled_traffic("gqa_ragged", "softmax", rec["kernel"]) is None
+    assert bench.profiled_traffic("gqa_ragged", "softmax", main["kernel"]) is None
+    assert bench.profiled_traffic("gqa_ragged", "softmax", alone["kernel"]) is None
 
 
 def test_cpu_baseline_request_copy_gives_the_same_step():
