@@ -129,6 +129,17 @@ def test_a_library_built_from_other_sources_is_refused(monkeypatch, lib):
         skv.load_library()
 
 
+def test_a_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No library, no fallback: every entry point goes through
+    load_library, which raises."""
+    monkeypatch.setattr(skv, "_LIB_PATH", str(tmp_path / "libsparsekv.so"))
+    monkeypatch.setattr(skv, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        skv.load_library()
+    with pytest.raises(RuntimeError, match="not built"):
+        skv.lse_merge(None, None, None)
+
+
 def _msg(lib):
     return lib.sparsekv_last_error().decode()
 
