@@ -25,11 +25,18 @@
 
 namespace {
 
-constexpr int kWaves = 4;
 constexpr int kIter = 2;
+// Waves per block: 4, or (per-head scores) 8 when the 4-wave grid is at most
+// kWideGrid blocks (8 per CU: the whole grid resident at once), where fewer,
+// larger blocks stage the query rows fewer times (long_context, 8,192 pages x
+// 8 kv heads: 16.4 against 17.1-17.5 us; with ALiBi 16.9 against 18.5).
+// Larger grids keep the finer 4-wave blocks (high_batch: 215.7 against 221.5
+// us with 8), and so does the group score, whose one-row blocks have less to
+// stage (long_context: 17.3 against 15.2 us with 8).
+constexpr int kWideGrid = 2048;
 
-template <int D, int GS, bool AGG>
-__global__ __launch_bounds__(256) void page_score_kernel(
+template <int D, int GS, bool AGG, int NW>
+__global__ __launch_bounds__(NW * 64) void page_score_kernel(
     const float* __restrict__ q, int H_q, int H_kv, int G,
     const uint16_t* __restrict__ kmin, const uint16_t* __restrict__ kmax,
     const float* __restrict__ kmean, const int32_t* __restrict__ bt,
@@ -38,7 +45,7 @@ __global__ __launch_bounds__(256) void page_score_kernel(
     int64_t max_pages, const float* __restrict__ alibi) {
   constexpr int LPR = D / 8;          // lanes per page-head
   constexpr int PPW = 64 / LPR;       // page-heads per wave load
-  constexpr int TILE = kIter * kWaves * PPW;
+  constexpr int TILE = kIter * NW * PPW;
   // kv heads vary fastest in launch order: blocks dispatched together read
   // neighbouring statistics rows (all heads of a page are contiguous)
   const int b = blockIdx.z;
@@ -74,7 +81,7 @@ __global__ __launch_bounds__(256) void page_score_kernel(
   int64_t pg[kIter];
 #pragma unroll
   for (int it = 0; it < kIter; ++it) {
-    pg[it] = p0 + (it * kWaves + wave) * PPW + sub;
+    pg[it] = p0 + (it * NW + wave) * PPW + sub;
     // unconditional loads (pages past N read page p0's entry, whose result
     // is never stored) keep the count of loads in flight static
     const int64_t blk = btr[pg[it] < N ? pg[it] : p0];
@@ -168,13 +175,21 @@ __global__ __launch_bounds__(256) void page_score_kernel(
 }
 
 template <int D, int GS, bool AGG>
-void launch_score(dim3 grid, hipStream_t stream, const float* q, int H_q,
+void launch_score(bool wide, dim3 grid, hipStream_t stream, const float* q, int H_q,
                   int H_kv, int G, const uint16_t* kmin, const uint16_t* kmax,
                   const float* kmean, const int32_t* bt, int64_t bt_ld,
                   const int32_t* seq_lens, int P, float w_avg, float w_peak,
                   float* scores, int64_t score_ld, int64_t max_pages,
                   const float* alibi) {
-  hipLaunchKernelGGL((page_score_kernel<D, GS, AGG>), grid, dim3(256), 0, stream, q,
+  if constexpr (!AGG) {
+    if (wide) {
+      hipLaunchKernelGGL((page_score_kernel<D, GS, AGG, 8>), grid, dim3(512), 0, stream, q,
+                         H_q, H_kv, G, kmin, kmax, kmean, bt, bt_ld, seq_lens, P,
+                         w_avg, w_peak, scores, score_ld, max_pages, alibi);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((page_score_kernel<D, GS, AGG, 4>), grid, dim3(256), 0, stream, q,
                      H_q, H_kv, G, kmin, kmax, kmean, bt, bt_ld, seq_lens, P,
                      w_avg, w_peak, scores, score_ld, max_pages, alibi);
 }
@@ -209,15 +224,17 @@ int score_pages(const char* who, bool group, const float* q, int B, int H_q,
   const int GS = group ? 1 : G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
   const int slices = group ? 1 : (G + GS - 1) / GS;
   const int ppw = 64 / (D / 8);
-  const int tile = kIter * kWaves * ppw;
+  const int64_t tiles4 = (max_pages + kIter * 4 * ppw - 1) / (kIter * 4 * ppw);
+  const bool wide = !group && static_cast<int64_t>(H_kv) * slices * tiles4 * B <= kWideGrid;
+  const int tile = kIter * (wide ? 8 : 4) * ppw;
   const int64_t tiles = (max_pages + tile - 1) / tile;
   SKV_REQUIRE(tiles <= 65535, "%s: bt_ld %lld too long", who, (long long)bt_ld);
   dim3 grid(static_cast<unsigned>(H_kv * slices), static_cast<unsigned>(tiles),
             static_cast<unsigned>(B));
 #define SKV_SCORE(DD, GG, AA)                                                    \
-  launch_score<DD, GG, AA>(grid, stream, q, H_q, H_kv, G, k_min, k_max, k_mean,   \
-                           block_table, bt_ld, seq_lens, page_size, w_avg,      \
-                           w_peak, scores, score_ld, max_pages, alibi)
+  launch_score<DD, GG, AA>(wide, grid, stream, q, H_q, H_kv, G, k_min, k_max,     \
+                           k_mean, block_table, bt_ld, seq_lens, page_size,     \
+                           w_avg, w_peak, scores, score_ld, max_pages, alibi)
   if (group) {
     if (D == 128) SKV_SCORE(128, 1, true); else SKV_SCORE(64, 1, true);
   } else if (D == 128) {

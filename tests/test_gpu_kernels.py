@@ -264,6 +264,46 @@ def test_page_level_step_with_128_query_heads():
     say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}")
 
 
+# (D, H_q, H_kv): group slices of 1, 2, 4 and 8 query heads (and two of 8)
+SCORE_SHAPES = [(64, 2, 2), (64, 4, 2), (64, 8, 2), (64, 16, 2), (128, 2, 2), (128, 4, 2),
+                (128, 8, 2), (128, 16, 2), (128, 32, 2)]
+
+
+@pytest.mark.parametrize("D,H_q,H_kv", SCORE_SHAPES,
+                         ids=[f"D{d}-G{h // k}" for d, h, k in SCORE_SHAPES])
+def test_page_score_both_block_shapes(D, H_q, H_kv):
+    """page_score runs 8-wave blocks while its 4-wave grid fits on the
+    device at once (at most 2048 blocks) and 4-wave blocks past that. The grid
+    follows the block-table row length (blocks past a request's pages return
+    at once), so the same batch scored through a short and a long row takes
+    both shapes; each must match the oracle fed the same statistics, for
+    every group-slice width."""
+    say(f"[gpu] page_score block shapes, D={D} G={H_q // H_kv}")
+    B, P = 32, 16
+    wl = W.small_case(seed=97, B=B, H_q=H_q, H_kv=H_kv, D=D, P=P, max_pages=40)
+    cache = dev(W.make_cache(wl))
+    q_cpu = W.make_queries(wl)
+    q, sl = dev(q_cpu), dev(wl.seq_lens)
+    k_min = torch.empty((wl.num_blocks, H_kv, D), dtype=torch.bfloat16, device="cuda")
+    k_max = torch.empty_like(k_min)
+    k_mean = torch.empty((wl.num_blocks, H_kv, D), dtype=torch.float32, device="cuda")
+    ppw, slices = 64 // (D // 8), -(-(H_q // H_kv) // 8)
+    for ld in (48, 2100):
+        tiles4 = -(-ld // (2 * 4 * ppw))
+        assert (H_kv * slices * tiles4 * B <= 2048) == (ld == 48)
+        bt_np = np.zeros((B, ld), dtype=np.int32)
+        bt_np[:, :wl.block_table.shape[1]] = wl.block_table
+        bt = dev(bt_np)
+        skv.pagestats_update(cache, k_min, k_max, k_mean, bt, sl)
+        scores = torch.full((B, H_q, ld), float("nan"), device="cuda")
+        skv.page_score(q, k_min, k_max, k_mean, bt, sl, P, wl.w_avg, wl.w_peak, scores)
+        torch.cuda.synchronize()
+        gst = (oracle.bf16_decode(bits(k_min)), oracle.bf16_decode(bits(k_max)),
+               k_mean.cpu().numpy().astype(np.float64))
+        check_scores(scores.cpu().numpy(), q_cpu.double().numpy(), gst, bt_np, wl.seq_lens,
+                     P, wl.w_avg, wl.w_peak)
+
+
 # seed, B, H_q, H_kv, D, P, max_pages, topk, frac, bos, eos, splits, w_avg, w_peak
 GROUP_CASES = [
     (40, 2, 8, 2, 128, 16, 20, 5, 0.0, 0, 1, 3, 1.0, 1.0),
