@@ -255,6 +255,38 @@ def test_page_level_step_long_rows(case):
     say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}")
 
 
+# seed, B, H_q, H_kv, D, P, max_pages, min_pages, topk, splits, alibi: the
+# selection inside the split decode at its limits (rows of 8192, k_cap 4096;
+# the generic page size's 8-wave blocks with 16 entries a thread; a few
+# hundred splits; 4096 splits, most of them past the selection)
+SPLIT_ROW_CASES = [
+    (100, 1, 4, 2, 64, 16, 8192, 7000, 4096, 64, False),
+    (101, 1, 2, 1, 64, 4, 8192, 6000, 1500, 40, False),
+    (102, 2, 4, 2, 64, 16, 3000, 1000, 800, 300, False),
+    (103, 1, 4, 2, 128, 16, 8192, 8000, 256, 4096, False),
+    (104, 1, 4, 2, 64, 16, 8192, 7000, 3000, 48, True),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_ROW_CASES, ids=[f"split{c[0]}" for c in SPLIT_ROW_CASES])
+def test_split_select_decode_at_its_limits(case):
+    (seed, B, H_q, H_kv, D, P, maxp, minp, topk, ns, al) = case
+    say(f"[gpu] split select-decode {case}")
+    wl = W.small_case(seed=seed, B=B, H_q=H_q, H_kv=H_kv, D=D, P=P, max_pages=maxp,
+                      topk_pages=topk, num_splits=ns, min_len=minp * P)
+    d = _decoder(wl)
+    assert d.select_in_split_decode and not d.fused
+    del d
+    cache, q = W.make_cache(wl), W.make_queries(wl)
+    if al:
+        from sparse_kv_cache_amd.decode import alibi_slopes
+        slopes = alibi_slopes(H_q, device="cpu").numpy()
+        worst, ex = run_alibi_case(wl, cache, q, False, slopes)
+    else:
+        worst, ex = run_page_case(wl, cache, q)
+    say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}")
+
+
 def test_page_level_step_with_128_query_heads():
     """128 query heads over 8 kv heads (G = 16) at D = 64."""
     say("[gpu] page-level step, 128 query heads")
