@@ -365,8 +365,13 @@ int sparse_select_decode_split(const float *scores, int64_t score_ld, int topk_p
  *            with H_sel = H_kv (split s of a row holds the selected entries
  *            [s c, min((s + 1) c, cnt)), c = ceil(k_cap / num_splits))
  *   o_part   fp32 [B, H_q, num_splits, D], lse_part fp32 [B, H_q, num_splits]:
- *            exactly what sparse_paged_decode writes for that selection
- *            (lse_merge combines them)
+ *            what sparse_paged_decode writes for that selection (lse_merge
+ *            combines them): bit for bit while a split holds at most 4
+ *            groups of 16 rows (16 / page_size entries each); past that the
+ *            8 waves of this form fold a split's groups in another order
+ *            than the standalone kernel's 4, which moves values by about
+ *            1e-5 of their magnitude (the online softmax rescales by other
+ *            running maxima)
  *   sel_idx, sel_cnt (both or neither), sel_blk (needs sel_idx):
  *            [B, H_kv, k_cap] / [B, H_kv]; when given, receive the selection
  *            exactly as page_topk_blk writes it.
@@ -622,9 +627,11 @@ int h2o_accumulate_noalloc(const float *q, int B, int H_q, int H_kv, int D,
  *   update), selects the row's tokens in-block (page_topk's selection), and
  *   attends over its chunk of the selection for the G query heads; the
  *   row's split blocks then share writing the new hh values (and the fp32
- *   row, when scores is given).  Results equal h2o_accumulate (per_head:
- *   h2o_accumulate_heads) +
- *   page_topk_blk + sparse_paged_decode bit for bit.
+ *   row, when scores is given).  The accumulator, the score rows and the
+ *   selection equal h2o_accumulate (per_head: h2o_accumulate_heads) +
+ *   page_topk_blk bit for bit, and the partials equal sparse_paged_decode's
+ *   as sparse_select_decode_group's do (bit for bit while a split holds at
+ *   most 64 tokens).
  *
  *   q ... seq_lens, reserved_bos, reserved_eos, scale, decay, hh_score: as
  *            h2o_accumulate (page_size 1); bt_ld <= 8192.

@@ -53,11 +53,43 @@ def poison(dec):
     dec.sel_blk.fill_(-7)
 
 
+def group_forms_fold_alike(dec):
+    """Whether the group decode's two forms fold a split's rows in the same
+    order: the standalone kernel deals a split's 16-row groups to 4 waves, the
+    in-block-selection form (and the token-level step's) to 8, each wave
+    folding groups w, w + waves, ... before the waves merge; with at most 4
+    groups per split both forms fold the same groups in the same order."""
+    epg = max(1, 16 // dec.P)                       # entries per 16-row group
+    per_split = -(-dec.k_cap // dec.decode_splits)
+    return -(-per_split // epg) <= 4
+
+
+def check_close_partials(o_ref, l_ref, o, l, what):
+    """The same attention states folded in another order: the online softmax
+    rescales by other running maxima and splits other probabilities into
+    bf16 hi + lo halves (about 16 significant bits), so the values agree to
+    about 1e-5 of the row's magnitude; empty entries match exactly."""
+    a, b = o_ref.reshape(-1, o_ref.shape[-1]), o.reshape(-1, o.shape[-1])
+    assert torch.isfinite(b).all(), f"{what}: not finite"
+    scale = a.abs().amax(dim=1, keepdim=True).clamp_min(1.0)
+    err = ((a - b).abs() / scale).max().item()
+    assert err <= 1e-4, f"{what}: output differs by {err} of the row's magnitude"
+    la, lb = l_ref.reshape(-1), l.reshape(-1)
+    fin = torch.isfinite(la)
+    assert torch.equal(torch.isfinite(lb), fin), f"{what}: lse finiteness differs"
+    assert torch.equal(la[~fin], lb[~fin]), f"{what}: empty entries' lse differs"
+    if fin.any():
+        e = ((la[fin] - lb[fin]).abs() / la[fin].abs().clamp_min(1.0)).max().item()
+        assert e <= 1e-5, f"{what}: lse differs by {e}"
+
+
 def check_group_select_decode_matches(dec, q, cache, bt, sl):
     """With a selection shared by each kv head's group, the one-launch form
-    (selection inside the group decode) must give exactly the bits the
-    separate page_topk + sparse_paged_decode (+ lse_merge) launches just
-    wrote into dec's buffers: selection, block ids, partials, merged output."""
+    (selection inside the group decode) must give exactly the selection and
+    block ids the separate page_topk + sparse_paged_decode (+ lse_merge)
+    launches just wrote into dec's buffers, and their partials and merged
+    output: bit for bit where both forms fold a split's rows alike
+    (group_forms_fold_alike), else to within that refolding's rounding."""
     assert dec.select_in_group_decode
     ref = [t.clone() for t in (dec.sel_idx, dec.sel_cnt, dec.sel_blk, dec.o_part,
                                dec.lse_part, dec.out, dec.lse)]
@@ -71,10 +103,15 @@ def check_group_select_decode_matches(dec, q, cache, bt, sl):
     dec.merge()
     dec.keep_selection = keep
     torch.cuda.synchronize()
+    exact = group_forms_fold_alike(dec)
     names = ("sel_idx", "sel_cnt", "sel_blk", "o_part", "lse_part", "out", "lse")
-    for name, a, b in zip(names, ref, (dec.sel_idx, dec.sel_cnt, dec.sel_blk, dec.o_part,
-                                       dec.lse_part, dec.out, dec.lse)):
-        assert torch.equal(a, b), f"select-in-decode {name} differs from separate launches"
+    got = (dec.sel_idx, dec.sel_cnt, dec.sel_blk, dec.o_part, dec.lse_part, dec.out, dec.lse)
+    for name, a, b in zip(names, ref, got):
+        if exact or name.startswith("sel"):
+            assert torch.equal(a, b), f"select-in-decode {name} differs from separate launches"
+    if not exact:
+        check_close_partials(ref[3], ref[4], dec.o_part, dec.lse_part, "select-in-decode partials")
+        check_close_partials(ref[5], ref[6], dec.out, dec.lse, "select-in-decode output")
 
 
 def check_split_select_decode_matches(dec, q, cache, bt, sl):
@@ -134,6 +171,7 @@ def check_token_fused_matches(dec, q, cache, bt, sl, pre_hh, k_new=None, v_new=N
     if ref_cache is not None:
         assert torch.equal(ref_cache, cache), "fused token step: the appended cache differs"
     N = sl.cpu().numpy()
+    exact = group_forms_fold_alike(dec)
     for n in names:
         a, b = ref[n], getattr(dec, n)
         if n == "scores":   # entries past each request's length are not written
@@ -141,7 +179,12 @@ def check_token_fused_matches(dec, q, cache, bt, sl, pre_hh, k_new=None, v_new=N
                 assert torch.equal(a[r, :, :int(N[r])], b[r, :, :int(N[r])]), \
                     f"fused token step: scores of request {r} differ"
             continue
-        assert torch.equal(a, b), f"fused token step: {n} differs from separate launches"
+        if exact or n not in ("o_part", "lse_part", "out", "lse"):
+            assert torch.equal(a, b), f"fused token step: {n} differs from separate launches"
+    if not exact:
+        check_close_partials(ref["o_part"], ref["lse_part"], dec.o_part, dec.lse_part,
+                             "fused token step partials")
+        check_close_partials(ref["out"], ref["lse"], dec.out, dec.lse, "fused token step output")
 
 
 def bits(t):

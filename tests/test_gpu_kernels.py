@@ -344,6 +344,10 @@ GROUP_CASES = [
     (43, 1, 64, 8, 128, 16, 70, 16, 0.0, 0, 1, 8, 1.0, 1.0),
     (44, 2, 4, 2, 64, 1, 150, 20, 0.0, 2, 3, 5, 1.0, 1.0),
     (45, 2, 6, 3, 128, 16, 5, 50, 0.0, 0, 1, 2, 1.0, 1.0),
+    # rows up to 8192 with k_cap 4096 (the in-decode selection's 16 entries a
+    # thread), and a generic page size with a reserved window
+    (46, 1, 8, 2, 64, 16, 8192, 4096, 0.0, 0, 1, 8, 1.0, 1.0),
+    (47, 2, 8, 4, 128, 4, 6000, 1000, 0.0, 1, 2, 16, 1.0, 0.5),
 ]
 
 
@@ -903,11 +907,25 @@ def test_append_refresh_and_reset(P):
     ("per_head", 40, 10, 128, 8), ("per_head", 16, 8, 64, 8), ("per_head", 24, 12, 64, 8),
     ("per_head", 32, 16, 64, 8)])
 def test_token_level_step_teacher_forced(reading, H_q, H_kv, D, eos):
-    say(f"[gpu] h2o small, teacher forced, {reading} H_q {H_q} H_kv {H_kv} D {D} eos {eos}")
+    _token_teacher_forced(reading, H_q, H_kv, D, eos)
+
+
+@pytest.mark.parametrize("reading", ["group_mean", "per_head"])
+def test_token_level_step_long_splits(reading):
+    """More than 64 tokens a split (200 selected over 2 splits): the
+    two-launch step's group decode folds a split's row groups over 8 waves,
+    the standalone one over 4, so their partials agree to within rounding
+    rather than bit for bit; both must match the oracle."""
+    _token_teacher_forced(reading, 8, 2, 128, 1, topk=200, splits=2)
+
+
+def _token_teacher_forced(reading, H_q, H_kv, D, eos, topk=40, splits=5):
+    say(f"[gpu] h2o small, teacher forced, {reading} H_q {H_q} H_kv {H_kv} D {D} eos {eos} "
+        f"top-{topk} over {splits} splits")
     S0, B = 300, 3
     wl = W.h2o_token(seed=40, steps=6, prompt=S0, B=B)
     wl.H_q, wl.H_kv, wl.D = H_q, H_kv, D
-    wl.bos, wl.eos, wl.topk_pages, wl.num_splits = 4, eos, 40, 5
+    wl.bos, wl.eos, wl.topk_pages, wl.num_splits = 4, eos, topk, splits
     wl.seq_lens = np.array([S0, S0 - 37, 11], dtype=np.int32)
     cache = dev(W.make_cache(wl))
     bt = dev(wl.block_table)
