@@ -919,11 +919,19 @@ def test_token_level_step_long_splits(reading):
     _token_teacher_forced(reading, 8, 2, 128, 1, topk=200, splits=2)
 
 
-def _token_teacher_forced(reading, H_q, H_kv, D, eos, topk=40, splits=5):
+@pytest.mark.parametrize("reading,S0,D", [("group_mean", 3000, 64), ("per_head", 3000, 64),
+                                           ("group_mean", 7000, 128), ("per_head", 7000, 128)])
+def test_token_level_step_long_rows(reading, S0, D):
+    """Rows of 3,000 and 7,000 tokens: the two-launch step's in-block
+    selection at 8 and 16 entries a thread."""
+    _token_teacher_forced(reading, 8, 2, D, 1, topk=40, splits=5, S0=S0, steps=2)
+
+
+def _token_teacher_forced(reading, H_q, H_kv, D, eos, topk=40, splits=5, S0=300, steps=6):
     say(f"[gpu] h2o small, teacher forced, {reading} H_q {H_q} H_kv {H_kv} D {D} eos {eos} "
-        f"top-{topk} over {splits} splits")
-    S0, B = 300, 3
-    wl = W.h2o_token(seed=40, steps=6, prompt=S0, B=B)
+        f"top-{topk} over {splits} splits, {S0} tokens")
+    B = 3
+    wl = W.h2o_token(seed=40, steps=steps, prompt=S0, B=B)
     wl.H_q, wl.H_kv, wl.D = H_q, H_kv, D
     wl.bos, wl.eos, wl.topk_pages, wl.num_splits = 4, eos, topk, splits
     wl.seq_lens = np.array([S0, S0 - 37, 11], dtype=np.int32)
