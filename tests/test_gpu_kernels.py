@@ -297,8 +297,8 @@ def test_page_level_step_with_128_query_heads():
 
 
 # (D, H_q, H_kv): group slices of 1, 2, 4 and 8 query heads (and two of 8)
-SCORE_SHAPES = [(64, 2, 2), (64, 4, 2), (64, 8, 2), (64, 16, 2), (128, 2, 2), (128, 4, 2),
-                (128, 8, 2), (128, 16, 2), (128, 32, 2)]
+SCORE_SHAPES = [(64, 2, 2), (64, 4, 2), (64, 8, 2), (64, 16, 2), (64, 32, 2),
+                (128, 2, 2), (128, 4, 2), (128, 8, 2), (128, 16, 2), (128, 32, 2)]
 
 
 @pytest.mark.parametrize("D,H_q,H_kv", SCORE_SHAPES,
