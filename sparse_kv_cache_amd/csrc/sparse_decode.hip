@@ -1489,7 +1489,7 @@ extern "C" int sparse_select_decode_split(const float* scores, int64_t score_ld,
     else if (tki == 2) SKV_SPL(DD, PP, 2);                                           \
     else if (tki == 4) SKV_SPL(DD, PP, 4);                                           \
     else if (tki == 8) SKV_SPL(DD, PP, 8);                                           \
-    else if (PP != 16) SKV_SPL(DD, PP, 16);                                          \
+    else if constexpr (PP != 16) SKV_SPL(DD, PP, 16);                                \
   } while (0)
   if (page_size == 16) {
     if (D == 128) SKV_SPL_T(128, 16); else SKV_SPL_T(64, 16);

@@ -287,6 +287,78 @@ def test_split_select_decode_at_its_limits(case):
     say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}")
 
 
+def _short_rows(wl, pages):
+    """Cap every request at `pages` pages (a ragged tail kept): the block-table
+    row keeps its width, which sets how many selection entries a thread of the
+    in-decode top-k holds, while the data and the oracle's work stay small."""
+    cap = pages * wl.P - (np.arange(wl.B) % wl.P)
+    wl.seq_lens = np.minimum(wl.seq_lens, cap).astype(np.int32)
+    return wl
+
+
+# (page size, row width): every entries-per-thread count of the split
+# select-decode (1-8 with 16-wave blocks at page size 16, 1-16 with 8-wave
+# blocks below it)
+SPLIT_FORMS = [(16, 600), (16, 1500), (16, 3000), (16, 6000),
+               (4, 400), (4, 900), (4, 1800), (4, 3500), (4, 7000)]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("alibi", [False, True], ids=["plain", "alibi"])
+@pytest.mark.parametrize("P,ld", SPLIT_FORMS, ids=[f"P{p}-ld{l}" for p, l in SPLIT_FORMS])
+def test_split_select_decode_every_form(P, ld, alibi, D):
+    say(f"[gpu] split select-decode form P={P} ld={ld} alibi={alibi} D={D}")
+    wl = _short_rows(W.small_case(seed=110 + ld % 89, B=2, H_q=4, H_kv=2, D=D, P=P,
+                                  max_pages=ld, topk_pages=10, num_splits=12), 40)
+    d = _decoder(wl)
+    assert d.select_in_split_decode and not d.fused
+    del d
+    cache, q = W.make_cache(wl), W.make_queries(wl)
+    if alibi:
+        from sparse_kv_cache_amd.decode import alibi_slopes
+        worst, ex = run_alibi_case(wl, cache, q, False, alibi_slopes(4, device="cpu").numpy())
+    else:
+        worst, ex = run_page_case(wl, cache, q)
+    say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}")
+
+
+# row widths for every entries-per-thread count (4, 8, 12, 16) of the group
+# decode's in-block selection
+GROUP_FORMS = [100, 3000, 5000, 7000]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("alibi", [False, True], ids=["plain", "alibi"])
+@pytest.mark.parametrize("ld", GROUP_FORMS)
+def test_group_select_decode_every_form(ld, alibi, D):
+    say(f"[gpu] group select-decode form ld={ld} alibi={alibi} D={D}")
+    wl = _short_rows(W.small_case(seed=120 + ld % 83, B=2, H_q=8, H_kv=2, D=D, P=16,
+                                  max_pages=ld, topk_pages=10, num_splits=4), 40)
+    cache, q = W.make_cache(wl), W.make_queries(wl)
+    if alibi:
+        from sparse_kv_cache_amd.decode import alibi_slopes
+        worst, ex = run_alibi_case(wl, cache, q, True, alibi_slopes(8, device="cpu").numpy())
+    else:
+        worst, ex = run_group_case(wl, cache, q)
+    say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}")
+
+
+def test_bandwidth_references_run():
+    """The two read-only references (measurement tools, no arithmetic of the
+    method) run over valid inputs, at both head sizes; their sink is written
+    only when a read word equals a sentinel, which zeros never do."""
+    say("[gpu] bandwidth references")
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    skv.skv_ref_stream_read(torch.zeros(1 << 22, dtype=torch.uint8, device="cuda"), sink)
+    for D in (64, 128):
+        kv = torch.zeros((2, 8, 16, 2, D), dtype=torch.bfloat16, device="cuda")
+        items = torch.tensor([[blk, h, n] for blk in range(8) for h in range(2) for n in (16, 5)],
+                             dtype=torch.int32, device="cuda")
+        skv.skv_ref_gather_read(kv, items, sink)
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum().item()) == 0
+
+
 def test_page_level_step_with_128_query_heads():
     """128 query heads over 8 kv heads (G = 16) at D = 64."""
     say("[gpu] page-level step, 128 query heads")
@@ -503,6 +575,8 @@ def run_alibi_case(wl, cache_cpu, q_cpu, group, slopes_np):
     worst = check_attention(d.out.cpu().numpy(), d.lse.cpu().numpy(), qd, cb,
                             wl.block_table, wl.seq_lens, per, wl.G, wl.softmax_scale,
                             slopes=sl64)
+    if d.select_in_group_decode:
+        check_group_select_decode_matches(d, q, cache, bt, sl)
     return worst, ex
 
 
@@ -919,11 +993,12 @@ def test_token_level_step_long_splits(reading):
     _token_teacher_forced(reading, 8, 2, 128, 1, topk=200, splits=2)
 
 
-@pytest.mark.parametrize("reading,S0,D", [("group_mean", 3000, 64), ("per_head", 3000, 64),
-                                           ("group_mean", 7000, 128), ("per_head", 7000, 128)])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("S0", [3000, 5000, 7000])
+@pytest.mark.parametrize("reading", ["group_mean", "per_head"])
 def test_token_level_step_long_rows(reading, S0, D):
-    """Rows of 3,000 and 7,000 tokens: the two-launch step's in-block
-    selection at 8 and 16 entries a thread."""
+    """Rows of 3,000, 5,000 and 7,000 tokens: the two-launch step's in-block
+    selection at 8, 12 and 16 entries a thread."""
     _token_teacher_forced(reading, 8, 2, D, 1, topk=40, splits=5, S0=S0, steps=2)
 
 
