@@ -278,6 +278,54 @@ def test_validation_rejects_bad_scalars(lib):
     assert lib.lse_merge(p, p, 4, 0, 128, p, None, s) == EINVAL
 
 
+def test_validation_of_the_fused_select_decode_forms(lib):
+    """The selection-inside-the-decode forms refuse bad scalars and missing
+    pointers before any launch (no GPU here: a launch would report -EIO)."""
+    p = ctypes.c_void_p(16)          # never dereferenced: rejected first
+    s = ctypes.c_void_p(0)
+
+    def split(ld=64, topk=4, frac=0.0, D=128, P=16, k_cap=8, ns=12, scores=p, sel=(None, None),
+              fn=lib.sparse_select_decode_split, H_q=8, H_kv=2, B=1):
+        return fn(scores, ld, topk, frac, 0, 1, p, B, H_q, H_kv, D, p, 64, P, p, 64, p,
+                  k_cap, 0.1, ns, None, p, p, sel[0], sel[1], None, s)
+
+    assert split(ns=4097) == EINVAL and "num_splits" in _msg(lib)
+    assert split(ld=8193) == EINVAL and "score_ld" in _msg(lib)
+    assert split(k_cap=4097, topk=4097, ld=8192) == EINVAL
+    assert split(topk=10, k_cap=5) == EINVAL and "k_cap" in _msg(lib)
+    assert split(D=96) == EINVAL
+    assert split(P=3) == EINVAL
+    assert split(H_q=9) == EINVAL
+    assert split(frac=1.5) == EINVAL
+    assert split(scores=None) == EFAULT
+    assert split(sel=(p, None)) == EINVAL
+    assert "sparse_select_decode_split" in _msg(lib)
+    assert split(B=0, scores=None) == 0               # no rows: nothing to do
+
+    group = lib.sparse_select_decode_group
+    assert split(fn=group, ld=8193) == EINVAL and "score_ld" in _msg(lib)
+    assert split(fn=group, ns=0) == EINVAL
+    assert split(fn=group, topk=10, k_cap=5) == EINVAL and "k_cap" in _msg(lib)
+    assert split(fn=group, scores=None) == EFAULT
+    assert "sparse_select_decode_group" in _msg(lib)
+
+    def h2o(P=1, ld=64, decay=0.5, scores=None, score_ld=0, kn=None, vn=None,
+            scratch_floats=1 << 20, k_cap=8, topk=4, ns=4):
+        return lib.h2o_select_decode(p, 1, 8, 2, 128, p, 64, P, p, ld, p, 0, 1, 0.1, decay, 0,
+                                     p, scores, score_ld, topk, 0.0, k_cap, ns, p, p, None,
+                                     None, None, kn, vn, p, scratch_floats, s)
+
+    assert h2o(P=16) == EINVAL and "page_size" in _msg(lib)
+    assert h2o(ld=8193) == EINVAL and "bt_ld" in _msg(lib)
+    assert h2o(scores=p, score_ld=32) == EINVAL and "score_ld" in _msg(lib)
+    assert h2o(kn=p) == EINVAL and "k_new" in _msg(lib)
+    assert h2o(topk=10, k_cap=5) == EINVAL and "k_cap" in _msg(lib)
+    assert h2o(ns=0) == EINVAL
+    assert h2o(decay=1.5) == EINVAL
+    assert h2o(scratch_floats=16) == EINVAL
+    assert "h2o_select_decode" in _msg(lib)
+
+
 def test_validation_rejects_null_pointers(lib):
     p = ctypes.c_void_p(16)
     s = ctypes.c_void_p(0)
