@@ -315,8 +315,9 @@ int sparse_select_decode(const float *scores, int64_t score_ld, int topk_pages,
  * sparse_select_decode_split -- page_topk and sparse_paged_decode in one
  * launch for one selection per query head (H_sel = H_q) at any split count:
  * the split partials go to lse_merge.  One 16-wave block per (query head,
- * group of 16 splits) first selects its head's row from the scores into LDS
- * (the top-k of page_topk; the blocks of a head derive the same selection),
+ * group of 16 splits; 8-wave blocks of 8 splits below page size 16) first
+ * selects its head's row from the scores into LDS (the top-k of page_topk;
+ * the blocks of a head derive the same selection),
  * then each wave attends over one split's chunk of it.  This is
  * sparse_select_decode without its in-block merge, for rows with more than
  * 8 splits or up to 8192 entries.  [Same sources as page_topk and
