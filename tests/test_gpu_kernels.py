@@ -287,6 +287,35 @@ def test_split_select_decode_at_its_limits(case):
     say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}")
 
 
+# seed, D, P, max_pages, min_pages, topk, frac, bos, eos, splits, alibi: the
+# split select-decode's ranked window between reserved leading and trailing
+# pages, with a budget that grows with the row (topk_frac)
+SPLIT_WINDOW_CASES = [
+    (106, 128, 16, 6000, 3000, 100, 0.05, 3, 5, 24, False),
+    (107, 64, 4, 5000, 1000, 20, 0.1, 7, 2, 40, True),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_WINDOW_CASES,
+                         ids=[f"window{c[0]}" for c in SPLIT_WINDOW_CASES])
+def test_split_select_decode_reserved_window_and_fraction(case):
+    (seed, D, P, maxp, minp, topk, frac, bos, eos, ns, al) = case
+    say(f"[gpu] split select-decode with a reserved window {case}")
+    wl = W.small_case(seed=seed, B=2, H_q=4, H_kv=2, D=D, P=P, max_pages=maxp,
+                      topk_pages=topk, topk_frac=frac, bos=bos, eos=eos, num_splits=ns,
+                      min_len=minp * P)
+    d = _decoder(wl)
+    assert d.select_in_split_decode
+    del d
+    cache, q = W.make_cache(wl), W.make_queries(wl)
+    if al:
+        from sparse_kv_cache_amd.decode import alibi_slopes
+        worst, ex = run_alibi_case(wl, cache, q, False, alibi_slopes(4, device="cpu").numpy())
+    else:
+        worst, ex = run_page_case(wl, cache, q)
+    say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}")
+
+
 def _short_rows(wl, pages):
     """Cap every request at `pages` pages (a ragged tail kept): the block-table
     row keeps its width, which sets how many selection entries a thread of the
