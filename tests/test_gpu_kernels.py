@@ -372,6 +372,22 @@ def test_group_select_decode_every_form(ld, alibi, D):
     say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}")
 
 
+@pytest.mark.parametrize("alibi", [False, True], ids=["plain", "alibi"])
+def test_group_select_decode_sixteen_heads(alibi):
+    """A query group of 16 (every column of the matrix-core tile) sharing one
+    selection over rows of up to 3,000 pages."""
+    say(f"[gpu] group select-decode, G = 16, alibi={alibi}")
+    wl = _short_rows(W.small_case(seed=131, B=2, H_q=32, H_kv=2, D=128, P=16,
+                                  max_pages=3000, topk_pages=24, num_splits=6), 300)
+    cache, q = W.make_cache(wl), W.make_queries(wl)
+    if alibi:
+        from sparse_kv_cache_amd.decode import alibi_slopes
+        worst, ex = run_alibi_case(wl, cache, q, True, alibi_slopes(32, device="cpu").numpy())
+    else:
+        worst, ex = run_group_case(wl, cache, q)
+    say(f"  max |out - oracle| = {worst:.2e}, exempt rows {ex}")
+
+
 def test_bandwidth_references_run():
     """The two read-only references (measurement tools, no arithmetic of the
     method) run over valid inputs, at both head sizes; their sink is written
