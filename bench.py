@@ -6,8 +6,8 @@ One step = one pass of the whole hot path over the batch:
       page_score -> page_topk -> sparse_paged_decode -> lse_merge
       (with one selection per query head and at most 8 splits the merge runs
       inside the decode launch: sparse_paged_decode_merged; with more splits
-      the selection runs inside the split decode, sparse_select_decode_split,
-      and lse_merge follows)
+      the selection runs inside the split decode, whose blocks also merge
+      their splits, sparse_select_decode_split_blocks, and lse_merge follows)
       (statistics built once beforehand, timed separately)
   high_batch: pagestats_update (append + refresh) -> the four above
   h2o_token:  pagestats_update (append + reset) -> h2o_accumulate ->
@@ -524,6 +524,8 @@ def measure(args, workload, cpu=True):
     in_decode = decs[0].select_in_decode
     in_group_decode = decs[0].select_in_group_decode and not gauss and not token_level
     in_split_decode = decs[0].select_in_split_decode
+    split_name = ("sparse_select_decode_split_blocks" if decs[0].split_blocks
+                  else "sparse_select_decode_split")
     token_fused = decs[0].token_fused
     one_launch = decs[0].score_in_decode
     new_kv = [W.make_new_kv(wl, s, device=dev) for s in range(min(wl.steps, 64))] \
@@ -573,7 +575,7 @@ def measure(args, workload, cpu=True):
              (["h2o_accumulate"] if token_level else [] if one_launch else ["page_score"]) +
             (["sparse_page_decode"] if one_launch else ["sparse_select_decode"] if in_decode
              else ["sparse_select_decode_group", "lse_merge"] if in_group_decode
-             else ["sparse_select_decode_split", "lse_merge"] if in_split_decode
+             else [split_name, "lse_merge"] if in_split_decode
              else ["page_topk", "sparse_paged_decode"] + ([] if fused else ["lse_merge"])))
 
     def enqueue(i, name):
@@ -604,7 +606,7 @@ def measure(args, workload, cpu=True):
             d.select_attend(q, c, bt, sl)
         elif name == "sparse_select_decode_group":
             d.select_attend_group(q, c, bt, sl)
-        elif name == "sparse_select_decode_split":
+        elif name in ("sparse_select_decode_split", "sparse_select_decode_split_blocks"):
             d.select_attend_split(q, c, bt, sl)
         elif name == "sparse_page_decode":
             d.score_select_attend(q, c, bt, sl)
@@ -696,7 +698,10 @@ def measure(args, workload, cpu=True):
         per_kernel_ms[n] = k0.elapsed_time(k1) / reps
         del g
 
-    kb, upages = kernel_bytes(wl, sel_idx, sel_cnt, sl_last, decs[0].decode_splits,
+    # partials per head the step's decode wrote (one per block of splits in
+    # the block-merged split decode)
+    n_part = decs[0].partials[0].shape[2]
+    kb, upages = kernel_bytes(wl, sel_idx, sel_cnt, sl_last, n_part,
                               token_level, group, fused, entmax, gauss,
                               h2o_per_head=decs[0].h2o_per_head)
     if one_launch:
@@ -717,7 +722,7 @@ def measure(args, workload, cpu=True):
         if "pagestats_update" in kb:   # the append, less its table reads (counted once)
             kb["h2o_select_decode"] += kb.pop("pagestats_update") - wl.B * 8
     elif in_group_decode or in_split_decode:   # the top-k's score read plus the decode
-        name = "sparse_select_decode_group" if in_group_decode else "sparse_select_decode_split"
+        name = "sparse_select_decode_group" if in_group_decode else split_name
         kb[name] = kb.pop("page_topk") - int(sel_cnt.sum()) * 4 + kb.pop("sparse_paged_decode")
     step_bytes = sum(kb.values())
     kern = {}
@@ -729,7 +734,7 @@ def measure(args, workload, cpu=True):
     focus = ("sparse_page_decode" if one_launch else
              "sparse_select_decode" if in_decode else
              "sparse_select_decode_group" if in_group_decode else
-             "sparse_select_decode_split" if in_split_decode else
+             split_name if in_split_decode else
              "h2o_select_decode" if token_fused else "sparse_paged_decode")
     a = kb[focus] / (per_kernel_ms[focus] * 1e-3) / 1e9
     # the committed counter summary of this workload and mode

@@ -349,6 +349,40 @@ int sparse_select_decode_split(const float *scores, int64_t score_ld, int topk_p
                                int32_t *sel_blk, hipStream_t stream);
 
 /*
+ * sparse_select_decode_split_blocks -- sparse_select_decode_split whose
+ * blocks also merge their splits: each block folds its waves' split states
+ * with lse_merge's algebra (in LDS) and writes one partial, so lse_merge
+ * then combines nb = sparse_select_decode_split_blocks_count(num_splits,
+ * page_size) partials per query head instead of num_splits.  The merged
+ * output equals that of sparse_select_decode_split + lse_merge up to the
+ * order of its fp32 sums.  [Same sources as sparse_select_decode_split and
+ * lse_merge.]
+ *
+ *   Arguments as sparse_select_decode_split, except
+ *   o_part   fp32 [B, H_q, nb, D], lse_part fp32 [B, H_q, nb]: block j of a
+ *            head's partial (its splits j*w .. j*w + w - 1, w = 16 at page
+ *            size 16, else 8; splits past num_splits are empty), normalised
+ *            output and natural-log lse; a block with no selected entry
+ *            writes zeros and -inf.
+ *   Errors as sparse_select_decode_split.
+ */
+int sparse_select_decode_split_blocks(const float *scores, int64_t score_ld, int topk_pages,
+                                      float topk_frac, int reserved_bos, int reserved_eos,
+                                      const float *q, int B, int H_q, int H_kv, int D,
+                                      const uint16_t *kv_cache, int64_t num_blocks,
+                                      int page_size, const int32_t *block_table,
+                                      int64_t bt_ld, const int32_t *seq_lens, int k_cap,
+                                      float scale, int num_splits,
+                                      const float *alibi_slopes, float *o_part,
+                                      float *lse_part, int32_t *sel_idx, int32_t *sel_cnt,
+                                      int32_t *sel_blk, hipStream_t stream);
+
+/* Partials per query head sparse_select_decode_split_blocks writes (nb);
+ * no device work; -1 on bad arguments (num_splits outside [1, 4096], an
+ * unsupported page size). */
+int sparse_select_decode_split_blocks_count(int num_splits, int page_size);
+
+/*
  * sparse_select_decode_group -- page_topk and sparse_paged_decode in one
  * launch for a selection shared by each kv head's query group (H_sel = H_kv:
  * the token-level flow, page_score_group).  One block per (split, kv head,

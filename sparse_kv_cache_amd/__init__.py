@@ -24,7 +24,8 @@ __all__ = [
     "h2o_heads_scratch_floats", "h2o_accumulate_noalloc", "h2o_select_decode", "h2o_select_decode_scratch_floats", "NOALLOC_SCRATCH_FLOATS",
     "entmax15_paged_decode",
     "entmax_scratch_floats", "sparse_select_decode", "sparse_select_decode_group",
-    "sparse_select_decode_split", "sparse_page_decode",
+    "sparse_select_decode_split", "sparse_select_decode_split_blocks",
+    "sparse_select_decode_split_blocks_count", "sparse_page_decode",
     "page_var_update", "gauss_moments", "gauss_select", "entmax15_paged_decode_merged",
     "skv_ref_stream_read", "skv_ref_gather_read", "library_path",
     "load_library", "SparseKVError", "EXPORTED_SYMBOLS",
@@ -41,7 +42,8 @@ EXPORTED_SYMBOLS = (
     "h2o_accumulate", "h2o_scratch_floats", "h2o_accumulate_heads",
     "h2o_heads_scratch_floats", "h2o_accumulate_noalloc", "h2o_select_decode", "h2o_select_decode_scratch_floats", "entmax15_paged_decode",
     "entmax_scratch_floats", "sparse_select_decode", "sparse_select_decode_group",
-    "sparse_select_decode_split", "sparse_page_decode",
+    "sparse_select_decode_split", "sparse_select_decode_split_blocks",
+    "sparse_select_decode_split_blocks_count", "sparse_page_decode",
     "page_var_update", "gauss_moments", "gauss_select", "entmax15_paged_decode_merged",
     "skv_ref_stream_read", "skv_ref_gather_read", "sparsekv_last_error",
     "sparsekv_build_id",
@@ -55,7 +57,8 @@ _INT_RETURNING = ("pagestats_update", "page_score", "page_score_ex", "page_score
                   "h2o_select_decode",
                   "entmax15_paged_decode",
                   "sparse_select_decode", "sparse_select_decode_group",
-                  "sparse_select_decode_split", "sparse_page_decode", "page_var_update", "gauss_moments", "gauss_select",
+                  "sparse_select_decode_split", "sparse_select_decode_split_blocks",
+                  "sparse_page_decode", "page_var_update", "gauss_moments", "gauss_select",
                   "entmax15_paged_decode_merged", "skv_ref_stream_read",
                   "skv_ref_gather_read")
 
@@ -136,6 +139,9 @@ def load_library():
     lib.sparse_select_decode_group.argtypes = [V, L, I, F, I, I, V, I, I, I, I, V, L, I, V,
                                                L, V, I, F, I, V, V, V, V, V, V, V]
     lib.sparse_select_decode_split.argtypes = lib.sparse_select_decode_group.argtypes
+    lib.sparse_select_decode_split_blocks.argtypes = lib.sparse_select_decode_group.argtypes
+    lib.sparse_select_decode_split_blocks_count.argtypes = [I, I]
+    lib.sparse_select_decode_split_blocks_count.restype = ctypes.c_int
     lib.sparse_page_decode.argtypes = [V, I, I, I, I, V, L, I, V, V, V, V, L, V, F, F, I, F,
                                        I, I, I, F, I, V, V, V, V, V, V, V, V]
     lib.entmax_scratch_floats.restype = ctypes.c_int64
@@ -708,6 +714,48 @@ def sparse_select_decode_split(scores, q, kv_cache, block_table, seq_lens, topk_
         _ptr(block_table), block_table.shape[1], _ptr(seq_lens), int(k_cap), float(scale),
         ns, _ptr(alibi_slopes), _ptr(o_part), _ptr(lse_part), _ptr(sel_idx), _ptr(sel_cnt),
         _ptr(sel_blk), _stream(stream)))
+
+
+def sparse_select_decode_split_blocks_count(num_splits, page_size) -> int:
+    """Partials per query head that sparse_select_decode_split_blocks writes."""
+    n = load_library().sparse_select_decode_split_blocks_count(int(num_splits), int(page_size))
+    if n < 0:
+        raise ValueError(f"no block count for num_splits={num_splits}, page_size={page_size}")
+    return n
+
+
+def sparse_select_decode_split_blocks(scores, q, kv_cache, block_table, seq_lens, topk_pages,
+                                      k_cap, scale, num_splits, o_part, lse_part,
+                                      topk_frac=0.0, reserved_bos=0, reserved_eos=1,
+                                      sel_idx=None, sel_cnt=None, sel_blk=None,
+                                      alibi_slopes=None, stream=None):
+    """sparse_select_decode_split whose blocks merge their splits: o_part
+    [B, H_q, nb, D] / lse_part [B, H_q, nb] receive one partial per block,
+    nb = sparse_select_decode_split_blocks_count(num_splits, page_size), for
+    lse_merge."""
+    lib = load_library()
+    _check("q", q, torch.float32, 3)
+    dev = q.device
+    B, H_q, D = q.shape
+    _check("scores", scores, torch.float32, 3, dev)
+    NB, P, H_kv = _cache(kv_cache, D, dev)
+    if scores is None or tuple(scores.shape[:2]) != (B, H_q):
+        raise ValueError("scores must be [B, H_q, score_ld]")
+    _check("block_table", block_table, torch.int32, 2, dev)
+    _check("seq_lens", seq_lens, torch.int32, 1, dev)
+    _batch(B, block_table, seq_lens)
+    if o_part is None or lse_part is None:
+        raise ValueError("o_part and lse_part are required")
+    nb = sparse_select_decode_split_blocks_count(num_splits, P)
+    _partials(o_part, lse_part, B, H_q, D, dev, num_splits=nb)
+    _optional_selection(sel_idx, sel_cnt, sel_blk, B, H_q, k_cap, dev)
+    alibi_slopes = _alibi_arg(alibi_slopes, H_q, dev)
+    _rc("sparse_select_decode_split_blocks", lib.sparse_select_decode_split_blocks(
+        _ptr(scores), scores.shape[2], int(topk_pages), float(topk_frac), int(reserved_bos),
+        int(reserved_eos), _ptr(q), B, H_q, H_kv, D, _ptr(kv_cache), NB, P,
+        _ptr(block_table), block_table.shape[1], _ptr(seq_lens), int(k_cap), float(scale),
+        int(num_splits), _ptr(alibi_slopes), _ptr(o_part), _ptr(lse_part), _ptr(sel_idx),
+        _ptr(sel_cnt), _ptr(sel_blk), _stream(stream)))
 
 
 def sparse_page_decode(q, kv_cache, k_min, k_max, k_mean, block_table, seq_lens, w_avg,

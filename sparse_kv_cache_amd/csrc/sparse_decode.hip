@@ -203,6 +203,9 @@ struct TopkArgs {
   // in-block accumulator update (token level): the logits pass's output
   const float* h_logits; const float* h_part; const uint16_t* h_snap; uint16_t* h_hh;
   int h_nchunk, h_chunk; float h_decay;
+  // split decode with in-block selection: nonzero merges each block's splits
+  // and writes one partial per block instead of one per split
+  int block_partials;
 };
 
 // Bits [0, x) set (x clipped to [0, 32]).
@@ -522,6 +525,51 @@ void sparse_decode_wave_kernel(
   }
 
   merge_slots<LPR>(m, l, acc);
+  if constexpr (TKI > 0 && !FUSE) {
+    if (ta.block_partials) {
+      // The block's splits merged through LDS with FUSE's algebra into one
+      // partial of the row (normalised output, natural-log lse), block j of
+      // the head writing partial j; lse_merge then combines a head's
+      // ceil(num_splits / WB) partials instead of its num_splits.
+      __shared__ float x_m[WB], x_l[WB];
+      __shared__ __align__(16) float x_acc[WB][D];
+      float mabs = m;
+      if (AL && m != -INFINITY) mabs = fmaf(slope2, static_cast<float>(pref * P - (S - 1)), m);
+      if (slot == 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x_acc[wave][c * 8 + i] = acc[i];
+      }
+      if (lane == 0) { x_m[wave] = mabs; x_l[wave] = l; }
+      __syncthreads();
+      if (wave != 0) return;
+      constexpr int DPL = D / 64;          // dims per lane
+      const int64_t brow = qrow * nsg + kb % nsg;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < WB; ++w) M = fmaxf(M, x_m[w]);
+      if (M == -INFINITY) {
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) o_part[brow * D + lane + 64 * j] = 0.0f;
+        if (lane == 0) lse_part[brow] = -INFINITY;
+        return;
+      }
+      float L = 0.0f, A[DPL];
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) A[j] = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WB; ++w) {
+        if (x_m[w] == -INFINITY) continue;
+        const float e = exp2f(x_m[w] - M);
+        L = fmaf(x_l[w], e, L);
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) A[j] = fmaf(x_acc[w][lane + 64 * j], e, A[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) o_part[brow * D + lane + 64 * j] = A[j] / L;
+      if (lane == 0) lse_part[brow] = (M + log2f(L)) * skv::kLn2;
+      return;
+    }
+  }
   if constexpr (FUSE) {
     // the split's state in absolute base-2 units, then the block merge
     __shared__ float f_m[WB], f_l[WB];
@@ -1411,18 +1459,18 @@ extern "C" int sparse_page_decode(const float* q, int B, int H_q, int H_kv, int 
   SKV_CHECK_LAUNCH();
 }
 
-extern "C" int sparse_select_decode_split(const float* scores, int64_t score_ld,
-                                          int topk_pages, float topk_frac, int reserved_bos,
-                                          int reserved_eos, const float* q, int B, int H_q,
-                                          int H_kv, int D, const uint16_t* kv_cache,
-                                          int64_t num_blocks, int page_size,
-                                          const int32_t* block_table, int64_t bt_ld,
-                                          const int32_t* seq_lens, int k_cap, float scale,
-                                          int num_splits, const float* alibi_slopes,
-                                          float* o_part, float* lse_part, int32_t* sel_idx,
-                                          int32_t* sel_cnt, int32_t* sel_blk,
-                                          hipStream_t stream) {
-  const char* who = "sparse_select_decode_split";
+namespace {
+
+// Split selection + decode, one partial per split, or (blocks) one per block
+// of split_waves splits.
+int split_select_decode(const char* who, bool blocks, const float* scores, int64_t score_ld,
+                        int topk_pages, float topk_frac, int reserved_bos, int reserved_eos,
+                        const float* q, int B, int H_q, int H_kv, int D,
+                        const uint16_t* kv_cache, int64_t num_blocks, int page_size,
+                        const int32_t* block_table, int64_t bt_ld, const int32_t* seq_lens,
+                        int k_cap, float scale, int num_splits, const float* alibi_slopes,
+                        float* o_part, float* lse_part, int32_t* sel_idx, int32_t* sel_cnt,
+                        int32_t* sel_blk, hipStream_t stream) {
   SKV_REQUIRE(B >= 0 && H_kv > 0 && H_q > 0 && H_q % H_kv == 0,
               "%s: need H_q a positive multiple of H_kv", who);
   const int G = H_q / H_kv;
@@ -1471,8 +1519,9 @@ extern "C" int sparse_select_decode_split(const float* scores, int64_t score_ld,
   const Args a{q, H_q, H_kv, G, kv_cache, num_blocks, page_size, block_table, bt_ld,
                seq_lens, nullptr, nullptr, nullptr, k_cap, scale * skv::kLog2e, num_splits,
                o_part, lse_part, alibi_slopes};
-  const TopkArgs ta{scores, score_ld, topk_pages, frac, reserved_bos, reserved_eos,
-                    sel_idx, sel_cnt, sel_blk};
+  TopkArgs ta{scores, score_ld, topk_pages, frac, reserved_bos, reserved_eos,
+              sel_idx, sel_cnt, sel_blk};
+  ta.block_partials = blocks ? 1 : 0;
   const bool al = alibi_slopes != nullptr;
   // entries per thread of the block's selection (wb * 64 threads)
   const int64_t per_thread = (score_ld + wb * 64 - 1) / (wb * 64);
@@ -1498,7 +1547,47 @@ extern "C" int sparse_select_decode_split(const float* scores, int64_t score_ld,
   }
 #undef SKV_SPL_T
 #undef SKV_SPL
-  SKV_CHECK_LAUNCH();
+  SKV_CHECK_LAUNCH_W(who);
+}
+
+}  // namespace
+
+extern "C" int sparse_select_decode_split(const float* scores, int64_t score_ld,
+                                          int topk_pages, float topk_frac, int reserved_bos,
+                                          int reserved_eos, const float* q, int B, int H_q,
+                                          int H_kv, int D, const uint16_t* kv_cache,
+                                          int64_t num_blocks, int page_size,
+                                          const int32_t* block_table, int64_t bt_ld,
+                                          const int32_t* seq_lens, int k_cap, float scale,
+                                          int num_splits, const float* alibi_slopes,
+                                          float* o_part, float* lse_part, int32_t* sel_idx,
+                                          int32_t* sel_cnt, int32_t* sel_blk,
+                                          hipStream_t stream) {
+  return split_select_decode("sparse_select_decode_split", false, scores, score_ld, topk_pages,
+                             topk_frac, reserved_bos, reserved_eos, q, B, H_q, H_kv, D,
+                             kv_cache, num_blocks, page_size, block_table, bt_ld, seq_lens,
+                             k_cap, scale, num_splits, alibi_slopes, o_part, lse_part,
+                             sel_idx, sel_cnt, sel_blk, stream);
+}
+
+extern "C" int sparse_select_decode_split_blocks_count(int num_splits, int page_size) {
+  if (num_splits < 1 || num_splits > 4096 || !skv_supported_page_size(page_size)) return -1;
+  const int wb = split_waves(page_size == 16 ? 16 : 0);
+  return (num_splits + wb - 1) / wb;
+}
+
+extern "C" int sparse_select_decode_split_blocks(
+    const float* scores, int64_t score_ld, int topk_pages, float topk_frac, int reserved_bos,
+    int reserved_eos, const float* q, int B, int H_q, int H_kv, int D, const uint16_t* kv_cache,
+    int64_t num_blocks, int page_size, const int32_t* block_table, int64_t bt_ld,
+    const int32_t* seq_lens, int k_cap, float scale, int num_splits, const float* alibi_slopes,
+    float* o_part, float* lse_part, int32_t* sel_idx, int32_t* sel_cnt, int32_t* sel_blk,
+    hipStream_t stream) {
+  return split_select_decode("sparse_select_decode_split_blocks", true, scores, score_ld,
+                             topk_pages, topk_frac, reserved_bos, reserved_eos, q, B, H_q,
+                             H_kv, D, kv_cache, num_blocks, page_size, block_table, bt_ld,
+                             seq_lens, k_cap, scale, num_splits, alibi_slopes, o_part,
+                             lse_part, sel_idx, sel_cnt, sel_blk, stream);
 }
 
 extern "C" int sparse_select_decode_group(const float* scores, int64_t score_ld,

@@ -45,7 +45,8 @@ from . import (entmax15_paged_decode, entmax15_paged_decode_merged, entmax_scrat
                page_score_group, page_topk, page_topk_blk, page_var_update,
                pagestats_update, sparse_page_decode, sparse_paged_decode,
                sparse_paged_decode_ex, sparse_paged_decode_merged, sparse_select_decode,
-               sparse_select_decode_group, sparse_select_decode_split)
+               sparse_select_decode_group, sparse_select_decode_split,
+               sparse_select_decode_split_blocks, sparse_select_decode_split_blocks_count)
 
 
 def alibi_slopes(H, device="cuda"):
@@ -212,6 +213,16 @@ class SparseDecoder:
                                        and selection == "topk" and bt_ld <= 8192
                                        and self.k_cap <= 4096)
         self.keep_selection = False
+        # ... whose blocks also merge their splits, so lse_merge combines a
+        # head's few block partials (split_blocks; False: one per split)
+        self.split_blocks = True
+        self.o_blk = self.lse_blk = None
+        if self.select_in_split_decode:
+            nb = sparse_select_decode_split_blocks_count(num_splits, page_size)
+            self.o_blk = torch.empty((B, H_q, nb, D), dtype=f32, device=dev)
+            self.lse_blk = torch.empty((B, H_q, nb), dtype=f32, device=dev)
+        # the partials merge() combines: the last decode form's
+        self.partials = (self.o_part, self.lse_part)
         # and scoring too: the whole page-level step in one launch, while the
         # device holds every block of it at once (two 8-wave blocks per CU,
         # 512 query rows); past that the separate page_score, which reads a
@@ -321,6 +332,7 @@ class SparseDecoder:
                       self.sel_cnt, self.topk_frac, self.bos, self.eos, stream=stream)
 
     def attend(self, q, kv_cache, block_table, seq_lens, stream=None):
+        self.partials = (self.o_part, self.lse_part)
         if self.attention == "entmax15" and self.entmax_fused:
             entmax15_paged_decode_merged(
                 q, kv_cache, block_table, seq_lens, self.sel_idx, self.sel_cnt, self.scale,
@@ -368,6 +380,7 @@ class SparseDecoder:
         """Selection (per kv head) and the group decode in one launch
         (select_in_group_decode); the partials still go through merge()."""
         keep = self.keep_selection
+        self.partials = (self.o_part, self.lse_part)
         sparse_select_decode_group(
             self.scores, q, kv_cache, block_table, seq_lens, self.topk_pages, self.k_cap,
             self.scale, self.o_part, self.lse_part, topk_frac=self.topk_frac,
@@ -375,16 +388,29 @@ class SparseDecoder:
             sel_idx=self.sel_idx if keep else None, sel_cnt=self.sel_cnt if keep else None,
             sel_blk=self.sel_blk if keep else None, alibi_slopes=self.alibi, stream=stream)
 
-    def select_attend_split(self, q, kv_cache, block_table, seq_lens, stream=None):
+    def select_attend_split(self, q, kv_cache, block_table, seq_lens, stream=None,
+                            blocks=None):
         """Selection (per query head) and the split decode in one launch
-        (select_in_split_decode); the partials go through merge()."""
+        (select_in_split_decode); the partials go through merge(): one per
+        block of splits (blocks, default split_blocks), else one per split."""
         keep = self.keep_selection
+        sel = dict(sel_idx=self.sel_idx if keep else None,
+                   sel_cnt=self.sel_cnt if keep else None,
+                   sel_blk=self.sel_blk if keep else None)
+        if self.split_blocks if blocks is None else blocks:
+            sparse_select_decode_split_blocks(
+                self.scores, q, kv_cache, block_table, seq_lens, self.topk_pages, self.k_cap,
+                self.scale, self.num_splits, self.o_blk, self.lse_blk,
+                topk_frac=self.topk_frac, reserved_bos=self.bos, reserved_eos=self.eos,
+                alibi_slopes=self.alibi, stream=stream, **sel)
+            self.partials = (self.o_blk, self.lse_blk)
+            return
         sparse_select_decode_split(
             self.scores, q, kv_cache, block_table, seq_lens, self.topk_pages, self.k_cap,
             self.scale, self.o_part, self.lse_part, topk_frac=self.topk_frac,
-            reserved_bos=self.bos, reserved_eos=self.eos,
-            sel_idx=self.sel_idx if keep else None, sel_cnt=self.sel_cnt if keep else None,
-            sel_blk=self.sel_blk if keep else None, alibi_slopes=self.alibi, stream=stream)
+            reserved_bos=self.bos, reserved_eos=self.eos, alibi_slopes=self.alibi,
+            stream=stream, **sel)
+        self.partials = (self.o_part, self.lse_part)
 
     def accumulate_select_attend(self, q, kv_cache, block_table, seq_lens, k_new=None,
                                  v_new=None, stream=None):
@@ -392,6 +418,7 @@ class SparseDecoder:
         accumulate, select and decode in two launches; hh updated, partials
         for merge()."""
         keep = self.keep_selection
+        self.partials = (self.o_part, self.lse_part)
         h2o_select_decode(
             q, kv_cache, block_table, seq_lens, self.hh, self.scratch, self.scale,
             self.topk_pages, self.k_cap, self.o_part, self.lse_part, decay=self.decay,
@@ -416,7 +443,8 @@ class SparseDecoder:
     def merge(self, stream=None):
         if self.fused or (self.attention == "entmax15" and self.entmax_fused):
             return                      # merged inside attend()
-        lse_merge(self.o_part, self.lse_part, self.out, self.lse, stream=stream)
+        o, lse = self.partials
+        lse_merge(o, lse, self.out, self.lse, stream=stream)
 
     # -------------------------------------------------------------- step
     def step(self, q, kv_cache, block_table, seq_lens, k_new=None, v_new=None,

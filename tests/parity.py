@@ -46,8 +46,10 @@ def dev(a, dtype=None):
 
 
 def poison(dec):
-    for t in (dec.scores, dec.o_part, dec.lse_part, dec.out, dec.lse):
-        t.fill_(float("nan"))
+    for t in (dec.scores, dec.o_part, dec.lse_part, dec.o_blk, dec.lse_blk, dec.out,
+              dec.lse):
+        if t is not None:
+            t.fill_(float("nan"))
     dec.sel_idx.fill_(-7)
     dec.sel_cnt.fill_(-7)
     dec.sel_blk.fill_(-7)
@@ -129,7 +131,7 @@ def check_split_select_decode_matches(dec, q, cache, bt, sl):
         t.fill_(-7)
     keep = dec.keep_selection
     dec.keep_selection = True
-    dec.select_attend_split(q, cache, bt, sl)
+    dec.select_attend_split(q, cache, bt, sl, blocks=False)
     dec.merge()
     dec.keep_selection = keep
     torch.cuda.synchronize()
@@ -137,6 +139,80 @@ def check_split_select_decode_matches(dec, q, cache, bt, sl):
     for name, a, b in zip(names, ref, (dec.sel_idx, dec.sel_cnt, dec.sel_blk, dec.o_part,
                                        dec.lse_part, dec.out, dec.lse)):
         assert torch.equal(a, b), f"select-in-split-decode {name} differs from separate launches"
+    # the block-merged form: the same selection; each block's partial the
+    # merge of its splits' partials; the merged output the same up to the
+    # order of the fold
+    for t in (dec.o_blk, dec.lse_blk, dec.out, dec.lse):
+        t.fill_(float("nan"))
+    for t in (dec.sel_idx, dec.sel_cnt, dec.sel_blk):
+        t.fill_(-7)
+    dec.keep_selection = True
+    dec.select_attend_split(q, cache, bt, sl, blocks=True)
+    dec.merge()
+    dec.keep_selection = keep
+    torch.cuda.synchronize()
+    for name, a, b in zip(names[:3], ref, (dec.sel_idx, dec.sel_cnt, dec.sel_blk)):
+        assert torch.equal(a, b), f"block-merged split decode: {name} differs"
+    check_block_partials(ref[3].cpu().numpy(), ref[4].cpu().numpy(),
+                         dec.o_blk.cpu().numpy(), dec.lse_blk.cpu().numpy(),
+                         split_block_waves(dec.P))
+    check_close_partials(ref[5], ref[6], dec.out, dec.lse, "block-merged split decode output")
+
+
+def split_block_waves(P):
+    """Splits one block of the block-merged split decode holds at page size P."""
+    import sparse_kv_cache_amd as skv
+    return 4096 // skv.sparse_select_decode_split_blocks_count(4096, P)
+
+
+def split_block_chunk(dec):
+    """Selection entries one block partial of dec's block-merged split decode
+    covers: its splits' chunks of ceil(k_cap / num_splits) entries each."""
+    return split_block_waves(dec.P) * -(-dec.k_cap // dec.num_splits)
+
+
+def check_decoder_partials(dec, q, cache_bits, bt, sl, rows_sel, G, scale, slopes=None,
+                           rows=None, heads=None):
+    """The partials dec's last decode wrote, against the oracle: one per
+    split, and with the split select-decode also the block-merged ones when
+    that form ran last.  rows / heads restrict the check (q, rows_sel, bt, sl
+    are then already the restricted ones)."""
+    def pick(t):
+        a = t.cpu().numpy()
+        if rows is not None:
+            a = a[rows]
+        return a if heads is None else a[:, heads]
+    o, lse = dec.partials
+    if o is not dec.o_part:
+        check_partials(pick(o), pick(lse), q, cache_bits, bt, sl, rows_sel, G, scale,
+                       dec.k_cap, slopes=slopes, chunk=split_block_chunk(dec))
+    else:
+        check_partials(pick(o), pick(lse), q, cache_bits, bt, sl, rows_sel, G, scale,
+                       dec.k_cap, slopes=slopes)
+
+
+def check_block_partials(o_part, lse_part, o_blk, lse_blk, wb):
+    """Block j of a row holds the oracle's LSE merge of the row's split
+    partials [j*wb, (j+1)*wb) (the kernel folds them in fp32 from the
+    unnormalised states: about 1e-6 of the row's magnitude apart); a block of
+    empty splits holds zeros and -inf."""
+    B, H, ns, D = o_part.shape
+    nb = o_blk.shape[2]
+    assert nb == -(-ns // wb), f"{nb} block partials for {ns} splits of {wb}"
+    for b in range(B):
+        for i in range(H):
+            for j in range(nb):
+                lo, hi = j * wb, min(ns, (j + 1) * wb)
+                o, lse = oracle.lse_merge(o_part[b, i, lo:hi], lse_part[b, i, lo:hi])
+                if np.isinf(lse):
+                    assert np.isinf(lse_blk[b, i, j]) and lse_blk[b, i, j] < 0, (b, i, j)
+                    assert np.all(o_blk[b, i, j] == 0), (b, i, j)
+                    continue
+                g = o_blk[b, i, j].astype(np.float64)
+                e = np.abs(g - o).max() / max(1.0, np.abs(o).max())
+                assert e <= 1e-5, f"block partial ({b},{i},{j}) err {e}"
+                assert abs(float(lse_blk[b, i, j]) - lse) <= lse_tol(lse), \
+                    f"block lse ({b},{i},{j}) {lse_blk[b, i, j]} vs {lse}"
 
 
 def check_token_fused_matches(dec, q, cache, bt, sl, pre_hh, k_new=None, v_new=None,
@@ -417,10 +493,11 @@ def check_attention(gpu_out, gpu_lse, q, cache_bits, bt, sl, rows_sel, G, scale,
 
 
 def check_partials(o_part, lse_part, q, cache_bits, bt, sl, rows_sel, G, scale,
-                   k_cap, slopes=None):
-    """Split s of a row holds entries [s*c, (s+1)*c), c = ceil(k_cap/splits)."""
+                   k_cap, slopes=None, chunk=None):
+    """Partial s of a row holds entries [s*c, (s+1)*c): c = chunk, by default
+    ceil(k_cap/splits) (one partial per split)."""
     B, H_q, ns, D = o_part.shape
-    c = -(-k_cap // ns)
+    c = -(-k_cap // ns) if chunk is None else chunk
     for b in range(B):
         for i in range(H_q):
             pages = list(rows_sel[b][i])

@@ -97,6 +97,7 @@ def test_header_declares_every_operation():
               "entmax15_paged_decode_merged",
               "lse_merge", "h2o_accumulate", "h2o_scratch_floats",
               "h2o_accumulate_heads", "h2o_heads_scratch_floats", "h2o_accumulate_noalloc",
+              "sparse_select_decode_split_blocks", "sparse_select_decode_split_blocks_count",
               "skv_ref_stream_read", "skv_ref_gather_read", "sparsekv_last_error"):
         assert n in names
     assert set(names) == set(skv.EXPORTED_SYMBOLS)
@@ -302,6 +303,15 @@ def test_validation_of_the_fused_select_decode_forms(lib):
     assert "sparse_select_decode_split" in _msg(lib)
     assert split(B=0, scores=None) == 0               # no rows: nothing to do
 
+    blocks = lib.sparse_select_decode_split_blocks
+    assert split(fn=blocks, ns=4097) == EINVAL and "num_splits" in _msg(lib)
+    assert split(fn=blocks, ld=8193) == EINVAL and "score_ld" in _msg(lib)
+    assert split(fn=blocks, topk=10, k_cap=5) == EINVAL and "k_cap" in _msg(lib)
+    assert split(fn=blocks, P=3) == EINVAL
+    assert split(fn=blocks, scores=None) == EFAULT
+    assert "sparse_select_decode_split_blocks" in _msg(lib)
+    assert split(fn=blocks, B=0, scores=None) == 0
+
     group = lib.sparse_select_decode_group
     assert split(fn=group, ld=8193) == EINVAL and "score_ld" in _msg(lib)
     assert split(fn=group, ns=0) == EINVAL
@@ -398,6 +408,19 @@ def test_scratch_size_query(lib):
     assert skv.h2o_scratch_floats(4, 8, 4352) == n
     assert lib.h2o_heads_scratch_floats(4, 32, 4352) == 4 * 32 * 4352 + 4 * 32 * chunks * 2
     assert skv.h2o_heads_scratch_floats(4, 32, 4352) == lib.h2o_heads_scratch_floats(4, 32, 4352)
+
+
+def test_split_block_count_query(lib):
+    """Block partials per query head of the block-merged split decode: one
+    per 16 splits at page size 16 (16-wave blocks), per 8 below it."""
+    count = lib.sparse_select_decode_split_blocks_count
+    assert count(1, 16) == 1 and count(16, 16) == 1 and count(17, 16) == 2
+    assert count(40, 16) == 3 and count(64, 16) == 4 and count(4096, 16) == 256
+    assert count(8, 4) == 1 and count(9, 4) == 2 and count(40, 1) == 5
+    assert count(0, 16) == -1 and count(4097, 16) == -1 and count(12, 3) == -1
+    assert skv.sparse_select_decode_split_blocks_count(64, 16) == 4
+    with pytest.raises(ValueError):
+        skv.sparse_select_decode_split_blocks_count(12, 32)
 
 
 def test_product_package_never_imports_the_oracle():

@@ -27,6 +27,12 @@ def test_launch_forms_by_splits_rows_and_selection():
     assert _dec(1, H_q=64, num_splits=64, bt_ld=8192).select_in_split_decode
     assert not _dec(1, H_q=64, num_splits=64, bt_ld=8193).select_in_split_decode
     assert not _dec(8).select_in_split_decode     # merged in-block instead
+    # whose blocks merge their 16 splits: a head's 64 splits leave 4 partials
+    d = _dec(1, H_q=64, num_splits=64)
+    assert d.split_blocks and tuple(d.o_blk.shape) == (1, 64, 4, 128)
+    assert tuple(d.lse_blk.shape) == (1, 64, 4)
+    assert d.partials[0] is d.o_part              # until a decode has run
+    assert _dec(8).o_blk is None
     assert not _dec(8, num_splits=16, group_select=True).select_in_split_decode
     assert not _dec(8, bt_ld=5000).select_in_decode
     d = _dec(8, group_select=True)                # one selection per kv head

@@ -13,7 +13,7 @@ from sparse_kv_cache_amd.decode import SparseDecoder
 
 from parity import (OUT_ATOL, bits, check_attention, check_gauss_row, check_partials,
                     check_group_select_decode_matches, check_scores,
-                    check_split_select_decode_matches,
+                    check_split_select_decode_matches, check_decoder_partials,
                     check_token_fused_matches, check_scores_alibi, check_scores_group, page_rows,
                     check_selection_exact, check_selection_vs_oracle,
                     check_stats, dev, per_head_rows, poison, say,
@@ -176,6 +176,9 @@ def run_page_case(wl, cache_cpu, q_cpu, exact_ties=False):
     per = per_head_rows(rows, wl.B, wl.H_q, wl.H_q)
     check_partials(d.o_part.cpu().numpy(), d.lse_part.cpu().numpy(), qd, cb,
                    wl.block_table, wl.seq_lens, per, wl.G, wl.softmax_scale, d.k_cap)
+    if d.select_in_split_decode:
+        check_decoder_partials(d, qd, cb, wl.block_table, wl.seq_lens, per, wl.G,
+                               wl.softmax_scale)
     worst = check_attention(d.out.cpu().numpy(), d.lse.cpu().numpy(), qd, cb,
                             wl.block_table, wl.seq_lens, per, wl.G,
                             wl.softmax_scale)
@@ -617,6 +620,9 @@ def run_alibi_case(wl, cache_cpu, q_cpu, group, slopes_np):
     check_partials(d.o_part.cpu().numpy(), d.lse_part.cpu().numpy(), qd, cb,
                    wl.block_table, wl.seq_lens, per, wl.G, wl.softmax_scale, d.k_cap,
                    slopes=sl64)
+    if d.select_in_split_decode:
+        check_decoder_partials(d, qd, cb, wl.block_table, wl.seq_lens, per, wl.G,
+                               wl.softmax_scale, slopes=sl64)
     worst = check_attention(d.out.cpu().numpy(), d.lse.cpu().numpy(), qd, cb,
                             wl.block_table, wl.seq_lens, per, wl.G, wl.softmax_scale,
                             slopes=sl64)

@@ -18,11 +18,15 @@ from parity import say
 pytestmark = pytest.mark.gpu
 
 B, H_Q, H_KV, D, P, NB, LD, K_CAP, NS = 2, 8, 2, 64, 16, 16, 8, 4, 2
+# splits of the block-merged split decode: more than one block of them
+NS_BLK = 40
 
 
 def _buffers():
     f32, i32, bf = torch.float32, torch.int32, torch.bfloat16
     z = lambda shape, dt=f32: torch.zeros(shape, dtype=dt, device="cuda")
+    nblk = skv.sparse_select_decode_split_blocks_count(NS_BLK, P)
+    assert 1 < nblk < NS_BLK
     t = dict(
         q=z((B, H_Q, D)), kv=z((2, NB, P, H_KV, D), bf),
         kmin=z((NB, H_KV, D), bf), kmax=z((NB, H_KV, D), bf), kmean=z((NB, H_KV, D)),
@@ -31,7 +35,8 @@ def _buffers():
         scores=z((B, H_Q, LD)), gscores=z((B, H_KV, LD)),
         sel_idx=z((B, H_Q, K_CAP), i32), sel_cnt=z((B, H_Q), i32),
         sel_blk=z((B, H_Q, K_CAP), i32), o_part=z((B, H_Q, NS, D)),
-        lse_part=z((B, H_Q, NS)), out=z((B, H_Q, D)), lse=z((B, H_Q)),
+        lse_part=z((B, H_Q, NS)), o_blk=z((B, H_Q, nblk, D)), lse_blk=z((B, H_Q, nblk)),
+        out=z((B, H_Q, D)), lse=z((B, H_Q)),
         tau=z((B, H_Q)), hh=z((NB * P, H_KV), bf), scratch=z((4096,)),
         mu=z((B, H_Q, LD)), var=z((B, H_Q, LD)), est=z((B, H_Q, LD)),
         knew=z((B, H_KV, D), bf),
@@ -92,6 +97,9 @@ def _calls(t):
         "sparse_select_decode_split": lambda: skv.sparse_select_decode_split(
             t["scores"], t["q"], t["kv"], t["bt"], t["sl"], 2, K_CAP, s, t["o_part"],
             t["lse_part"], sel_idx=t["sel_idx"], sel_cnt=t["sel_cnt"], sel_blk=t["sel_blk"]),
+        "sparse_select_decode_split_blocks": lambda: skv.sparse_select_decode_split_blocks(
+            t["scores"], t["q"], t["kv"], t["bt"], t["sl"], 2, K_CAP, s, NS_BLK, t["o_blk"],
+            t["lse_blk"], sel_idx=t["sel_idx"], sel_cnt=t["sel_cnt"], sel_blk=t["sel_blk"]),
         "sparse_select_decode_group": lambda: skv.sparse_select_decode_group(
             t["gscores"], t["q"], t["kv"], t["bt"], t["sl"], 2, K_CAP, s, t["o_part"],
             t["lse_part"], sel_idx=t["gsel_idx"], sel_cnt=t["gsel_cnt"],
@@ -151,6 +159,9 @@ CASES = [
     ("sparse_select_decode_split", "o_part", (B, H_Q, NS, D + 8)),
     ("sparse_select_decode_split", "sel_idx", (B, H_KV, K_CAP)),
     ("sparse_select_decode_split", "sl", (B + 1,)),
+    ("sparse_select_decode_split_blocks", "o_blk", (B, H_Q, NS_BLK, D)),
+    ("sparse_select_decode_split_blocks", "lse_blk", (B, H_Q - 1, 1)),
+    ("sparse_select_decode_split_blocks", "scores", (B, H_KV, LD)),
     ("sparse_select_decode_group", "gscores", (B, H_Q, LD)),
     ("sparse_select_decode_group", "gsel_cnt", (B, H_Q)),
     ("sparse_select_decode_group", "lse_part", (B, H_Q, NS + 1)),
@@ -162,12 +173,19 @@ CASES = [
 
 
 class _StubLibrary:
-    """Stands in for libsparsekv.so: records the entry points called, returns 0."""
+    """Stands in for libsparsekv.so: records the entry points called, returns 0.
+    Size queries, which only do host arithmetic, go to the real library."""
 
-    def __init__(self):
+    QUERIES = ("sparse_select_decode_split_blocks_count",)
+
+    def __init__(self, real):
         self.calls = []
+        self.real = real
 
     def __getattr__(self, name):
+        if name in self.QUERIES:
+            return getattr(self.real, name)
+
         def entry(*args):
             self.calls.append(name)
             return 0
@@ -176,7 +194,7 @@ class _StubLibrary:
 
 @pytest.fixture
 def stub(monkeypatch):
-    lib = _StubLibrary()
+    lib = _StubLibrary(skv.load_library())
     monkeypatch.setattr(skv, "_lib", lib)
     return lib
 

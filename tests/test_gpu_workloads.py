@@ -17,7 +17,8 @@ import oracle
 from sparse_kv_cache_amd import workloads as W
 from sparse_kv_cache_amd.decode import SparseDecoder
 
-from parity import (bits, bf16_bits_apart, check_attention, check_partials,
+from parity import (bits, bf16_bits_apart, check_attention, check_decoder_partials,
+                    check_partials,
                     check_scores, check_scores_group, check_selection_exact,
                     check_selection_vs_oracle, check_stats, dev, per_head_rows,
                     poison, say, selection_rows, sub_batch, check_sel_blk)
@@ -60,9 +61,8 @@ def page_level_parity(wl, cache, q_cpu, seq_lens_np, rows, d, partial_heads=4,
     per = per_head_rows(sel_rows, len(rows), wl.H_q, d.H_sel)
     hs = slice(0, partial_heads)
     if not d.select_in_decode:   # (selection + decode + merge in one launch: no partials)
-        check_partials(d.o_part.cpu().numpy()[rows][:, hs],
-                       d.lse_part.cpu().numpy()[rows][:, hs], qd[:, hs], cb, bt, sl,
-                       [p[hs] for p in per], wl.G, wl.softmax_scale, d.k_cap)
+        check_decoder_partials(d, qd[:, hs], cb, bt, sl, [p[hs] for p in per], wl.G,
+                               wl.softmax_scale, rows=list(rows), heads=hs)
     worst = check_attention(d.out.cpu().numpy()[rows], d.lse.cpu().numpy()[rows], qd,
                             cb, bt, sl, per, wl.G, wl.softmax_scale)
     return worst, ex
